@@ -1,0 +1,162 @@
+"""fp64 CPU oracle of the E2-TTT chunk forward -- TEST INFRASTRUCTURE.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The HIP library never calls it and has
+no fallback to it.
+
+The arithmetic lives in ``e2ttt_oracle.c`` (plain C, fp64, OpenMP); this
+module only compiles it with gcc and marshals numpy arrays.  Every input is
+widened to fp64 from exactly the values the GPU receives (bf16 inputs are
+widened after their rounding), so input rounding is never charged to the GPU.
+
+Citations are to "Rethinking Expressivity and Efficiency in Test-Time
+Training" (E2-TTT): the token-wise recurrence with chunk-start gradients is
+the optimisation-style view of App. A.5 (Eq. 7), the decay coupling is Eq. 14
+(App. A.3), the readout is Eq. 6 (§3.2).
+
+Parity pins (tests/test_oracle.py) tie every function here to something other
+than itself: the paper's kernel formulas of §3.2 in their ratio-sum form,
+torch autograd and finite differences for the gradients, the
+momentum-free/decay-free reduction to a summed-gradient update, the C = 1
+reduction to token-wise online descent (App. B.3), the gamma = 0 limit of
+App. A.3, geometric-series closed forms for constant scalars, and a worked
+example by hand under tests/golden/.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "e2ttt_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+LINEAR = 0
+SWIGLU = 1
+GAMMA_1_MINUS_ETA_ALPHA = 0
+ALPHA_IS_GAMMA = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+               "-shared", "-fPIC", "-std=c99", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB) or (
+                    os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
+                build()
+            lib = ctypes.CDLL(_LIB)
+            P = ctypes.POINTER(ctypes.c_double)
+            i64 = ctypes.c_int64
+            lib.oracle_chunk_forward.argtypes = (
+                [ctypes.c_int, ctypes.c_int] + [i64] * 6 + [P] * 11)
+            lib.oracle_chunk_forward.restype = ctypes.c_int
+            lib.oracle_token_descent.argtypes = [ctypes.c_int, i64, i64, P, P, P, P]
+            lib.oracle_token_descent.restype = ctypes.c_int
+            lib.oracle_fast_forward.argtypes = [ctypes.c_int, i64, i64, P, P, P]
+            lib.oracle_fast_forward.restype = ctypes.c_int
+            lib.oracle_scalar_kernels.argtypes = [ctypes.c_int, i64, i64] + [P] * 6
+            lib.oracle_scalar_kernels.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def state_size(kind: int, d: int, h: int) -> int:
+    return d * d if kind == LINEAR else 3 * d * h
+
+
+def set_threads(n: int) -> None:
+    """Set the OpenMP thread count used by the oracle (process-wide)."""
+    os.environ["OMP_NUM_THREADS"] = str(int(n))
+    try:
+        libgomp = ctypes.CDLL("libgomp.so.1")
+        libgomp.omp_set_num_threads(ctypes.c_int(int(n)))
+    except OSError:
+        pass
+
+
+def chunk_forward(kind, q, k, v, eta, alpha, beta, W0, M0, chunk, hidden=0,
+                  decay_mode=GAMMA_1_MINUS_ETA_ALPHA):
+    """Run the literal recurrence.  q,k,v: [B,H,L,d]; eta/alpha/beta: [B,H,L];
+    W0, M0: [B,H,P].  Returns (out [B,H,L,d], Wend, Mend), all float64."""
+    lib = _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    eta, alpha, beta = _f64(eta), _f64(alpha), _f64(beta)
+    W0, M0 = _f64(W0), _f64(M0)
+    B, H, L, d = q.shape
+    P = state_size(kind, d, hidden)
+    assert k.shape == q.shape and v.shape == q.shape
+    assert eta.shape == (B, H, L) and alpha.shape == (B, H, L) and beta.shape == (B, H, L)
+    assert W0.shape == (B, H, P) and M0.shape == (B, H, P)
+    out = np.empty_like(q)
+    Wend = np.empty_like(W0)
+    Mend = np.empty_like(M0)
+    rc = lib.oracle_chunk_forward(kind, decay_mode, B, H, L, d, hidden, chunk,
+                                  _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
+                                  _ptr(alpha), _ptr(beta), _ptr(W0), _ptr(M0),
+                                  _ptr(out), _ptr(Wend), _ptr(Mend))
+    if rc != 0:
+        raise RuntimeError(f"oracle_chunk_forward failed with code {rc}")
+    return out, Wend, Mend
+
+
+def token_descent(kind, W, k, v, d, hidden=0):
+    """Dense descent direction -grad_W 0.5||f_W(k)-v||^2 for one token."""
+    lib = _load()
+    W, k, v = _f64(W), _f64(k), _f64(v)
+    G = np.empty_like(W)
+    rc = lib.oracle_token_descent(kind, d, hidden, _ptr(W), _ptr(k), _ptr(v), _ptr(G))
+    if rc != 0:
+        raise RuntimeError(f"oracle_token_descent failed with code {rc}")
+    return G
+
+
+def fast_forward(kind, W, x, d, hidden=0):
+    """f_W(x) for one vector."""
+    lib = _load()
+    W, x = _f64(W), _f64(x)
+    y = np.empty(d, dtype=np.float64)
+    rc = lib.oracle_fast_forward(kind, d, hidden, _ptr(W), _ptr(x), _ptr(y))
+    if rc != 0:
+        raise RuntimeError(f"oracle_fast_forward failed with code {rc}")
+    return y
+
+
+def scalar_kernels(eta, alpha, beta, decay_mode=GAMMA_1_MINUS_ETA_ALPHA):
+    """Impulse-response kernels of each segment.  eta/alpha/beta: [nseg, n].
+    Returns kw [nseg,n], km [nseg,n], coef [nseg,3] = (cW, cM, cWM)."""
+    lib = _load()
+    eta, alpha, beta = _f64(eta), _f64(alpha), _f64(beta)
+    nseg, n = eta.shape
+    kw = np.empty_like(eta)
+    km = np.empty_like(eta)
+    coef = np.empty((nseg, 3), dtype=np.float64)
+    rc = lib.oracle_scalar_kernels(decay_mode, nseg, n, _ptr(eta), _ptr(alpha),
+                                   _ptr(beta), _ptr(kw), _ptr(km), _ptr(coef))
+    if rc != 0:
+        raise RuntimeError(f"oracle_scalar_kernels failed with code {rc}")
+    return kw, km, coef

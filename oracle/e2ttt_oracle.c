@@ -1,0 +1,347 @@
+/*
+ * e2ttt_oracle.c -- fp64 CPU oracle for the E2-TTT chunk forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the correctness reference that the
+ * HIP library is checked against.  It shares no code, header, table or helper
+ * with the GPU path and must never be linked into it; only the test suite, the
+ * smoke check and the benchmark's CPU-baseline leg load it.
+ *
+ * What it computes, and where the pages fix it
+ * (all citations are to "Rethinking Expressivity and Efficiency in Test-Time
+ *  Training", E2-TTT, as served by paperpeel.com, unless noted):
+ *
+ *   - The state is the fast weight W and a momentum buffer M of the same shape
+ *     ("W_t denotes the full collection of fast-weight tensors", §2).
+ *   - Within chunk r all per-token gradients are evaluated at the chunk-start
+ *     weights W_0 (§1, §3, App. A.5 "evaluated at the frozen W_0").
+ *   - The token-wise state recurrence (Eq. 7, the "optimisation-style view" of
+ *     App. A.5: momentum factor beta_t, L2 decay factor gamma_t) is taken as
+ *         M_t = beta_t * M_{t-1} + eta_t * G_t
+ *         W_t = gamma_t * W_{t-1} + M_t
+ *     with G_t the descent direction -grad_W l_t(W_0).  The display equation is
+ *     missing from the page; this is the reading whose closed form yields the
+ *     two kernels named in §3.2 (K^M = eta*beta~, K^W = eta*beta~*R).
+ *   - gamma_t = 1 - eta_t * alpha_t (Eq. 14, App. A.3 "Coupled
+ *     parameterization"); an alternative mode takes alpha_t as gamma_t itself.
+ *   - The inner loss is the key-value regression 0.5*||f_W(k_t) - v_t||^2
+ *     summed over the d outputs (§2).
+ *   - Output: o_t = f_{W_0}(q_t), the chunk-start weights (Eq. 6, §3.2).
+ *   - (W_C, M_C) of chunk r is (W_0, M_0) of chunk r+1 (§3 notation, §3.2
+ *     "Cross-chunk equivalence ... follows by induction").
+ *   - Inner learners: linear f_W(x) = W x (§2) and the three-matrix SwiGLU
+ *     f(x) = W2 (silu(W1 x) * (W3 x)) (§5.2, App. B.5 "three-matrix
+ *     fast-weight network").
+ *
+ * The recurrence is run literally, token by token, on every state entry.
+ * Each entry's recurrence involves only that entry, so the loops are ordered
+ * state-row outer, token inner; this performs the identical sequence of fp64
+ * operations per entry as a token-outer loop.
+ *
+ * State packing per (batch, head): linear W is d x d row-major.  SwiGLU is
+ * [W1 (h x d) | W3 (h x d) | W2 (d x h)], each row-major.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (no fast-math, so
+ * every operation is an IEEE fp64 operation in program order).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_LINEAR = 0, OR_SWIGLU = 1 };
+enum { OR_GAMMA_1_MINUS_ETA_ALPHA = 0, OR_ALPHA_IS_GAMMA = 1 };
+
+static double sigm(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/* gamma_t from the per-token scalars (Eq. 14, or alpha taken as gamma). */
+static double decay_factor(int decay_mode, double eta, double alpha) {
+  if (decay_mode == OR_ALPHA_IS_GAMMA) return alpha;
+  return 1.0 - eta * alpha;
+}
+
+static int64_t state_size(int kind, int64_t d, int64_t h) {
+  return kind == OR_LINEAR ? d * d : 3 * d * h;
+}
+
+/* y = f_W(x).  For SwiGLU also returns the hidden pre-activations a1 = W1 x,
+ * a3 = W3 x and z = silu(a1) * a3 (any of them may be NULL for linear). */
+static void fast_forward(int kind, int64_t d, int64_t h, const double* W,
+                         const double* x, double* a1, double* a3, double* z,
+                         double* y) {
+  if (kind == OR_LINEAR) {
+    for (int64_t i = 0; i < d; ++i) {
+      double s = 0.0;
+      for (int64_t j = 0; j < d; ++j) s += W[i * d + j] * x[j];
+      y[i] = s;
+    }
+    return;
+  }
+  const double* W1 = W;
+  const double* W3 = W + h * d;
+  const double* W2 = W + 2 * h * d;
+  for (int64_t i = 0; i < h; ++i) {
+    double s1 = 0.0, s3 = 0.0;
+    for (int64_t j = 0; j < d; ++j) {
+      s1 += W1[i * d + j] * x[j];
+      s3 += W3[i * d + j] * x[j];
+    }
+    a1[i] = s1;
+    a3[i] = s3;
+    z[i] = s1 * sigm(s1) * s3;
+  }
+  for (int64_t i = 0; i < d; ++i) {
+    double s = 0.0;
+    for (int64_t j = 0; j < h; ++j) s += W2[i * h + j] * z[j];
+    y[i] = s;
+  }
+}
+
+/* Rank-one factors of the descent direction G = -grad_W 0.5||f_W(k)-v||^2.
+ *   linear : G = e k^T,                e = v - W k                 (d)
+ *   SwiGLU : G_W2 = e z^T,             e = v - W2 z                (d)
+ *            G_W3 = u3 k^T,            u3 = (W2^T e) * silu(a1)    (h)
+ *            G_W1 = u1 k^T,            u1 = (W2^T e) * a3 * silu'(a1)
+ *   with silu'(a) = sigma(a) (1 + a (1 - sigma(a))).
+ * Chain rule of the loss of §2 through the learner; z is also returned. */
+static void descent_factors(int kind, int64_t d, int64_t h, const double* W,
+                            const double* k, const double* v, double* e,
+                            double* u1, double* u3, double* z, double* a1,
+                            double* a3, double* y) {
+  fast_forward(kind, d, h, W, k, a1, a3, z, y);
+  for (int64_t i = 0; i < d; ++i) e[i] = v[i] - y[i];
+  if (kind == OR_LINEAR) return;
+  const double* W2 = W + 2 * h * d;
+  for (int64_t j = 0; j < h; ++j) {
+    double dz = 0.0;
+    for (int64_t i = 0; i < d; ++i) dz += W2[i * h + j] * e[i];
+    double sg = sigm(a1[j]);
+    u3[j] = dz * (a1[j] * sg);
+    u1[j] = dz * a3[j] * (sg * (1.0 + a1[j] * (1.0 - sg)));
+  }
+}
+
+/* Dense descent direction G for one token at weights W (P entries, packed as
+ * the state).  Exposed for the gradient checks of the test suite. */
+int oracle_token_descent(int kind, int64_t d, int64_t h, const double* W,
+                         const double* k, const double* v, double* G) {
+  if (kind != OR_LINEAR && kind != OR_SWIGLU) return 1;
+  int64_t hh = kind == OR_LINEAR ? 1 : h;
+  double* buf = (double*)malloc(sizeof(double) * (size_t)(2 * d + 5 * hh));
+  if (!buf) return 2;
+  double *e = buf, *y = buf + d, *u1 = buf + 2 * d, *u3 = u1 + hh,
+         *z = u3 + hh, *a1 = z + hh, *a3 = a1 + hh;
+  descent_factors(kind, d, h, W, k, v, e, u1, u3, z, a1, a3, y);
+  if (kind == OR_LINEAR) {
+    for (int64_t i = 0; i < d; ++i)
+      for (int64_t j = 0; j < d; ++j) G[i * d + j] = e[i] * k[j];
+  } else {
+    double* G1 = G;
+    double* G3 = G + h * d;
+    double* G2 = G + 2 * h * d;
+    for (int64_t i = 0; i < h; ++i)
+      for (int64_t j = 0; j < d; ++j) {
+        G1[i * d + j] = u1[i] * k[j];
+        G3[i * d + j] = u3[i] * k[j];
+      }
+    for (int64_t i = 0; i < d; ++i)
+      for (int64_t j = 0; j < h; ++j) G2[i * h + j] = e[i] * z[j];
+  }
+  free(buf);
+  return 0;
+}
+
+/* y = f_W(x) for one vector (readout check helper). */
+int oracle_fast_forward(int kind, int64_t d, int64_t h, const double* W,
+                        const double* x, double* y) {
+  if (kind != OR_LINEAR && kind != OR_SWIGLU) return 1;
+  int64_t hh = kind == OR_LINEAR ? 1 : h;
+  double* buf = (double*)malloc(sizeof(double) * (size_t)(3 * hh));
+  if (!buf) return 2;
+  fast_forward(kind, d, h, W, x, buf, buf + hh, buf + 2 * hh, y);
+  free(buf);
+  return 0;
+}
+
+/*
+ * The chunk forward over a whole sequence, literal recurrence.
+ *   q, k, v, out : [B, H, L, d]      eta, alpha, beta : [B, H, L]
+ *   W0, M0, Wend, Mend : [B, H, P]
+ * Chunks are consecutive runs of C tokens; a final run shorter than C (when
+ * C does not divide L) is a chunk of its own.  L == 0 copies the state.
+ * Returns 0 on success, nonzero on bad arguments or allocation failure.
+ */
+int oracle_chunk_forward(int kind, int decay_mode, int64_t B, int64_t H,
+                         int64_t L, int64_t d, int64_t h, int64_t C,
+                         const double* q, const double* k, const double* v,
+                         const double* eta, const double* alpha,
+                         const double* beta, const double* W0,
+                         const double* M0, double* out, double* Wend,
+                         double* Mend) {
+  if (kind != OR_LINEAR && kind != OR_SWIGLU) return 1;
+  if (decay_mode != OR_GAMMA_1_MINUS_ETA_ALPHA &&
+      decay_mode != OR_ALPHA_IS_GAMMA)
+    return 1;
+  if (B < 0 || H < 0 || L < 0 || d <= 0 || C <= 0) return 1;
+  if (kind == OR_SWIGLU && h <= 0) return 1;
+  const int64_t P = state_size(kind, d, h);
+  const int64_t hh = kind == OR_LINEAR ? 1 : h;
+  const int64_t Cmax = C < L ? C : (L > 0 ? L : 1);
+  int status = 0;
+
+  for (int64_t u = 0; u < B * H; ++u) {
+    double* W = Wend + u * P;
+    double* M = Mend + u * P;
+    memmove(W, W0 + u * P, sizeof(double) * (size_t)P);
+    memmove(M, M0 + u * P, sizeof(double) * (size_t)P);
+    const double* qu = q + u * L * d;
+    const double* ku = k + u * L * d;
+    const double* vu = v + u * L * d;
+    const double* etu = eta + u * L;
+    const double* alu = alpha + u * L;
+    const double* beu = beta + u * L;
+    double* ou = out + u * L * d;
+
+    /* Per-chunk buffers: frozen chunk-start weights and per-token factors. */
+    double* Ws = (double*)malloc(sizeof(double) * (size_t)P);
+    double* fe = (double*)malloc(sizeof(double) * (size_t)(Cmax * d));
+    double* fu1 = (double*)malloc(sizeof(double) * (size_t)(Cmax * hh));
+    double* fu3 = (double*)malloc(sizeof(double) * (size_t)(Cmax * hh));
+    double* fz = (double*)malloc(sizeof(double) * (size_t)(Cmax * hh));
+    double* gam = (double*)malloc(sizeof(double) * (size_t)Cmax);
+    if (!Ws || !fe || !fu1 || !fu3 || !fz || !gam) {
+      status = 2;
+    }
+
+    for (int64_t t0 = 0; status == 0 && t0 < L; t0 += C) {
+      const int64_t n = (L - t0) < C ? (L - t0) : C;
+      memcpy(Ws, W, sizeof(double) * (size_t)P); /* W_0 of this chunk */
+
+      /* Readout o_t = f_{W_0}(q_t) and descent factors at W_0. */
+#pragma omp parallel
+      {
+        double* tmp = (double*)malloc(sizeof(double) * (size_t)(3 * hh + 2 * d));
+        double *a1 = tmp, *a3 = tmp + hh, *zz = tmp + 2 * hh, *y = zz + hh,
+               *y2 = y + d;
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < n; ++t) {
+          const int64_t tt = t0 + t;
+          fast_forward(kind, d, h, Ws, qu + tt * d, a1, a3, zz, y);
+          for (int64_t i = 0; i < d; ++i) ou[tt * d + i] = y[i];
+          descent_factors(kind, d, h, Ws, ku + tt * d, vu + tt * d,
+                          fe + t * d, fu1 + t * hh, fu3 + t * hh,
+                          fz + t * hh, a1, a3, y2);
+        }
+        free(tmp);
+      }
+      for (int64_t t = 0; t < n; ++t)
+        gam[t] = decay_factor(decay_mode, etu[t0 + t], alu[t0 + t]);
+
+      /* Token-wise recurrence on every state entry:
+       *   M <- beta_t M + eta_t G_t ;  W <- gamma_t W + M.
+       * Row r of the packed state has a fixed left factor index and a right
+       * factor vector (k_t or z_t). */
+      int64_t nrows, ncols;
+      if (kind == OR_LINEAR) {
+        nrows = d;
+        ncols = d;
+      } else {
+        nrows = 2 * h + d;
+        ncols = 0; /* per row, below */
+      }
+#pragma omp parallel for schedule(dynamic, 4)
+      for (int64_t r = 0; r < nrows; ++r) {
+        const double* left;  /* left factor per token, stride lstride */
+        int64_t lidx, lstride;
+        const double* right; /* right factor per token, stride rstride */
+        int64_t rstride, nc;
+        double* w;
+        double* m;
+        if (kind == OR_LINEAR) {
+          left = fe; lidx = r; lstride = d;
+          right = ku + t0 * d; rstride = d; nc = ncols;
+          w = W + r * d; m = M + r * d;
+        } else if (r < h) { /* W1 row r */
+          left = fu1; lidx = r; lstride = hh;
+          right = ku + t0 * d; rstride = d; nc = d;
+          w = W + r * d; m = M + r * d;
+        } else if (r < 2 * h) { /* W3 row r-h */
+          left = fu3; lidx = r - h; lstride = hh;
+          right = ku + t0 * d; rstride = d; nc = d;
+          w = W + r * d; m = M + r * d;
+        } else { /* W2 row r-2h */
+          left = fe; lidx = r - 2 * h; lstride = d;
+          right = fz; rstride = hh; nc = h;
+          w = W + 2 * h * d + (r - 2 * h) * h;
+          m = M + 2 * h * d + (r - 2 * h) * h;
+        }
+        for (int64_t t = 0; t < n; ++t) {
+          const double bt = beu[t0 + t];
+          const double et = etu[t0 + t];
+          const double gt = gam[t];
+          const double lt = left[t * lstride + lidx];
+          const double* rt = right + t * rstride;
+          for (int64_t j = 0; j < nc; ++j) {
+            const double g = lt * rt[j];        /* G_t entry (descent) */
+            m[j] = bt * m[j] + et * g;          /* momentum */
+            w[j] = gt * w[j] + m[j];            /* weight */
+          }
+        }
+      }
+    }
+    free(Ws); free(fe); free(fu1); free(fu3); free(fz); free(gam);
+    if (status) return status;
+  }
+  return 0;
+}
+
+/*
+ * Per-token scalar kernels of one chunk by their definition: the factor with
+ * which a unit impulse enters the chunk-end state when the recurrence above is
+ * run on scalars.
+ *   kw[t] : W_C when G_t = 1 and every other input is 0   (weight kernel)
+ *   km[t] : M_C for the same impulse                       (momentum kernel)
+ *   coef[0] = cW  : W_C when W_0 = 1 (M_0 = 0, G = 0)
+ *   coef[1] = cM  : M_C when M_0 = 1 (W_0 = 0, G = 0)
+ *   coef[2] = cWM : W_C when M_0 = 1 (W_0 = 0, G = 0)
+ * Arrays are [nseg, n] with nseg segments of n tokens; coef is [nseg, 3].
+ * O(n^2) per segment: each impulse is propagated literally to the chunk end.
+ */
+int oracle_scalar_kernels(int decay_mode, int64_t nseg, int64_t n,
+                          const double* eta, const double* alpha,
+                          const double* beta, double* kw, double* km,
+                          double* coef) {
+  if (decay_mode != OR_GAMMA_1_MINUS_ETA_ALPHA &&
+      decay_mode != OR_ALPHA_IS_GAMMA)
+    return 1;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t sg = 0; sg < nseg; ++sg) {
+    const double* e = eta + sg * n;
+    const double* a = alpha + sg * n;
+    const double* b = beta + sg * n;
+    for (int64_t t = 0; t < n; ++t) {
+      /* token t receives the impulse: M = beta*0 + eta*1, W = gamma*0 + M */
+      double m = e[t] * 1.0;
+      double w = m;
+      for (int64_t s = t + 1; s < n; ++s) {
+        m = b[s] * m;
+        w = decay_factor(decay_mode, e[s], a[s]) * w + m;
+      }
+      kw[sg * n + t] = w;
+      km[sg * n + t] = m;
+    }
+    double w = 1.0, m = 0.0; /* W_0 impulse */
+    for (int64_t s = 0; s < n; ++s) {
+      m = b[s] * m;
+      w = decay_factor(decay_mode, e[s], a[s]) * w + m;
+    }
+    coef[sg * 3 + 0] = w;
+    w = 0.0; m = 1.0; /* M_0 impulse */
+    for (int64_t s = 0; s < n; ++s) {
+      m = b[s] * m;
+      w = decay_factor(decay_mode, e[s], a[s]) * w + m;
+    }
+    coef[sg * 3 + 1] = m;
+    coef[sg * 3 + 2] = w;
+  }
+  return 0;
+}

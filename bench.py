@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the E2-TTT chunk forward on one MI355X.
+
+One step = one e2ttt_chunk_forward over the whole workload (all batch x head
+units, all chunks: scan, forward at W_0, readout, backward, both scaled
+aggregations, chunk-end states), inputs already resident in HBM.
+
+Prints ONE JSON line:
+  value         tokens/s = batch * seq_len / (time per step), N = 1 GPU
+  roofline      dominant kernel: algorithmic flops per launch / its average
+                launch duration (HIP events around every launch of that
+                kernel, recorded by e2ttt_chunk_forward_timed in a second
+                timed pass of the same steps) against the published peak
+  cpu_baseline  the fp64 oracle timed on this host's cores on a bounded
+                sample of the same workload, scaled to tokens/s
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (needed to bracket launches inside the library)."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self.h.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        f = ctypes.c_float()
+        rc = self.h.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(f.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.h.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def kernel_work(w, cls):
+    """Algorithmic work of ALL launches of one kernel class in one step:
+    (amount, unit).  Flops for the contractions, HBM bytes for the rest."""
+    import chunk_weight_update_amd as cwu
+    BH, L, d, h = w.B * w.H, w.L, w.d, w.h
+    iob = 2 if w.io == 1 else 4
+    if w.kind == 0:
+        if cls == cwu.KERNEL_LINEAR_FWD:
+            return 2.0 * 2 * L * d * d * BH, "flop"
+        if cls == cwu.KERNEL_LINEAR_AGG:
+            return 4.0 * L * d * d * BH, "flop"
+    else:
+        if cls == cwu.KERNEL_FWD13:
+            return 8.0 * L * d * h * BH, "flop"
+        if cls == cwu.KERNEL_FWD2:
+            return 4.0 * L * d * h * BH, "flop"
+        if cls == cwu.KERNEL_BWD:
+            return 2.0 * L * d * h * BH, "flop"
+        if cls == cwu.KERNEL_AGG:
+            return 12.0 * L * d * h * BH, "flop"
+        if cls == cwu.KERNEL_PREP:
+            # K read + K^T written; W0 read + operand shadows written
+            return 2.0 * BH * L * d * iob + BH * 3 * d * h * (4 + 4 * iob), "byte"
+    if cls == cwu.KERNEL_SCAN:
+        return 20.0 * BH * L, "byte"  # eta, alpha, beta read; K^W, K^M written
+    return 0.0, "byte"
+
+
+def algorithmic_flops(w):
+    if w.kind == 0:
+        return 8.0 * w.d * w.d * w.L * w.B * w.H
+    return 26.0 * w.d * w.h * w.L * w.B * w.H
+
+
+def cpu_baseline(w, inp, budget_s):
+    """Time the fp64 oracle on a bounded sample: the first n (b, h) units of
+    the workload over the full sequence, n chosen so that it runs for about
+    budget_s; scaled to workload tokens/s."""
+    import numpy as np
+
+    import oracle
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    oracle.set_threads(cores)
+    oracle.build(force=False)
+    BH = w.B * w.H
+
+    def run_units(n):
+        sl = lambda a: a.reshape((BH,) + a.shape[2:])[:n][None]
+        t0 = time.perf_counter()
+        oracle.chunk_forward(w.kind, sl(inp["q64"]), sl(inp["k64"]), sl(inp["v64"]),
+                             sl(inp["eta"]), sl(inp["alpha"]), sl(inp["beta"]), sl(inp["W0"]),
+                             sl(inp["M0"]), w.C, w.h)
+        return time.perf_counter() - t0
+
+    t1 = run_units(1)
+    n = int(max(1, min(BH, budget_s / max(t1, 1e-6))))
+    tn = run_units(n) if n > 1 else t1
+    t_full = tn * BH / n
+    return {"value": w.B * w.L / t_full, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of {BH} (batch, head) units x all {w.L} tokens "
+                      f"({tn:.1f} s fp64, literal token-wise recurrence), scaled to the "
+                      f"whole workload"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--flags", type=int, default=0, help="e2ttt_problem.flags")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the (batch, head) units would shard across GPUs with no communication); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import chunk_weight_update_amd as cwu
+    from chunk_weight_update_amd.inputs import BENCH_WORKLOAD, WORKLOADS, make_workload_inputs
+
+    w = WORKLOADS[args.workload or BENCH_WORKLOAD]
+    torch.cuda.set_device(0)
+    log(f"bench: workload {w.name}")
+    inp = make_workload_inputs(w, seed=0)
+    dev = "cuda:0"
+    t = {}
+    for n in ("q", "k", "v"):
+        a = np.ascontiguousarray(inp[n])
+        t[n] = (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if w.io == 1
+                else torch.from_numpy(a)).to(dev)
+    for n in ("eta", "alpha", "beta", "W0", "M0"):
+        t[n] = torch.from_numpy(inp[n]).to(dev)
+    prob = cwu.make_problem(w.kind, w.B, w.H, w.L, w.d, w.h, w.C, w.io, 0, args.flags)
+    run = cwu.ChunkForward(prob, device=dev)
+    call_args = (t["q"], t["k"], t["v"], t["eta"], t["alpha"], t["beta"], t["W0"], t["M0"])
+
+    for _ in range(args.warmup):
+        run(*call_args)
+    torch.cuda.synchronize()
+    log(f"bench: warmup {args.warmup} done")
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        run(*call_args)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tokens = w.B * w.L
+    value = tokens / (ms * 1e-3)
+    log(f"bench: {args.steps} steps, {ms:.4f} ms/step, {value:.4g} tokens/s")
+
+    # Second timed pass: per-kernel-class launch durations with HIP events.
+    ev = HipEvents()
+    classes = ([cwu.KERNEL_SCAN, cwu.KERNEL_LINEAR_FWD, cwu.KERNEL_LINEAR_AGG] if w.kind == 0
+               else [cwu.KERNEL_SCAN, cwu.KERNEL_PREP, cwu.KERNEL_FWD13, cwu.KERNEL_FWD2,
+                     cwu.KERNEL_BWD, cwu.KERNEL_AGG])
+    per_step_launches = 2 * max(w.n_chunks, 2) + 2
+    kernels = {}
+    steps_k = max(1, min(args.steps, 10))
+    for cls in classes:
+        evs = ev.create(2 * per_step_launches * steps_k)
+        per = []
+        for s in range(steps_k):
+            chunk = evs[2 * per_step_launches * s: 2 * per_step_launches * (s + 1)]
+            _, nrec = cwu.chunk_forward_timed(prob, *call_args, run.out, run.W_end, run.M_end,
+                                              run.workspace, cls, chunk)
+            per.append((chunk, nrec))
+        torch.cuda.synchronize()
+        durs = []
+        for chunk, nrec in per:
+            durs += [ev.elapsed_ms(chunk[2 * j], chunk[2 * j + 1]) for j in range(nrec)]
+        ev.destroy(evs)
+        if not durs:
+            continue
+        launches_per_step = len(durs) / steps_k
+        avg_ms = sum(durs) / len(durs)
+        work, unit = kernel_work(w, cls)
+        per_launch = work / launches_per_step
+        rate = per_launch / (avg_ms * 1e-3)
+        kernels[cwu.KERNEL_NAMES[cls]] = {
+            "launches_per_step": launches_per_step, "avg_launch_ms": avg_ms,
+            "ms_per_step": avg_ms * launches_per_step,
+            ("tflops" if unit == "flop" else "gbs"): rate / (1e12 if unit == "flop" else 1e9),
+            "work_per_launch": per_launch, "work_unit": unit}
+        log(f"bench: kernel {cwu.KERNEL_NAMES[cls]}: {launches_per_step:g} launches/step, "
+            f"avg {avg_ms * 1e3:.1f} us, {kernels[cwu.KERNEL_NAMES[cls]]}")
+
+    peak_mfma = PEAK_BF16_TFLOPS if w.io == 1 else PEAK_FP32_TFLOPS
+    dom_name = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    dk = kernels[dom_name]
+    if dk["work_unit"] == "flop":
+        roof = {"kernel": dom_name, "bound": "mfma", "achieved": dk["tflops"],
+                "peak": peak_mfma, "unit": "TFLOP/s", "frac": dk["tflops"] / peak_mfma,
+                "traffic": None}
+    else:
+        roof = {"kernel": dom_name, "bound": "hbm", "achieved": dk["gbs"], "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": dk["gbs"] / PEAK_HBM_GBS, "traffic": None}
+    flops = algorithmic_flops(w)
+    line = {
+        "metric": "TTT-layer fwd tokens/sec on 1 MI355X; MFMA util % of bf16 peak",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.io == 1 else "fp32", "data": "synthetic",
+        "config": w.describe() | {"flags": args.flags},
+        "mfma_util_pct_of_bf16_peak": 100.0 * flops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+        "tflops_algorithmic": flops / (ms * 1e-3) / 1e12,
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the fp64 oracle on the host cores")
+        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

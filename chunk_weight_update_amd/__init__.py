@@ -1,0 +1,202 @@
+"""E2-TTT chunk-parallel fast-weight update on AMD MI355X (gfx950).
+
+Thin Python binding of the C ABI in ``include/e2ttt.h`` (``libe2ttt.so``,
+built in-tree by ``chunk_weight_update_amd.build``).  This module only
+marshals arguments: every step of the computation runs in the HIP kernels.
+There is no CPU fallback; if the library is missing, calls raise.
+
+The names mirror the C entry points: ``validate``, ``workspace_bytes``,
+``chunk_forward``, ``scalar_kernels``, ``status_string``.  Tensors are torch
+tensors on the GPU (PyTorch supplies device memory and streams).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libe2ttt.so")
+
+OK, EINVAL, EWORKSPACE, EUNSUPPORTED, EHIP = 0, 1, 2, 3, 4
+LINEAR, SWIGLU = 0, 1
+F32, BF16 = 0, 1
+GAMMA_1_MINUS_ETA_ALPHA, ALPHA_IS_GAMMA = 0, 1
+FLAG_COMPENSATED_WEIGHTS = 1
+
+
+class Problem(ctypes.Structure):
+    """Mirror of ``e2ttt_problem``."""
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("kind", ctypes.c_int32),
+        ("batch", ctypes.c_int64),
+        ("heads", ctypes.c_int64),
+        ("seq_len", ctypes.c_int64),
+        ("dim", ctypes.c_int64),
+        ("hidden", ctypes.c_int64),
+        ("chunk", ctypes.c_int64),
+        ("io_dtype", ctypes.c_int32),
+        ("decay_mode", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
+    ]
+
+
+def make_problem(kind: int, batch: int, heads: int, seq_len: int, dim: int, hidden: int,
+                 chunk: int, io_dtype: int, decay_mode: int = GAMMA_1_MINUS_ETA_ALPHA,
+                 flags: int = 0) -> Problem:
+    return Problem(ctypes.sizeof(Problem), kind, batch, heads, seq_len, dim, hidden, chunk,
+                   io_dtype, decay_mode, flags, 0)
+
+
+class E2tttError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+        self.status = status
+
+
+_lock = threading.Lock()
+_lib = None
+
+EXPORTED = ("e2ttt_validate", "e2ttt_workspace_bytes", "e2ttt_chunk_forward",
+            "e2ttt_scalar_kernels", "e2ttt_chunk_forward_timed", "e2ttt_status_string")
+
+# e2ttt_kernel_class
+KERNEL_SCAN, KERNEL_PREP, KERNEL_FWD13, KERNEL_FWD2, KERNEL_BWD, KERNEL_AGG = range(6)
+KERNEL_LINEAR_FWD, KERNEL_LINEAR_AGG, KERNEL_NUM_CLASSES = 6, 7, 8
+KERNEL_NAMES = ("scan", "prep", "fwd13", "fwd2", "bwd", "agg", "linear_fwd", "linear_agg")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libe2ttt.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it first (python -m "
+                    "chunk_weight_update_amd.build or __graft_entry__.build()); there is no "
+                    "fallback implementation")
+            L = ctypes.CDLL(LIB_PATH)
+            P = ctypes.POINTER(Problem)
+            vp = ctypes.c_void_p
+            L.e2ttt_validate.argtypes = [P]
+            L.e2ttt_validate.restype = ctypes.c_int
+            L.e2ttt_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+            L.e2ttt_workspace_bytes.restype = ctypes.c_int
+            L.e2ttt_chunk_forward.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t, vp]
+            L.e2ttt_chunk_forward.restype = ctypes.c_int
+            L.e2ttt_chunk_forward_timed.argtypes = ([P] + [vp] * 12 + [ctypes.c_size_t, vp] +
+                                                    [ctypes.c_int, ctypes.POINTER(vp),
+                                                     ctypes.c_int,
+                                                     ctypes.POINTER(ctypes.c_int)])
+            L.e2ttt_chunk_forward_timed.restype = ctypes.c_int
+            L.e2ttt_scalar_kernels.argtypes = [P] + [vp] * 7
+            L.e2ttt_scalar_kernels.restype = ctypes.c_int
+            L.e2ttt_status_string.argtypes = [ctypes.c_int]
+            L.e2ttt_status_string.restype = ctypes.c_char_p
+            _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().e2ttt_status_string(int(status)).decode()
+
+
+def validate(prob: Problem) -> int:
+    return lib().e2ttt_validate(ctypes.byref(prob))
+
+
+def workspace_bytes(prob: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    st = lib().e2ttt_workspace_bytes(ctypes.byref(prob), ctypes.byref(n))
+    if st != OK:
+        raise E2tttError(st, "e2ttt_workspace_bytes")
+    return int(n.value)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def chunk_forward(prob: Problem, q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end,
+                  workspace, workspace_nbytes: Optional[int] = None, stream=None,
+                  check: bool = True) -> int:
+    """Call ``e2ttt_chunk_forward`` on device tensors (or raw pointers).
+    Returns the status; raises E2tttError on failure when ``check``."""
+    if workspace_nbytes is None:
+        workspace_nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().e2ttt_chunk_forward(
+        ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(alpha), _ptr(beta),
+        _ptr(W0), _ptr(M0), _ptr(out), _ptr(W_end), _ptr(M_end), _ptr(workspace),
+        int(workspace_nbytes), _stream(stream))
+    if check and st != OK:
+        raise E2tttError(st, "e2ttt_chunk_forward")
+    return st
+
+
+def chunk_forward_timed(prob: Problem, q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end,
+                        workspace, kernel_class: int, events, workspace_nbytes=None,
+                        stream=None, check: bool = True):
+    """Call ``e2ttt_chunk_forward_timed``: same work as chunk_forward, with the
+    HIP events ``events`` (raw hipEvent_t handles as ints) recorded around
+    each launch of ``kernel_class``.  Returns (status, n_recorded)."""
+    if workspace_nbytes is None:
+        workspace_nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    arr = (ctypes.c_void_p * max(len(events), 1))(*[ctypes.c_void_p(e) for e in events])
+    nrec = ctypes.c_int(0)
+    st = lib().e2ttt_chunk_forward_timed(
+        ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(alpha), _ptr(beta),
+        _ptr(W0), _ptr(M0), _ptr(out), _ptr(W_end), _ptr(M_end), _ptr(workspace),
+        int(workspace_nbytes), _stream(stream), int(kernel_class), arr, len(events),
+        ctypes.byref(nrec))
+    if check and st != OK:
+        raise E2tttError(st, "e2ttt_chunk_forward_timed")
+    return st, int(nrec.value)
+
+
+def scalar_kernels(prob: Problem, eta, alpha, beta, k_w, k_m, chunk_coef, stream=None,
+                   check: bool = True) -> int:
+    """Call ``e2ttt_scalar_kernels`` on device tensors."""
+    st = lib().e2ttt_scalar_kernels(ctypes.byref(prob), _ptr(eta), _ptr(alpha), _ptr(beta),
+                                    _ptr(k_w), _ptr(k_m), _ptr(chunk_coef), _stream(stream))
+    if check and st != OK:
+        raise E2tttError(st, "e2ttt_scalar_kernels")
+    return st
+
+
+class ChunkForward:
+    """Holds the output and workspace tensors of one problem shape, so that
+    repeated calls allocate nothing."""
+
+    def __init__(self, prob: Problem, device="cuda"):
+        import torch
+        self.prob = prob
+        B, H, L, d = prob.batch, prob.heads, prob.seq_len, prob.dim
+        P = d * d if prob.kind == LINEAR else 3 * d * prob.hidden
+        io = torch.bfloat16 if prob.io_dtype == BF16 else torch.float32
+        self.out = torch.empty((B, H, L, d), dtype=io, device=device)
+        self.W_end = torch.empty((B, H, P), dtype=torch.float32, device=device)
+        self.M_end = torch.empty((B, H, P), dtype=torch.float32, device=device)
+        nbytes = workspace_bytes(prob)
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+    def __call__(self, q, k, v, eta, alpha, beta, W0, M0, stream=None):
+        chunk_forward(self.prob, q, k, v, eta, alpha, beta, W0, M0, self.out, self.W_end,
+                      self.M_end, self.workspace, stream=stream)
+        return self.out, self.W_end, self.M_end

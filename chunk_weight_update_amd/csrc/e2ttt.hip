@@ -1,0 +1,431 @@
+// e2ttt.hip -- C ABI of the E2-TTT chunk forward (host side + launches).
+//
+// Call sequence of e2ttt_chunk_forward (all on the caller's stream):
+//   scan (all chunks, one launch) -> K^T staging (all chunks) -> operand
+//   shadow of W0 -> per chunk r: fwd13, fwd2, bwd, agg.  The chunk loop is
+//   serial because chunk r+1 starts from chunk r's end state (§3.2 of
+//   "Rethinking Expressivity and Efficiency in Test-Time Training").
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "e2ttt.h"
+#include "kernels.hpp"
+
+using namespace e2ttt;
+
+namespace {
+
+constexpr int64_t kMaxChunk = 12288;
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+struct Plan {
+  int64_t B, H, BH, L, d, h, C, Cp, nC, P;
+  int kind, io, mode, krep;
+  size_t opsz;  // bytes per GEMM operand element (2 for bf16, 4 for fp32)
+  // workspace offsets (bytes)
+  size_t kw, km, coef, kt, w13s, w2s, w2ts, zrow, a1s, a3s, grow, ut, gt, zt, gw, gm, total;
+};
+
+e2ttt_status check_problem(const e2ttt_problem* p) {
+  if (!p || p->struct_size != sizeof(e2ttt_problem)) return E2TTT_EINVAL;
+  if (p->kind != E2TTT_LINEAR && p->kind != E2TTT_SWIGLU) return E2TTT_EINVAL;
+  if (p->io_dtype != E2TTT_F32 && p->io_dtype != E2TTT_BF16) return E2TTT_EINVAL;
+  if (p->decay_mode != E2TTT_GAMMA_1_MINUS_ETA_ALPHA && p->decay_mode != E2TTT_ALPHA_IS_GAMMA)
+    return E2TTT_EINVAL;
+  if ((p->flags & ~static_cast<uint32_t>(E2TTT_FLAG_COMPENSATED_WEIGHTS)) != 0u) return E2TTT_EINVAL;
+  if (p->reserved != 0u) return E2TTT_EINVAL;
+  if (p->batch < 1 || p->heads < 1 || p->seq_len < 0 || p->dim < 1 || p->chunk < 1)
+    return E2TTT_EINVAL;
+  if (p->kind == E2TTT_LINEAR) {
+    if (p->hidden != 0) return E2TTT_EINVAL;
+    if (p->dim % 16 != 0 || p->dim > 128) return E2TTT_EUNSUPPORTED;
+  } else {
+    if (p->hidden < 1) return E2TTT_EINVAL;
+    if (p->dim % 128 != 0 || p->hidden % 128 != 0 || p->dim > 1024 || p->hidden > 4096)
+      return E2TTT_EUNSUPPORTED;
+  }
+  if (p->chunk > kMaxChunk) return E2TTT_EUNSUPPORTED;
+  // Every element count must fit comfortably in int64 and every grid in 2^31.
+  int64_t bh, bhl, tot;
+  if (!mul_ok(p->batch, p->heads, &bh) || !mul_ok(bh, p->seq_len + kMaxChunk, &bhl) ||
+      !mul_ok(bhl, 4 * p->dim, &tot))
+    return E2TTT_EUNSUPPORTED;
+  if (p->kind == E2TTT_SWIGLU) {
+    int64_t a, b;
+    if (!mul_ok(bh, 12 * p->dim, &a) || !mul_ok(a, p->hidden, &b)) return E2TTT_EUNSUPPORTED;
+    if (!mul_ok(bhl, 4 * p->hidden, &a)) return E2TTT_EUNSUPPORTED;
+  }
+  if (tot > (int64_t(1) << 46)) return E2TTT_EUNSUPPORTED;
+  return E2TTT_OK;
+}
+
+e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
+  const e2ttt_status st = check_problem(p);
+  if (st != E2TTT_OK) return st;
+  Plan& q = *pl;
+  std::memset(&q, 0, sizeof(q));
+  q.B = p->batch; q.H = p->heads; q.BH = q.B * q.H; q.L = p->seq_len;
+  q.d = p->dim; q.h = p->hidden; q.C = p->chunk;
+  q.kind = p->kind; q.io = p->io_dtype; q.mode = p->decay_mode;
+  q.nC = q.L > 0 ? (q.L + q.C - 1) / q.C : 0;
+  q.P = q.kind == E2TTT_LINEAR ? q.d * q.d : 3 * q.d * q.h;
+  const size_t f4 = 4;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o = align256(o + bytes); return at; };
+  if (q.kind == E2TTT_LINEAR) {
+    q.Cp = (q.C + 63) / 64 * 64;
+    q.krep = 1;
+    q.opsz = 4;
+    q.kw = take(f4 * q.BH * q.nC * q.Cp);
+    q.km = take(f4 * q.BH * q.nC * q.Cp);
+    q.coef = take(f4 * q.BH * q.nC * 4);
+    q.gw = take(f4 * q.BH * q.Cp * q.d);
+    q.gm = take(f4 * q.BH * q.Cp * q.d);
+  } else {
+    q.Cp = (q.C + 127) / 128 * 128;
+    q.opsz = q.io == E2TTT_BF16 ? 2 : 4;
+    q.krep = (q.io == E2TTT_BF16 && (p->flags & E2TTT_FLAG_COMPENSATED_WEIGHTS)) ? 2 : 1;
+    const size_t T = q.opsz;
+    q.kw = take(f4 * q.BH * q.nC * q.Cp);
+    q.km = take(f4 * q.BH * q.nC * q.Cp);
+    q.coef = take(f4 * q.BH * q.nC * 4);
+    q.kt = take(T * q.BH * q.nC * q.d * q.Cp);
+    q.w13s = take(T * q.BH * 2 * q.h * q.krep * q.d);
+    q.w2s = take(T * q.BH * q.d * q.krep * q.h);
+    q.w2ts = take(T * q.BH * q.h * q.krep * q.d);
+    q.zrow = take(T * q.BH * 2 * q.Cp * q.h);
+    q.a1s = take(f4 * q.BH * q.Cp * q.h);
+    q.a3s = take(f4 * q.BH * q.Cp * q.h);
+    q.grow = take(T * q.BH * q.Cp * q.d);
+    q.ut = take(T * q.BH * 4 * q.h * q.Cp);
+    q.gt = take(T * q.BH * 2 * q.d * q.Cp);
+    q.zt = take(T * q.BH * q.h * q.Cp);
+  }
+  q.total = q.L == 0 ? 0 : o;  // an empty sequence only copies the state
+  return E2TTT_OK;
+}
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+Range rng(const void* p, size_t bytes) {
+  const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+  return Range{b, b + bytes};
+}
+
+// gfx950 check, cached per device (a property of the device, not of a call).
+std::atomic<int> g_arch_ok[64];
+
+e2ttt_status device_ok() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return E2TTT_EHIP;
+  if (dev < 0 || dev >= 64) return E2TTT_EUNSUPPORTED;
+  int v = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return E2TTT_EHIP;
+    v = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_ok[dev].store(v, std::memory_order_relaxed);
+  }
+  return v == 1 ? E2TTT_OK : E2TTT_EUNSUPPORTED;
+}
+
+std::atomic<int> g_attr_done{0};
+
+void set_lds_attributes() {
+  if (g_attr_done.load(std::memory_order_acquire)) return;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_scan),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lin_fwd<float>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lin_fwd<bf16_t>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  g_attr_done.store(1, std::memory_order_release);
+}
+
+unsigned grid1(int64_t n) { return static_cast<unsigned>(n); }
+
+// Optional event bracketing of one kernel class (benchmark instrumentation).
+struct Instr {
+  int kclass = -1;
+  void* const* ev = nullptr;
+  int n_pairs = 0;
+  int used = 0;
+  void before(int c, hipStream_t s) {
+    if (c == kclass && used < n_pairs) (void)hipEventRecord(static_cast<hipEvent_t>(ev[2 * used]), s);
+  }
+  void after(int c, hipStream_t s) {
+    if (c == kclass && used < n_pairs) {
+      (void)hipEventRecord(static_cast<hipEvent_t>(ev[2 * used + 1]), s);
+      ++used;
+    }
+  }
+};
+
+#define E2TTT_LAUNCH(I, cls, ...)   \
+  do {                              \
+    (I).before((cls), st);          \
+    hipLaunchKernelGGL(__VA_ARGS__); \
+    (I).after((cls), st);           \
+  } while (0)
+
+void launch_scan(const Plan& q, const float* eta, const float* alpha, const float* beta,
+                 float* kw, float* km, int64_t ustride, int64_t rstride, int64_t pad,
+                 float* coef, int cstride, hipStream_t st, Instr& I) {
+  const size_t lds = static_cast<size_t>(3 * q.C) * sizeof(float);
+  E2TTT_LAUNCH(I, E2TTT_KERNEL_SCAN, k_scan, dim3(grid1(q.BH * q.nC)), dim3(64), lds, st, eta,
+               alpha, beta, q.L, q.C, q.nC, q.mode, kw, km, ustride, rstride, pad, coef, cstride);
+}
+
+template <typename T>
+void launch_swiglu(const Plan& q, const void* qv, const void* kv, const void* vv,
+                   const float* eta, const float* alpha, const float* beta, const float* W0,
+                   const float* M0, void* outv, float* Wend, float* Mend, char* ws,
+                   hipStream_t st, Instr& I) {
+  const T* Q = static_cast<const T*>(qv);
+  const T* K = static_cast<const T*>(kv);
+  const T* V = static_cast<const T*>(vv);
+  T* O = static_cast<T*>(outv);
+  Shape s{q.BH, q.L, q.d, q.h, q.C, q.Cp, q.nC, q.krep};
+  float* kw = reinterpret_cast<float*>(ws + q.kw);
+  float* km = reinterpret_cast<float*>(ws + q.km);
+  float* coef = reinterpret_cast<float*>(ws + q.coef);
+  T* kt = reinterpret_cast<T*>(ws + q.kt);
+  T* w13s = reinterpret_cast<T*>(ws + q.w13s);
+  T* w2s = reinterpret_cast<T*>(ws + q.w2s);
+  T* w2ts = reinterpret_cast<T*>(ws + q.w2ts);
+  T* zrow = reinterpret_cast<T*>(ws + q.zrow);
+  float* a1s = reinterpret_cast<float*>(ws + q.a1s);
+  float* a3s = reinterpret_cast<float*>(ws + q.a3s);
+  T* grow = reinterpret_cast<T*>(ws + q.grow);
+  T* ut = reinterpret_cast<T*>(ws + q.ut);
+  T* gt = reinterpret_cast<T*>(ws + q.gt);
+  T* zt = reinterpret_cast<T*>(ws + q.zt);
+
+  launch_scan(q, eta, alpha, beta, kw, km, q.nC * q.Cp, q.Cp, q.Cp, coef, 4, st, I);
+  E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, k_prep_kt<T>,
+               dim3(grid1(q.BH * q.nC * (q.Cp / 64) * (q.d / 64))), dim3(256), 0, st, s, K, kt);
+  E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, k_prep_shadow<T>, dim3(grid1((q.BH * q.P + 255) / 256)),
+               dim3(256), 0, st, s, W0, w13s, w2s, w2ts);
+  const int64_t na = (4 * q.h / 128) * (q.d / 128), nb = (2 * q.d / 128) * (q.h / 128);
+  for (int64_t r = 0; r < q.nC; ++r) {
+    const float* Win = r == 0 ? W0 : Wend;
+    const float* Min = r == 0 ? M0 : Mend;
+    const int ri = static_cast<int>(r);
+    E2TTT_LAUNCH(I, E2TTT_KERNEL_FWD13, k_fwd13<T>,
+                 dim3(grid1(q.BH * (2 * q.Cp / 128) * (2 * q.h / 128))), dim3(256), 0, st, s, ri,
+                 Q, K, w13s, zrow, a1s, a3s, zt);
+    E2TTT_LAUNCH(I, E2TTT_KERNEL_FWD2, k_fwd2<T>,
+                 dim3(grid1(q.BH * (2 * q.Cp / 128) * (q.d / 128))), dim3(256), 0, st, s, ri, V,
+                 O, zrow, w2s, kw, km, grow, gt);
+    E2TTT_LAUNCH(I, E2TTT_KERNEL_BWD, k_bwd<T>, dim3(grid1(q.BH * (q.Cp / 128) * (q.h / 128))),
+                 dim3(256), 0, st, s, ri, grow, w2ts, a1s, a3s, kw, km, ut);
+    E2TTT_LAUNCH(I, E2TTT_KERNEL_AGG, k_agg<T>, dim3(grid1(q.BH * (na + nb))), dim3(256), 0, st,
+                 s, ri, static_cast<int>(r == q.nC - 1), ut, kt, gt, zt, coef, Win, Min, Wend,
+                 Mend, w13s, w2s, w2ts);
+  }
+}
+
+template <typename IO>
+void launch_linear(const Plan& q, const void* qv, const void* kv, const void* vv,
+                   const float* eta, const float* alpha, const float* beta, const float* W0,
+                   const float* M0, void* outv, float* Wend, float* Mend, char* ws,
+                   hipStream_t st, Instr& I) {
+  const IO* Q = static_cast<const IO*>(qv);
+  const IO* K = static_cast<const IO*>(kv);
+  const IO* V = static_cast<const IO*>(vv);
+  IO* O = static_cast<IO*>(outv);
+  Shape s{q.BH, q.L, q.d, 0, q.C, q.Cp, q.nC, 1};
+  float* kw = reinterpret_cast<float*>(ws + q.kw);
+  float* km = reinterpret_cast<float*>(ws + q.km);
+  float* coef = reinterpret_cast<float*>(ws + q.coef);
+  float* gw = reinterpret_cast<float*>(ws + q.gw);
+  float* gm = reinterpret_cast<float*>(ws + q.gm);
+  launch_scan(q, eta, alpha, beta, kw, km, q.nC * q.Cp, q.Cp, q.Cp, coef, 4, st, I);
+  const size_t lds_f = static_cast<size_t>(q.d * (q.d + 1) + 64 * (q.d + 1)) * sizeof(float);
+  const size_t lds_a = static_cast<size_t>(2 * 64 * 16 + 64 * q.d) * sizeof(float);
+  for (int64_t r = 0; r < q.nC; ++r) {
+    const float* Win = r == 0 ? W0 : Wend;
+    const float* Min = r == 0 ? M0 : Mend;
+    const int ri = static_cast<int>(r);
+    E2TTT_LAUNCH(I, E2TTT_KERNEL_LINEAR_FWD, k_lin_fwd<IO>, dim3(grid1(q.BH * (2 * q.Cp / 64))),
+                 dim3(256), lds_f, st, s, ri, Q, K, V, Win, kw, km, O, gw, gm);
+    E2TTT_LAUNCH(I, E2TTT_KERNEL_LINEAR_AGG, k_lin_agg<IO>, dim3(grid1(q.BH * (q.d / 16))),
+                 dim3(256), lds_a, st, s, ri, K, gw, gm, coef, Win, Min, Wend, Mend);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* e2ttt_status_string(e2ttt_status s) {
+  switch (s) {
+    case E2TTT_OK: return "E2TTT_OK";
+    case E2TTT_EINVAL: return "E2TTT_EINVAL: invalid argument";
+    case E2TTT_EWORKSPACE: return "E2TTT_EWORKSPACE: workspace too small";
+    case E2TTT_EUNSUPPORTED: return "E2TTT_EUNSUPPORTED: shape, dtype or device not supported";
+    case E2TTT_EHIP: return "E2TTT_EHIP: HIP runtime error";
+  }
+  return "E2TTT: unknown status";
+}
+
+e2ttt_status e2ttt_validate(const e2ttt_problem* prob) { return check_problem(prob); }
+
+e2ttt_status e2ttt_workspace_bytes(const e2ttt_problem* prob, size_t* bytes) {
+  if (!bytes) return E2TTT_EINVAL;
+  Plan q;
+  const e2ttt_status st = make_plan(prob, &q);
+  if (st != E2TTT_OK) return st;
+  *bytes = q.total;
+  return E2TTT_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+e2ttt_status forward_impl(const e2ttt_problem* prob, const void* q, const void* k, const void* v,
+                          const float* eta, const float* alpha, const float* beta,
+                          const float* W0, const float* M0, void* out, float* W_end,
+                          float* M_end, void* workspace, size_t workspace_bytes, void* stream,
+                          Instr& I) {
+  Plan pl;
+  e2ttt_status status = make_plan(prob, &pl);
+  if (status != E2TTT_OK) return status;
+  if (!W0 || !M0 || !W_end || !M_end) return E2TTT_EINVAL;
+  const bool empty = pl.L == 0;
+  if (!empty && (!q || !k || !v || !eta || !alpha || !beta || !out)) return E2TTT_EINVAL;
+  if (!empty && pl.total > 0 && !workspace) return E2TTT_EINVAL;
+  const void* ptrs16[] = {q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end};
+  for (const void* p : ptrs16)
+    if (p && !aligned(p, 16)) return E2TTT_EINVAL;
+  if (workspace && !aligned(workspace, 256)) return E2TTT_EINVAL;
+  if (!empty && workspace_bytes < pl.total) return E2TTT_EWORKSPACE;
+
+  const size_t iosz = pl.io == E2TTT_BF16 ? 2 : 4;
+  const size_t nx = static_cast<size_t>(pl.BH * pl.L * pl.d) * iosz;
+  const size_t ns = static_cast<size_t>(pl.BH * pl.L) * 4;
+  const size_t np = static_cast<size_t>(pl.BH * pl.P) * 4;
+  const Range in[] = {rng(q, nx), rng(k, nx), rng(v, nx), rng(eta, ns), rng(alpha, ns),
+                      rng(beta, ns), rng(W0, np), rng(M0, np)};
+  const Range o_out = rng(out, nx), o_w = rng(W_end, np), o_m = rng(M_end, np),
+              o_ws = rng(workspace, empty ? 0 : pl.total);
+  const Range outs[] = {o_out, o_w, o_m, o_ws};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = a + 1; b < 4; ++b)
+      if (overlap(outs[a], outs[b])) return E2TTT_EINVAL;
+    for (int i = 0; i < 8; ++i) {
+      if (!overlap(outs[a], in[i])) continue;
+      const bool exact_w = a == 1 && i == 6 && o_w.lo == in[6].lo;
+      const bool exact_m = a == 2 && i == 7 && o_m.lo == in[7].lo;
+      if (!exact_w && !exact_m) return E2TTT_EINVAL;
+    }
+  }
+
+  status = device_ok();
+  if (status != E2TTT_OK) return status;
+  set_lds_attributes();
+  (void)hipGetLastError();  // clear a stale error so only our launches are reported
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (empty) {
+    if (W_end != W0 || M_end != M0) {
+      const int64_t n = pl.BH * pl.P;
+      hipLaunchKernelGGL(k_copy2, dim3(grid1((n + 255) / 256)), dim3(256), 0, st, W0, M0, W_end,
+                         M_end, n);
+    }
+  } else {
+    char* ws = static_cast<char*>(workspace);
+    if (pl.kind == E2TTT_LINEAR) {
+      if (pl.io == E2TTT_BF16)
+        launch_linear<bf16_t>(pl, q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end, ws, st, I);
+      else
+        launch_linear<float>(pl, q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end, ws, st, I);
+    } else {
+      if (pl.io == E2TTT_BF16)
+        launch_swiglu<bf16_t>(pl, q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end, ws, st, I);
+      else
+        launch_swiglu<float>(pl, q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end, ws, st, I);
+    }
+  }
+  return hipGetLastError() == hipSuccess ? E2TTT_OK : E2TTT_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+e2ttt_status e2ttt_chunk_forward(const e2ttt_problem* prob, const void* q, const void* k,
+                                 const void* v, const float* eta, const float* alpha,
+                                 const float* beta, const float* W0, const float* M0, void* out,
+                                 float* W_end, float* M_end, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  Instr none;
+  return forward_impl(prob, q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end, workspace,
+                      workspace_bytes, stream, none);
+}
+
+e2ttt_status e2ttt_chunk_forward_timed(const e2ttt_problem* prob, const void* q, const void* k,
+                                       const void* v, const float* eta, const float* alpha,
+                                       const float* beta, const float* W0, const float* M0,
+                                       void* out, float* W_end, float* M_end, void* workspace,
+                                       size_t workspace_bytes, void* stream, int kernel_class,
+                                       void* const* events, int n_events, int* n_recorded) {
+  if (kernel_class < 0 || kernel_class >= E2TTT_KERNEL_NUM_CLASSES || n_events < 0)
+    return E2TTT_EINVAL;
+  if (n_events > 0 && !events) return E2TTT_EINVAL;
+  for (int i = 0; i < n_events; ++i)
+    if (!events[i]) return E2TTT_EINVAL;
+  Instr I;
+  I.kclass = kernel_class;
+  I.ev = events;
+  I.n_pairs = n_events / 2;
+  const e2ttt_status st = forward_impl(prob, q, k, v, eta, alpha, beta, W0, M0, out, W_end,
+                                       M_end, workspace, workspace_bytes, stream, I);
+  if (n_recorded) *n_recorded = st == E2TTT_OK ? I.used : 0;
+  return st;
+}
+
+e2ttt_status e2ttt_scalar_kernels(const e2ttt_problem* prob, const float* eta,
+                                  const float* alpha, const float* beta, float* k_w, float* k_m,
+                                  float* chunk_coef, void* stream) {
+  Plan pl;
+  e2ttt_status st = make_plan(prob, &pl);
+  if (st != E2TTT_OK) return st;
+  if (pl.L == 0) return E2TTT_OK;
+  if (!eta || !alpha || !beta || !k_w || !k_m || !chunk_coef) return E2TTT_EINVAL;
+  const void* p16[] = {eta, alpha, beta, k_w, k_m};
+  for (const void* p : p16)
+    if (!aligned(p, 16)) return E2TTT_EINVAL;
+  if (!aligned(chunk_coef, 4)) return E2TTT_EINVAL;
+  const size_t ns = static_cast<size_t>(pl.BH * pl.L) * 4;
+  const Range in[] = {rng(eta, ns), rng(alpha, ns), rng(beta, ns)};
+  const Range outs[] = {rng(k_w, ns), rng(k_m, ns),
+                        rng(chunk_coef, static_cast<size_t>(pl.BH * pl.nC * 3) * 4)};
+  for (int a = 0; a < 3; ++a) {
+    for (int b = a + 1; b < 3; ++b)
+      if (overlap(outs[a], outs[b])) return E2TTT_EINVAL;
+    for (int i = 0; i < 3; ++i)
+      if (overlap(outs[a], in[i])) return E2TTT_EINVAL;
+  }
+  st = device_ok();
+  if (st != E2TTT_OK) return st;
+  set_lds_attributes();
+  (void)hipGetLastError();
+  Instr none;
+  launch_scan(pl, eta, alpha, beta, k_w, k_m, pl.L, pl.C, 0, chunk_coef, 3,
+              static_cast<hipStream_t>(stream), none);
+  return hipGetLastError() == hipSuccess ? E2TTT_OK : E2TTT_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,685 @@
+// kernels.hpp -- HIP kernels of the E2-TTT chunk forward for gfx950.
+//
+// Method: "Rethinking Expressivity and Efficiency in Test-Time Training"
+// (E2-TTT).  Per chunk of C tokens and per (batch, head) unit:
+//   scan   : the scalar kernels K^W_t, K^M_t and the carried-state factors
+//            (cW, cM, cWM) from eta, alpha, beta (§3.2, App. A.2-A.3);
+//   fwd13  : A1 = X W1^T, A3 = X W3^T, Z = silu(A1) * A3 for X = [K; Q]
+//            at the chunk-start weights (§3, Eq. 6);
+//   fwd2   : Y = Z W2^T; Q rows give the readout o_t (Eq. 6), K rows give
+//            the activation gradient g_t = v_t - f(k_t) (§3.2 "one backward
+//            pass", App. A.4);
+//   bwd    : dZ = g W2, dA3 = dZ * silu(A1), dA1 = dZ * A3 * silu'(A1);
+//   agg    : the two scaled aggregations U^T diag(K^W|K^M) X (App. A.4) and
+//            the chunk-end state W_C = cW W_0 + cWM M_0 + A^W,
+//            M_C = cM M_0 + A^M, which becomes the next chunk's start state.
+//
+// Internal layouts (per unit u, chunk-local token row p in [0, Cp), Cp = C
+// rounded up to 128; rows past the chunk's valid tokens are zero inputs with
+// zero kernels, so they add nothing):
+//   kw, km   fp32 [BH][nC][Cp]         coef fp32 [BH][nC][4] (cW, cM, cWM, 0)
+//   kt       T [BH][nC][d][Cp]         K of every chunk, feature-major
+//   w13s     T [BH][2h][krep*d]        bf16/f32 shadow of W1,W3: 32-row blocks
+//                                      interleaved W1,W3,W1,W3,...; with
+//                                      krep = 2 columns [d, 2d) hold the low
+//                                      part W - hi (compensated operands)
+//   w2s      T [BH][d][krep*h]         W2 shadow;  w2ts T [BH][h][krep*d] W2^T
+//   zrow     T [BH][2Cp][h]            Z of K rows then Q rows
+//   a1s, a3s fp32 [BH][Cp][h]          A1, A3 of K rows (backward stash)
+//   grow     T [BH][Cp][d]             g of K rows
+//   ut       T [BH][4h][Cp]            K^W*dA1, K^M*dA1 (32-row interleave),
+//                                      then K^W*dA3, K^M*dA3
+//   gt       T [BH][2d][Cp]            K^W*g, K^M*g (32-row interleave)
+//   zt       T [BH][h][Cp]             Z of K rows, feature-major
+// The 32-row W/M interleave puts the W and M aggregates of one state entry
+// in the same lane of the aggregation kernel's accumulators.
+#pragma once
+#include "common.hpp"
+
+namespace e2ttt {
+
+struct Shape {
+  int64_t BH, L, d, h, C, Cp, nC;
+  int krep;
+};
+
+__device__ __forceinline__ int64_t n_valid(const Shape& s, int r) {
+  const int64_t rem = s.L - static_cast<int64_t>(r) * s.C;
+  return rem < s.C ? rem : s.C;
+}
+
+// ---------------------------------------------------------------------------
+// Scalar kernels (§3.2 K^M = eta*beta~, K^W = eta*beta~*R; App. A.2 log-space
+// suffix products).  One wave per (unit, chunk) segment of n <= C tokens.
+// Lane i owns the contiguous block [i*per, min((i+1)*per, n)).
+//   b_t = prod_{s>t} beta_s,  c_t = prod_{s>t} gamma_s   (exclusive suffix
+//        products, as exp of suffix sums of log|.| with a sign parity)
+//   P_t = c_t + beta_{t+1} P_{t+1},  P_{n-1} = 1   (= beta~_t R_t, bounded)
+//   K^W_t = eta_t P_t,  K^M_t = eta_t b_t,  cW = prod gamma, cM = prod beta,
+//   cWM = beta_0 P_0.
+// All scan arithmetic is fp64.  Output index of token p of chunk r of unit
+// u is u*ustride + r*rstride + p; with pad > n tokens p in [n, pad) are
+// written as 0.  coef of (u, r) starts at (u*nC + r)*cstride.
+
+struct LogSigned {  // log|x| and the sign of x (as a parity bit)
+  double l;
+  int neg;
+};
+
+__device__ __forceinline__ LogSigned log_signed(double x) {
+  LogSigned r;
+  r.neg = x < 0.0;
+  r.l = log(fabs(x));  // -inf for 0
+  return r;
+}
+
+__device__ __forceinline__ double exp_signed(double l, int neg) {
+  const double e = exp(l);
+  return neg ? -e : e;
+}
+
+__global__ __launch_bounds__(64) void k_scan(const float* __restrict__ eta,
+                                              const float* __restrict__ alpha,
+                                              const float* __restrict__ beta, int64_t L,
+                                              int64_t C, int64_t nC, int mode, float* kw,
+                                              float* km, int64_t ustride, int64_t rstride,
+                                              int64_t pad, float* coef, int cstride) {
+  extern __shared__ float sm[];  // 3 * C floats: eta, alpha, beta of the segment
+  const int64_t seg = blockIdx.x;
+  const int64_t u = seg / nC;
+  const int r = static_cast<int>(seg % nC);
+  const int lane = threadIdx.x;
+  const int64_t t0 = static_cast<int64_t>(r) * C;
+  const int64_t n = (L - t0) < C ? (L - t0) : C;
+  const float* e_g = eta + u * L + t0;
+  const float* a_g = alpha + u * L + t0;
+  const float* b_g = beta + u * L + t0;
+  float* se = sm;
+  float* sa = sm + C;
+  float* sb = sm + 2 * C;
+  for (int64_t i = lane; i < n; i += 64) {
+    se[i] = e_g[i];
+    sa[i] = a_g[i];
+    sb[i] = b_g[i];
+  }
+  __syncthreads();
+
+  const int64_t per = (n + 63) / 64;
+  const int64_t s0 = lane * per < n ? lane * per : n;
+  const int64_t s1 = (lane + 1) * per < n ? (lane + 1) * per : n;
+  auto log_gamma = [&](int64_t i) -> LogSigned {
+    if (mode == 1) return log_signed(static_cast<double>(sa[i]));
+    const double ea = static_cast<double>(se[i]) * static_cast<double>(sa[i]);
+    LogSigned r;
+    r.neg = ea > 1.0;
+    r.l = ea <= 1.0 ? log1p(-ea) : log(ea - 1.0);  // log1p keeps 1 - eta*alpha exact-ish
+    return r;
+  };
+
+  // Pass 1: block totals of log|beta|, log|gamma| and sign parities.
+  double lb_blk = 0.0, lg_blk = 0.0;
+  int nb_blk = 0, ng_blk = 0;
+  for (int64_t i = s0; i < s1; ++i) {
+    const LogSigned lb = log_signed(static_cast<double>(sb[i]));
+    const LogSigned lg = log_gamma(i);
+    lb_blk += lb.l; nb_blk ^= lb.neg;
+    lg_blk += lg.l; ng_blk ^= lg.neg;
+  }
+  // Reverse scan over lanes: inclusive (lanes >= i), then shifted by one
+  // lane to the exclusive sums of the later blocks (no subtraction, so -inf
+  // logs of zero factors never produce NaN).
+  double xb = lb_blk, xg = lg_blk;
+  int pb_inc = nb_blk, pg_inc = ng_blk;
+  for (int off = 1; off < 64; off <<= 1) {
+    const double yb = __shfl_down(xb, off, 64);
+    const double yg = __shfl_down(xg, off, 64);
+    const int qb = __shfl_down(pb_inc, off, 64);
+    const int qg = __shfl_down(pg_inc, off, 64);
+    if (lane + off < 64) { xb += yb; xg += yg; pb_inc ^= qb; pg_inc ^= qg; }
+  }
+  const double sh_b = __shfl_down(xb, 1, 64);
+  const double sh_g = __shfl_down(xg, 1, 64);
+  const double lb_after = lane < 63 ? sh_b : 0.0;
+  const double lg_after = lane < 63 ? sh_g : 0.0;
+  const int nb_after = pb_inc ^ nb_blk;
+  const int ng_after = pg_inc ^ ng_blk;
+  const double lb_total = __shfl(xb, 0, 64);
+  const double lg_total = __shfl(xg, 0, 64);
+  const int nb_total = __shfl(pb_inc, 0, 64);
+  const int ng_total = __shfl(pg_inc, 0, 64);
+
+  // Pass 2: this block's affine map P_{s0} = A + B * P_{s1}.
+  double A = 0.0, Bm = 1.0;
+  {
+    double lb = lb_after, lg = lg_after;
+    int pb = nb_after, pg = ng_after;
+    double beta_next = s1 < n ? static_cast<double>(sb[s1]) : 0.0;
+    for (int64_t i = s1 - 1; i >= s0; --i) {
+      const double c = exp_signed(lg, pg);
+      A = c + beta_next * A;
+      Bm = beta_next * Bm;
+      const LogSigned b = log_signed(static_cast<double>(sb[i]));
+      const LogSigned g = log_gamma(i);
+      lb += b.l; pb ^= b.neg;
+      lg += g.l; pg ^= g.neg;
+      beta_next = static_cast<double>(sb[i]);
+    }
+    (void)lb; (void)pb;
+  }
+  // Reverse scan of affine maps: lane i gets the composition of lanes >= i,
+  // (A_i, B_i) o (A_j, B_j) = (A_i + B_i A_j, B_i B_j).  The last non-empty
+  // block has B = 0 (beta past the end is 0), empty blocks are (0, 1).
+  double cA = A, cB = Bm;
+  for (int off = 1; off < 64; off <<= 1) {
+    const double oA = __shfl_down(cA, off, 64);
+    const double oB = __shfl_down(cB, off, 64);
+    if (lane + off < 64) { cA = cA + cB * oA; cB = cB * oB; }
+  }
+  double P_next = __shfl_down(cA, 1, 64);  // P at s1 (first token of next block)
+  if (lane == 63) P_next = 0.0;
+
+  // Pass 3: kernels of every token of the block.
+  {
+    double lb = lb_after, lg = lg_after;
+    int pb = nb_after, pg = ng_after;
+    double beta_next = s1 < n ? static_cast<double>(sb[s1]) : 0.0;
+    double P = P_next;
+    for (int64_t i = s1 - 1; i >= s0; --i) {
+      const double bt = exp_signed(lb, pb);
+      const double ct = exp_signed(lg, pg);
+      P = ct + beta_next * P;
+      const double e = static_cast<double>(se[i]);
+      const LogSigned b = log_signed(static_cast<double>(sb[i]));
+      const LogSigned g = log_gamma(i);  // reads se[i], sa[i]: before they are overwritten
+      se[i] = static_cast<float>(e * P);   // K^W
+      sa[i] = static_cast<float>(e * bt);  // K^M
+      lb += b.l; pb ^= b.neg;
+      lg += g.l; pg ^= g.neg;
+      beta_next = static_cast<double>(sb[i]);
+    }
+    if (lane == 0 && n > 0) {
+      float* cf = coef + (u * nC + r) * cstride;
+      cf[0] = static_cast<float>(exp_signed(lg_total, ng_total));
+      cf[1] = static_cast<float>(exp_signed(lb_total, nb_total));
+      cf[2] = static_cast<float>(static_cast<double>(sb[0]) * P);
+    }
+  }
+  __syncthreads();
+  float* kw_o = kw + u * ustride + r * rstride;
+  float* km_o = km + u * ustride + r * rstride;
+  const int64_t lim = pad > n ? pad : n;
+  for (int64_t i = lane; i < lim; i += 64) {
+    kw_o[i] = i < n ? se[i] : 0.0f;
+    km_o[i] = i < n ? sa[i] : 0.0f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K of every chunk, feature-major: kt[u][r][c][p] = k[u][r*C + p][c] (zero
+// for rows past the chunk's valid tokens).  64x64 tiles through LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void k_prep_kt(Shape s, const T* __restrict__ k, T* kt) {
+  __shared__ T tile[64][64 + 1];
+  const int64_t ptiles = s.Cp / 64, ctiles = s.d / 64;
+  int64_t bid = blockIdx.x;
+  const int64_t ct = bid % ctiles; bid /= ctiles;
+  const int64_t pt = bid % ptiles; bid /= ptiles;
+  const int r = static_cast<int>(bid % s.nC);
+  const int64_t u = bid / s.nC;
+  const int64_t nv = n_valid(s, r);
+  const T* ks = k + (u * s.L + static_cast<int64_t>(r) * s.C) * s.d;
+  for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
+    const int pr = idx / 64, cc = idx % 64;
+    const int64_t p = pt * 64 + pr;
+    tile[pr][cc] = p < nv ? ks[p * s.d + ct * 64 + cc] : from_f32<T>(0.0f);
+  }
+  __syncthreads();
+  T* dst = kt + ((u * s.nC + r) * s.d + ct * 64) * s.Cp + pt * 64;
+  for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
+    const int cr = idx / 64, pc = idx % 64;
+    dst[cr * s.Cp + pc] = tile[pc][cr];
+  }
+}
+
+// Hi/lo split of a state value into the operand type.
+template <typename T>
+__device__ __forceinline__ void split_store(float w, T* hi, T* lo) {
+  const T h = from_f32<T>(w);
+  *hi = h;
+  if (lo) *lo = from_f32<T>(w - to_f32<T>(h));
+}
+
+// Operand shadows of one state entry (unit u, packed offset o).
+template <typename T>
+__device__ __forceinline__ void write_shadow(const Shape& s, int64_t u, int64_t o, float w,
+                                             T* w13s, T* w2s, T* w2ts) {
+  const int64_t d = s.d, h = s.h, kr = s.krep;
+  const int64_t hd = h * d;
+  if (o < 2 * hd) {
+    const int isW3 = o >= hd;
+    const int64_t oo = isW3 ? o - hd : o;
+    const int64_t sr = oo / d, c = oo % d;
+    const int64_t srow = 64 * (sr / 32) + (isW3 ? 32 : 0) + sr % 32;
+    T* base = w13s + (u * 2 * h + srow) * (kr * d);
+    split_store<T>(w, base + c, kr == 2 ? base + d + c : nullptr);
+  } else {
+    const int64_t oo = o - 2 * hd;
+    const int64_t i = oo / h, j = oo % h;
+    T* b2 = w2s + (u * d + i) * (kr * h);
+    split_store<T>(w, b2 + j, kr == 2 ? b2 + h + j : nullptr);
+    T* bt = w2ts + (u * h + j) * (kr * d);
+    split_store<T>(w, bt + i, kr == 2 ? bt + d + i : nullptr);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_prep_shadow(Shape s, const float* __restrict__ W,
+                                                     T* w13s, T* w2s, T* w2ts) {
+  const int64_t P = 3 * s.d * s.h;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= s.BH * P) return;
+  const int64_t u = idx / P, o = idx % P;
+  write_shadow<T>(s, u, o, W[idx], w13s, w2s, w2ts);
+}
+
+// ---------------------------------------------------------------------------
+// fwd13: [K;Q] rows x shadow W13 -> A1, A3 -> Z.
+template <typename T>
+__global__ __launch_bounds__(256) void k_fwd13(Shape s, int r, const T* __restrict__ q,
+                                               const T* __restrict__ k, const T* __restrict__ w13s,
+                                               T* zrow, float* a1s, float* a3s, T* zt) {
+  __shared__ __attribute__((aligned(16))) T lds[Tile<T>::LDS_BYTES / sizeof(T)];
+  const int64_t ntn = 2 * s.h / 128, ntm = 2 * s.Cp / 128, mtK = s.Cp / 128;
+  int64_t bid = blockIdx.x;
+  const int64_t nt = bid % ntn; bid /= ntn;
+  const int64_t mt = bid % ntm;
+  const int64_t u = bid / ntm;
+  const bool isQ = mt >= mtK;
+  const int64_t p0 = (mt - (isQ ? mtK : 0)) * 128;
+  const int64_t tok0 = static_cast<int64_t>(r) * s.C;
+  const int64_t nv = n_valid(s, r);
+  const T* X = (isQ ? q : k) + (u * s.L + tok0) * s.d;
+  RowLoader<T> la, lb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t p = p0 + loader_row(i);
+    la.rowp[i] = p < nv ? X + p * s.d : nullptr;
+    lb.rowp[i] = w13s + (u * 2 * s.h + nt * 128 + loader_row(i)) * (s.krep * s.d);
+  }
+  f32x16_t acc[2][2];
+  gemm_tile<T>(acc, la, lb, s.krep * s.d, s.d, lds);
+
+  const AccPos ps;
+  const int64_t j = nt * 64 + ps.wn * 32 + ps.r32;  // hidden unit of this lane
+  float zv[2][2][16];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t p = p0 + ps.row(mi, v);
+      const float a1 = acc[mi][0][v], a3 = acc[mi][1][v];
+      const float z = a1 * sigmoidf_(a1) * a3;
+      zv[mi][0][v] = z;
+      zrow[(u * 2 * s.Cp + (isQ ? s.Cp : 0) + p) * s.h + j] = from_f32<T>(z);
+      if (!isQ) {
+        a1s[(u * s.Cp + p) * s.h + j] = a1;
+        a3s[(u * s.Cp + p) * s.h + j] = a3;
+      }
+    }
+  if (!isQ) {
+    // Z^T tile (64 hidden rows x 128 tokens) through LDS.
+    constexpr int VE = Tile<T>::VE, W = 128 + VE;
+    __syncthreads();
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        lds[(ps.wn * 32 + ps.r32) * W + ps.row(mi, v)] = from_f32<T>(zv[mi][0][v]);
+    __syncthreads();
+    T* dst = zt + (u * s.h + nt * 64) * s.Cp + p0;
+    constexpr int VPR = 128 / VE;
+    for (int idx = threadIdx.x; idx < 64 * VPR; idx += 256) {
+      const int rr = idx / VPR, c = idx % VPR;
+      *reinterpret_cast<uint4*>(dst + rr * s.Cp + c * VE) =
+          *reinterpret_cast<const uint4*>(lds + rr * W + c * VE);
+    }
+  }
+}
+
+// Transposed store of a 128x128 accumulator-layout tile whose column c goes
+// to destination row dst_row(c) (row-contiguous along the tile's rows).
+template <typename T, typename RowFn>
+__device__ __forceinline__ void store_T(const float (&val)[2][2][16], T* lds, RowFn dst_row) {
+  constexpr int VE = Tile<T>::VE, W = 128 + VE, VPR = 128 / VE;
+  const AccPos ps;
+  __syncthreads();
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        lds[ps.col(ni) * W + ps.row(mi, v)] = from_f32<T>(val[mi][ni][v]);
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 128 * VPR; idx += 256) {
+    const int rr = idx / VPR, c = idx % VPR;
+    *reinterpret_cast<uint4*>(dst_row(rr) + c * VE) =
+        *reinterpret_cast<const uint4*>(lds + rr * W + c * VE);
+  }
+}
+
+// fwd2: Z x W2^T -> Y; readout for Q rows, g = v - Y for K rows.
+template <typename T>
+__global__ __launch_bounds__(256) void k_fwd2(Shape s, int r, const T* __restrict__ v,
+                                              T* out, const T* __restrict__ zrow,
+                                              const T* __restrict__ w2s,
+                                              const float* __restrict__ kw,
+                                              const float* __restrict__ km, T* grow, T* gt) {
+  __shared__ __attribute__((aligned(16))) T lds[Tile<T>::LDS_BYTES / sizeof(T)];
+  const int64_t ntn = s.d / 128, ntm = 2 * s.Cp / 128, mtK = s.Cp / 128;
+  int64_t bid = blockIdx.x;
+  const int64_t nt = bid % ntn; bid /= ntn;
+  const int64_t mt = bid % ntm;
+  const int64_t u = bid / ntm;
+  const bool isQ = mt >= mtK;
+  const int64_t p0 = (mt - (isQ ? mtK : 0)) * 128;
+  const int64_t tok0 = static_cast<int64_t>(r) * s.C;
+  const int64_t nv = n_valid(s, r);
+  RowLoader<T> la, lb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    la.rowp[i] = zrow + (u * 2 * s.Cp + mt * 128 + loader_row(i)) * s.h;
+    lb.rowp[i] = w2s + (u * s.d + nt * 128 + loader_row(i)) * (s.krep * s.h);
+  }
+  f32x16_t acc[2][2];
+  gemm_tile<T>(acc, la, lb, s.krep * s.h, s.h, lds);
+
+  const AccPos ps;
+  if (isQ) {
+    T* o = out + (u * s.L + tok0) * s.d;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) {
+          const int64_t p = p0 + ps.row(mi, vv);
+          if (p < nv) o[p * s.d + nt * 128 + ps.col(ni)] = from_f32<T>(acc[mi][ni][vv]);
+        }
+    return;
+  }
+  const T* vs = v + (u * s.L + tok0) * s.d;
+  const float* kwr = kw + (u * s.nC + r) * s.Cp;
+  const float* kmr = km + (u * s.nC + r) * s.Cp;
+  float gW[2][2][16], gM[2][2][16];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int vv = 0; vv < 16; ++vv) {
+        const int64_t p = p0 + ps.row(mi, vv);
+        const int64_t i = nt * 128 + ps.col(ni);
+        const float vin = p < nv ? to_f32<T>(vs[p * s.d + i]) : 0.0f;
+        const float g = vin - acc[mi][ni][vv];
+        grow[(u * s.Cp + p) * s.d + i] = from_f32<T>(g);
+        gW[mi][ni][vv] = kwr[p] * g;
+        gM[mi][ni][vv] = kmr[p] * g;
+      }
+  // gt row of d-index i: 64*(i/32) + i%32 (+32 for the momentum copy)
+  T* gbase = gt + u * 2 * s.d * s.Cp + p0;
+  store_T<T>(gW, lds, [&](int c) {
+    const int64_t i = nt * 128 + c;
+    return gbase + (64 * (i / 32) + i % 32) * s.Cp;
+  });
+  store_T<T>(gM, lds, [&](int c) {
+    const int64_t i = nt * 128 + c;
+    return gbase + (64 * (i / 32) + 32 + i % 32) * s.Cp;
+  });
+}
+
+// bwd: g x W2 -> dZ -> dA1, dA3, scaled by both kernels, feature-major.
+template <typename T>
+__global__ __launch_bounds__(256) void k_bwd(Shape s, int r, const T* __restrict__ grow,
+                                             const T* __restrict__ w2ts,
+                                             const float* __restrict__ a1s,
+                                             const float* __restrict__ a3s,
+                                             const float* __restrict__ kw,
+                                             const float* __restrict__ km, T* ut) {
+  __shared__ __attribute__((aligned(16))) T lds[Tile<T>::LDS_BYTES / sizeof(T)];
+  const int64_t ntn = s.h / 128, ntm = s.Cp / 128;
+  int64_t bid = blockIdx.x;
+  const int64_t nt = bid % ntn; bid /= ntn;
+  const int64_t mt = bid % ntm;
+  const int64_t u = bid / ntm;
+  const int64_t p0 = mt * 128;
+  RowLoader<T> la, lb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    la.rowp[i] = grow + (u * s.Cp + p0 + loader_row(i)) * s.d;
+    lb.rowp[i] = w2ts + (u * s.h + nt * 128 + loader_row(i)) * (s.krep * s.d);
+  }
+  f32x16_t acc[2][2];
+  gemm_tile<T>(acc, la, lb, s.krep * s.d, s.d, lds);
+
+  const AccPos ps;
+  const float* kwr = kw + (u * s.nC + r) * s.Cp;
+  const float* kmr = km + (u * s.nC + r) * s.Cp;
+  float d1[2][2][16], d3[2][2][16];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int vv = 0; vv < 16; ++vv) {
+        const int64_t p = p0 + ps.row(mi, vv);
+        const int64_t j = nt * 128 + ps.col(ni);
+        const float a1 = a1s[(u * s.Cp + p) * s.h + j];
+        const float a3 = a3s[(u * s.Cp + p) * s.h + j];
+        const float sg = sigmoidf_(a1);
+        const float dz = acc[mi][ni][vv];
+        d3[mi][ni][vv] = dz * (a1 * sg);
+        d1[mi][ni][vv] = dz * a3 * (sg * (1.0f + a1 * (1.0f - sg)));
+      }
+  T* ubase = ut + u * 4 * s.h * s.Cp + p0;
+  float sc[2][2][16];
+  for (int which = 0; which < 4; ++which) {
+    const bool isM = which & 1;
+    const bool isA3 = which >= 2;
+    const float* kr = isM ? kmr : kwr;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv)
+          sc[mi][ni][vv] = kr[p0 + ps.row(mi, vv)] * (isA3 ? d3[mi][ni][vv] : d1[mi][ni][vv]);
+    store_T<T>(sc, lds, [&](int c) {
+      const int64_t j = nt * 128 + c;
+      return ubase + ((isA3 ? 2 * s.h : 0) + 64 * (j / 32) + (isM ? 32 : 0) + j % 32) * s.Cp;
+    });
+  }
+}
+
+// agg: both scaled aggregations over the chunk's tokens + chunk-end state.
+template <typename T>
+__global__ __launch_bounds__(256) void k_agg(Shape s, int r, int last, const T* __restrict__ ut,
+                                             const T* __restrict__ kt, const T* __restrict__ gt,
+                                             const T* __restrict__ zt,
+                                             const float* __restrict__ coef, const float* Win,
+                                             const float* Min, float* Wout, float* Mout, T* w13s,
+                                             T* w2s, T* w2ts) {
+  __shared__ __attribute__((aligned(16))) T lds[Tile<T>::LDS_BYTES / sizeof(T)];
+  const int64_t d = s.d, h = s.h;
+  const int64_t na = (4 * h / 128) * (d / 128), nb = (2 * d / 128) * (h / 128);
+  const int64_t u = blockIdx.x / (na + nb);
+  const int64_t t = blockIdx.x % (na + nb);
+  const bool famA = t < na;
+  int64_t mt, nt;
+  RowLoader<T> la, lb;
+  if (famA) {
+    mt = t / (d / 128); nt = t % (d / 128);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      la.rowp[i] = ut + (u * 4 * h + mt * 128 + loader_row(i)) * s.Cp;
+      lb.rowp[i] = kt + ((u * s.nC + r) * d + nt * 128 + loader_row(i)) * s.Cp;
+    }
+  } else {
+    const int64_t tb = t - na;
+    mt = tb / (h / 128); nt = tb % (h / 128);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      la.rowp[i] = gt + (u * 2 * d + mt * 128 + loader_row(i)) * s.Cp;
+      lb.rowp[i] = zt + (u * h + nt * 128 + loader_row(i)) * s.Cp;
+    }
+  }
+  f32x16_t acc[2][2];
+  gemm_tile<T>(acc, la, lb, s.Cp, s.Cp, lds);
+
+  const float* cf = coef + (u * s.nC + r) * 4;
+  const float cW = cf[0], cM = cf[1], cWM = cf[2];
+  const int64_t P = 3 * d * h;
+  const float* wi = Win + u * P;
+  const float* mi_ = Min + u * P;
+  float* wo = Wout + u * P;
+  float* mo = Mout + u * P;
+  const AccPos ps;
+  const int64_t blk64 = mt * 2 + ps.wm;  // 64-row block: rows 0-31 W part, 32-63 M part
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+    for (int vv = 0; vv < 16; ++vv) {
+      const int64_t idx32 = 8 * (vv >> 2) + 4 * ps.hf + (vv & 3);
+      int64_t off;
+      if (famA) {
+        const int64_t c = nt * 128 + ps.col(ni);
+        if (blk64 < h / 32) off = (blk64 * 32 + idx32) * d + c;
+        else off = h * d + ((blk64 - h / 32) * 32 + idx32) * d + c;
+      } else {
+        const int64_t i = blk64 * 32 + idx32;
+        const int64_t j = nt * 128 + ps.col(ni);
+        off = 2 * h * d + i * h + j;
+      }
+      const float w0 = wi[off], m0 = mi_[off];
+      const float wn = cW * w0 + cWM * m0 + acc[0][ni][vv];
+      const float mn = cM * m0 + acc[1][ni][vv];
+      wo[off] = wn;
+      mo[off] = mn;
+      if (!last) write_shadow<T>(s, u, off, wn, w13s, w2s, w2ts);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Linear learner f_W(x) = W x (fp32 arithmetic; io fp32 or bf16).
+// fwd: Y = X W^T for X = [K; Q] rows of chunk r; readout or scaled residuals
+// gw = K^W g, gm = K^M g with g = v - W k (fp32, [BH][Cp][d]).
+template <typename IO>
+__global__ __launch_bounds__(256) void k_lin_fwd(Shape s, int r, const IO* __restrict__ q,
+                                                 const IO* __restrict__ k,
+                                                 const IO* __restrict__ v,
+                                                 const float* __restrict__ Wst,
+                                                 const float* __restrict__ kw,
+                                                 const float* __restrict__ km, IO* out,
+                                                 float* gw, float* gm) {
+  extern __shared__ float lsm[];
+  const int64_t d = s.d;
+  float* Ws = lsm;                 // [d][d+1]
+  float* Xs = lsm + d * (d + 1);   // [64][d+1]
+  const int64_t ntm = 2 * s.Cp / 64, mtK = s.Cp / 64;
+  const int64_t mt = blockIdx.x % ntm, u = blockIdx.x / ntm;
+  const bool isQ = mt >= mtK;
+  const int64_t p0 = (mt - (isQ ? mtK : 0)) * 64;
+  const int64_t tok0 = static_cast<int64_t>(r) * s.C;
+  const int64_t nv = n_valid(s, r);
+  const IO* X = (isQ ? q : k) + (u * s.L + tok0) * d;
+  for (int64_t idx = threadIdx.x; idx < d * d; idx += 256)
+    Ws[(idx / d) * (d + 1) + idx % d] = Wst[u * d * d + idx];
+  for (int64_t idx = threadIdx.x; idx < 64 * d; idx += 256) {
+    const int64_t pr = idx / d, c = idx % d, p = p0 + pr;
+    Xs[pr * (d + 1) + c] = p < nv ? to_f32<IO>(X[p * d + c]) : 0.0f;
+  }
+  __syncthreads();
+  const float* kwr = kw + (u * s.nC + r) * s.Cp;
+  const float* kmr = km + (u * s.nC + r) * s.Cp;
+  for (int64_t idx = threadIdx.x; idx < 64 * d; idx += 256) {
+    const int64_t pr = idx / d, c = idx % d, p = p0 + pr;
+    float y = 0.0f;
+    for (int64_t kk = 0; kk < d; ++kk) y += Xs[pr * (d + 1) + kk] * Ws[c * (d + 1) + kk];
+    if (isQ) {
+      if (p < nv) out[(u * s.L + tok0 + p) * d + c] = from_f32<IO>(y);
+    } else {
+      const float vin = p < nv ? to_f32<IO>(v[(u * s.L + tok0 + p) * d + c]) : 0.0f;
+      const float g = vin - y;
+      gw[(u * s.Cp + p) * d + c] = kwr[p] * g;
+      gm[(u * s.Cp + p) * d + c] = kmr[p] * g;
+    }
+  }
+}
+
+// agg: A^W = gw^T K, A^M = gm^T K over the chunk; chunk-end state.
+template <typename IO>
+__global__ __launch_bounds__(256) void k_lin_agg(Shape s, int r, const IO* __restrict__ k,
+                                                 const float* __restrict__ gw,
+                                                 const float* __restrict__ gm,
+                                                 const float* __restrict__ coef,
+                                                 const float* Win, const float* Min, float* Wout,
+                                                 float* Mout) {
+  extern __shared__ float lsm[];
+  const int64_t d = s.d;
+  float* sw = lsm;              // [64][16]
+  float* smm = lsm + 64 * 16;   // [64][16]
+  float* sk = lsm + 2 * 64 * 16;  // [64][d]
+  const int64_t nrb = d / 16;
+  const int64_t rb = blockIdx.x % nrb, u = blockIdx.x / nrb;
+  const int64_t tok0 = static_cast<int64_t>(r) * s.C;
+  const int64_t nv = n_valid(s, r);
+  const int nper = static_cast<int>(d / 16);  // entries per thread (16*d / 256)
+  float aw[8], am[8];
+  for (int e = 0; e < 8; ++e) { aw[e] = 0.0f; am[e] = 0.0f; }
+  for (int64_t pb = 0; pb < s.Cp; pb += 64) {
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 64 * 16; idx += 256) {
+      const int64_t pr = idx / 16, i = idx % 16;
+      sw[idx] = gw[(u * s.Cp + pb + pr) * d + rb * 16 + i];
+      smm[idx] = gm[(u * s.Cp + pb + pr) * d + rb * 16 + i];
+    }
+    for (int64_t idx = threadIdx.x; idx < 64 * d; idx += 256) {
+      const int64_t pr = idx / d, c = idx % d, p = pb + pr;
+      sk[idx] = p < nv ? to_f32<IO>(k[(u * s.L + tok0 + p) * d + c]) : 0.0f;
+    }
+    __syncthreads();
+    for (int e = 0; e < nper; ++e) {
+      const int64_t ent = threadIdx.x + 256 * e;
+      const int64_t i = ent / d, j = ent % d;
+      float sW = 0.0f, sM = 0.0f;
+      for (int pr = 0; pr < 64; ++pr) {
+        const float kv = sk[pr * d + j];
+        sW += sw[pr * 16 + i] * kv;
+        sM += smm[pr * 16 + i] * kv;
+      }
+      aw[e] += sW;
+      am[e] += sM;
+    }
+  }
+  const float* cf = coef + (u * s.nC + r) * 4;
+  const float cW = cf[0], cM = cf[1], cWM = cf[2];
+  for (int e = 0; e < nper; ++e) {
+    const int64_t ent = threadIdx.x + 256 * e;
+    const int64_t off = u * d * d + (rb * 16 + ent / d) * d + ent % d;
+    const float w0 = Win[off], m0 = Min[off];
+    Wout[off] = cW * w0 + cWM * m0 + aw[e];
+    Mout[off] = cM * m0 + am[e];
+  }
+}
+
+__global__ __launch_bounds__(256) void k_copy2(const float* __restrict__ a,
+                                               const float* __restrict__ b, float* ao, float* bo,
+                                               int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) {
+    ao[i] = a[i];
+    bo[i] = b[i];
+  }
+}
+
+}  // namespace e2ttt

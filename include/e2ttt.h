@@ -1,0 +1,187 @@
+/*
+ * e2ttt.h -- C ABI of the E2-TTT chunk-parallel fast-weight update (gfx950).
+ *
+ * The operation is the chunk forward of "Rethinking Expressivity and
+ * Efficiency in Test-Time Training" (E2-TTT):
+ *   - per chunk of C tokens, every token's descent direction
+ *     G_t = -grad_W 0.5*||f_W(k_t) - v_t||^2 is evaluated at the chunk-start
+ *     fast weights W_0 (§1, §3; App. A.5);
+ *   - the chunk-end pair (W_C, M_C) equals that of the token-wise recurrence
+ *     M_t = beta_t M_{t-1} + eta_t G_t,  W_t = gamma_t W_{t-1} + M_t
+ *     (Eq. 7 as read from §3.2 and App. A.5), reached through the two scalar
+ *     kernels K^M_t = eta_t*beta~_t and K^W_t = eta_t*beta~_t*R_t of §3.2:
+ *         M_C = cM*M_0 + sum_t K^M_t G_t
+ *         W_C = cW*W_0 + cWM*M_0 + sum_t K^W_t G_t
+ *     with beta~_t, gamma~_t suffix products taken in log space (App. A.2);
+ *   - gamma_t = 1 - eta_t*alpha_t (Eq. 14, App. A.3), or gamma_t = alpha_t
+ *     with E2TTT_ALPHA_IS_GAMMA;
+ *   - the readout is o_t = f_{W_0}(q_t) with the chunk-start weights (Eq. 6);
+ *   - (W_C, M_C) of one chunk is (W_0, M_0) of the next (§3.2, induction).
+ *
+ * Fast-weight learners (§2, §5.2, App. B.5):
+ *   E2TTT_LINEAR : f_W(x) = W x, W is d x d row-major.
+ *   E2TTT_SWIGLU : f(x) = W2 (silu(W1 x) * (W3 x)); the state of one
+ *                  (batch, head) is packed [W1 (h x d) | W3 (h x d) | W2 (d x h)],
+ *                  each row-major, P = 3*d*h floats.
+ *
+ * Layouts (all contiguous, row-major):
+ *   q, k, v, out          [B, H, L, d]   io_dtype (fp32 or bf16)
+ *   eta, alpha, beta      [B, H, L]      fp32
+ *   W0, M0, W_end, M_end  [B, H, P]      fp32   (P = d*d or 3*d*h)
+ * Chunks are consecutive runs of C tokens from the start of the sequence; if
+ * C does not divide L the last chunk is shorter (same recurrence, fewer
+ * tokens).  L == 0 copies (W0, M0) to (W_end, M_end).
+ *
+ * Ownership and concurrency: every tensor pointer is a DEVICE pointer owned
+ * by the caller; the library allocates nothing and keeps no state between
+ * calls.  Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ * stream) and the call returns without synchronising.  Inputs are read only.
+ * W_end may be exactly W0 and M_end exactly M0 (in-place state advance);
+ * any other overlap between outputs, inputs or the workspace is EINVAL.
+ *
+ * Errors: every check runs on the host before anything is enqueued; on error
+ * nothing is launched and nothing is written.  NaN/Inf in the inputs are
+ * propagated, not detected.  No C++ exception crosses this interface.
+ */
+#ifndef E2TTT_H_
+#define E2TTT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define E2TTT_API __attribute__((visibility("default")))
+#else
+#define E2TTT_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  E2TTT_OK = 0,
+  E2TTT_EINVAL = 1,       /* bad pointer, size, alignment, overlap or flags */
+  E2TTT_EWORKSPACE = 2,   /* workspace smaller than e2ttt_workspace_bytes() */
+  E2TTT_EUNSUPPORTED = 3, /* shape/dtype outside the compiled kernels */
+  E2TTT_EHIP = 4          /* a HIP runtime call or kernel launch failed */
+} e2ttt_status;
+
+typedef enum { E2TTT_LINEAR = 0, E2TTT_SWIGLU = 1 } e2ttt_fast_weight;
+typedef enum { E2TTT_F32 = 0, E2TTT_BF16 = 1 } e2ttt_dtype;
+typedef enum {
+  E2TTT_GAMMA_1_MINUS_ETA_ALPHA = 0, /* gamma = 1 - eta*alpha (Eq. 14) */
+  E2TTT_ALPHA_IS_GAMMA = 1           /* gamma = alpha                  */
+} e2ttt_decay_mode;
+
+/* Bits of e2ttt_problem.flags. */
+enum {
+  /* SwiGLU with bf16 io: feed the fast weights to the matrix cores as a
+   * bf16 hi/lo pair (W = hi + lo, both operands multiplied against the same
+   * activations) in the forward and backward products.  The weight operand
+   * then carries ~16 mantissa bits instead of 8, at about 1.5x the
+   * matrix-core work of the whole call.  Ignored for fp32 io and LINEAR. */
+  E2TTT_FLAG_COMPENSATED_WEIGHTS = 1u
+};
+
+/* Problem description.  struct_size must equal sizeof(e2ttt_problem). */
+typedef struct {
+  uint32_t struct_size;
+  int32_t kind;       /* e2ttt_fast_weight */
+  int64_t batch;      /* B >= 1 */
+  int64_t heads;      /* H >= 1 */
+  int64_t seq_len;    /* L >= 0 */
+  int64_t dim;        /* d >= 1 */
+  int64_t hidden;     /* h (SwiGLU); must be 0 for LINEAR */
+  int64_t chunk;      /* C >= 1 */
+  int32_t io_dtype;   /* e2ttt_dtype of q, k, v, out; states are fp32 */
+  int32_t decay_mode; /* e2ttt_decay_mode */
+  uint32_t flags;     /* E2TTT_FLAG_* bits; others must be 0 */
+  uint32_t reserved;  /* must be 0 */
+} e2ttt_problem;
+
+/* Host-only argument check (no HIP call).  Returns E2TTT_OK if the problem is
+ * well formed and supported:
+ *   LINEAR : 16 <= d <= 128, d % 16 == 0, io fp32 or bf16.
+ *   SWIGLU : d % 128 == 0, h % 128 == 0, d <= 1024, h <= 4096, io fp32 or bf16.
+ *   Both   : 1 <= C <= 12288.
+ * EINVAL for malformed values, EUNSUPPORTED for well-formed but uncompiled. */
+E2TTT_API e2ttt_status e2ttt_validate(const e2ttt_problem* prob);
+
+/* Host-only: bytes of device workspace e2ttt_chunk_forward needs for `prob`
+ * (written to *bytes).  The workspace must be 256-byte aligned. */
+E2TTT_API e2ttt_status e2ttt_workspace_bytes(const e2ttt_problem* prob, size_t* bytes);
+
+/* The chunk forward over the whole sequence (all B*H units, all chunks).
+ * Inputs: q, k, v [B,H,L,d] io_dtype; eta, alpha, beta [B,H,L] fp32;
+ * W0, M0 [B,H,P] fp32.  Outputs: out [B,H,L,d] io_dtype, W_end, M_end
+ * [B,H,P] fp32 (the state after the last chunk).  workspace: device memory
+ * of at least e2ttt_workspace_bytes() bytes, 256-byte aligned, not
+ * overlapping anything else; its contents are scratch.  All tensor pointers
+ * must be 16-byte aligned.  Enqueued on `stream`; returns E2TTT_EHIP if a
+ * launch fails (asynchronous faults surface at the caller's next sync). */
+E2TTT_API e2ttt_status e2ttt_chunk_forward(const e2ttt_problem* prob, const void* q,
+                                 const void* k, const void* v,
+                                 const float* eta, const float* alpha,
+                                 const float* beta, const float* W0,
+                                 const float* M0, void* out, float* W_end,
+                                 float* M_end, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* The per-token scalar kernels alone (§3.2, App. A.2-A.3), for every chunk:
+ *   k_w[b,h,t] = K^W_t = eta_t * beta~_t * R_t  (weight kernel)
+ *   k_m[b,h,t] = K^M_t = eta_t * beta~_t        (momentum kernel)
+ *   chunk_coef[b,h,r,0..2] = (cW, cM, cWM): the factors of W_0 in W_C, of
+ *   M_0 in M_C and of M_0 in W_C for chunk r.
+ * beta~_t is the product of beta_s over the later tokens s > t of the chunk;
+ * R_t sums the ratios gamma~_i / beta~_i over i >= t.  The ratio sum is never
+ * formed: beta~_t R_t is evaluated as the bounded recursion
+ * P_t = gamma~_t + beta_{t+1} P_{t+1}, P_last = 1, in fp64.
+ * Shapes: eta, alpha, beta, k_w, k_m [B,H,L] fp32; chunk_coef [B,H,nC,3]
+ * fp32 with nC = ceil(L/C).  Only batch, heads, seq_len, chunk and
+ * decay_mode of `prob` are used (kind/dim/hidden/io_dtype are still
+ * validated).  Pointers 16-byte aligned except chunk_coef (4-byte). */
+E2TTT_API e2ttt_status e2ttt_scalar_kernels(const e2ttt_problem* prob, const float* eta,
+                                  const float* alpha, const float* beta,
+                                  float* k_w, float* k_m, float* chunk_coef,
+                                  void* stream);
+
+/* Kernel classes of the chunk forward, for e2ttt_chunk_forward_timed. */
+typedef enum {
+  E2TTT_KERNEL_SCAN = 0,       /* scalar kernels, all chunks (one launch)    */
+  E2TTT_KERNEL_PREP = 1,       /* K^T staging and W0 operand shadow          */
+  E2TTT_KERNEL_FWD13 = 2,      /* [K;Q] x [W1;W3]^T -> Z (per chunk)          */
+  E2TTT_KERNEL_FWD2 = 3,       /* Z x W2^T -> readout, g (per chunk)         */
+  E2TTT_KERNEL_BWD = 4,        /* g x W2 -> dA1, dA3 (per chunk)             */
+  E2TTT_KERNEL_AGG = 5,        /* scaled aggregations + state (per chunk)    */
+  E2TTT_KERNEL_LINEAR_FWD = 6, /* linear learner: readout and residuals      */
+  E2TTT_KERNEL_LINEAR_AGG = 7, /* linear learner: aggregations + state       */
+  E2TTT_KERNEL_NUM_CLASSES = 8
+} e2ttt_kernel_class;
+
+/* Benchmark instrumentation: enqueue exactly the work of e2ttt_chunk_forward
+ * (same arguments, same results) and additionally record caller-created HIP
+ * events (hipEvent_t, passed as void*) around every launch of one kernel
+ * class: events[2j] just before and events[2j+1] just after the j-th launch
+ * of that class, for j < n_events/2.  *n_recorded (may be NULL) receives the
+ * number of launches bracketed.  The caller reads the elapsed times after
+ * synchronising.  Same error behaviour as e2ttt_chunk_forward; EINVAL for a
+ * bad kernel_class or n_events < 0. */
+E2TTT_API e2ttt_status e2ttt_chunk_forward_timed(const e2ttt_problem* prob, const void* q,
+                                       const void* k, const void* v,
+                                       const float* eta, const float* alpha,
+                                       const float* beta, const float* W0,
+                                       const float* M0, void* out, float* W_end,
+                                       float* M_end, void* workspace,
+                                       size_t workspace_bytes, void* stream,
+                                       int kernel_class, void* const* events,
+                                       int n_events, int* n_recorded);
+
+/* Static, human-readable name of a status code. */
+E2TTT_API const char* e2ttt_status_string(e2ttt_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* E2TTT_H_ */

@@ -1,0 +1,197 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/e2ttt.h, and rejects bad arguments on the host before
+anything is enqueued (fake device pointers are never dereferenced there)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import chunk_weight_update_amd as cwu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "e2ttt.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(e2ttt_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_entry_point():
+    names = declared_functions()
+    assert set(names) == set(cwu.EXPORTED)
+    L = cwu.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", cwu.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (e2ttt_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_problem_struct_layout_matches_header():
+    # uint32, int32, 6 x int64, int32, int32, uint32, uint32
+    assert ctypes.sizeof(cwu.Problem) == 4 + 4 + 6 * 8 + 4 * 4
+
+
+def swiglu(**kw):
+    a = dict(kind=cwu.SWIGLU, batch=2, heads=4, seq_len=4096, dim=128, hidden=256, chunk=512,
+             io_dtype=cwu.BF16)
+    a.update(kw)
+    return cwu.make_problem(**a)
+
+
+def linear(**kw):
+    a = dict(kind=cwu.LINEAR, batch=1, heads=1, seq_len=256, dim=64, hidden=0, chunk=64,
+             io_dtype=cwu.F32)
+    a.update(kw)
+    return cwu.make_problem(**a)
+
+
+def test_status_strings():
+    for s in range(5):
+        assert cwu.status_string(s).startswith("E2TTT")
+    assert "unknown" in cwu.status_string(99)
+
+
+@pytest.mark.parametrize("prob,expected", [
+    (swiglu(), cwu.OK),
+    (linear(), cwu.OK),
+    (swiglu(dim=768, hidden=1536, chunk=8192, seq_len=57344, batch=1, heads=1), cwu.OK),
+    (swiglu(io_dtype=cwu.F32), cwu.OK),
+    (swiglu(flags=cwu.FLAG_COMPENSATED_WEIGHTS), cwu.OK),
+    (swiglu(seq_len=0), cwu.OK),
+    (swiglu(seq_len=1000), cwu.OK),  # short last chunk
+    (swiglu(chunk=100), cwu.OK),  # chunk not a multiple of the tile
+    (swiglu(batch=0), cwu.EINVAL),
+    (swiglu(heads=-1), cwu.EINVAL),
+    (swiglu(seq_len=-5), cwu.EINVAL),
+    (swiglu(chunk=0), cwu.EINVAL),
+    (swiglu(hidden=0), cwu.EINVAL),
+    (swiglu(kind=7), cwu.EINVAL),
+    (swiglu(io_dtype=5), cwu.EINVAL),
+    (swiglu(decay_mode=3), cwu.EINVAL),
+    (swiglu(flags=2), cwu.EINVAL),
+    (linear(hidden=3), cwu.EINVAL),
+    (swiglu(dim=96), cwu.EUNSUPPORTED),
+    (swiglu(hidden=200), cwu.EUNSUPPORTED),
+    (swiglu(dim=2048), cwu.EUNSUPPORTED),
+    (linear(dim=72), cwu.EUNSUPPORTED),
+    (linear(dim=256), cwu.EUNSUPPORTED),
+    (swiglu(chunk=20000), cwu.EUNSUPPORTED),
+    (swiglu(batch=1 << 40, heads=1 << 20), cwu.EUNSUPPORTED),
+])
+def test_validate(prob, expected):
+    assert cwu.validate(prob) == expected
+
+
+def test_struct_size_and_reserved_checked():
+    p = swiglu()
+    p.struct_size = 12
+    assert cwu.validate(p) == cwu.EINVAL
+    p = swiglu()
+    p.reserved = 1
+    assert cwu.validate(p) == cwu.EINVAL
+    assert cwu.lib().e2ttt_validate(None) == cwu.EINVAL
+
+
+def test_workspace_bytes():
+    n = cwu.workspace_bytes(swiglu())
+    assert n > 0 and n % 256 == 0
+    assert cwu.workspace_bytes(swiglu(flags=cwu.FLAG_COMPENSATED_WEIGHTS)) > n
+    assert cwu.workspace_bytes(swiglu(io_dtype=cwu.F32)) > n
+    assert cwu.workspace_bytes(swiglu(seq_len=0)) == 0
+    with pytest.raises(cwu.E2tttError):
+        cwu.workspace_bytes(swiglu(dim=96))
+    assert cwu.lib().e2ttt_workspace_bytes(ctypes.byref(swiglu()), None) == cwu.EINVAL
+
+
+class Fake:
+    """Non-overlapping, 256-aligned fake device addresses."""
+
+    def __init__(self):
+        self.next = 1 << 40
+
+    def __call__(self, nbytes):
+        a = self.next
+        self.next += (int(nbytes) + (1 << 20)) & ~255
+        return a
+
+
+def fake_args(prob):
+    f = Fake()
+    B, H, L, d = prob.batch, prob.heads, prob.seq_len, prob.dim
+    P = d * d if prob.kind == cwu.LINEAR else 3 * d * prob.hidden
+    io = 2 if prob.io_dtype == cwu.BF16 else 4
+    a = dict(q=f(B * H * L * d * io), k=f(B * H * L * d * io), v=f(B * H * L * d * io),
+             eta=f(B * H * L * 4), alpha=f(B * H * L * 4), beta=f(B * H * L * 4),
+             W0=f(B * H * P * 4), M0=f(B * H * P * 4), out=f(B * H * L * d * io),
+             W_end=f(B * H * P * 4), M_end=f(B * H * P * 4))
+    nws = cwu.workspace_bytes(prob)
+    a["workspace"] = f(nws)
+    a["nws"] = nws
+    return a
+
+
+def call(prob, a):
+    return cwu.chunk_forward(prob, a["q"], a["k"], a["v"], a["eta"], a["alpha"], a["beta"],
+                             a["W0"], a["M0"], a["out"], a["W_end"], a["M_end"],
+                             a["workspace"], a["nws"], stream=0, check=False)
+
+
+@pytest.mark.parametrize("mutate,expected", [
+    (lambda a: a.update(q=None), cwu.EINVAL),
+    (lambda a: a.update(W_end=None), cwu.EINVAL),
+    (lambda a: a.update(workspace=None), cwu.EINVAL),
+    (lambda a: a.update(k=a["k"] + 4), cwu.EINVAL),            # misaligned
+    (lambda a: a.update(workspace=a["workspace"] + 16), cwu.EINVAL),  # not 256-aligned
+    (lambda a: a.update(nws=a["nws"] - 256), cwu.EWORKSPACE),
+    (lambda a: a.update(out=a["q"]), cwu.EINVAL),               # out aliases q
+    (lambda a: a.update(W_end=a["W0"] + 256), cwu.EINVAL),      # partial overlap
+    (lambda a: a.update(M_end=a["W_end"]), cwu.EINVAL),         # outputs alias
+    (lambda a: a.update(workspace=a["out"]), cwu.EINVAL),       # workspace aliases out
+    (lambda a: a.update(W_end=a["M0"]), cwu.EINVAL),            # W_end over M0
+])
+def test_forward_host_errors(mutate, expected):
+    prob = swiglu()
+    a = fake_args(prob)
+    mutate(a)
+    assert call(prob, a) == expected
+
+
+def test_forward_rejects_bad_problem_before_pointers():
+    a = fake_args(swiglu())
+    assert call(swiglu(dim=96), a) == cwu.EUNSUPPORTED
+    assert call(swiglu(batch=0), a) == cwu.EINVAL
+
+
+def test_scalar_kernels_host_errors():
+    prob = swiglu()
+    f = Fake()
+    n = prob.batch * prob.heads * prob.seq_len * 4
+    e, al, b, kw, km, cf = (f(n) for _ in range(6))
+    assert cwu.scalar_kernels(prob, e, al, b, kw, None, cf, stream=0, check=False) == cwu.EINVAL
+    assert cwu.scalar_kernels(prob, e, al, b, e, km, cf, stream=0, check=False) == cwu.EINVAL
+    assert cwu.scalar_kernels(prob, e + 8, al, b, kw, km, cf, stream=0, check=False) == cwu.EINVAL
+    assert cwu.scalar_kernels(swiglu(chunk=0), e, al, b, kw, km, cf, stream=0,
+                              check=False) == cwu.EINVAL
+
+
+def test_timed_entry_host_errors():
+    prob = swiglu()
+    a = fake_args(prob)
+    L = cwu.lib()
+
+    def timed(kclass, events, n):
+        arr = (ctypes.c_void_p * max(n, 1))(*events)
+        return L.e2ttt_chunk_forward_timed(
+            ctypes.byref(prob), a["q"], a["k"], a["v"], a["eta"], a["alpha"], a["beta"],
+            a["W0"], a["M0"], a["out"], a["W_end"], a["M_end"], a["workspace"], a["nws"], 0,
+            kclass, arr, n, None)
+
+    assert timed(99, [], 0) == cwu.EINVAL
+    assert timed(-1, [], 0) == cwu.EINVAL
+    assert timed(cwu.KERNEL_AGG, [None, None], 2) == cwu.EINVAL
+    assert timed(cwu.KERNEL_AGG, [], -2) == cwu.EINVAL

@@ -12,6 +12,7 @@
 
 #include "e2ttt.h"
 #include "kernels.hpp"
+#include "fused.hpp"
 
 using namespace e2ttt;
 
@@ -26,9 +27,11 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow
 struct Plan {
   int64_t B, H, BH, L, d, h, C, Cp, nC, P;
   int kind, io, mode, krep;
+  bool fused;   // two-kernel chunk step (SwiGLU, d = 128, bf16 io)
+  int rbA;      // phase A rows per workgroup (32 or 64)
   size_t opsz;  // bytes per GEMM operand element (2 for bf16, 4 for fp32)
   // workspace offsets (bytes)
-  size_t kw, km, coef, kt, w13s, w2s, w2ts, zrow, a1s, a3s, grow, ut, gt, zt, gw, gm, total;
+  size_t kw, km, coef, kt, w13s, w2s, w2ts, zrow, a1s, a3s, grow, ut, gt, zt, gw, gm, gf, total;
 };
 
 e2ttt_status check_problem(const e2ttt_problem* p) {
@@ -86,6 +89,20 @@ e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
     q.coef = take(f4 * q.BH * q.nC * 4);
     q.gw = take(f4 * q.BH * q.Cp * q.d);
     q.gm = take(f4 * q.BH * q.Cp * q.d);
+  } else if (q.io == E2TTT_BF16 && q.d == FD) {
+    q.fused = true;
+    q.Cp = (q.C + 127) / 128 * 128;
+    q.opsz = 2;
+    q.krep = (p->flags & E2TTT_FLAG_COMPENSATED_WEIGHTS) ? 2 : 1;
+    q.rbA = (q.krep == 2 || q.BH * (2 * q.Cp / 64) >= 512) ? 64 : 32;
+    const size_t T = q.opsz;
+    q.kw = take(f4 * q.BH * q.nC * q.Cp);
+    q.km = take(f4 * q.BH * q.nC * q.Cp);
+    q.coef = take(f4 * q.BH * q.nC * 4);
+    q.w13s = take(T * q.BH * 2 * q.h * q.krep * q.d);
+    q.w2s = take(T * q.BH * q.d * q.krep * q.h);
+    q.w2ts = take(T * q.BH * q.h * q.krep * q.d);
+    q.gf = take(f4 * q.BH * q.Cp * q.d);
   } else {
     q.Cp = (q.C + 127) / 128 * 128;
     q.opsz = q.io == E2TTT_BF16 ? 2 : 4;
@@ -149,6 +166,12 @@ void set_lds_attributes() {
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lin_fwd<float>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lin_fwd<bf16_t>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_phaseA<32>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_phaseA<64>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_phaseB),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   g_attr_done.store(1, std::memory_order_release);
 }
@@ -233,6 +256,48 @@ void launch_swiglu(const Plan& q, const void* qv, const void* kv, const void* vv
     E2TTT_LAUNCH(I, E2TTT_KERNEL_AGG, k_agg<T>, dim3(grid1(q.BH * (na + nb))), dim3(256), 0, st,
                  s, ri, static_cast<int>(r == q.nC - 1), ut, kt, gt, zt, coef, Win, Min, Wend,
                  Mend, w13s, w2s, w2ts);
+  }
+}
+
+void launch_fused(const Plan& q, const void* qv, const void* kv, const void* vv,
+                  const float* eta, const float* alpha, const float* beta, const float* W0,
+                  const float* M0, void* outv, float* Wend, float* Mend, char* ws,
+                  hipStream_t st, Instr& I) {
+  FusedArgs a;
+  a.BH = q.BH; a.L = q.L; a.h = q.h; a.C = q.C; a.Cp = q.Cp; a.nC = q.nC; a.krep = q.krep;
+  a.q = static_cast<const bf16_t*>(qv);
+  a.k = static_cast<const bf16_t*>(kv);
+  a.v = static_cast<const bf16_t*>(vv);
+  a.out = static_cast<bf16_t*>(outv);
+  a.kw = reinterpret_cast<const float*>(ws + q.kw);
+  a.km = reinterpret_cast<const float*>(ws + q.km);
+  a.coef = reinterpret_cast<const float*>(ws + q.coef);
+  a.w13s = reinterpret_cast<bf16_t*>(ws + q.w13s);
+  a.w2s = reinterpret_cast<bf16_t*>(ws + q.w2s);
+  a.w2ts = reinterpret_cast<bf16_t*>(ws + q.w2ts);
+  a.gf = reinterpret_cast<float*>(ws + q.gf);
+  a.Wout = Wend;
+  a.Mout = Mend;
+  Shape s{q.BH, q.L, q.d, q.h, q.C, q.Cp, q.nC, q.krep};
+  launch_scan(q, eta, alpha, beta, reinterpret_cast<float*>(ws + q.kw),
+              reinterpret_cast<float*>(ws + q.km), q.nC * q.Cp, q.Cp, q.Cp,
+              reinterpret_cast<float*>(ws + q.coef), 4, st, I);
+  E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, k_prep_shadow<bf16_t>, dim3(grid1((q.BH * q.P + 255) / 256)),
+               dim3(256), 0, st, s, W0, a.w13s, a.w2s, a.w2ts);
+  const size_t ldsA = q.rbA == 64 ? phaseA_lds_bytes<64>(q.krep) : phaseA_lds_bytes<32>(q.krep);
+  const size_t ldsB = phaseB_lds_bytes(q.krep);
+  const unsigned gA = grid1(q.BH * (2 * q.Cp / q.rbA));
+  const unsigned gB = grid1(q.BH * (q.h / 32));
+  for (int64_t r = 0; r < q.nC; ++r) {
+    a.r = static_cast<int>(r);
+    a.last = static_cast<int>(r == q.nC - 1);
+    a.Win = r == 0 ? W0 : Wend;
+    a.Min = r == 0 ? M0 : Mend;
+    if (q.rbA == 64)
+      E2TTT_LAUNCH(I, E2TTT_KERNEL_PHASE_A, k_phaseA<64>, dim3(gA), dim3(256), ldsA, st, a);
+    else
+      E2TTT_LAUNCH(I, E2TTT_KERNEL_PHASE_A, k_phaseA<32>, dim3(gA), dim3(256), ldsA, st, a);
+    E2TTT_LAUNCH(I, E2TTT_KERNEL_PHASE_B, k_phaseB, dim3(gB), dim3(256), ldsB, st, a);
   }
 }
 
@@ -351,6 +416,8 @@ e2ttt_status forward_impl(const e2ttt_problem* prob, const void* q, const void* 
         launch_linear<bf16_t>(pl, q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end, ws, st, I);
       else
         launch_linear<float>(pl, q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end, ws, st, I);
+    } else if (pl.fused) {
+      launch_fused(pl, q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end, ws, st, I);
     } else {
       if (pl.io == E2TTT_BF16)
         launch_swiglu<bf16_t>(pl, q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end, ws, st, I);

@@ -70,7 +70,8 @@ WORKLOADS = {w.name: w for w in [
     Workload("swiglu-d128h256-b8h16-l4096-c2048-bf16", SWIGLU, 8, 16, 4096, 128, 256, 2048, BF16),
     Workload("swiglu-d128h256-b1h16-l32768-c2048-bf16", SWIGLU, 1, 16, 32768, 128, 256, 2048, BF16),
     Workload("swiglu-d768h1536-b1h1-l57344-c8192-bf16", SWIGLU, 1, 1, 57344, 768, 1536, 8192, BF16),
-    Workload("swiglu-d128h256-b1h1-l65536-c512-fp32", SWIGLU, 1, 1, 65536, 128, 256, 512, F32),
+    Workload("swiglu-d128h256-b1h1-l65536-c512-fp32-nearunit", SWIGLU, 1, 1, 65536, 128, 256, 512,
+             F32, "nearunit"),
     Workload("swiglu-d128h256-b2h4-l4096-c512-bf16-nearunit", SWIGLU, 2, 4, 4096, 128, 256, 512, BF16,
              "nearunit"),
 ]}

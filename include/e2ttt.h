@@ -156,7 +156,10 @@ typedef enum {
   E2TTT_KERNEL_AGG = 5,        /* scaled aggregations + state (per chunk)    */
   E2TTT_KERNEL_LINEAR_FWD = 6, /* linear learner: readout and residuals      */
   E2TTT_KERNEL_LINEAR_AGG = 7, /* linear learner: aggregations + state       */
-  E2TTT_KERNEL_NUM_CLASSES = 8
+  E2TTT_KERNEL_PHASE_A = 8,    /* d = 128 bf16: fused forward, readout, g     */
+  E2TTT_KERNEL_PHASE_B = 9,    /* d = 128 bf16: fused backward, aggregations,
+                                  chunk-end state                           */
+  E2TTT_KERNEL_NUM_CLASSES = 10
 } e2ttt_kernel_class;
 
 /* Benchmark instrumentation: enqueue exactly the work of e2ttt_chunk_forward

@@ -145,6 +145,8 @@ def main():
     ap.add_argument("--flags", type=int, default=0, help="e2ttt_problem.flags")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true",
+                    help="skip the per-kernel event pass (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -191,6 +193,11 @@ def main():
     value = tokens / (ms * 1e-3)
     log(f"bench: {args.steps} steps, {ms:.4f} ms/step, {value:.4g} tokens/s")
 
+    if args.no_kernel_timing:
+        print(json.dumps({"metric": "TTT-layer fwd tokens/sec on 1 MI355X; MFMA util % of bf16 peak",
+                          "value": value, "unit": "tokens/s", "ms_per_step": ms,
+                          "config": w.describe()}), flush=True)
+        return
     # Second timed pass: per-kernel-class launch durations with HIP events.
     ev = HipEvents()
     classes = ([cwu.KERNEL_SCAN, cwu.KERNEL_LINEAR_FWD, cwu.KERNEL_LINEAR_AGG] if w.kind == 0

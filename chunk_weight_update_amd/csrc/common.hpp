@@ -32,7 +32,11 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return f2bf(x); }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// Logistic function with the hardware reciprocal (about 1 ulp), which keeps
+// the epilogues free of the multi-instruction IEEE divide sequence.
+__device__ __forceinline__ float sigmoidf_(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
 
 // ---------------------------------------------------------------------------
 // MFMA 32x32 wrappers.  Output layout (both types): lane l, register v holds
@@ -137,14 +141,16 @@ __device__ __forceinline__ void gemm_tile(f32x16_t (&acc)[2][2], const RowLoader
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
   constexpr int BK = Tile<T>::BK, SLAB = Tile<T>::SLAB;
-  T* As[2] = {lds, lds + 2 * SLAB};
-  T* Bs[2] = {lds + SLAB, lds + 3 * SLAB};
+  // Buffer b of A is lds + 2*b*SLAB, of B lds + (2*b+1)*SLAB.  Selected by
+  // arithmetic on the LDS pointer (not through an array of pointers) so the
+  // compiler keeps LDS address space and emits ds_* instead of flat_* ops,
+  // which would otherwise wait on the in-flight global prefetch.
   uint4 ra[4], rb[4];
   const int64_t nk = K / BK;
   la.load(ra, 0);
   lb.load(rb, 0);
-  stage_lds(As[0], ra);
-  stage_lds(Bs[0], rb);
+  stage_lds(lds, ra);
+  stage_lds(lds + SLAB, rb);
   __syncthreads();
   for (int64_t ks = 0; ks < nk; ++ks) {
     const int cur = static_cast<int>(ks & 1);
@@ -154,10 +160,12 @@ __device__ __forceinline__ void gemm_tile(f32x16_t (&acc)[2][2], const RowLoader
       la.load(ra, k1 % ka);
       lb.load(rb, k1);
     }
-    mma_slab<T>(As[cur], Bs[cur], acc);
+    T* Ac = lds + 2 * cur * SLAB;
+    mma_slab<T>(Ac, Ac + SLAB, acc);
     if (more) {
-      stage_lds(As[cur ^ 1], ra);
-      stage_lds(Bs[cur ^ 1], rb);
+      T* An = lds + 2 * (cur ^ 1) * SLAB;
+      stage_lds(An, ra);
+      stage_lds(An + SLAB, rb);
     }
     __syncthreads();
   }

@@ -31,7 +31,8 @@ struct Plan {
   int rbA;      // phase A rows per workgroup (32 or 64)
   size_t opsz;  // bytes per GEMM operand element (2 for bf16, 4 for fp32)
   // workspace offsets (bytes)
-  size_t kw, km, coef, kt, w13s, w2s, w2ts, zrow, a1s, a3s, grow, ut, gt, zt, gw, gm, gf, total;
+  size_t kw, km, coef, kt, w13s, w2s, w2ts, zrow, a1s, a3s, grow, ut, gt, zt, gw, gm, gbf, gtw,
+      gtm, total;
 };
 
 e2ttt_status check_problem(const e2ttt_problem* p) {
@@ -102,7 +103,10 @@ e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
     q.w13s = take(T * q.BH * 2 * q.h * q.krep * q.d);
     q.w2s = take(T * q.BH * q.d * q.krep * q.h);
     q.w2ts = take(T * q.BH * q.h * q.krep * q.d);
-    q.gf = take(f4 * q.BH * q.Cp * q.d);
+    q.kt = take(T * q.BH * q.nC * q.d * q.Cp);
+    q.gbf = take(T * q.BH * q.Cp * q.d);
+    q.gtw = take(T * q.BH * q.d * q.Cp);
+    q.gtm = take(T * q.BH * q.d * q.Cp);
   } else {
     q.Cp = (q.C + 127) / 128 * 128;
     q.opsz = q.io == E2TTT_BF16 ? 2 : 4;
@@ -167,12 +171,12 @@ void set_lds_attributes() {
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lin_fwd<bf16_t>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_phaseA<32>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_phaseA<64>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_phaseB),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  const void* fused_kernels[] = {
+      reinterpret_cast<const void*>(&k_phaseA<32, 1>), reinterpret_cast<const void*>(&k_phaseA<64, 1>),
+      reinterpret_cast<const void*>(&k_phaseA<64, 2>), reinterpret_cast<const void*>(&k_phaseB<1>),
+      reinterpret_cast<const void*>(&k_phaseB<2>)};
+  for (const void* f : fused_kernels)
+    (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   g_attr_done.store(1, std::memory_order_release);
 }
 
@@ -264,7 +268,7 @@ void launch_fused(const Plan& q, const void* qv, const void* kv, const void* vv,
                   const float* M0, void* outv, float* Wend, float* Mend, char* ws,
                   hipStream_t st, Instr& I) {
   FusedArgs a;
-  a.BH = q.BH; a.L = q.L; a.h = q.h; a.C = q.C; a.Cp = q.Cp; a.nC = q.nC; a.krep = q.krep;
+  a.BH = q.BH; a.L = q.L; a.h = q.h; a.C = q.C; a.Cp = q.Cp; a.nC = q.nC;
   a.q = static_cast<const bf16_t*>(qv);
   a.k = static_cast<const bf16_t*>(kv);
   a.v = static_cast<const bf16_t*>(vv);
@@ -275,29 +279,36 @@ void launch_fused(const Plan& q, const void* qv, const void* kv, const void* vv,
   a.w13s = reinterpret_cast<bf16_t*>(ws + q.w13s);
   a.w2s = reinterpret_cast<bf16_t*>(ws + q.w2s);
   a.w2ts = reinterpret_cast<bf16_t*>(ws + q.w2ts);
-  a.gf = reinterpret_cast<float*>(ws + q.gf);
+  a.kt = reinterpret_cast<const bf16_t*>(ws + q.kt);
+  a.gbf = reinterpret_cast<bf16_t*>(ws + q.gbf);
+  a.gtw = reinterpret_cast<bf16_t*>(ws + q.gtw);
+  a.gtm = reinterpret_cast<bf16_t*>(ws + q.gtm);
   a.Wout = Wend;
   a.Mout = Mend;
   Shape s{q.BH, q.L, q.d, q.h, q.C, q.Cp, q.nC, q.krep};
   launch_scan(q, eta, alpha, beta, reinterpret_cast<float*>(ws + q.kw),
               reinterpret_cast<float*>(ws + q.km), q.nC * q.Cp, q.Cp, q.Cp,
               reinterpret_cast<float*>(ws + q.coef), 4, st, I);
+  E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, k_prep_kt<bf16_t>,
+               dim3(grid1(q.BH * q.nC * (q.Cp / 64) * (q.d / 64))), dim3(256), 0, st, s, a.k,
+               reinterpret_cast<bf16_t*>(ws + q.kt));
   E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, k_prep_shadow<bf16_t>, dim3(grid1((q.BH * q.P + 255) / 256)),
                dim3(256), 0, st, s, W0, a.w13s, a.w2s, a.w2ts);
-  const size_t ldsA = q.rbA == 64 ? phaseA_lds_bytes<64>(q.krep) : phaseA_lds_bytes<32>(q.krep);
-  const size_t ldsB = phaseB_lds_bytes(q.krep);
   const unsigned gA = grid1(q.BH * (2 * q.Cp / q.rbA));
-  const unsigned gB = grid1(q.BH * (q.h / 32));
+  const unsigned gB = grid1(q.BH * (q.h / 64));
   for (int64_t r = 0; r < q.nC; ++r) {
     a.r = static_cast<int>(r);
     a.last = static_cast<int>(r == q.nC - 1);
     a.Win = r == 0 ? W0 : Wend;
     a.Min = r == 0 ? M0 : Mend;
-    if (q.rbA == 64)
-      E2TTT_LAUNCH(I, E2TTT_KERNEL_PHASE_A, k_phaseA<64>, dim3(gA), dim3(256), ldsA, st, a);
-    else
-      E2TTT_LAUNCH(I, E2TTT_KERNEL_PHASE_A, k_phaseA<32>, dim3(gA), dim3(256), ldsA, st, a);
-    E2TTT_LAUNCH(I, E2TTT_KERNEL_PHASE_B, k_phaseB, dim3(gB), dim3(256), ldsB, st, a);
+    void (*kA)(FusedArgs) = q.krep == 2 ? k_phaseA<64, 2>
+                           : (q.rbA == 64 ? k_phaseA<64, 1> : k_phaseA<32, 1>);
+    const size_t ldsA = q.krep == 2 ? PhaseACfg<64, 2>::LDS_BYTES
+                        : (q.rbA == 64 ? PhaseACfg<64, 1>::LDS_BYTES : PhaseACfg<32, 1>::LDS_BYTES);
+    void (*kB)(FusedArgs) = q.krep == 2 ? k_phaseB<2> : k_phaseB<1>;
+    E2TTT_LAUNCH(I, E2TTT_KERNEL_PHASE_A, kA, dim3(gA), dim3(256), ldsA, st, a);
+    const size_t ldsB = q.krep == 2 ? PhaseBCfg<2>::LDS_BYTES : PhaseBCfg<1>::LDS_BYTES;
+    E2TTT_LAUNCH(I, E2TTT_KERNEL_PHASE_B, kB, dim3(gB), dim3(512), ldsB, st, a);
   }
 }
 

@@ -1,5 +1,5 @@
 // fused.hpp -- two-kernel chunk step of the SwiGLU learner for head dim 128,
-// bf16 operands (gfx950 MFMA 32x32x16).
+// bf16 operands (gfx950 MFMA).
 //
 // "Rethinking Expressivity and Efficiency in Test-Time Training" (E2-TTT):
 // every per-token gradient of a chunk is taken at the chunk-start weights
@@ -8,22 +8,28 @@
 //
 // Phase A (k_phaseA): one workgroup per block of RB rows of [K; Q] of one
 //   (batch, head) unit.  It streams the hidden units in blocks: A1, A3 of the
-//   block (MFMA against the W1/W3 shadow), Z = silu(A1) * A3 kept in LDS, and
+//   block (MFMA against the W1/W3 operand shadow), Z = silu(A1) * A3 in LDS,
 //   Y += Z W2[:, block]^T.  Q rows: the readout o = Y (Eq. 6).  K rows: the
-//   activation gradient g = v - Y (fp32, token-major) for phase B.
-// Phase B (k_phaseB): one workgroup per block of 32 hidden units i of one
-//   unit.  Hidden unit i owns row i of W1 and W3 and column i of W2, so the
-//   state is partitioned with no overlap.  For tiles of 32 tokens it
-//   recomputes A1, A3 (K W1[I]^T, K W3[I]^T) and dZ = g W2[:, I], forms
-//   dA1 = dZ A3 silu'(A1), dA3 = dZ silu(A1), Z = silu(A1) A3, and feeds them
-//   straight into the aggregations over the tile's tokens:
-//     A^W_{W1}[I,:] += (K^W dA1)^T K,  A^M_{W1}[I,:] += (K^M dA1)^T K
-//     A^W_{W3}[I,:], A^M_{W3}[I,:] likewise with dA3
-//     A^W_{W2}[:,I] += (K^W g)^T Z,   A^M_{W2}[:,I] += (K^M g)^T Z
-//   and ends with the chunk-end state W_C = cW W_0 + cWM M_0 + A^W,
-//   M_C = cM M_0 + A^M and the next chunk's operand shadows.
-// The per-token scale multiplies the fp32 factor (dA1, dA3, g) before its
-// single rounding to bf16; K enters exactly (it is bf16 already).
+//   activation gradient g = v - Y, written as bf16 token-major (operand of
+//   the backward) and as K^W g, K^M g feature-major (operands of the W2
+//   aggregation), each rounded once from fp32.
+// Phase B (k_phaseB): one workgroup per block of 64 hidden units of one unit;
+//   wave w owns 16 hidden units i.  Hidden unit i owns row i of W1 and W3 and
+//   column i of W2, so waves and workgroups write disjoint state.  Per tile
+//   of 32 tokens a wave recomputes A1, A3 = K W1[i]^T, K W3[i]^T and
+//   dZ = g W2[:, i] (16x16x32 MFMAs), forms dA1 = dZ A3 silu'(A1),
+//   dA3 = dZ silu(A1), Z = silu(A1) A3 in registers, and feeds them without
+//   leaving registers into the aggregations over the tile's tokens:
+//     A^W_{W1}[i,:] += (K^W dA1)^T K,  A^M_{W1}[i,:] += (K^M dA1)^T K
+//     A^W_{W3}[i,:], A^M_{W3}[i,:] likewise with dA3
+//     A^W_{W2}[:,i] += (K^W g)^T Z,   A^M_{W2}[:,i] += (K^M g)^T Z
+//   This works because a 16x16 accumulator gives lane l the column l%16 and
+//   rows 4*(l/16)+v: a lane holds one hidden unit for 8 tokens of the tile,
+//   which is exactly an operand fragment of a 16x16x32 MFMA that contracts
+//   over tokens, once the partner operand (K or K^W g, feature-major in LDS)
+//   is read with the same token order.  The chunk-end state
+//   W_C = cW W_0 + cWM M_0 + A^W, M_C = cM M_0 + A^M and the next chunk's
+//   operand shadows are written at the end.
 #pragma once
 #include "common.hpp"
 
@@ -31,9 +37,11 @@ namespace e2ttt {
 
 constexpr int FD = 128;  // head dim of the fused path
 
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 struct FusedArgs {
   int64_t BH, L, h, C, Cp, nC;
-  int krep;   // 1, or 2 for hi/lo weight operands
   int r;      // chunk index
   int last;   // 1 on the last chunk (no shadow update)
   const bf16_t* q;
@@ -47,10 +55,13 @@ struct FusedArgs {
   const float* Min;
   float* Wout;
   float* Mout;
-  bf16_t* w13s;  // [BH][2h][krep*FD]
-  bf16_t* w2s;   // [BH][FD][krep*h]
-  bf16_t* w2ts;  // [BH][h][krep*FD]
-  float* gf;     // [BH][Cp][FD] fp32 residuals of the chunk's K rows
+  bf16_t* w13s;       // [BH][2h][KREP*FD]
+  bf16_t* w2s;        // [BH][FD][KREP*h]
+  bf16_t* w2ts;       // [BH][h][KREP*FD]
+  const bf16_t* kt;   // [BH][nC][FD][Cp]  K feature-major
+  bf16_t* gbf;        // [BH][Cp][FD]      bf16(g), token-major
+  bf16_t* gtw;        // [BH][FD][Cp]      bf16(K^W g), feature-major
+  bf16_t* gtm;        // [BH][FD][Cp]      bf16(K^M g), feature-major
 };
 
 __device__ __forceinline__ int64_t fused_nvalid(const FusedArgs& a) {
@@ -58,86 +69,119 @@ __device__ __forceinline__ int64_t fused_nvalid(const FusedArgs& a) {
   return rem < a.C ? rem : a.C;
 }
 
-// Copy `rows` rows of `cols` bf16 (cols % 8 == 0) from global (row stride gs,
-// null row pointer -> zeros) into LDS (row stride ls) with 16-byte vectors.
-template <typename RowPtr>
-__device__ __forceinline__ void copy_rows_bf16(bf16_t* lds, int ls, int rows, int cols,
-                                               RowPtr rowp) {
-  const int vpr = cols / 8;
-  for (int idx = threadIdx.x; idx < rows * vpr; idx += blockDim.x) {
-    const int rr = idx / vpr, c = idx % vpr;
-    const bf16_t* src = rowp(rr);
-    uint4 val = src ? *reinterpret_cast<const uint4*>(src + c * 8) : make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(lds + rr * ls + c * 8) = val;
+// Tile copy global -> registers -> LDS with compile-time counts, so that all
+// of a thread's global loads are in flight together.  ROWS x COLS bf16
+// (COLS % 8 == 0); row rr comes from rowp(rr) (nullptr -> zeros) and lands at
+// lds + rr * LS.
+template <int ROWS, int COLS, int NT>
+struct TileCopy {
+  static constexpr int VPR = COLS / 8;
+  static constexpr int TOTAL = ROWS * VPR;
+  static constexpr int PER = (TOTAL + NT - 1) / NT;
+  // One wide vector value rather than an array, so the compiler keeps the
+  // prefetched data in registers across loop iterations (an array of uint4
+  // held across the loop was demoted to scratch memory).
+  typedef uint32_t regs_t __attribute__((ext_vector_type(4 * PER)));
+  regs_t reg;
+  __device__ __forceinline__ void put(int i, uint4 v) {
+    reg[4 * i + 0] = v.x; reg[4 * i + 1] = v.y; reg[4 * i + 2] = v.z; reg[4 * i + 3] = v.w;
   }
-}
-
-// One 32x32 MFMA block: acc += A[32 x K] * B[32 x K]^T, both row-major in LDS
-// (row strides la, lb elements), K a multiple of 16.
-__device__ __forceinline__ void mma_32x32(f32x16_t& acc, const bf16_t* A, int la,
-                                          const bf16_t* B, int lb, int K) {
-  const int lane = threadIdx.x & 63;
-  const int r32 = lane & 31, hf = lane >> 5;
-  const bf16_t* pa = A + r32 * la + hf * 8;
-  const bf16_t* pb = B + r32 * lb + hf * 8;
-#pragma unroll 4
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(pa + k0),
-                                                  *reinterpret_cast<const bf16x8_t*>(pb + k0),
-                                                  acc, 0, 0, 0);
+  __device__ __forceinline__ uint4 get(int i) const {
+    return make_uint4(reg[4 * i + 0], reg[4 * i + 1], reg[4 * i + 2], reg[4 * i + 3]);
   }
-}
-
-// Same with the A operand's k index wrapping at ka (hi/lo split B operand).
-__device__ __forceinline__ void mma_32x32_wrapA(f32x16_t& acc, const bf16_t* A, int la, int ka,
-                                                const bf16_t* B, int lb, int K) {
-  const int lane = threadIdx.x & 63;
-  const int r32 = lane & 31, hf = lane >> 5;
-  const bf16_t* pa = A + r32 * la + hf * 8;
-  const bf16_t* pb = B + r32 * lb + hf * 8;
-#pragma unroll 4
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    const int ka0 = k0 < ka ? k0 : k0 - ka;
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(pa + ka0),
-                                                  *reinterpret_cast<const bf16x8_t*>(pb + k0),
-                                                  acc, 0, 0, 0);
+  // Branch-free: a null row loads from `dummy` (any valid address) and the
+  // value is replaced by zeros, so all loads issue back to back.
+  template <typename RowPtr>
+  __device__ __forceinline__ void load(RowPtr rowp, const bf16_t* dummy) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = threadIdx.x + i * NT;
+      if (TOTAL % NT == 0 || idx < TOTAL) {
+        const bf16_t* src = rowp(idx / VPR);
+        const bool ok = src != nullptr;
+        const uint4 val = *reinterpret_cast<const uint4*>(ok ? src + (idx % VPR) * 8 : dummy);
+        put(i, ok ? val : make_uint4(0u, 0u, 0u, 0u));
+      }
+    }
   }
-}
+  template <typename RowPtr>
+  __device__ __forceinline__ void load(RowPtr rowp) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = threadIdx.x + i * NT;
+      if (TOTAL % NT == 0 || idx < TOTAL)
+        put(i, *reinterpret_cast<const uint4*>(rowp(idx / VPR) + (idx % VPR) * 8));
+    }
+  }
+  __device__ __forceinline__ void store(bf16_t* lds, int LS) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = threadIdx.x + i * NT;
+      if (TOTAL % NT == 0 || idx < TOTAL)
+        *reinterpret_cast<uint4*>(lds + (idx / VPR) * LS + (idx % VPR) * 8) = get(i);
+    }
+  }
+};
 
 __device__ __forceinline__ void zero16(f32x16_t& a) {
 #pragma unroll
   for (int v = 0; v < 16; ++v) a[v] = 0.0f;
 }
-
-// Row of a 32x32 accumulator held by this lane for register v.
-__device__ __forceinline__ int acc_row(int v) {
-  const int hf = (threadIdx.x & 63) >> 5;
-  return 8 * (v >> 2) + 4 * hf + (v & 3);
+__device__ __forceinline__ void zero4(f32x4_t& a) {
+#pragma unroll
+  for (int v = 0; v < 4; ++v) a[v] = 0.0f;
 }
-__device__ __forceinline__ int acc_col() { return threadIdx.x & 31; }
+
+// acc += A[32 x K] * B[32 x K]^T from LDS (row strides la, lb); A's k index
+// wraps at ka (hi/lo split B operand repeats the same A).
+template <int K, int KA>
+__device__ __forceinline__ void mma32_lds(f32x16_t& acc, const bf16_t* A, int la,
+                                          const bf16_t* B, int lb) {
+  const int lane = threadIdx.x & 63;
+  const bf16_t* pa = A + (lane & 31) * la + (lane >> 5) * 8;
+  const bf16_t* pb = B + (lane & 31) * lb + (lane >> 5) * 8;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        *reinterpret_cast<const bf16x8_t*>(pa + (k0 % KA)),
+        *reinterpret_cast<const bf16x8_t*>(pb + k0), acc, 0, 0, 0);
+  }
+}
+
+// Row of a 32x32 accumulator held by this lane for register v; column = lane%32.
+__device__ __forceinline__ int acc32_row(int v) {
+  return 8 * (v >> 2) + 4 * ((threadIdx.x & 63) >> 5) + (v & 3);
+}
 
 // ---------------------------------------------------------------------------
-// Phase A.  RB = 64: waves 2 (rows) x 2 (cols); a hidden block is 64 units
-// (128 shadow columns).  RB = 32: waves 1 x 4; a hidden block is 128 units.
-template <int RB>
-__global__ __launch_bounds__(256) void k_phaseA(FusedArgs a) {
-  constexpr int WM = RB / 32;           // waves along rows
-  constexpr int WN = 4 / WM;            // waves along columns
-  constexpr int HBK = WN * 32;          // hidden units per block
-  constexpr int NS = 2 * HBK;           // shadow rows (W1/W3 interleaved) per block
-  constexpr int XW = FD + 8;            // X tile row stride
-  constexpr int ZW = HBK + 8;           // Z tile row stride
-  constexpr int YN = FD / WN;           // Y columns per wave (64 or 32)
-  const int kd = a.krep * FD;           // contraction length of GEMM1 (with hi/lo)
-  const int W13W = kd + 8;              // W13 block row stride
-  const int kh = a.krep * HBK;          // contraction length of GEMM2 per block
-  const int W2W = kh + 8;
+// Phase A.  RB = 64: waves 2 (rows) x 2 (cols), hidden block of 64 units.
+// RB = 32: waves 1 x 4, hidden block of 128 units.
+template <int RB, int KREP> struct PhaseACfg {
+  static constexpr int WM = RB / 32, WN = 4 / WM;
+  static constexpr int HBK = WN * 32;       // hidden units per block
+  static constexpr int NS = 2 * HBK;        // shadow rows per block (W1/W3 interleaved)
+  static constexpr int KD = KREP * FD;      // GEMM1 contraction (with hi/lo)
+  static constexpr int KH = KREP * HBK;     // GEMM2 contraction per block
+  static constexpr int XW = FD + 8, W13W = KD + 8, ZW = HBK + 8, W2W = KH + 8;
+  static constexpr int YN = FD / WN;        // Y columns per wave
+  static constexpr int GW = RB + 8;         // transposed g staging row stride
+  static constexpr size_t LDS_ELEMS = static_cast<size_t>(RB) * XW + static_cast<size_t>(NS) * W13W +
+                                      static_cast<size_t>(RB) * ZW + static_cast<size_t>(FD) * W2W;
+  static constexpr size_t LDS_BYTES = LDS_ELEMS * sizeof(bf16_t);
+};
 
+// One or two workgroups fit a CU (dynamic LDS), so let the compiler use up to
+// 256 VGPRs instead of spilling the prefetch registers for an occupancy the
+// LDS budget rules out anyway.
+template <int RB, int KREP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_phaseA(
+    FusedArgs a) {
+  typedef PhaseACfg<RB, KREP> P;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   bf16_t* Xs = reinterpret_cast<bf16_t*>(smem_raw);
-  bf16_t* W13b = Xs + RB * XW;
-  bf16_t* Zs = W13b + NS * W13W;
-  bf16_t* W2b = Zs + RB * ZW;
+  bf16_t* W13b = Xs + RB * P::XW;
+  bf16_t* Zs = W13b + P::NS * P::W13W;
+  bf16_t* W2b = Zs + RB * P::ZW;
 
   const int64_t nrb = 2 * a.Cp / RB, krb = a.Cp / RB;
   const int64_t u = blockIdx.x / nrb;
@@ -147,272 +191,415 @@ __global__ __launch_bounds__(256) void k_phaseA(FusedArgs a) {
   const int64_t tok0 = static_cast<int64_t>(a.r) * a.C;
   const int64_t nv = fused_nvalid(a);
   const bf16_t* X = (isQ ? a.q : a.k) + (u * a.L + tok0) * FD;
-  const bf16_t* W13 = a.w13s + u * 2 * a.h * kd;
-  const bf16_t* W2 = a.w2s + u * FD * (a.krep * a.h);
-  const int64_t w2ld = a.krep * a.h;
+  const bf16_t* W13 = a.w13s + u * 2 * a.h * P::KD;
+  const bf16_t* W2 = a.w2s + u * FD * (KREP * a.h);
+  const int64_t w2ld = KREP * a.h;
+  const int nhb = static_cast<int>(a.h / P::HBK);
 
   const int wave = threadIdx.x >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  const int wm = wave / P::WN, wn = wave % P::WN;
 
-  copy_rows_bf16(Xs, XW, RB, FD, [&](int rr) -> const bf16_t* {
-    return p0 + rr < nv ? X + (p0 + rr) * FD : nullptr;
-  });
+  TileCopy<RB, FD, 256> cx;
+  TileCopy<P::NS, P::KD, 256> c13;
+  auto w13_rows = [&](int hb) {
+    return [=](int rr) -> const bf16_t* { return W13 + (static_cast<int64_t>(hb) * P::NS + rr) * P::KD; };
+  };
 
-  f32x16_t yacc[YN / 32];
+  cx.load([&](int rr) -> const bf16_t* { return p0 + rr < nv ? X + (p0 + rr) * FD : nullptr; }, X);
+  c13.load(w13_rows(0));
+  // W2 block: row j holds [hi: hidden hb*HBK .. +HBK | lo: same at offset h],
+  // copied as FD*KREP rows of HBK.
+  TileCopy<FD * KREP, P::HBK, 256> c2s;
+  auto w2_rows = [&](int hb) {
+    return [=](int rr) -> const bf16_t* {
+      const int j = rr / KREP, part = rr % KREP;
+      return W2 + j * w2ld + part * a.h + static_cast<int64_t>(hb) * P::HBK;
+    };
+  };
+  c2s.load(w2_rows(0));
+  cx.store(Xs, P::XW);
+  c13.store(W13b, P::W13W);
+  // row rr of c2s -> W2b row rr/KREP, column offset (rr%KREP)*HBK
 #pragma unroll
-  for (int i = 0; i < YN / 32; ++i) zero16(yacc[i]);
-
-  const int nhb = static_cast<int>(a.h / HBK);
-  for (int hb = 0; hb < nhb; ++hb) {
-    // Stage this block's W13 rows (NS x kd) and W2 columns (FD x kh).
-    __syncthreads();  // previous block's GEMM2 is done with Zs/W2b/W13b
-    copy_rows_bf16(W13b, W13W, NS, kd, [&](int rr) -> const bf16_t* {
-      return W13 + (static_cast<int64_t>(hb) * NS + rr) * kd;
-    });
-    // W2 block: row j holds [hi cols hb*HBK.. +HBK | lo cols h + hb*HBK .. +HBK]
-    {
-      const int vpr = HBK / 8;
-      for (int idx = threadIdx.x; idx < FD * a.krep * vpr; idx += blockDim.x) {
-        const int rr = idx / (a.krep * vpr), rem = idx % (a.krep * vpr);
-        const int part = rem / vpr, c = rem % vpr;
-        const bf16_t* src = W2 + rr * w2ld + part * a.h + hb * HBK + c * 8;
-        *reinterpret_cast<uint4*>(W2b + rr * W2W + part * HBK + c * 8) =
-            *reinterpret_cast<const uint4*>(src);
-      }
+  for (int i = 0; i < decltype(c2s)::PER; ++i) {
+    const int idx = threadIdx.x + i * 256;
+    if (decltype(c2s)::TOTAL % 256 == 0 || idx < decltype(c2s)::TOTAL) {
+      const int rr = idx / decltype(c2s)::VPR, c = idx % decltype(c2s)::VPR;
+      *reinterpret_cast<uint4*>(W2b + (rr / KREP) * P::W2W + (rr % KREP) * P::HBK + c * 8) =
+          c2s.get(i);
     }
-    __syncthreads();
+  }
+  __syncthreads();
+
+  f32x16_t yacc[P::YN / 32];
+#pragma unroll
+  for (int i = 0; i < P::YN / 32; ++i) zero16(yacc[i]);
+
+  for (int hb = 0; hb < nhb; ++hb) {
+    const bool more = hb + 1 < nhb;
+    if (more) {  // prefetch the next block's weights; they land after this block
+      c13.load(w13_rows(hb + 1));
+      c2s.load(w2_rows(hb + 1));
+    }
     // GEMM1: this wave's 32 rows x (32 A1 + 32 A3) columns.
     f32x16_t a1, a3;
     zero16(a1);
     zero16(a3);
-    const bf16_t* Ar = Xs + wm * 32 * XW;
-    const bf16_t* B1 = W13b + (wn * 64) * W13W;
-    mma_32x32_wrapA(a1, Ar, XW, FD, B1, W13W, kd);
-    mma_32x32_wrapA(a3, Ar, XW, FD, B1 + 32 * W13W, W13W, kd);
-    // Z = silu(A1) * A3 -> Zs[row][hidden in block]
+    const bf16_t* Ar = Xs + wm * 32 * P::XW;
+    const bf16_t* B1 = W13b + (wn * 64) * P::W13W;
+    mma32_lds<P::KD, FD>(a1, Ar, P::XW, B1, P::W13W);
+    mma32_lds<P::KD, FD>(a3, Ar, P::XW, B1 + 32 * P::W13W, P::W13W);
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const float x1 = a1[v];
       const float z = x1 * sigmoidf_(x1) * a3[v];
-      Zs[(wm * 32 + acc_row(v)) * ZW + wn * 32 + acc_col()] = f2bf(z);
+      Zs[(wm * 32 + acc32_row(v)) * P::ZW + wn * 32 + (threadIdx.x & 31)] = f2bf(z);
     }
     __syncthreads();
-    // GEMM2: Y[32 rows of wm][YN cols of wn] += Z[rows][HBK] W2b[cols][HBK]^T
+    // GEMM2: Y[32 rows of wm][YN cols of wn] += Z[rows][HBK] W2b[cols][KH]^T
 #pragma unroll
-    for (int i = 0; i < YN / 32; ++i)
-      mma_32x32_wrapA(yacc[i], Zs + wm * 32 * ZW, ZW, HBK, W2b + (wn * YN + i * 32) * W2W, W2W,
-                      kh);
+    for (int i = 0; i < P::YN / 32; ++i)
+      mma32_lds<P::KH, P::HBK>(yacc[i], Zs + wm * 32 * P::ZW, P::ZW,
+                               W2b + (wn * P::YN + i * 32) * P::W2W, P::W2W);
+    __syncthreads();
+    if (more) {
+      c13.store(W13b, P::W13W);
+#pragma unroll
+      for (int i = 0; i < decltype(c2s)::PER; ++i) {
+        const int idx = threadIdx.x + i * 256;
+        if (decltype(c2s)::TOTAL % 256 == 0 || idx < decltype(c2s)::TOTAL) {
+          const int rr = idx / decltype(c2s)::VPR, c = idx % decltype(c2s)::VPR;
+          *reinterpret_cast<uint4*>(W2b + (rr / KREP) * P::W2W + (rr % KREP) * P::HBK + c * 8) =
+              c2s.get(i);
+        }
+      }
+      __syncthreads();
+    }
   }
 
   // Epilogue.
+  if (isQ) {
 #pragma unroll
-  for (int i = 0; i < YN / 32; ++i)
+    for (int i = 0; i < P::YN / 32; ++i)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t p = p0 + wm * 32 + acc_row(v);
-      const int64_t j = wn * YN + i * 32 + acc_col();
-      const float y = yacc[i][v];
-      if (isQ) {
-        if (p < nv) a.out[(u * a.L + tok0 + p) * FD + j] = f2bf(y);
-      } else {
-        const float vin = p < nv ? bf2f(a.v[(u * a.L + tok0 + p) * FD + j]) : 0.0f;
-        a.gf[(u * a.Cp + p) * FD + j] = vin - y;
+      for (int v = 0; v < 16; ++v) {
+        const int64_t p = p0 + wm * 32 + acc32_row(v);
+        const int64_t j = wn * P::YN + i * 32 + (threadIdx.x & 31);
+        if (p < nv) a.out[(u * a.L + tok0 + p) * FD + j] = f2bf(yacc[i][v]);
       }
+    return;
+  }
+  const float* kwr = a.kw + (u * a.nC + a.r) * a.Cp;
+  const float* kmr = a.km + (u * a.nC + a.r) * a.Cp;
+  // g = v - Y; bf16 token-major directly; K^W g, K^M g feature-major through
+  // LDS (Xs/W13b are free now: [FD][RB + 8] each).  All loads first: the
+  // stores below could alias them as far as the compiler knows.
+  bf16_t* TW_ = W13b;                      // [FD][GW]
+  bf16_t* TM_ = W13b + FD * P::GW;          // [FD][GW]
+  // v is an input and gbf workspace: they never overlap (checked on the
+  // host), which the restrict qualifiers pass on to the compiler.
+  const bf16_t* __restrict__ vsrc = a.v + (u * a.L + tok0) * FD;
+  bf16_t* __restrict__ gdst = a.gbf + u * a.Cp * FD;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int pr = wm * 32 + acc32_row(v);
+    const int64_t p = p0 + pr;
+    const float sw = kwr[p], sm = kmr[p];
+#pragma unroll
+    for (int i = 0; i < P::YN / 32; ++i) {
+      const int j = wn * P::YN + i * 32 + (threadIdx.x & 31);
+      const float vin = p < nv ? bf2f(vsrc[p * FD + j]) : 0.0f;
+      const float g = vin - yacc[i][v];
+      gdst[p * FD + j] = f2bf(g);
+      TW_[j * P::GW + pr] = f2bf(sw * g);
+      TM_[j * P::GW + pr] = f2bf(sm * g);
     }
-}
-
-template <int RB>
-size_t phaseA_lds_bytes(int krep) {
-  constexpr int WM = RB / 32, WN = 4 / WM, HBK = WN * 32, NS = 2 * HBK;
-  const size_t e = static_cast<size_t>(RB) * (FD + 8) + static_cast<size_t>(NS) * (krep * FD + 8) +
-                   static_cast<size_t>(RB) * (HBK + 8) +
-                   static_cast<size_t>(FD) * (krep * HBK + 8);
-  return e * sizeof(bf16_t);
+  }
+  __syncthreads();
+  constexpr int VPR = RB / 8;
+  for (int idx = threadIdx.x; idx < FD * VPR; idx += 256) {
+    const int j = idx / VPR, c = idx % VPR;
+    *reinterpret_cast<uint4*>(a.gtw + (u * FD + j) * a.Cp + p0 + c * 8) =
+        *reinterpret_cast<const uint4*>(TW_ + j * P::GW + c * 8);
+    *reinterpret_cast<uint4*>(a.gtm + (u * FD + j) * a.Cp + p0 + c * 8) =
+        *reinterpret_cast<const uint4*>(TM_ + j * P::GW + c * 8);
+  }
 }
 
 // ---------------------------------------------------------------------------
-// Phase B.  One workgroup per (unit, block I of 32 hidden units); wave w owns
-// output columns j in [32w, 32w+32) of the W1/W3 aggregates and rows j of the
-// W2 aggregate.  Token tiles of TB = 32.
-struct PhaseBLds {
-  static constexpr int TB = 32;
-  static constexpr int KW_ = FD + 8;   // token-major K / g tiles
-  static constexpr int TW = TB + 8;    // feature-major tiles (row = feature)
+// Phase B.  LDS: the recompute weights of the workgroup's 64 hidden units
+// ([4 waves][W1, W3, W2^T][16][KREP*FD + 8]), then NBUF token-tile buffers
+// (two for KREP = 1, one for the hi/lo variant, which needs twice the weights).
+template <int KREP> struct PhaseBCfg {
+  static constexpr int TB = 32;               // tokens per tile
+  static constexpr int KS = FD + 8;           // token-major tile row stride
+  static constexpr int TS = TB + 8;           // feature-major tile row stride
+  static constexpr int WS = KREP * FD + 8;    // weight row stride
+  static constexpr int NBUF = KREP == 1 ? 2 : 1;
+  static constexpr int BUF_ELEMS = 2 * TB * KS + 3 * FD * TS;  // K, g | K^T, K^W g, K^M g
+  static constexpr size_t W_BYTES = static_cast<size_t>(4 * 3 * 16 * WS) * sizeof(bf16_t);
+  static constexpr size_t BUF_BYTES = BUF_ELEMS * sizeof(bf16_t) + 2 * TB * sizeof(float);
+  static constexpr size_t LDS_BYTES = W_BYTES + NBUF * BUF_BYTES;
+  static_assert((BUF_ELEMS * sizeof(bf16_t)) % 16 == 0, "buffer alignment");
+  static_assert(W_BYTES % 16 == 0, "weight alignment");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-__device__ __forceinline__ void state_update_store(const FusedArgs& a, int64_t u, int64_t off,
-                                                   float aw, float am, float cW, float cM,
-                                                   float cWM, int shadow_kind, int64_t srow,
-                                                   int64_t scol) {
+__device__ __forceinline__ f32x4_t mfma16(const bf16x8_t& a, const bf16x8_t& b,
+                                          const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Two 8-byte pieces -> one 8 x bf16 fragment.
+__device__ __forceinline__ bf16x8_t frag_2x4(const bf16_t* p0, const bf16_t* p1) {
+  const bf16x4_t lo = *reinterpret_cast<const bf16x4_t*>(p0);
+  const bf16x4_t hi = *reinterpret_cast<const bf16x4_t*>(p1);
+  bf16x8_t r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+// Chunk-end state of one entry from its preloaded start values, plus the
+// next chunk's operand shadow.  Loads are done by the caller in batches: the
+// outputs may alias the inputs (in-place state advance), so a load placed
+// after a store could not be hoisted by the compiler and every entry would
+// cost a full memory round trip.
+__device__ __forceinline__ void state_store(const FusedArgs& a, int krep, int64_t u, int64_t off,
+                                            float w0, float m0, float aw, float am, float cW,
+                                            float cM, float cWM, int shadow_kind, int64_t srow,
+                                            int64_t scol) {
   const int64_t P = 3 * FD * a.h;
-  const float w0 = a.Win[u * P + off], m0 = a.Min[u * P + off];
   const float wn = cW * w0 + cWM * m0 + aw;
   const float mn = cM * m0 + am;
   a.Wout[u * P + off] = wn;
   a.Mout[u * P + off] = mn;
   if (a.last) return;
   const bf16_t hi = f2bf(wn);
-  const bf16_t lo = a.krep == 2 ? f2bf(wn - bf2f(hi)) : bf16_t(0);
-  if (shadow_kind == 0) {  // W1 or W3 entry: shadow row srow, column scol (d index)
-    bf16_t* b = a.w13s + (u * 2 * a.h + srow) * (a.krep * FD);
+  const bf16_t lo = krep == 2 ? f2bf(wn - bf2f(hi)) : bf16_t(0);
+  if (shadow_kind == 0) {  // W1 / W3 entry: shadow row srow, column scol (d index)
+    bf16_t* b = a.w13s + (u * 2 * a.h + srow) * (krep * FD);
     b[scol] = hi;
-    if (a.krep == 2) b[FD + scol] = lo;
+    if (krep == 2) b[FD + scol] = lo;
   } else {  // W2 entry (j = srow, i = scol)
-    bf16_t* b2 = a.w2s + (u * FD + srow) * (a.krep * a.h);
+    bf16_t* b2 = a.w2s + (u * FD + srow) * (krep * a.h);
     b2[scol] = hi;
-    if (a.krep == 2) b2[a.h + scol] = lo;
-    bf16_t* bt = a.w2ts + (u * a.h + scol) * (a.krep * FD);
+    if (krep == 2) b2[a.h + scol] = lo;
+    bf16_t* bt = a.w2ts + (u * a.h + scol) * (krep * FD);
     bt[srow] = hi;
-    if (a.krep == 2) bt[FD + srow] = lo;
+    if (krep == 2) bt[FD + srow] = lo;
   }
 }
 
-__global__ __launch_bounds__(256) void k_phaseB(FusedArgs a) {
-  typedef PhaseBLds S;
-  constexpr int TB = S::TB, KW_ = S::KW_, TW = S::TW;
-  const int kd = a.krep * FD;
-  const int WW = kd + 8;  // weight slice row stride
-
+template <int KREP>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_phaseB(
+    FusedArgs a) {
+  typedef PhaseBCfg<KREP> S;
+  constexpr int TB = S::TB, KS = S::KS, TS = S::TS, WS = S::WS;
+  constexpr int NT = 512;                 // 8 waves
+  constexpr int KSTEPS = KREP * FD / 32;  // recompute k-steps (16x16x32)
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  bf16_t* W1I = reinterpret_cast<bf16_t*>(smem_raw);  // [32][WW]
-  bf16_t* W3I = W1I + 32 * WW;
-  bf16_t* W2I = W3I + 32 * WW;                         // W2^T rows of I
-  bf16_t* Ks = W2I + 32 * WW;                          // [TB][KW_] token-major K
-  bf16_t* KT = Ks + TB * KW_;                          // [FD][TW] feature-major K
-  bf16_t* Gs = KT + FD * TW;                           // [TB][KW_] bf16(g)
-  bf16_t* GTW = Gs + TB * KW_;                         // [FD][TW] bf16(K^W g)
-  bf16_t* GTM = GTW + FD * TW;                         // [FD][TW] bf16(K^M g)
-  bf16_t* DA = GTM + FD * TW;                          // 4 x [32][TW]: dA1 W,M, dA3 W,M
-  bf16_t* ZT = DA + 4 * 32 * TW;                       // [32][TW] Z^T
-  float* R = reinterpret_cast<float*>(ZT + 32 * TW);   // 3 x [TB][33]: A1, A3, dZ
-  float* ksc = R + 3 * TB * 33;                        // [2][TB] K^W, K^M of the tile
+  // Weights first, then buffer b: bf16 tiles, then 2*TB floats of kernels.
+  // Selected arithmetically so LDS accesses stay ds_* ops.
+  bf16_t* Wl = reinterpret_cast<bf16_t*>(smem_raw);
+  auto bufp = [&](int b) -> bf16_t* {
+    return reinterpret_cast<bf16_t*>(smem_raw + S::W_BYTES + b * S::BUF_BYTES);
+  };
+  auto kscp = [&](int b) -> float* {
+    return reinterpret_cast<float*>(smem_raw + S::W_BYTES + b * S::BUF_BYTES +
+                                    S::BUF_ELEMS * sizeof(bf16_t));
+  };
 
-  const int64_t nib = a.h / 32;
+  const int64_t nib = a.h / 64;
   const int64_t u = blockIdx.x / nib;
   const int64_t ib = blockIdx.x % nib;
   const int64_t tok0 = static_cast<int64_t>(a.r) * a.C;
   const int64_t nv = fused_nvalid(a);
   const int wave = threadIdx.x >> 6;
-  const int tid = threadIdx.x;
+  const int hg = wave >> 1;   // hidden group: 16 hidden units
+  const int jh = wave & 1;    // half of the output columns j (64 each)
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int64_t i_glob = 64 * ib + 16 * hg + l16;  // this lane's hidden unit (B column)
 
-  // Weight slices of this hidden block (rows of the operand shadows).
+  // Recompute B operands of the workgroup's 64 hidden units (row = hidden
+  // unit, k = d; hi/lo halves when KREP = 2) into LDS: [group][q][16][WS].
   {
-    const bf16_t* w13 = a.w13s + u * 2 * a.h * kd;
-    copy_rows_bf16(W1I, WW, 32, kd, [&](int rr) -> const bf16_t* {
-      return w13 + (64 * ib + rr) * kd;
+    const bf16_t* w13 = a.w13s + u * 2 * a.h * (KREP * FD);
+    const bf16_t* w2t = a.w2ts + u * a.h * (KREP * FD);
+    TileCopy<4 * 3 * 16, KREP * FD, NT> cw;
+    cw.load([&](int rr) -> const bf16_t* {
+      const int grp = rr / 48, q = (rr / 16) % 3, il = rr % 16;
+      const int64_t i = 64 * ib + 16 * grp + il;
+      if (q == 2) return w2t + i * (KREP * FD);
+      return w13 + (64 * (i / 32) + (q == 1 ? 32 : 0) + i % 32) * (KREP * FD);
     });
-    copy_rows_bf16(W3I, WW, 32, kd, [&](int rr) -> const bf16_t* {
-      return w13 + (64 * ib + 32 + rr) * kd;
-    });
-    const bf16_t* w2t = a.w2ts + u * a.h * kd;
-    copy_rows_bf16(W2I, WW, 32, kd, [&](int rr) -> const bf16_t* {
-      return w2t + (32 * ib + rr) * kd;
-    });
+    cw.store(Wl, WS);
   }
+  const bf16_t* Wq = Wl + hg * 3 * 16 * WS;  // this wave's [3][16][WS]
 
-  f32x16_t acc[6];  // W1^W, W1^M, W3^W, W3^M (rows i, cols j of wave), W2^W, W2^M (rows j, cols i)
+  // Accumulators (16x16 blocks over this wave's 16 hidden units and its 64
+  // columns j): [0..3] A^W_W1 (rows i, cols j block), [4..7] A^M_W1,
+  // [8..11] A^W_W3, [12..15] A^M_W3, [16..19] A^W_W2 (rows j block, cols i),
+  // [20..23] A^M_W2.
+  f32x4_t acc[24];
 #pragma unroll
-  for (int q = 0; q < 6; ++q) zero16(acc[q]);
+  for (int q = 0; q < 24; ++q) zero4(acc[q]);
 
   const bf16_t* Kg = a.k + (u * a.L + tok0) * FD;
-  const float* gfu = a.gf + u * a.Cp * FD;
+  const bf16_t* Gg = a.gbf + u * a.Cp * FD;
+  const bf16_t* KTg = a.kt + (u * a.nC + a.r) * FD * a.Cp;
+  const bf16_t* GWg = a.gtw + u * FD * a.Cp;
+  const bf16_t* GMg = a.gtm + u * FD * a.Cp;
   const float* kwr = a.kw + (u * a.nC + a.r) * a.Cp;
   const float* kmr = a.km + (u * a.nC + a.r) * a.Cp;
 
-  for (int64_t t0 = 0; t0 < a.Cp; t0 += TB) {
-    __syncthreads();  // previous tile fully consumed
-    // K tile: token-major (recompute operand) and feature-major (aggregation operand).
-    for (int idx = tid; idx < TB * (FD / 8); idx += 256) {
-      const int tr = idx / (FD / 8), c = idx % (FD / 8);
-      const int64_t p = t0 + tr;
-      uint4 val = p < nv ? *reinterpret_cast<const uint4*>(Kg + p * FD + c * 8)
-                         : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(Ks + tr * KW_ + c * 8) = val;
-      const bf16_t* e = reinterpret_cast<const bf16_t*>(&val);
+  TileCopy<TB, FD, NT> ck, cg;          // token-major K, bf16(g)
+  TileCopy<FD, TB, NT> ckt, cgw, cgm;   // feature-major K^T, K^W g, K^M g
+  float sk = 0.0f;
+  auto load_tile = [&](int64_t t0) {
+    ck.load([&](int rr) -> const bf16_t* { return t0 + rr < nv ? Kg + (t0 + rr) * FD : nullptr; },
+            Kg);
+    cg.load([&](int rr) -> const bf16_t* { return Gg + (t0 + rr) * FD; });
+    ckt.load([&](int rr) -> const bf16_t* { return KTg + rr * a.Cp + t0; });
+    cgw.load([&](int rr) -> const bf16_t* { return GWg + rr * a.Cp + t0; });
+    cgm.load([&](int rr) -> const bf16_t* { return GMg + rr * a.Cp + t0; });
+    if (threadIdx.x < 2 * TB)
+      sk = threadIdx.x < TB ? kwr[t0 + threadIdx.x] : kmr[t0 + threadIdx.x - TB];
+  };
+  auto store_tile = [&](int b) {
+    bf16_t* B = bufp(b);
+    ck.store(B, KS);
+    cg.store(B + TB * KS, KS);
+    ckt.store(B + 2 * TB * KS, TS);
+    cgw.store(B + 2 * TB * KS + FD * TS, TS);
+    cgm.store(B + 2 * TB * KS + 2 * FD * TS, TS);
+    if (threadIdx.x < 2 * TB) kscp(b)[threadIdx.x] = sk;
+  };
+
+  const int ntiles = static_cast<int>(a.Cp / TB);
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int b = S::NBUF == 2 ? (it & 1) : 0;
+    if (it + 1 < ntiles) load_tile(static_cast<int64_t>(it + 1) * TB);
+    const bf16_t* Ks = bufp(b);
+    const bf16_t* Gs = Ks + TB * KS;
+    const bf16_t* KTs = Ks + 2 * TB * KS;
+    const bf16_t* GWs = KTs + FD * TS;
+    const bf16_t* GMs = KTs + 2 * FD * TS;
+    const float* kws = kscp(b);
+    const float* kms = kws + TB;
+
+    // Recompute: rows = tokens (2 blocks of 16), cols = this wave's 16 hidden.
+    f32x4_t ra1[2], ra3[2], rdz[2];
 #pragma unroll
-      for (int x = 0; x < 8; ++x) KT[(c * 8 + x) * TW + tr] = e[x];
-    }
-    if (tid < TB) {
-      ksc[tid] = kwr[t0 + tid];
-      ksc[TB + tid] = kmr[t0 + tid];
-    }
-    __syncthreads();
-    // g tile (fp32): bf16 token-major, and K^W / K^M scaled feature-major.
-    for (int idx = tid; idx < TB * (FD / 4); idx += 256) {
-      const int tr = idx / (FD / 4), c = idx % (FD / 4);
-      const float4 g4 = *reinterpret_cast<const float4*>(gfu + (t0 + tr) * FD + c * 4);
-      const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
-      const float sw = ksc[tr], sm = ksc[TB + tr];
+    for (int tb = 0; tb < 2; ++tb) {
+      zero4(ra1[tb]);
+      zero4(ra3[tb]);
+      zero4(rdz[tb]);
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int j = c * 4 + x;
-        Gs[tr * KW_ + j] = f2bf(gv[x]);
-        GTW[j * TW + tr] = f2bf(sw * gv[x]);
-        GTM[j * TW + tr] = f2bf(sm * gv[x]);
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int ko = (ks * 32) % FD;
+        const bf16x8_t fk = *reinterpret_cast<const bf16x8_t*>(Ks + (tb * 16 + l16) * KS + g4 * 8 + ko);
+        const bf16x8_t fg = *reinterpret_cast<const bf16x8_t*>(Gs + (tb * 16 + l16) * KS + g4 * 8 + ko);
+        const bf16_t* wr = Wq + l16 * WS + ks * 32 + g4 * 8;
+        ra1[tb] = mfma16(fk, *reinterpret_cast<const bf16x8_t*>(wr), ra1[tb]);
+        ra3[tb] = mfma16(fk, *reinterpret_cast<const bf16x8_t*>(wr + 16 * WS), ra3[tb]);
+        rdz[tb] = mfma16(fg, *reinterpret_cast<const bf16x8_t*>(wr + 32 * WS), rdz[tb]);
       }
     }
-    __syncthreads();
-    // Recompute A1, A3 (waves 0, 1) and dZ (wave 2) for the tile: [TB x 32 hidden].
-    if (wave < 3) {
-      f32x16_t racc;
-      zero16(racc);
-      const bf16_t* Aop = wave == 2 ? Gs : Ks;
-      const bf16_t* Bop = wave == 0 ? W1I : (wave == 1 ? W3I : W2I);
-      mma_32x32_wrapA(racc, Aop, KW_, FD, Bop, WW, kd);
-      float* Rq = R + wave * TB * 33;
+    // Elementwise; fragment slot s <-> token 16*(s/4) + 4*g4 + s%4.
+    bf16x8_t fW1, fM1, fW3, fM3, fZ;
+    {
+      const f32x4_t kw0 = *reinterpret_cast<const f32x4_t*>(kws + 4 * g4);
+      const f32x4_t kw1 = *reinterpret_cast<const f32x4_t*>(kws + 16 + 4 * g4);
+      const f32x4_t km0 = *reinterpret_cast<const f32x4_t*>(kms + 4 * g4);
+      const f32x4_t km1 = *reinterpret_cast<const f32x4_t*>(kms + 16 + 4 * g4);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) Rq[acc_row(v) * 33 + acc_col()] = racc[v];
+      for (int s = 0; s < 8; ++s) {
+        const int tb = s >> 2, v = s & 3;
+        const float x1 = ra1[tb][v], x3 = ra3[tb][v], dz = rdz[tb][v];
+        const float sg = sigmoidf_(x1);
+        const float d3 = dz * (x1 * sg);
+        const float d1 = dz * x3 * (sg * (1.0f + x1 * (1.0f - sg)));
+        const float sw = tb ? kw1[v] : kw0[v];
+        const float sm = tb ? km1[v] : km0[v];
+        fW1[s] = static_cast<__bf16>(sw * d1);
+        fM1[s] = static_cast<__bf16>(sm * d1);
+        fW3[s] = static_cast<__bf16>(sw * d3);
+        fM3[s] = static_cast<__bf16>(sm * d3);
+        fZ[s] = static_cast<__bf16>(x1 * sg * x3);
+      }
+    }
+    // Aggregations over the tile's 32 tokens for this wave's 64 columns.
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      const int jr = 64 * jh + 16 * jb + l16;  // partner-operand row (feature j)
+      const bf16_t* pk = KTs + jr * TS + 4 * g4;
+      const bf16_t* pw = GWs + jr * TS + 4 * g4;
+      const bf16_t* pm = GMs + jr * TS + 4 * g4;
+      const bf16x8_t fk = frag_2x4(pk, pk + 16);
+      const bf16x8_t fgw = frag_2x4(pw, pw + 16);
+      const bf16x8_t fgm = frag_2x4(pm, pm + 16);
+      acc[jb] = mfma16(fW1, fk, acc[jb]);
+      acc[4 + jb] = mfma16(fM1, fk, acc[4 + jb]);
+      acc[8 + jb] = mfma16(fW3, fk, acc[8 + jb]);
+      acc[12 + jb] = mfma16(fM3, fk, acc[12 + jb]);
+      acc[16 + jb] = mfma16(fgw, fZ, acc[16 + jb]);
+      acc[20 + jb] = mfma16(fgm, fZ, acc[20 + jb]);
+    }
+    if (S::NBUF == 1) __syncthreads();  // single buffer: everyone is done reading it
+    if (it + 1 < ntiles) {
+      // With two buffers, b^1 was last read in iteration it-1 (barrier since).
+      store_tile(S::NBUF == 2 ? (b ^ 1) : 0);
     }
     __syncthreads();
-    // Elementwise: dA1, dA3 scaled by both kernels, and Z, written feature-major.
-    for (int idx = tid; idx < TB * 32; idx += 256) {
-      const int tr = idx / 32, i = idx % 32;
-      const float x1 = R[tr * 33 + i], x3 = R[TB * 33 + tr * 33 + i];
-      const float dz = R[2 * TB * 33 + tr * 33 + i];
-      const float sg = sigmoidf_(x1);
-      const float d3 = dz * (x1 * sg);
-      const float d1 = dz * x3 * (sg * (1.0f + x1 * (1.0f - sg)));
-      const float sw = ksc[tr], sm = ksc[TB + tr];
-      DA[0 * 32 * TW + i * TW + tr] = f2bf(sw * d1);
-      DA[1 * 32 * TW + i * TW + tr] = f2bf(sm * d1);
-      DA[2 * 32 * TW + i * TW + tr] = f2bf(sw * d3);
-      DA[3 * 32 * TW + i * TW + tr] = f2bf(sm * d3);
-      ZT[i * TW + tr] = f2bf(x1 * sg * x3);
-    }
-    __syncthreads();
-    // Aggregations over the tile's tokens.
-    const bf16_t* KTw = KT + (wave * 32) * TW;  // B rows j of this wave
-#pragma unroll
-    for (int q = 0; q < 4; ++q) mma_32x32(acc[q], DA + q * 32 * TW, TW, KTw, TW, TB);
-    mma_32x32(acc[4], GTW + (wave * 32) * TW, TW, ZT, TW, TB);
-    mma_32x32(acc[5], GTM + (wave * 32) * TW, TW, ZT, TW, TB);
   }
 
-  // Chunk-end state and operand shadows of this hidden block.
+  // Chunk-end state and operand shadows of this wave's entries, in batches of
+  // one 16-column block: all start values first, then the stores.
   const float* cf = a.coef + (u * a.nC + a.r) * 4;
   const float cW = cf[0], cM = cf[1], cWM = cf[2];
-  const int64_t jc = wave * 32 + acc_col();
+  const int64_t P = 3 * FD * a.h;
+  const float* __restrict__ Wi = a.Win + u * P;
+  const float* __restrict__ Mi = a.Min + u * P;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int64_t i = 32 * ib + acc_row(v);  // hidden unit (rows of acc 0..3)
-    // W1[i][jc], W3[i][jc]
-    state_update_store(a, u, i * FD + jc, acc[0][v], acc[1][v], cW, cM, cWM, 0,
-                       64 * ib + acc_row(v), jc);
-    state_update_store(a, u, a.h * FD + i * FD + jc, acc[2][v], acc[3][v], cW, cM, cWM, 0,
-                       64 * ib + 32 + acc_row(v), jc);
-    // W2[j][i]: acc 4/5 rows are j (wave*32 + acc_row), cols i (acc_col)
-    const int64_t j2 = wave * 32 + acc_row(v);
-    const int64_t i2 = 32 * ib + acc_col();
-    state_update_store(a, u, 2 * a.h * FD + j2 * a.h + i2, acc[4][v], acc[5][v], cW, cM, cWM, 1,
-                       j2, i2);
+  for (int jb = 0; jb < 4; ++jb) {
+    int64_t off[3][4];
+    float w0[3][4], m0[3][4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      // W1/W3: rows i = 16*hg + 4*g4 + v (hidden), col j = 64*jh + 16*jb + l16
+      const int64_t i = 64 * ib + 16 * hg + 4 * g4 + v;
+      const int64_t j = 64 * jh + 16 * jb + l16;
+      off[0][v] = i * FD + j;
+      off[1][v] = a.h * FD + i * FD + j;
+      // W2: rows j2 = 64*jh + 16*jb + 4*g4 + v, col = this lane's hidden unit
+      off[2][v] = 2 * a.h * FD + (64 * jh + 16 * jb + 4 * g4 + v) * a.h + i_glob;
+    }
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        w0[t][v] = Wi[off[t][v]];
+        m0[t][v] = Mi[off[t][v]];
+      }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t i = 64 * ib + 16 * hg + 4 * g4 + v;
+      const int64_t j = 64 * jh + 16 * jb + l16;
+      const int64_t srow = 64 * (i / 32) + i % 32;
+      state_store(a, KREP, u, off[0][v], w0[0][v], m0[0][v], acc[jb][v], acc[4 + jb][v], cW, cM,
+                  cWM, 0, srow, j);
+      state_store(a, KREP, u, off[1][v], w0[1][v], m0[1][v], acc[8 + jb][v], acc[12 + jb][v],
+                  cW, cM, cWM, 0, srow + 32, j);
+      const int64_t j2 = 64 * jh + 16 * jb + 4 * g4 + v;
+      state_store(a, KREP, u, off[2][v], w0[2][v], m0[2][v], acc[16 + jb][v], acc[20 + jb][v],
+                  cW, cM, cWM, 1, j2, i_glob);
+    }
   }
-}
-
-inline size_t phaseB_lds_bytes(int krep) {
-  typedef PhaseBLds S;
-  const size_t ww = static_cast<size_t>(krep) * FD + 8;
-  const size_t bf = 3 * 32 * ww + 2 * S::TB * S::KW_ + 3 * FD * S::TW + 5 * 32 * S::TW;
-  return bf * sizeof(bf16_t) + (3 * S::TB * 33 + 2 * S::TB) * sizeof(float);
 }
 
 }  // namespace e2ttt

@@ -411,6 +411,8 @@ __global__ __launch_bounds__(256) void k_fwd2(Shape s, int r, const T* __restric
   const T* vs = v + (u * s.L + tok0) * s.d;
   const float* kwr = kw + (u * s.nC + r) * s.Cp;
   const float* kmr = km + (u * s.nC + r) * s.Cp;
+  // Loads first (v, kernels), then the stores: grow may alias v as far as the
+  // compiler knows, so interleaving would serialise every element.
   float gW[2][2][16], gM[2][2][16];
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
@@ -420,11 +422,28 @@ __global__ __launch_bounds__(256) void k_fwd2(Shape s, int r, const T* __restric
       for (int vv = 0; vv < 16; ++vv) {
         const int64_t p = p0 + ps.row(mi, vv);
         const int64_t i = nt * 128 + ps.col(ni);
-        const float vin = p < nv ? to_f32<T>(vs[p * s.d + i]) : 0.0f;
-        const float g = vin - acc[mi][ni][vv];
+        gW[mi][ni][vv] = p < nv ? to_f32<T>(vs[p * s.d + i]) : 0.0f;
+      }
+  float kwv[2][16], kmv[2][16];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int vv = 0; vv < 16; ++vv) {
+      kwv[mi][vv] = kwr[p0 + ps.row(mi, vv)];
+      kmv[mi][vv] = kmr[p0 + ps.row(mi, vv)];
+    }
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int vv = 0; vv < 16; ++vv) {
+        const int64_t p = p0 + ps.row(mi, vv);
+        const int64_t i = nt * 128 + ps.col(ni);
+        const float g = gW[mi][ni][vv] - acc[mi][ni][vv];
         grow[(u * s.Cp + p) * s.d + i] = from_f32<T>(g);
-        gW[mi][ni][vv] = kwr[p] * g;
-        gM[mi][ni][vv] = kmr[p] * g;
+        gW[mi][ni][vv] = kwv[mi][vv] * g;
+        gM[mi][ni][vv] = kmv[mi][vv] * g;
       }
   // gt row of d-index i: 64*(i/32) + i%32 (+32 for the momentum copy)
   T* gbase = gt + u * 2 * s.d * s.Cp + p0;
@@ -545,6 +564,9 @@ __global__ __launch_bounds__(256) void k_agg(Shape s, int r, int last, const T* 
   float* mo = Mout + u * P;
   const AccPos ps;
   const int64_t blk64 = mt * 2 + ps.wm;  // 64-row block: rows 0-31 W part, 32-63 M part
+  // Offsets and start values first, then the stores (W_end may be W_0).
+  int64_t offs[2][16];
+  float w0v[2][16], m0v[2][16];
 #pragma unroll
   for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
@@ -560,9 +582,17 @@ __global__ __launch_bounds__(256) void k_agg(Shape s, int r, int last, const T* 
         const int64_t j = nt * 128 + ps.col(ni);
         off = 2 * h * d + i * h + j;
       }
-      const float w0 = wi[off], m0 = mi_[off];
-      const float wn = cW * w0 + cWM * m0 + acc[0][ni][vv];
-      const float mn = cM * m0 + acc[1][ni][vv];
+      offs[ni][vv] = off;
+      w0v[ni][vv] = wi[off];
+      m0v[ni][vv] = mi_[off];
+    }
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+    for (int vv = 0; vv < 16; ++vv) {
+      const int64_t off = offs[ni][vv];
+      const float wn = cW * w0v[ni][vv] + cWM * m0v[ni][vv] + acc[0][ni][vv];
+      const float mn = cM * m0v[ni][vv] + acc[1][ni][vv];
       wo[off] = wn;
       mo[off] = mn;
       if (!last) write_shadow<T>(s, u, off, wn, w13s, w2s, w2ts);

@@ -240,7 +240,8 @@ void launch_swiglu(const Plan& q, const void* qv, const void* kv, const void* vv
   T* zt = reinterpret_cast<T*>(ws + q.zt);
 
   launch_scan(q, eta, alpha, beta, kw, km, q.nC * q.Cp, q.Cp, q.Cp, coef, 4, st, I);
-  E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, k_prep_kt<T>,
+  void (*kprep)(Shape, const T*, T*) = k_prep_kt<T, false>;
+  E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, kprep,
                dim3(grid1(q.BH * q.nC * (q.Cp / 64) * (q.d / 64))), dim3(256), 0, st, s, K, kt);
   E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, k_prep_shadow<T>, dim3(grid1((q.BH * q.P + 255) / 256)),
                dim3(256), 0, st, s, W0, w13s, w2s, w2ts);
@@ -289,7 +290,8 @@ void launch_fused(const Plan& q, const void* qv, const void* kv, const void* vv,
   launch_scan(q, eta, alpha, beta, reinterpret_cast<float*>(ws + q.kw),
               reinterpret_cast<float*>(ws + q.km), q.nC * q.Cp, q.Cp, q.Cp,
               reinterpret_cast<float*>(ws + q.coef), 4, st, I);
-  E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, k_prep_kt<bf16_t>,
+  void (*kprep)(Shape, const bf16_t*, bf16_t*) = k_prep_kt<bf16_t, true>;
+  E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, kprep,
                dim3(grid1(q.BH * q.nC * (q.Cp / 64) * (q.d / 64))), dim3(256), 0, st, s, a.k,
                reinterpret_cast<bf16_t*>(ws + q.kt));
   E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, k_prep_shadow<bf16_t>, dim3(grid1((q.BH * q.P + 255) / 256)),
@@ -308,7 +310,7 @@ void launch_fused(const Plan& q, const void* qv, const void* kv, const void* vv,
     void (*kB)(FusedArgs) = q.krep == 2 ? k_phaseB<2> : k_phaseB<1>;
     E2TTT_LAUNCH(I, E2TTT_KERNEL_PHASE_A, kA, dim3(gA), dim3(256), ldsA, st, a);
     const size_t ldsB = q.krep == 2 ? PhaseBCfg<2>::LDS_BYTES : PhaseBCfg<1>::LDS_BYTES;
-    E2TTT_LAUNCH(I, E2TTT_KERNEL_PHASE_B, kB, dim3(gB), dim3(512), ldsB, st, a);
+    E2TTT_LAUNCH(I, E2TTT_KERNEL_PHASE_B, kB, dim3(gB), dim3(256), ldsB, st, a);
   }
 }
 

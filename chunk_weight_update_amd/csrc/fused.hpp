@@ -12,7 +12,8 @@
 //   Y += Z W2[:, block]^T.  Q rows: the readout o = Y (Eq. 6).  K rows: the
 //   activation gradient g = v - Y, written as bf16 token-major (operand of
 //   the backward) and as K^W g, K^M g feature-major (operands of the W2
-//   aggregation), each rounded once from fp32.
+//   aggregation), each rounded once from fp32.  Feature-major buffers keep
+//   the token order of tok_perm32 inside each group of 32 tokens.
 // Phase B (k_phaseB): one workgroup per block of 64 hidden units of one unit;
 //   wave w owns 16 hidden units i.  Hidden unit i owns row i of W1 and W3 and
 //   column i of W2, so waves and workgroups write disjoint state.  Per tile
@@ -32,6 +33,7 @@
 //   operand shadows are written at the end.
 #pragma once
 #include "common.hpp"
+#include "kernels.hpp"
 
 namespace e2ttt {
 
@@ -311,8 +313,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       const float vin = p < nv ? bf2f(vsrc[p * FD + j]) : 0.0f;
       const float g = vin - yacc[i][v];
       gdst[p * FD + j] = f2bf(g);
-      TW_[j * P::GW + pr] = f2bf(sw * g);
-      TM_[j * P::GW + pr] = f2bf(sm * g);
+      TW_[j * P::GW + tok_perm32(pr)] = f2bf(sw * g);
+      TM_[j * P::GW + tok_perm32(pr)] = f2bf(sm * g);
     }
   }
   __syncthreads();
@@ -327,9 +329,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 }
 
 // ---------------------------------------------------------------------------
-// Phase B.  LDS: the recompute weights of the workgroup's 64 hidden units
-// ([4 waves][W1, W3, W2^T][16][KREP*FD + 8]), then NBUF token-tile buffers
-// (two for KREP = 1, one for the hi/lo variant, which needs twice the weights).
+// Phase B.  LDS: for the hi/lo variant (KREP = 2) the recompute weights of
+// the workgroup's 64 hidden units ([4 waves][W1, W3, W2^T][16][KREP*FD + 8]);
+// with KREP = 1 they live in registers.  Then NBUF token-tile buffers (two
+// for KREP = 1, one for the hi/lo variant).
 template <int KREP> struct PhaseBCfg {
   static constexpr int TB = 32;               // tokens per tile
   static constexpr int KS = FD + 8;           // token-major tile row stride
@@ -337,7 +340,8 @@ template <int KREP> struct PhaseBCfg {
   static constexpr int WS = KREP * FD + 8;    // weight row stride
   static constexpr int NBUF = KREP == 1 ? 2 : 1;
   static constexpr int BUF_ELEMS = 2 * TB * KS + 3 * FD * TS;  // K, g | K^T, K^W g, K^M g
-  static constexpr size_t W_BYTES = static_cast<size_t>(4 * 3 * 16 * WS) * sizeof(bf16_t);
+  static constexpr size_t W_BYTES =
+      KREP == 1 ? 0 : static_cast<size_t>(4 * 3 * 16 * WS) * sizeof(bf16_t);
   static constexpr size_t BUF_BYTES = BUF_ELEMS * sizeof(bf16_t) + 2 * TB * sizeof(float);
   static constexpr size_t LDS_BYTES = W_BYTES + NBUF * BUF_BYTES;
   static_assert((BUF_ELEMS * sizeof(bf16_t)) % 16 == 0, "buffer alignment");
@@ -391,16 +395,20 @@ __device__ __forceinline__ void state_store(const FusedArgs& a, int krep, int64_
   }
 }
 
+// Phase B: 4 waves (one per SIMD), wave w owns hidden units
+// 64*ib + 16*w .. +15 for all FD output columns.  The recompute weights of
+// the wave's hidden units stay in registers (KREP = 1) or are read from LDS
+// per tile (KREP = 2).  Fragments of the next step are read from LDS before
+// the MFMAs of the current step are issued.
 template <int KREP>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_phaseB(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_phaseB(
     FusedArgs a) {
   typedef PhaseBCfg<KREP> S;
   constexpr int TB = S::TB, KS = S::KS, TS = S::TS, WS = S::WS;
-  constexpr int NT = 512;                 // 8 waves
+  constexpr int NT = 256;
   constexpr int KSTEPS = KREP * FD / 32;  // recompute k-steps (16x16x32)
+  constexpr bool WREG = KREP == 1;        // weights in registers
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  // Weights first, then buffer b: bf16 tiles, then 2*TB floats of kernels.
-  // Selected arithmetically so LDS accesses stay ds_* ops.
   bf16_t* Wl = reinterpret_cast<bf16_t*>(smem_raw);
   auto bufp = [&](int b) -> bf16_t* {
     return reinterpret_cast<bf16_t*>(smem_raw + S::W_BYTES + b * S::BUF_BYTES);
@@ -416,35 +424,47 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   const int64_t tok0 = static_cast<int64_t>(a.r) * a.C;
   const int64_t nv = fused_nvalid(a);
   const int wave = threadIdx.x >> 6;
-  const int hg = wave >> 1;   // hidden group: 16 hidden units
-  const int jh = wave & 1;    // half of the output columns j (64 each)
   const int lane = threadIdx.x & 63;
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int64_t i_glob = 64 * ib + 16 * hg + l16;  // this lane's hidden unit (B column)
+  const int64_t i_glob = 64 * ib + 16 * wave + l16;  // this lane's hidden unit (B column)
 
-  // Recompute B operands of the workgroup's 64 hidden units (row = hidden
-  // unit, k = d; hi/lo halves when KREP = 2) into LDS: [group][q][16][WS].
+  // Recompute B operands: row = hidden unit, k = d (hi | lo when KREP = 2).
+  bf16x8_t wreg[3][WREG ? KSTEPS : 1];
   {
     const bf16_t* w13 = a.w13s + u * 2 * a.h * (KREP * FD);
     const bf16_t* w2t = a.w2ts + u * a.h * (KREP * FD);
-    TileCopy<4 * 3 * 16, KREP * FD, NT> cw;
-    cw.load([&](int rr) -> const bf16_t* {
-      const int grp = rr / 48, q = (rr / 16) % 3, il = rr % 16;
-      const int64_t i = 64 * ib + 16 * grp + il;
-      if (q == 2) return w2t + i * (KREP * FD);
-      return w13 + (64 * (i / 32) + (q == 1 ? 32 : 0) + i % 32) * (KREP * FD);
-    });
-    cw.store(Wl, WS);
-  }
-  const bf16_t* Wq = Wl + hg * 3 * 16 * WS;  // this wave's [3][16][WS]
-
-  // Accumulators (16x16 blocks over this wave's 16 hidden units and its 64
-  // columns j): [0..3] A^W_W1 (rows i, cols j block), [4..7] A^M_W1,
-  // [8..11] A^W_W3, [12..15] A^M_W3, [16..19] A^W_W2 (rows j block, cols i),
-  // [20..23] A^M_W2.
-  f32x4_t acc[24];
+    if (WREG) {
+      const bf16_t* w1r = w13 + (64 * (i_glob / 32) + i_glob % 32) * (KREP * FD);
+      const bf16_t* w2r = a.w2ts + (u * a.h + i_glob) * (KREP * FD);
 #pragma unroll
-  for (int q = 0; q < 24; ++q) zero4(acc[q]);
+      for (int ks = 0; ks < (WREG ? KSTEPS : 1); ++ks) {
+        wreg[0][ks] = *reinterpret_cast<const bf16x8_t*>(w1r + ks * 32 + g4 * 8);
+        wreg[1][ks] = *reinterpret_cast<const bf16x8_t*>(w1r + 32 * (KREP * FD) + ks * 32 + g4 * 8);
+        wreg[2][ks] = *reinterpret_cast<const bf16x8_t*>(w2r + ks * 32 + g4 * 8);
+      }
+    } else {
+      TileCopy<4 * 3 * 16, KREP * FD, NT> cw;
+      cw.load([&](int rr) -> const bf16_t* {
+        const int grp = rr / 48, q = (rr / 16) % 3, il = rr % 16;
+        const int64_t i = 64 * ib + 16 * grp + il;
+        if (q == 2) return w2t + i * (KREP * FD);
+        return w13 + (64 * (i / 32) + (q == 1 ? 32 : 0) + i % 32) * (KREP * FD);
+      });
+      cw.store(Wl, WS);
+    }
+  }
+  const bf16_t* Wq = Wl + wave * 3 * 16 * WS;  // this wave's [3][16][WS] (KREP = 2)
+  auto wfrag = [&](int q, int ks) -> bf16x8_t {
+    if (WREG) return wreg[q][WREG ? ks : 0];
+    return *reinterpret_cast<const bf16x8_t*>(Wq + (q * 16 + l16) * WS + ks * 32 + g4 * 8);
+  };
+
+  // Accumulators (16x16 blocks): [0..7] A^W_W1 (rows i of this wave, cols j
+  // block jb), [8..15] A^M_W1, [16..23] A^W_W3, [24..31] A^M_W3,
+  // [32..39] A^W_W2 (rows j block jb, cols i), [40..47] A^M_W2.
+  f32x4_t acc[48];
+#pragma unroll
+  for (int q = 0; q < 48; ++q) zero4(acc[q]);
 
   const bf16_t* Kg = a.k + (u * a.L + tok0) * FD;
   const bf16_t* Gg = a.gbf + u * a.Cp * FD;
@@ -455,7 +475,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   const float* kmr = a.km + (u * a.nC + a.r) * a.Cp;
 
   TileCopy<TB, FD, NT> ck, cg;          // token-major K, bf16(g)
-  TileCopy<FD, TB, NT> ckt, cgw, cgm;   // feature-major K^T, K^W g, K^M g
+  TileCopy<FD, TB, NT> ckt, cgw, cgm;   // feature-major (permuted tokens) K^T, K^W g, K^M g
   float sk = 0.0f;
   auto load_tile = [&](int64_t t0) {
     ck.load([&](int rr) -> const bf16_t* { return t0 + rr < nv ? Kg + (t0 + rr) * FD : nullptr; },
@@ -490,7 +510,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     const bf16_t* GWs = KTs + FD * TS;
     const bf16_t* GMs = KTs + 2 * FD * TS;
     const float* kws = kscp(b);
-    const float* kms = kws + TB;
 
     // Recompute: rows = tokens (2 blocks of 16), cols = this wave's 16 hidden.
     f32x4_t ra1[2], ra3[2], rdz[2];
@@ -499,56 +518,73 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       zero4(ra1[tb]);
       zero4(ra3[tb]);
       zero4(rdz[tb]);
+    }
+    {
+      constexpr int NSTEP = 2 * KSTEPS;
+      auto kfrag = [&](const bf16_t* base, int n) {
+        const int tb = n / KSTEPS, ks = n % KSTEPS;
+        return *reinterpret_cast<const bf16x8_t*>(base + (tb * 16 + l16) * KS + g4 * 8 +
+                                                  (ks * 32) % FD);
+      };
+      bf16x8_t fk = kfrag(Ks, 0), fg = kfrag(Gs, 0);
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int ko = (ks * 32) % FD;
-        const bf16x8_t fk = *reinterpret_cast<const bf16x8_t*>(Ks + (tb * 16 + l16) * KS + g4 * 8 + ko);
-        const bf16x8_t fg = *reinterpret_cast<const bf16x8_t*>(Gs + (tb * 16 + l16) * KS + g4 * 8 + ko);
-        const bf16_t* wr = Wq + l16 * WS + ks * 32 + g4 * 8;
-        ra1[tb] = mfma16(fk, *reinterpret_cast<const bf16x8_t*>(wr), ra1[tb]);
-        ra3[tb] = mfma16(fk, *reinterpret_cast<const bf16x8_t*>(wr + 16 * WS), ra3[tb]);
-        rdz[tb] = mfma16(fg, *reinterpret_cast<const bf16x8_t*>(wr + 32 * WS), rdz[tb]);
+      for (int n = 0; n < NSTEP; ++n) {
+        const int tb = n / KSTEPS, ks = n % KSTEPS;
+        bf16x8_t fk_n = fk, fg_n = fg;
+        if (n + 1 < NSTEP) {
+          fk_n = kfrag(Ks, n + 1);
+          fg_n = kfrag(Gs, n + 1);
+        }
+        ra1[tb] = mfma16(fk, wfrag(0, ks), ra1[tb]);
+        ra3[tb] = mfma16(fk, wfrag(1, ks), ra3[tb]);
+        rdz[tb] = mfma16(fg, wfrag(2, ks), rdz[tb]);
+        fk = fk_n;
+        fg = fg_n;
       }
     }
     // Elementwise; fragment slot s <-> token 16*(s/4) + 4*g4 + s%4.
     bf16x8_t fW1, fM1, fW3, fM3, fZ;
-    {
-      const f32x4_t kw0 = *reinterpret_cast<const f32x4_t*>(kws + 4 * g4);
-      const f32x4_t kw1 = *reinterpret_cast<const f32x4_t*>(kws + 16 + 4 * g4);
-      const f32x4_t km0 = *reinterpret_cast<const f32x4_t*>(kms + 4 * g4);
-      const f32x4_t km1 = *reinterpret_cast<const f32x4_t*>(kms + 16 + 4 * g4);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int tb = s >> 2, v = s & 3;
-        const float x1 = ra1[tb][v], x3 = ra3[tb][v], dz = rdz[tb][v];
-        const float sg = sigmoidf_(x1);
-        const float d3 = dz * (x1 * sg);
-        const float d1 = dz * x3 * (sg * (1.0f + x1 * (1.0f - sg)));
-        const float sw = tb ? kw1[v] : kw0[v];
-        const float sm = tb ? km1[v] : km0[v];
-        fW1[s] = static_cast<__bf16>(sw * d1);
-        fM1[s] = static_cast<__bf16>(sm * d1);
-        fW3[s] = static_cast<__bf16>(sw * d3);
-        fM3[s] = static_cast<__bf16>(sm * d3);
-        fZ[s] = static_cast<__bf16>(x1 * sg * x3);
-      }
+    for (int s = 0; s < 8; ++s) {
+      const int tb = s >> 2, v = s & 3;
+      const int t = 16 * tb + 4 * g4 + v;
+      const float x1 = ra1[tb][v], x3 = ra3[tb][v], dz = rdz[tb][v];
+      const float sg = sigmoidf_(x1);
+      const float d3 = dz * (x1 * sg);
+      const float d1 = dz * x3 * (sg * (1.0f + x1 * (1.0f - sg)));
+      const float sw = kws[t], sm = kws[TB + t];
+      fW1[s] = static_cast<__bf16>(sw * d1);
+      fM1[s] = static_cast<__bf16>(sm * d1);
+      fW3[s] = static_cast<__bf16>(sw * d3);
+      fM3[s] = static_cast<__bf16>(sm * d3);
+      fZ[s] = static_cast<__bf16>(x1 * sg * x3);
     }
-    // Aggregations over the tile's 32 tokens for this wave's 64 columns.
+    // Aggregations over the tile's 32 tokens: partner fragments (one 16-byte
+    // read each thanks to the permuted token order) of block jb+1 are read
+    // while block jb's six MFMAs issue.
+    {
+      auto pfrag = [&](const bf16_t* base, int jb) {
+        return *reinterpret_cast<const bf16x8_t*>(base + (jb * 16 + l16) * TS + 8 * g4);
+      };
+      bf16x8_t fk = pfrag(KTs, 0), fgw = pfrag(GWs, 0), fgm = pfrag(GMs, 0);
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      const int jr = 64 * jh + 16 * jb + l16;  // partner-operand row (feature j)
-      const bf16_t* pk = KTs + jr * TS + 4 * g4;
-      const bf16_t* pw = GWs + jr * TS + 4 * g4;
-      const bf16_t* pm = GMs + jr * TS + 4 * g4;
-      const bf16x8_t fk = frag_2x4(pk, pk + 16);
-      const bf16x8_t fgw = frag_2x4(pw, pw + 16);
-      const bf16x8_t fgm = frag_2x4(pm, pm + 16);
-      acc[jb] = mfma16(fW1, fk, acc[jb]);
-      acc[4 + jb] = mfma16(fM1, fk, acc[4 + jb]);
-      acc[8 + jb] = mfma16(fW3, fk, acc[8 + jb]);
-      acc[12 + jb] = mfma16(fM3, fk, acc[12 + jb]);
-      acc[16 + jb] = mfma16(fgw, fZ, acc[16 + jb]);
-      acc[20 + jb] = mfma16(fgm, fZ, acc[20 + jb]);
+      for (int jb = 0; jb < FD / 16; ++jb) {
+        bf16x8_t fk_n = fk, fgw_n = fgw, fgm_n = fgm;
+        if (jb + 1 < FD / 16) {
+          fk_n = pfrag(KTs, jb + 1);
+          fgw_n = pfrag(GWs, jb + 1);
+          fgm_n = pfrag(GMs, jb + 1);
+        }
+        acc[jb] = mfma16(fW1, fk, acc[jb]);
+        acc[8 + jb] = mfma16(fM1, fk, acc[8 + jb]);
+        acc[16 + jb] = mfma16(fW3, fk, acc[16 + jb]);
+        acc[24 + jb] = mfma16(fM3, fk, acc[24 + jb]);
+        acc[32 + jb] = mfma16(fgw, fZ, acc[32 + jb]);
+        acc[40 + jb] = mfma16(fgm, fZ, acc[40 + jb]);
+        fk = fk_n;
+        fgw = fgw_n;
+        fgm = fgm_n;
+      }
     }
     if (S::NBUF == 1) __syncthreads();  // single buffer: everyone is done reading it
     if (it + 1 < ntiles) {
@@ -558,26 +594,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     __syncthreads();
   }
 
-  // Chunk-end state and operand shadows of this wave's entries, in batches of
-  // one 16-column block: all start values first, then the stores.
+  // Chunk-end state and operand shadows of this wave's hidden units, in
+  // batches of one 16-column block: all start values first, then the stores.
   const float* cf = a.coef + (u * a.nC + a.r) * 4;
   const float cW = cf[0], cM = cf[1], cWM = cf[2];
   const int64_t P = 3 * FD * a.h;
   const float* __restrict__ Wi = a.Win + u * P;
   const float* __restrict__ Mi = a.Min + u * P;
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb) {
+  for (int jb = 0; jb < FD / 16; ++jb) {
     int64_t off[3][4];
     float w0[3][4], m0[3][4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      // W1/W3: rows i = 16*hg + 4*g4 + v (hidden), col j = 64*jh + 16*jb + l16
-      const int64_t i = 64 * ib + 16 * hg + 4 * g4 + v;
-      const int64_t j = 64 * jh + 16 * jb + l16;
+      // W1/W3: rows i = 16*wave + 4*g4 + v (hidden), col j = 16*jb + l16
+      const int64_t i = 64 * ib + 16 * wave + 4 * g4 + v;
+      const int64_t j = 16 * jb + l16;
       off[0][v] = i * FD + j;
       off[1][v] = a.h * FD + i * FD + j;
-      // W2: rows j2 = 64*jh + 16*jb + 4*g4 + v, col = this lane's hidden unit
-      off[2][v] = 2 * a.h * FD + (64 * jh + 16 * jb + 4 * g4 + v) * a.h + i_glob;
+      // W2: rows j2 = 16*jb + 4*g4 + v, col = this lane's hidden unit
+      off[2][v] = 2 * a.h * FD + (16 * jb + 4 * g4 + v) * a.h + i_glob;
     }
 #pragma unroll
     for (int t = 0; t < 3; ++t)
@@ -588,15 +624,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       }
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int64_t i = 64 * ib + 16 * hg + 4 * g4 + v;
-      const int64_t j = 64 * jh + 16 * jb + l16;
+      const int64_t i = 64 * ib + 16 * wave + 4 * g4 + v;
+      const int64_t j = 16 * jb + l16;
       const int64_t srow = 64 * (i / 32) + i % 32;
-      state_store(a, KREP, u, off[0][v], w0[0][v], m0[0][v], acc[jb][v], acc[4 + jb][v], cW, cM,
+      state_store(a, KREP, u, off[0][v], w0[0][v], m0[0][v], acc[jb][v], acc[8 + jb][v], cW, cM,
                   cWM, 0, srow, j);
-      state_store(a, KREP, u, off[1][v], w0[1][v], m0[1][v], acc[8 + jb][v], acc[12 + jb][v],
+      state_store(a, KREP, u, off[1][v], w0[1][v], m0[1][v], acc[16 + jb][v], acc[24 + jb][v],
                   cW, cM, cWM, 0, srow + 32, j);
-      const int64_t j2 = 64 * jh + 16 * jb + 4 * g4 + v;
-      state_store(a, KREP, u, off[2][v], w0[2][v], m0[2][v], acc[16 + jb][v], acc[20 + jb][v],
+      const int64_t j2 = 16 * jb + 4 * g4 + v;
+      state_store(a, KREP, u, off[2][v], w0[2][v], m0[2][v], acc[32 + jb][v], acc[40 + jb][v],
                   cW, cM, cWM, 1, j2, i_glob);
     }
   }

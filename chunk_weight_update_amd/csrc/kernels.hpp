@@ -215,10 +215,22 @@ __global__ __launch_bounds__(64) void k_scan(const float* __restrict__ eta,
 }
 
 // ---------------------------------------------------------------------------
-// K of every chunk, feature-major: kt[u][r][c][p] = k[u][r*C + p][c] (zero
-// for rows past the chunk's valid tokens).  64x64 tiles through LDS.
-template <typename T>
-__global__ __launch_bounds__(256) void k_prep_kt(Shape s, const T* __restrict__ k, T* kt) {
+// K of every chunk, feature-major: kt[u][r][c][p'] = k[u][r*C + p][c] (zero
+// for rows past the chunk's valid tokens).  With PERM, the token position p'
+// is permuted inside each group of 32 tokens so that the 8 tokens one lane
+// feeds to a 16x16x32 MFMA (tokens 4g..4g+3 and 16+4g..16+4g+3 of the group)
+// are contiguous: p' = 8*((p%16)/4) + 4*((p%32)/16) + p%4.  64x64 tiles
+// through LDS, all global accesses 16-byte vectors.
+__host__ __device__ constexpr int tok_perm32(int p) {
+  return (p & ~31) + 8 * ((p & 15) >> 2) + 4 * ((p & 31) >> 4) + (p & 3);
+}
+
+template <typename T, bool PERM>
+__global__ __launch_bounds__(256) void k_prep_kt(Shape s, const T* __restrict__ k,
+                                                 T* __restrict__ kt) {
+  constexpr int VE = 16 / sizeof(T);            // elements per 16-byte vector
+  constexpr int NV = 64 * 64 / VE;              // vectors per 64x64 tile
+  constexpr int PER = NV / 256;
   __shared__ T tile[64][64 + 1];
   const int64_t ptiles = s.Cp / 64, ctiles = s.d / 64;
   int64_t bid = blockIdx.x;
@@ -227,17 +239,35 @@ __global__ __launch_bounds__(256) void k_prep_kt(Shape s, const T* __restrict__ 
   const int r = static_cast<int>(bid % s.nC);
   const int64_t u = bid / s.nC;
   const int64_t nv = n_valid(s, r);
-  const T* ks = k + (u * s.L + static_cast<int64_t>(r) * s.C) * s.d;
-  for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
-    const int pr = idx / 64, cc = idx % 64;
+  const T* ks = k + (u * s.L + static_cast<int64_t>(r) * s.C) * s.d + ct * 64;
+  uint4 reg[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {  // 64 token rows x (64 / VE) vectors
+    const int idx = threadIdx.x + 256 * i;
+    const int pr = idx / (64 / VE), cv = idx % (64 / VE);
     const int64_t p = pt * 64 + pr;
-    tile[pr][cc] = p < nv ? ks[p * s.d + ct * 64 + cc] : from_f32<T>(0.0f);
+    const uint4 val = *reinterpret_cast<const uint4*>(ks + (p < nv ? p : 0) * s.d + cv * VE);
+    reg[i] = p < nv ? val : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = threadIdx.x + 256 * i;
+    const int pr = idx / (64 / VE), cv = idx % (64 / VE);
+    const int pos = PERM ? tok_perm32(pr) : pr;
+    const T* e = reinterpret_cast<const T*>(&reg[i]);
+#pragma unroll
+    for (int x = 0; x < VE; ++x) tile[cv * VE + x][pos] = e[x];
   }
   __syncthreads();
   T* dst = kt + ((u * s.nC + r) * s.d + ct * 64) * s.Cp + pt * 64;
-  for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
-    const int cr = idx / 64, pc = idx % 64;
-    dst[cr * s.Cp + pc] = tile[pc][cr];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {  // 64 feature rows x (64 / VE) vectors
+    const int idx = threadIdx.x + 256 * i;
+    const int cr = idx / (64 / VE), pv = idx % (64 / VE);
+    T vals[VE];
+#pragma unroll
+    for (int x = 0; x < VE; ++x) vals[x] = tile[cr][pv * VE + x];
+    *reinterpret_cast<uint4*>(dst + cr * s.Cp + pv * VE) = *reinterpret_cast<const uint4*>(vals);
   }
 }
 

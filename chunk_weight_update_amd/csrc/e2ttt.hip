@@ -31,8 +31,8 @@ struct Plan {
   int rbA;      // phase A rows per workgroup (32 or 64)
   size_t opsz;  // bytes per GEMM operand element (2 for bf16, 4 for fp32)
   // workspace offsets (bytes)
-  size_t kw, km, coef, kt, w13s, w2s, w2ts, zrow, a1s, a3s, grow, ut, gt, zt, gw, gm, gbf, gtw,
-      gtm, total;
+  size_t kw, km, coef, kt, w13s, w2s, w2ts, zrow, a1s, a3s, grow, ut, gt, zt, gw, gm, gbf, gft,
+      total;
 };
 
 e2ttt_status check_problem(const e2ttt_problem* p) {
@@ -105,8 +105,7 @@ e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
     q.w2ts = take(T * q.BH * q.h * q.krep * q.d);
     q.kt = take(T * q.BH * q.nC * q.d * q.Cp);
     q.gbf = take(T * q.BH * q.Cp * q.d);
-    q.gtw = take(T * q.BH * q.d * q.Cp);
-    q.gtm = take(T * q.BH * q.d * q.Cp);
+    q.gft = take(T * q.BH * q.d * q.Cp);
   } else {
     q.Cp = (q.C + 127) / 128 * 128;
     q.opsz = q.io == E2TTT_BF16 ? 2 : 4;
@@ -165,8 +164,6 @@ std::atomic<int> g_attr_done{0};
 
 void set_lds_attributes() {
   if (g_attr_done.load(std::memory_order_acquire)) return;
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_scan),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lin_fwd<float>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lin_fwd<bf16_t>),
@@ -209,8 +206,7 @@ struct Instr {
 void launch_scan(const Plan& q, const float* eta, const float* alpha, const float* beta,
                  float* kw, float* km, int64_t ustride, int64_t rstride, int64_t pad,
                  float* coef, int cstride, hipStream_t st, Instr& I) {
-  const size_t lds = static_cast<size_t>(3 * q.C) * sizeof(float);
-  E2TTT_LAUNCH(I, E2TTT_KERNEL_SCAN, k_scan, dim3(grid1(q.BH * q.nC)), dim3(64), lds, st, eta,
+  E2TTT_LAUNCH(I, E2TTT_KERNEL_SCAN, k_scan, dim3(grid1(q.BH * q.nC)), dim3(SCAN_NT), 0, st, eta,
                alpha, beta, q.L, q.C, q.nC, q.mode, kw, km, ustride, rstride, pad, coef, cstride);
 }
 
@@ -282,8 +278,7 @@ void launch_fused(const Plan& q, const void* qv, const void* kv, const void* vv,
   a.w2ts = reinterpret_cast<bf16_t*>(ws + q.w2ts);
   a.kt = reinterpret_cast<const bf16_t*>(ws + q.kt);
   a.gbf = reinterpret_cast<bf16_t*>(ws + q.gbf);
-  a.gtw = reinterpret_cast<bf16_t*>(ws + q.gtw);
-  a.gtm = reinterpret_cast<bf16_t*>(ws + q.gtm);
+  a.gft = reinterpret_cast<bf16_t*>(ws + q.gft);
   a.Wout = Wend;
   a.Mout = Mend;
   Shape s{q.BH, q.L, q.d, q.h, q.C, q.Cp, q.nC, q.krep};

@@ -10,25 +10,26 @@
 //   (batch, head) unit.  It streams the hidden units in blocks: A1, A3 of the
 //   block (MFMA against the W1/W3 operand shadow), Z = silu(A1) * A3 in LDS,
 //   Y += Z W2[:, block]^T.  Q rows: the readout o = Y (Eq. 6).  K rows: the
-//   activation gradient g = v - Y, written as bf16 token-major (operand of
-//   the backward) and as K^W g, K^M g feature-major (operands of the W2
-//   aggregation), each rounded once from fp32.  Feature-major buffers keep
-//   the token order of tok_perm32 inside each group of 32 tokens.
+//   activation gradient g = v - Y, rounded once to bf16 and written
+//   token-major (operand of the backward) and feature-major (operand of the
+//   W2 aggregation).  Feature-major buffers keep the token order of
+//   tok_perm32 inside each group of 32 tokens.
 // Phase B (k_phaseB): one workgroup per block of 64 hidden units of one unit;
 //   wave w owns 16 hidden units i.  Hidden unit i owns row i of W1 and W3 and
 //   column i of W2, so waves and workgroups write disjoint state.  Per tile
 //   of 32 tokens a wave recomputes A1, A3 = K W1[i]^T, K W3[i]^T and
 //   dZ = g W2[:, i] (16x16x32 MFMAs), forms dA1 = dZ A3 silu'(A1),
 //   dA3 = dZ silu(A1), Z = silu(A1) A3 in registers, and feeds them without
-//   leaving registers into the aggregations over the tile's tokens:
+//   leaving registers into the aggregations over the tile's tokens, the
+//   per-token kernels folded into the register-side operand:
 //     A^W_{W1}[i,:] += (K^W dA1)^T K,  A^M_{W1}[i,:] += (K^M dA1)^T K
 //     A^W_{W3}[i,:], A^M_{W3}[i,:] likewise with dA3
-//     A^W_{W2}[:,i] += (K^W g)^T Z,   A^M_{W2}[:,i] += (K^M g)^T Z
+//     A^W_{W2}[:,i] += g^T (K^W Z),    A^M_{W2}[:,i] += g^T (K^M Z)
 //   This works because a 16x16 accumulator gives lane l the column l%16 and
 //   rows 4*(l/16)+v: a lane holds one hidden unit for 8 tokens of the tile,
 //   which is exactly an operand fragment of a 16x16x32 MFMA that contracts
-//   over tokens, once the partner operand (K or K^W g, feature-major in LDS)
-//   is read with the same token order.  The chunk-end state
+//   over tokens, once the partner operand (K or g, feature-major in LDS) is
+//   read with the same token order.  The chunk-end state
 //   W_C = cW W_0 + cWM M_0 + A^W, M_C = cM M_0 + A^M and the next chunk's
 //   operand shadows are written at the end.
 #pragma once
@@ -40,6 +41,15 @@ namespace e2ttt {
 constexpr int FD = 128;  // head dim of the fused path
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> one dword of two bf16 (round to nearest even), lo = a.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 struct FusedArgs {
@@ -62,8 +72,7 @@ struct FusedArgs {
   bf16_t* w2ts;       // [BH][h][KREP*FD]
   const bf16_t* kt;   // [BH][nC][FD][Cp]  K feature-major
   bf16_t* gbf;        // [BH][Cp][FD]      bf16(g), token-major
-  bf16_t* gtw;        // [BH][FD][Cp]      bf16(K^W g), feature-major
-  bf16_t* gtm;        // [BH][FD][Cp]      bf16(K^M g), feature-major
+  bf16_t* gft;        // [BH][FD][Cp]      bf16(g), feature-major
 };
 
 __device__ __forceinline__ int64_t fused_nvalid(const FusedArgs& a) {
@@ -291,13 +300,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       }
     return;
   }
-  const float* kwr = a.kw + (u * a.nC + a.r) * a.Cp;
-  const float* kmr = a.km + (u * a.nC + a.r) * a.Cp;
-  // g = v - Y; bf16 token-major directly; K^W g, K^M g feature-major through
-  // LDS (Xs/W13b are free now: [FD][RB + 8] each).  All loads first: the
-  // stores below could alias them as far as the compiler knows.
-  bf16_t* TW_ = W13b;                      // [FD][GW]
-  bf16_t* TM_ = W13b + FD * P::GW;          // [FD][GW]
+  // g = v - Y, rounded once to bf16: token-major directly, feature-major
+  // through LDS (W13b is free now: [FD][RB + 8]).
+  bf16_t* T_ = W13b;  // [FD][GW]
   // v is an input and gbf workspace: they never overlap (checked on the
   // host), which the restrict qualifiers pass on to the compiler.
   const bf16_t* __restrict__ vsrc = a.v + (u * a.L + tok0) * FD;
@@ -306,40 +311,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   for (int v = 0; v < 16; ++v) {
     const int pr = wm * 32 + acc32_row(v);
     const int64_t p = p0 + pr;
-    const float sw = kwr[p], sm = kmr[p];
 #pragma unroll
     for (int i = 0; i < P::YN / 32; ++i) {
       const int j = wn * P::YN + i * 32 + (threadIdx.x & 31);
       const float vin = p < nv ? bf2f(vsrc[p * FD + j]) : 0.0f;
-      const float g = vin - yacc[i][v];
-      gdst[p * FD + j] = f2bf(g);
-      TW_[j * P::GW + tok_perm32(pr)] = f2bf(sw * g);
-      TM_[j * P::GW + tok_perm32(pr)] = f2bf(sm * g);
+      const bf16_t g = f2bf(vin - yacc[i][v]);
+      gdst[p * FD + j] = g;
+      T_[j * P::GW + tok_perm32(pr)] = g;
     }
   }
   __syncthreads();
   constexpr int VPR = RB / 8;
   for (int idx = threadIdx.x; idx < FD * VPR; idx += 256) {
     const int j = idx / VPR, c = idx % VPR;
-    *reinterpret_cast<uint4*>(a.gtw + (u * FD + j) * a.Cp + p0 + c * 8) =
-        *reinterpret_cast<const uint4*>(TW_ + j * P::GW + c * 8);
-    *reinterpret_cast<uint4*>(a.gtm + (u * FD + j) * a.Cp + p0 + c * 8) =
-        *reinterpret_cast<const uint4*>(TM_ + j * P::GW + c * 8);
+    *reinterpret_cast<uint4*>(a.gft + (u * FD + j) * a.Cp + p0 + c * 8) =
+        *reinterpret_cast<const uint4*>(T_ + j * P::GW + c * 8);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Phase B.  LDS: for the hi/lo variant (KREP = 2) the recompute weights of
 // the workgroup's 64 hidden units ([4 waves][W1, W3, W2^T][16][KREP*FD + 8]);
-// with KREP = 1 they live in registers.  Then NBUF token-tile buffers (two
+// with KREP = 1 they live in registers.  Then NBUF token-tile buffers (three
 // for KREP = 1, one for the hi/lo variant).
 template <int KREP> struct PhaseBCfg {
   static constexpr int TB = 32;               // tokens per tile
   static constexpr int KS = FD + 8;           // token-major tile row stride
   static constexpr int TS = TB + 8;           // feature-major tile row stride
   static constexpr int WS = KREP * FD + 8;    // weight row stride
-  static constexpr int NBUF = KREP == 1 ? 2 : 1;
-  static constexpr int BUF_ELEMS = 2 * TB * KS + 3 * FD * TS;  // K, g | K^T, K^W g, K^M g
+  static constexpr int NBUF = KREP == 1 ? 3 : 1;
+  static constexpr int BUF_ELEMS = 2 * TB * KS + 2 * FD * TS;  // K, g | K^T, g^T
   static constexpr size_t W_BYTES =
       KREP == 1 ? 0 : static_cast<size_t>(4 * 3 * 16 * WS) * sizeof(bf16_t);
   static constexpr size_t BUF_BYTES = BUF_ELEMS * sizeof(bf16_t) + 2 * TB * sizeof(float);
@@ -469,172 +470,304 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const bf16_t* Kg = a.k + (u * a.L + tok0) * FD;
   const bf16_t* Gg = a.gbf + u * a.Cp * FD;
   const bf16_t* KTg = a.kt + (u * a.nC + a.r) * FD * a.Cp;
-  const bf16_t* GWg = a.gtw + u * FD * a.Cp;
-  const bf16_t* GMg = a.gtm + u * FD * a.Cp;
+  const bf16_t* GTg = a.gft + u * FD * a.Cp;
   const float* kwr = a.kw + (u * a.nC + a.r) * a.Cp;
   const float* kmr = a.km + (u * a.nC + a.r) * a.Cp;
 
   TileCopy<TB, FD, NT> ck, cg;          // token-major K, bf16(g)
-  TileCopy<FD, TB, NT> ckt, cgw, cgm;   // feature-major (permuted tokens) K^T, K^W g, K^M g
+  TileCopy<FD, TB, NT> ckt, cgt;        // feature-major (permuted tokens) K^T, g^T
   float sk = 0.0f;
   auto load_tile = [&](int64_t t0) {
     ck.load([&](int rr) -> const bf16_t* { return t0 + rr < nv ? Kg + (t0 + rr) * FD : nullptr; },
             Kg);
     cg.load([&](int rr) -> const bf16_t* { return Gg + (t0 + rr) * FD; });
     ckt.load([&](int rr) -> const bf16_t* { return KTg + rr * a.Cp + t0; });
-    cgw.load([&](int rr) -> const bf16_t* { return GWg + rr * a.Cp + t0; });
-    cgm.load([&](int rr) -> const bf16_t* { return GMg + rr * a.Cp + t0; });
-    if (threadIdx.x < 2 * TB)
-      sk = threadIdx.x < TB ? kwr[t0 + threadIdx.x] : kmr[t0 + threadIdx.x - TB];
+    cgt.load([&](int rr) -> const bf16_t* { return GTg + rr * a.Cp + t0; });
+    // Every wave loads (and stores) the same 2*TB kernel values, so no lane
+    // mask splits the loop body into several scheduling regions.
+    const int ks_i = threadIdx.x & (2 * TB - 1);
+    sk = (ks_i < TB ? kwr : kmr - TB)[t0 + ks_i];
   };
   auto store_tile = [&](int b) {
     bf16_t* B = bufp(b);
     ck.store(B, KS);
     cg.store(B + TB * KS, KS);
     ckt.store(B + 2 * TB * KS, TS);
-    cgw.store(B + 2 * TB * KS + FD * TS, TS);
-    cgm.store(B + 2 * TB * KS + 2 * FD * TS, TS);
-    if (threadIdx.x < 2 * TB) kscp(b)[threadIdx.x] = sk;
+    cgt.store(B + 2 * TB * KS + FD * TS, TS);
+    kscp(b)[threadIdx.x & (2 * TB - 1)] = sk;
   };
 
   const int ntiles = static_cast<int>(a.Cp / TB);
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
-    const int b = S::NBUF == 2 ? (it & 1) : 0;
-    if (it + 1 < ntiles) load_tile(static_cast<int64_t>(it + 1) * TB);
-    const bf16_t* Ks = bufp(b);
-    const bf16_t* Gs = Ks + TB * KS;
-    const bf16_t* KTs = Ks + 2 * TB * KS;
-    const bf16_t* GWs = KTs + FD * TS;
-    const bf16_t* GMs = KTs + 2 * FD * TS;
-    const float* kws = kscp(b);
 
-    // Recompute: rows = tokens (2 blocks of 16), cols = this wave's 16 hidden.
-    f32x4_t ra1[2], ra3[2], rdz[2];
+  // Recompute of one tile: rows = tokens (2 blocks of 16), cols = this
+  // wave's 16 hidden units; A1, A3 from K, dZ from g.
+  struct Rec {
+    f32x4_t a1[2], a3[2], dz[2];
+  };
+  auto recompute = [&](const bf16_t* Ks) -> Rec {
+    const bf16_t* Gs = Ks + TB * KS;
+    Rec rc;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      zero4(ra1[tb]);
-      zero4(ra3[tb]);
-      zero4(rdz[tb]);
+      zero4(rc.a1[tb]);
+      zero4(rc.a3[tb]);
+      zero4(rc.dz[tb]);
     }
-    {
-      constexpr int NSTEP = 2 * KSTEPS;
-      auto kfrag = [&](const bf16_t* base, int n) {
-        const int tb = n / KSTEPS, ks = n % KSTEPS;
-        return *reinterpret_cast<const bf16x8_t*>(base + (tb * 16 + l16) * KS + g4 * 8 +
-                                                  (ks * 32) % FD);
-      };
-      bf16x8_t fk = kfrag(Ks, 0), fg = kfrag(Gs, 0);
+    constexpr int NSTEP = 2 * KSTEPS;
+    auto kfrag = [&](const bf16_t* base, int n) {
+      const int tb = n / KSTEPS, ks = n % KSTEPS;
+      return *reinterpret_cast<const bf16x8_t*>(base + (tb * 16 + l16) * KS + g4 * 8 +
+                                                (ks * 32) % FD);
+    };
+    bf16x8_t fk = kfrag(Ks, 0), fg = kfrag(Gs, 0);
 #pragma unroll
-      for (int n = 0; n < NSTEP; ++n) {
-        const int tb = n / KSTEPS, ks = n % KSTEPS;
-        bf16x8_t fk_n = fk, fg_n = fg;
-        if (n + 1 < NSTEP) {
-          fk_n = kfrag(Ks, n + 1);
-          fg_n = kfrag(Gs, n + 1);
-        }
-        ra1[tb] = mfma16(fk, wfrag(0, ks), ra1[tb]);
-        ra3[tb] = mfma16(fk, wfrag(1, ks), ra3[tb]);
-        rdz[tb] = mfma16(fg, wfrag(2, ks), rdz[tb]);
-        fk = fk_n;
-        fg = fg_n;
+    for (int n = 0; n < NSTEP; ++n) {
+      const int tb = n / KSTEPS, ks = n % KSTEPS;
+      bf16x8_t fk_n = fk, fg_n = fg;
+      if (n + 1 < NSTEP) {
+        fk_n = kfrag(Ks, n + 1);
+        fg_n = kfrag(Gs, n + 1);
       }
+      rc.a1[tb] = mfma16(fk, wfrag(0, ks), rc.a1[tb]);
+      rc.a3[tb] = mfma16(fk, wfrag(1, ks), rc.a3[tb]);
+      rc.dz[tb] = mfma16(fg, wfrag(2, ks), rc.dz[tb]);
+      fk = fk_n;
+      fg = fg_n;
     }
-    // Elementwise; fragment slot s <-> token 16*(s/4) + 4*g4 + s%4.
-    bf16x8_t fW1, fM1, fW3, fM3, fZ;
+    return rc;
+  };
+  // Elementwise; fragment slot s <-> token 16*(s/4) + 4*g4 + s%4.
+  struct Frags {
+    bf16x8_t w1, m1, w3, m3, zw, zm;
+  };
+  auto elementwise = [&](const Rec& rc, const float* kws) -> Frags {
+    Frags f;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int tb = s >> 2, v = s & 3;
       const int t = 16 * tb + 4 * g4 + v;
-      const float x1 = ra1[tb][v], x3 = ra3[tb][v], dz = rdz[tb][v];
+      const float x1 = rc.a1[tb][v], x3 = rc.a3[tb][v], dz = rc.dz[tb][v];
       const float sg = sigmoidf_(x1);
       const float d3 = dz * (x1 * sg);
       const float d1 = dz * x3 * (sg * (1.0f + x1 * (1.0f - sg)));
       const float sw = kws[t], sm = kws[TB + t];
-      fW1[s] = static_cast<__bf16>(sw * d1);
-      fM1[s] = static_cast<__bf16>(sm * d1);
-      fW3[s] = static_cast<__bf16>(sw * d3);
-      fM3[s] = static_cast<__bf16>(sm * d3);
-      fZ[s] = static_cast<__bf16>(x1 * sg * x3);
+      const float z = x1 * sg * x3;
+      f.w1[s] = static_cast<__bf16>(sw * d1);
+      f.m1[s] = static_cast<__bf16>(sm * d1);
+      f.w3[s] = static_cast<__bf16>(sw * d3);
+      f.m3[s] = static_cast<__bf16>(sm * d3);
+      f.zw[s] = static_cast<__bf16>(sw * z);
+      f.zm[s] = static_cast<__bf16>(sm * z);
     }
-    // Aggregations over the tile's 32 tokens: partner fragments (one 16-byte
-    // read each thanks to the permuted token order) of block jb+1 are read
-    // while block jb's six MFMAs issue.
-    {
-      auto pfrag = [&](const bf16_t* base, int jb) {
-        return *reinterpret_cast<const bf16x8_t*>(base + (jb * 16 + l16) * TS + 8 * g4);
-      };
-      bf16x8_t fk = pfrag(KTs, 0), fgw = pfrag(GWs, 0), fgm = pfrag(GMs, 0);
+    return f;
+  };
+  // Aggregations over a tile's 32 tokens: partner fragments (one 16-byte
+  // read each thanks to the permuted token order) of block jb+1 are read
+  // while block jb's six MFMAs issue.
+  auto pfrag = [&](const bf16_t* base, int jb) {
+    return *reinterpret_cast<const bf16x8_t*>(base + (jb * 16 + l16) * TS + 8 * g4);
+  };
+  auto mma_block = [&](const Frags& f, int jb, const bf16x8_t& fk, const bf16x8_t& fg) {
+    acc[jb] = mfma16(f.w1, fk, acc[jb]);
+    acc[8 + jb] = mfma16(f.m1, fk, acc[8 + jb]);
+    acc[16 + jb] = mfma16(f.w3, fk, acc[16 + jb]);
+    acc[24 + jb] = mfma16(f.m3, fk, acc[24 + jb]);
+    acc[32 + jb] = mfma16(fg, f.zw, acc[32 + jb]);
+    acc[40 + jb] = mfma16(fg, f.zm, acc[40 + jb]);
+  };
+  auto aggregate = [&](const Frags& f, const bf16_t* Ks) {
+    const bf16_t* KTs = Ks + 2 * TB * KS;
+    const bf16_t* GTs = KTs + FD * TS;
+    bf16x8_t fk = pfrag(KTs, 0), fg = pfrag(GTs, 0);
 #pragma unroll
-      for (int jb = 0; jb < FD / 16; ++jb) {
-        bf16x8_t fk_n = fk, fgw_n = fgw, fgm_n = fgm;
-        if (jb + 1 < FD / 16) {
-          fk_n = pfrag(KTs, jb + 1);
-          fgw_n = pfrag(GWs, jb + 1);
-          fgm_n = pfrag(GMs, jb + 1);
-        }
-        acc[jb] = mfma16(fW1, fk, acc[jb]);
-        acc[8 + jb] = mfma16(fM1, fk, acc[8 + jb]);
-        acc[16 + jb] = mfma16(fW3, fk, acc[16 + jb]);
-        acc[24 + jb] = mfma16(fM3, fk, acc[24 + jb]);
-        acc[32 + jb] = mfma16(fgw, fZ, acc[32 + jb]);
-        acc[40 + jb] = mfma16(fgm, fZ, acc[40 + jb]);
-        fk = fk_n;
-        fgw = fgw_n;
-        fgm = fgm_n;
+    for (int jb = 0; jb < FD / 16; ++jb) {
+      bf16x8_t fk_n = fk, fg_n = fg;
+      if (jb + 1 < FD / 16) {
+        fk_n = pfrag(KTs, jb + 1);
+        fg_n = pfrag(GTs, jb + 1);
       }
+      mma_block(f, jb, fk, fg);
+      fk = fk_n;
+      fg = fg_n;
     }
-    if (S::NBUF == 1) __syncthreads();  // single buffer: everyone is done reading it
-    if (it + 1 < ntiles) {
-      // With two buffers, b^1 was last read in iteration it-1 (barrier since).
-      store_tile(S::NBUF == 2 ? (b ^ 1) : 0);
+  };
+
+  // aggregate() of tile it fused with elementwise() of tile it+1: step jb
+  // issues the six MFMAs of column block jb alternating with the VALU work
+  // of fragment slot jb of the next tile (8 slots, 8 blocks), and a
+  // scheduling fence after each step keeps the compiler from clustering the
+  // MFMAs, so the VALU work runs while the matrix core is busy.
+  auto aggregate_next = [&](const Frags& f, const bf16_t* Ks, const Rec& rc,
+                            const float* kws) -> Frags {
+    const bf16_t* KTs = Ks + 2 * TB * KS;
+    const bf16_t* GTs = KTs + FD * TS;
+    float sw[8], sm[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int t = 16 * (s >> 2) + 4 * g4 + (s & 3);
+      sw[s] = kws[t];
+      sm[s] = kws[TB + t];
+    }
+    // Packed bf16 pairs of the next tile's fragments: [output][slot pair].
+    u32x4_t pk[6];
+    float ev[6];  // even slot's values, packed with the odd slot after it
+    bf16x8_t fk = pfrag(KTs, 0), fg = pfrag(GTs, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int jb = 0; jb < FD / 16; ++jb) {
+      bf16x8_t fk_n = fk, fg_n = fg;
+      if (jb + 1 < FD / 16) {
+        fk_n = pfrag(KTs, jb + 1);
+        fg_n = pfrag(GTs, jb + 1);
+      }
+      mma_block(f, jb, fk, fg);
+      {
+        const int s = jb, tb = s >> 2, v = s & 3;
+        const float x1 = rc.a1[tb][v], x3 = rc.a3[tb][v], dz = rc.dz[tb][v];
+        const float sg = sigmoidf_(x1);
+        const float d3 = dz * (x1 * sg);
+        const float d1 = dz * x3 * (sg * (1.0f + x1 * (1.0f - sg)));
+        const float z = x1 * sg * x3;
+        float o[6] = {sw[s] * d1, sm[s] * d1, sw[s] * d3, sm[s] * d3, sw[s] * z, sm[s] * z};
+        if ((s & 1) == 0) {
+#pragma unroll
+          for (int q = 0; q < 6; ++q) {
+            ev[q] = o[q];
+            // Pin the value here: pure arithmetic would otherwise be sunk
+            // to its use after the last block, out of the MFMA shadow.
+            asm volatile("" : "+v"(ev[q]));
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 6; ++q) {
+            uint32_t w = pack_bf16x2(ev[q], o[q]);
+            asm volatile("" : "+v"(w));
+            pk[q][s >> 1] = w;
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < 6; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      fk = fk_n;
+      fg = fg_n;
+    }
+    Frags fn;
+    fn.w1 = __builtin_bit_cast(bf16x8_t, pk[0]);
+    fn.m1 = __builtin_bit_cast(bf16x8_t, pk[1]);
+    fn.w3 = __builtin_bit_cast(bf16x8_t, pk[2]);
+    fn.m3 = __builtin_bit_cast(bf16x8_t, pk[3]);
+    fn.zw = __builtin_bit_cast(bf16x8_t, pk[4]);
+    fn.zm = __builtin_bit_cast(bf16x8_t, pk[5]);
+    return fn;
+  };
+
+  if constexpr (S::NBUF == 3) {
+    // Software pipeline over three buffers: iteration it aggregates tile it
+    // (fragments formed in the previous iteration) while it recomputes tile
+    // it+1 and forms its fragments, so the elementwise VALU work of one tile
+    // overlaps the MFMAs of the other; tile it+2 is in flight from global
+    // memory meanwhile and lands in the buffer tile it-1 used.  The recompute
+    // past the last tile reads a stale (in-bounds) buffer and is discarded.
+    load_tile(0);
+    store_tile(0);
+    if (ntiles > 1) {
+      load_tile(TB);
+      store_tile(1);
     }
     __syncthreads();
+    Frags f = elementwise(recompute(bufp(0)), kscp(0));
+    // No conditional loads or stores in the body: past the end the last
+    // tile is fetched again and stored into the free buffer.
+    int bc = 0;  // buffer of tile it
+    for (int it = 0; it < ntiles; ++it) {
+      const int bn = bc == 2 ? 0 : bc + 1;  // tile it+1
+      const int bnn = bn == 2 ? 0 : bn + 1; // tile it+2 (= tile it-1's)
+      const int tl = it + 2 < ntiles ? it + 2 : ntiles - 1;
+      load_tile(static_cast<int64_t>(tl) * TB);
+      const Rec rn = recompute(bufp(bn));
+      f = aggregate_next(f, bufp(bc), rn, kscp(bn));
+      store_tile(bnn);
+      __syncthreads();
+      bc = bn;
+    }
+  } else {
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+      const int b = S::NBUF == 2 ? (it & 1) : 0;
+      if (it + 1 < ntiles) load_tile(static_cast<int64_t>(it + 1) * TB);
+      aggregate(elementwise(recompute(bufp(b)), kscp(b)), bufp(b));
+      if (S::NBUF == 1) __syncthreads();  // single buffer: everyone is done reading it
+      if (it + 1 < ntiles) {
+        // With two buffers, b^1 was last read in iteration it-1 (barrier since).
+        store_tile(S::NBUF == 2 ? (b ^ 1) : 0);
+      }
+      __syncthreads();
+    }
   }
 
-  // Chunk-end state and operand shadows of this wave's hidden units, in
-  // batches of one 16-column block: all start values first, then the stores.
+  // Chunk-end state and operand shadows of this wave's hidden units, one
+  // 16-column block jb at a time, software-pipelined: the start values of
+  // blocks jb+2, jb+3 are loaded before blocks jb, jb+1 are stored.  (The
+  // outputs may alias the inputs, so the compiler keeps loads placed after
+  // a store behind it; issuing them early in program order is what lets
+  // them overlap.)
   const float* cf = a.coef + (u * a.nC + a.r) * 4;
   const float cW = cf[0], cM = cf[1], cWM = cf[2];
   const int64_t P = 3 * FD * a.h;
   const float* __restrict__ Wi = a.Win + u * P;
   const float* __restrict__ Mi = a.Min + u * P;
-#pragma unroll
-  for (int jb = 0; jb < FD / 16; ++jb) {
-    int64_t off[3][4];
-    float w0[3][4], m0[3][4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      // W1/W3: rows i = 16*wave + 4*g4 + v (hidden), col j = 16*jb + l16
-      const int64_t i = 64 * ib + 16 * wave + 4 * g4 + v;
-      const int64_t j = 16 * jb + l16;
-      off[0][v] = i * FD + j;
-      off[1][v] = a.h * FD + i * FD + j;
-      // W2: rows j2 = 16*jb + 4*g4 + v, col = this lane's hidden unit
-      off[2][v] = 2 * a.h * FD + (16 * jb + 4 * g4 + v) * a.h + i_glob;
-    }
+  constexpr int NJB = FD / 16;
+  auto off_of = [&](int jb, int t, int v) -> int64_t {
+    // W1/W3: row i = 16*wave + 4*g4 + v (hidden), col j = 16*jb + l16.
+    // W2: row j2 = 16*jb + 4*g4 + v, col = this lane's hidden unit.
+    const int64_t i = 64 * ib + 16 * wave + 4 * g4 + v;
+    const int64_t j = 16 * jb + l16;
+    if (t == 0) return i * FD + j;
+    if (t == 1) return a.h * FD + i * FD + j;
+    return 2 * a.h * FD + (16 * jb + 4 * g4 + v) * a.h + i_glob;
+  };
+  float w0[NJB][3][4], m0[NJB][3][4];
+  auto load_jb = [&](int jb) {
 #pragma unroll
     for (int t = 0; t < 3; ++t)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        w0[t][v] = Wi[off[t][v]];
-        m0[t][v] = Mi[off[t][v]];
+        w0[jb][t][v] = Wi[off_of(jb, t, v)];
+        m0[jb][t][v] = Mi[off_of(jb, t, v)];
       }
+  };
+  auto store_jb = [&](int jb) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int64_t i = 64 * ib + 16 * wave + 4 * g4 + v;
       const int64_t j = 16 * jb + l16;
       const int64_t srow = 64 * (i / 32) + i % 32;
-      state_store(a, KREP, u, off[0][v], w0[0][v], m0[0][v], acc[jb][v], acc[8 + jb][v], cW, cM,
-                  cWM, 0, srow, j);
-      state_store(a, KREP, u, off[1][v], w0[1][v], m0[1][v], acc[16 + jb][v], acc[24 + jb][v],
-                  cW, cM, cWM, 0, srow + 32, j);
+      state_store(a, KREP, u, off_of(jb, 0, v), w0[jb][0][v], m0[jb][0][v], acc[jb][v],
+                  acc[8 + jb][v], cW, cM, cWM, 0, srow, j);
+      state_store(a, KREP, u, off_of(jb, 1, v), w0[jb][1][v], m0[jb][1][v], acc[16 + jb][v],
+                  acc[24 + jb][v], cW, cM, cWM, 0, srow + 32, j);
       const int64_t j2 = 16 * jb + 4 * g4 + v;
-      state_store(a, KREP, u, off[2][v], w0[2][v], m0[2][v], acc[32 + jb][v], acc[40 + jb][v],
-                  cW, cM, cWM, 1, j2, i_glob);
+      state_store(a, KREP, u, off_of(jb, 2, v), w0[jb][2][v], m0[jb][2][v], acc[32 + jb][v],
+                  acc[40 + jb][v], cW, cM, cWM, 1, j2, i_glob);
     }
+  };
+  load_jb(0);
+  load_jb(1);
+#pragma unroll
+  for (int jb = 0; jb < NJB; jb += 2) {
+    if (jb + 2 < NJB) {
+      load_jb(jb + 2);
+      load_jb(jb + 3);
+    }
+    store_jb(jb);
+    store_jb(jb + 1);
   }
 }
 

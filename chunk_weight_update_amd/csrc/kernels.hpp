@@ -50,16 +50,27 @@ __device__ __forceinline__ int64_t n_valid(const Shape& s, int r) {
 
 // ---------------------------------------------------------------------------
 // Scalar kernels (§3.2 K^M = eta*beta~, K^W = eta*beta~*R; App. A.2 log-space
-// suffix products).  One wave per (unit, chunk) segment of n <= C tokens.
-// Lane i owns the contiguous block [i*per, min((i+1)*per, n)).
+// suffix products).  One workgroup of SCAN_NT threads per (unit, chunk)
+// segment of n <= C tokens, walked in rounds of SCAN_NT consecutive tokens
+// from the last round to the first; thread i takes token rd*SCAN_NT + i, so
+// every global access is coalesced and each token's logarithms are taken
+// once.
 //   b_t = prod_{s>t} beta_s,  c_t = prod_{s>t} gamma_s   (exclusive suffix
 //        products, as exp of suffix sums of log|.| with a sign parity)
 //   P_t = c_t + beta_{t+1} P_{t+1},  P_{n-1} = 1   (= beta~_t R_t, bounded)
 //   K^W_t = eta_t P_t,  K^M_t = eta_t b_t,  cW = prod gamma, cM = prod beta,
 //   cWM = beta_0 P_0.
-// All scan arithmetic is fp64.  Output index of token p of chunk r of unit
-// u is u*ustride + r*rstride + p; with pad > n tokens p in [n, pad) are
-// written as 0.  coef of (u, r) starts at (u*nC + r)*cstride.
+// P is the suffix composition of the affine maps x -> c_t + beta_{t+1} x
+// ((A1,B1) o (A2,B2) = (A1 + B1 A2, B1 B2)); the token past the segment
+// has beta = 0, which ends the recursion at P_{n-1} = c_{n-1} = 1.
+// Within a round: wave-level suffix scans by shuffles, wave totals through
+// LDS (double-buffered by round parity, so two barriers per round), and the
+// carry of the later rounds (suffix log sums, parities, P and beta of the
+// first token of the later round).  No subtraction of log sums anywhere, so
+// the -inf of a zero factor never turns into NaN.  All scan arithmetic is
+// fp64.  Output index of token p of chunk r of unit u is
+// u*ustride + r*rstride + p; with pad > n tokens p in [n, pad) are written
+// as 0.  coef of (u, r) starts at (u*nC + r)*cstride.
 
 struct LogSigned {  // log|x| and the sign of x (as a parity bit)
   double l;
@@ -78,139 +89,150 @@ __device__ __forceinline__ double exp_signed(double l, int neg) {
   return neg ? -e : e;
 }
 
-__global__ __launch_bounds__(64) void k_scan(const float* __restrict__ eta,
-                                              const float* __restrict__ alpha,
-                                              const float* __restrict__ beta, int64_t L,
-                                              int64_t C, int64_t nC, int mode, float* kw,
-                                              float* km, int64_t ustride, int64_t rstride,
-                                              int64_t pad, float* coef, int cstride) {
-  extern __shared__ float sm[];  // 3 * C floats: eta, alpha, beta of the segment
+constexpr int SCAN_NT = 1024;
+
+__global__ __launch_bounds__(SCAN_NT) void k_scan(const float* __restrict__ eta,
+                                                  const float* __restrict__ alpha,
+                                                  const float* __restrict__ beta, int64_t L,
+                                                  int64_t C, int64_t nC, int mode, float* kw,
+                                                  float* km, int64_t ustride, int64_t rstride,
+                                                  int64_t pad, float* coef, int cstride) {
+  constexpr int NW = SCAN_NT / 64;
+  __shared__ double s_lb[2][NW], s_lg[2][NW], s_A[2][NW], s_B[2][NW], s_b0[2][NW];
+  __shared__ int s_par[2][NW];
   const int64_t seg = blockIdx.x;
   const int64_t u = seg / nC;
   const int r = static_cast<int>(seg % nC);
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t t0 = static_cast<int64_t>(r) * C;
   const int64_t n = (L - t0) < C ? (L - t0) : C;
   const float* e_g = eta + u * L + t0;
   const float* a_g = alpha + u * L + t0;
   const float* b_g = beta + u * L + t0;
-  float* se = sm;
-  float* sa = sm + C;
-  float* sb = sm + 2 * C;
-  for (int64_t i = lane; i < n; i += 64) {
-    se[i] = e_g[i];
-    sa[i] = a_g[i];
-    sb[i] = b_g[i];
-  }
-  __syncthreads();
-
-  const int64_t per = (n + 63) / 64;
-  const int64_t s0 = lane * per < n ? lane * per : n;
-  const int64_t s1 = (lane + 1) * per < n ? (lane + 1) * per : n;
-  auto log_gamma = [&](int64_t i) -> LogSigned {
-    if (mode == 1) return log_signed(static_cast<double>(sa[i]));
-    const double ea = static_cast<double>(se[i]) * static_cast<double>(sa[i]);
-    LogSigned r;
-    r.neg = ea > 1.0;
-    r.l = ea <= 1.0 ? log1p(-ea) : log(ea - 1.0);  // log1p keeps 1 - eta*alpha exact-ish
-    return r;
-  };
-
-  // Pass 1: block totals of log|beta|, log|gamma| and sign parities.
-  double lb_blk = 0.0, lg_blk = 0.0;
-  int nb_blk = 0, ng_blk = 0;
-  for (int64_t i = s0; i < s1; ++i) {
-    const LogSigned lb = log_signed(static_cast<double>(sb[i]));
-    const LogSigned lg = log_gamma(i);
-    lb_blk += lb.l; nb_blk ^= lb.neg;
-    lg_blk += lg.l; ng_blk ^= lg.neg;
-  }
-  // Reverse scan over lanes: inclusive (lanes >= i), then shifted by one
-  // lane to the exclusive sums of the later blocks (no subtraction, so -inf
-  // logs of zero factors never produce NaN).
-  double xb = lb_blk, xg = lg_blk;
-  int pb_inc = nb_blk, pg_inc = ng_blk;
-  for (int off = 1; off < 64; off <<= 1) {
-    const double yb = __shfl_down(xb, off, 64);
-    const double yg = __shfl_down(xg, off, 64);
-    const int qb = __shfl_down(pb_inc, off, 64);
-    const int qg = __shfl_down(pg_inc, off, 64);
-    if (lane + off < 64) { xb += yb; xg += yg; pb_inc ^= qb; pg_inc ^= qg; }
-  }
-  const double sh_b = __shfl_down(xb, 1, 64);
-  const double sh_g = __shfl_down(xg, 1, 64);
-  const double lb_after = lane < 63 ? sh_b : 0.0;
-  const double lg_after = lane < 63 ? sh_g : 0.0;
-  const int nb_after = pb_inc ^ nb_blk;
-  const int ng_after = pg_inc ^ ng_blk;
-  const double lb_total = __shfl(xb, 0, 64);
-  const double lg_total = __shfl(xg, 0, 64);
-  const int nb_total = __shfl(pb_inc, 0, 64);
-  const int ng_total = __shfl(pg_inc, 0, 64);
-
-  // Pass 2: this block's affine map P_{s0} = A + B * P_{s1}.
-  double A = 0.0, Bm = 1.0;
-  {
-    double lb = lb_after, lg = lg_after;
-    int pb = nb_after, pg = ng_after;
-    double beta_next = s1 < n ? static_cast<double>(sb[s1]) : 0.0;
-    for (int64_t i = s1 - 1; i >= s0; --i) {
-      const double c = exp_signed(lg, pg);
-      A = c + beta_next * A;
-      Bm = beta_next * Bm;
-      const LogSigned b = log_signed(static_cast<double>(sb[i]));
-      const LogSigned g = log_gamma(i);
-      lb += b.l; pb ^= b.neg;
-      lg += g.l; pg ^= g.neg;
-      beta_next = static_cast<double>(sb[i]);
-    }
-    (void)lb; (void)pb;
-  }
-  // Reverse scan of affine maps: lane i gets the composition of lanes >= i,
-  // (A_i, B_i) o (A_j, B_j) = (A_i + B_i A_j, B_i B_j).  The last non-empty
-  // block has B = 0 (beta past the end is 0), empty blocks are (0, 1).
-  double cA = A, cB = Bm;
-  for (int off = 1; off < 64; off <<= 1) {
-    const double oA = __shfl_down(cA, off, 64);
-    const double oB = __shfl_down(cB, off, 64);
-    if (lane + off < 64) { cA = cA + cB * oA; cB = cB * oB; }
-  }
-  double P_next = __shfl_down(cA, 1, 64);  // P at s1 (first token of next block)
-  if (lane == 63) P_next = 0.0;
-
-  // Pass 3: kernels of every token of the block.
-  {
-    double lb = lb_after, lg = lg_after;
-    int pb = nb_after, pg = ng_after;
-    double beta_next = s1 < n ? static_cast<double>(sb[s1]) : 0.0;
-    double P = P_next;
-    for (int64_t i = s1 - 1; i >= s0; --i) {
-      const double bt = exp_signed(lb, pb);
-      const double ct = exp_signed(lg, pg);
-      P = ct + beta_next * P;
-      const double e = static_cast<double>(se[i]);
-      const LogSigned b = log_signed(static_cast<double>(sb[i]));
-      const LogSigned g = log_gamma(i);  // reads se[i], sa[i]: before they are overwritten
-      se[i] = static_cast<float>(e * P);   // K^W
-      sa[i] = static_cast<float>(e * bt);  // K^M
-      lb += b.l; pb ^= b.neg;
-      lg += g.l; pg ^= g.neg;
-      beta_next = static_cast<double>(sb[i]);
-    }
-    if (lane == 0 && n > 0) {
-      float* cf = coef + (u * nC + r) * cstride;
-      cf[0] = static_cast<float>(exp_signed(lg_total, ng_total));
-      cf[1] = static_cast<float>(exp_signed(lb_total, nb_total));
-      cf[2] = static_cast<float>(static_cast<double>(sb[0]) * P);
-    }
-  }
-  __syncthreads();
   float* kw_o = kw + u * ustride + r * rstride;
   float* km_o = km + u * ustride + r * rstride;
-  const int64_t lim = pad > n ? pad : n;
-  for (int64_t i = lane; i < lim; i += 64) {
-    kw_o[i] = i < n ? se[i] : 0.0f;
-    km_o[i] = i < n ? sa[i] : 0.0f;
+  for (int64_t i = n + tid; i < pad; i += SCAN_NT) {
+    kw_o[i] = 0.0f;
+    km_o[i] = 0.0f;
+  }
+
+  // Carry from the later rounds.
+  double cLB = 0.0, cLG = 0.0, cP = 0.0, cBeta = 0.0;
+  int cPar = 0;  // bit 0: parity of beta signs, bit 1: of gamma signs
+  const int64_t nr = (n + SCAN_NT - 1) / SCAN_NT;
+  for (int64_t rd = nr - 1; rd >= 0; --rd) {
+    const int pb = static_cast<int>(rd & 1);
+    const int64_t i = rd * SCAN_NT + tid;
+    const bool valid = i < n;
+    double e = 0.0, bt = 0.0, lb = 0.0, lg = 0.0;
+    int par = 0;
+    if (valid) {
+      e = static_cast<double>(e_g[i]);
+      const double al = static_cast<double>(a_g[i]);
+      bt = static_cast<double>(b_g[i]);
+      const LogSigned b = log_signed(bt);
+      lb = b.l;
+      par = b.neg;
+      if (mode == 1) {
+        const LogSigned g = log_signed(al);
+        lg = g.l;
+        par |= g.neg << 1;
+      } else {
+        const double ea = e * al;
+        lg = ea <= 1.0 ? log1p(-ea) : log(ea - 1.0);  // log|1 - eta*alpha|
+        par |= (ea > 1.0 ? 1 : 0) << 1;
+      }
+    }
+    // Wave-level inclusive suffix sums (lanes >= lane).
+    double xb = lb, xg = lg;
+    int xp = par;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double yb = __shfl_down(xb, off, 64);
+      const double yg = __shfl_down(xg, off, 64);
+      const int yp = __shfl_down(xp, off, 64);
+      if (lane + off < 64) {
+        xb += yb;
+        xg += yg;
+        xp ^= yp;
+      }
+    }
+    if (lane == 0) {
+      s_lb[pb][w] = xb;
+      s_lg[pb][w] = xg;
+      s_par[pb][w] = xp;
+      s_b0[pb][w] = bt;
+    }
+    __syncthreads();
+    // Exclusive suffix of this token: the next lane's inclusive value, plus
+    // the totals of the later waves of the round, plus the carry.
+    double eb = __shfl_down(xb, 1, 64), eg = __shfl_down(xg, 1, 64);
+    int ep = __shfl_down(xp, 1, 64);
+    if (lane == 63) {
+      eb = 0.0;
+      eg = 0.0;
+      ep = 0;
+    }
+    double lbw = cLB, lgw = cLG;
+    int pw = cPar;
+    for (int v = NW - 1; v > w; --v) {
+      lbw += s_lb[pb][v];
+      lgw += s_lg[pb][v];
+      pw ^= s_par[pb][v];
+    }
+    eb += lbw;
+    eg += lgw;
+    ep ^= pw;
+    const double b_t = exp_signed(eb, ep & 1);
+    const double c_t = exp_signed(eg, (ep >> 1) & 1);
+    // beta of the next token (0 past the segment end).
+    double bnext = __shfl_down(bt, 1, 64);
+    if (lane == 63) bnext = w + 1 < NW ? s_b0[pb][w + 1] : cBeta;
+    // Wave-level suffix composition of x -> A + B x.
+    double A = valid ? c_t : 0.0, B = valid ? bnext : 1.0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double oA = __shfl_down(A, off, 64);
+      const double oB = __shfl_down(B, off, 64);
+      if (lane + off < 64) {
+        A = A + B * oA;
+        B = B * oB;
+      }
+    }
+    if (lane == 0) {
+      s_A[pb][w] = A;
+      s_B[pb][w] = B;
+    }
+    __syncthreads();
+    // P at the first token after this wave, and P at the round's first token
+    // (the carry of the next round), by composing the later waves' maps.
+    double x = cP, x_after_w = cP;
+    for (int v = NW - 1; v >= 0; --v) {
+      if (v == w) x_after_w = x;
+      x = s_A[pb][v] + s_B[pb][v] * x;
+    }
+    const double P = A + B * x_after_w;
+    if (valid) {
+      kw_o[i] = static_cast<float>(e * P);
+      km_o[i] = static_cast<float>(e * b_t);
+    }
+    // Carry into the earlier round.
+    for (int v = w; v >= 0; --v) {  // the later waves were added above
+      lbw += s_lb[pb][v];
+      lgw += s_lg[pb][v];
+      pw ^= s_par[pb][v];
+    }
+    cLB = lbw;
+    cLG = lgw;
+    cPar = pw;
+    cP = x;
+    cBeta = s_b0[pb][0];
+  }
+  if (tid == 0 && n > 0) {
+    float* cf = coef + (u * nC + r) * cstride;
+    cf[0] = static_cast<float>(exp_signed(cLG, (cPar >> 1) & 1));
+    cf[1] = static_cast<float>(exp_signed(cLB, cPar & 1));
+    cf[2] = static_cast<float>(cBeta * cP);
   }
 }
 

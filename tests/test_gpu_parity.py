@@ -69,6 +69,42 @@ def test_scalar_kernels_match_oracle(B, H, L, C, regime, mode):
             assert np.all(err <= 1e-6 * np.abs(ref) + 2e-38), float(np.max(err / (np.abs(ref) + 1e-300)))
 
 
+@pytest.mark.parametrize("L,C,mode", [(3 * 12288 - 5, 12288, 0), (4096 + 1000, 2048, 1)])
+def test_scalar_kernels_signs_and_zeros(L, C, mode):
+    """Negative and zero factors: beta in [-1, 1] with exact zeros, and
+    eta*alpha up to 4 so that gamma = 1 - eta*alpha changes sign (mode 0), or
+    alpha itself in [-1, 1] (mode 1).  Exercises the sign parities and the
+    -inf logarithm of a zero factor across several rounds of the scan."""
+    import torch
+    import chunk_weight_update_amd as cwu
+    log(f"scan signs L={L} C={C} mode={mode}")
+    rng = np.random.default_rng(11)
+    eta = rng.uniform(0.0, 2.0, (1, 2, L)).astype(np.float32)
+    alpha = (rng.uniform(0.0, 2.0, (1, 2, L)) if mode == 0
+             else rng.uniform(-1.0, 1.0, (1, 2, L))).astype(np.float32)
+    beta = rng.uniform(-1.0, 1.0, (1, 2, L)).astype(np.float32)
+    beta[0, 0, ::997] = 0.0
+    prob = cwu.make_problem(LINEAR, 1, 2, L, 16, 0, C, F32, mode)
+    dev = [torch.from_numpy(x).cuda() for x in (eta, alpha, beta)]
+    nC = -(-L // C)
+    kw = torch.empty(1, 2, L, device="cuda")
+    km = torch.empty(1, 2, L, device="cuda")
+    cf = torch.empty(1, 2, nC, 3, device="cuda")
+    cwu.scalar_kernels(prob, *dev, kw, km, cf)
+    torch.cuda.synchronize()
+    kw, km, cf = (x.cpu().numpy().astype(np.float64) for x in (kw, km, cf))
+    for r in range(nC):
+        sl = slice(r * C, min((r + 1) * C, L))
+        n = sl.stop - sl.start
+        okw, okm, ocf = oracle.scalar_kernels(eta[..., sl].reshape(-1, n),
+                                              alpha[..., sl].reshape(-1, n),
+                                              beta[..., sl].reshape(-1, n), mode)
+        for got, ref in ((kw[..., sl].reshape(-1, n), okw), (km[..., sl].reshape(-1, n), okm),
+                         (cf[:, :, r, :].reshape(-1, 3), ocf)):
+            err = np.abs(got - ref)
+            assert np.all(err <= 1e-6 * np.abs(ref) + 2e-38), float(np.max(err / (np.abs(ref) + 1e-300)))
+
+
 # --- linear learner ---------------------------------------------------------
 
 def test_linear_d64_l256_c64_fp32():

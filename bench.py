@@ -92,6 +92,8 @@ def kernel_work(w, cls):
             return 12.0 * L * d * h * BH, "flop"
         if cls == cwu.KERNEL_PHASE_B:   # backward (dZ) + both aggregations
             return 14.0 * L * d * h * BH, "flop"
+        if cls == cwu.KERNEL_STATE:     # W0, M0 read; W_end, M_end written; bf16 shadow
+            return 18.0 * 3 * d * h * BH * w.n_chunks, "byte"
         if cls == cwu.KERNEL_PREP:
             # K read + K^T written; W0 read + operand shadows written
             return 2.0 * BH * L * d * iob + BH * 3 * d * h * (4 + 4 * iob), "byte"
@@ -202,7 +204,8 @@ def main():
     ev = HipEvents()
     classes = ([cwu.KERNEL_SCAN, cwu.KERNEL_LINEAR_FWD, cwu.KERNEL_LINEAR_AGG] if w.kind == 0
                else [cwu.KERNEL_SCAN, cwu.KERNEL_PREP, cwu.KERNEL_FWD13, cwu.KERNEL_FWD2,
-                     cwu.KERNEL_BWD, cwu.KERNEL_AGG, cwu.KERNEL_PHASE_A, cwu.KERNEL_PHASE_B])
+                     cwu.KERNEL_BWD, cwu.KERNEL_AGG, cwu.KERNEL_PHASE_A, cwu.KERNEL_PHASE_B,
+                     cwu.KERNEL_STATE])
     per_step_launches = 2 * max(w.n_chunks, 2) + 2
     kernels = {}
     steps_k = max(1, min(args.steps, 10))

@@ -19,6 +19,11 @@ using namespace e2ttt;
 namespace {
 
 constexpr int64_t kMaxChunk = 12288;
+// Phase B token split: target grid of one workgroup per compute unit of a
+// gfx950 (MI355X: 256 CUs), at most 8 splits.  A plan constant, so that the
+// workspace size stays a pure function of the problem.
+constexpr int64_t kCUs = 256;
+constexpr int kMaxSplitB = 8;
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -29,10 +34,11 @@ struct Plan {
   int kind, io, mode, krep;
   bool fused;   // two-kernel chunk step (SwiGLU, d = 128, bf16 io)
   int rbA;      // phase A rows per workgroup (32 or 64)
+  int nsplitB;  // phase B token split (1: fused state epilogue)
   size_t opsz;  // bytes per GEMM operand element (2 for bf16, 4 for fp32)
   // workspace offsets (bytes)
   size_t kw, km, coef, kt, w13s, w2s, w2ts, zrow, a1s, a3s, grow, ut, gt, zt, gw, gm, gbf, gft,
-      total;
+      part, total;
 };
 
 e2ttt_status check_problem(const e2ttt_problem* p) {
@@ -106,6 +112,15 @@ e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
     q.kt = take(T * q.BH * q.nC * q.d * q.Cp);
     q.gbf = take(T * q.BH * q.Cp * q.d);
     q.gft = take(T * q.BH * q.d * q.Cp);
+    // Phase B has BH * h/64 workgroups of one CU each; when that leaves most
+    // of the chip idle, split the chunk's token tiles over up to 8
+    // workgroups per hidden block (a divisor of the tile count) and add the
+    // splits in a separate state epilogue.
+    const int64_t wgB = q.BH * (q.h / 64), ntile = q.Cp / 32;
+    q.nsplitB = 1;
+    while (q.nsplitB < kMaxSplitB && wgB * q.nsplitB * 2 <= kCUs && ntile % (q.nsplitB * 2) == 0)
+      q.nsplitB *= 2;
+    if (q.nsplitB > 1) q.part = take(f4 * static_cast<size_t>(q.nsplitB) * q.BH * 2 * q.P);
   } else {
     q.Cp = (q.C + 127) / 128 * 128;
     q.opsz = q.io == E2TTT_BF16 ? 2 : 4;
@@ -281,6 +296,9 @@ void launch_fused(const Plan& q, const void* qv, const void* kv, const void* vv,
   a.gft = reinterpret_cast<bf16_t*>(ws + q.gft);
   a.Wout = Wend;
   a.Mout = Mend;
+  a.nsplit = q.nsplitB;
+  a.krep = q.krep;
+  a.part = q.nsplitB > 1 ? reinterpret_cast<float*>(ws + q.part) : nullptr;
   Shape s{q.BH, q.L, q.d, q.h, q.C, q.Cp, q.nC, q.krep};
   launch_scan(q, eta, alpha, beta, reinterpret_cast<float*>(ws + q.kw),
               reinterpret_cast<float*>(ws + q.km), q.nC * q.Cp, q.Cp, q.Cp,
@@ -292,7 +310,7 @@ void launch_fused(const Plan& q, const void* qv, const void* kv, const void* vv,
   E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, k_prep_shadow<bf16_t>, dim3(grid1((q.BH * q.P + 255) / 256)),
                dim3(256), 0, st, s, W0, a.w13s, a.w2s, a.w2ts);
   const unsigned gA = grid1(q.BH * (2 * q.Cp / q.rbA));
-  const unsigned gB = grid1(q.BH * (q.h / 64));
+  const unsigned gB = grid1(q.BH * (q.h / 64) * q.nsplitB);
   for (int64_t r = 0; r < q.nC; ++r) {
     a.r = static_cast<int>(r);
     a.last = static_cast<int>(r == q.nC - 1);
@@ -306,6 +324,9 @@ void launch_fused(const Plan& q, const void* qv, const void* kv, const void* vv,
     E2TTT_LAUNCH(I, E2TTT_KERNEL_PHASE_A, kA, dim3(gA), dim3(256), ldsA, st, a);
     const size_t ldsB = q.krep == 2 ? PhaseBCfg<2>::LDS_BYTES : PhaseBCfg<1>::LDS_BYTES;
     E2TTT_LAUNCH(I, E2TTT_KERNEL_PHASE_B, kB, dim3(gB), dim3(256), ldsB, st, a);
+    if (q.nsplitB > 1)
+      E2TTT_LAUNCH(I, E2TTT_KERNEL_STATE, k_state_epi, dim3(grid1(q.BH * (q.h / 64) * 24)),
+                   dim3(256), 0, st, a);
   }
 }
 

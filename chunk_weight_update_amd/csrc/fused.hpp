@@ -73,6 +73,9 @@ struct FusedArgs {
   const bf16_t* kt;   // [BH][nC][FD][Cp]  K feature-major
   bf16_t* gbf;        // [BH][Cp][FD]      bf16(g), token-major
   bf16_t* gft;        // [BH][FD][Cp]      bf16(g), feature-major
+  int nsplit;         // phase B token split (1: fused state epilogue)
+  int krep;           // 2 with hi/lo operand shadows
+  float* part;        // [BH*h/64][nsplit][48][256] x 4 floats: phase B partial sums
 };
 
 __device__ __forceinline__ int64_t fused_nvalid(const FusedArgs& a) {
@@ -396,6 +399,35 @@ __device__ __forceinline__ void state_store(const FusedArgs& a, int krep, int64_
   }
 }
 
+// State entry behind phase B accumulator value v of thread tid for column
+// block jb of weight t (0: W1, 1: W3, 2: W2) in hidden block ib: its offset
+// in the packed state and its position in the operand shadow.  Shared by the
+// fused epilogue and the split-sum epilogue so the two agree by construction.
+struct StateSlot {
+  int off, srow, scol;  // within one unit's state (< 3*128*4096 entries)
+  int kind;             // 0: W1/W3 entry, 1: W2 entry
+};
+__device__ __forceinline__ StateSlot phaseB_slot(int h, int ib, int tid, int t, int jb, int v) {
+  const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+  StateSlot r;
+  if (t < 2) {  // row i = hidden unit (16*wave + 4*g4 + v), column j = 16*jb + l16
+    const int i = 64 * ib + 16 * wave + 4 * g4 + v;
+    const int j = 16 * jb + l16;
+    r.off = t * h * FD + i * FD + j;
+    r.srow = 64 * (i / 32) + i % 32 + 32 * t;
+    r.scol = j;
+    r.kind = 0;
+  } else {      // row j2 = 16*jb + 4*g4 + v, column = hidden unit 16*wave + l16
+    const int i = 64 * ib + 16 * wave + l16;
+    const int j2 = 16 * jb + 4 * g4 + v;
+    r.off = 2 * h * FD + j2 * h + i;
+    r.srow = j2;
+    r.scol = i;
+    r.kind = 1;
+  }
+  return r;
+}
+
 // Phase B: 4 waves (one per SIMD), wave w owns hidden units
 // 64*ib + 16*w .. +15 for all FD output columns.  The recompute weights of
 // the wave's hidden units stay in registers (KREP = 1) or are read from LDS
@@ -420,8 +452,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
 
   const int64_t nib = a.h / 64;
-  const int64_t u = blockIdx.x / nib;
-  const int64_t ib = blockIdx.x % nib;
+  const int64_t grp = blockIdx.x / a.nsplit;  // (unit, hidden block)
+  const int sp = static_cast<int>(blockIdx.x % a.nsplit);
+  const int64_t u = grp / nib;
+  const int64_t ib = grp % nib;
   const int64_t tok0 = static_cast<int64_t>(a.r) * a.C;
   const int64_t nv = fused_nvalid(a);
   const int wave = threadIdx.x >> 6;
@@ -497,7 +531,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     kscp(b)[threadIdx.x & (2 * TB - 1)] = sk;
   };
 
-  const int ntiles = static_cast<int>(a.Cp / TB);
+  // This workgroup's token tiles: split sp of nsplit (the host picks nsplit
+  // dividing Cp / TB).
+  const int ntiles = static_cast<int>(a.Cp / TB) / a.nsplit;
+  const int64_t tbase = static_cast<int64_t>(sp) * ntiles * TB;
 
   // Recompute of one tile: rows = tokens (2 blocks of 16), cols = this
   // wave's 16 hidden units; A1, A3 from K, dZ from g.
@@ -673,10 +710,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // overlaps the MFMAs of the other; tile it+2 is in flight from global
     // memory meanwhile and lands in the buffer tile it-1 used.  The recompute
     // past the last tile reads a stale (in-bounds) buffer and is discarded.
-    load_tile(0);
+    load_tile(tbase);
     store_tile(0);
     if (ntiles > 1) {
-      load_tile(TB);
+      load_tile(tbase + TB);
       store_tile(1);
     }
     __syncthreads();
@@ -688,7 +725,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const int bn = bc == 2 ? 0 : bc + 1;  // tile it+1
       const int bnn = bn == 2 ? 0 : bn + 1; // tile it+2 (= tile it-1's)
       const int tl = it + 2 < ntiles ? it + 2 : ntiles - 1;
-      load_tile(static_cast<int64_t>(tl) * TB);
+      load_tile(tbase + static_cast<int64_t>(tl) * TB);
       const Rec rn = recompute(bufp(bn));
       f = aggregate_next(f, bufp(bc), rn, kscp(bn));
       store_tile(bnn);
@@ -696,12 +733,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       bc = bn;
     }
   } else {
-    load_tile(0);
+    load_tile(tbase);
     store_tile(0);
     __syncthreads();
     for (int it = 0; it < ntiles; ++it) {
       const int b = S::NBUF == 2 ? (it & 1) : 0;
-      if (it + 1 < ntiles) load_tile(static_cast<int64_t>(it + 1) * TB);
+      if (it + 1 < ntiles) load_tile(tbase + static_cast<int64_t>(it + 1) * TB);
       aggregate(elementwise(recompute(bufp(b)), kscp(b)), bufp(b));
       if (S::NBUF == 1) __syncthreads();  // single buffer: everyone is done reading it
       if (it + 1 < ntiles) {
@@ -712,9 +749,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
   }
 
+  if (a.nsplit > 1) {
+    // Token-split: this workgroup's partial sums as [q][tid] 16-byte vectors
+    // (coalesced); k_state_epi adds the splits in a fixed order and writes
+    // the state.
+    f32x4_t* __restrict__ dst =
+        reinterpret_cast<f32x4_t*>(a.part) + (grp * a.nsplit + sp) * (48 * NT);
+#pragma unroll
+    for (int q = 0; q < 48; ++q) dst[q * NT + threadIdx.x] = acc[q];
+    return;
+  }
   // Chunk-end state and operand shadows of this wave's hidden units, one
   // 16-column block jb at a time, software-pipelined: the start values of
-  // blocks jb+2, jb+3 are loaded before blocks jb, jb+1 are stored.  (The
+  // block jb+1 are loaded before block jb is stored.  (The
   // outputs may alias the inputs, so the compiler keeps loads placed after
   // a store behind it; issuing them early in program order is what lets
   // them overlap.)
@@ -724,51 +771,69 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const float* __restrict__ Wi = a.Win + u * P;
   const float* __restrict__ Mi = a.Min + u * P;
   constexpr int NJB = FD / 16;
-  auto off_of = [&](int jb, int t, int v) -> int64_t {
-    // W1/W3: row i = 16*wave + 4*g4 + v (hidden), col j = 16*jb + l16.
-    // W2: row j2 = 16*jb + 4*g4 + v, col = this lane's hidden unit.
-    const int64_t i = 64 * ib + 16 * wave + 4 * g4 + v;
-    const int64_t j = 16 * jb + l16;
-    if (t == 0) return i * FD + j;
-    if (t == 1) return a.h * FD + i * FD + j;
-    return 2 * a.h * FD + (16 * jb + 4 * g4 + v) * a.h + i_glob;
-  };
   float w0[NJB][3][4], m0[NJB][3][4];
   auto load_jb = [&](int jb) {
 #pragma unroll
     for (int t = 0; t < 3; ++t)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        w0[jb][t][v] = Wi[off_of(jb, t, v)];
-        m0[jb][t][v] = Mi[off_of(jb, t, v)];
+        const int off = phaseB_slot(static_cast<int>(a.h), static_cast<int>(ib), threadIdx.x, t, jb, v).off;
+        w0[jb][t][v] = Wi[off];
+        m0[jb][t][v] = Mi[off];
       }
   };
   auto store_jb = [&](int jb) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t i = 64 * ib + 16 * wave + 4 * g4 + v;
-      const int64_t j = 16 * jb + l16;
-      const int64_t srow = 64 * (i / 32) + i % 32;
-      state_store(a, KREP, u, off_of(jb, 0, v), w0[jb][0][v], m0[jb][0][v], acc[jb][v],
-                  acc[8 + jb][v], cW, cM, cWM, 0, srow, j);
-      state_store(a, KREP, u, off_of(jb, 1, v), w0[jb][1][v], m0[jb][1][v], acc[16 + jb][v],
-                  acc[24 + jb][v], cW, cM, cWM, 0, srow + 32, j);
-      const int64_t j2 = 16 * jb + 4 * g4 + v;
-      state_store(a, KREP, u, off_of(jb, 2, v), w0[jb][2][v], m0[jb][2][v], acc[32 + jb][v],
-                  acc[40 + jb][v], cW, cM, cWM, 1, j2, i_glob);
-    }
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const StateSlot sl = phaseB_slot(static_cast<int>(a.h), static_cast<int>(ib), threadIdx.x, t, jb, v);
+        state_store(a, KREP, u, sl.off, w0[jb][t][v], m0[jb][t][v], acc[16 * t + jb][v],
+                    acc[16 * t + 8 + jb][v], cW, cM, cWM, sl.kind, sl.srow, sl.scol);
+      }
   };
   load_jb(0);
-  load_jb(1);
 #pragma unroll
-  for (int jb = 0; jb < NJB; jb += 2) {
-    if (jb + 2 < NJB) {
-      load_jb(jb + 2);
-      load_jb(jb + 3);
-    }
+  for (int jb = 0; jb < NJB; ++jb) {
+    if (jb + 1 < NJB) load_jb(jb + 1);
     store_jb(jb);
-    store_jb(jb + 1);
   }
+}
+
+// State epilogue of a token-split phase B: W_C = cW W_0 + cWM M_0 + sum of
+// the splits' A^W, M_C = cM M_0 + sum of A^M (splits added in index order,
+// so the result does not depend on scheduling), plus the operand shadows.
+// One thread per (W, M) accumulator pair of one phase B thread (four state
+// entries each): grid (BH * h/64) x 24 workgroups of 256 threads.
+__global__ __launch_bounds__(256) void k_state_epi(FusedArgs a) {
+  const int64_t grp = blockIdx.x / 24;
+  const int pr = static_cast<int>(blockIdx.x % 24);  // (t, jb) pair
+  const int t = pr >> 3, jb = pr & 7;
+  const int tid = threadIdx.x;
+  const int64_t nib = a.h / 64;
+  const int64_t u = grp / nib, ib = grp % nib;
+  const int qW = 16 * t + jb, qM = qW + 8;
+  const f32x4_t* src = reinterpret_cast<const f32x4_t*>(a.part) + grp * a.nsplit * (48 * 256);
+  f32x4_t sw = src[qW * 256 + tid], sm = src[qM * 256 + tid];
+  for (int sp = 1; sp < a.nsplit; ++sp) {
+    sw += src[sp * (48 * 256) + qW * 256 + tid];
+    sm += src[sp * (48 * 256) + qM * 256 + tid];
+  }
+  const int64_t P = 3 * FD * a.h;
+  const float* cf = a.coef + (u * a.nC + a.r) * 4;
+  const float cW = cf[0], cM = cf[1], cWM = cf[2];
+  StateSlot sl[4];
+  float w0[4], m0[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    sl[v] = phaseB_slot(static_cast<int>(a.h), static_cast<int>(ib), tid, t, jb, v);
+    w0[v] = a.Win[u * P + sl[v].off];
+    m0[v] = a.Min[u * P + sl[v].off];
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+    state_store(a, a.krep, u, sl[v].off, w0[v], m0[v], sw[v], sm[v], cW, cM, cWM, sl[v].kind,
+                sl[v].srow, sl[v].scol);
 }
 
 }  // namespace e2ttt

@@ -158,8 +158,10 @@ typedef enum {
   E2TTT_KERNEL_LINEAR_AGG = 7, /* linear learner: aggregations + state       */
   E2TTT_KERNEL_PHASE_A = 8,    /* d = 128 bf16: fused forward, readout, g     */
   E2TTT_KERNEL_PHASE_B = 9,    /* d = 128 bf16: fused backward, aggregations,
-                                  chunk-end state                           */
-  E2TTT_KERNEL_NUM_CLASSES = 10
+                                  chunk-end state (unless token-split)      */
+  E2TTT_KERNEL_STATE = 10,     /* d = 128 bf16, token-split phase B: sum of
+                                  the splits, chunk-end state, shadows      */
+  E2TTT_KERNEL_NUM_CLASSES = 11
 } e2ttt_kernel_class;
 
 /* Benchmark instrumentation: enqueue exactly the work of e2ttt_chunk_forward

@@ -144,6 +144,21 @@ def test_swiglu_bf16_small_nearunit(L, C, d, h):
     check(SWIGLU, 2, 2, L, d, h, C, BF16, seed=4, regime="nearunit", m0_scale=M0["nearunit"])
 
 
+def test_swiglu_bf16_compensated_small():
+    """hi/lo operand shadows on a token-split phase B (the split-sum state
+    epilogue writes both shadow halves)."""
+    import chunk_weight_update_amd as cwu
+    check(SWIGLU, 2, 2, 512, 128, 256, 256, BF16, seed=6, regime="nearunit",
+          m0_scale=M0["nearunit"], flags=cwu.FLAG_COMPENSATED_WEIGHTS)
+
+
+def test_swiglu_bf16_many_units_unsplit():
+    """Enough (unit, hidden block) workgroups that phase B is not
+    token-split: the fused state epilogue inside phase B."""
+    check(SWIGLU, 4, 32, 256, 128, 128, 128, BF16, seed=7, regime="nearunit",
+          m0_scale=M0["nearunit"])
+
+
 def test_swiglu_alpha_is_gamma_fp32():
     check(SWIGLU, 1, 2, 384, 128, 128, 128, F32, seed=5, regime="nearunit",
           m0_scale=M0["nearunit"], decay_mode=1)

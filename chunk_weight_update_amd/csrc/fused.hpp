@@ -291,44 +291,68 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     }
   }
 
-  // Epilogue.
+  // Epilogue: Y through LDS in fp32 (all of LDS is free after the last
+  // block's barrier), then every global access is a coalesced 16-byte
+  // vector.  Q rows: o = bf16(Y).  K rows: g = bf16(v - Y), rounded once,
+  // written token-major and, through a transposed LDS copy in tok_perm32
+  // order, feature-major.  Rows past the valid tokens have X = 0, so Y = 0
+  // and g = 0 there.
+  constexpr int YW = FD + 4;  // fp32 row stride of the Y staging
+  static_assert(static_cast<size_t>(RB) * YW * 4 + static_cast<size_t>(FD) * P::GW * 2 <=
+                    P::LDS_BYTES, "epilogue staging fits the workgroup's LDS");
+  float* Ys = reinterpret_cast<float*>(smem_raw);
+#pragma unroll
+  for (int i = 0; i < P::YN / 32; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      Ys[(wm * 32 + acc32_row(v)) * YW + wn * P::YN + i * 32 + (threadIdx.x & 31)] = yacc[i][v];
+  __syncthreads();
+  constexpr int VPR = FD / 8;  // 8-element vectors per row
   if (isQ) {
-#pragma unroll
-    for (int i = 0; i < P::YN / 32; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t p = p0 + wm * 32 + acc32_row(v);
-        const int64_t j = wn * P::YN + i * 32 + (threadIdx.x & 31);
-        if (p < nv) a.out[(u * a.L + tok0 + p) * FD + j] = f2bf(yacc[i][v]);
+    for (int idx = threadIdx.x; idx < RB * VPR; idx += 256) {
+      const int pr = idx / VPR, c = idx % VPR;
+      const int64_t p = p0 + pr;
+      if (p < nv) {
+        const float* y = Ys + pr * YW + c * 8;
+        uint4 o;
+        o.x = pack_bf16x2(y[0], y[1]);
+        o.y = pack_bf16x2(y[2], y[3]);
+        o.z = pack_bf16x2(y[4], y[5]);
+        o.w = pack_bf16x2(y[6], y[7]);
+        *reinterpret_cast<uint4*>(a.out + (u * a.L + tok0 + p) * FD + c * 8) = o;
       }
+    }
     return;
   }
-  // g = v - Y, rounded once to bf16: token-major directly, feature-major
-  // through LDS (W13b is free now: [FD][RB + 8]).
-  bf16_t* T_ = W13b;  // [FD][GW]
+  bf16_t* Tg = reinterpret_cast<bf16_t*>(smem_raw + static_cast<size_t>(RB) * YW * 4);  // [FD][GW]
   // v is an input and gbf workspace: they never overlap (checked on the
   // host), which the restrict qualifiers pass on to the compiler.
   const bf16_t* __restrict__ vsrc = a.v + (u * a.L + tok0) * FD;
   bf16_t* __restrict__ gdst = a.gbf + u * a.Cp * FD;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int pr = wm * 32 + acc32_row(v);
+  for (int idx = threadIdx.x; idx < RB * VPR; idx += 256) {
+    const int pr = idx / VPR, c = idx % VPR;
     const int64_t p = p0 + pr;
+    uint4 vin = make_uint4(0u, 0u, 0u, 0u);
+    if (p < nv) vin = *reinterpret_cast<const uint4*>(vsrc + p * FD + c * 8);
+    const float* y = Ys + pr * YW + c * 8;
+    const uint32_t vw[4] = {vin.x, vin.y, vin.z, vin.w};
+    uint32_t gw[4];
 #pragma unroll
-    for (int i = 0; i < P::YN / 32; ++i) {
-      const int j = wn * P::YN + i * 32 + (threadIdx.x & 31);
-      const float vin = p < nv ? bf2f(vsrc[p * FD + j]) : 0.0f;
-      const bf16_t g = f2bf(vin - yacc[i][v]);
-      gdst[p * FD + j] = g;
-      T_[j * P::GW + tok_perm32(pr)] = g;
+    for (int e = 0; e < 4; ++e) {
+      const float v0 = __uint_as_float(vw[e] << 16), v1 = __uint_as_float(vw[e] & 0xffff0000u);
+      gw[e] = pack_bf16x2(v0 - y[2 * e], v1 - y[2 * e + 1]);
+      const int col = tok_perm32(pr);
+      Tg[(c * 8 + 2 * e) * P::GW + col] = static_cast<bf16_t>(gw[e] & 0xffffu);
+      Tg[(c * 8 + 2 * e + 1) * P::GW + col] = static_cast<bf16_t>(gw[e] >> 16);
     }
+    *reinterpret_cast<uint4*>(gdst + p * FD + c * 8) = make_uint4(gw[0], gw[1], gw[2], gw[3]);
   }
   __syncthreads();
-  constexpr int VPR = RB / 8;
-  for (int idx = threadIdx.x; idx < FD * VPR; idx += 256) {
-    const int j = idx / VPR, c = idx % VPR;
+  constexpr int VPT = RB / 8;
+  for (int idx = threadIdx.x; idx < FD * VPT; idx += 256) {
+    const int j = idx / VPT, c = idx % VPT;
     *reinterpret_cast<uint4*>(a.gft + (u * FD + j) * a.Cp + p0 + c * 8) =
-        *reinterpret_cast<const uint4*>(T_ + j * P::GW + c * 8);
+        *reinterpret_cast<const uint4*>(Tg + j * P::GW + c * 8);
   }
 }
 

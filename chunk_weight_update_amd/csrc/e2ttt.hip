@@ -2,9 +2,15 @@
 //
 // Call sequence of e2ttt_chunk_forward (all on the caller's stream):
 //   scan (all chunks, one launch) -> K^T staging (all chunks) -> operand
-//   shadow of W0 -> per chunk r: fwd13, fwd2, bwd, agg.  The chunk loop is
-//   serial because chunk r+1 starts from chunk r's end state (§3.2 of
-//   "Rethinking Expressivity and Efficiency in Test-Time Training").
+//   shadow of W0 -> per chunk r:
+//     SwiGLU, d = 128, bf16: phase A, phase B (+ split-sum state epilogue
+//       when phase B is token-split);
+//     other SwiGLU shapes: fwd13, fwd2, bwd, agg;
+//     linear: linear_fwd, linear_agg.
+//   The chunk loop is serial because chunk r+1 starts from chunk r's end
+//   state (§3.2 of "Rethinking Expressivity and Efficiency in Test-Time
+//   Training").
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -20,10 +26,11 @@ namespace {
 
 constexpr int64_t kMaxChunk = 12288;
 // Phase B token split: target grid of one workgroup per compute unit of a
-// gfx950 (MI355X: 256 CUs), at most 8 splits.  A plan constant, so that the
+// gfx950 (MI355X: 256 CUs), at most 4 splits (measured: more splits cost
+// more in the split-sum epilogue than they save).  A plan constant, so that the
 // workspace size stays a pure function of the problem.
 constexpr int64_t kCUs = 256;
-constexpr int kMaxSplitB = 8;
+constexpr int kMaxSplitB = 4;
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -113,7 +120,7 @@ e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
     q.gbf = take(T * q.BH * q.Cp * q.d);
     q.gft = take(T * q.BH * q.d * q.Cp);
     // Phase B has BH * h/64 workgroups of one CU each; when that leaves most
-    // of the chip idle, split the chunk's token tiles over up to 8
+    // of the chip idle, split the chunk's token tiles over up to kMaxSplitB
     // workgroups per hidden block (a divisor of the tile count) and add the
     // splits in a separate state epilogue.
     const int64_t wgB = q.BH * (q.h / 64), ntile = q.Cp / 32;
@@ -200,22 +207,28 @@ struct Instr {
   void* const* ev = nullptr;
   int n_pairs = 0;
   int used = 0;
-  void before(int c, hipStream_t s) {
-    if (c == kclass && used < n_pairs) (void)hipEventRecord(static_cast<hipEvent_t>(ev[2 * used]), s);
-  }
-  void after(int c, hipStream_t s) {
+  // Events of the next launch of class c (null when c is not the timed class
+  // or the caller's events are used up).
+  void events(int c, hipEvent_t* start, hipEvent_t* stop) {
+    *start = nullptr;
+    *stop = nullptr;
     if (c == kclass && used < n_pairs) {
-      (void)hipEventRecord(static_cast<hipEvent_t>(ev[2 * used + 1]), s);
+      *start = static_cast<hipEvent_t>(ev[2 * used]);
+      *stop = static_cast<hipEvent_t>(ev[2 * used + 1]);
       ++used;
     }
   }
 };
 
-#define E2TTT_LAUNCH(I, cls, ...)   \
-  do {                              \
-    (I).before((cls), st);          \
-    hipLaunchKernelGGL(__VA_ARGS__); \
-    (I).after((cls), st);           \
+// Every launch goes through hipExtLaunchKernelGGL, which records the timed
+// class's events at the kernel's own start and end (not around the launch,
+// which would add the dispatch latency to the measured duration).
+#define E2TTT_LAUNCH(I, cls, kern, grid, block, shmem, stream, ...)                          \
+  do {                                                                                     \
+    hipEvent_t e2_start_, e2_stop_;                                                        \
+    (I).events((cls), &e2_start_, &e2_stop_);                                              \
+    hipExtLaunchKernelGGL(kern, grid, block, static_cast<uint32_t>(shmem), stream, e2_start_, \
+                          e2_stop_, 0u, __VA_ARGS__);                                      \
   } while (0)
 
 void launch_scan(const Plan& q, const float* eta, const float* alpha, const float* beta,

@@ -425,8 +425,8 @@ __device__ __forceinline__ void state_store(const FusedArgs& a, int krep, int64_
 
 // State entry behind phase B accumulator value v of thread tid for column
 // block jb of weight t (0: W1, 1: W3, 2: W2) in hidden block ib: its offset
-// in the packed state and its position in the operand shadow.  Shared by the
-// fused epilogue and the split-sum epilogue so the two agree by construction.
+// in the packed state and its position in the operand shadow (the layout
+// k_state_epi's block transpose follows as well).
 struct StateSlot {
   int off, srow, scol;  // within one unit's state (< 3*128*4096 entries)
   int kind;             // 0: W1/W3 entry, 1: W2 entry
@@ -827,9 +827,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // State epilogue of a token-split phase B: W_C = cW W_0 + cWM M_0 + sum of
 // the splits' A^W, M_C = cM M_0 + sum of A^M (splits added in index order,
 // so the result does not depend on scheduling), plus the operand shadows.
-// One thread per (W, M) accumulator pair of one phase B thread (four state
-// entries each): grid (BH * h/64) x 24 workgroups of 256 threads.
+// Workgroup (unit, hidden block, t, jb) of 256 threads takes the 1024 state
+// entries of one (W, M) accumulator pair of all phase B threads: a 64 x 16
+// block of W1 or W3 (t = 0, 1) or a 16 x 64 block of W2 (t = 2).  Thread tid
+// sums the splits of phase B thread tid's four entries, the block is
+// transposed through LDS, and each thread then owns four consecutive
+// columns of one row: 16-byte loads and stores of W_0, M_0, W_C, M_C and
+// 8-byte stores of the row-major shadows.
 __global__ __launch_bounds__(256) void k_state_epi(FusedArgs a) {
+  __shared__ float sW[64 * 17], sM[64 * 17];
   const int64_t grp = blockIdx.x / 24;
   const int pr = static_cast<int>(blockIdx.x % 24);  // (t, jb) pair
   const int t = pr >> 3, jb = pr & 7;
@@ -843,21 +849,70 @@ __global__ __launch_bounds__(256) void k_state_epi(FusedArgs a) {
     sw += src[sp * (48 * 256) + qW * 256 + tid];
     sm += src[sp * (48 * 256) + qM * 256 + tid];
   }
-  const int64_t P = 3 * FD * a.h;
-  const float* cf = a.coef + (u * a.nC + a.r) * 4;
-  const float cW = cf[0], cM = cf[1], cWM = cf[2];
-  StateSlot sl[4];
-  float w0[4], m0[4];
+  // Block-local coordinates (row r, column c) of accumulator register v.
+  const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+  const int CC = t < 2 ? 16 : 64;  // columns of the block
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    sl[v] = phaseB_slot(static_cast<int>(a.h), static_cast<int>(ib), tid, t, jb, v);
-    w0[v] = a.Win[u * P + sl[v].off];
-    m0[v] = a.Min[u * P + sl[v].off];
+    const int r = t < 2 ? 16 * wave + 4 * g4 + v : 4 * g4 + v;
+    const int c = t < 2 ? l16 : 16 * wave + l16;
+    sW[r * (CC + 1) + c] = sw[v];
+    sM[r * (CC + 1) + c] = sm[v];
   }
+  __syncthreads();
+  const int r = tid / (CC / 4), c0 = 4 * (tid % (CC / 4));
+  f32x4_t aw, am;
 #pragma unroll
-  for (int v = 0; v < 4; ++v)
-    state_store(a, a.krep, u, sl[v].off, w0[v], m0[v], sw[v], sm[v], cW, cM, cWM, sl[v].kind,
-                sl[v].srow, sl[v].scol);
+  for (int e = 0; e < 4; ++e) {
+    aw[e] = sW[r * (CC + 1) + c0 + e];
+    am[e] = sM[r * (CC + 1) + c0 + e];
+  }
+  const int64_t P = 3 * FD * a.h;
+  const int64_t h = a.h;
+  int64_t off;  // of the first of the four entries, inside the unit's state
+  if (t < 2) off = t * h * FD + (64 * ib + r) * FD + 16 * jb + c0;
+  else off = 2 * h * FD + (16 * jb + r) * h + 64 * ib + c0;
+  const float* cf = a.coef + (u * a.nC + a.r) * 4;
+  const float cW = cf[0], cM = cf[1], cWM = cf[2];
+  const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(a.Win + u * P + off);
+  const f32x4_t m0 = *reinterpret_cast<const f32x4_t*>(a.Min + u * P + off);
+  f32x4_t wn, mn;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    wn[e] = cW * w0[e] + cWM * m0[e] + aw[e];
+    mn[e] = cM * m0[e] + am[e];
+  }
+  *reinterpret_cast<f32x4_t*>(a.Wout + u * P + off) = wn;
+  *reinterpret_cast<f32x4_t*>(a.Mout + u * P + off) = mn;
+  if (a.last) return;
+  const int kr = a.krep;
+  bf16_t hi[4], lo[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    hi[e] = f2bf(wn[e]);
+    lo[e] = kr == 2 ? f2bf(wn[e] - bf2f(hi[e])) : bf16_t(0);
+  }
+  auto put4 = [](bf16_t* dst, const bf16_t (&x)[4]) {
+    *reinterpret_cast<uint2*>(dst) =
+        make_uint2(x[0] | (static_cast<uint32_t>(x[1]) << 16), x[2] | (static_cast<uint32_t>(x[3]) << 16));
+  };
+  if (t < 2) {  // W1 / W3 row i -> shadow row 64*(i/32) + i%32 (+32 for W3)
+    const int64_t i = 64 * ib + r, j = 16 * jb + c0;
+    bf16_t* b = a.w13s + (u * 2 * h + 64 * (i / 32) + i % 32 + 32 * t) * (kr * FD);
+    put4(b + j, hi);
+    if (kr == 2) put4(b + FD + j, lo);
+  } else {      // W2 row j2, hidden columns i .. i+3
+    const int64_t j2 = 16 * jb + r, i = 64 * ib + c0;
+    bf16_t* b2 = a.w2s + (u * FD + j2) * (kr * h);
+    put4(b2 + i, hi);
+    if (kr == 2) put4(b2 + h + i, lo);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bf16_t* bt = a.w2ts + (u * h + i + e) * (kr * FD);
+      bt[j2] = hi[e];
+      if (kr == 2) bt[FD + j2] = lo[e];
+    }
+  }
 }
 
 }  // namespace e2ttt

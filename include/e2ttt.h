@@ -166,12 +166,14 @@ typedef enum {
 
 /* Benchmark instrumentation: enqueue exactly the work of e2ttt_chunk_forward
  * (same arguments, same results) and additionally record caller-created HIP
- * events (hipEvent_t, passed as void*) around every launch of one kernel
- * class: events[2j] just before and events[2j+1] just after the j-th launch
- * of that class, for j < n_events/2.  *n_recorded (may be NULL) receives the
- * number of launches bracketed.  The caller reads the elapsed times after
- * synchronising.  Same error behaviour as e2ttt_chunk_forward; EINVAL for a
- * bad kernel_class or n_events < 0. */
+ * events (hipEvent_t, passed as void*) on every launch of one kernel class:
+ * events[2j] at the start and events[2j+1] at the end of the j-th launch of
+ * that class, for j < n_events/2 (recorded with the kernel dispatch itself,
+ * so the elapsed time is the kernel's execution without the dispatch
+ * latency).  *n_recorded (may be NULL) receives the number of launches
+ * timed.  The caller reads the elapsed times after synchronising.  Same
+ * error behaviour as e2ttt_chunk_forward; EINVAL for a bad kernel_class or
+ * n_events < 0. */
 E2TTT_API e2ttt_status e2ttt_chunk_forward_timed(const e2ttt_problem* prob, const void* q,
                                        const void* k, const void* v,
                                        const float* eta, const float* alpha,

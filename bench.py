@@ -8,9 +8,11 @@ aggregations, chunk-end states), inputs already resident in HBM.
 Prints ONE JSON line:
   value         tokens/s = batch * seq_len / (time per step), N = 1 GPU
   roofline      dominant kernel: algorithmic flops per launch / its average
-                launch duration (HIP events around every launch of that
-                kernel, recorded by e2ttt_chunk_forward_timed in a second
-                timed pass of the same steps) against the published peak
+                launch duration (HIP events recorded at the start and end of
+                every launch of that kernel by e2ttt_chunk_forward_timed, in
+                a second timed pass of the same steps) against the published
+                peak; traffic = HBM bytes per launch from the committed
+                rocprofv3 counter summary when it matches the current code
   cpu_baseline  the fp64 oracle timed on this host's cores on a bounded
                 sample of the same workload, scaled to tokens/s
 """
@@ -34,6 +36,41 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def source_sha256():
+    """Hash of the HIP sources (kernels and host code): a committed traffic
+    measurement only counts for the code it was taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "chunk_weight_update_amd", "csrc")
+    for name in sorted(os.listdir(src)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            with open(os.path.join(src, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (profiles/traffic_<kernel>_
+    <workload>.txt, counters scaled by what they read for a copy kernel of
+    known size), or None when there is none or it was taken on other code."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != source_sha256():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 class HipEvents:
@@ -149,6 +186,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="skip the per-kernel event pass (for profiler runs)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed steps, run a plain device-to-device copy of this "
+                         "many MiB 5 times (the known-size reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -195,6 +235,17 @@ def main():
     value = tokens / (ms * 1e-3)
     log(f"bench: {args.steps} steps, {ms:.4f} ms/step, {value:.4g} tokens/s")
 
+    if args.copy_calibration_mib > 0:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"bench: copy calibration, 5 x {nbytes} bytes device to device")
+        del src, dst
+
     if args.no_kernel_timing:
         print(json.dumps({"metric": "TTT-layer fwd tokens/sec on 1 MI355X; MFMA util % of bf16 peak",
                           "value": value, "unit": "tokens/s", "ms_per_step": ms,
@@ -240,13 +291,14 @@ def main():
     peak_mfma = PEAK_BF16_TFLOPS if w.io == 1 else PEAK_FP32_TFLOPS
     dom_name = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     dk = kernels[dom_name]
+    traffic = measured_traffic(dom_name, w.name)
     if dk["work_unit"] == "flop":
         roof = {"kernel": dom_name, "bound": "mfma", "achieved": dk["tflops"],
                 "peak": peak_mfma, "unit": "TFLOP/s", "frac": dk["tflops"] / peak_mfma,
-                "traffic": None}
+                "traffic": traffic}
     else:
         roof = {"kernel": dom_name, "bound": "hbm", "achieved": dk["gbs"], "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": dk["gbs"] / PEAK_HBM_GBS, "traffic": None}
+                "unit": "GB/s", "frac": dk["gbs"] / PEAK_HBM_GBS, "traffic": traffic}
     flops = algorithmic_flops(w)
     line = {
         "metric": "TTT-layer fwd tokens/sec on 1 MI355X; MFMA util % of bf16 peak",

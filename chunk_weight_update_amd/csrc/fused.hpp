@@ -532,28 +532,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const float* kwr = a.kw + (u * a.nC + a.r) * a.Cp;
   const float* kmr = a.km + (u * a.nC + a.r) * a.Cp;
 
-  TileCopy<TB, FD, NT> ck, cg;          // token-major K, bf16(g)
-  TileCopy<FD, TB, NT> ckt, cgt;        // feature-major (permuted tokens) K^T, g^T
-  float sk = 0.0f;
-  auto load_tile = [&](int64_t t0) {
-    ck.load([&](int rr) -> const bf16_t* { return t0 + rr < nv ? Kg + (t0 + rr) * FD : nullptr; },
-            Kg);
-    cg.load([&](int rr) -> const bf16_t* { return Gg + (t0 + rr) * FD; });
-    ckt.load([&](int rr) -> const bf16_t* { return KTg + rr * a.Cp + t0; });
-    cgt.load([&](int rr) -> const bf16_t* { return GTg + rr * a.Cp + t0; });
+  // Registers of one tile in flight from global memory.
+  struct TileRegs {
+    TileCopy<TB, FD, NT> k, g;    // token-major K, bf16(g)
+    TileCopy<FD, TB, NT> kt, gt;  // feature-major (permuted tokens) K^T, g^T
+    float sk;                     // K^W (first TB) and K^M (next TB) of the tile
+  };
+  auto load_tile = [&](TileRegs& R, int64_t t0) {
+    R.k.load([&](int rr) -> const bf16_t* { return t0 + rr < nv ? Kg + (t0 + rr) * FD : nullptr; },
+             Kg);
+    R.g.load([&](int rr) -> const bf16_t* { return Gg + (t0 + rr) * FD; });
+    R.kt.load([&](int rr) -> const bf16_t* { return KTg + rr * a.Cp + t0; });
+    R.gt.load([&](int rr) -> const bf16_t* { return GTg + rr * a.Cp + t0; });
     // Every wave loads (and stores) the same 2*TB kernel values, so no lane
     // mask splits the loop body into several scheduling regions.
     const int ks_i = threadIdx.x & (2 * TB - 1);
-    sk = (ks_i < TB ? kwr : kmr - TB)[t0 + ks_i];
+    R.sk = (ks_i < TB ? kwr : kmr - TB)[t0 + ks_i];
   };
-  auto store_tile = [&](int b) {
+  auto store_tile = [&](const TileRegs& R, int b) {
     bf16_t* B = bufp(b);
-    ck.store(B, KS);
-    cg.store(B + TB * KS, KS);
-    ckt.store(B + 2 * TB * KS, TS);
-    cgt.store(B + 2 * TB * KS + FD * TS, TS);
-    kscp(b)[threadIdx.x & (2 * TB - 1)] = sk;
+    R.k.store(B, KS);
+    R.g.store(B + TB * KS, KS);
+    R.kt.store(B + 2 * TB * KS, TS);
+    R.gt.store(B + 2 * TB * KS + FD * TS, TS);
+    kscp(b)[threadIdx.x & (2 * TB - 1)] = R.sk;
   };
+  TileRegs tr;
 
   // This workgroup's token tiles: split sp of nsplit (the host picks nsplit
   // dividing Cp / TB).
@@ -734,11 +738,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // overlaps the MFMAs of the other; tile it+2 is in flight from global
     // memory meanwhile and lands in the buffer tile it-1 used.  The recompute
     // past the last tile reads a stale (in-bounds) buffer and is discarded.
-    load_tile(tbase);
-    store_tile(0);
-    if (ntiles > 1) {
-      load_tile(tbase + TB);
-      store_tile(1);
+    {  // the first two tiles' loads in flight together
+      TileRegs tr1;
+      load_tile(tr, tbase);
+      if (ntiles > 1) load_tile(tr1, tbase + TB);
+      store_tile(tr, 0);
+      if (ntiles > 1) store_tile(tr1, 1);
     }
     __syncthreads();
     Frags f = elementwise(recompute(bufp(0)), kscp(0));
@@ -749,25 +754,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const int bn = bc == 2 ? 0 : bc + 1;  // tile it+1
       const int bnn = bn == 2 ? 0 : bn + 1; // tile it+2 (= tile it-1's)
       const int tl = it + 2 < ntiles ? it + 2 : ntiles - 1;
-      load_tile(tbase + static_cast<int64_t>(tl) * TB);
+      load_tile(tr, tbase + static_cast<int64_t>(tl) * TB);
       const Rec rn = recompute(bufp(bn));
       f = aggregate_next(f, bufp(bc), rn, kscp(bn));
-      store_tile(bnn);
+      store_tile(tr, bnn);
       __syncthreads();
       bc = bn;
     }
   } else {
-    load_tile(tbase);
-    store_tile(0);
+    load_tile(tr, tbase);
+    store_tile(tr, 0);
     __syncthreads();
     for (int it = 0; it < ntiles; ++it) {
       const int b = S::NBUF == 2 ? (it & 1) : 0;
-      if (it + 1 < ntiles) load_tile(tbase + static_cast<int64_t>(it + 1) * TB);
+      if (it + 1 < ntiles) load_tile(tr, tbase + static_cast<int64_t>(it + 1) * TB);
       aggregate(elementwise(recompute(bufp(b)), kscp(b)), bufp(b));
       if (S::NBUF == 1) __syncthreads();  // single buffer: everyone is done reading it
       if (it + 1 < ntiles) {
         // With two buffers, b^1 was last read in iteration it-1 (barrier since).
-        store_tile(S::NBUF == 2 ? (b ^ 1) : 0);
+        store_tile(tr, S::NBUF == 2 ? (b ^ 1) : 0);
       }
       __syncthreads();
     }
@@ -842,6 +847,17 @@ __global__ __launch_bounds__(256) void k_state_epi(FusedArgs a) {
   const int tid = threadIdx.x;
   const int64_t nib = a.h / 64;
   const int64_t u = grp / nib, ib = grp % nib;
+  const int64_t P = 3 * FD * a.h;
+  const int64_t h = a.h;
+  // After the transpose this thread owns columns c0 .. c0+3 of block row r;
+  // their start values are loaded first, in flight with the partial sums.
+  const int CC = t < 2 ? 16 : 64;  // columns of the block
+  const int r = tid / (CC / 4), c0 = 4 * (tid % (CC / 4));
+  int64_t off;  // of the first of the four entries, inside the unit's state
+  if (t < 2) off = t * h * FD + (64 * ib + r) * FD + 16 * jb + c0;
+  else off = 2 * h * FD + (16 * jb + r) * h + 64 * ib + c0;
+  const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(a.Win + u * P + off);
+  const f32x4_t m0 = *reinterpret_cast<const f32x4_t*>(a.Min + u * P + off);
   const int qW = 16 * t + jb, qM = qW + 8;
   const f32x4_t* src = reinterpret_cast<const f32x4_t*>(a.part) + grp * a.nsplit * (48 * 256);
   f32x4_t sw = src[qW * 256 + tid], sm = src[qM * 256 + tid];
@@ -849,33 +865,24 @@ __global__ __launch_bounds__(256) void k_state_epi(FusedArgs a) {
     sw += src[sp * (48 * 256) + qW * 256 + tid];
     sm += src[sp * (48 * 256) + qM * 256 + tid];
   }
-  // Block-local coordinates (row r, column c) of accumulator register v.
+  // Block-local coordinates (row, column) of phase B register v.
   const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
-  const int CC = t < 2 ? 16 : 64;  // columns of the block
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const int r = t < 2 ? 16 * wave + 4 * g4 + v : 4 * g4 + v;
-    const int c = t < 2 ? l16 : 16 * wave + l16;
-    sW[r * (CC + 1) + c] = sw[v];
-    sM[r * (CC + 1) + c] = sm[v];
+    const int rr = t < 2 ? 16 * wave + 4 * g4 + v : 4 * g4 + v;
+    const int cc = t < 2 ? l16 : 16 * wave + l16;
+    sW[rr * (CC + 1) + cc] = sw[v];
+    sM[rr * (CC + 1) + cc] = sm[v];
   }
   __syncthreads();
-  const int r = tid / (CC / 4), c0 = 4 * (tid % (CC / 4));
   f32x4_t aw, am;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     aw[e] = sW[r * (CC + 1) + c0 + e];
     am[e] = sM[r * (CC + 1) + c0 + e];
   }
-  const int64_t P = 3 * FD * a.h;
-  const int64_t h = a.h;
-  int64_t off;  // of the first of the four entries, inside the unit's state
-  if (t < 2) off = t * h * FD + (64 * ib + r) * FD + 16 * jb + c0;
-  else off = 2 * h * FD + (16 * jb + r) * h + 64 * ib + c0;
   const float* cf = a.coef + (u * a.nC + a.r) * 4;
   const float cW = cf[0], cM = cf[1], cWM = cf[2];
-  const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(a.Win + u * P + off);
-  const f32x4_t m0 = *reinterpret_cast<const f32x4_t*>(a.Min + u * P + off);
   f32x4_t wn, mn;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {

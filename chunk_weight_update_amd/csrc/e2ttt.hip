@@ -40,7 +40,8 @@ struct Plan {
   int64_t B, H, BH, L, d, h, C, Cp, nC, P;
   int kind, io, mode, krep;
   bool fused;   // two-kernel chunk step (SwiGLU, d = 128, bf16 io)
-  int rbA;      // phase A rows per workgroup (32 or 64)
+  int rbA;      // phase A rows per workgroup (32 or 64; LDS-streamed variant)
+  int wpuA;     // register-resident phase A: workgroups per unit (0: not used)
   int nsplitB;  // phase B token split (1: fused state epilogue)
   size_t opsz;  // bytes per GEMM operand element (2 for bf16, 4 for fp32)
   // workspace offsets (bytes)
@@ -109,6 +110,21 @@ e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
     q.opsz = 2;
     q.krep = (p->flags & E2TTT_FLAG_COMPENSATED_WEIGHTS) ? 2 : 1;
     q.rbA = (q.krep == 2 || q.BH * (2 * q.Cp / 64) >= 512) ? 64 : 32;
+    // Register-resident phase A (plain bf16 operands, h = 128 or 256): about
+    // one workgroup per CU, each taking a contiguous run of one unit's 32-row
+    // tiles (the count divides the unit's tiles so none is left empty).  Used
+    // when a workgroup gets at least two tiles; with one tile each the load of
+    // every wave's weights is not amortised and the LDS-streamed variant, which
+    // overlaps the second hidden block's weights with the first block's
+    // compute, is faster (measured).
+    q.wpuA = 0;
+    if (q.krep == 1 && (q.h == 128 || q.h == 256)) {
+      const int64_t ntA = 2 * q.Cp / 32;
+      int64_t w = (kCUs + q.BH - 1) / q.BH;
+      if (w > ntA) w = ntA;
+      while (ntA % w != 0) --w;
+      if (ntA / w >= 2) q.wpuA = static_cast<int>(w);
+    }
     const size_t T = q.opsz;
     q.kw = take(f4 * q.BH * q.nC * q.Cp);
     q.km = take(f4 * q.BH * q.nC * q.Cp);
@@ -193,7 +209,8 @@ void set_lds_attributes() {
   const void* fused_kernels[] = {
       reinterpret_cast<const void*>(&k_phaseA<32, 1>), reinterpret_cast<const void*>(&k_phaseA<64, 1>),
       reinterpret_cast<const void*>(&k_phaseA<64, 2>), reinterpret_cast<const void*>(&k_phaseB<1>),
-      reinterpret_cast<const void*>(&k_phaseB<2>)};
+      reinterpret_cast<const void*>(&k_phaseB<2>), reinterpret_cast<const void*>(&k_phaseA2<32>),
+      reinterpret_cast<const void*>(&k_phaseA2<64>)};
   for (const void* f : fused_kernels)
     (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   g_attr_done.store(1, std::memory_order_release);
@@ -334,7 +351,13 @@ void launch_fused(const Plan& q, const void* qv, const void* kv, const void* vv,
     const size_t ldsA = q.krep == 2 ? PhaseACfg<64, 2>::LDS_BYTES
                         : (q.rbA == 64 ? PhaseACfg<64, 1>::LDS_BYTES : PhaseACfg<32, 1>::LDS_BYTES);
     void (*kB)(FusedArgs) = q.krep == 2 ? k_phaseB<2> : k_phaseB<1>;
-    E2TTT_LAUNCH(I, E2TTT_KERNEL_PHASE_A, kA, dim3(gA), dim3(256), ldsA, st, a);
+    if (q.wpuA > 0) {
+      void (*kA2)(FusedArgs, int) = q.h == 256 ? k_phaseA2<64> : k_phaseA2<32>;
+      E2TTT_LAUNCH(I, E2TTT_KERNEL_PHASE_A, kA2, dim3(grid1(q.BH * q.wpuA)), dim3(256),
+                   PhaseA2Cfg::LDS_BYTES, st, a, q.wpuA);
+    } else {
+      E2TTT_LAUNCH(I, E2TTT_KERNEL_PHASE_A, kA, dim3(gA), dim3(256), ldsA, st, a);
+    }
     const size_t ldsB = q.krep == 2 ? PhaseBCfg<2>::LDS_BYTES : PhaseBCfg<1>::LDS_BYTES;
     E2TTT_LAUNCH(I, E2TTT_KERNEL_PHASE_B, kB, dim3(gB), dim3(256), ldsB, st, a);
     if (q.nsplitB > 1)

@@ -357,6 +357,289 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 }
 
 // ---------------------------------------------------------------------------
+// Phase A, register-resident variant (bf16 operands without hi/lo, h = 4*HW,
+// HW in {32, 64}).  Wave w keeps the weights of its HW hidden units in
+// registers for the whole launch (W1, W3 rows and W2 columns of units
+// w*HW .. w*HW+HW-1, as 32x32x16 MFMA A-fragments), so no weight passes
+// through LDS.  A workgroup takes the rows of one (batch, head) unit in
+// tiles of 32 ([K; Q] rows of the chunk; a tile is all K or all Q rows):
+//   GEMM1 (transposed): A1^T, A3^T [hidden x token] = W1, W3 [hidden x d] X^T;
+//   Z^T = silu(A1^T) * A3^T, rounded to bf16 in registers: a 32x32
+//     accumulator gives lane l token l%32 and hidden rows 8*(v/4) + 4*(l/32)
+//     + v%4, so registers 8*(kb%2) .. +7 of m-block kb/2 are exactly the
+//     B-fragment of hidden k-block kb, taken in the order
+//     {4*(l/32) + 0..3, 8 + 4*(l/32) + 0..3}; the W2 A-fragments are loaded in
+//     that same order;
+//   GEMM2 (transposed): the wave's partial Y^T [d x token] = W2[:, its units]
+//     Z^T over its HW units.
+// The four partials meet in LDS (fp32) and the epilogue adds them in wave
+// order and writes out = bf16(Y) (Q rows) or g = bf16(v - Y) token-major and
+// feature-major (K rows), all as 16-byte vectors.  The next tile's X rows
+// are loaded while the current tile computes.
+struct PhaseA2Cfg {
+  static constexpr int TR = 32;      // rows per tile
+  static constexpr int YW = FD + 4;  // fp32 row stride of one wave's Y partial
+  static constexpr int GW = TR + 8;  // g^T staging row stride (bf16)
+  static constexpr size_t Y_BYTES = static_cast<size_t>(4) * TR * YW * 4;
+  static constexpr size_t LDS_BYTES = Y_BYTES + static_cast<size_t>(FD) * GW * 2;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <int HW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_phaseA2(
+    FusedArgs a, int wpu) {
+  typedef PhaseA2Cfg P;
+  constexpr int TR = P::TR;
+  constexpr int MB = HW / 32;  // 32-unit m-blocks of GEMM1 per wave
+  constexpr int KB2 = HW / 16; // 16-unit k-blocks of GEMM2 per wave
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  float* Yp = reinterpret_cast<float*>(smem_raw);                 // [4][TR][YW]
+  bf16_t* Tg = reinterpret_cast<bf16_t*>(smem_raw + P::Y_BYTES);  // [FD][GW]
+
+  const int64_t u = blockIdx.x / wpu;
+  const int g = static_cast<int>(blockIdx.x % wpu);
+  const int ntile = static_cast<int>(2 * a.Cp / TR);  // tiles of the unit: K rows, then Q rows
+  const int per = (ntile + wpu - 1) / wpu;
+  const int tb = g * per;
+  const int te = tb + per < ntile ? tb + per : ntile;
+  const int64_t tok0 = static_cast<int64_t>(a.r) * a.C;
+  const int64_t nv = fused_nvalid(a);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l32 = lane & 31, hf = lane >> 5;
+
+  // X rows of a tile as GEMM1 B-fragments: lane l holds row l%32, d 16*kb + 8*hf .. +8.
+  // Rows past the valid tokens are zero.  The loads are predicated rather than
+  // selected afterwards: a select right after a load would make the wave
+  // wait for the prefetch at once.
+  auto load_x = [&](int t, bf16x8_t (&x)[8]) {
+    const bool isQ = t * TR >= a.Cp;
+    const int64_t p = t * TR - (isQ ? a.Cp : 0) + l32;
+    const bf16_t* src = (isQ ? a.q : a.k) + (u * a.L + tok0 + p) * FD + 8 * hf;
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) x[kb] = bf16x8_t{};
+    if (p < nv) {
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) x[kb] = *reinterpret_cast<const bf16x8_t*>(src + 16 * kb);
+    }
+  };
+  // v of a K tile for the epilogue: thread slot e takes (row, 8-column chunk)
+  // idx = threadIdx.x + 256*e of the tile's TR x FD/8 chunks.
+  constexpr int VPR = FD / 8;
+  constexpr int EPT = TR * VPR / 256;  // epilogue chunks per thread
+  const bf16_t* vsrc = a.v + (u * a.L + tok0) * FD;
+  auto load_v = [&](int t, uint4 (&vv)[EPT]) {
+    const bool isQ = t * TR >= a.Cp;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int idx = threadIdx.x + 256 * e;
+      const int64_t p = t * TR + idx / VPR;
+      uint4 x = make_uint4(0u, 0u, 0u, 0u);
+      if (!isQ && p < nv) x = *reinterpret_cast<const uint4*>(vsrc + p * FD + (idx % VPR) * 8);
+      vv[e] = x;
+    }
+  };
+
+  // First tile's inputs, then the weights: GEMM1 waits for X and W1/W3 only
+  // while W2 is still in flight (loads complete in issue order).
+  bf16x8_t xc[8], xn[8];
+  uint4 vc[EPT], vn[EPT];
+  if (tb < te) {
+    load_v(tb, vc);
+    load_x(tb, xc);
+  }
+  bf16x8_t w13[MB][2][8];  // [m-block][W1, W3][d k-block]
+  bf16x8_t w2[4][KB2];     // [d m-block of 32][hidden k-block of 16]
+  {
+    const bf16_t* W13 = a.w13s + u * 2 * a.h * FD;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int64_t i = wave * HW + 32 * mb + l32;  // hidden unit of this lane
+      const bf16_t* r1 = W13 + (64 * (i / 32) + i % 32) * FD + 8 * hf;
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        w13[mb][0][kb] = *reinterpret_cast<const bf16x8_t*>(r1 + 16 * kb);
+        w13[mb][1][kb] = *reinterpret_cast<const bf16x8_t*>(r1 + 32 * FD + 16 * kb);
+      }
+    }
+    const bf16_t* W2 = a.w2s + u * FD * a.h;
+#pragma unroll
+    for (int jm = 0; jm < 4; ++jm) {
+      const bf16_t* rj = W2 + (32 * jm + l32) * a.h + wave * HW;
+#pragma unroll
+      for (int kb = 0; kb < KB2; ++kb) {
+        const bf16x4_t lo = *reinterpret_cast<const bf16x4_t*>(rj + 16 * kb + 4 * hf);
+        const bf16x4_t hi = *reinterpret_cast<const bf16x4_t*>(rj + 16 * kb + 8 + 4 * hf);
+        bf16x8_t f;
+        f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+        f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+        w2[jm][kb] = f;
+      }
+    }
+  }
+
+  for (int t = tb; t < te; ++t) {
+    if (t + 1 < te) {  // next tile's inputs, in flight during this tile
+      load_v(t + 1, vn);
+      load_x(t + 1, xn);
+    }
+    f32x16_t y[4];
+#pragma unroll
+    for (int jm = 0; jm < 4; ++jm) zero16(y[jm]);
+    bf16x8_t zf[KB2];
+    // z of accumulator registers r, r+1, rounded and packed; the empty asm
+    // pins the arithmetic here, inside the MFMA shadow it is interleaved with
+    // (pure arithmetic would otherwise be sunk to its first use).
+    auto zpair = [](const f32x16_t& a1, const f32x16_t& a3, int r) -> uint32_t {
+      const float x0 = a1[r], x1 = a1[r + 1];
+      uint32_t w = pack_bf16x2(x0 * sigmoidf_(x0) * a3[r], x1 * sigmoidf_(x1) * a3[r + 1]);
+      asm volatile("" : "+v"(w));
+      return w;
+    };
+    if constexpr (MB == 2) {
+      // GEMM1 of m-block 0; GEMM1 of m-block 1 interleaved with Z of m-block
+      // 0; GEMM2 over k-blocks 0, 1 interleaved with Z of m-block 1; GEMM2
+      // over k-blocks 2, 3.
+      f32x16_t a1[2], a3[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        zero16(a1[mb]);
+        zero16(a3[mb]);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        a1[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w13[0][0][kb], xc[kb], a1[0], 0, 0, 0);
+        a3[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w13[0][1][kb], xc[kb], a3[0], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      u32x4_t zp[4];
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        a1[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w13[1][0][kb], xc[kb], a1[1], 0, 0, 0);
+        a3[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w13[1][1][kb], xc[kb], a3[1], 0, 0, 0);
+        zp[kb >> 2][kb & 3] = zpair(a1[0], a3[0], 2 * kb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      zf[0] = __builtin_bit_cast(bf16x8_t, zp[0]);
+      zf[1] = __builtin_bit_cast(bf16x8_t, zp[1]);
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const int jm = st >> 1, kb = st & 1;
+        y[jm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w2[jm][kb], zf[kb], y[jm], 0, 0, 0);
+        zp[2 + (st >> 2)][st & 3] = zpair(a1[1], a3[1], 2 * st);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      zf[2] = __builtin_bit_cast(bf16x8_t, zp[2]);
+      zf[3] = __builtin_bit_cast(bf16x8_t, zp[3]);
+#pragma unroll
+      for (int jm = 0; jm < 4; ++jm)
+#pragma unroll
+        for (int kb = 2; kb < 4; ++kb)
+          y[jm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w2[jm][kb], zf[kb], y[jm], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        f32x16_t a1, a3;
+        zero16(a1);
+        zero16(a3);
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+          a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w13[mb][0][kb], xc[kb], a1, 0, 0, 0);
+          a3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w13[mb][1][kb], xc[kb], a3, 0, 0, 0);
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          u32x4_t zq;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) zq[q] = zpair(a1, a3, 8 * h2 + 2 * q);
+          zf[2 * mb + h2] = __builtin_bit_cast(bf16x8_t, zq);
+        }
+      }
+#pragma unroll
+      for (int jm = 0; jm < 4; ++jm)
+#pragma unroll
+        for (int kb = 0; kb < KB2; ++kb)
+          y[jm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w2[jm][kb], zf[kb], y[jm], 0, 0, 0);
+    }
+    // Partial to LDS as [wave][token][j]: registers 4q .. 4q+3 are four
+    // consecutive j of one token.
+    float* yw = Yp + (wave * TR + l32) * P::YW;
+#pragma unroll
+    for (int jm = 0; jm < 4; ++jm)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4_t v4;
+        v4[0] = y[jm][4 * q]; v4[1] = y[jm][4 * q + 1]; v4[2] = y[jm][4 * q + 2]; v4[3] = y[jm][4 * q + 3];
+        *reinterpret_cast<f32x4_t*>(yw + 32 * jm + 8 * q + 4 * hf) = v4;
+      }
+    __syncthreads();
+    // Epilogue of the tile.
+    const bool isQ = t * TR >= a.Cp;
+    const int64_t p0 = t * TR - (isQ ? a.Cp : 0);
+    bf16_t* gdst = a.gbf + u * a.Cp * FD;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int idx = threadIdx.x + 256 * e;
+      const int pr = idx / VPR, c = idx % VPR;
+      const int64_t p = p0 + pr;
+      const uint4 vin = vc[e];
+      float yv[8];
+      {
+        const float* s0 = Yp + pr * P::YW + c * 8;
+        f32x4_t lo = *reinterpret_cast<const f32x4_t*>(s0);
+        f32x4_t hi = *reinterpret_cast<const f32x4_t*>(s0 + 4);
+#pragma unroll
+        for (int w = 1; w < 4; ++w) {
+          lo += *reinterpret_cast<const f32x4_t*>(s0 + w * TR * P::YW);
+          hi += *reinterpret_cast<const f32x4_t*>(s0 + w * TR * P::YW + 4);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          yv[e] = lo[e];
+          yv[4 + e] = hi[e];
+        }
+      }
+      if (isQ) {
+        if (p < nv) {
+          uint4 o;
+          o.x = pack_bf16x2(yv[0], yv[1]);
+          o.y = pack_bf16x2(yv[2], yv[3]);
+          o.z = pack_bf16x2(yv[4], yv[5]);
+          o.w = pack_bf16x2(yv[6], yv[7]);
+          *reinterpret_cast<uint4*>(a.out + (u * a.L + tok0 + p) * FD + c * 8) = o;
+        }
+      } else {
+        const uint32_t vw[4] = {vin.x, vin.y, vin.z, vin.w};
+        uint32_t gw[4];
+        const int col = tok_perm32(pr);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v0 = __uint_as_float(vw[e] << 16), v1 = __uint_as_float(vw[e] & 0xffff0000u);
+          gw[e] = pack_bf16x2(v0 - yv[2 * e], v1 - yv[2 * e + 1]);
+          Tg[(c * 8 + 2 * e) * P::GW + col] = static_cast<bf16_t>(gw[e] & 0xffffu);
+          Tg[(c * 8 + 2 * e + 1) * P::GW + col] = static_cast<bf16_t>(gw[e] >> 16);
+        }
+        *reinterpret_cast<uint4*>(gdst + p * FD + c * 8) = make_uint4(gw[0], gw[1], gw[2], gw[3]);
+      }
+    }
+    __syncthreads();
+    if (!isQ) {
+      constexpr int VPT = TR / 8;
+      for (int idx = threadIdx.x; idx < FD * VPT; idx += 256) {
+        const int j = idx / VPT, c = idx % VPT;
+        *reinterpret_cast<uint4*>(a.gft + (u * FD + j) * a.Cp + p0 + c * 8) =
+            *reinterpret_cast<const uint4*>(Tg + j * P::GW + c * 8);
+      }
+    }
+    if (t + 1 < te) {
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) xc[kb] = xn[kb];
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) vc[e] = vn[e];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Phase B.  LDS: for the hi/lo variant (KREP = 2) the recompute weights of
 // the workgroup's 64 hidden units ([4 waves][W1, W3, W2^T][16][KREP*FD + 8]);
 // with KREP = 1 they live in registers.  Then NBUF token-tile buffers (three

@@ -159,6 +159,13 @@ def test_swiglu_bf16_many_units_unsplit():
           m0_scale=M0["nearunit"])
 
 
+def test_swiglu_bf16_register_resident_phase_a():
+    """64 units: several 32-row tiles per phase A workgroup (the variant with
+    register-resident weights, h = 256), two chunks, the second ragged."""
+    check(SWIGLU, 2, 32, 200, 128, 256, 128, BF16, seed=8, regime="nearunit",
+          m0_scale=M0["nearunit"])
+
+
 def test_swiglu_alpha_is_gamma_fp32():
     check(SWIGLU, 1, 2, 384, 128, 128, 128, F32, seed=5, regime="nearunit",
           m0_scale=M0["nearunit"], decay_mode=1)

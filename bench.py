@@ -139,6 +139,40 @@ def kernel_work(w, cls):
     return 0.0, "byte"
 
 
+def scan_microbench(reps=10):
+    """The scalar-kernel scan alone at 2^26 token-heads (B64 x H16 x L65536,
+    C = 2048: 32768 segments), through e2ttt_scalar_kernels, seeded synthetic
+    scalars drawn as in the workloads.  The in-situ scan of the bench workload
+    moves under 1 MB, so its rate says little about the kernel; this one is
+    sized for HBM.  Algorithmic bytes: 20 per token-head."""
+    import torch
+    import chunk_weight_update_amd as cwu
+    B, H, L, C = 64, 16, 65536, 2048
+    g = torch.Generator(device="cuda").manual_seed(0)
+    shp = (B, H, L)
+    eta = 0.1 * torch.sigmoid(torch.randn(shp, generator=g, device="cuda"))
+    alpha = 1.0 - 0.05 * torch.sigmoid(torch.randn(shp, generator=g, device="cuda"))
+    beta = 0.9 * torch.sigmoid(torch.randn(shp, generator=g, device="cuda"))
+    kw = torch.empty(shp, device="cuda")
+    km = torch.empty(shp, device="cuda")
+    cf = torch.empty((B, H, L // C, 3), device="cuda")
+    prob = cwu.make_problem(cwu.LINEAR, B, H, L, 16, 0, C, cwu.F32, 0)
+    for _ in range(2):
+        cwu.scalar_kernels(prob, eta, alpha, beta, kw, km, cf)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        cwu.scalar_kernels(prob, eta, alpha, beta, kw, km, cf)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbs = 20.0 * B * H * L / (ms * 1e-3) / 1e9
+    return {"label": "scan-only microbenchmark, 2^26 token-heads (not the bench workload)",
+            "shape": {"batch": B, "heads": H, "seq_len": L, "chunk": C}, "ms": ms,
+            "gbs": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS}
+
+
 def algorithmic_flops(w):
     if w.kind == 0:
         return 8.0 * w.d * w.d * w.L * w.B * w.H
@@ -186,6 +220,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="skip the per-kernel event pass (for profiler runs)")
+    ap.add_argument("--no-scan-microbench", action="store_true",
+                    help="skip the 2^26-token scan microbenchmark")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, run a plain device-to-device copy of this "
                          "many MiB 5 times (the known-size reference for HBM byte counters)")
@@ -311,6 +347,9 @@ def main():
         "roofline": roof,
         "kernels": kernels,
     }
+    if not args.no_scan_microbench:
+        line["scan_microbench"] = scan_microbench()
+        log(f"bench: scan microbenchmark {line['scan_microbench']}")
     if not args.no_cpu_baseline:
         log("bench: timing the fp64 oracle on the host cores")
         line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)

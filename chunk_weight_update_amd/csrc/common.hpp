@@ -11,6 +11,7 @@ typedef uint16_t bf16_t;  // bf16 storage (upper half of an fp32)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf2f(bf16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);

@@ -18,6 +18,7 @@
 
 #include "e2ttt.h"
 #include "kernels.hpp"
+#include "gemm256.hpp"
 #include "fused.hpp"
 
 using namespace e2ttt;
@@ -42,11 +43,12 @@ struct Plan {
   bool fused;   // two-kernel chunk step (SwiGLU, d = 128, bf16 io)
   int rbA;      // phase A rows per workgroup (32 or 64; LDS-streamed variant)
   int wpuA;     // register-resident phase A: workgroups per unit (0: not used)
+  int nsplitAgg;  // generic bf16 path: token split of the 256x256-tile aggregation (0: 128x128 tiles)
   int nsplitB;  // phase B token split (1: fused state epilogue)
   size_t opsz;  // bytes per GEMM operand element (2 for bf16, 4 for fp32)
   // workspace offsets (bytes)
   size_t kw, km, coef, kt, w13s, w2s, w2ts, zrow, a1s, a3s, grow, ut, gt, zt, gw, gm, gbf, gft,
-      part, total;
+      part, part256, total;
 };
 
 e2ttt_status check_problem(const e2ttt_problem* p) {
@@ -163,6 +165,18 @@ e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
     q.ut = take(T * q.BH * 4 * q.h * q.Cp);
     q.gt = take(T * q.BH * 2 * q.d * q.Cp);
     q.zt = take(T * q.BH * q.h * q.Cp);
+    // bf16 operands with d, h multiples of 256: the aggregation runs on
+    // 256x256 tiles; the chunk's token slabs are split so that the grid comes
+    // close to one workgroup per CU, and k_agg_reduce adds the splits.
+    q.nsplitAgg = 0;
+    if (q.io == E2TTT_BF16 && q.d % 256 == 0 && q.h % 256 == 0) {
+      const int64_t tiles = q.BH * ((4 * q.h / 256) * (q.d / 256) + (2 * q.d / 256) * (q.h / 256));
+      int S = 1;
+      // (S divides the slab count, so every split has at least one slab)
+      while (S < 8 && tiles * S * 2 <= kCUs && (q.Cp / 32) % (S * 2) == 0) S *= 2;
+      q.nsplitAgg = S;
+      q.part256 = take(f4 * static_cast<size_t>(S) * 2 * q.BH * q.P);
+    }
   }
   q.total = q.L == 0 ? 0 : o;  // an empty sequence only copies the state
   return E2TTT_OK;
@@ -210,7 +224,7 @@ void set_lds_attributes() {
       reinterpret_cast<const void*>(&k_phaseA<32, 1>), reinterpret_cast<const void*>(&k_phaseA<64, 1>),
       reinterpret_cast<const void*>(&k_phaseA<64, 2>), reinterpret_cast<const void*>(&k_phaseB<1>),
       reinterpret_cast<const void*>(&k_phaseB<2>), reinterpret_cast<const void*>(&k_phaseA2<32>),
-      reinterpret_cast<const void*>(&k_phaseA2<64>)};
+      reinterpret_cast<const void*>(&k_phaseA2<64>), reinterpret_cast<const void*>(&k_agg256)};
   for (const void* f : fused_kernels)
     (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   g_attr_done.store(1, std::memory_order_release);
@@ -253,6 +267,26 @@ void launch_scan(const Plan& q, const float* eta, const float* alpha, const floa
                  float* coef, int cstride, hipStream_t st, Instr& I) {
   E2TTT_LAUNCH(I, E2TTT_KERNEL_SCAN, k_scan, dim3(grid1(q.BH * q.nC)), dim3(SCAN_NT), 0, st, eta,
                alpha, beta, q.L, q.C, q.nC, q.mode, kw, km, ustride, rstride, pad, coef, cstride);
+}
+
+// 256x256-tile aggregation with a token split, then the split-sum state
+// epilogue (bf16 operands only).
+template <typename T>
+void launch_agg256(const Plan& q, const Shape& s, int r, int last, const T* ut, const T* kt,
+                   const T* gt, const T* zt, const float* coef, const float* Win,
+                   const float* Min, float* Wend, float* Mend, T* w13s, T* w2s, T* w2ts,
+                   float* part, hipStream_t st, Instr& I) {
+  static_assert(sizeof(T) == 2 || sizeof(T) == 4, "operand type");
+  if constexpr (sizeof(T) == 2) {
+    const int64_t tiles = (4 * q.h / 256) * (q.d / 256) + (2 * q.d / 256) * (q.h / 256);
+    E2TTT_LAUNCH(I, E2TTT_KERNEL_AGG, k_agg256, dim3(grid1(q.BH * tiles * q.nsplitAgg)),
+                 dim3(256), Tile256::LDS_BYTES, st, s, q.nsplitAgg, ut, kt, gt, zt, r, part);
+    void (*kred)(Shape, int, int, int, const float*, const float*, const float*, const float*,
+                 float*, float*, T*, T*, T*) = k_agg_reduce<T>;
+    E2TTT_LAUNCH(I, E2TTT_KERNEL_STATE, kred, dim3(grid1((q.BH * q.P / 4 + 255) / 256)),
+                 dim3(256), 0, st, s, q.nsplitAgg, r, last, part, coef, Win, Min, Wend, Mend,
+                 w13s, w2s, w2ts);
+  }
 }
 
 template <typename T>
@@ -299,9 +333,14 @@ void launch_swiglu(const Plan& q, const void* qv, const void* kv, const void* vv
                  O, zrow, w2s, kw, km, grow, gt);
     E2TTT_LAUNCH(I, E2TTT_KERNEL_BWD, k_bwd<T>, dim3(grid1(q.BH * (q.Cp / 128) * (q.h / 128))),
                  dim3(256), 0, st, s, ri, grow, w2ts, a1s, a3s, kw, km, ut);
-    E2TTT_LAUNCH(I, E2TTT_KERNEL_AGG, k_agg<T>, dim3(grid1(q.BH * (na + nb))), dim3(256), 0, st,
-                 s, ri, static_cast<int>(r == q.nC - 1), ut, kt, gt, zt, coef, Win, Min, Wend,
-                 Mend, w13s, w2s, w2ts);
+    if (q.nsplitAgg > 0) {  // the plan sets nsplitAgg for bf16 operands only
+      launch_agg256(q, s, ri, static_cast<int>(r == q.nC - 1), ut, kt, gt, zt, coef, Win, Min,
+                    Wend, Mend, w13s, w2s, w2ts, reinterpret_cast<float*>(ws + q.part256), st, I);
+    } else {
+      E2TTT_LAUNCH(I, E2TTT_KERNEL_AGG, k_agg<T>, dim3(grid1(q.BH * (na + nb))), dim3(256), 0,
+                   st, s, ri, static_cast<int>(r == q.nC - 1), ut, kt, gt, zt, coef, Win, Min,
+                   Wend, Mend, w13s, w2s, w2ts);
+    }
   }
 }
 

@@ -50,7 +50,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   f32x2_t v = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 struct FusedArgs {
   int64_t BH, L, h, C, Cp, nC;

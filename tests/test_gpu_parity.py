@@ -166,6 +166,14 @@ def test_swiglu_bf16_register_resident_phase_a():
           m0_scale=M0["nearunit"])
 
 
+@pytest.mark.parametrize("L,C", [(700, 256), (512, 512)])
+def test_swiglu_bf16_d256_tiled_aggregation(L, C):
+    """d = 256, h = 512 bf16: the 256x256-tile aggregation with a token
+    split and the split-sum state epilogue (generic path)."""
+    check(SWIGLU, 1, 2, L, 256, 512, C, BF16, seed=9, regime="nearunit",
+          m0_scale=M0["nearunit"])
+
+
 def test_swiglu_alpha_is_gamma_fp32():
     check(SWIGLU, 1, 2, 384, 128, 128, 128, F32, seed=5, regime="nearunit",
           m0_scale=M0["nearunit"], decay_mode=1)

@@ -39,6 +39,18 @@ __device__ __forceinline__ float sigmoidf_(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
+// Logical workgroup index for an XCD-aware layout.  gfx950 hands consecutive
+// workgroups of a grid to its 8 XCDs in turn, and each XCD has its own L2, so
+// workgroups that read the same data (the hidden blocks of one unit, the
+// row tiles of one unit's weights) are numbered so that each XCD receives a
+// contiguous logical range: physical b -> (b % 8) * (G / 8) + b / 8.  A
+// bijection on [0, G) when G is a multiple of 8; otherwise the identity.
+__device__ __forceinline__ int64_t xcd_logical_block() {
+  const int64_t b = blockIdx.x, G = gridDim.x;
+  if (G % 8 != 0) return b;
+  return (b % 8) * (G / 8) + b / 8;
+}
+
 // ---------------------------------------------------------------------------
 // MFMA 32x32 wrappers.  Output layout (both types): lane l, register v holds
 // D[row = 8*(v/4) + 4*(l/32) + v%4][col = l%32].  Operand fragments: lane l

@@ -197,8 +197,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   bf16_t* W2b = Zs + RB * P::ZW;
 
   const int64_t nrb = 2 * a.Cp / RB, krb = a.Cp / RB;
-  const int64_t u = blockIdx.x / nrb;
-  const int64_t mb = blockIdx.x % nrb;
+  const int64_t bid = xcd_logical_block();  // a unit's row blocks share one XCD's L2
+  const int64_t u = bid / nrb;
+  const int64_t mb = bid % nrb;
   const bool isQ = mb >= krb;
   const int64_t p0 = (mb - (isQ ? krb : 0)) * RB;
   const int64_t tok0 = static_cast<int64_t>(a.r) * a.C;
@@ -395,8 +396,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   float* Yp = reinterpret_cast<float*>(smem_raw);                 // [4][TR][YW]
   bf16_t* Tg = reinterpret_cast<bf16_t*>(smem_raw + P::Y_BYTES);  // [FD][GW]
 
-  const int64_t u = blockIdx.x / wpu;
-  const int g = static_cast<int>(blockIdx.x % wpu);
+  const int64_t bid = xcd_logical_block();  // a unit's workgroups share one XCD's L2
+  const int64_t u = bid / wpu;
+  const int g = static_cast<int>(bid % wpu);
   const int ntile = static_cast<int>(2 * a.Cp / TR);  // tiles of the unit: K rows, then Q rows
   const int per = (ntile + wpu - 1) / wpu;
   const int tb = g * per;
@@ -758,8 +760,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
 
   const int64_t nib = a.h / 64;
-  const int64_t grp = blockIdx.x / a.nsplit;  // (unit, hidden block)
-  const int sp = static_cast<int>(blockIdx.x % a.nsplit);
+  // A unit's hidden blocks read the same token tiles: XCD-aware numbering
+  // keeps them on one L2.  Measured: it helps the unsplit kernel, and the
+  // token-split one (fewer, shorter workgroups) runs faster without it.
+  const int64_t bid = a.nsplit == 1 ? xcd_logical_block() : static_cast<int64_t>(blockIdx.x);
+  const int64_t grp = bid / a.nsplit;  // (unit, hidden block)
+  const int sp = static_cast<int>(bid % a.nsplit);
   const int64_t u = grp / nib;
   const int64_t ib = grp % nib;
   const int64_t tok0 = static_cast<int64_t>(a.r) * a.C;

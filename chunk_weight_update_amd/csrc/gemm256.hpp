@@ -129,8 +129,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int64_t d = s.d, h = s.h;
   const int64_t na = (4 * h / 256) * (d / 256), nb = (2 * d / 256) * (h / 256);
   const int64_t per_unit = (na + nb) * nsplit;
-  const int64_t u = blockIdx.x / per_unit;
-  const int64_t rest = blockIdx.x % per_unit;
+  const int64_t bid = xcd_logical_block();  // a unit's tiles share one XCD's L2
+  const int64_t u = bid / per_unit;
+  const int64_t rest = bid % per_unit;
   const int sp = static_cast<int>(rest / (na + nb));
   const int64_t t = rest % (na + nb);
   const bool famA = t < na;

@@ -265,8 +265,14 @@ struct Instr {
 void launch_scan(const Plan& q, const float* eta, const float* alpha, const float* beta,
                  float* kw, float* km, int64_t ustride, int64_t rstride, int64_t pad,
                  float* coef, int cstride, hipStream_t st, Instr& I) {
-  E2TTT_LAUNCH(I, E2TTT_KERNEL_SCAN, k_scan, dim3(grid1(q.BH * q.nC)), dim3(SCAN_NT), 0, st, eta,
-               alpha, beta, q.L, q.C, q.nC, q.mode, kw, km, ustride, rstride, pad, coef, cstride);
+  // Tokens per thread: every thread busy on short segments, up to 8 on long
+  // ones (fewer block-wide scan steps per token).
+  typedef void (*ScanFn)(const float*, const float*, const float*, int64_t, int64_t, int64_t,
+                         int, float*, float*, int64_t, int64_t, int64_t, float*, int);
+  ScanFn f = q.C <= 256 ? k_scan<256, 1> : q.C <= 512 ? k_scan<256, 2>
+           : q.C <= 1024 ? k_scan<256, 4> : k_scan<256, 8>;
+  E2TTT_LAUNCH(I, E2TTT_KERNEL_SCAN, f, dim3(grid1(q.BH * q.nC)), dim3(256), 0, st, eta, alpha,
+               beta, q.L, q.C, q.nC, q.mode, kw, km, ustride, rstride, pad, coef, cstride);
 }
 
 // 256x256-tile aggregation with a token split, then the split-sum state

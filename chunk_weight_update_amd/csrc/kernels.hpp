@@ -50,11 +50,12 @@ __device__ __forceinline__ int64_t n_valid(const Shape& s, int r) {
 
 // ---------------------------------------------------------------------------
 // Scalar kernels (§3.2 K^M = eta*beta~, K^W = eta*beta~*R; App. A.2 log-space
-// suffix products).  One workgroup of SCAN_NT threads per (unit, chunk)
-// segment of n <= C tokens, walked in rounds of SCAN_NT consecutive tokens
-// from the last round to the first; thread i takes token rd*SCAN_NT + i, so
-// every global access is coalesced and each token's logarithms are taken
-// once.
+// suffix products).  One workgroup of NT threads per (unit, chunk) segment of
+// n <= C tokens, walked in rounds of R = NT * TPT tokens from the last round
+// to the first.  Each round is staged through LDS (coalesced loads and
+// stores), and thread i then takes the TPT consecutive tokens i*TPT ...: each
+// token's logarithms are taken once, and the block-wide scans run once per
+// TPT tokens.
 //   b_t = prod_{s>t} beta_s,  c_t = prod_{s>t} gamma_s   (exclusive suffix
 //        products, as exp of suffix sums of log|.| with a sign parity)
 //   P_t = c_t + beta_{t+1} P_{t+1},  P_{n-1} = 1   (= beta~_t R_t, bounded)
@@ -63,14 +64,83 @@ __device__ __forceinline__ int64_t n_valid(const Shape& s, int r) {
 // P is the suffix composition of the affine maps x -> c_t + beta_{t+1} x
 // ((A1,B1) o (A2,B2) = (A1 + B1 A2, B1 B2)); the token past the segment
 // has beta = 0, which ends the recursion at P_{n-1} = c_{n-1} = 1.
-// Within a round: wave-level suffix scans by shuffles, wave totals through
-// LDS (double-buffered by round parity, so two barriers per round), and the
-// carry of the later rounds (suffix log sums, parities, P and beta of the
-// first token of the later round).  No subtraction of log sums anywhere, so
-// the -inf of a zero factor never turns into NaN.  All scan arithmetic is
-// fp64.  Output index of token p of chunk r of unit u is
+// Suffix sums and compositions: sequential inside a thread, then across the
+// threads of a wave by shuffles, across the 4 waves through LDS (double-
+// buffered by round parity), plus the carry of the later rounds (suffix log
+// sums, parities, P and beta of the first token of the later round).  No
+// subtraction of log sums anywhere, so the -inf of a zero factor never turns
+// into NaN.  All scan arithmetic is fp64, with the logarithm and exponential
+// below.  Output index of token p of chunk r of unit u is
 // u*ustride + r*rstride + p; with pad > n tokens p in [n, pad) are written
 // as 0.  coef of (u, r) starts at (u*nC + r)*cstride.
+
+// Natural log of a normal positive fp64 x to about 1 ulp: x = 2^e m with
+// m in [sqrt(1/2), sqrt(2)), log m = 2 atanh(s), s = (m - 1) / (m + 1),
+// |s| <= 0.1716, by the odd series of atanh to s^21 (the first omitted term
+// is below 1e-17 relative).  Zero gives -inf; subnormal, infinite and NaN
+// inputs take the library log.
+__device__ __forceinline__ double log_fast(double x) {
+  if (!(x >= 2.2250738585072014e-308 && x <= 1.7976931348623157e308))
+    return x == 0.0 ? -__builtin_huge_val() : log(x);
+  const long long bits = __double_as_longlong(x);
+  int e = static_cast<int>((bits >> 52) & 0x7ff) - 1023;
+  double m = __longlong_as_double((bits & 0x000fffffffffffffLL) | 0x3ff0000000000000LL);
+  if (m > 1.4142135623730951) {
+    m *= 0.5;
+    ++e;
+  }
+  const double f = m - 1.0;  // exact
+  const double den = m + 1.0;
+  double rc = __builtin_amdgcn_rcp(den);  // refined twice by Newton's iteration
+  rc = rc * fma(-den, rc, 2.0);
+  rc = rc * fma(-den, rc, 2.0);
+  const double s = f * rc;
+  const double z = s * s;
+  double p = 1.0 / 21.0;
+  p = fma(p, z, 1.0 / 19.0);
+  p = fma(p, z, 1.0 / 17.0);
+  p = fma(p, z, 1.0 / 15.0);
+  p = fma(p, z, 1.0 / 13.0);
+  p = fma(p, z, 1.0 / 11.0);
+  p = fma(p, z, 1.0 / 9.0);
+  p = fma(p, z, 1.0 / 7.0);
+  p = fma(p, z, 1.0 / 5.0);
+  p = fma(p, z, 1.0 / 3.0);
+  p = fma(p, z, 1.0);
+  constexpr double LN2_HI = 6.93147180369123816490e-01, LN2_LO = 1.90821492927058770002e-10;
+  const double de = static_cast<double>(e);
+  return fma(de, LN2_HI, fma(de, LN2_LO, 2.0 * s * p));
+}
+
+// exp of fp64 y to about 1 ulp: y = k ln2 + r, |r| <= ln2/2, exp r by its
+// Taylor series to r^13 (the first omitted term is below 1e-17 relative),
+// times 2^k.  Results below the normal range are returned as 0 (they vanish
+// in every fp32 output); -inf gives 0, NaN stays NaN.
+__device__ __forceinline__ double exp_fast(double y) {
+  if (!(y > -708.0)) return y != y ? y : 0.0;
+  if (y > 709.0) return exp(y);
+  constexpr double LOG2E = 1.44269504088896338700e+00;
+  constexpr double LN2_HI = 6.93147180369123816490e-01, LN2_LO = 1.90821492927058770002e-10;
+  const double k = __builtin_rint(y * LOG2E);
+  double r = fma(-k, LN2_HI, y);
+  r = fma(-k, LN2_LO, r);
+  double p = 1.0 / 6227020800.0;  // 1/13!
+  p = fma(p, r, 1.0 / 479001600.0);
+  p = fma(p, r, 1.0 / 39916800.0);
+  p = fma(p, r, 1.0 / 3628800.0);
+  p = fma(p, r, 1.0 / 362880.0);
+  p = fma(p, r, 1.0 / 40320.0);
+  p = fma(p, r, 1.0 / 5040.0);
+  p = fma(p, r, 1.0 / 720.0);
+  p = fma(p, r, 1.0 / 120.0);
+  p = fma(p, r, 1.0 / 24.0);
+  p = fma(p, r, 1.0 / 6.0);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  const long long ki = static_cast<long long>(k);
+  return p * __longlong_as_double((ki + 1023) << 52);
+}
 
 struct LogSigned {  // log|x| and the sign of x (as a parity bit)
   double l;
@@ -80,25 +150,29 @@ struct LogSigned {  // log|x| and the sign of x (as a parity bit)
 __device__ __forceinline__ LogSigned log_signed(double x) {
   LogSigned r;
   r.neg = x < 0.0;
-  r.l = log(fabs(x));  // -inf for 0
+  r.l = log_fast(fabs(x));  // -inf for 0
   return r;
 }
 
 __device__ __forceinline__ double exp_signed(double l, int neg) {
-  const double e = exp(l);
+  const double e = exp_fast(l);
   return neg ? -e : e;
 }
 
-constexpr int SCAN_NT = 1024;
-
-__global__ __launch_bounds__(SCAN_NT) void k_scan(const float* __restrict__ eta,
+// NT threads per workgroup, TPT tokens per thread (the host picks them from
+// the chunk length so that short segments keep every thread busy).
+template <int NT, int TPT>
+__global__ __launch_bounds__(NT) void k_scan(const float* __restrict__ eta,
                                                   const float* __restrict__ alpha,
                                                   const float* __restrict__ beta, int64_t L,
                                                   int64_t C, int64_t nC, int mode, float* kw,
                                                   float* km, int64_t ustride, int64_t rstride,
                                                   int64_t pad, float* coef, int cstride) {
-  constexpr int NW = SCAN_NT / 64;
-  __shared__ double s_lb[2][NW], s_lg[2][NW], s_A[2][NW], s_B[2][NW], s_b0[2][NW];
+  constexpr int NW = NT / 64, R = NT * TPT;
+  // Staged round: eta, alpha, beta (s_b[R] = beta of the next round's first
+  // token, 0 past the segment), then K^W, K^M of the round.
+  __shared__ float s_e[R], s_a[R], s_b[R + 4], s_kw[R], s_km[R];
+  __shared__ double s_lb[2][NW], s_lg[2][NW], s_A[2][NW], s_B[2][NW];
   __shared__ int s_par[2][NW];
   const int64_t seg = blockIdx.x;
   const int64_t u = seg / nC;
@@ -111,7 +185,7 @@ __global__ __launch_bounds__(SCAN_NT) void k_scan(const float* __restrict__ eta,
   const float* b_g = beta + u * L + t0;
   float* kw_o = kw + u * ustride + r * rstride;
   float* km_o = km + u * ustride + r * rstride;
-  for (int64_t i = n + tid; i < pad; i += SCAN_NT) {
+  for (int64_t i = n + tid; i < pad; i += NT) {
     kw_o[i] = 0.0f;
     km_o[i] = 0.0f;
   }
@@ -119,33 +193,62 @@ __global__ __launch_bounds__(SCAN_NT) void k_scan(const float* __restrict__ eta,
   // Carry from the later rounds.
   double cLB = 0.0, cLG = 0.0, cP = 0.0, cBeta = 0.0;
   int cPar = 0;  // bit 0: parity of beta signs, bit 1: of gamma signs
-  const int64_t nr = (n + SCAN_NT - 1) / SCAN_NT;
+  const int64_t nr = (n + R - 1) / R;
   for (int64_t rd = nr - 1; rd >= 0; --rd) {
     const int pb = static_cast<int>(rd & 1);
-    const int64_t i = rd * SCAN_NT + tid;
-    const bool valid = i < n;
-    double e = 0.0, bt = 0.0, lb = 0.0, lg = 0.0;
-    int par = 0;
-    if (valid) {
-      e = static_cast<double>(e_g[i]);
-      const double al = static_cast<double>(a_g[i]);
-      bt = static_cast<double>(b_g[i]);
-      const LogSigned b = log_signed(bt);
-      lb = b.l;
-      par = b.neg;
-      if (mode == 1) {
-        const LogSigned g = log_signed(al);
-        lg = g.l;
-        par |= g.neg << 1;
-      } else {
-        const double ea = e * al;
-        lg = ea <= 1.0 ? log1p(-ea) : log(ea - 1.0);  // log|1 - eta*alpha|
-        par |= (ea > 1.0 ? 1 : 0) << 1;
+    const int64_t base = rd * R;
+#pragma unroll
+    for (int k = 0; k < TPT; ++k) {
+      const int idx = k * NT + tid;
+      const bool ok = base + idx < n;
+      s_e[idx] = ok ? e_g[base + idx] : 0.0f;
+      s_a[idx] = ok ? a_g[base + idx] : 0.0f;
+      s_b[idx] = ok ? b_g[base + idx] : 0.0f;
+    }
+    if (tid == 0) s_b[R] = static_cast<float>(cBeta);  // exact: cBeta is a staged fp32
+    __syncthreads();
+
+    // This thread's tokens j0 .. j0+TPT-1 of the round.
+    const int j0 = tid * TPT;
+    double lb[TPT], lg[TPT];
+    int par[TPT];
+    float bt[TPT + 1];
+    double TLB = 0.0, TLG = 0.0;
+    int TPAR = 0;
+#pragma unroll
+    for (int j = 0; j < TPT + 1; ++j) bt[j] = s_b[j0 + j];
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+      lb[j] = 0.0;
+      lg[j] = 0.0;
+      par[j] = 0;
+      if (base + j0 + j < n) {
+        const LogSigned b = log_signed(static_cast<double>(bt[j]));
+        lb[j] = b.l;
+        par[j] = b.neg;
+        const double al = static_cast<double>(s_a[j0 + j]);
+        if (mode == 1) {
+          const LogSigned g = log_signed(al);
+          lg[j] = g.l;
+          par[j] |= g.neg << 1;
+        } else {
+          const double ea = static_cast<double>(s_e[j0 + j]) * al;  // exact
+          lg[j] = log_fast(fabs(1.0 - ea));  // log|1 - eta*alpha|
+          par[j] |= (ea > 1.0 ? 1 : 0) << 1;
+        }
       }
     }
-    // Wave-level inclusive suffix sums (lanes >= lane).
-    double xb = lb, xg = lg;
-    int xp = par;
+    for (int j = TPT - 1; j >= 0; --j) {  // (fixed order: same sums in every use)
+      TLB += lb[j];
+      TLG += lg[j];
+      TPAR ^= par[j];
+    }
+    const double beta_first = static_cast<double>(s_b[0]);  // read before the next round restages
+
+    // Sums over the later threads of the round: wave-level inclusive suffix,
+    // then the later waves' totals, then the carry.
+    double xb = TLB, xg = TLG;
+    int xp = TPAR;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const double yb = __shfl_down(xb, off, 64);
@@ -161,11 +264,8 @@ __global__ __launch_bounds__(SCAN_NT) void k_scan(const float* __restrict__ eta,
       s_lb[pb][w] = xb;
       s_lg[pb][w] = xg;
       s_par[pb][w] = xp;
-      s_b0[pb][w] = bt;
     }
     __syncthreads();
-    // Exclusive suffix of this token: the next lane's inclusive value, plus
-    // the totals of the later waves of the round, plus the carry.
     double eb = __shfl_down(xb, 1, 64), eg = __shfl_down(xg, 1, 64);
     int ep = __shfl_down(xp, 1, 64);
     if (lane == 63) {
@@ -183,13 +283,28 @@ __global__ __launch_bounds__(SCAN_NT) void k_scan(const float* __restrict__ eta,
     eb += lbw;
     eg += lgw;
     ep ^= pw;
-    const double b_t = exp_signed(eb, ep & 1);
-    const double c_t = exp_signed(eg, (ep >> 1) & 1);
-    // beta of the next token (0 past the segment end).
-    double bnext = __shfl_down(bt, 1, 64);
-    if (lane == 63) bnext = w + 1 < NW ? s_b0[pb][w + 1] : cBeta;
-    // Wave-level suffix composition of x -> A + B x.
-    double A = valid ? c_t : 0.0, B = valid ? bnext : 1.0;
+
+    // b, c of this thread's tokens, and the thread's affine map.
+    double bj[TPT], cj[TPT];
+    double A = 0.0, B = 1.0;
+    {
+      double sb = eb, sg = eg;
+      int sp = ep;
+#pragma unroll
+      for (int j = TPT - 1; j >= 0; --j) {
+        bj[j] = exp_signed(sb, sp & 1);
+        cj[j] = exp_signed(sg, (sp >> 1) & 1);
+        sb += lb[j];
+        sg += lg[j];
+        sp ^= par[j];
+        if (base + j0 + j < n) {
+          const double bn = static_cast<double>(bt[j + 1]);
+          A = cj[j] + bn * A;
+          B = bn * B;
+        }
+      }
+    }
+    // Compositions over the later threads of the wave, then the later waves.
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const double oA = __shfl_down(A, off, 64);
@@ -204,19 +319,37 @@ __global__ __launch_bounds__(SCAN_NT) void k_scan(const float* __restrict__ eta,
       s_B[pb][w] = B;
     }
     __syncthreads();
-    // P at the first token after this wave, and P at the round's first token
-    // (the carry of the next round), by composing the later waves' maps.
     double x = cP, x_after_w = cP;
     for (int v = NW - 1; v >= 0; --v) {
       if (v == w) x_after_w = x;
       x = s_A[pb][v] + s_B[pb][v] * x;
     }
-    const double P = A + B * x_after_w;
-    if (valid) {
-      kw_o[i] = static_cast<float>(e * P);
-      km_o[i] = static_cast<float>(e * b_t);
+    double nA = __shfl_down(A, 1, 64), nB = __shfl_down(B, 1, 64);
+    if (lane == 63) {
+      nA = 0.0;
+      nB = 1.0;
     }
-    // Carry into the earlier round.
+    double P = nA + nB * x_after_w;  // P at the first token after this thread's
+#pragma unroll
+    for (int j = TPT - 1; j >= 0; --j) {
+      if (base + j0 + j < n) {
+        P = cj[j] + static_cast<double>(bt[j + 1]) * P;
+        const double e = static_cast<double>(s_e[j0 + j]);
+        s_kw[j0 + j] = static_cast<float>(e * P);
+        s_km[j0 + j] = static_cast<float>(e * bj[j]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < TPT; ++k) {
+      const int idx = k * NT + tid;
+      if (base + idx < n) {
+        kw_o[base + idx] = s_kw[idx];
+        km_o[base + idx] = s_km[idx];
+      }
+    }
+    // Carry into the earlier round (every thread adds the same totals in the
+    // same order).
     for (int v = w; v >= 0; --v) {  // the later waves were added above
       lbw += s_lb[pb][v];
       lgw += s_lg[pb][v];
@@ -226,7 +359,7 @@ __global__ __launch_bounds__(SCAN_NT) void k_scan(const float* __restrict__ eta,
     cLG = lgw;
     cPar = pw;
     cP = x;
-    cBeta = s_b0[pb][0];
+    cBeta = beta_first;
   }
   if (tid == 0 && n > 0) {
     float* cf = coef + (u * nC + r) * cstride;

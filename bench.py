@@ -134,6 +134,9 @@ def kernel_work(w, cls):
         if cls == cwu.KERNEL_PREP:
             # K read + K^T written; W0 read + operand shadows written
             return 2.0 * BH * L * d * iob + BH * 3 * d * h * (4 + 4 * iob), "byte"
+        if cls == cwu.KERNEL_PROLOGUE:  # scan + K^T staging + W0 shadow
+            return (20.0 * BH * L + 2.0 * BH * L * d * iob
+                    + BH * 3 * d * h * (4 + 4 * iob)), "byte"
     if cls == cwu.KERNEL_SCAN:
         return 20.0 * BH * L, "byte"  # eta, alpha, beta read; K^W, K^M written
     return 0.0, "byte"
@@ -292,7 +295,7 @@ def main():
     classes = ([cwu.KERNEL_SCAN, cwu.KERNEL_LINEAR_FWD, cwu.KERNEL_LINEAR_AGG] if w.kind == 0
                else [cwu.KERNEL_SCAN, cwu.KERNEL_PREP, cwu.KERNEL_FWD13, cwu.KERNEL_FWD2,
                      cwu.KERNEL_BWD, cwu.KERNEL_AGG, cwu.KERNEL_PHASE_A, cwu.KERNEL_PHASE_B,
-                     cwu.KERNEL_STATE])
+                     cwu.KERNEL_STATE, cwu.KERNEL_PROLOGUE])
     per_step_launches = 2 * max(w.n_chunks, 2) + 2
     kernels = {}
     steps_k = max(1, min(args.steps, 10))

@@ -66,10 +66,10 @@ EXPORTED = ("e2ttt_validate", "e2ttt_workspace_bytes", "e2ttt_chunk_forward",
 # e2ttt_kernel_class
 KERNEL_SCAN, KERNEL_PREP, KERNEL_FWD13, KERNEL_FWD2, KERNEL_BWD, KERNEL_AGG = range(6)
 KERNEL_LINEAR_FWD, KERNEL_LINEAR_AGG, KERNEL_PHASE_A, KERNEL_PHASE_B = 6, 7, 8, 9
-KERNEL_STATE = 10
-KERNEL_NUM_CLASSES = 11
+KERNEL_STATE, KERNEL_PROLOGUE = 10, 11
+KERNEL_NUM_CLASSES = 12
 KERNEL_NAMES = ("scan", "prep", "fwd13", "fwd2", "bwd", "agg", "linear_fwd", "linear_agg",
-                "phase_a", "phase_b", "state")
+                "phase_a", "phase_b", "state", "prologue")
 
 
 def lib() -> ctypes.CDLL:

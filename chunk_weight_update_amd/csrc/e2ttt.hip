@@ -32,6 +32,9 @@ constexpr int64_t kMaxChunk = 12288;
 // workspace size stays a pure function of the problem.
 constexpr int64_t kCUs = 256;
 constexpr int kMaxSplitB = 4;
+// Above this many K^T and shadow workgroups the set-up steps are launched
+// separately (the combined launch runs at the scan's lower occupancy).
+constexpr int64_t kMaxPrologueBlocks = int64_t(1) << 40;
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -262,17 +265,44 @@ struct Instr {
                           e2_stop_, 0u, __VA_ARGS__);                                      \
   } while (0)
 
+// Tokens per scan thread: every thread busy on short segments, up to 8 on
+// long ones (fewer block-wide steps per token).
+int scan_tpt(int64_t C) { return C <= 256 ? 1 : C <= 512 ? 2 : C <= 1024 ? 4 : 8; }
+
+// Vector accesses of min(tpt, 4) floats need every segment start (u*L + r*C),
+// every output row start and every segment length to be multiples of it
+// (the base pointers are 16-byte aligned).
+bool scan_vec_ok(const Plan& q, int tpt, int64_t ustride, int64_t rstride) {
+  const int64_t vw = tpt < 4 ? tpt : 4;
+  return q.L % vw == 0 && q.C % vw == 0 && ustride % vw == 0 && rstride % vw == 0;
+}
+
+ScanArgs scan_args(const Plan& q, const float* eta, const float* alpha, const float* beta,
+                   float* kw, float* km, int64_t ustride, int64_t rstride, int64_t pad,
+                   float* coef, int cstride) {
+  ScanArgs sa;
+  sa.eta = eta; sa.alpha = alpha; sa.beta = beta;
+  sa.L = q.L; sa.C = q.C; sa.nC = q.nC; sa.mode = q.mode;
+  sa.kw = kw; sa.km = km;
+  sa.ustride = ustride; sa.rstride = rstride; sa.pad = pad;
+  sa.coef = coef; sa.cstride = cstride;
+  return sa;
+}
+
 void launch_scan(const Plan& q, const float* eta, const float* alpha, const float* beta,
                  float* kw, float* km, int64_t ustride, int64_t rstride, int64_t pad,
                  float* coef, int cstride, hipStream_t st, Instr& I) {
   // Tokens per thread: every thread busy on short segments, up to 8 on long
   // ones (fewer block-wide scan steps per token).
-  typedef void (*ScanFn)(const float*, const float*, const float*, int64_t, int64_t, int64_t,
-                         int, float*, float*, int64_t, int64_t, int64_t, float*, int);
-  ScanFn f = q.C <= 256 ? k_scan<256, 1> : q.C <= 512 ? k_scan<256, 2>
-           : q.C <= 1024 ? k_scan<256, 4> : k_scan<256, 8>;
-  E2TTT_LAUNCH(I, E2TTT_KERNEL_SCAN, f, dim3(grid1(q.BH * q.nC)), dim3(256), 0, st, eta, alpha,
-               beta, q.L, q.C, q.nC, q.mode, kw, km, ustride, rstride, pad, coef, cstride);
+  const ScanArgs sa = scan_args(q, eta, alpha, beta, kw, km, ustride, rstride, pad, coef,
+                                cstride);
+  const int tpt = scan_tpt(q.C);
+  const bool vec = scan_vec_ok(q, tpt, ustride, rstride);
+  void (*f)(ScanArgs) = tpt == 1 ? k_scan<256, 1, 1>
+                      : tpt == 2 ? (vec ? k_scan<256, 2, 2> : k_scan<256, 2, 1>)
+                      : tpt == 4 ? (vec ? k_scan<256, 4, 4> : k_scan<256, 4, 1>)
+                                 : (vec ? k_scan<256, 8, 4> : k_scan<256, 8, 1>);
+  E2TTT_LAUNCH(I, E2TTT_KERNEL_SCAN, f, dim3(grid1(q.BH * q.nC)), dim3(256), 0, st, sa);
 }
 
 // 256x256-tile aggregation with a token split, then the split-sum state
@@ -375,15 +405,34 @@ void launch_fused(const Plan& q, const void* qv, const void* kv, const void* vv,
   a.krep = q.krep;
   a.part = q.nsplitB > 1 ? reinterpret_cast<float*>(ws + q.part) : nullptr;
   Shape s{q.BH, q.L, q.d, q.h, q.C, q.Cp, q.nC, q.krep};
-  launch_scan(q, eta, alpha, beta, reinterpret_cast<float*>(ws + q.kw),
-              reinterpret_cast<float*>(ws + q.km), q.nC * q.Cp, q.Cp, q.Cp,
-              reinterpret_cast<float*>(ws + q.coef), 4, st, I);
-  void (*kprep)(Shape, const bf16_t*, bf16_t*) = k_prep_kt<bf16_t, true>;
-  E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, kprep,
-               dim3(grid1(q.BH * q.nC * (q.Cp / 64) * (q.d / 64))), dim3(256), 0, st, s, a.k,
-               reinterpret_cast<bf16_t*>(ws + q.kt));
-  E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, k_prep_shadow<bf16_t>, dim3(grid1((q.BH * q.P + 255) / 256)),
-               dim3(256), 0, st, s, W0, a.w13s, a.w2s, a.w2ts);
+  // Scalar kernels, K^T staging and the W0 shadow: independent, one launch.
+  const ScanArgs sa = scan_args(q, eta, alpha, beta, reinterpret_cast<float*>(ws + q.kw),
+                                reinterpret_cast<float*>(ws + q.km), q.nC * q.Cp, q.Cp, q.Cp,
+                                reinterpret_cast<float*>(ws + q.coef), 4);
+  const int64_t nscan = q.BH * q.nC, nkt = q.BH * q.nC * (q.Cp / 64) * (q.d / 64);
+  const int64_t nshadow = (q.BH * q.P + 255) / 256;
+  if (nkt + nshadow <= kMaxPrologueBlocks) {
+    const int tpt = scan_tpt(q.C);
+    const bool vec = scan_vec_ok(q, tpt, q.nC * q.Cp, q.Cp);
+    void (*kpro)(ScanArgs, Shape, const bf16_t*, bf16_t*, const float*, bf16_t*, bf16_t*,
+                 bf16_t*, int64_t, int64_t) =
+        tpt == 1 ? k_prologue<1, 1>
+        : tpt == 2 ? (vec ? k_prologue<2, 2> : k_prologue<2, 1>)
+        : tpt == 4 ? (vec ? k_prologue<4, 4> : k_prologue<4, 1>)
+                   : (vec ? k_prologue<8, 4> : k_prologue<8, 1>);
+    E2TTT_LAUNCH(I, E2TTT_KERNEL_PROLOGUE, kpro, dim3(grid1(nscan + nkt + nshadow)), dim3(256),
+                 0, st, sa, s, a.k, reinterpret_cast<bf16_t*>(ws + q.kt), W0, a.w13s, a.w2s,
+                 a.w2ts, nscan, nkt);
+  } else {  // large set-up work: three launches, each at its own occupancy
+    launch_scan(q, eta, alpha, beta, reinterpret_cast<float*>(ws + q.kw),
+                reinterpret_cast<float*>(ws + q.km), q.nC * q.Cp, q.Cp, q.Cp,
+                reinterpret_cast<float*>(ws + q.coef), 4, st, I);
+    void (*kprep)(Shape, const bf16_t*, bf16_t*) = k_prep_kt<bf16_t, true>;
+    E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, kprep, dim3(grid1(nkt)), dim3(256), 0, st, s, a.k,
+                 reinterpret_cast<bf16_t*>(ws + q.kt));
+    E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, k_prep_shadow<bf16_t>, dim3(grid1(nshadow)), dim3(256),
+                 0, st, s, W0, a.w13s, a.w2s, a.w2ts);
+  }
   const unsigned gA = grid1(q.BH * (2 * q.Cp / q.rbA));
   const unsigned gB = grid1(q.BH * (q.h / 64) * q.nsplitB);
   for (int64_t r = 0; r < q.nC; ++r) {

@@ -49,324 +49,210 @@ __device__ __forceinline__ int64_t n_valid(const Shape& s, int r) {
 }
 
 // ---------------------------------------------------------------------------
-// Scalar kernels (§3.2 K^M = eta*beta~, K^W = eta*beta~*R; App. A.2 log-space
-// suffix products).  One workgroup of NT threads per (unit, chunk) segment of
-// n <= C tokens, walked in rounds of R = NT * TPT tokens from the last round
-// to the first.  Each round is staged through LDS (coalesced loads and
-// stores), and thread i then takes the TPT consecutive tokens i*TPT ...: each
-// token's logarithms are taken once, and the block-wide scans run once per
-// TPT tokens.
+// Scalar kernels (§3.2 K^M = eta*beta~, K^W = eta*beta~*R; App. A.2 suffix
+// products).  For the tokens t = 0 .. n-1 of one (unit, chunk) segment:
 //   b_t = prod_{s>t} beta_s,  c_t = prod_{s>t} gamma_s   (exclusive suffix
-//        products, as exp of suffix sums of log|.| with a sign parity)
+//        products; gamma = 1 - eta*alpha, or alpha itself in mode 1)
 //   P_t = c_t + beta_{t+1} P_{t+1},  P_{n-1} = 1   (= beta~_t R_t, bounded)
-//   K^W_t = eta_t P_t,  K^M_t = eta_t b_t,  cW = prod gamma, cM = prod beta,
-//   cWM = beta_0 P_0.
-// P is the suffix composition of the affine maps x -> c_t + beta_{t+1} x
-// ((A1,B1) o (A2,B2) = (A1 + B1 A2, B1 B2)); the token past the segment
-// has beta = 0, which ends the recursion at P_{n-1} = c_{n-1} = 1.
-// Suffix sums and compositions: sequential inside a thread, then across the
-// threads of a wave by shuffles, across the 4 waves through LDS (double-
-// buffered by round parity), plus the carry of the later rounds (suffix log
-// sums, parities, P and beta of the first token of the later round).  No
-// subtraction of log sums anywhere, so the -inf of a zero factor never turns
-// into NaN.  All scan arithmetic is fp64, with the logarithm and exponential
-// below.  Output index of token p of chunk r of unit u is
-// u*ustride + r*rstride + p; with pad > n tokens p in [n, pad) are written
-// as 0.  coef of (u, r) starts at (u*nC + r)*cstride.
+//   K^W_t = eta_t P_t,  K^M_t = eta_t b_t,
+//   cW = prod gamma = gamma_0 c_0,  cM = prod beta = beta_0 b_0,  cWM = beta_0 P_0.
+// The triple v_t = (b_t, c_t, P_t) obeys v_{t-1} = T_t v_t with the linear map
+//   T_t: (b, c, P) -> (beta_t b, gamma_t c, gamma_t c + beta_t P),
+// starting from v_{n-1} = (1, 1, 1).  Maps of this shape, (b, c, P) ->
+// (B b, G c, Z c + B P), are closed under composition, so v_t for every token
+// is a suffix scan of 3-number maps.  The products are formed directly in
+// fp64 (no logarithms): a factor of 0 gives exact zeros, negative factors
+// need no sign bookkeeping, and the relative error of a product of n factors
+// stays below n ulp.  Products that leave the fp64 range underflow to 0 or
+// overflow to inf exactly where the fp32 outputs would.
+//
+// One workgroup of NT threads per segment, walked in rounds of R = NT * TPT
+// tokens from the last round to the first.  Thread i takes the TPT
+// consecutive tokens i*TPT ... of the round (vector loads and stores of VW
+// floats when the host has checked the alignment): it composes its tokens'
+// maps, the wave composes the threads' maps by shuffles, the waves' totals
+// go through LDS (double-buffered by round parity, one barrier per round),
+// and each thread then walks its own tokens backwards from the value at its
+// last token.  The vector entering a round is the previous round's total
+// applied to the one before.  Output index of token p of chunk r of unit u
+// is u*ustride + r*rstride + p; with pad > n tokens p in [n, pad) are
+// written as 0.  coef of (u, r) starts at (u*nC + r)*cstride.
 
-// Natural log of a normal positive fp64 x to about 1 ulp: x = 2^e m with
-// m in [sqrt(1/2), sqrt(2)), log m = 2 atanh(s), s = (m - 1) / (m + 1),
-// |s| <= 0.1716, by the odd series of atanh to s^21 (the first omitted term
-// is below 1e-17 relative).  Zero gives -inf; subnormal, infinite and NaN
-// inputs take the library log.
-__device__ __forceinline__ double log_fast(double x) {
-  if (!(x >= 2.2250738585072014e-308 && x <= 1.7976931348623157e308))
-    return x == 0.0 ? -__builtin_huge_val() : log(x);
-  const long long bits = __double_as_longlong(x);
-  int e = static_cast<int>((bits >> 52) & 0x7ff) - 1023;
-  double m = __longlong_as_double((bits & 0x000fffffffffffffLL) | 0x3ff0000000000000LL);
-  if (m > 1.4142135623730951) {
-    m *= 0.5;
-    ++e;
-  }
-  const double f = m - 1.0;  // exact
-  const double den = m + 1.0;
-  double rc = __builtin_amdgcn_rcp(den);  // refined twice by Newton's iteration
-  rc = rc * fma(-den, rc, 2.0);
-  rc = rc * fma(-den, rc, 2.0);
-  const double s = f * rc;
-  const double z = s * s;
-  double p = 1.0 / 21.0;
-  p = fma(p, z, 1.0 / 19.0);
-  p = fma(p, z, 1.0 / 17.0);
-  p = fma(p, z, 1.0 / 15.0);
-  p = fma(p, z, 1.0 / 13.0);
-  p = fma(p, z, 1.0 / 11.0);
-  p = fma(p, z, 1.0 / 9.0);
-  p = fma(p, z, 1.0 / 7.0);
-  p = fma(p, z, 1.0 / 5.0);
-  p = fma(p, z, 1.0 / 3.0);
-  p = fma(p, z, 1.0);
-  constexpr double LN2_HI = 6.93147180369123816490e-01, LN2_LO = 1.90821492927058770002e-10;
-  const double de = static_cast<double>(e);
-  return fma(de, LN2_HI, fma(de, LN2_LO, 2.0 * s * p));
-}
-
-// exp of fp64 y to about 1 ulp: y = k ln2 + r, |r| <= ln2/2, exp r by its
-// Taylor series to r^13 (the first omitted term is below 1e-17 relative),
-// times 2^k.  Results below the normal range are returned as 0 (they vanish
-// in every fp32 output); -inf gives 0, NaN stays NaN.
-__device__ __forceinline__ double exp_fast(double y) {
-  if (!(y > -708.0)) return y != y ? y : 0.0;
-  if (y > 709.0) return exp(y);
-  constexpr double LOG2E = 1.44269504088896338700e+00;
-  constexpr double LN2_HI = 6.93147180369123816490e-01, LN2_LO = 1.90821492927058770002e-10;
-  const double k = __builtin_rint(y * LOG2E);
-  double r = fma(-k, LN2_HI, y);
-  r = fma(-k, LN2_LO, r);
-  double p = 1.0 / 6227020800.0;  // 1/13!
-  p = fma(p, r, 1.0 / 479001600.0);
-  p = fma(p, r, 1.0 / 39916800.0);
-  p = fma(p, r, 1.0 / 3628800.0);
-  p = fma(p, r, 1.0 / 362880.0);
-  p = fma(p, r, 1.0 / 40320.0);
-  p = fma(p, r, 1.0 / 5040.0);
-  p = fma(p, r, 1.0 / 720.0);
-  p = fma(p, r, 1.0 / 120.0);
-  p = fma(p, r, 1.0 / 24.0);
-  p = fma(p, r, 1.0 / 6.0);
-  p = fma(p, r, 0.5);
-  p = fma(p, r, 1.0);
-  p = fma(p, r, 1.0);
-  const long long ki = static_cast<long long>(k);
-  return p * __longlong_as_double((ki + 1023) << 52);
-}
-
-struct LogSigned {  // log|x| and the sign of x (as a parity bit)
-  double l;
-  int neg;
+struct ScanMap {  // (b, c, P) -> (B b, G c, Z c + B P)
+  double B, G, Z;
 };
 
-__device__ __forceinline__ LogSigned log_signed(double x) {
-  LogSigned r;
-  r.neg = x < 0.0;
-  r.l = log_fast(fabs(x));  // -inf for 0
-  return r;
+// F o E: E applied first.
+__device__ __forceinline__ ScanMap scan_compose(const ScanMap& F, const ScanMap& E) {
+  return {F.B * E.B, F.G * E.G, fma(F.Z, E.G, F.B * E.Z)};
 }
 
-__device__ __forceinline__ double exp_signed(double l, int neg) {
-  const double e = exp_fast(l);
-  return neg ? -e : e;
+struct ScanVec {
+  double b, c, P;
+};
+
+__device__ __forceinline__ ScanVec scan_apply(const ScanMap& F, const ScanVec& v) {
+  return {F.B * v.b, F.G * v.c, fma(F.Z, v.c, F.B * v.P)};
 }
 
-// NT threads per workgroup, TPT tokens per thread (the host picks them from
-// the chunk length so that short segments keep every thread busy).
-template <int NT, int TPT>
-__global__ __launch_bounds__(NT) void k_scan(const float* __restrict__ eta,
-                                                  const float* __restrict__ alpha,
-                                                  const float* __restrict__ beta, int64_t L,
-                                                  int64_t C, int64_t nC, int mode, float* kw,
-                                                  float* km, int64_t ustride, int64_t rstride,
-                                                  int64_t pad, float* coef, int cstride) {
+__device__ __forceinline__ ScanMap scan_shfl_down(const ScanMap& m, int off) {
+  return {__shfl_down(m.B, off, 64), __shfl_down(m.G, off, 64), __shfl_down(m.Z, off, 64)};
+}
+
+// Arguments of the scan (one launch covers all (unit, chunk) segments).
+struct ScanArgs {
+  const float* eta;
+  const float* alpha;
+  const float* beta;
+  int64_t L, C, nC;
+  int mode;
+  float* kw;
+  float* km;
+  int64_t ustride, rstride, pad;
+  float* coef;
+  int cstride;
+};
+
+// VW consecutive floats at p (p aligned to VW floats).
+template <int VW>
+__device__ __forceinline__ void load_vw(const float* p, float* x) {
+  if constexpr (VW == 4) {
+    const float4 t = *reinterpret_cast<const float4*>(p);
+    x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
+  } else if constexpr (VW == 2) {
+    const float2 t = *reinterpret_cast<const float2*>(p);
+    x[0] = t.x; x[1] = t.y;
+  } else {
+    x[0] = *p;
+  }
+}
+
+template <int VW>
+__device__ __forceinline__ void store_vw(float* p, const float* x) {
+  if constexpr (VW == 4) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  } else if constexpr (VW == 2) {
+    *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
+  } else {
+    *p = x[0];
+  }
+}
+
+// Segment `seg` = (unit, chunk) by a workgroup of NT threads, TPT tokens per
+// thread, VW-float vector accesses (VW divides TPT; VW > 1 needs every
+// segment start, output row start and n to be multiples of VW).
+template <int NT, int TPT, int VW>
+__device__ __forceinline__ void scan_segment(int64_t seg, const ScanArgs& sa) {
+  static_assert(TPT % VW == 0, "vector width divides tokens per thread");
   constexpr int NW = NT / 64, R = NT * TPT;
-  // Staged round: eta, alpha, beta (s_b[R] = beta of the next round's first
-  // token, 0 past the segment), then K^W, K^M of the round.
-  __shared__ float s_e[R], s_a[R], s_b[R + 4], s_kw[R], s_km[R];
-  __shared__ double s_lb[2][NW], s_lg[2][NW], s_A[2][NW], s_B[2][NW];
-  __shared__ int s_par[2][NW];
-  const int64_t seg = blockIdx.x;
-  const int64_t u = seg / nC;
-  const int r = static_cast<int>(seg % nC);
+  __shared__ double s_m[2][NW][3];
+  const int64_t u = seg / sa.nC;
+  const int r = static_cast<int>(seg % sa.nC);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t t0 = static_cast<int64_t>(r) * C;
-  const int64_t n = (L - t0) < C ? (L - t0) : C;
-  const float* e_g = eta + u * L + t0;
-  const float* a_g = alpha + u * L + t0;
-  const float* b_g = beta + u * L + t0;
-  float* kw_o = kw + u * ustride + r * rstride;
-  float* km_o = km + u * ustride + r * rstride;
-  for (int64_t i = n + tid; i < pad; i += NT) {
+  const int64_t t0 = static_cast<int64_t>(r) * sa.C;
+  const int64_t n = (sa.L - t0) < sa.C ? (sa.L - t0) : sa.C;
+  const float* e_g = sa.eta + u * sa.L + t0;
+  const float* a_g = sa.alpha + u * sa.L + t0;
+  const float* b_g = sa.beta + u * sa.L + t0;
+  float* kw_o = sa.kw + u * sa.ustride + r * sa.rstride;
+  float* km_o = sa.km + u * sa.ustride + r * sa.rstride;
+  for (int64_t i = n + tid; i < sa.pad; i += NT) {
     kw_o[i] = 0.0f;
     km_o[i] = 0.0f;
   }
 
-  // Carry from the later rounds.
-  double cLB = 0.0, cLG = 0.0, cP = 0.0, cBeta = 0.0;
-  int cPar = 0;  // bit 0: parity of beta signs, bit 1: of gamma signs
+  ScanVec vin = {1.0, 1.0, 1.0};  // v at the last token of the current round
   const int64_t nr = (n + R - 1) / R;
   for (int64_t rd = nr - 1; rd >= 0; --rd) {
     const int pb = static_cast<int>(rd & 1);
-    const int64_t base = rd * R;
+    const int64_t j0 = rd * R + static_cast<int64_t>(tid) * TPT;  // first token of the thread
+    float e[TPT], be[TPT];
+    double ga[TPT];
 #pragma unroll
-    for (int k = 0; k < TPT; ++k) {
-      const int idx = k * NT + tid;
-      const bool ok = base + idx < n;
-      s_e[idx] = ok ? e_g[base + idx] : 0.0f;
-      s_a[idx] = ok ? a_g[base + idx] : 0.0f;
-      s_b[idx] = ok ? b_g[base + idx] : 0.0f;
-    }
-    if (tid == 0) s_b[R] = static_cast<float>(cBeta);  // exact: cBeta is a staged fp32
-    __syncthreads();
-
-    // This thread's tokens j0 .. j0+TPT-1 of the round.
-    const int j0 = tid * TPT;
-    double lb[TPT], lg[TPT];
-    int par[TPT];
-    float bt[TPT + 1];
-    double TLB = 0.0, TLG = 0.0;
-    int TPAR = 0;
+    for (int q = 0; q < TPT; q += VW) {
+      float ev[VW], av[VW], bv[VW];
+      const bool ok = j0 + q < n;  // all VW tokens valid or none (n % VW == 0)
 #pragma unroll
-    for (int j = 0; j < TPT + 1; ++j) bt[j] = s_b[j0 + j];
+      for (int i = 0; i < VW; ++i) { ev[i] = 0.0f; av[i] = 0.0f; bv[i] = 1.0f; }
+      if (ok) {
+        load_vw<VW>(e_g + j0 + q, ev);
+        load_vw<VW>(a_g + j0 + q, av);
+        load_vw<VW>(b_g + j0 + q, bv);
+      }
 #pragma unroll
-    for (int j = 0; j < TPT; ++j) {
-      lb[j] = 0.0;
-      lg[j] = 0.0;
-      par[j] = 0;
-      if (base + j0 + j < n) {
-        const LogSigned b = log_signed(static_cast<double>(bt[j]));
-        lb[j] = b.l;
-        par[j] = b.neg;
-        const double al = static_cast<double>(s_a[j0 + j]);
-        if (mode == 1) {
-          const LogSigned g = log_signed(al);
-          lg[j] = g.l;
-          par[j] |= g.neg << 1;
-        } else {
-          const double ea = static_cast<double>(s_e[j0 + j]) * al;  // exact
-          lg[j] = log_fast(fabs(1.0 - ea));  // log|1 - eta*alpha|
-          par[j] |= (ea > 1.0 ? 1 : 0) << 1;
-        }
+      for (int i = 0; i < VW; ++i) {
+        e[q + i] = ev[i];
+        be[q + i] = bv[i];
+        // eta*alpha of two fp32 values is exact in fp64; one rounding in 1 - x.
+        ga[q + i] = sa.mode == 1 ? static_cast<double>(av[i])
+                                 : 1.0 - static_cast<double>(ev[i]) * static_cast<double>(av[i]);
       }
     }
-    for (int j = TPT - 1; j >= 0; --j) {  // (fixed order: same sums in every use)
-      TLB += lb[j];
-      TLG += lg[j];
-      TPAR ^= par[j];
-    }
-    const double beta_first = static_cast<double>(s_b[0]);  // read before the next round restages
-
-    // Sums over the later threads of the round: wave-level inclusive suffix,
-    // then the later waves' totals, then the carry.
-    double xb = TLB, xg = TLG;
-    int xp = TPAR;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const double yb = __shfl_down(xb, off, 64);
-      const double yg = __shfl_down(xg, off, 64);
-      const int yp = __shfl_down(xp, off, 64);
-      if (lane + off < 64) {
-        xb += yb;
-        xg += yg;
-        xp ^= yp;
-      }
-    }
-    if (lane == 0) {
-      s_lb[pb][w] = xb;
-      s_lg[pb][w] = xg;
-      s_par[pb][w] = xp;
-    }
-    __syncthreads();
-    double eb = __shfl_down(xb, 1, 64), eg = __shfl_down(xg, 1, 64);
-    int ep = __shfl_down(xp, 1, 64);
-    if (lane == 63) {
-      eb = 0.0;
-      eg = 0.0;
-      ep = 0;
-    }
-    double lbw = cLB, lgw = cLG;
-    int pw = cPar;
-    for (int v = NW - 1; v > w; --v) {
-      lbw += s_lb[pb][v];
-      lgw += s_lg[pb][v];
-      pw ^= s_par[pb][v];
-    }
-    eb += lbw;
-    eg += lgw;
-    ep ^= pw;
-
-    // b, c of this thread's tokens, and the thread's affine map.
-    double bj[TPT], cj[TPT];
-    double A = 0.0, B = 1.0;
-    {
-      double sb = eb, sg = eg;
-      int sp = ep;
-#pragma unroll
-      for (int j = TPT - 1; j >= 0; --j) {
-        bj[j] = exp_signed(sb, sp & 1);
-        cj[j] = exp_signed(sg, (sp >> 1) & 1);
-        sb += lb[j];
-        sg += lg[j];
-        sp ^= par[j];
-        if (base + j0 + j < n) {
-          const double bn = static_cast<double>(bt[j + 1]);
-          A = cj[j] + bn * A;
-          B = bn * B;
-        }
-      }
-    }
-    // Compositions over the later threads of the wave, then the later waves.
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const double oA = __shfl_down(A, off, 64);
-      const double oB = __shfl_down(B, off, 64);
-      if (lane + off < 64) {
-        A = A + B * oA;
-        B = B * oB;
-      }
-    }
-    if (lane == 0) {
-      s_A[pb][w] = A;
-      s_B[pb][w] = B;
-    }
-    __syncthreads();
-    double x = cP, x_after_w = cP;
-    for (int v = NW - 1; v >= 0; --v) {
-      if (v == w) x_after_w = x;
-      x = s_A[pb][v] + s_B[pb][v] * x;
-    }
-    double nA = __shfl_down(A, 1, 64), nB = __shfl_down(B, 1, 64);
-    if (lane == 63) {
-      nA = 0.0;
-      nB = 1.0;
-    }
-    double P = nA + nB * x_after_w;  // P at the first token after this thread's
+    // This thread's map T_{j0} o ... o T_{j0+TPT-1}; tokens past n are the
+    // identity (B = G = 1, Z = 0).
+    ScanMap m = {1.0, 1.0, 0.0};
 #pragma unroll
     for (int j = TPT - 1; j >= 0; --j) {
-      if (base + j0 + j < n) {
-        P = cj[j] + static_cast<double>(bt[j + 1]) * P;
-        const double e = static_cast<double>(s_e[j0 + j]);
-        s_kw[j0 + j] = static_cast<float>(e * P);
-        s_km[j0 + j] = static_cast<float>(e * bj[j]);
+      if (j0 + j < n) {
+        const ScanMap t = {static_cast<double>(be[j]), ga[j], ga[j]};
+        m = scan_compose(t, m);
       }
     }
-    __syncthreads();
+    // Inclusive suffix composition over the later lanes of the wave.
+    ScanMap x = m;
 #pragma unroll
-    for (int k = 0; k < TPT; ++k) {
-      const int idx = k * NT + tid;
-      if (base + idx < n) {
-        kw_o[base + idx] = s_kw[idx];
-        km_o[base + idx] = s_km[idx];
+    for (int off = 1; off < 64; off <<= 1) {
+      const ScanMap y = scan_shfl_down(x, off);
+      if (lane + off < 64) x = scan_compose(x, y);
+    }
+    if (lane == 0) {
+      s_m[pb][w][0] = x.B;
+      s_m[pb][w][1] = x.G;
+      s_m[pb][w][2] = x.Z;
+    }
+    ScanMap ex = scan_shfl_down(x, 1);  // exclusive: the later lanes only
+    if (lane == 63) ex = {1.0, 1.0, 0.0};
+    __syncthreads();
+    // v at the last token of this wave, then of this thread; every thread
+    // also forms the vector entering the earlier round (same order in all).
+    ScanVec vw = vin, vprev = vin;
+    for (int v = NW - 1; v >= 0; --v) {
+      if (v == w) vw = vprev;
+      const ScanMap wt = {s_m[pb][v][0], s_m[pb][v][1], s_m[pb][v][2]};
+      vprev = scan_apply(wt, vprev);
+    }
+    ScanVec cur = scan_apply(ex, vw);
+    float okw[TPT], okm[TPT];
+#pragma unroll
+    for (int j = TPT - 1; j >= 0; --j) {
+      okw[j] = static_cast<float>(static_cast<double>(e[j]) * cur.P);
+      okm[j] = static_cast<float>(static_cast<double>(e[j]) * cur.b);
+      if (j > 0) {
+        const ScanMap t = {static_cast<double>(be[j]), ga[j], ga[j]};
+        if (j0 + j < n) cur = scan_apply(t, cur);
       }
     }
-    // Carry into the earlier round (every thread adds the same totals in the
-    // same order).
-    for (int v = w; v >= 0; --v) {  // the later waves were added above
-      lbw += s_lb[pb][v];
-      lgw += s_lg[pb][v];
-      pw ^= s_par[pb][v];
+#pragma unroll
+    for (int q = 0; q < TPT; q += VW) {
+      if (j0 + q < n) {
+        store_vw<VW>(kw_o + j0 + q, okw + q);
+        store_vw<VW>(km_o + j0 + q, okm + q);
+      }
     }
-    cLB = lbw;
-    cLG = lgw;
-    cPar = pw;
-    cP = x;
-    cBeta = beta_first;
+    if (rd == 0 && tid == 0 && n > 0) {  // token 0: cur = v_0
+      const double b0 = static_cast<double>(be[0]);
+      float* cf = sa.coef + (u * sa.nC + r) * sa.cstride;
+      cf[0] = static_cast<float>(ga[0] * cur.c);
+      cf[1] = static_cast<float>(b0 * cur.b);
+      cf[2] = static_cast<float>(b0 * cur.P);
+    }
+    vin = vprev;
   }
-  if (tid == 0 && n > 0) {
-    float* cf = coef + (u * nC + r) * cstride;
-    cf[0] = static_cast<float>(exp_signed(cLG, (cPar >> 1) & 1));
-    cf[1] = static_cast<float>(exp_signed(cLB, cPar & 1));
-    cf[2] = static_cast<float>(cBeta * cP);
-  }
+}
+
+template <int NT, int TPT, int VW>
+__global__ __launch_bounds__(NT) void k_scan(ScanArgs sa) {
+  scan_segment<NT, TPT, VW>(blockIdx.x, sa);
 }
 
 // ---------------------------------------------------------------------------
@@ -381,14 +267,13 @@ __host__ __device__ constexpr int tok_perm32(int p) {
 }
 
 template <typename T, bool PERM>
-__global__ __launch_bounds__(256) void k_prep_kt(Shape s, const T* __restrict__ k,
-                                                 T* __restrict__ kt) {
+__device__ __forceinline__ void prep_kt_block(const Shape& s, int64_t bid,
+                                              const T* __restrict__ k, T* __restrict__ kt) {
   constexpr int VE = 16 / sizeof(T);            // elements per 16-byte vector
   constexpr int NV = 64 * 64 / VE;              // vectors per 64x64 tile
   constexpr int PER = NV / 256;
   __shared__ T tile[64][64 + 1];
   const int64_t ptiles = s.Cp / 64, ctiles = s.d / 64;
-  int64_t bid = blockIdx.x;
   const int64_t ct = bid % ctiles; bid /= ctiles;
   const int64_t pt = bid % ptiles; bid /= ptiles;
   const int r = static_cast<int>(bid % s.nC);
@@ -426,6 +311,12 @@ __global__ __launch_bounds__(256) void k_prep_kt(Shape s, const T* __restrict__ 
   }
 }
 
+template <typename T, bool PERM>
+__global__ __launch_bounds__(256) void k_prep_kt(Shape s, const T* __restrict__ k,
+                                                 T* __restrict__ kt) {
+  prep_kt_block<T, PERM>(s, blockIdx.x, k, kt);
+}
+
 // Hi/lo split of a state value into the operand type.
 template <typename T>
 __device__ __forceinline__ void split_store(float w, T* hi, T* lo) {
@@ -458,13 +349,35 @@ __device__ __forceinline__ void write_shadow(const Shape& s, int64_t u, int64_t 
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void k_prep_shadow(Shape s, const float* __restrict__ W,
-                                                     T* w13s, T* w2s, T* w2ts) {
+__device__ __forceinline__ void prep_shadow_block(const Shape& s, int64_t bid,
+                                                  const float* __restrict__ W, T* w13s, T* w2s,
+                                                  T* w2ts) {
   const int64_t P = 3 * s.d * s.h;
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t idx = bid * 256 + threadIdx.x;
   if (idx >= s.BH * P) return;
   const int64_t u = idx / P, o = idx % P;
   write_shadow<T>(s, u, o, W[idx], w13s, w2s, w2ts);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_prep_shadow(Shape s, const float* __restrict__ W,
+                                                     T* w13s, T* w2s, T* w2ts) {
+  prep_shadow_block<T>(s, blockIdx.x, W, w13s, w2s, w2ts);
+}
+
+// The three independent set-up steps of a call in one launch (fewer launch
+// latencies on short sequences): workgroups [0, nscan) scan segments, the
+// next nkt stage K feature-major (token-permuted), the rest write the bf16
+// operand shadow of W_0.  The branch is uniform per workgroup.
+template <int TPT, int VW>
+__global__ __launch_bounds__(256) void k_prologue(ScanArgs sa, Shape s, const bf16_t* k,
+                                                  bf16_t* kt, const float* W0, bf16_t* w13s,
+                                                  bf16_t* w2s, bf16_t* w2ts, int64_t nscan,
+                                                  int64_t nkt) {
+  const int64_t b = blockIdx.x;
+  if (b < nscan) scan_segment<256, TPT, VW>(b, sa);
+  else if (b < nscan + nkt) prep_kt_block<bf16_t, true>(s, b - nscan, k, kt);
+  else prep_shadow_block<bf16_t>(s, b - nscan - nkt, W0, w13s, w2s, w2ts);
 }
 
 // ---------------------------------------------------------------------------

@@ -161,7 +161,9 @@ typedef enum {
                                   chunk-end state (unless token-split)      */
   E2TTT_KERNEL_STATE = 10,     /* d = 128 bf16, token-split phase B: sum of
                                   the splits, chunk-end state, shadows      */
-  E2TTT_KERNEL_NUM_CLASSES = 11
+  E2TTT_KERNEL_PROLOGUE = 11,  /* d = 128 bf16: scalar kernels, K^T staging
+                                  and W0 shadow in one launch               */
+  E2TTT_KERNEL_NUM_CLASSES = 12
 } e2ttt_kernel_class;
 
 /* Benchmark instrumentation: enqueue exactly the work of e2ttt_chunk_forward

@@ -354,7 +354,7 @@ void launch_swiglu(const Plan& q, const void* qv, const void* kv, const void* vv
   void (*kprep)(Shape, const T*, T*) = k_prep_kt<T, false>;
   E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, kprep,
                dim3(grid1(q.BH * q.nC * (q.Cp / 64) * (q.d / 64))), dim3(256), 0, st, s, K, kt);
-  E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, k_prep_shadow<T>, dim3(grid1((q.BH * q.P + 255) / 256)),
+  E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, k_prep_shadow<T>, dim3(grid1(shadow_blocks(s))),
                dim3(256), 0, st, s, W0, w13s, w2s, w2ts);
   const int64_t na = (4 * q.h / 128) * (q.d / 128), nb = (2 * q.d / 128) * (q.h / 128);
   for (int64_t r = 0; r < q.nC; ++r) {
@@ -410,7 +410,7 @@ void launch_fused(const Plan& q, const void* qv, const void* kv, const void* vv,
                                 reinterpret_cast<float*>(ws + q.km), q.nC * q.Cp, q.Cp, q.Cp,
                                 reinterpret_cast<float*>(ws + q.coef), 4);
   const int64_t nscan = q.BH * q.nC, nkt = q.BH * q.nC * (q.Cp / 64) * (q.d / 64);
-  const int64_t nshadow = (q.BH * q.P + 255) / 256;
+  const int64_t nshadow = shadow_blocks(s);
   if (nkt + nshadow <= kMaxPrologueBlocks) {
     const int tpt = scan_tpt(q.C);
     const bool vec = scan_vec_ok(q, tpt, q.nC * q.Cp, q.Cp);

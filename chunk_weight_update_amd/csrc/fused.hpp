@@ -1128,7 +1128,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // columns of one row: 16-byte loads and stores of W_0, M_0, W_C, M_C and
 // 8-byte stores of the row-major shadows.
 __global__ __launch_bounds__(256) void k_state_epi(FusedArgs a) {
-  __shared__ float sW[64 * 17], sM[64 * 17];
+  __shared__ float sW[64 * 17], sM[64 * 17], sT[64 * 17];
   const int64_t grp = blockIdx.x / 24;
   const int pr = static_cast<int>(blockIdx.x % 24);  // (t, jb) pair
   const int t = pr >> 3, jb = pr & 7;
@@ -1201,12 +1201,22 @@ __global__ __launch_bounds__(256) void k_state_epi(FusedArgs a) {
     bf16_t* b2 = a.w2s + (u * FD + j2) * (kr * h);
     put4(b2 + i, hi);
     if (kr == 2) put4(b2 + h + i, lo);
+    // W2^T through LDS: thread (il, jq) writes hidden row 64*ib + il, entries
+    // 16*jb + jq .. +3 (coalesced 8-byte stores instead of scattered halves).
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sT[(c0 + e) * 17 + r] = wn[e];
+    __syncthreads();
+    const int il = tid >> 2, jq = 4 * (tid & 3);
+    bf16_t th[4], tlo[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      bf16_t* bt = a.w2ts + (u * h + i + e) * (kr * FD);
-      bt[j2] = hi[e];
-      if (kr == 2) bt[FD + j2] = lo[e];
+      const float x = sT[il * 17 + jq + e];
+      th[e] = f2bf(x);
+      tlo[e] = kr == 2 ? f2bf(x - bf2f(th[e])) : bf16_t(0);
     }
+    bf16_t* bt = a.w2ts + (u * h + 64 * ib + il) * (kr * FD) + 16 * jb + jq;
+    put4(bt, th);
+    if (kr == 2) put4(bt + FD, tlo);
   }
 }
 

@@ -348,16 +348,83 @@ __device__ __forceinline__ void write_shadow(const Shape& s, int64_t u, int64_t 
   }
 }
 
+// Four consecutive operand values (hi part, and the lo part when lo != null).
+template <typename T>
+__device__ __forceinline__ void split_store4(const float (&w)[4], T* hi, T* lo) {
+  T h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = from_f32<T>(w[e]);
+    l[e] = from_f32<T>(w[e] - to_f32<T>(h[e]));
+  }
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<float4*>(hi) = make_float4(h[0], h[1], h[2], h[3]);
+    if (lo) *reinterpret_cast<float4*>(lo) = make_float4(l[0], l[1], l[2], l[3]);
+  } else {
+    auto pk = [](const T (&x)[4]) {
+      return make_uint2(x[0] | (static_cast<uint32_t>(x[1]) << 16),
+                        x[2] | (static_cast<uint32_t>(x[3]) << 16));
+    };
+    *reinterpret_cast<uint2*>(hi) = pk(h);
+    if (lo) *reinterpret_cast<uint2*>(lo) = pk(l);
+  }
+}
+
+// Operand shadows of one 64 x 64 tile of a unit's state (d, h multiples of
+// 64): tiles [0, 2(h/64)(d/64)) cover the stacked [W1; W3] (2h x d), the
+// rest W2 (d x h).  Loads and stores are coalesced 16-byte (fp32) or 8-byte
+// (bf16) accesses; the transposed copy of W2 goes through LDS.
 template <typename T>
 __device__ __forceinline__ void prep_shadow_block(const Shape& s, int64_t bid,
                                                   const float* __restrict__ W, T* w13s, T* w2s,
                                                   T* w2ts) {
-  const int64_t P = 3 * s.d * s.h;
-  const int64_t idx = bid * 256 + threadIdx.x;
-  if (idx >= s.BH * P) return;
-  const int64_t u = idx / P, o = idx % P;
-  write_shadow<T>(s, u, o, W[idx], w13s, w2s, w2ts);
+  __shared__ float tileT[64 * 65];
+  const int64_t d = s.d, h = s.h, kr = s.krep;
+  const int64_t n13 = 2 * (h / 64) * (d / 64), n2 = (d / 64) * (h / 64);
+  const int64_t u = bid / (n13 + n2), tl = bid % (n13 + n2);
+  const float* Wu = W + u * 3 * d * h;
+  const int tid = threadIdx.x, rr = tid >> 4, c0 = 4 * (tid & 15);
+  if (tl < n13) {  // rows of [W1; W3]
+    const int64_t R0 = 64 * (tl / (d / 64)), C0 = 64 * (tl % (d / 64));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t sr = R0 + rr + 16 * k;  // stacked row
+      const float4 x = *reinterpret_cast<const float4*>(Wu + sr * d + C0 + c0);
+      const float w[4] = {x.x, x.y, x.z, x.w};
+      const int isW3 = sr >= h;
+      const int64_t oo = isW3 ? sr - h : sr;
+      const int64_t srow = 64 * (oo / 32) + 32 * isW3 + oo % 32;
+      T* base = w13s + (u * 2 * h + srow) * (kr * d) + C0 + c0;
+      split_store4<T>(w, base, kr == 2 ? base + d : nullptr);
+    }
+    return;
+  }
+  const int64_t t2 = tl - n13;
+  const int64_t J0 = 64 * (t2 / (h / 64)), I0 = 64 * (t2 % (h / 64));  // W2 rows, columns
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int jr = rr + 16 * k;
+    const float4 x = *reinterpret_cast<const float4*>(Wu + 2 * h * d + (J0 + jr) * h + I0 + c0);
+    const float w[4] = {x.x, x.y, x.z, x.w};
+    T* b2 = w2s + (u * d + J0 + jr) * (kr * h) + I0 + c0;
+    split_store4<T>(w, b2, kr == 2 ? b2 + h : nullptr);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tileT[(c0 + e) * 65 + jr] = w[e];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {  // W2^T row I0 + ir, columns J0 + c0 ..
+    const int ir = rr + 16 * k;
+    float w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = tileT[ir * 65 + c0 + e];
+    T* bt = w2ts + (u * h + I0 + ir) * (kr * d) + J0 + c0;
+    split_store4<T>(w, bt, kr == 2 ? bt + d : nullptr);
+  }
 }
+
+// Workgroups of the shadow of all units' states.
+inline int64_t shadow_blocks(const Shape& s) { return s.BH * 3 * (s.d / 64) * (s.h / 64); }
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_prep_shadow(Shape s, const float* __restrict__ W,

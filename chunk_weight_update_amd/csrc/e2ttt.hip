@@ -32,9 +32,6 @@ constexpr int64_t kMaxChunk = 12288;
 // workspace size stays a pure function of the problem.
 constexpr int64_t kCUs = 256;
 constexpr int kMaxSplitB = 4;
-// Above this many K^T and shadow workgroups the set-up steps are launched
-// separately (the combined launch runs at the scan's lower occupancy).
-constexpr int64_t kMaxPrologueBlocks = int64_t(1) << 40;
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -411,28 +408,17 @@ void launch_fused(const Plan& q, const void* qv, const void* kv, const void* vv,
                                 reinterpret_cast<float*>(ws + q.coef), 4);
   const int64_t nscan = q.BH * q.nC, nkt = q.BH * q.nC * (q.Cp / 64) * (q.d / 64);
   const int64_t nshadow = shadow_blocks(s);
-  if (nkt + nshadow <= kMaxPrologueBlocks) {
-    const int tpt = scan_tpt(q.C);
-    const bool vec = scan_vec_ok(q, tpt, q.nC * q.Cp, q.Cp);
-    void (*kpro)(ScanArgs, Shape, const bf16_t*, bf16_t*, const float*, bf16_t*, bf16_t*,
-                 bf16_t*, int64_t, int64_t) =
-        tpt == 1 ? k_prologue<1, 1>
-        : tpt == 2 ? (vec ? k_prologue<2, 2> : k_prologue<2, 1>)
-        : tpt == 4 ? (vec ? k_prologue<4, 4> : k_prologue<4, 1>)
-                   : (vec ? k_prologue<8, 4> : k_prologue<8, 1>);
-    E2TTT_LAUNCH(I, E2TTT_KERNEL_PROLOGUE, kpro, dim3(grid1(nscan + nkt + nshadow)), dim3(256),
-                 0, st, sa, s, a.k, reinterpret_cast<bf16_t*>(ws + q.kt), W0, a.w13s, a.w2s,
-                 a.w2ts, nscan, nkt);
-  } else {  // large set-up work: three launches, each at its own occupancy
-    launch_scan(q, eta, alpha, beta, reinterpret_cast<float*>(ws + q.kw),
-                reinterpret_cast<float*>(ws + q.km), q.nC * q.Cp, q.Cp, q.Cp,
-                reinterpret_cast<float*>(ws + q.coef), 4, st, I);
-    void (*kprep)(Shape, const bf16_t*, bf16_t*) = k_prep_kt<bf16_t, true>;
-    E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, kprep, dim3(grid1(nkt)), dim3(256), 0, st, s, a.k,
-                 reinterpret_cast<bf16_t*>(ws + q.kt));
-    E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, k_prep_shadow<bf16_t>, dim3(grid1(nshadow)), dim3(256),
-                 0, st, s, W0, a.w13s, a.w2s, a.w2ts);
-  }
+  const int tpt = scan_tpt(q.C);
+  const bool vec = scan_vec_ok(q, tpt, q.nC * q.Cp, q.Cp);
+  void (*kpro)(ScanArgs, Shape, const bf16_t*, bf16_t*, const float*, bf16_t*, bf16_t*,
+               bf16_t*, int64_t, int64_t) =
+      tpt == 1 ? k_prologue<1, 1>
+      : tpt == 2 ? (vec ? k_prologue<2, 2> : k_prologue<2, 1>)
+      : tpt == 4 ? (vec ? k_prologue<4, 4> : k_prologue<4, 1>)
+                 : (vec ? k_prologue<8, 4> : k_prologue<8, 1>);
+  E2TTT_LAUNCH(I, E2TTT_KERNEL_PROLOGUE, kpro, dim3(grid1(nscan + nkt + nshadow)), dim3(256),
+               0, st, sa, s, a.k, reinterpret_cast<bf16_t*>(ws + q.kt), W0, a.w13s, a.w2s,
+               a.w2ts, nscan, nkt);
   const unsigned gA = grid1(q.BH * (2 * q.Cp / q.rbA));
   const unsigned gB = grid1(q.BH * (q.h / 64) * q.nsplitB);
   for (int64_t r = 0; r < q.nC; ++r) {

@@ -11,12 +11,14 @@
 //
 // Tile: 256 x 256 per workgroup, 4 waves in a 2 x 2 grid, 128 x 128 per wave
 // (4 x 4 blocks of 32x32x16 MFMA, 256 accumulator registers), k-slabs of 32
-// tokens double-buffered in LDS with rows padded to 40 elements (80 bytes:
-// eight consecutive rows of a 16-byte fragment read hit distinct banks).  Per
-// slab a wave reads 16 KB of fragments for 32 MFMAs (1024 cycles), about 64
-// B/clk per CU of LDS: well under what four waves sustain (~86 B/clk), where
-// the 128 x 128 tile with 64 x 64 per wave needs 128 B/clk.
-//
+// tokens.  Slabs go from global memory straight into LDS (global_load_lds,
+// no registers), four stages deep, so three slabs are in flight while one is
+// computed: the memory latency is covered by three slabs of MFMA work rather
+// than one.  LDS rows are 64 bytes, unpadded; the four 16-byte pieces of row
+// r are stored in the order kc ^ swz256(r), so the 8 or 16 rows that one
+// fragment read serves together hit distinct bank groups.  Per slab a wave
+// reads 16 KB of fragments for 32 MFMAs.
+
 // Token split: the tile count of one unit can be small (108 at d = 768,
 // h = 1536), so the chunk's token slabs are split over S workgroups.  Each
 // writes its fp32 partial aggregates in the packed state layout, and
@@ -29,45 +31,91 @@ namespace e2ttt {
 
 struct Tile256 {
   static constexpr int BM = 256, BN = 256, BK = 32;
-  static constexpr int LS = BK + 8;                   // LDS row stride (elements)
-  static constexpr int SLAB = BM * LS;                // elements per operand slab
-  static constexpr size_t LDS_BYTES = 4 * SLAB * 2;  // A, B x double buffer, bf16
+  static constexpr int NST = 4;                             // LDS stages
+  static constexpr int SLAB_BYTES = BM * BK * 2;            // one operand slab (bf16)
+  static constexpr size_t LDS_BYTES = NST * 2 * SLAB_BYTES;  // A and B per stage: 128 KB
 };
 
-// Per-thread loader of one 256-row operand: thread t loads rows t/4 + 64*i,
-// 16-byte vector t%4 of each 32-element slab.  The four vectors travel as one
-// wide value (an array held across the k loop was demoted to scratch).
-typedef uint32_t u32x16_t __attribute__((ext_vector_type(16)));
+// Source of one 256-row operand for the direct LDS loads.  Load i (0..3) of
+// wave w fills the 1 KB of LDS that holds slab rows 16*(4w+i) .. +15: lane l
+// brings row 16*(4w+i) + l/4, physical piece l%4, which holds logical k-chunk
+// loader256_chunk(i).  rowp[i] points at that row's chunk (k offset 0).
 struct Loader256 {
   const bf16_t* rowp[4];
-  __device__ __forceinline__ u32x16_t load(int64_t k0) const {
-    const int vec = threadIdx.x & 3;
-    u32x16_t r;
+  __device__ __forceinline__ void issue(int64_t k0, char* slab) const {
+    const int wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 v = *reinterpret_cast<const uint4*>(rowp[i] + k0 + vec * 8);
-      r[4 * i] = v.x; r[4 * i + 1] = v.y; r[4 * i + 2] = v.z; r[4 * i + 3] = v.w;
-    }
-    return r;
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(
+          static_cast<const void*>(rowp[i] + k0),
+          (__attribute__((address_space(3))) void*)(slab + (4 * wave + i) * 1024),
+          16, 0, 0);
   }
 };
 
-__device__ __forceinline__ void stage256(bf16_t* slab, const u32x16_t& r) {
-  const int row0 = threadIdx.x >> 2, vec = threadIdx.x & 3;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<uint4*>(slab + (row0 + 64 * i) * Tile256::LS + vec * 8) =
-        make_uint4(r[4 * i], r[4 * i + 1], r[4 * i + 2], r[4 * i + 3]);
+// Physical 16-byte piece of logical k-chunk kc in slab row r: kc ^ swz(r),
+// with swz chosen so that 8 or 16 consecutive rows read at one chunk hit
+// distinct 16-byte bank groups.
+__device__ __forceinline__ int swz256(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+__device__ __forceinline__ int loader256_row(int i) {
+  return 16 * (4 * (threadIdx.x >> 6) + i) + ((threadIdx.x & 63) >> 2);
+}
+__device__ __forceinline__ int loader256_chunk(int i) {
+  return (threadIdx.x & 3) ^ swz256(loader256_row(i));
 }
 
-__device__ __forceinline__ int loader256_row(int i) { return (threadIdx.x >> 2) + 64 * i; }
+// Workgroup barrier without the memory fence of __syncthreads (whose
+// release would wait for every load in flight, the prefetched slabs
+// included).  LDS visibility is ordered by hand: the slab a barrier
+// publishes was waited for with wait_vmcnt before it, and every LDS read of
+// a stage is consumed (its MFMAs issued) before the barrier after which the
+// stage is refilled.  The empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void barrier_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most 8n of this wave's slab loads are in flight (n slabs).
+__device__ __forceinline__ void wait_slabs(int n);
+
+// Wait until at most N vector memory operations of this wave are in flight
+// (gfx9 s_waitcnt encoding; expcnt and lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+__device__ __forceinline__ void wait_slabs(int n) {
+  if (n >= 3) wait_vmcnt<24>();
+  else if (n == 2) wait_vmcnt<16>();
+  else if (n == 1) wait_vmcnt<8>();
+  else wait_vmcnt<0>();
+}
+
+// Fragments of one slab for one wave as one wide value (an array or struct
+// of fragments held across the k loop is demoted to scratch): fragment q =
+// 8*ks + i (A, block i) or 8*ks + 4 + j (B, block j) is dwords 4q .. 4q+3.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x64_t __attribute__((ext_vector_type(64)));
+
+template <int Q>
+__device__ __forceinline__ bf16x8_t frag256(const u32x64_t& f) {
+  const u32x4_t v = __builtin_shufflevector(f, f, 4 * Q, 4 * Q + 1, 4 * Q + 2, 4 * Q + 3);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
 
 // acc[mi][ni] (rows wm*128 + 32*mi, cols wn*128 + 32*ni) += A B^T over k
-// [k0, k1) (multiples of 32).
+// [k0, k1) (multiples of 32).  Each slab costs a wave 8 loads (4 per
+// operand); NST-1 slabs are in flight from global memory while one is
+// computed.
 __device__ __forceinline__ void gemm_tile256(f32x16_t (&acc)[4][4], const Loader256& la,
                                              const Loader256& lb, int64_t k0, int64_t k1,
-                                             bf16_t* lds) {
-  constexpr int SLAB = Tile256::SLAB, LS = Tile256::LS;
+                                             char* lds) {
+  constexpr int NST = Tile256::NST, SB = Tile256::SLAB_BYTES, BK = Tile256::BK;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -76,45 +124,87 @@ __device__ __forceinline__ void gemm_tile256(f32x16_t (&acc)[4][4], const Loader
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int r32 = lane & 31, hf = lane >> 5;
-  // One slab in flight from global memory while the current one is computed
-  // from LDS.  (A second register set for a deeper prefetch does not fit
-  // beside the 256 accumulators: measured, it spills.)
-  u32x16_t ra = la.load(k0), rb = lb.load(k0);
-  stage256(lds, ra);
-  stage256(lds + SLAB, rb);
-  __syncthreads();
-  const int64_t ns = (k1 - k0) / Tile256::BK;
-  for (int64_t s = 0; s < ns; ++s) {
-    const int cur = static_cast<int>(s & 1);
-    const bool more = s + 1 < ns;
-    if (more) {
-      ra = la.load(k0 + (s + 1) * Tile256::BK);
-      rb = lb.load(k0 + (s + 1) * Tile256::BK);
-    }
-    const bf16_t* As = lds + 2 * cur * SLAB + (wm * 128 + r32) * LS + 8 * hf;
-    const bf16_t* Bs = lds + (2 * cur + 1) * SLAB + (wn * 128 + r32) * LS + 8 * hf;
+  const int r32 = lane & 31, hf = lane >> 5, sw = swz256(r32);
+  // Byte offset of this lane's fragment piece in k-step ks, inside a
+  // 32-row block (the block bases are multiples of 32 rows, so the swizzle
+  // only depends on r32).
+  const int off0 = r32 * 64 + ((hf ^ sw) << 4), off1 = r32 * 64 + (((2 + hf) ^ sw) << 4);
+  const int64_t ns = (k1 - k0) / BK;
+  auto issue = [&](int64_t slab) {
+    char* st = lds + (slab % NST) * 2 * SB;
+    la.issue(k0 + slab * BK, st);
+    lb.issue(k0 + slab * BK, st + SB);
+  };
+  auto read = [&](int64_t slab) -> u32x64_t {
+    const char* As = lds + (slab % NST) * 2 * SB + wm * 128 * 64;
+    const char* Bs = lds + (slab % NST) * 2 * SB + SB + wn * 128 * 64;
+    u32x64_t f;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t fa[4], fb[4];
+    for (int ks = 0; ks < 2; ++ks) {  // in order of use: B fragments, then A
+      const int off = ks == 0 ? off0 : off1;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        fa[i] = *reinterpret_cast<const bf16x8_t*>(As + i * 32 * LS + 16 * ks);
-        fb[i] = *reinterpret_cast<const bf16x8_t*>(Bs + i * 32 * LS + 16 * ks);
+        const u32x4_t vb = *reinterpret_cast<const u32x4_t*>(Bs + i * 32 * 64 + off);
+        const int qb = 8 * ks + 4 + i;
+        f[4 * qb] = vb[0]; f[4 * qb + 1] = vb[1]; f[4 * qb + 2] = vb[2]; f[4 * qb + 3] = vb[3];
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        const u32x4_t va = *reinterpret_cast<const u32x4_t*>(As + i * 32 * 64 + off);
+        const int qa = 8 * ks + i;
+        f[4 * qa] = va[0]; f[4 * qa + 1] = va[1]; f[4 * qa + 2] = va[2]; f[4 * qa + 3] = va[3];
+      }
+    }
+    return f;
+  };
+  auto mma = [&](const u32x64_t& f) {
+#define E2TTT_MMA256(KS, I)                                                                    \
+    {                                                                                          \
+      const bf16x8_t fa = frag256<8 * KS + I>(f);                                              \
+      acc[I][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, frag256<8 * KS + 4>(f), acc[I][0], 0, 0, 0); \
+      acc[I][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, frag256<8 * KS + 5>(f), acc[I][1], 0, 0, 0); \
+      acc[I][2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, frag256<8 * KS + 6>(f), acc[I][2], 0, 0, 0); \
+      acc[I][3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, frag256<8 * KS + 7>(f), acc[I][3], 0, 0, 0); \
+    }
+    E2TTT_MMA256(0, 0) E2TTT_MMA256(0, 1) E2TTT_MMA256(0, 2) E2TTT_MMA256(0, 3)
+    E2TTT_MMA256(1, 0) E2TTT_MMA256(1, 1) E2TTT_MMA256(1, 2) E2TTT_MMA256(1, 3)
+#undef E2TTT_MMA256
+  };
+  // Iteration s: wait for slab s+1 (at most one later slab may still be in
+  // flight), barrier (every wave has it, and every wave has read slab s-1,
+  // whose stage takes slab s+3), refill, read slab s+1, then slab s's MFMAs.
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      bf16_t* An = lds + 2 * (cur ^ 1) * SLAB;
-      stage256(An, ra);
-      stage256(An + SLAB, rb);
-    }
-    __syncthreads();
+  for (int p = 0; p < NST - 1; ++p)
+    if (p < ns) issue(p);
+  for (int64_t s = 0; s < ns; ++s) {
+    // Slab s has landed once at most the later slabs' loads are in flight;
+    // the barrier then also tells that every wave is done with slab s-1,
+    // whose stage takes slab s+NST-1.
+    const int64_t later = ns - 1 - s;
+    wait_slabs(static_cast<int>(later < NST - 2 ? later : NST - 2));
+    barrier_nofence();
+    if (s + NST - 1 < ns) issue(s + NST - 1);
+    mma(read(s));
+    // Interleave the slab's 16 fragment reads with its 32 MFMAs (reads one
+    // group ahead of their use) instead of the compiler's read, wait, MFMA
+    // clusters.
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   }
+  barrier_nofence();  // every wave's last reads are done before LDS is reused
 }
 
 // Partial aggregates of split sp over token slabs [k0, k1): workgroup
@@ -125,7 +215,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     Shape s, int nsplit, const bf16_t* __restrict__ ut, const bf16_t* __restrict__ kt,
     const bf16_t* __restrict__ gt, const bf16_t* __restrict__ zt, int r, float* part) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  bf16_t* lds = reinterpret_cast<bf16_t*>(smem_raw);
   const int64_t d = s.d, h = s.h;
   const int64_t na = (4 * h / 256) * (d / 256), nb = (2 * d / 256) * (h / 256);
   const int64_t per_unit = (na + nb) * nsplit;
@@ -141,16 +230,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     mt = t / (d / 256); nt = t % (d / 256);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      la.rowp[i] = ut + (u * 4 * h + mt * 256 + loader256_row(i)) * s.Cp;
-      lb.rowp[i] = kt + ((u * s.nC + r) * d + nt * 256 + loader256_row(i)) * s.Cp;
+      const int c8 = 8 * loader256_chunk(i);
+      la.rowp[i] = ut + (u * 4 * h + mt * 256 + loader256_row(i)) * s.Cp + c8;
+      lb.rowp[i] = kt + ((u * s.nC + r) * d + nt * 256 + loader256_row(i)) * s.Cp + c8;
     }
   } else {
     const int64_t tb = t - na;
     mt = tb / (h / 256); nt = tb % (h / 256);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      la.rowp[i] = gt + (u * 2 * d + mt * 256 + loader256_row(i)) * s.Cp;
-      lb.rowp[i] = zt + (u * h + nt * 256 + loader256_row(i)) * s.Cp;
+      const int c8 = 8 * loader256_chunk(i);
+      la.rowp[i] = gt + (u * 2 * d + mt * 256 + loader256_row(i)) * s.Cp + c8;
+      lb.rowp[i] = zt + (u * h + nt * 256 + loader256_row(i)) * s.Cp + c8;
     }
   }
   const int64_t nslab = s.Cp / Tile256::BK;
@@ -158,7 +249,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int64_t k0 = sp * per * Tile256::BK;
   const int64_t k1 = (sp * per + per < nslab ? sp * per + per : nslab) * Tile256::BK;
   f32x16_t acc[4][4];
-  gemm_tile256(acc, la, lb, k0, k1, lds);
+  gemm_tile256(acc, la, lb, k0, k1, smem_raw);
 
   // Output row R (tile row): 64-row block R/64 holds 32 W rows then 32 M rows
   // of the same 32 state rows, so accumulator block mi is W (mi even) or M.

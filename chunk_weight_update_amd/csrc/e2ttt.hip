@@ -44,6 +44,7 @@ struct Plan {
   int rbA;      // phase A rows per workgroup (32 or 64; LDS-streamed variant)
   int wpuA;     // register-resident phase A: workgroups per unit (0: not used)
   int nsplitAgg;  // generic bf16 path: token split of the 256x256-tile aggregation (0: 128x128 tiles)
+  bool tile256 = false;  // generic path: forward GEMMs on 256x256 tiles
   int nsplitB;  // phase B token split (1: fused state epilogue)
   size_t opsz;  // bytes per GEMM operand element (2 for bf16, 4 for fp32)
   // workspace offsets (bytes)
@@ -165,6 +166,10 @@ e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
     q.ut = take(T * q.BH * 4 * q.h * q.Cp);
     q.gt = take(T * q.BH * 2 * q.d * q.Cp);
     q.zt = take(T * q.BH * q.h * q.Cp);
+    // Plain bf16 operands with d, h and the padded chunk multiples of 256:
+    // the forward GEMMs (fwd13, fwd2) run on 256x256 tiles.
+    q.tile256 = q.io == E2TTT_BF16 && q.krep == 1 && q.d % 256 == 0 && q.h % 256 == 0 &&
+                q.Cp % 256 == 0;
     // bf16 operands with d, h multiples of 256: the aggregation runs on
     // 256x256 tiles; the chunk's token slabs are split so that the grid comes
     // close to one workgroup per CU, and k_agg_reduce adds the splits.
@@ -224,7 +229,8 @@ void set_lds_attributes() {
       reinterpret_cast<const void*>(&k_phaseA<32, 1>), reinterpret_cast<const void*>(&k_phaseA<64, 1>),
       reinterpret_cast<const void*>(&k_phaseA<64, 2>), reinterpret_cast<const void*>(&k_phaseB<1>),
       reinterpret_cast<const void*>(&k_phaseB<2>), reinterpret_cast<const void*>(&k_phaseA2<32>),
-      reinterpret_cast<const void*>(&k_phaseA2<64>), reinterpret_cast<const void*>(&k_agg256)};
+      reinterpret_cast<const void*>(&k_phaseA2<64>), reinterpret_cast<const void*>(&k_agg256),
+      reinterpret_cast<const void*>(&k_fwd13_256), reinterpret_cast<const void*>(&k_fwd2_256)};
   for (const void* f : fused_kernels)
     (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   g_attr_done.store(1, std::memory_order_release);
@@ -322,6 +328,28 @@ void launch_agg256(const Plan& q, const Shape& s, int r, int last, const T* ut, 
   }
 }
 
+// Forward GEMMs of one chunk on 256x256 tiles (plain bf16), then the backward.
+template <typename T>
+void launch_fwd_bwd256(const Plan& q, const Shape& s, int r, const T* Q, const T* K, const T* V,
+                       T* O, const T* w13s, const T* w2s, const T* w2ts, T* zrow, float* a1s,
+                       float* a3s, T* zt, const float* kw, const float* km, T* grow, T* gt, T* ut,
+                       hipStream_t st, Instr& I) {
+  static_assert(sizeof(T) == 2 || sizeof(T) == 4, "operand type");
+  if constexpr (sizeof(T) == 2) {
+    E2TTT_LAUNCH(I, E2TTT_KERNEL_FWD13, k_fwd13_256,
+                 dim3(grid1(q.BH * (2 * q.Cp / 256) * (2 * q.h / 256))), dim3(256),
+                 Tile256::LDS_BYTES, st, s, r, Q, K, w13s, zrow, a1s, a3s, zt);
+    E2TTT_LAUNCH(I, E2TTT_KERNEL_FWD2, k_fwd2_256,
+                 dim3(grid1(q.BH * (2 * q.Cp / 256) * (q.d / 256))), dim3(256), Tile256::LDS_BYTES,
+                 st, s, r, V, O, zrow, w2s, kw, km, grow, gt);
+    // The backward stays on 128x128 tiles: its epilogue is memory-bound (fp32
+    // A1, A3 in, four scaled outputs out), and the 128-tile kernel overlaps
+    // it with other workgroups' MFMAs (measured faster at d = 768).
+    E2TTT_LAUNCH(I, E2TTT_KERNEL_BWD, k_bwd<T>, dim3(grid1(q.BH * (q.Cp / 128) * (q.h / 128))),
+                 dim3(256), 0, st, s, r, grow, w2ts, a1s, a3s, kw, km, ut);
+  }
+}
+
 template <typename T>
 void launch_swiglu(const Plan& q, const void* qv, const void* kv, const void* vv,
                    const float* eta, const float* alpha, const float* beta, const float* W0,
@@ -358,14 +386,20 @@ void launch_swiglu(const Plan& q, const void* qv, const void* kv, const void* vv
     const float* Win = r == 0 ? W0 : Wend;
     const float* Min = r == 0 ? M0 : Mend;
     const int ri = static_cast<int>(r);
-    E2TTT_LAUNCH(I, E2TTT_KERNEL_FWD13, k_fwd13<T>,
-                 dim3(grid1(q.BH * (2 * q.Cp / 128) * (2 * q.h / 128))), dim3(256), 0, st, s, ri,
-                 Q, K, w13s, zrow, a1s, a3s, zt);
-    E2TTT_LAUNCH(I, E2TTT_KERNEL_FWD2, k_fwd2<T>,
-                 dim3(grid1(q.BH * (2 * q.Cp / 128) * (q.d / 128))), dim3(256), 0, st, s, ri, V,
-                 O, zrow, w2s, kw, km, grow, gt);
-    E2TTT_LAUNCH(I, E2TTT_KERNEL_BWD, k_bwd<T>, dim3(grid1(q.BH * (q.Cp / 128) * (q.h / 128))),
-                 dim3(256), 0, st, s, ri, grow, w2ts, a1s, a3s, kw, km, ut);
+    if (q.tile256) {
+      launch_fwd_bwd256(q, s, ri, Q, K, V, O, w13s, w2s, w2ts, zrow, a1s, a3s, zt, kw, km, grow,
+                        gt, ut, st, I);
+    } else {
+      E2TTT_LAUNCH(I, E2TTT_KERNEL_FWD13, k_fwd13<T>,
+                   dim3(grid1(q.BH * (2 * q.Cp / 128) * (2 * q.h / 128))), dim3(256), 0, st, s,
+                   ri, Q, K, w13s, zrow, a1s, a3s, zt);
+      E2TTT_LAUNCH(I, E2TTT_KERNEL_FWD2, k_fwd2<T>,
+                   dim3(grid1(q.BH * (2 * q.Cp / 128) * (q.d / 128))), dim3(256), 0, st, s, ri, V,
+                   O, zrow, w2s, kw, km, grow, gt);
+      E2TTT_LAUNCH(I, E2TTT_KERNEL_BWD, k_bwd<T>,
+                   dim3(grid1(q.BH * (q.Cp / 128) * (q.h / 128))), dim3(256), 0, st, s, ri, grow,
+                   w2ts, a1s, a3s, kw, km, ut);
+    }
     if (q.nsplitAgg > 0) {  // the plan sets nsplitAgg for bf16 operands only
       launch_agg256(q, s, ri, static_cast<int>(r == q.nC - 1), ut, kt, gt, zt, coef, Win, Min,
                     Wend, Mend, w13s, w2s, w2ts, reinterpret_cast<float*>(ws + q.part256), st, I);

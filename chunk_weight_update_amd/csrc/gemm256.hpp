@@ -25,6 +25,8 @@
 // k_agg_reduce adds the S partials in split order (deterministic) and applies
 // W_C = cW W_0 + cWM M_0 + A^W, M_C = cM M_0 + A^M plus the operand shadows.
 #pragma once
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace e2ttt {
@@ -316,6 +318,262 @@ __global__ __launch_bounds__(256) void k_agg_reduce(Shape s, int nsplit, int r, 
 #pragma unroll
     for (int i = 0; i < 4; ++i) write_shadow<T>(s, u, e + i, wn[i], w13s, w2s, w2ts);
   }
+}
+
+
+// ---------------------------------------------------------------------------
+// Forward of the generic path on the same 256 x 256 tiles (plain bf16
+// operands, d, h and the padded chunk multiples of 256).  Same products and
+// epilogues as k_fwd13 / k_fwd2; feature-major outputs go through
+// LDS one accumulator band at a time: band mi holds tile rows 32*mi + [0,32)
+// of both wave rows, i.e. tokens p0 + 32*mi + [0,32) and p0 + 128 + 32*mi +
+// [0,32), as a [column][72] bf16 array (64 tokens + 8 pad).
+
+// Operand rows past a chunk's valid tokens load from here (d <= 1024).
+__device__ const bf16_t kZeroRow256[1024] = {};
+
+struct Acc256Pos {
+  int lane, wave, wm, wn, r32, hf;
+  __device__ Acc256Pos() {
+    lane = threadIdx.x & 63;
+    wave = threadIdx.x >> 6;
+    wm = wave >> 1;
+    wn = wave & 1;
+    r32 = lane & 31;
+    hf = lane >> 5;
+  }
+  // Tile row of accumulator block (mi, *) register v.
+  __device__ int row(int mi, int v) const { return 128 * wm + 32 * mi + 8 * (v >> 2) + 4 * hf + (v & 3); }
+  // Tile column of accumulator block (*, ni).
+  __device__ int col(int ni) const { return 128 * wn + 32 * ni + r32; }
+};
+
+// This lane's four consecutive band tokens 8*vq + 4*hf .. +3 of column c.
+__device__ __forceinline__ void band_put(bf16_t* lds, int c, const Acc256Pos& ps, int vq,
+                                         float x0, float x1, float x2, float x3) {
+  *reinterpret_cast<uint2*>(lds + c * 72 + 32 * ps.wm + 8 * vq + 4 * ps.hf) =
+      make_uint2(f2bf(x0) | (static_cast<uint32_t>(f2bf(x1)) << 16),
+                 f2bf(x2) | (static_cast<uint32_t>(f2bf(x3)) << 16));
+}
+
+// Copy ncol band columns out: column c's 64 tokens go to dst_row(c)[0 .. 31]
+// and dst_row(c)[128 .. 159] (16-byte vectors).
+template <typename RowFn>
+__device__ __forceinline__ void band_copy(const bf16_t* lds, int ncol, RowFn dst_row) {
+  for (int idx = threadIdx.x; idx < ncol * 8; idx += 256) {
+    const int c = idx >> 3, q = idx & 7, half = q >> 2, tok = 8 * (q & 3);
+    *reinterpret_cast<uint4*>(dst_row(c) + 128 * half + tok) =
+        *reinterpret_cast<const uint4*>(lds + c * 72 + 32 * half + tok);
+  }
+}
+
+// Compile-time band index (the accumulator array must only be indexed by
+// constants, or it is moved to scratch memory).
+template <int N>
+using Band = std::integral_constant<int, N>;
+
+template <bool B>
+using Flag = std::integral_constant<bool, B>;
+
+// Keeps an accumulator block in AGPRs up to this point: without it the
+// compiler moves all 256 accumulators to VGPRs right after the k loop, which
+// do not fit next to the epilogue's own values.
+__device__ __forceinline__ void pin_acc(f32x16_t& x) { asm volatile("" : "+a"(x)); }
+
+template <typename F>
+__device__ __forceinline__ void for_bands(F&& f) {
+  f(Band<0>{});
+  f(Band<1>{});
+  f(Band<2>{});
+  f(Band<3>{});
+}
+
+// fwd13: [K; Q] rows x [W1; W3]^T (w13s rows interleaved in blocks of 32, so
+// accumulator blocks 2*pr and 2*pr+1 are A1 and A3 of the same 32 hidden
+// units) -> Z = silu(A1) A3 row-major, A1 and A3 (fp32) and Z^T for K rows.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_fwd13_256(
+    Shape s, int r, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+    const bf16_t* __restrict__ w13s, bf16_t* zrow, float* a1s, float* a3s, bf16_t* zt) {
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  const int64_t ntn = 2 * s.h / 256, ntm = 2 * s.Cp / 256, mtK = s.Cp / 256;
+  int64_t bid = xcd_logical_block();
+  const int64_t nt = bid % ntn; bid /= ntn;
+  const int64_t mt = bid % ntm;
+  const int64_t u = bid / ntm;
+  const bool isQ = mt >= mtK;
+  const int64_t p0 = (mt - (isQ ? mtK : 0)) * 256;
+  const int64_t tok0 = static_cast<int64_t>(r) * s.C;
+  const int64_t nv = n_valid(s, r);
+  const bf16_t* X = (isQ ? q : k) + (u * s.L + tok0) * s.d;
+  Loader256 la, lb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c8 = 8 * loader256_chunk(i);
+    const int64_t p = p0 + loader256_row(i);
+    la.rowp[i] = (p < nv ? X + p * s.d : kZeroRow256) + c8;
+    lb.rowp[i] = w13s + (u * 2 * s.h + nt * 256 + loader256_row(i)) * s.d + c8;
+  }
+  f32x16_t acc[4][4];
+  gemm_tile256(acc, la, lb, 0, s.d, smem_raw);
+
+  const Acc256Pos ps;
+  bf16_t* lds = reinterpret_cast<bf16_t*>(smem_raw);
+  const int h = static_cast<int>(s.h);
+  // Row p0 of this tile in each output; offsets below are 32-bit.
+  bf16_t* zq = zrow + (u * 2 * s.Cp + (isQ ? s.Cp : 0) + p0) * s.h + nt * 128;
+  float* a1u = a1s + (u * s.Cp + p0) * s.h + nt * 128;
+  float* a3u = a3s + (u * s.Cp + p0) * s.h + nt * 128;
+  // Each band in two pieces (one per 32 hidden units), kept apart by
+  // scheduling barriers so that only one piece's values are live at a time.
+  auto band = [&](auto MI, auto KROWS) {
+    constexpr int mi = decltype(MI)::value;
+    constexpr bool krows = decltype(KROWS)::value;
+    if constexpr (krows) __syncthreads();  // the previous Z^T band has been copied out
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      const int j = ps.wn * 64 + pr * 32 + ps.r32;  // hidden unit - nt*128
+      pin_acc(acc[mi][2 * pr]);
+      pin_acc(acc[mi][2 * pr + 1]);
+      float zv[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int off = ps.row(mi, v) * h + j;
+        const float a1 = acc[mi][2 * pr][v], a3 = acc[mi][2 * pr + 1][v];
+        const float z = a1 * sigmoidf_(a1) * a3;
+        zv[v] = z;
+        zq[off] = f2bf(z);
+        if constexpr (krows) {
+          a1u[off] = a1;
+          a3u[off] = a3;
+        }
+      }
+      if constexpr (krows) {
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq)
+          band_put(lds, j, ps, vq, zv[4 * vq], zv[4 * vq + 1], zv[4 * vq + 2], zv[4 * vq + 3]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (krows) {  // Z^T band: 128 hidden rows x 64 tokens
+      __syncthreads();
+      band_copy(lds, 128, [&](int c) { return zt + (u * s.h + nt * 128 + c) * s.Cp + p0 + 32 * mi; });
+    }
+  };
+  if (isQ) for_bands([&](auto MI) { band(MI, Flag<false>{}); });
+  else for_bands([&](auto MI) { band(MI, Flag<true>{}); });
+}
+
+// fwd2: Z rows x W2^T -> Y; the readout for Q rows, g = v - Y for K rows
+// (row-major) and K^W g, K^M g feature-major (rows 64*(i/32) + i%32, +32 for
+// the momentum copy).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_fwd2_256(
+    Shape s, int r, const bf16_t* __restrict__ v, bf16_t* out, const bf16_t* __restrict__ zrow,
+    const bf16_t* __restrict__ w2s, const float* __restrict__ kw, const float* __restrict__ km,
+    bf16_t* grow, bf16_t* gt) {
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  const int64_t ntn = s.d / 256, ntm = 2 * s.Cp / 256, mtK = s.Cp / 256;
+  int64_t bid = xcd_logical_block();
+  const int64_t nt = bid % ntn; bid /= ntn;
+  const int64_t mt = bid % ntm;
+  const int64_t u = bid / ntm;
+  const bool isQ = mt >= mtK;
+  const int64_t p0 = (mt - (isQ ? mtK : 0)) * 256;
+  const int64_t tok0 = static_cast<int64_t>(r) * s.C;
+  const int64_t nv = n_valid(s, r);
+  Loader256 la, lb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c8 = 8 * loader256_chunk(i);
+    la.rowp[i] = zrow + (u * 2 * s.Cp + mt * 256 + loader256_row(i)) * s.h + c8;
+    lb.rowp[i] = w2s + (u * s.d + nt * 256 + loader256_row(i)) * s.h + c8;
+  }
+  f32x16_t acc[4][4];
+  gemm_tile256(acc, la, lb, 0, s.h, smem_raw);
+
+  const Acc256Pos ps;
+  const int d = static_cast<int>(s.d);
+  const int nvt = static_cast<int>(nv - p0 < 256 ? nv - p0 : 256);  // valid rows of the tile
+  if (isQ) {
+    bf16_t* o = out + (u * s.L + tok0) * s.d + nt * 256;
+    auto band = [&](auto MI, auto FULL) {
+      constexpr int mi = decltype(MI)::value;
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        pin_acc(acc[mi][ni]);
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) {
+          const int pr = ps.row(mi, vv);
+          if (decltype(FULL)::value || pr < nvt)
+            o[(p0 + pr) * s.d + ps.col(ni)] = f2bf(acc[mi][ni][vv]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    if (nvt == 256) for_bands([&](auto MI) { band(MI, Flag<true>{}); });
+    else for_bands([&](auto MI) { band(MI, Flag<false>{}); });
+    return;
+  }
+  bf16_t* lds = reinterpret_cast<bf16_t*>(smem_raw);
+  bf16_t* ldsM = lds + 256 * 72;
+  const bf16_t* vs = v + (u * s.L + tok0 + p0) * s.d + nt * 256;
+  bf16_t* gr = grow + (u * s.Cp + p0) * s.d + nt * 256;
+  const float* kwr = kw + (u * s.nC + r) * s.Cp + p0;
+  const float* kmr = km + (u * s.nC + r) * s.Cp + p0;
+  bf16_t* gbase = gt + u * 2 * s.d * s.Cp + p0;
+  auto band = [&](auto MI, auto FULL) {
+    constexpr int mi = decltype(MI)::value;
+    constexpr bool full = decltype(FULL)::value;
+    // All loads of the band first (v as bf16, the kernels): grow may alias v
+    // as far as the compiler knows.  Rows past the valid tokens read row 0
+    // and use 0.  Then one piece per accumulator column block, kept apart by
+    // scheduling barriers.
+    bf16_t vb[4][16];
+    float kwv[16], kmv[16];
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int vv = 0; vv < 16; ++vv) {
+        const int pr = ps.row(mi, vv);
+        vb[ni][vv] = vs[(full || pr < nvt ? pr : 0) * d + ps.col(ni)];
+      }
+#pragma unroll
+    for (int vv = 0; vv < 16; ++vv) {
+      kwv[vv] = kwr[ps.row(mi, vv)];
+      kmv[vv] = kmr[ps.row(mi, vv)];
+    }
+    __syncthreads();  // the previous band has been copied out
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      pin_acc(acc[mi][ni]);
+      float g[16];
+#pragma unroll
+      for (int vv = 0; vv < 16; ++vv) {
+        const int pr = ps.row(mi, vv);
+        g[vv] = (full || pr < nvt ? bf2f(vb[ni][vv]) : 0.0f) - acc[mi][ni][vv];
+        gr[pr * d + ps.col(ni)] = f2bf(g[vv]);
+      }
+      const int c = ps.col(ni);
+#pragma unroll
+      for (int vq = 0; vq < 4; ++vq) {
+        band_put(lds, c, ps, vq, kwv[4 * vq] * g[4 * vq], kwv[4 * vq + 1] * g[4 * vq + 1],
+                 kwv[4 * vq + 2] * g[4 * vq + 2], kwv[4 * vq + 3] * g[4 * vq + 3]);
+        band_put(ldsM, c, ps, vq, kmv[4 * vq] * g[4 * vq], kmv[4 * vq + 1] * g[4 * vq + 1],
+                 kmv[4 * vq + 2] * g[4 * vq + 2], kmv[4 * vq + 3] * g[4 * vq + 3]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    band_copy(lds, 256, [&](int c) {
+      const int64_t i = nt * 256 + c;
+      return gbase + (64 * (i / 32) + i % 32) * s.Cp + 32 * mi;
+    });
+    band_copy(ldsM, 256, [&](int c) {
+      const int64_t i = nt * 256 + c;
+      return gbase + (64 * (i / 32) + 32 + i % 32) * s.Cp + 32 * mi;
+    });
+  };
+  if (nvt == 256) for_bands([&](auto MI) { band(MI, Flag<true>{}); });
+  else for_bands([&](auto MI) { band(MI, Flag<false>{}); });
 }
 
 }  // namespace e2ttt

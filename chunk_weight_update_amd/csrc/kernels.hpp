@@ -512,8 +512,9 @@ __global__ __launch_bounds__(256) void k_fwd13(Shape s, int r, const T* __restri
 }
 
 // Transposed store of a 128x128 accumulator-layout tile whose column c goes
-// to destination row dst_row(c) (row-contiguous along the tile's rows).
-template <typename T, typename RowFn>
+// to destination row dst_row(c) (row-contiguous along the tile's rows).  BR
+// selects the early-return bf16 conversion.
+template <typename T, bool BR = false, typename RowFn>
 __device__ __forceinline__ void store_T(const float (&val)[2][2][16], T* lds, RowFn dst_row) {
   constexpr int VE = Tile<T>::VE, W = 128 + VE, VPR = 128 / VE;
   const AccPos ps;
@@ -524,7 +525,8 @@ __device__ __forceinline__ void store_T(const float (&val)[2][2][16], T* lds, Ro
     for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
       for (int v = 0; v < 16; ++v)
-        lds[ps.col(ni) * W + ps.row(mi, v)] = from_f32<T>(val[mi][ni][v]);
+        if constexpr (BR && sizeof(T) == 2) lds[ps.col(ni) * W + ps.row(mi, v)] = f2bf_br(val[mi][ni][v]);
+        else lds[ps.col(ni) * W + ps.row(mi, v)] = from_f32<T>(val[mi][ni][v]);
   __syncthreads();
   for (int idx = threadIdx.x; idx < 128 * VPR; idx += 256) {
     const int rr = idx / VPR, c = idx % VPR;
@@ -678,7 +680,7 @@ __global__ __launch_bounds__(256) void k_bwd(Shape s, int r, const T* __restrict
 #pragma unroll
         for (int vv = 0; vv < 16; ++vv)
           sc[mi][ni][vv] = kr[p0 + ps.row(mi, vv)] * (isA3 ? d3[mi][ni][vv] : d1[mi][ni][vv]);
-    store_T<T>(sc, lds, [&](int c) {
+    store_T<T, true>(sc, lds, [&](int c) {
       const int64_t j = nt * 128 + c;
       return ubase + ((isA3 ? 2 * s.h : 0) + 64 * (j / 32) + (isM ? 32 : 0) + j % 32) * s.Cp;
     });

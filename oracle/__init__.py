@@ -65,13 +65,13 @@ def _load():
             P = ctypes.POINTER(ctypes.c_double)
             i64 = ctypes.c_int64
             lib.oracle_chunk_forward.argtypes = (
-                [ctypes.c_int, ctypes.c_int] + [i64] * 6 + [P] * 11)
+                [ctypes.c_int, ctypes.c_int] + [i64] * 6 + [P] * 11 + [ctypes.c_int])
             lib.oracle_chunk_forward.restype = ctypes.c_int
             lib.oracle_token_descent.argtypes = [ctypes.c_int, i64, i64, P, P, P, P]
             lib.oracle_token_descent.restype = ctypes.c_int
             lib.oracle_fast_forward.argtypes = [ctypes.c_int, i64, i64, P, P, P]
             lib.oracle_fast_forward.restype = ctypes.c_int
-            lib.oracle_scalar_kernels.argtypes = [ctypes.c_int, i64, i64] + [P] * 6
+            lib.oracle_scalar_kernels.argtypes = [ctypes.c_int, i64, i64] + [P] * 6 + [ctypes.c_int]
             lib.oracle_scalar_kernels.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -100,9 +100,11 @@ def set_threads(n: int) -> None:
 
 
 def chunk_forward(kind, q, k, v, eta, alpha, beta, W0, M0, chunk, hidden=0,
-                  decay_mode=GAMMA_1_MINUS_ETA_ALPHA):
+                  decay_mode=GAMMA_1_MINUS_ETA_ALPHA, averaged=False):
     """Run the literal recurrence.  q,k,v: [B,H,L,d]; eta/alpha/beta: [B,H,L];
-    W0, M0: [B,H,P].  Returns (out [B,H,L,d], Wend, Mend), all float64."""
+    W0, M0: [B,H,P].  averaged: the chunk-averaged variant (beta, gamma
+    replaced by their means over each chunk).  Returns (out [B,H,L,d], Wend,
+    Mend), all float64."""
     lib = _load()
     q, k, v = _f64(q), _f64(k), _f64(v)
     eta, alpha, beta = _f64(eta), _f64(alpha), _f64(beta)
@@ -118,7 +120,7 @@ def chunk_forward(kind, q, k, v, eta, alpha, beta, W0, M0, chunk, hidden=0,
     rc = lib.oracle_chunk_forward(kind, decay_mode, B, H, L, d, hidden, chunk,
                                   _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
                                   _ptr(alpha), _ptr(beta), _ptr(W0), _ptr(M0),
-                                  _ptr(out), _ptr(Wend), _ptr(Mend))
+                                  _ptr(out), _ptr(Wend), _ptr(Mend), int(bool(averaged)))
     if rc != 0:
         raise RuntimeError(f"oracle_chunk_forward failed with code {rc}")
     return out, Wend, Mend
@@ -146,7 +148,7 @@ def fast_forward(kind, W, x, d, hidden=0):
     return y
 
 
-def scalar_kernels(eta, alpha, beta, decay_mode=GAMMA_1_MINUS_ETA_ALPHA):
+def scalar_kernels(eta, alpha, beta, decay_mode=GAMMA_1_MINUS_ETA_ALPHA, averaged=False):
     """Impulse-response kernels of each segment.  eta/alpha/beta: [nseg, n].
     Returns kw [nseg,n], km [nseg,n], coef [nseg,3] = (cW, cM, cWM)."""
     lib = _load()
@@ -156,7 +158,8 @@ def scalar_kernels(eta, alpha, beta, decay_mode=GAMMA_1_MINUS_ETA_ALPHA):
     km = np.empty_like(eta)
     coef = np.empty((nseg, 3), dtype=np.float64)
     rc = lib.oracle_scalar_kernels(decay_mode, nseg, n, _ptr(eta), _ptr(alpha),
-                                   _ptr(beta), _ptr(kw), _ptr(km), _ptr(coef))
+                                   _ptr(beta), _ptr(kw), _ptr(km), _ptr(coef),
+                                   int(bool(averaged)))
     if rc != 0:
         raise RuntimeError(f"oracle_scalar_kernels failed with code {rc}")
     return kw, km, coef

@@ -31,6 +31,12 @@
  *   - Inner learners: linear f_W(x) = W x (§2) and the three-matrix SwiGLU
  *     f(x) = W2 (silu(W1 x) * (W3 x)) (§5.2, App. B.5 "three-matrix
  *     fast-weight network").
+ *   - Variant (averaged != 0): the chunk-averaged ablation of §4.3 (Table 5)
+ *     and App. B.3 (Table 8), where the per-token momentum and decay factors
+ *     beta_t, gamma_t of a chunk are collapsed to chunk-level scalars.  The
+ *     pages do not say which average; this takes the arithmetic mean over the
+ *     chunk's tokens (of gamma_t, after Eq. 14), and otherwise the same
+ *     recurrence.
  *
  * The recurrence is run literally, token by token, on every state entry.
  * Each entry's recurrence involves only that entry, so the loops are ordered
@@ -168,6 +174,7 @@ int oracle_fast_forward(int kind, int64_t d, int64_t h, const double* W,
  *   W0, M0, Wend, Mend : [B, H, P]
  * Chunks are consecutive runs of C tokens; a final run shorter than C (when
  * C does not divide L) is a chunk of its own.  L == 0 copies the state.
+ * averaged != 0 selects the chunk-averaged variant (see the header).
  * Returns 0 on success, nonzero on bad arguments or allocation failure.
  */
 int oracle_chunk_forward(int kind, int decay_mode, int64_t B, int64_t H,
@@ -176,7 +183,7 @@ int oracle_chunk_forward(int kind, int decay_mode, int64_t B, int64_t H,
                          const double* eta, const double* alpha,
                          const double* beta, const double* W0,
                          const double* M0, double* out, double* Wend,
-                         double* Mend) {
+                         double* Mend, int averaged) {
   if (kind != OR_LINEAR && kind != OR_SWIGLU) return 1;
   if (decay_mode != OR_GAMMA_1_MINUS_ETA_ALPHA &&
       decay_mode != OR_ALPHA_IS_GAMMA)
@@ -208,7 +215,8 @@ int oracle_chunk_forward(int kind, int decay_mode, int64_t B, int64_t H,
     double* fu3 = (double*)malloc(sizeof(double) * (size_t)(Cmax * hh));
     double* fz = (double*)malloc(sizeof(double) * (size_t)(Cmax * hh));
     double* gam = (double*)malloc(sizeof(double) * (size_t)Cmax);
-    if (!Ws || !fe || !fu1 || !fu3 || !fz || !gam) {
+    double* bet = (double*)malloc(sizeof(double) * (size_t)Cmax);
+    if (!Ws || !fe || !fu1 || !fu3 || !fz || !gam || !bet) {
       status = 2;
     }
 
@@ -233,8 +241,23 @@ int oracle_chunk_forward(int kind, int decay_mode, int64_t B, int64_t H,
         }
         free(tmp);
       }
-      for (int64_t t = 0; t < n; ++t)
+      for (int64_t t = 0; t < n; ++t) {
         gam[t] = decay_factor(decay_mode, etu[t0 + t], alu[t0 + t]);
+        bet[t] = beu[t0 + t];
+      }
+      if (averaged) { /* chunk-level scalars: the means over the chunk */
+        double sb = 0.0, sgm = 0.0;
+        for (int64_t t = 0; t < n; ++t) {
+          sb += bet[t];
+          sgm += gam[t];
+        }
+        sb /= (double)n;
+        sgm /= (double)n;
+        for (int64_t t = 0; t < n; ++t) {
+          bet[t] = sb;
+          gam[t] = sgm;
+        }
+      }
 
       /* Token-wise recurrence on every state entry:
        *   M <- beta_t M + eta_t G_t ;  W <- gamma_t W + M.
@@ -275,7 +298,7 @@ int oracle_chunk_forward(int kind, int decay_mode, int64_t B, int64_t H,
           m = M + 2 * h * d + (r - 2 * h) * h;
         }
         for (int64_t t = 0; t < n; ++t) {
-          const double bt = beu[t0 + t];
+          const double bt = bet[t];
           const double et = etu[t0 + t];
           const double gt = gam[t];
           const double lt = left[t * lstride + lidx];
@@ -288,7 +311,7 @@ int oracle_chunk_forward(int kind, int decay_mode, int64_t B, int64_t H,
         }
       }
     }
-    free(Ws); free(fe); free(fu1); free(fu3); free(fz); free(gam);
+    free(Ws); free(fe); free(fu1); free(fu3); free(fz); free(gam); free(bet);
     if (status) return status;
   }
   return 0;
@@ -305,26 +328,53 @@ int oracle_chunk_forward(int kind, int decay_mode, int64_t B, int64_t H,
  *   coef[2] = cWM : W_C when M_0 = 1 (W_0 = 0, G = 0)
  * Arrays are [nseg, n] with nseg segments of n tokens; coef is [nseg, 3].
  * O(n^2) per segment: each impulse is propagated literally to the chunk end.
+ * averaged != 0: beta and gamma replaced by their segment means first.
  */
 int oracle_scalar_kernels(int decay_mode, int64_t nseg, int64_t n,
                           const double* eta, const double* alpha,
                           const double* beta, double* kw, double* km,
-                          double* coef) {
+                          double* coef, int averaged) {
   if (decay_mode != OR_GAMMA_1_MINUS_ETA_ALPHA &&
       decay_mode != OR_ALPHA_IS_GAMMA)
     return 1;
+  int status = 0;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t sg = 0; sg < nseg; ++sg) {
     const double* e = eta + sg * n;
     const double* a = alpha + sg * n;
-    const double* b = beta + sg * n;
+    const double* b0 = beta + sg * n;
+    double* b = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    double* g = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    if (!b || !g) {
+#pragma omp atomic write
+      status = 2;
+      free(b); free(g);
+      continue;
+    }
+    for (int64_t s = 0; s < n; ++s) {
+      b[s] = b0[s];
+      g[s] = decay_factor(decay_mode, e[s], a[s]);
+    }
+    if (averaged && n > 0) {
+      double sb = 0.0, sgm = 0.0;
+      for (int64_t s = 0; s < n; ++s) {
+        sb += b[s];
+        sgm += g[s];
+      }
+      sb /= (double)n;
+      sgm /= (double)n;
+      for (int64_t s = 0; s < n; ++s) {
+        b[s] = sb;
+        g[s] = sgm;
+      }
+    }
     for (int64_t t = 0; t < n; ++t) {
       /* token t receives the impulse: M = beta*0 + eta*1, W = gamma*0 + M */
       double m = e[t] * 1.0;
       double w = m;
       for (int64_t s = t + 1; s < n; ++s) {
         m = b[s] * m;
-        w = decay_factor(decay_mode, e[s], a[s]) * w + m;
+        w = g[s] * w + m;
       }
       kw[sg * n + t] = w;
       km[sg * n + t] = m;
@@ -332,16 +382,17 @@ int oracle_scalar_kernels(int decay_mode, int64_t nseg, int64_t n,
     double w = 1.0, m = 0.0; /* W_0 impulse */
     for (int64_t s = 0; s < n; ++s) {
       m = b[s] * m;
-      w = decay_factor(decay_mode, e[s], a[s]) * w + m;
+      w = g[s] * w + m;
     }
     coef[sg * 3 + 0] = w;
     w = 0.0; m = 1.0; /* M_0 impulse */
     for (int64_t s = 0; s < n; ++s) {
       m = b[s] * m;
-      w = decay_factor(decay_mode, e[s], a[s]) * w + m;
+      w = g[s] * w + m;
     }
     coef[sg * 3 + 1] = m;
     coef[sg * 3 + 2] = w;
+    free(b); free(g);
   }
-  return 0;
+  return status;
 }

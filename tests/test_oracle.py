@@ -319,3 +319,57 @@ def test_planted_mistakes_are_caught():
     assert _rel(mutated(), Wref) <= 1e-10
     assert _rel(mutated(sign=-1.0), Wref) > 1e-3
     assert _rel(mutated(use_decay=False), Wref) > 1e-3
+
+
+# --- Chunk-averaged variant (the ablation of §4.3 / App. B.3 of the E2-TTT
+# page: per-token beta_t, gamma_t collapsed to chunk-level scalars; reading:
+# arithmetic means over the chunk's tokens).
+
+def _chunk_means(x, C):
+    """Per-token array whose entries are the means of x over each chunk."""
+    y = np.empty_like(x)
+    L = x.shape[-1]
+    for t0 in range(0, L, C):
+        y[..., t0:t0 + C] = np.mean(x[..., t0:t0 + C], axis=-1, keepdims=True)
+    return y
+
+
+@pytest.mark.parametrize("kind,d,h", [(oracle.LINEAR, 4, 0), (oracle.SWIGLU, 3, 5)])
+@pytest.mark.parametrize("C,L", [(3, 9), (7, 17), (5, 5)])
+def test_chunk_averaged_is_recurrence_on_averaged_factors(kind, d, h, C, L):
+    """The averaged run equals the plain recurrence fed the chunk means of beta
+    and of gamma = 1 - eta*alpha (passed as gamma directly), means by numpy."""
+    rng = np.random.default_rng(7 + C)
+    q, k, v, eta, alpha, beta, W0, M0 = _rand_problem(rng, kind, L, d, h)
+    out, Wend, Mend = oracle.chunk_forward(kind, q, k, v, eta, alpha, beta, W0, M0, C, h,
+                                           averaged=True)
+    gbar = _chunk_means(1.0 - eta * alpha, C)
+    bbar = _chunk_means(beta, C)
+    out2, W2, M2 = oracle.chunk_forward(kind, q, k, v, eta, gbar, bbar, W0, M0, C, h,
+                                        decay_mode=oracle.ALPHA_IS_GAMMA)
+    assert _rel(Wend, W2) <= 1e-12 and _rel(Mend, M2) <= 1e-12
+    assert np.array_equal(out, out2)  # the readout does not depend on the factors
+    # and it differs from the per-token rule once the factors vary
+    _, W3, _ = oracle.chunk_forward(kind, q, k, v, eta, alpha, beta, W0, M0, C, h)
+    assert _rel(Wend, W3) > 1e-6
+
+
+def test_chunk_averaged_kernels_are_geometric_in_the_means():
+    """Closed form with constant factors, evaluated at numpy's chunk means."""
+    rng = np.random.default_rng(11)
+    n = 29
+    eta = 0.05 + 0.2 * rng.random((2, n))
+    alpha = rng.random((2, n))
+    beta = 0.3 + 0.6 * rng.random((2, n))
+    kw, km, coef = oracle.scalar_kernels(eta, alpha, beta, averaged=True)
+    for sg in range(2):
+        b = float(np.mean(beta[sg]))
+        g = float(np.mean(1.0 - eta[sg] * alpha[sg]))
+        m = n - 1 - np.arange(n)
+        assert np.max(np.abs(km[sg] - eta[sg] * b ** m) / (eta[sg] * b ** m)) <= 1e-12
+        P = (g ** (m + 1) - b ** (m + 1)) / (g - b)
+        assert np.max(np.abs(kw[sg] - eta[sg] * P) / (eta[sg] * P)) <= 1e-12
+        assert abs(coef[sg, 0] - g ** n) <= 1e-13 * g ** n
+        assert abs(coef[sg, 1] - b ** n) <= 1e-13 * b ** n
+        P0 = (g ** n - b ** n) / (g - b)
+        assert abs(coef[sg, 2] - b * P0) <= 1e-12 * b * P0

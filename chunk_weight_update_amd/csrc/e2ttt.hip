@@ -40,6 +40,7 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow
 struct Plan {
   int64_t B, H, BH, L, d, h, C, Cp, nC, P;
   int kind, io, mode, krep;
+  int averaged = 0;  // chunk-averaged beta, gamma (E2TTT_FLAG_CHUNK_AVERAGED_DECAY)
   bool fused;   // two-kernel chunk step (SwiGLU, d = 128, bf16 io)
   int rbA;      // phase A rows per workgroup (32 or 64; LDS-streamed variant)
   int wpuA;     // register-resident phase A: workgroups per unit (0: not used)
@@ -58,7 +59,9 @@ e2ttt_status check_problem(const e2ttt_problem* p) {
   if (p->io_dtype != E2TTT_F32 && p->io_dtype != E2TTT_BF16) return E2TTT_EINVAL;
   if (p->decay_mode != E2TTT_GAMMA_1_MINUS_ETA_ALPHA && p->decay_mode != E2TTT_ALPHA_IS_GAMMA)
     return E2TTT_EINVAL;
-  if ((p->flags & ~static_cast<uint32_t>(E2TTT_FLAG_COMPENSATED_WEIGHTS)) != 0u) return E2TTT_EINVAL;
+  if ((p->flags & ~static_cast<uint32_t>(E2TTT_FLAG_COMPENSATED_WEIGHTS |
+                                         E2TTT_FLAG_CHUNK_AVERAGED_DECAY)) != 0u)
+    return E2TTT_EINVAL;
   if (p->reserved != 0u) return E2TTT_EINVAL;
   if (p->batch < 1 || p->heads < 1 || p->seq_len < 0 || p->dim < 1 || p->chunk < 1)
     return E2TTT_EINVAL;
@@ -93,6 +96,7 @@ e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
   q.B = p->batch; q.H = p->heads; q.BH = q.B * q.H; q.L = p->seq_len;
   q.d = p->dim; q.h = p->hidden; q.C = p->chunk;
   q.kind = p->kind; q.io = p->io_dtype; q.mode = p->decay_mode;
+  q.averaged = (p->flags & E2TTT_FLAG_CHUNK_AVERAGED_DECAY) ? 1 : 0;
   q.nC = q.L > 0 ? (q.L + q.C - 1) / q.C : 0;
   q.P = q.kind == E2TTT_LINEAR ? q.d * q.d : 3 * q.d * q.h;
   const size_t f4 = 4;
@@ -285,7 +289,7 @@ ScanArgs scan_args(const Plan& q, const float* eta, const float* alpha, const fl
                    float* coef, int cstride) {
   ScanArgs sa;
   sa.eta = eta; sa.alpha = alpha; sa.beta = beta;
-  sa.L = q.L; sa.C = q.C; sa.nC = q.nC; sa.mode = q.mode;
+  sa.L = q.L; sa.C = q.C; sa.nC = q.nC; sa.mode = q.mode; sa.averaged = q.averaged;
   sa.kw = kw; sa.km = km;
   sa.ustride = ustride; sa.rstride = rstride; sa.pad = pad;
   sa.coef = coef; sa.cstride = cstride;

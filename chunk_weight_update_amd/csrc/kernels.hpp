@@ -106,6 +106,7 @@ struct ScanArgs {
   const float* beta;
   int64_t L, C, nC;
   int mode;
+  int averaged;  // beta, gamma replaced by their segment means
   float* kw;
   float* km;
   int64_t ustride, rstride, pad;
@@ -161,13 +162,45 @@ __device__ __forceinline__ void scan_segment(int64_t seg, const ScanArgs& sa) {
     km_o[i] = 0.0f;
   }
 
+  // Chunk-averaged variant: the segment's means of beta and gamma, summed in
+  // fp64 by a fixed-order block reduction (lane 0 of each wave, then the
+  // waves in order), so every thread holds the same two values.
+  double bbar = 0.0, gbar = 0.0;
+  if (sa.averaged) {
+    __shared__ double s_red[2][NW];
+    double sb = 0.0, sg = 0.0;
+    for (int64_t i = tid; i < n; i += NT) {
+      const double a = static_cast<double>(a_g[i]);
+      sb += static_cast<double>(b_g[i]);
+      sg += sa.mode == 1 ? a : 1.0 - static_cast<double>(e_g[i]) * a;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      sb += __shfl_xor(sb, off, 64);
+      sg += __shfl_xor(sg, off, 64);
+    }
+    if (lane == 0) {
+      s_red[0][w] = sb;
+      s_red[1][w] = sg;
+    }
+    __syncthreads();
+    sb = 0.0;
+    sg = 0.0;
+    for (int v = 0; v < NW; ++v) {
+      sb += s_red[0][v];
+      sg += s_red[1][v];
+    }
+    bbar = sb / static_cast<double>(n);
+    gbar = sg / static_cast<double>(n);
+  }
+
   ScanVec vin = {1.0, 1.0, 1.0};  // v at the last token of the current round
   const int64_t nr = (n + R - 1) / R;
   for (int64_t rd = nr - 1; rd >= 0; --rd) {
     const int pb = static_cast<int>(rd & 1);
     const int64_t j0 = rd * R + static_cast<int64_t>(tid) * TPT;  // first token of the thread
-    float e[TPT], be[TPT];
-    double ga[TPT];
+    float e[TPT];
+    double be[TPT], ga[TPT];
 #pragma unroll
     for (int q = 0; q < TPT; q += VW) {
       float ev[VW], av[VW], bv[VW];
@@ -182,10 +215,11 @@ __device__ __forceinline__ void scan_segment(int64_t seg, const ScanArgs& sa) {
 #pragma unroll
       for (int i = 0; i < VW; ++i) {
         e[q + i] = ev[i];
-        be[q + i] = bv[i];
+        be[q + i] = sa.averaged ? bbar : static_cast<double>(bv[i]);
         // eta*alpha of two fp32 values is exact in fp64; one rounding in 1 - x.
-        ga[q + i] = sa.mode == 1 ? static_cast<double>(av[i])
-                                 : 1.0 - static_cast<double>(ev[i]) * static_cast<double>(av[i]);
+        ga[q + i] = sa.averaged ? gbar
+                    : sa.mode == 1 ? static_cast<double>(av[i])
+                                   : 1.0 - static_cast<double>(ev[i]) * static_cast<double>(av[i]);
       }
     }
     // This thread's map T_{j0} o ... o T_{j0+TPT-1}; tokens past n are the
@@ -194,7 +228,7 @@ __device__ __forceinline__ void scan_segment(int64_t seg, const ScanArgs& sa) {
 #pragma unroll
     for (int j = TPT - 1; j >= 0; --j) {
       if (j0 + j < n) {
-        const ScanMap t = {static_cast<double>(be[j]), ga[j], ga[j]};
+        const ScanMap t = {be[j], ga[j], ga[j]};
         m = scan_compose(t, m);
       }
     }
@@ -228,7 +262,7 @@ __device__ __forceinline__ void scan_segment(int64_t seg, const ScanArgs& sa) {
       okw[j] = static_cast<float>(static_cast<double>(e[j]) * cur.P);
       okm[j] = static_cast<float>(static_cast<double>(e[j]) * cur.b);
       if (j > 0) {
-        const ScanMap t = {static_cast<double>(be[j]), ga[j], ga[j]};
+        const ScanMap t = {be[j], ga[j], ga[j]};
         if (j0 + j < n) cur = scan_apply(t, cur);
       }
     }
@@ -240,7 +274,7 @@ __device__ __forceinline__ void scan_segment(int64_t seg, const ScanArgs& sa) {
       }
     }
     if (rd == 0 && tid == 0 && n > 0) {  // token 0: cur = v_0
-      const double b0 = static_cast<double>(be[0]);
+      const double b0 = be[0];
       float* cf = sa.coef + (u * sa.nC + r) * sa.cstride;
       cf[0] = static_cast<float>(ga[0] * cur.c);
       cf[1] = static_cast<float>(b0 * cur.b);

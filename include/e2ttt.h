@@ -81,7 +81,15 @@ enum {
    * activations) in the forward and backward products.  The weight operand
    * then carries ~16 mantissa bits instead of 8, at about 1.5x the
    * matrix-core work of the whole call.  Ignored for fp32 io and LINEAR. */
-  E2TTT_FLAG_COMPENSATED_WEIGHTS = 1u
+  E2TTT_FLAG_COMPENSATED_WEIGHTS = 1u,
+  /* The chunk-averaged variant ("Rethinking Expressivity and Efficiency in
+   * Test-Time Training", §4.3 Table 5 and App. B.3 Table 8): within each
+   * chunk the per-token momentum factors beta_t and decay factors gamma_t
+   * (after decay_mode) are replaced by their arithmetic means over the
+   * chunk's tokens before the scalar kernels are formed; eta_t stays per
+   * token.  Applies to e2ttt_chunk_forward, its timed twin and
+   * e2ttt_scalar_kernels, for every kind and dtype. */
+  E2TTT_FLAG_CHUNK_AVERAGED_DECAY = 2u
 };
 
 /* Problem description.  struct_size must equal sizeof(e2ttt_problem). */

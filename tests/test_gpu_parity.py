@@ -24,7 +24,7 @@ def check(kind, B, H, L, d, h, C, io, seed=0, regime="default", m0_scale=0.0, de
     inp = make_inputs(kind, B, H, L, d, h, io, seed=seed, regime=regime, m0_scale=m0_scale)
     prob = problem_for(kind, B, H, L, d, h, C, io, decay_mode, flags)
     out, W, M = run_gpu(prob, to_device(inp, io))
-    ro, rW, rM = run_oracle(kind, inp, C, h, decay_mode)
+    ro, rW, rM = run_oracle(kind, inp, C, h, decay_mode, averaged=bool(flags & 2))
     e = (rel_fro(out, ro), rel_fro(W, rW), rel_fro(M, rM))
     log(f"  rel_fro out={e[0]:.3e} W={e[1]:.3e} M={e[2]:.3e}")
     t = tol or TOL[io]
@@ -73,8 +73,8 @@ def test_scalar_kernels_match_oracle(B, H, L, C, regime, mode):
 def test_scalar_kernels_signs_and_zeros(L, C, mode):
     """Negative and zero factors: beta in [-1, 1] with exact zeros, and
     eta*alpha up to 4 so that gamma = 1 - eta*alpha changes sign (mode 0), or
-    alpha itself in [-1, 1] (mode 1).  Exercises the sign parities and the
-    -inf logarithm of a zero factor across several rounds of the scan."""
+    alpha itself in [-1, 1] (mode 1).  Exercises negative factors and exact
+    zeros across several rounds of the scan."""
     import torch
     import chunk_weight_update_amd as cwu
     log(f"scan signs L={L} C={C} mode={mode}")
@@ -103,6 +103,53 @@ def test_scalar_kernels_signs_and_zeros(L, C, mode):
                          (cf[:, :, r, :].reshape(-1, 3), ocf)):
             err = np.abs(got - ref)
             assert np.all(err <= 1e-6 * np.abs(ref) + 2e-38), float(np.max(err / (np.abs(ref) + 1e-300)))
+
+
+@pytest.mark.parametrize("B,H,L,C,regime,mode", [
+    (2, 4, 4096, 512, "default", 0),
+    (1, 2, 1000, 300, "nearunit", 0),     # short last chunk
+    (1, 1, 8192 * 2 + 17, 8192, "default", 0),
+    (1, 2, 640, 128, "default", 1),
+])
+def test_scalar_kernels_chunk_averaged(B, H, L, C, regime, mode):
+    """The chunk-averaged variant: beta and gamma replaced by their chunk
+    means (segment reduction in the scan) before the kernels are formed."""
+    import torch
+    import chunk_weight_update_amd as cwu
+    log(f"scan averaged B={B} H={H} L={L} C={C} {regime} mode={mode}")
+    inp = make_inputs(LINEAR, B, H, L, 16, 0, F32, seed=5, regime=regime)
+    prob = cwu.make_problem(LINEAR, B, H, L, 16, 0, C, F32, mode, cwu.FLAG_CHUNK_AVERAGED_DECAY)
+    dev = {n: torch.from_numpy(inp[n]).cuda() for n in ("eta", "alpha", "beta")}
+    nC = -(-L // C)
+    kw = torch.empty(B, H, L, device="cuda")
+    km = torch.empty(B, H, L, device="cuda")
+    cf = torch.empty(B, H, nC, 3, device="cuda")
+    cwu.scalar_kernels(prob, dev["eta"], dev["alpha"], dev["beta"], kw, km, cf)
+    torch.cuda.synchronize()
+    kw, km, cf = (x.cpu().numpy().astype(np.float64) for x in (kw, km, cf))
+    for r in range(nC):
+        sl = slice(r * C, min((r + 1) * C, L))
+        n = sl.stop - sl.start
+        okw, okm, ocf = oracle.scalar_kernels(inp["eta"][..., sl].reshape(-1, n),
+                                              inp["alpha"][..., sl].reshape(-1, n),
+                                              inp["beta"][..., sl].reshape(-1, n), mode,
+                                              averaged=True)
+        for got, ref in ((kw[..., sl].reshape(-1, n), okw), (km[..., sl].reshape(-1, n), okm),
+                         (cf[:, :, r, :].reshape(-1, 3), ocf)):
+            err = np.abs(got - ref)
+            assert np.all(err <= 1e-6 * np.abs(ref) + 2e-38), float(np.max(err / (np.abs(ref) + 1e-300)))
+
+
+@pytest.mark.parametrize("kind,B,H,L,d,h,C,io,regime", [
+    (LINEAR, 1, 2, 600, 64, 0, 128, F32, "default"),          # ragged last chunk
+    (SWIGLU, 1, 2, 600, 128, 256, 256, F32, "nearunit"),      # generic fp32 path
+    (SWIGLU, 2, 2, 512, 128, 256, 256, BF16, "nearunit"),     # fused path, split phase B
+    (SWIGLU, 1, 1, 700, 256, 512, 256, BF16, "nearunit"),     # 256-tile generic path
+])
+def test_chunk_averaged_forward(kind, B, H, L, d, h, C, io, regime):
+    import chunk_weight_update_amd as cwu
+    check(kind, B, H, L, d, h, C, io, seed=8, regime=regime,
+          m0_scale=M0.get(regime, 0.0), flags=cwu.FLAG_CHUNK_AVERAGED_DECAY)
 
 
 # --- linear learner ---------------------------------------------------------

@@ -176,6 +176,67 @@ def scan_microbench(reps=10):
             "gbs": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS}
 
 
+def decode_bench(w, reps=200):
+    """The decode step (one token of every unit per call, e2ttt_decode_step)
+    on the workload's B, H, d, h and io dtype, seeded synthetic inputs.
+    Algorithmic bytes per step and unit: W0 read once, W and M read and
+    written (5 P fp32), plus q, k, v, out.  Reported beside the main metric,
+    not as it."""
+    import torch
+    import chunk_weight_update_amd as cwu
+    B, H, d, h = w.B, w.H, w.d, w.h
+    io = torch.bfloat16 if w.io == 1 else torch.float32
+    P = d * d if w.kind == 0 else 3 * d * h
+    g = torch.Generator(device="cuda").manual_seed(1)
+    x = [torch.nn.functional.normalize(torch.randn((B, H, d), generator=g, device="cuda"),
+                                       dim=-1).to(io) for _ in range(3)]
+    eta = 0.1 * torch.sigmoid(torch.randn((B, H), generator=g, device="cuda"))
+    alpha = 1.0 - 0.05 * torch.sigmoid(torch.randn((B, H), generator=g, device="cuda"))
+    beta = 0.9 * torch.sigmoid(torch.randn((B, H), generator=g, device="cuda"))
+    W0 = torch.randn((B, H, P), generator=g, device="cuda") * (1.0 / d) ** 0.5
+    W, M = W0.clone(), torch.zeros_like(W0)
+    out = torch.empty_like(x[0])
+    prob = cwu.make_problem(w.kind, B, H, w.C, d, h, w.C, w.io, 0)
+    ws = torch.empty(cwu.decode_workspace_bytes(prob), dtype=torch.uint8, device="cuda")
+    for _ in range(20):
+        cwu.decode_step(prob, *x, eta, alpha, beta, W0, W, M, out, False, ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        cwu.decode_step(prob, *x, eta, alpha, beta, W0, W, M, out, False, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us_eager = e0.elapsed_time(e1) / reps * 1e3  # includes the host's per-call cost
+    # Device time per step: 50 steps captured in a graph (the step makes no
+    # allocation and no memset, so it captures), replayed.
+    us = None
+    try:
+        steps = 50
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(steps):
+                cwu.decode_step(prob, *x, eta, alpha, beta, W0, W, M, out, False, ws)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(4):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / (4 * steps) * 1e3
+    except Exception as exc:  # report the eager rate only
+        log(f"bench: decode graph capture unavailable ({exc})")
+    t = us if us is not None else us_eager
+    nbytes = B * H * (20.0 * P + 4 * d * (2 if w.io == 1 else 4))
+    gbs = nbytes / (t * 1e-6) / 1e9
+    return {"label": "decode step, one token per (b,h) unit per call (not the main metric)",
+            "shape": {"batch": B, "heads": H, "dim": d, "hidden": h},
+            "us_per_step": t, "us_per_step_eager_calls": us_eager,
+            "timing": "graph replay" if us is not None else "eager calls",
+            "tokens_per_s": B * H / (t * 1e-6), "gbs": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS}
+
+
 def algorithmic_flops(w):
     if w.kind == 0:
         return 8.0 * w.d * w.d * w.L * w.B * w.H
@@ -351,6 +412,8 @@ def main():
         "kernels": kernels,
     }
     if not args.no_scan_microbench:
+        line["decode"] = decode_bench(w)
+        log(f"bench: decode step {line['decode']}")
         line["scan_microbench"] = scan_microbench()
         log(f"bench: scan microbenchmark {line['scan_microbench']}")
     if not args.no_cpu_baseline:

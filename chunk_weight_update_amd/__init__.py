@@ -62,7 +62,8 @@ _lock = threading.Lock()
 _lib = None
 
 EXPORTED = ("e2ttt_validate", "e2ttt_workspace_bytes", "e2ttt_chunk_forward",
-            "e2ttt_scalar_kernels", "e2ttt_chunk_forward_timed", "e2ttt_status_string")
+            "e2ttt_scalar_kernels", "e2ttt_chunk_forward_timed", "e2ttt_status_string",
+            "e2ttt_decode_workspace_bytes", "e2ttt_decode_step")
 
 # e2ttt_kernel_class
 KERNEL_SCAN, KERNEL_PREP, KERNEL_FWD13, KERNEL_FWD2, KERNEL_BWD, KERNEL_AGG = range(6)
@@ -99,6 +100,11 @@ def lib() -> ctypes.CDLL:
             L.e2ttt_chunk_forward_timed.restype = ctypes.c_int
             L.e2ttt_scalar_kernels.argtypes = [P] + [vp] * 7
             L.e2ttt_scalar_kernels.restype = ctypes.c_int
+            L.e2ttt_decode_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+            L.e2ttt_decode_workspace_bytes.restype = ctypes.c_int
+            L.e2ttt_decode_step.argtypes = [P] + [vp] * 10 + [ctypes.c_int, vp, ctypes.c_size_t,
+                                                              vp]
+            L.e2ttt_decode_step.restype = ctypes.c_int
             L.e2ttt_status_string.argtypes = [ctypes.c_int]
             L.e2ttt_status_string.restype = ctypes.c_char_p
             _lib = L
@@ -181,6 +187,31 @@ def scalar_kernels(prob: Problem, eta, alpha, beta, k_w, k_m, chunk_coef, stream
                                     _ptr(k_w), _ptr(k_m), _ptr(chunk_coef), _stream(stream))
     if check and st != OK:
         raise E2tttError(st, "e2ttt_scalar_kernels")
+    return st
+
+
+def decode_workspace_bytes(prob: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    st = lib().e2ttt_decode_workspace_bytes(ctypes.byref(prob), ctypes.byref(n))
+    if st != OK:
+        raise E2tttError(st, "e2ttt_decode_workspace_bytes")
+    return int(n.value)
+
+
+def decode_step(prob: Problem, q, k, v, eta, alpha, beta, W0, W, M, out, chunk_end: bool,
+                workspace, workspace_nbytes: Optional[int] = None, stream=None,
+                check: bool = True) -> int:
+    """Call ``e2ttt_decode_step``: one token of every (b, h) unit; W0, W, M
+    are updated in place.  Returns the status; raises on failure when
+    ``check``."""
+    if workspace_nbytes is None:
+        workspace_nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().e2ttt_decode_step(
+        ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(alpha), _ptr(beta),
+        _ptr(W0), _ptr(W), _ptr(M), _ptr(out), int(bool(chunk_end)), _ptr(workspace),
+        int(workspace_nbytes), _stream(stream))
+    if check and st != OK:
+        raise E2tttError(st, "e2ttt_decode_step")
     return st
 
 

@@ -20,6 +20,7 @@
 #include "kernels.hpp"
 #include "gemm256.hpp"
 #include "fused.hpp"
+#include "decode.hpp"
 
 using namespace e2ttt;
 
@@ -675,6 +676,97 @@ e2ttt_status e2ttt_scalar_kernels(const e2ttt_problem* prob, const float* eta,
   Instr none;
   launch_scan(pl, eta, alpha, beta, k_w, k_m, pl.L, pl.C, 0, chunk_coef, 3,
               static_cast<hipStream_t>(stream), none);
+  return hipGetLastError() == hipSuccess ? E2TTT_OK : E2TTT_EHIP;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Decode workspace: z(q), z(k), A1(k), A3(k), dA1, dA3 [BH][h], g [BH][d]
+// and the W2^T g partials [d/64][BH][h], fp32.
+size_t decode_ws_bytes(int64_t BH, int64_t d, int64_t h) {
+  return align256(4 * static_cast<size_t>(BH) * static_cast<size_t>(6 * h + d + (d / 64) * h));
+}
+
+}  // namespace
+
+extern "C" {
+
+e2ttt_status e2ttt_decode_workspace_bytes(const e2ttt_problem* prob, size_t* bytes) {
+  if (!bytes) return E2TTT_EINVAL;
+  const e2ttt_status st = check_problem(prob);
+  if (st != E2TTT_OK) return st;
+  if (prob->flags & E2TTT_FLAG_CHUNK_AVERAGED_DECAY) return E2TTT_EUNSUPPORTED;
+  const int64_t h = prob->kind == E2TTT_LINEAR ? 0 : prob->hidden;
+  *bytes = decode_ws_bytes(prob->batch * prob->heads, prob->dim, h);
+  return E2TTT_OK;
+}
+
+e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* q, const void* k,
+                               const void* v, const float* eta, const float* alpha,
+                               const float* beta, float* W0, float* W, float* M, void* out,
+                               int chunk_end, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  e2ttt_status st = check_problem(prob);
+  if (st != E2TTT_OK) return st;
+  if (prob->flags & E2TTT_FLAG_CHUNK_AVERAGED_DECAY) return E2TTT_EUNSUPPORTED;
+  const int64_t BH = prob->batch * prob->heads, d = prob->dim;
+  const int64_t h = prob->kind == E2TTT_LINEAR ? 0 : prob->hidden;
+  const int64_t P = h == 0 ? d * d : 3 * d * h;
+  const size_t need = decode_ws_bytes(BH, d, h);
+  if (!q || !k || !v || !eta || !alpha || !beta || !W0 || !W || !M || !out || !workspace)
+    return E2TTT_EINVAL;
+  const void* p16[] = {q, k, v, eta, alpha, beta, W0, W, M, out};
+  for (const void* p : p16)
+    if (!aligned(p, 16)) return E2TTT_EINVAL;
+  if (!aligned(workspace, 256)) return E2TTT_EINVAL;
+  if (workspace_bytes < need) return E2TTT_EWORKSPACE;
+  const size_t iosz = prob->io_dtype == E2TTT_BF16 ? 2 : 4;
+  const size_t nx = static_cast<size_t>(BH * d) * iosz, ns = static_cast<size_t>(BH) * 4,
+               np = static_cast<size_t>(BH * P) * 4;
+  const Range in[] = {rng(q, nx), rng(k, nx), rng(v, nx), rng(eta, ns), rng(alpha, ns),
+                      rng(beta, ns)};
+  const Range outs[] = {rng(W0, np), rng(W, np), rng(M, np), rng(out, nx), rng(workspace, need)};
+  for (int a = 0; a < 5; ++a) {
+    for (int b = a + 1; b < 5; ++b)
+      if (overlap(outs[a], outs[b])) return E2TTT_EINVAL;
+    for (int i = 0; i < 6; ++i)
+      if (overlap(outs[a], in[i])) return E2TTT_EINVAL;
+  }
+  st = device_ok();
+  if (st != E2TTT_OK) return st;
+  (void)hipGetLastError();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* ws = static_cast<float*>(workspace);
+  DecodeArgs a;
+  a.BH = BH; a.d = d; a.h = h; a.mode = prob->decay_mode; a.chunk_end = chunk_end != 0;
+  a.eta = eta; a.alpha = alpha; a.beta = beta;
+  a.W0 = W0; a.W = W; a.M = M;
+  a.zq = ws; a.zk = ws + BH * h; a.a1k = ws + 2 * BH * h; a.a3k = ws + 3 * BH * h;
+  a.dA1 = ws + 4 * BH * h; a.dA3 = ws + 5 * BH * h; a.g = ws + 6 * BH * h;
+  const unsigned gu = grid1((BH * P / 4 + 255) / 256);
+  auto run = [&](auto tag) {
+    typedef decltype(tag) T;
+    const T* Q = static_cast<const T*>(q);
+    const T* K = static_cast<const T*>(k);
+    const T* V = static_cast<const T*>(v);
+    T* O = static_cast<T*>(out);
+    if (h == 0) {
+      hipLaunchKernelGGL(k_dec_lin_fwd<T>, dim3(grid1(BH)), dim3(256), 0, s, a, Q, K, V, O);
+    } else {
+      float* part = ws + 6 * BH * h + BH * d;
+      hipLaunchKernelGGL(k_dec_fwd13<T>, dim3(grid1(BH * (h / 16))), dim3(256), 0, s, a, Q, K);
+      hipLaunchKernelGGL(k_dec_fwd2<T>, dim3(grid1(BH * (d / 16))), dim3(256), 0, s, a, V, O);
+      hipLaunchKernelGGL(k_dec_bwd, dim3(grid1(BH * (h / 64) * (d / 64))), dim3(256), 0, s, a,
+                         part);
+      hipLaunchKernelGGL(k_dec_dact, dim3(grid1((BH * h + 255) / 256)), dim3(256), 0, s, a,
+                         static_cast<const float*>(part));
+    }
+    hipLaunchKernelGGL(k_dec_update<T>, dim3(gu), dim3(256), 0, s, a, K);
+  };
+  if (prob->io_dtype == E2TTT_BF16) run(bf16_t{});
+  else run(float{});
   return hipGetLastError() == hipSuccess ? E2TTT_OK : E2TTT_EHIP;
 }
 

@@ -197,6 +197,35 @@ E2TTT_API e2ttt_status e2ttt_chunk_forward_timed(const e2ttt_problem* prob, cons
 /* Static, human-readable name of a status code. */
 E2TTT_API const char* e2ttt_status_string(e2ttt_status status);
 
+/* Streaming / decode use ("Rethinking Expressivity and Efficiency in
+ * Test-Time Training": readout at the chunk-start weights, Eq. 6 and §3.2;
+ * gradients at the chunk-start weights, §1 and §3; the token-wise state
+ * recurrence whose chunk-end values the closed form reproduces, §3.2 and
+ * App. A.5).  One call processes ONE token of every (b, h) unit:
+ *   out = f_{W0}(q);  G = -grad_W 0.5 ||f_W(k) - v||^2 at W = W0;
+ *   M <- beta M + eta G;  W <- gamma W + M   (gamma by decay_mode);
+ *   and, when chunk_end != 0, W0 <- W (the next chunk starts from it).
+ * Calling it for the tokens of a sequence in order, with chunk_end set on
+ * every C-th token and on the last, gives the outputs and end states of
+ * e2ttt_chunk_forward on that sequence (up to rounding).
+ * Shapes: q, k, v, out [B,H,d] io_dtype (this token); eta, alpha, beta [B,H]
+ * fp32; W0, W, M [B,H,P] fp32, updated in place (W0 only at a chunk end).
+ * Only batch, heads, dim, hidden, kind, io_dtype and decay_mode of `prob` are
+ * used (the rest must still validate); E2TTT_FLAG_CHUNK_AVERAGED_DECAY gives
+ * EUNSUPPORTED (chunk means need the whole chunk), the compensated-weights
+ * flag is ignored (the state is used in fp32).  W0, W, M, out and the
+ * workspace must not overlap one another or the inputs (EINVAL).  All
+ * tensor pointers 16-byte aligned, the workspace 256-byte aligned with at
+ * least e2ttt_decode_workspace_bytes() bytes (EWORKSPACE).  Asynchronous on
+ * `stream`; nothing is launched when an argument check fails. */
+E2TTT_API e2ttt_status e2ttt_decode_workspace_bytes(const e2ttt_problem* prob, size_t* bytes);
+E2TTT_API e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* q,
+                                         const void* k, const void* v, const float* eta,
+                                         const float* alpha, const float* beta, float* W0,
+                                         float* W, float* M, void* out, int chunk_end,
+                                         void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -196,3 +196,16 @@ def test_timed_entry_host_errors():
     assert timed(-1, [], 0) == cwu.EINVAL
     assert timed(cwu.KERNEL_AGG, [None, None], 2) == cwu.EINVAL
     assert timed(cwu.KERNEL_AGG, [], -2) == cwu.EINVAL
+
+
+def test_decode_host_checks():
+    """Host-side checks of the decode entry points (no device call)."""
+    base = swiglu()
+    n = cwu.decode_workspace_bytes(base)
+    B, H, d, h = base.batch, base.heads, base.dim, base.hidden
+    assert n >= 4 * B * H * (6 * h + d) and n % 256 == 0
+    with pytest.raises(cwu.E2tttError):
+        cwu.decode_workspace_bytes(swiglu(flags=cwu.FLAG_CHUNK_AVERAGED_DECAY))
+    # null tensors are rejected before anything touches a device
+    st = cwu.lib().e2ttt_decode_step(ctypes.byref(base), *([None] * 10), 0, None, 0, None)
+    assert st == cwu.EINVAL

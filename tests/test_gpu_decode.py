@@ -1,0 +1,58 @@
+"""Decode step (one token of the recurrence per call) against the oracle.
+
+Running e2ttt_decode_step over every token of a sequence, with chunk_end on
+every C-th token and on the last, must give the chunk forward's outputs and
+end states: the oracle's literal recurrence (readout and gradients at the
+chunk-start weights, token-wise momentum/decay update) is the reference."""
+import numpy as np
+import pytest
+
+from chunk_weight_update_amd.inputs import BF16, F32, LINEAR, SWIGLU, make_inputs
+from gpu_util import log, problem_for, rel_fro, run_oracle, to_device
+
+pytestmark = pytest.mark.gpu
+
+TOL = {F32: (1e-5, 1e-5, 1e-5), BF16: (1e-2, 1e-5, 1e-5)}
+
+
+def run_decode(prob, t, L, C):
+    import torch
+    import chunk_weight_update_amd as cwu
+    B, H, _, d = t["q"].shape
+    W0 = t["W0"].clone()
+    W = t["W0"].clone()
+    M = t["M0"].clone()
+    outs = torch.empty_like(t["q"])
+    out_t = torch.empty_like(t["q"][:, :, 0])
+    ws = torch.empty(cwu.decode_workspace_bytes(prob), dtype=torch.uint8, device="cuda")
+    for s in range(L):
+        col = lambda x: x[:, :, s].clone()  # fresh, aligned (a [1,1] slice is a view)
+        cwu.decode_step(prob, col(t["q"]), col(t["k"]), col(t["v"]), col(t["eta"]),
+                        col(t["alpha"]), col(t["beta"]), W0, W, M, out_t,
+                        (s + 1) % C == 0 or s == L - 1, ws)
+        outs[:, :, s] = out_t
+    torch.cuda.synchronize()
+    return (outs.float().cpu().numpy().astype(np.float64), W.cpu().numpy().astype(np.float64),
+            M.cpu().numpy().astype(np.float64), W0.cpu().numpy().astype(np.float64))
+
+
+@pytest.mark.parametrize("kind,B,H,L,d,h,C,io,regime", [
+    (LINEAR, 1, 2, 40, 64, 0, 16, F32, "default"),          # ragged last chunk
+    (LINEAR, 2, 1, 33, 32, 0, 8, BF16, "default"),
+    (SWIGLU, 1, 2, 48, 128, 256, 16, F32, "nearunit"),
+    (SWIGLU, 2, 2, 40, 128, 256, 16, BF16, "nearunit"),     # ragged
+    (SWIGLU, 1, 1, 24, 256, 512, 8, BF16, "default"),
+])
+def test_decode_matches_oracle(kind, B, H, L, d, h, C, io, regime):
+    log(f"decode kind={kind} B={B} H={H} L={L} d={d} h={h} C={C} io={io} {regime}")
+    inp = make_inputs(kind, B, H, L, d, h, io, seed=9, regime=regime,
+                      m0_scale=1e-6 if regime == "nearunit" else 0.01)
+    prob = problem_for(kind, B, H, L, d, h, C, io)
+    out, W, M, W0 = run_decode(prob, to_device(inp, io), L, C)
+    ro, rW, rM = run_oracle(kind, inp, C, h)
+    e = (rel_fro(out, ro), rel_fro(W, rW), rel_fro(M, rM))
+    log(f"  rel_fro out={e[0]:.3e} W={e[1]:.3e} M={e[2]:.3e}")
+    t = TOL[io]
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(W)) and np.all(np.isfinite(M))
+    assert e[0] <= t[0] and e[1] <= t[1] and e[2] <= t[2], e
+    assert np.array_equal(W0, W)  # the last token closed the chunk: W0 <- W

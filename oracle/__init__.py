@@ -65,7 +65,7 @@ def _load():
             P = ctypes.POINTER(ctypes.c_double)
             i64 = ctypes.c_int64
             lib.oracle_chunk_forward.argtypes = (
-                [ctypes.c_int, ctypes.c_int] + [i64] * 6 + [P] * 11 + [ctypes.c_int])
+                [ctypes.c_int, ctypes.c_int] + [i64] * 6 + [P] * 11 + [ctypes.c_int] * 2)
             lib.oracle_chunk_forward.restype = ctypes.c_int
             lib.oracle_token_descent.argtypes = [ctypes.c_int, i64, i64, P, P, P, P]
             lib.oracle_token_descent.restype = ctypes.c_int
@@ -100,11 +100,12 @@ def set_threads(n: int) -> None:
 
 
 def chunk_forward(kind, q, k, v, eta, alpha, beta, W0, M0, chunk, hidden=0,
-                  decay_mode=GAMMA_1_MINUS_ETA_ALPHA, averaged=False):
+                  decay_mode=GAMMA_1_MINUS_ETA_ALPHA, averaged=False, qk_norm=False):
     """Run the literal recurrence.  q,k,v: [B,H,L,d]; eta/alpha/beta: [B,H,L];
     W0, M0: [B,H,P].  averaged: the chunk-averaged variant (beta, gamma
-    replaced by their means over each chunk).  Returns (out [B,H,L,d], Wend,
-    Mend), all float64."""
+    replaced by their means over each chunk).  qk_norm: the q/k prologue (SiLU,
+    then L2 normalisation per token) before use.  Returns (out [B,H,L,d],
+    Wend, Mend), all float64."""
     lib = _load()
     q, k, v = _f64(q), _f64(k), _f64(v)
     eta, alpha, beta = _f64(eta), _f64(alpha), _f64(beta)
@@ -120,7 +121,8 @@ def chunk_forward(kind, q, k, v, eta, alpha, beta, W0, M0, chunk, hidden=0,
     rc = lib.oracle_chunk_forward(kind, decay_mode, B, H, L, d, hidden, chunk,
                                   _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
                                   _ptr(alpha), _ptr(beta), _ptr(W0), _ptr(M0),
-                                  _ptr(out), _ptr(Wend), _ptr(Mend), int(bool(averaged)))
+                                  _ptr(out), _ptr(Wend), _ptr(Mend), int(bool(averaged)),
+                                  int(bool(qk_norm)))
     if rc != 0:
         raise RuntimeError(f"oracle_chunk_forward failed with code {rc}")
     return out, Wend, Mend

@@ -31,6 +31,10 @@
  *   - Inner learners: linear f_W(x) = W x (§2) and the three-matrix SwiGLU
  *     f(x) = W2 (silu(W1 x) * (W3 x)) (§5.2, App. B.5 "three-matrix
  *     fast-weight network").
+ *   - Option (qk_norm != 0): the TTT branch's input prologue of §4 ("Overall
+ *     Architecture"): SiLU applied to q_t and k_t, then L2 normalisation of
+ *     each token's vector, before anything else uses them.  The pages give no
+ *     epsilon; this divides by max(||x||, 1e-12).
  *   - Variant (averaged != 0): the chunk-averaged ablation of §4.3 (Table 5)
  *     and App. B.3 (Table 8), where the per-token momentum and decay factors
  *     beta_t, gamma_t of a chunk are collapsed to chunk-level scalars.  The
@@ -58,6 +62,21 @@ enum { OR_LINEAR = 0, OR_SWIGLU = 1 };
 enum { OR_GAMMA_1_MINUS_ETA_ALPHA = 0, OR_ALPHA_IS_GAMMA = 1 };
 
 static double sigm(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/* x <- silu(x) / max(||silu(x)||_2, 1e-12) for L rows of d (the q/k prologue). */
+static void silu_l2_rows(double* x, int64_t L, int64_t d) {
+  for (int64_t t = 0; t < L; ++t) {
+    double* r = x + t * d;
+    double ss = 0.0;
+    for (int64_t i = 0; i < d; ++i) {
+      r[i] = r[i] * sigm(r[i]);
+      ss += r[i] * r[i];
+    }
+    double nrm = sqrt(ss);
+    if (nrm < 1e-12) nrm = 1e-12;
+    for (int64_t i = 0; i < d; ++i) r[i] = r[i] / nrm;
+  }
+}
 
 /* gamma_t from the per-token scalars (Eq. 14, or alpha taken as gamma). */
 static double decay_factor(int decay_mode, double eta, double alpha) {
@@ -174,7 +193,8 @@ int oracle_fast_forward(int kind, int64_t d, int64_t h, const double* W,
  *   W0, M0, Wend, Mend : [B, H, P]
  * Chunks are consecutive runs of C tokens; a final run shorter than C (when
  * C does not divide L) is a chunk of its own.  L == 0 copies the state.
- * averaged != 0 selects the chunk-averaged variant (see the header).
+ * averaged != 0 selects the chunk-averaged variant, qk_norm != 0 the q/k
+ * prologue (see the header).
  * Returns 0 on success, nonzero on bad arguments or allocation failure.
  */
 int oracle_chunk_forward(int kind, int decay_mode, int64_t B, int64_t H,
@@ -183,7 +203,7 @@ int oracle_chunk_forward(int kind, int decay_mode, int64_t B, int64_t H,
                          const double* eta, const double* alpha,
                          const double* beta, const double* W0,
                          const double* M0, double* out, double* Wend,
-                         double* Mend, int averaged) {
+                         double* Mend, int averaged, int qk_norm) {
   if (kind != OR_LINEAR && kind != OR_SWIGLU) return 1;
   if (decay_mode != OR_GAMMA_1_MINUS_ETA_ALPHA &&
       decay_mode != OR_ALPHA_IS_GAMMA)
@@ -202,6 +222,22 @@ int oracle_chunk_forward(int kind, int decay_mode, int64_t B, int64_t H,
     memmove(M, M0 + u * P, sizeof(double) * (size_t)P);
     const double* qu = q + u * L * d;
     const double* ku = k + u * L * d;
+    double* qn = NULL;
+    double* kn = NULL;
+    if (qk_norm && L > 0) {
+      qn = (double*)malloc(sizeof(double) * (size_t)(L * d));
+      kn = (double*)malloc(sizeof(double) * (size_t)(L * d));
+      if (!qn || !kn) {
+        free(qn); free(kn);
+        return 2;
+      }
+      memcpy(qn, qu, sizeof(double) * (size_t)(L * d));
+      memcpy(kn, ku, sizeof(double) * (size_t)(L * d));
+      silu_l2_rows(qn, L, d);
+      silu_l2_rows(kn, L, d);
+      qu = qn;
+      ku = kn;
+    }
     const double* vu = v + u * L * d;
     const double* etu = eta + u * L;
     const double* alu = alpha + u * L;
@@ -312,6 +348,7 @@ int oracle_chunk_forward(int kind, int decay_mode, int64_t B, int64_t H,
       }
     }
     free(Ws); free(fe); free(fu1); free(fu3); free(fz); free(gam); free(bet);
+    free(qn); free(kn);
     if (status) return status;
   }
   return 0;

@@ -373,3 +373,26 @@ def test_chunk_averaged_kernels_are_geometric_in_the_means():
         assert abs(coef[sg, 1] - b ** n) <= 1e-13 * b ** n
         P0 = (g ** n - b ** n) / (g - b)
         assert abs(coef[sg, 2] - b * P0) <= 1e-12 * b * P0
+
+
+# --- q/k prologue (§4 "Overall Architecture" of the E2-TTT page: SiLU on the
+# queries and keys, then L2 normalisation per token).
+
+@pytest.mark.parametrize("kind,d,h", [(oracle.LINEAR, 5, 0), (oracle.SWIGLU, 4, 6)])
+def test_qk_prologue_is_silu_then_l2_normalisation(kind, d, h):
+    """The option equals the plain run on inputs prepared by the library
+    routines torch.nn.functional.silu and .normalize (eps 1e-12)."""
+    rng = np.random.default_rng(21)
+    L, C = 11, 4
+    q, k, v, eta, alpha, beta, W0, M0 = _rand_problem(rng, kind, L, d, h)
+    q = 3.0 * rng.standard_normal(q.shape)  # raw projections, not normalised
+    k = 3.0 * rng.standard_normal(k.shape)
+    q[0, 0, 2] = 0.0                        # a zero row stays zero
+    out, Wend, Mend = oracle.chunk_forward(kind, q, k, v, eta, alpha, beta, W0, M0, C, h,
+                                           qk_norm=True)
+    F = torch.nn.functional
+    prep = lambda x: F.normalize(F.silu(torch.from_numpy(x)), dim=-1, eps=1e-12).numpy()
+    out2, W2, M2 = oracle.chunk_forward(kind, prep(q), prep(k), v, eta, alpha, beta, W0, M0,
+                                        C, h)
+    assert _rel(out, out2) <= 1e-13 and _rel(Wend, W2) <= 1e-13 and _rel(Mend, M2) <= 1e-13
+    assert np.all(out[0, 0, 2] == 0.0)

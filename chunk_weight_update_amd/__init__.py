@@ -25,6 +25,7 @@ F32, BF16 = 0, 1
 GAMMA_1_MINUS_ETA_ALPHA, ALPHA_IS_GAMMA = 0, 1
 FLAG_COMPENSATED_WEIGHTS = 1
 FLAG_CHUNK_AVERAGED_DECAY = 2
+FLAG_QK_SILU_L2 = 4
 
 
 class Problem(ctypes.Structure):

@@ -42,6 +42,7 @@ struct Plan {
   int64_t B, H, BH, L, d, h, C, Cp, nC, P;
   int kind, io, mode, krep;
   int averaged = 0;  // chunk-averaged beta, gamma (E2TTT_FLAG_CHUNK_AVERAGED_DECAY)
+  int qknorm = 0;    // SiLU + L2 prologue on q, k (E2TTT_FLAG_QK_SILU_L2)
   bool fused;   // two-kernel chunk step (SwiGLU, d = 128, bf16 io)
   int rbA;      // phase A rows per workgroup (32 or 64; LDS-streamed variant)
   int wpuA;     // register-resident phase A: workgroups per unit (0: not used)
@@ -51,7 +52,7 @@ struct Plan {
   size_t opsz;  // bytes per GEMM operand element (2 for bf16, 4 for fp32)
   // workspace offsets (bytes)
   size_t kw, km, coef, kt, w13s, w2s, w2ts, zrow, a1s, a3s, grow, ut, gt, zt, gw, gm, gbf, gft,
-      part, part256, total;
+      part, part256, qn, kn, total;
 };
 
 e2ttt_status check_problem(const e2ttt_problem* p) {
@@ -61,7 +62,8 @@ e2ttt_status check_problem(const e2ttt_problem* p) {
   if (p->decay_mode != E2TTT_GAMMA_1_MINUS_ETA_ALPHA && p->decay_mode != E2TTT_ALPHA_IS_GAMMA)
     return E2TTT_EINVAL;
   if ((p->flags & ~static_cast<uint32_t>(E2TTT_FLAG_COMPENSATED_WEIGHTS |
-                                         E2TTT_FLAG_CHUNK_AVERAGED_DECAY)) != 0u)
+                                         E2TTT_FLAG_CHUNK_AVERAGED_DECAY |
+                                         E2TTT_FLAG_QK_SILU_L2)) != 0u)
     return E2TTT_EINVAL;
   if (p->reserved != 0u) return E2TTT_EINVAL;
   if (p->batch < 1 || p->heads < 1 || p->seq_len < 0 || p->dim < 1 || p->chunk < 1)
@@ -98,6 +100,7 @@ e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
   q.d = p->dim; q.h = p->hidden; q.C = p->chunk;
   q.kind = p->kind; q.io = p->io_dtype; q.mode = p->decay_mode;
   q.averaged = (p->flags & E2TTT_FLAG_CHUNK_AVERAGED_DECAY) ? 1 : 0;
+  q.qknorm = (p->flags & E2TTT_FLAG_QK_SILU_L2) ? 1 : 0;
   q.nC = q.L > 0 ? (q.L + q.C - 1) / q.C : 0;
   q.P = q.kind == E2TTT_LINEAR ? q.d * q.d : 3 * q.d * q.h;
   const size_t f4 = 4;
@@ -187,6 +190,11 @@ e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
       q.nsplitAgg = S;
       q.part256 = take(f4 * static_cast<size_t>(S) * 2 * q.BH * q.P);
     }
+  }
+  if (q.qknorm) {  // normalised copies of q and k
+    const size_t nx = static_cast<size_t>(q.BH * q.L * q.d) * (q.io == E2TTT_BF16 ? 2 : 4);
+    q.qn = take(nx);
+    q.kn = take(nx);
   }
   q.total = q.L == 0 ? 0 : o;  // an empty sequence only copies the state
   return E2TTT_OK;
@@ -595,6 +603,27 @@ e2ttt_status forward_impl(const e2ttt_problem* prob, const void* q, const void* 
     }
   } else {
     char* ws = static_cast<char*>(workspace);
+    if (pl.qknorm) {  // q, k -> silu, L2-normalised copies in the workspace
+      const int64_t rows = pl.BH * pl.L;
+      const unsigned gq = grid1((rows + 3) / 4);
+      if (pl.io == E2TTT_BF16) {
+        E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, k_qk_norm<bf16_t>, dim3(gq), dim3(256), 0, st,
+                     static_cast<const bf16_t*>(q), reinterpret_cast<bf16_t*>(ws + pl.qn), rows,
+                     pl.d);
+        E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, k_qk_norm<bf16_t>, dim3(gq), dim3(256), 0, st,
+                     static_cast<const bf16_t*>(k), reinterpret_cast<bf16_t*>(ws + pl.kn), rows,
+                     pl.d);
+      } else {
+        E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, k_qk_norm<float>, dim3(gq), dim3(256), 0, st,
+                     static_cast<const float*>(q), reinterpret_cast<float*>(ws + pl.qn), rows,
+                     pl.d);
+        E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, k_qk_norm<float>, dim3(gq), dim3(256), 0, st,
+                     static_cast<const float*>(k), reinterpret_cast<float*>(ws + pl.kn), rows,
+                     pl.d);
+      }
+      q = ws + pl.qn;
+      k = ws + pl.kn;
+    }
     if (pl.kind == E2TTT_LINEAR) {
       if (pl.io == E2TTT_BF16)
         launch_linear<bf16_t>(pl, q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end, ws, st, I);
@@ -689,6 +718,15 @@ size_t decode_ws_bytes(int64_t BH, int64_t d, int64_t h) {
   return align256(4 * static_cast<size_t>(BH) * static_cast<size_t>(6 * h + d + (d / 64) * h));
 }
 
+// With the q/k prologue: the normalised q and k of the token follow, io
+// dtype, each 256-byte aligned.
+size_t decode_ws_total(const e2ttt_problem* p, int64_t BH, int64_t d, int64_t h) {
+  size_t n = decode_ws_bytes(BH, d, h);
+  if (p->flags & E2TTT_FLAG_QK_SILU_L2)
+    n += 2 * align256(static_cast<size_t>(BH * d) * (p->io_dtype == E2TTT_BF16 ? 2 : 4));
+  return n;
+}
+
 }  // namespace
 
 extern "C" {
@@ -699,7 +737,7 @@ e2ttt_status e2ttt_decode_workspace_bytes(const e2ttt_problem* prob, size_t* byt
   if (st != E2TTT_OK) return st;
   if (prob->flags & E2TTT_FLAG_CHUNK_AVERAGED_DECAY) return E2TTT_EUNSUPPORTED;
   const int64_t h = prob->kind == E2TTT_LINEAR ? 0 : prob->hidden;
-  *bytes = decode_ws_bytes(prob->batch * prob->heads, prob->dim, h);
+  *bytes = decode_ws_total(prob, prob->batch * prob->heads, prob->dim, h);
   return E2TTT_OK;
 }
 
@@ -714,7 +752,7 @@ e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* q, const v
   const int64_t BH = prob->batch * prob->heads, d = prob->dim;
   const int64_t h = prob->kind == E2TTT_LINEAR ? 0 : prob->hidden;
   const int64_t P = h == 0 ? d * d : 3 * d * h;
-  const size_t need = decode_ws_bytes(BH, d, h);
+  const size_t need = decode_ws_total(prob, BH, d, h);
   if (!q || !k || !v || !eta || !alpha || !beta || !W0 || !W || !M || !out || !workspace)
     return E2TTT_EINVAL;
   const void* p16[] = {q, k, v, eta, alpha, beta, W0, W, M, out};
@@ -750,6 +788,15 @@ e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* q, const v
     typedef decltype(tag) T;
     const T* Q = static_cast<const T*>(q);
     const T* K = static_cast<const T*>(k);
+    if (prob->flags & E2TTT_FLAG_QK_SILU_L2) {
+      char* xb = static_cast<char*>(workspace) + decode_ws_bytes(BH, d, h);
+      T* qn = reinterpret_cast<T*>(xb);
+      T* kn = reinterpret_cast<T*>(xb + align256(static_cast<size_t>(BH * d) * sizeof(T)));
+      hipLaunchKernelGGL(k_qk_norm<T>, dim3(grid1((BH + 3) / 4)), dim3(256), 0, s, Q, qn, BH, d);
+      hipLaunchKernelGGL(k_qk_norm<T>, dim3(grid1((BH + 3) / 4)), dim3(256), 0, s, K, kn, BH, d);
+      Q = qn;
+      K = kn;
+    }
     const T* V = static_cast<const T*>(v);
     T* O = static_cast<T*>(out);
     if (h == 0) {

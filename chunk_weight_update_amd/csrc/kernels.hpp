@@ -300,6 +300,37 @@ __host__ __device__ constexpr int tok_perm32(int p) {
   return (p & ~31) + 8 * ((p & 15) >> 2) + 4 * ((p & 31) >> 4) + (p & 3);
 }
 
+// The q/k prologue of the TTT branch (§4 Overall Architecture): each row of
+// d values becomes silu(x) / max(||silu(x)||_2, 1e-12), in fp32, rounded to
+// T.  One wave per row (lane l takes elements l + 64 m, d <= 1024), sum of
+// squares by a fixed shuffle tree.  Grid ceil(rows / 4).
+template <typename T>
+__global__ __launch_bounds__(256) void k_qk_norm(const T* __restrict__ x, T* __restrict__ y,
+                                                 int64_t rows, int64_t d) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const T* xr = x + row * d;
+  T* yr = y + row * d;
+  float s[16];
+  float ss = 0.0f;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const int64_t e = lane + 64 * m;
+    const float v = e < d ? to_f32<T>(xr[e]) : 0.0f;
+    s[m] = v * sigmoidf_(v);
+    ss = fmaf(s[m], s[m], ss);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const int64_t e = lane + 64 * m;
+    if (e < d) yr[e] = from_f32<T>(s[m] * inv);
+  }
+}
+
 template <typename T, bool PERM>
 __device__ __forceinline__ void prep_kt_block(const Shape& s, int64_t bid,
                                               const T* __restrict__ k, T* __restrict__ kt) {

@@ -74,7 +74,8 @@ def test_status_strings():
     (swiglu(io_dtype=5), cwu.EINVAL),
     (swiglu(decay_mode=3), cwu.EINVAL),
     (swiglu(flags=cwu.FLAG_CHUNK_AVERAGED_DECAY), cwu.OK),
-    (swiglu(flags=4), cwu.EINVAL),
+    (swiglu(flags=cwu.FLAG_QK_SILU_L2), cwu.OK),
+    (swiglu(flags=8), cwu.EINVAL),
     (linear(hidden=3), cwu.EINVAL),
     (swiglu(dim=96), cwu.EUNSUPPORTED),
     (swiglu(hidden=200), cwu.EUNSUPPORTED),

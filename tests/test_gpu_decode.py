@@ -56,3 +56,22 @@ def test_decode_matches_oracle(kind, B, H, L, d, h, C, io, regime):
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(W)) and np.all(np.isfinite(M))
     assert e[0] <= t[0] and e[1] <= t[1] and e[2] <= t[2], e
     assert np.array_equal(W0, W)  # the last token closed the chunk: W0 <- W
+
+
+def test_decode_with_qk_prologue():
+    """Raw q, k with the SiLU + L2 prologue flag, token by token."""
+    import chunk_weight_update_amd as cwu
+    from test_gpu_parity import raw_projections
+    kind, B, H, L, d, h, C, io = SWIGLU, 1, 2, 24, 128, 256, 8, BF16
+    log("decode with the q/k prologue")
+    inp = raw_projections(make_inputs(kind, B, H, L, d, h, io, seed=13, regime="nearunit",
+                                      m0_scale=1e-6), io, 13)
+    prob = problem_for(kind, B, H, L, d, h, C, io, 0, cwu.FLAG_QK_SILU_L2)
+    out, W, M, _ = run_decode(prob, to_device(inp, io), L, C)
+    import oracle
+    ro, rW, rM = oracle.chunk_forward(kind, inp["q64"], inp["k64"], inp["v64"], inp["eta"],
+                                      inp["alpha"], inp["beta"], inp["W0"], inp["M0"], C, h,
+                                      qk_norm=True)
+    e = (rel_fro(out, ro), rel_fro(W, rW), rel_fro(M, rM))
+    log(f"  rel_fro out={e[0]:.3e} W={e[1]:.3e} M={e[2]:.3e}")
+    assert e[0] <= 1e-2 and e[1] <= 5e-3 and e[2] <= 5e-3, e

@@ -17,14 +17,35 @@ pytestmark = pytest.mark.gpu
 TOL = {F32: (1e-5, 1e-5, 1e-5), BF16: (1e-2, 5e-3, 5e-3)}
 
 
+def raw_projections(inp, io, seed):
+    """Replace q, k by raw projection-like vectors (2 * N(0,1), not
+    normalised), rounded to the io dtype exactly as the workload inputs are."""
+    import torch
+    rng = np.random.default_rng(1000 + seed)
+    out = dict(inp)
+    for n in ("q", "k"):
+        x = (2.0 * rng.standard_normal(inp[n + "64"].shape)).astype(np.float32)
+        if io == BF16:  # the io representation is the bf16 bit pattern
+            xb = torch.from_numpy(x).to(torch.bfloat16)
+            out[n] = xb.view(torch.int16).numpy().view(np.uint16)
+            out[n + "64"] = xb.to(torch.float32).numpy().astype(np.float64)
+        else:
+            out[n] = x
+            out[n + "64"] = x.astype(np.float64)
+    return out
+
+
 def check(kind, B, H, L, d, h, C, io, seed=0, regime="default", m0_scale=0.0, decay_mode=0,
-          flags=0, tol=None):
+          flags=0, tol=None, raw_qk=False):
     log(f"case kind={kind} B={B} H={H} L={L} d={d} h={h} C={C} io={io} seed={seed} "
-        f"regime={regime} m0={m0_scale} mode={decay_mode} flags={flags}")
+        f"regime={regime} m0={m0_scale} mode={decay_mode} flags={flags} raw_qk={raw_qk}")
     inp = make_inputs(kind, B, H, L, d, h, io, seed=seed, regime=regime, m0_scale=m0_scale)
+    if raw_qk:
+        inp = raw_projections(inp, io, seed)
     prob = problem_for(kind, B, H, L, d, h, C, io, decay_mode, flags)
     out, W, M = run_gpu(prob, to_device(inp, io))
-    ro, rW, rM = run_oracle(kind, inp, C, h, decay_mode, averaged=bool(flags & 2))
+    ro, rW, rM = run_oracle(kind, inp, C, h, decay_mode, averaged=bool(flags & 2),
+                            qk_norm=bool(flags & 4))
     e = (rel_fro(out, ro), rel_fro(W, rW), rel_fro(M, rM))
     log(f"  rel_fro out={e[0]:.3e} W={e[1]:.3e} M={e[2]:.3e}")
     t = tol or TOL[io]
@@ -150,6 +171,20 @@ def test_chunk_averaged_forward(kind, B, H, L, d, h, C, io, regime):
     import chunk_weight_update_amd as cwu
     check(kind, B, H, L, d, h, C, io, seed=8, regime=regime,
           m0_scale=M0.get(regime, 0.0), flags=cwu.FLAG_CHUNK_AVERAGED_DECAY)
+
+
+@pytest.mark.parametrize("kind,B,H,L,d,h,C,io,regime", [
+    (LINEAR, 1, 2, 600, 64, 0, 128, F32, "default"),
+    (SWIGLU, 1, 2, 600, 128, 256, 256, F32, "nearunit"),
+    (SWIGLU, 2, 2, 512, 128, 256, 256, BF16, "nearunit"),     # fused path
+    (SWIGLU, 1, 1, 512, 256, 512, 256, BF16, "nearunit"),     # 256-tile generic path
+])
+def test_qk_prologue_forward(kind, B, H, L, d, h, C, io, regime):
+    """q, k passed raw (scaled N(0,1), not normalised); the library applies
+    SiLU and L2 normalisation per token, as the oracle does."""
+    import chunk_weight_update_amd as cwu
+    check(kind, B, H, L, d, h, C, io, seed=12, regime=regime, raw_qk=True,
+          m0_scale=M0.get(regime, 0.0), flags=cwu.FLAG_QK_SILU_L2)
 
 
 # --- linear learner ---------------------------------------------------------

@@ -433,3 +433,198 @@ int oracle_scalar_kernels(int decay_mode, int64_t nseg, int64_t n,
   }
   return status;
 }
+
+/*
+ * Reverse mode of the chunk forward for the linear learner (the outer-loop
+ * backward): the gradient of a scalar loss
+ *     l = <dout, out> + <dWend, Wend> + <dMend, Mend>
+ * with respect to every input of oracle_chunk_forward.  It differentiates the
+ * same literal recurrence, one token at a time in reverse:
+ *   - the chunk-start states (W, M) of every chunk are recorded by a forward
+ *     pass; each chunk is re-run to record the state before each token;
+ *   - token t of a chunk with frozen weights Ws did
+ *         e = v_t - Ws k_t,  G = e k_t^T,
+ *         M <- beta_t M + eta_t G,  W <- gamma_t W + M,
+ *     so with (dW, dM) the adjoint of the state after the token:
+ *         dMt    = dM + dW                      (W used the new M)
+ *         dgamma = <dW, W_before>,  dbeta = <dMt, M_before>
+ *         deta  += <dMt, G>,        dG = eta_t dMt
+ *         de = dG k_t,  dk_t += dG^T e - Ws^T de,  dv_t += de,
+ *         dWs   -= de k_t^T
+ *         dW <- gamma_t dW,  dM <- beta_t dMt;
+ *   - the readout o_t = Ws q_t adds dq_t = Ws^T do_t and dWs += do_t q_t^T;
+ *   - Ws is the state at the chunk start, so dW += dWs before the previous
+ *     chunk is processed;
+ *   - gamma_t = 1 - eta_t alpha_t (Eq. 14): deta_t -= alpha_t dgamma,
+ *     dalpha_t = -eta_t dgamma; with alpha taken as gamma, dalpha_t = dgamma.
+ * The chunk-averaged variant and the q/k prologue are not covered.
+ * dWend or dMend may be NULL (zero).  Returns 0 on success, 1 on bad
+ * arguments, 2 on allocation failure, 3 for a learner other than linear.
+ */
+int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
+                          int64_t L, int64_t d, int64_t C,
+                          const double* q, const double* k, const double* v,
+                          const double* eta, const double* alpha,
+                          const double* beta, const double* W0,
+                          const double* M0, const double* dout,
+                          const double* dWend, const double* dMend,
+                          double* dq, double* dk, double* dv, double* deta,
+                          double* dalpha, double* dbeta, double* dW0,
+                          double* dM0) {
+  if (kind != OR_LINEAR) return 3;
+  if (decay_mode != OR_GAMMA_1_MINUS_ETA_ALPHA &&
+      decay_mode != OR_ALPHA_IS_GAMMA)
+    return 1;
+  if (B < 0 || H < 0 || L < 0 || d <= 0 || C <= 0) return 1;
+  const int64_t P = d * d;
+  const int64_t nC = (L + C - 1) / C;
+  const int64_t Cmax = C < L ? C : (L > 0 ? L : 1);
+
+  for (int64_t u = 0; u < B * H; ++u) {
+    const double* qu = q + u * L * d;
+    const double* ku = k + u * L * d;
+    const double* vu = v + u * L * d;
+    const double* etu = eta + u * L;
+    const double* alu = alpha + u * L;
+    const double* beu = beta + u * L;
+    const double* dou = dout + u * L * d;
+    double* dqu = dq + u * L * d;
+    double* dku = dk + u * L * d;
+    double* dvu = dv + u * L * d;
+    double* detu = deta + u * L;
+    double* dalu = dalpha + u * L;
+    double* dbeu = dbeta + u * L;
+    for (int64_t i = 0; i < L * d; ++i) dqu[i] = dku[i] = dvu[i] = 0.0;
+    for (int64_t t = 0; t < L; ++t) detu[t] = dalu[t] = dbeu[t] = 0.0;
+
+    double* Wst = (double*)malloc(sizeof(double) * (size_t)((nC > 0 ? nC : 1) * P));
+    double* Mst = (double*)malloc(sizeof(double) * (size_t)((nC > 0 ? nC : 1) * P));
+    double* Wb = (double*)malloc(sizeof(double) * (size_t)(Cmax * P));
+    double* Mb = (double*)malloc(sizeof(double) * (size_t)(Cmax * P));
+    double* e = (double*)malloc(sizeof(double) * (size_t)(Cmax * d));
+    double* W = (double*)malloc(sizeof(double) * (size_t)P);
+    double* M = (double*)malloc(sizeof(double) * (size_t)P);
+    double* dW = (double*)malloc(sizeof(double) * (size_t)P);
+    double* dM = (double*)malloc(sizeof(double) * (size_t)P);
+    double* dMt = (double*)malloc(sizeof(double) * (size_t)P);
+    double* dWs = (double*)malloc(sizeof(double) * (size_t)P);
+    double* de = (double*)malloc(sizeof(double) * (size_t)d);
+    if (!Wst || !Mst || !Wb || !Mb || !e || !W || !M || !dW || !dM || !dMt || !dWs || !de) {
+      free(Wst); free(Mst); free(Wb); free(Mb); free(e); free(W); free(M);
+      free(dW); free(dM); free(dMt); free(dWs); free(de);
+      return 2;
+    }
+
+    /* Forward: chunk-start states. */
+    memcpy(W, W0 + u * P, sizeof(double) * (size_t)P);
+    memcpy(M, M0 + u * P, sizeof(double) * (size_t)P);
+    for (int64_t r = 0; r < nC; ++r) {
+      const int64_t t0 = r * C, n = (L - t0) < C ? (L - t0) : C;
+      memcpy(Wst + r * P, W, sizeof(double) * (size_t)P);
+      memcpy(Mst + r * P, M, sizeof(double) * (size_t)P);
+      const double* Ws = Wst + r * P;
+      for (int64_t t = 0; t < n; ++t) {
+        const int64_t tt = t0 + t;
+        const double g = decay_factor(decay_mode, etu[tt], alu[tt]);
+        for (int64_t i = 0; i < d; ++i) {
+          double y = 0.0;
+          for (int64_t j = 0; j < d; ++j) y += Ws[i * d + j] * ku[tt * d + j];
+          const double ei = vu[tt * d + i] - y;
+          for (int64_t j = 0; j < d; ++j) {
+            M[i * d + j] = beu[tt] * M[i * d + j] + etu[tt] * (ei * ku[tt * d + j]);
+            W[i * d + j] = g * W[i * d + j] + M[i * d + j];
+          }
+        }
+      }
+    }
+
+    /* Backward. */
+    for (int64_t i = 0; i < P; ++i) {
+      dW[i] = dWend ? dWend[u * P + i] : 0.0;
+      dM[i] = dMend ? dMend[u * P + i] : 0.0;
+    }
+    for (int64_t r = nC - 1; r >= 0; --r) {
+      const int64_t t0 = r * C, n = (L - t0) < C ? (L - t0) : C;
+      const double* Ws = Wst + r * P;
+      /* Re-run the chunk, recording the state before each token. */
+      memcpy(W, Ws, sizeof(double) * (size_t)P);
+      memcpy(M, Mst + r * P, sizeof(double) * (size_t)P);
+      for (int64_t t = 0; t < n; ++t) {
+        const int64_t tt = t0 + t;
+        const double g = decay_factor(decay_mode, etu[tt], alu[tt]);
+        memcpy(Wb + t * P, W, sizeof(double) * (size_t)P);
+        memcpy(Mb + t * P, M, sizeof(double) * (size_t)P);
+        for (int64_t i = 0; i < d; ++i) {
+          double y = 0.0;
+          for (int64_t j = 0; j < d; ++j) y += Ws[i * d + j] * ku[tt * d + j];
+          e[t * d + i] = vu[tt * d + i] - y;
+          for (int64_t j = 0; j < d; ++j) {
+            M[i * d + j] = beu[tt] * M[i * d + j] + etu[tt] * (e[t * d + i] * ku[tt * d + j]);
+            W[i * d + j] = g * W[i * d + j] + M[i * d + j];
+          }
+        }
+      }
+      for (int64_t i = 0; i < P; ++i) dWs[i] = 0.0;
+      for (int64_t t = n - 1; t >= 0; --t) {
+        const int64_t tt = t0 + t;
+        const double et = etu[tt];
+        const double g = decay_factor(decay_mode, et, alu[tt]);
+        const double* kt = ku + tt * d;
+        const double* ev = e + t * d;
+        double dgam = 0.0, dbet = 0.0, detd = 0.0;
+        for (int64_t i = 0; i < P; ++i) {
+          dMt[i] = dM[i] + dW[i];
+          dgam += dW[i] * Wb[t * P + i];
+          dbet += dMt[i] * Mb[t * P + i];
+        }
+        for (int64_t i = 0; i < d; ++i) {
+          double s = 0.0; /* (dMt k)_i */
+          for (int64_t j = 0; j < d; ++j) s += dMt[i * d + j] * kt[j];
+          detd += ev[i] * s;
+          de[i] = et * s;
+        }
+        for (int64_t j = 0; j < d; ++j) {
+          double s1 = 0.0, s2 = 0.0; /* (dMt^T e)_j and (Ws^T de)_j */
+          for (int64_t i = 0; i < d; ++i) {
+            s1 += dMt[i * d + j] * ev[i];
+            s2 += Ws[i * d + j] * de[i];
+          }
+          dku[tt * d + j] += et * s1 - s2;
+        }
+        for (int64_t i = 0; i < d; ++i) {
+          dvu[tt * d + i] += de[i];
+          for (int64_t j = 0; j < d; ++j) dWs[i * d + j] -= de[i] * kt[j];
+        }
+        for (int64_t i = 0; i < P; ++i) {
+          dW[i] = g * dW[i];
+          dM[i] = beu[tt] * dMt[i];
+        }
+        detu[tt] += detd;
+        dbeu[tt] += dbet;
+        if (decay_mode == OR_GAMMA_1_MINUS_ETA_ALPHA) {
+          detu[tt] -= alu[tt] * dgam;
+          dalu[tt] += -et * dgam;
+        } else {
+          dalu[tt] += dgam;
+        }
+      }
+      /* Readout o_t = Ws q_t. */
+      for (int64_t t = 0; t < n; ++t) {
+        const int64_t tt = t0 + t;
+        for (int64_t j = 0; j < d; ++j) {
+          double s = 0.0;
+          for (int64_t i = 0; i < d; ++i) s += Ws[i * d + j] * dou[tt * d + i];
+          dqu[tt * d + j] += s;
+        }
+        for (int64_t i = 0; i < d; ++i)
+          for (int64_t j = 0; j < d; ++j) dWs[i * d + j] += dou[tt * d + i] * qu[tt * d + j];
+      }
+      for (int64_t i = 0; i < P; ++i) dW[i] += dWs[i];
+    }
+    memcpy(dW0 + u * P, dW, sizeof(double) * (size_t)P);
+    memcpy(dM0 + u * P, dM, sizeof(double) * (size_t)P);
+    free(Wst); free(Mst); free(Wb); free(Mb); free(e); free(W); free(M);
+    free(dW); free(dM); free(dMt); free(dWs); free(de);
+  }
+  return 0;
+}

@@ -1,0 +1,140 @@
+"""Pins of the oracle's reverse mode (linear learner, CPU only).
+
+The outer-loop backward of the chunk forward is pinned to two things other
+than itself:
+  - central finite differences of the oracle's own forward (the literal
+    recurrence of App. A.5, itself pinned in test_oracle.py), one input class
+    at a time, so a wrong or missing term in any one gradient fails;
+  - torch autograd through an independent fp64 closed form of the chunk
+    update (the kernels of §3.2 / Appendix A: suffix products, the affine
+    reverse scan P_t = c_t + beta_{t+1} P_{t+1}, and the aggregation
+    E^T diag(K) K), written here in torch and differentiated by the library.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+NAMES = ("q", "k", "v", "eta", "alpha", "beta", "W0", "M0")
+
+
+def _problem(rng, B, H, L, d, mode):
+    q = rng.standard_normal((B, H, L, d))
+    k = rng.standard_normal((B, H, L, d)) / np.sqrt(d)
+    v = rng.standard_normal((B, H, L, d))
+    eta = 0.3 * rng.random((B, H, L)) + 0.05
+    alpha = rng.random((B, H, L)) if mode == oracle.GAMMA_1_MINUS_ETA_ALPHA else \
+        0.5 + 0.5 * rng.random((B, H, L))
+    beta = rng.random((B, H, L))
+    W0 = rng.standard_normal((B, H, d * d)) * 0.5
+    M0 = rng.standard_normal((B, H, d * d)) * 0.3
+    return dict(q=q, k=k, v=v, eta=eta, alpha=alpha, beta=beta, W0=W0, M0=M0)
+
+
+def _loss(x, C, mode, dout, dWe, dMe):
+    o, We, Me = oracle.chunk_forward(oracle.LINEAR, x["q"], x["k"], x["v"], x["eta"],
+                                     x["alpha"], x["beta"], x["W0"], x["M0"], C,
+                                     decay_mode=mode)
+    return float((dout * o).sum() + (dWe * We).sum() + (dMe * Me).sum())
+
+
+@pytest.mark.parametrize("mode", [oracle.GAMMA_1_MINUS_ETA_ALPHA, oracle.ALPHA_IS_GAMMA])
+@pytest.mark.parametrize("L,C", [(7, 3), (6, 6), (5, 1)])
+def test_backward_matches_finite_differences(mode, L, C):
+    rng = np.random.default_rng(100 + L + 10 * C + mode)
+    B, H, d = 1, 2, 3
+    x = _problem(rng, B, H, L, d, mode)
+    dout = rng.standard_normal((B, H, L, d))
+    dWe = rng.standard_normal((B, H, d * d))
+    dMe = rng.standard_normal((B, H, d * d))
+    g = oracle.chunk_backward(oracle.LINEAR, *[x[n] for n in NAMES], dout, dWe, dMe, C,
+                              decay_mode=mode)
+    h = 1e-6
+    for name in NAMES:
+        dl = rng.standard_normal(x[name].shape)
+        xp = dict(x); xp[name] = x[name] + h * dl
+        xm = dict(x); xm[name] = x[name] - h * dl
+        fd = (_loss(xp, C, mode, dout, dWe, dMe) - _loss(xm, C, mode, dout, dWe, dMe)) / (2 * h)
+        an = float((g[name] * dl).sum())
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (name, fd, an)
+
+
+def _closed_form_torch(x, C, mode):
+    """Chunk forward of the linear learner by the closed form, in torch fp64."""
+    q, k, v = x["q"], x["k"], x["v"]
+    eta, alpha, beta = x["eta"], x["alpha"], x["beta"]
+    B, H, L, d = q.shape
+    W = x["W0"].reshape(B, H, d, d)
+    M = x["M0"].reshape(B, H, d, d)
+    gam = 1.0 - eta * alpha if mode == oracle.GAMMA_1_MINUS_ETA_ALPHA else alpha
+    outs = []
+    for t0 in range(0, L, C):
+        n = min(C, L - t0)
+        sl = slice(t0, t0 + n)
+        Q, K, V = q[:, :, sl], k[:, :, sl], v[:, :, sl]
+        be, ga, et = beta[:, :, sl], gam[:, :, sl], eta[:, :, sl]
+        # exclusive suffix products b_t = prod_{s>t} beta_s, c_t likewise
+        ones = torch.ones_like(be[..., :1])
+        b_all = torch.flip(torch.cumprod(torch.flip(torch.cat([be[..., 1:], ones], -1), [-1]), -1), [-1])
+        c_all = torch.flip(torch.cumprod(torch.flip(torch.cat([ga[..., 1:], ones], -1), [-1]), -1), [-1])
+        # P_t = c_t + beta_{t+1} P_{t+1}, P of the last token = 1
+        Ps = [None] * n
+        Ps[n - 1] = c_all[..., n - 1]
+        for t in range(n - 2, -1, -1):
+            Ps[t] = c_all[..., t] + be[..., t + 1] * Ps[t + 1]
+        Pt = torch.stack(Ps, -1)
+        KW, KM = et * Pt, et * b_all
+        cW = torch.prod(ga, -1)
+        cM = torch.prod(be, -1)
+        cWM = be[..., 0] * Pt[..., 0]
+        E = V - torch.einsum("bhij,bhtj->bhti", W, K)
+        outs.append(torch.einsum("bhij,bhtj->bhti", W, Q))
+        AW = torch.einsum("bhti,bht,bhtj->bhij", E, KW, K)
+        AM = torch.einsum("bhti,bht,bhtj->bhij", E, KM, K)
+        W, M = (cW[..., None, None] * W + cWM[..., None, None] * M + AW,
+                cM[..., None, None] * M + AM)
+    return torch.cat(outs, 2), W.reshape(B, H, d * d), M.reshape(B, H, d * d)
+
+
+@pytest.mark.parametrize("mode", [oracle.GAMMA_1_MINUS_ETA_ALPHA, oracle.ALPHA_IS_GAMMA])
+@pytest.mark.parametrize("L,C,d", [(9, 4, 3), (16, 16, 4), (11, 3, 5)])
+def test_backward_matches_autograd_of_closed_form(mode, L, C, d):
+    rng = np.random.default_rng(200 + L + C + d + mode)
+    B, H = 2, 1
+    x = _problem(rng, B, H, L, d, mode)
+    dout = rng.standard_normal((B, H, L, d))
+    dWe = rng.standard_normal((B, H, d * d))
+    dMe = rng.standard_normal((B, H, d * d))
+    xt = {n: torch.tensor(x[n], dtype=torch.float64, requires_grad=True) for n in NAMES}
+    o, We, Me = _closed_form_torch(xt, C, mode)
+    loss = (torch.tensor(dout) * o).sum() + (torch.tensor(dWe) * We).sum() + \
+        (torch.tensor(dMe) * Me).sum()
+    loss.backward()
+    g = oracle.chunk_backward(oracle.LINEAR, *[x[n] for n in NAMES], dout, dWe, dMe, C,
+                              decay_mode=mode)
+    for n in NAMES:
+        ref = xt[n].grad.numpy()
+        err = np.linalg.norm(g[n] - ref) / max(np.linalg.norm(ref), 1e-300)
+        assert err <= 1e-10, (n, err)
+
+
+def test_backward_without_state_gradients_and_empty_sequence():
+    """dWend = dMend = None means zero; L = 0 passes the state gradients
+    through unchanged (Wend = W0, Mend = M0)."""
+    rng = np.random.default_rng(7)
+    B, H, L, d, C = 1, 1, 5, 3, 2
+    x = _problem(rng, B, H, L, d, 0)
+    dout = rng.standard_normal((B, H, L, d))
+    z = np.zeros((B, H, d * d))
+    g0 = oracle.chunk_backward(oracle.LINEAR, *[x[n] for n in NAMES], dout, None, None, C)
+    g1 = oracle.chunk_backward(oracle.LINEAR, *[x[n] for n in NAMES], dout, z, z, C)
+    for n in NAMES:
+        np.testing.assert_array_equal(g0[n], g1[n])
+    e = {n: (x[n][:, :, :0] if n not in ("W0", "M0") else x[n]) for n in NAMES}
+    dWe = rng.standard_normal((B, H, d * d))
+    dMe = rng.standard_normal((B, H, d * d))
+    ge = oracle.chunk_backward(oracle.LINEAR, *[e[n] for n in NAMES],
+                               np.zeros((B, H, 0, d)), dWe, dMe, C)
+    np.testing.assert_array_equal(ge["W0"], dWe)
+    np.testing.assert_array_equal(ge["M0"], dMe)

@@ -64,7 +64,8 @@ _lib = None
 
 EXPORTED = ("e2ttt_validate", "e2ttt_workspace_bytes", "e2ttt_chunk_forward",
             "e2ttt_scalar_kernels", "e2ttt_chunk_forward_timed", "e2ttt_status_string",
-            "e2ttt_decode_workspace_bytes", "e2ttt_decode_step")
+            "e2ttt_decode_workspace_bytes", "e2ttt_decode_step",
+            "e2ttt_backward_workspace_bytes", "e2ttt_chunk_backward")
 
 # e2ttt_kernel_class
 KERNEL_SCAN, KERNEL_PREP, KERNEL_FWD13, KERNEL_FWD2, KERNEL_BWD, KERNEL_AGG = range(6)
@@ -106,6 +107,10 @@ def lib() -> ctypes.CDLL:
             L.e2ttt_decode_step.argtypes = [P] + [vp] * 10 + [ctypes.c_int, vp, ctypes.c_size_t,
                                                               vp]
             L.e2ttt_decode_step.restype = ctypes.c_int
+            L.e2ttt_backward_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+            L.e2ttt_backward_workspace_bytes.restype = ctypes.c_int
+            L.e2ttt_chunk_backward.argtypes = [P] + [vp] * 20 + [ctypes.c_size_t, vp]
+            L.e2ttt_chunk_backward.restype = ctypes.c_int
             L.e2ttt_status_string.argtypes = [ctypes.c_int]
             L.e2ttt_status_string.restype = ctypes.c_char_p
             _lib = L
@@ -213,6 +218,34 @@ def decode_step(prob: Problem, q, k, v, eta, alpha, beta, W0, W, M, out, chunk_e
         int(workspace_nbytes), _stream(stream))
     if check and st != OK:
         raise E2tttError(st, "e2ttt_decode_step")
+    return st
+
+
+def backward_workspace_bytes(prob: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    st = lib().e2ttt_backward_workspace_bytes(ctypes.byref(prob), ctypes.byref(n))
+    if st != OK:
+        raise E2tttError(st, "e2ttt_backward_workspace_bytes")
+    return int(n.value)
+
+
+def chunk_backward(prob: Problem, q, k, v, eta, alpha, beta, W0, M0, dout, dW_end, dM_end,
+                   dq, dk, dv, deta, dalpha, dbeta, dW0, dM0, workspace,
+                   workspace_nbytes: Optional[int] = None, stream=None,
+                   check: bool = True) -> int:
+    """Call ``e2ttt_chunk_backward`` (linear learner): gradients of a loss
+    with respect to every input of the chunk forward, given its gradients
+    dout, dW_end, dM_end (the last two may be None).  Returns the status;
+    raises on failure when ``check``."""
+    if workspace_nbytes is None:
+        workspace_nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().e2ttt_chunk_backward(
+        ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(alpha), _ptr(beta),
+        _ptr(W0), _ptr(M0), _ptr(dout), _ptr(dW_end), _ptr(dM_end), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(deta), _ptr(dalpha), _ptr(dbeta), _ptr(dW0), _ptr(dM0), _ptr(workspace),
+        int(workspace_nbytes), _stream(stream))
+    if check and st != OK:
+        raise E2tttError(st, "e2ttt_chunk_backward")
     return st
 
 

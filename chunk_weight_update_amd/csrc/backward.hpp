@@ -1,0 +1,400 @@
+// backward.hpp -- outer-loop backward of the chunk forward for the linear
+// learner f_W(x) = W x (fp32 inputs, d <= 64, a multiple of 16).
+//
+// The chunk forward of "Rethinking Expressivity and Efficiency in Test-Time
+// Training" (E2-TTT, §3.2 and App. A) gives, per chunk with chunk-start state
+// (Ws, Ms), per-token residuals e_t = v_t - Ws k_t and kernels K^W, K^M:
+//   out_t = Ws q_t                                         (Eq. 6)
+//   W_C = cW Ws + cWM Ms + sum_t K^W_t e_t k_t^T
+//   M_C = cM Ms + sum_t K^M_t e_t k_t^T.
+// Given the adjoints (dW_C, dM_C) of the chunk-end state and dout, the
+// chunk's reverse step is, with u_t = dW_C k_t and m_t = dM_C k_t:
+//   dK^W_t = e_t . u_t,  dK^M_t = e_t . m_t
+//   de_t = K^W_t u_t + K^M_t m_t,  dv_t = de_t
+//   dq_t = Ws^T dout_t
+//   dk_t = K^W_t dW_C^T e_t + K^M_t dM_C^T e_t - Ws^T de_t
+//   dWs  = cW dW_C + sum_t (dout_t q_t^T - de_t k_t^T)
+//   dMs  = cWM dW_C + cM dM_C
+//   dcW = <dW_C, Ws>,  dcM = <dM_C, Ms>,  dcWM = <dW_C, Ms>
+// and (dWs, dMs) are the adjoints of the previous chunk's end state.  The
+// kernels' adjoints are carried to eta, alpha, beta by the reverse mode of the
+// scalar scan (App. A.2's suffix products and the affine reverse scan of P),
+// which runs forward in token order (k_lin_bwd_scalars).
+//
+//   k_lin_bwd_tok     per 64-token tile: e, u, m, de, dK^W, dK^M, dv, dq, dk
+//   k_lin_bwd_state   per 16-row block of the state: dWs, dMs and the block's
+//                     partial sums of dcW, dcM, dcWM (added later in block
+//                     order, so results do not depend on scheduling)
+//   k_lin_bwd_scalars per (unit, chunk) segment, one wave: deta, dalpha, dbeta
+#pragma once
+
+#include "kernels.hpp"
+
+namespace e2ttt {
+
+struct LinBwdArgs {
+  Shape s;
+  int r;     // chunk index
+  int mode;  // decay mode: 0 gamma = 1 - eta alpha (Eq. 14), 1 gamma = alpha
+  const float* q;
+  const float* k;
+  const float* v;
+  const float* dout;
+  const float* Ws;   // chunk-start state of chunk r, [BH][P]
+  const float* Ms;
+  const float* dWC;  // adjoints of chunk r's end state, [BH][P]
+  const float* dMC;
+  const float* kw;   // [BH][nC][Cp]
+  const float* km;
+  const float* coef; // [BH][nC][4]: cW, cM, cWM
+  float* dq;         // [BH][L][d]
+  float* dk;
+  float* dv;
+  float* de;         // [BH][Cp][d] (zero on padding tokens)
+  float* sw;         // dK^W, [BH][nC][Cp]
+  float* sm;         // dK^M
+  float* dots;       // [BH][nC][d/16][4]: block partials of dcW, dcM, dcWM
+  float* dWp;        // adjoints of chunk r's start state, [BH][P]
+  float* dMp;
+};
+
+// LDS floats of k_lin_bwd_tok: three d x (d+1) matrices and six 64 x (d+1)
+// token tiles.
+__host__ __device__ constexpr int64_t lin_bwd_tok_lds_floats(int64_t d) {
+  return (3 * d + 6 * 64) * (d + 1);
+}
+
+__global__ __launch_bounds__(256) void k_lin_bwd_tok(LinBwdArgs a) {
+  extern __shared__ float lsm[];
+  const Shape& s = a.s;
+  const int d = static_cast<int>(s.d), D1 = d + 1;
+  float* Wl = lsm;             // Ws
+  float* dWl = Wl + d * D1;    // dW_C
+  float* dMl = dWl + d * D1;   // dM_C
+  float* Kt = dMl + d * D1;    // k rows of the tile
+  float* Xt = Kt + 64 * D1;    // v rows, then dout rows
+  float* Et = Xt + 64 * D1;    // e
+  float* Dt = Et + 64 * D1;    // de
+  float* Pw = Dt + 64 * D1;    // e_i u_i
+  float* Pm = Pw + 64 * D1;    // e_i m_i
+  const int64_t ntm = s.Cp / 64;
+  const int64_t mt = blockIdx.x % ntm, u = blockIdx.x / ntm;
+  const int64_t p0 = mt * 64;
+  const int64_t tok0 = static_cast<int64_t>(a.r) * s.C;
+  const int64_t nv = n_valid(s, a.r);
+  const int64_t P = static_cast<int64_t>(d) * d;
+  const int64_t seg = u * s.nC + a.r;
+  for (int idx = threadIdx.x; idx < d * d; idx += 256) {
+    const int o = (idx / d) * D1 + idx % d;
+    Wl[o] = a.Ws[u * P + idx];
+    dWl[o] = a.dWC[u * P + idx];
+    dMl[o] = a.dMC[u * P + idx];
+  }
+  for (int idx = threadIdx.x; idx < 64 * d; idx += 256) {
+    const int pr = idx / d, c = idx % d;
+    const int64_t p = p0 + pr;
+    const bool ok = p < nv;
+    const int64_t g = (u * s.L + tok0 + p) * d + c;
+    Kt[pr * D1 + c] = ok ? a.k[g] : 0.0f;
+    Xt[pr * D1 + c] = ok ? a.v[g] : 0.0f;
+  }
+  __syncthreads();
+  const float* kwr = a.kw + seg * s.Cp;
+  const float* kmr = a.km + seg * s.Cp;
+  // Token pr, output row i: e, u, m and de.
+  for (int idx = threadIdx.x; idx < 64 * d; idx += 256) {
+    const int pr = idx / d, i = idx % d;
+    const int64_t p = p0 + pr;
+    float y = 0.0f, uu = 0.0f, mm = 0.0f;
+    for (int j = 0; j < d; ++j) {
+      const float kj = Kt[pr * D1 + j];
+      y += Wl[i * D1 + j] * kj;
+      uu += dWl[i * D1 + j] * kj;
+      mm += dMl[i * D1 + j] * kj;
+    }
+    const float e = Xt[pr * D1 + i] - y;
+    const float kwv = p < nv ? kwr[p] : 0.0f, kmv = p < nv ? kmr[p] : 0.0f;
+    const float de = kwv * uu + kmv * mm;
+    Et[pr * D1 + i] = e;
+    Dt[pr * D1 + i] = de;
+    Pw[pr * D1 + i] = e * uu;
+    Pm[pr * D1 + i] = e * mm;
+    a.de[(u * s.Cp + p) * d + i] = de;
+    if (p < nv) a.dv[(u * s.L + tok0 + p) * d + i] = de;
+  }
+  __syncthreads();
+  // dK^W, dK^M of each token, summed in row order.
+  if (threadIdx.x < 128) {
+    const int pr = threadIdx.x & 63;
+    const float* src = threadIdx.x < 64 ? Pw : Pm;
+    float acc = 0.0f;
+    for (int i = 0; i < d; ++i) acc += src[pr * D1 + i];
+    (threadIdx.x < 64 ? a.sw : a.sm)[seg * s.Cp + p0 + pr] = acc;
+  }
+  for (int idx = threadIdx.x; idx < 64 * d; idx += 256) {
+    const int pr = idx / d, c = idx % d;
+    const int64_t p = p0 + pr;
+    Xt[pr * D1 + c] = p < nv ? a.dout[(u * s.L + tok0 + p) * d + c] : 0.0f;
+  }
+  __syncthreads();
+  // Token pr, input column j: dq and dk.
+  for (int idx = threadIdx.x; idx < 64 * d; idx += 256) {
+    const int pr = idx / d, j = idx % d;
+    const int64_t p = p0 + pr;
+    float gq = 0.0f, gw = 0.0f, gm = 0.0f, gd = 0.0f;
+    for (int i = 0; i < d; ++i) {
+      const float wij = Wl[i * D1 + j];
+      const float ei = Et[pr * D1 + i];
+      gq += wij * Xt[pr * D1 + i];
+      gw += dWl[i * D1 + j] * ei;
+      gm += dMl[i * D1 + j] * ei;
+      gd += wij * Dt[pr * D1 + i];
+    }
+    if (p < nv) {
+      const int64_t g = (u * s.L + tok0 + p) * d + j;
+      a.dq[g] = gq;
+      a.dk[g] = kwr[p] * gw + kmr[p] * gm - gd;
+    }
+  }
+}
+
+// LDS floats of k_lin_bwd_state.
+__host__ __device__ constexpr int64_t lin_bwd_state_lds_floats(int64_t d) {
+  return 2 * 64 * 16 + 2 * 64 * d + 3 * 256;
+}
+
+__global__ __launch_bounds__(256) void k_lin_bwd_state(LinBwdArgs a) {
+  extern __shared__ float lsm[];
+  const Shape& s = a.s;
+  const int d = static_cast<int>(s.d);
+  float* so = lsm;              // [64][16] dout, this block's rows
+  float* sd = so + 64 * 16;     // [64][16] de, this block's rows
+  float* sq = sd + 64 * 16;     // [64][d]
+  float* sk = sq + 64 * d;      // [64][d]
+  float* red = sk + 64 * d;     // [3][256]
+  const int nrb = d / 16;
+  const int64_t rb = blockIdx.x % nrb, u = blockIdx.x / nrb;
+  const int64_t tok0 = static_cast<int64_t>(a.r) * s.C;
+  const int64_t nv = n_valid(s, a.r);
+  const int64_t P = static_cast<int64_t>(d) * d;
+  const int nper = d / 16;  // state entries per thread (16 d / 256)
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int64_t pb = 0; pb < s.Cp; pb += 64) {
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 64 * 16; idx += 256) {
+      const int pr = idx / 16, i = idx % 16;
+      const int64_t p = pb + pr;
+      so[idx] = p < nv ? a.dout[(u * s.L + tok0 + p) * d + rb * 16 + i] : 0.0f;
+      sd[idx] = a.de[(u * s.Cp + p) * d + rb * 16 + i];
+    }
+    for (int idx = threadIdx.x; idx < 64 * d; idx += 256) {
+      const int pr = idx / d, c = idx % d;
+      const int64_t p = pb + pr;
+      const bool ok = p < nv;
+      sq[idx] = ok ? a.q[(u * s.L + tok0 + p) * d + c] : 0.0f;
+      sk[idx] = ok ? a.k[(u * s.L + tok0 + p) * d + c] : 0.0f;
+    }
+    __syncthreads();
+    for (int e = 0; e < nper; ++e) {
+      const int ent = threadIdx.x + 256 * e;
+      const int i = ent / d, j = ent % d;
+      float t = 0.0f;
+      for (int pr = 0; pr < 64; ++pr)
+        t += so[pr * 16 + i] * sq[pr * d + j] - sd[pr * 16 + i] * sk[pr * d + j];
+      acc[e] += t;
+    }
+  }
+  const float* cf = a.coef + (u * s.nC + a.r) * 4;
+  const float cW = cf[0], cM = cf[1], cWM = cf[2];
+  float pw = 0.0f, pm = 0.0f, pwm = 0.0f;
+  for (int e = 0; e < nper; ++e) {
+    const int ent = threadIdx.x + 256 * e;
+    const int64_t off = u * P + (rb * 16 + ent / d) * d + ent % d;
+    const float gW = a.dWC[off], gM = a.dMC[off], w0 = a.Ws[off], m0 = a.Ms[off];
+    a.dWp[off] = cW * gW + acc[e];
+    a.dMp[off] = cWM * gW + cM * gM;
+    pw += gW * w0;
+    pm += gM * m0;
+    pwm += gW * m0;
+  }
+  red[threadIdx.x] = pw;
+  red[256 + threadIdx.x] = pm;
+  red[512 + threadIdx.x] = pwm;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w)
+#pragma unroll
+      for (int q = 0; q < 3; ++q) red[q * 256 + threadIdx.x] += red[q * 256 + threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x < 3)
+    a.dots[((u * s.nC + a.r) * nrb + rb) * 4 + threadIdx.x] = red[threadIdx.x * 256];
+}
+
+// ---------------------------------------------------------------------------
+// Reverse mode of the scalar scan for one segment (tokens i = 0 .. n-1 of a
+// chunk), one wave.  Forward quantities (App. A.2; K^W_i = eta_i P_i,
+// K^M_i = eta_i b_i):
+//   b_i = prod_{s>i} beta_s,  c_i = prod_{s>i} gamma_s,
+//   P_i = c_i + beta_{i+1} P_{i+1} (P_{n-1} = 1),
+//   cW = gamma_0 c_0,  cM = beta_0 b_0,  cWM = beta_0 P_0,
+// recomputed here in fp64 as the suffix scan of the linear maps
+// T_j: (b, c, P) -> (beta_j b, gamma_j c, gamma_j c + beta_j P).  Their
+// adjoints, with seeds Pbar_i = eta_i dK^W_i, bbar_i = eta_i dK^M_i (and the
+// chunk coefficients' terms at i = 0), run forward in token order:
+//   TP_i = Pbar_i + beta_i TP_{i-1},  Tb_i = bbar_i + beta_i Tb_{i-1},
+//   Tc_i = TP_i + gamma_i Tc_{i-1}    (TP_{-1} = Tb_{-1} = Tc_{-1} = 0),
+// and give dbeta_i = TP_{i-1} P_i + Tb_{i-1} b_i, dgamma_i = Tc_{i-1} c_i for
+// i >= 1, dbeta_0 = dcM b_0 + dcWM P_0, dgamma_0 = dcW c_0.  Each recurrence
+// is an affine map per token; lanes take contiguous token runs, compose them,
+// and exchange carries by a wave scan.
+struct AffD {  // x -> a x + s
+  double a, s;
+};
+__device__ __forceinline__ AffD aff_after(const AffD& f, const AffD& g) {  // g after f
+  return AffD{g.a * f.a, g.a * f.s + g.s};
+}
+
+__global__ __launch_bounds__(64) void k_lin_bwd_scalars(Shape s, int mode, const float* __restrict__ eta,
+                                                        const float* __restrict__ alpha,
+                                                        const float* __restrict__ beta,
+                                                        const float* __restrict__ sw,
+                                                        const float* __restrict__ sm,
+                                                        const float* __restrict__ dots,
+                                                        double* bcp, float* deta, float* dalpha,
+                                                        float* dbeta) {
+  const int64_t seg = blockIdx.x;
+  const int64_t u = seg / s.nC;
+  const int r = static_cast<int>(seg % s.nC);
+  const int64_t n = n_valid(s, r);
+  const int64_t t0 = u * s.L + static_cast<int64_t>(r) * s.C;
+  const int lane = threadIdx.x;
+  const int64_t tpl = (n + 63) / 64;
+  const int64_t lo = lane * tpl, hi = (lo + tpl < n ? lo + tpl : n);  // [lo, hi)
+  double* B3 = bcp + seg * s.Cp * 3;
+  auto gam = [&](int64_t i) -> double {
+    const double e = eta[t0 + i], al = alpha[t0 + i];
+    return mode == 0 ? 1.0 - e * al : al;
+  };
+  // Suffix scan of the maps T_j, j = 1 .. n-1 (B, G, Z): (b, c, P) ->
+  // (B b, G c, Z c + B P); F after E = (B_F B_E, G_F G_E, Z_F G_E + B_F Z_E).
+  double mB = 1.0, mG = 1.0, mZ = 0.0;  // this lane's composition, T_lo after ... after T_hi-1
+  for (int64_t j = hi - 1; j >= lo; --j) {
+    if (j < 1) continue;
+    const double bj = beta[t0 + j], gj = gam(j);
+    // (T_j after current): current applied first
+    const double nB = bj * mB, nG = gj * mG, nZ = gj * mG + bj * mZ;
+    mB = nB; mG = nG; mZ = nZ;
+  }
+  // Inclusive suffix over lanes: S_l = A_l after... applied to later lanes
+  // first: S_l = A_l o A_{l+1} o ... (A_{l+1} applied first).
+  double sB = mB, sG = mG, sZ = mZ;
+  for (int off = 1; off < 64; off <<= 1) {
+    const double oB = __shfl_down(sB, off), oG = __shfl_down(sG, off), oZ = __shfl_down(sZ, off);
+    if (lane + off < 64) {
+      // (this after other): other applied first
+      const double nB = sB * oB, nG = sG * oG, nZ = sZ * oG + sB * oZ;
+      sB = nB; sG = nG; sZ = nZ;
+    }
+  }
+  // Exclusive: the maps of the later lanes, applied to (1, 1, 1).
+  double xB = __shfl_down(sB, 1), xG = __shfl_down(sG, 1), xZ = __shfl_down(sZ, 1);
+  if (lane == 63) { xB = 1.0; xG = 1.0; xZ = 0.0; }
+  double vb = xB, vc = xG, vP = xZ + xB;  // v at index hi-1
+  for (int64_t i = hi - 1; i >= lo; --i) {
+    B3[3 * i] = vb;
+    B3[3 * i + 1] = vc;
+    B3[3 * i + 2] = vP;
+    if (i >= 1) {  // v_{i-1} = T_i(v_i)
+      const double bi = beta[t0 + i], gi = gam(i);
+      const double nb = bi * vb, nc = gi * vc, nP = gi * vc + bi * vP;
+      vb = nb; vc = nc; vP = nP;
+    }
+  }
+  __syncthreads();  // every lane's b, c, P written (read back below across lanes)
+  // Chunk-coefficient adjoints: block partials added in block order.
+  const int nrb = static_cast<int>(s.d / 16);
+  double dcW = 0.0, dcM = 0.0, dcWM = 0.0;
+  for (int rb = 0; rb < nrb; ++rb) {
+    dcW += dots[(seg * nrb + rb) * 4 + 0];
+    dcM += dots[(seg * nrb + rb) * 4 + 1];
+    dcWM += dots[(seg * nrb + rb) * 4 + 2];
+  }
+  const double b0 = B3[0], c0 = B3[1], P0 = B3[2];
+  const double beta0 = beta[t0], gamma0 = gam(0);
+  auto seedP = [&](int64_t i) -> double {
+    double v = static_cast<double>(eta[t0 + i]) * sw[seg * s.Cp + i];
+    if (i == 0) v += dcWM * beta0;
+    return v;
+  };
+  auto seedb = [&](int64_t i) -> double {
+    double v = static_cast<double>(eta[t0 + i]) * sm[seg * s.Cp + i];
+    if (i == 0) v += dcM * beta0;
+    return v;
+  };
+  // Pass 1: prefix carries of TP and Tb (multiplier beta_i).
+  AffD fP{1.0, 0.0}, fb{1.0, 0.0};
+  for (int64_t i = lo; i < hi; ++i) {
+    const double bi = beta[t0 + i];
+    fP = aff_after(fP, AffD{bi, seedP(i)});
+    fb = aff_after(fb, AffD{bi, seedb(i)});
+  }
+  auto prefix = [&](AffD f) -> double {  // value of the recurrence before this lane's run
+    for (int off = 1; off < 64; off <<= 1) {
+      const double oa = __shfl_up(f.a, off), os = __shfl_up(f.s, off);
+      if (lane >= off) f = aff_after(AffD{oa, os}, f);
+    }
+    const double carry = __shfl_up(f.s, 1);
+    return lane == 0 ? 0.0 : carry;
+  };
+  const double cP = prefix(fP), cb = prefix(fb);
+  // Pass 2: the Tc carries (seed TP_i, plus dcW gamma_0 at i = 0).
+  AffD fc{1.0, 0.0};
+  {
+    double TP = cP;
+    for (int64_t i = lo; i < hi; ++i) {
+      const double bi = beta[t0 + i];
+      TP = seedP(i) + bi * TP;
+      fc = aff_after(fc, AffD{gam(i), TP + (i == 0 ? dcW * gamma0 : 0.0)});
+    }
+  }
+  const double cc = prefix(fc);
+  // Pass 3: outputs.
+  double TP = cP, Tb = cb, Tc = cc;  // values at i-1
+  for (int64_t i = lo; i < hi; ++i) {
+    const double bi = beta[t0 + i], gi = gam(i);
+    const double b_i = B3[3 * i], c_i = B3[3 * i + 1], P_i = B3[3 * i + 2];
+    double dbe, dga;
+    if (i == 0) {
+      dbe = dcM * b0 + dcWM * P0;
+      dga = dcW * c0;
+    } else {
+      dbe = TP * P_i + Tb * b_i;
+      dga = Tc * c_i;
+    }
+    const double e = eta[t0 + i];
+    double det = static_cast<double>(sw[seg * s.Cp + i]) * P_i + static_cast<double>(sm[seg * s.Cp + i]) * b_i;
+    double dal;
+    if (mode == 0) {
+      det -= static_cast<double>(alpha[t0 + i]) * dga;
+      dal = -e * dga;
+    } else {
+      dal = dga;
+    }
+    deta[t0 + i] = static_cast<float>(det);
+    dalpha[t0 + i] = static_cast<float>(dal);
+    dbeta[t0 + i] = static_cast<float>(dbe);
+    TP = seedP(i) + bi * TP;
+    Tb = seedb(i) + bi * Tb;
+    Tc = TP + (i == 0 ? dcW * gamma0 : 0.0) + gi * Tc;
+  }
+}
+
+// dst = src, or zeros when src is null (an absent state gradient).
+__global__ __launch_bounds__(256) void k_copy_or_zero(const float* __restrict__ src, float* dst,
+                                                      int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) dst[i] = src ? src[i] : 0.0f;
+}
+
+}  // namespace e2ttt

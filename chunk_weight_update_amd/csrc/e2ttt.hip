@@ -21,6 +21,7 @@
 #include "gemm256.hpp"
 #include "fused.hpp"
 #include "decode.hpp"
+#include "backward.hpp"
 
 using namespace e2ttt;
 
@@ -243,7 +244,8 @@ void set_lds_attributes() {
       reinterpret_cast<const void*>(&k_phaseA<64, 2>), reinterpret_cast<const void*>(&k_phaseB<1>),
       reinterpret_cast<const void*>(&k_phaseB<2>), reinterpret_cast<const void*>(&k_phaseA2<32>),
       reinterpret_cast<const void*>(&k_phaseA2<64>), reinterpret_cast<const void*>(&k_agg256),
-      reinterpret_cast<const void*>(&k_fwd13_256), reinterpret_cast<const void*>(&k_fwd2_256)};
+      reinterpret_cast<const void*>(&k_fwd13_256), reinterpret_cast<const void*>(&k_fwd2_256),
+      reinterpret_cast<const void*>(&k_lin_bwd_tok)};
   for (const void* f : fused_kernels)
     (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   g_attr_done.store(1, std::memory_order_release);
@@ -814,6 +816,180 @@ e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* q, const v
   };
   if (prob->io_dtype == E2TTT_BF16) run(bf16_t{});
   else run(float{});
+  return hipGetLastError() == hipSuccess ? E2TTT_OK : E2TTT_EHIP;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of the linear learner's backward: the forward's scan and
+// residual buffers, then the chunk-start states, the state adjoints and the
+// per-token adjoint terms (byte offsets, 256-aligned).
+struct BwdPlan {
+  Plan f;
+  size_t wst, mst;            // chunk-start states of chunks 1 .. nC-1 (slot r), [nC][BH][P]
+  size_t dwa, dwb, dma, dmb;  // state adjoints, two of each in turn, [BH][P]
+  size_t de;                  // [BH][Cp][d]
+  size_t sw, sm;              // dK^W, dK^M, [BH][nC][Cp]
+  size_t dots;                // [BH][nC][d/16][4]
+  size_t bcp;                 // fp64 b, c, P, [BH][nC][Cp][3]
+  size_t total;
+};
+
+e2ttt_status make_bwd_plan(const e2ttt_problem* p, BwdPlan* bp) {
+  const e2ttt_status st = make_plan(p, &bp->f);
+  if (st != E2TTT_OK) return st;
+  const Plan& q = bp->f;
+  if (q.kind != E2TTT_LINEAR || q.io != E2TTT_F32 || p->flags != 0u || q.d > 64)
+    return E2TTT_EUNSUPPORTED;
+  size_t o = align256(q.total);
+  auto take = [&](size_t bytes) { const size_t at = o; o = align256(o + bytes); return at; };
+  const size_t np = 4 * static_cast<size_t>(q.BH * q.P);
+  bp->wst = take(np * q.nC);
+  bp->mst = take(np * q.nC);
+  bp->dwa = take(np);
+  bp->dwb = take(np);
+  bp->dma = take(np);
+  bp->dmb = take(np);
+  bp->de = take(4 * static_cast<size_t>(q.BH * q.Cp * q.d));
+  bp->sw = take(4 * static_cast<size_t>(q.BH * q.nC * q.Cp));
+  bp->sm = take(4 * static_cast<size_t>(q.BH * q.nC * q.Cp));
+  bp->dots = take(4 * static_cast<size_t>(q.BH * q.nC * (q.d / 16) * 4));
+  bp->bcp = take(8 * static_cast<size_t>(q.BH * q.nC * q.Cp * 3));
+  bp->total = q.L == 0 ? 0 : o;
+  return E2TTT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+e2ttt_status e2ttt_backward_workspace_bytes(const e2ttt_problem* prob, size_t* bytes) {
+  if (!bytes) return E2TTT_EINVAL;
+  BwdPlan bp;
+  const e2ttt_status st = make_bwd_plan(prob, &bp);
+  if (st != E2TTT_OK) return st;
+  *bytes = bp.total;
+  return E2TTT_OK;
+}
+
+e2ttt_status e2ttt_chunk_backward(const e2ttt_problem* prob, const void* q, const void* k,
+                                  const void* v, const float* eta, const float* alpha,
+                                  const float* beta, const float* W0, const float* M0,
+                                  const void* dout, const float* dW_end, const float* dM_end,
+                                  void* dq, void* dk, void* dv, float* deta, float* dalpha,
+                                  float* dbeta, float* dW0, float* dM0, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  BwdPlan bp;
+  e2ttt_status st = make_bwd_plan(prob, &bp);
+  if (st != E2TTT_OK) return st;
+  const Plan& pl = bp.f;
+  const bool empty = pl.L == 0;
+  if (!W0 || !M0 || !dW0 || !dM0) return E2TTT_EINVAL;
+  if (!empty && (!q || !k || !v || !eta || !alpha || !beta || !dout || !dq || !dk || !dv ||
+                 !deta || !dalpha || !dbeta || !workspace))
+    return E2TTT_EINVAL;
+  const void* p16[] = {q, k, v, eta, alpha, beta, W0, M0, dout, dW_end, dM_end,
+                       dq, dk, dv, deta, dalpha, dbeta, dW0, dM0};
+  for (const void* p : p16)
+    if (p && !aligned(p, 16)) return E2TTT_EINVAL;
+  if (workspace && !aligned(workspace, 256)) return E2TTT_EINVAL;
+  if (!empty && workspace_bytes < bp.total) return E2TTT_EWORKSPACE;
+  const size_t nx = static_cast<size_t>(pl.BH * pl.L * pl.d) * 4;
+  const size_t ns = static_cast<size_t>(pl.BH * pl.L) * 4;
+  const size_t np = static_cast<size_t>(pl.BH * pl.P) * 4;
+  const Range in[] = {rng(q, nx), rng(k, nx), rng(v, nx), rng(eta, ns), rng(alpha, ns),
+                      rng(beta, ns), rng(W0, np), rng(M0, np), rng(dout, nx),
+                      rng(dW_end, np), rng(dM_end, np)};
+  const Range outs[] = {rng(dq, nx), rng(dk, nx), rng(dv, nx), rng(deta, ns),
+                        rng(dalpha, ns), rng(dbeta, ns), rng(dW0, np), rng(dM0, np),
+                        rng(workspace, empty ? 0 : bp.total)};
+  constexpr int NO = 9, NI = 11;
+  for (int a = 0; a < NO; ++a) {
+    for (int b = a + 1; b < NO; ++b)
+      if (overlap(outs[a], outs[b])) return E2TTT_EINVAL;
+    for (int i = 0; i < NI; ++i)
+      if (overlap(outs[a], in[i])) return E2TTT_EINVAL;
+  }
+  st = device_ok();
+  if (st != E2TTT_OK) return st;
+  set_lds_attributes();
+  (void)hipGetLastError();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t nP = pl.BH * pl.P;
+  const unsigned gP = grid1((nP + 255) / 256);
+  if (empty) {  // Wend = W0, Mend = M0: the state gradients pass through
+    hipLaunchKernelGGL(k_copy_or_zero, dim3(gP), dim3(256), 0, s, dW_end, dW0, nP);
+    hipLaunchKernelGGL(k_copy_or_zero, dim3(gP), dim3(256), 0, s, dM_end, dM0, nP);
+    return hipGetLastError() == hipSuccess ? E2TTT_OK : E2TTT_EHIP;
+  }
+  char* ws = static_cast<char*>(workspace);
+  auto wsf = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  const Shape sh{pl.BH, pl.L, pl.d, 0, pl.C, pl.Cp, pl.nC, 1};
+  const float* Q = static_cast<const float*>(q);
+  const float* K = static_cast<const float*>(k);
+  const float* V = static_cast<const float*>(v);
+  float* kw = wsf(pl.kw);
+  float* km = wsf(pl.km);
+  float* coef = wsf(pl.coef);
+  Instr none;
+  launch_scan(pl, eta, alpha, beta, kw, km, pl.nC * pl.Cp, pl.Cp, pl.Cp, coef, 4, s, none);
+  // Forward re-run for the chunk-start states (the readout goes to dq, which
+  // the backward overwrites for every token).
+  auto Wst = [&](int64_t r) -> float* { return wsf(bp.wst) + r * nP; };
+  auto Mst = [&](int64_t r) -> float* { return wsf(bp.mst) + r * nP; };
+  auto Win = [&](int64_t r) -> const float* { return r == 0 ? W0 : Wst(r); };
+  auto Min = [&](int64_t r) -> const float* { return r == 0 ? M0 : Mst(r); };
+  const size_t lds_f = static_cast<size_t>(pl.d * (pl.d + 1) + 64 * (pl.d + 1)) * sizeof(float);
+  const size_t lds_a = static_cast<size_t>(2 * 64 * 16 + 64 * pl.d) * sizeof(float);
+  for (int64_t r = 0; r + 1 < pl.nC; ++r) {
+    const int ri = static_cast<int>(r);
+    hipLaunchKernelGGL(k_lin_fwd<float>, dim3(grid1(pl.BH * (2 * pl.Cp / 64))), dim3(256), lds_f,
+                       s, sh, ri, Q, K, V, Win(r), kw, km, static_cast<float*>(dq),
+                       wsf(pl.gw), wsf(pl.gm));
+    hipLaunchKernelGGL(k_lin_agg<float>, dim3(grid1(pl.BH * (pl.d / 16))), dim3(256), lds_a, s,
+                       sh, ri, K, wsf(pl.gw), wsf(pl.gm), coef, Win(r), Min(r), Wst(r + 1),
+                       Mst(r + 1));
+  }
+  // Reverse chunk loop.
+  const float* dWC = dW_end;
+  const float* dMC = dM_end;
+  if (!dWC || !dMC) {  // absent state gradients: zeros in the first adjoint pair
+    hipLaunchKernelGGL(k_copy_or_zero, dim3(gP), dim3(256), 0, s, dW_end, wsf(bp.dwb), nP);
+    hipLaunchKernelGGL(k_copy_or_zero, dim3(gP), dim3(256), 0, s, dM_end, wsf(bp.dmb), nP);
+    dWC = wsf(bp.dwb);
+    dMC = wsf(bp.dmb);
+  }
+  const size_t lds_t = static_cast<size_t>(lin_bwd_tok_lds_floats(pl.d)) * sizeof(float);
+  const size_t lds_s = static_cast<size_t>(lin_bwd_state_lds_floats(pl.d)) * sizeof(float);
+  for (int64_t r = pl.nC - 1; r >= 0; --r) {
+    LinBwdArgs a;
+    a.s = sh;
+    a.r = static_cast<int>(r);
+    a.mode = pl.mode;
+    a.q = Q; a.k = K; a.v = V; a.dout = static_cast<const float*>(dout);
+    a.Ws = Win(r); a.Ms = Min(r);
+    a.dWC = dWC; a.dMC = dMC;
+    a.kw = kw; a.km = km; a.coef = coef;
+    a.dq = static_cast<float*>(dq); a.dk = static_cast<float*>(dk); a.dv = static_cast<float*>(dv);
+    a.de = wsf(bp.de); a.sw = wsf(bp.sw); a.sm = wsf(bp.sm); a.dots = wsf(bp.dots);
+    if (r == 0) {
+      a.dWp = dW0;
+      a.dMp = dM0;
+    } else {
+      a.dWp = dWC == wsf(bp.dwa) ? wsf(bp.dwb) : wsf(bp.dwa);
+      a.dMp = dMC == wsf(bp.dma) ? wsf(bp.dmb) : wsf(bp.dma);
+    }
+    hipLaunchKernelGGL(k_lin_bwd_tok, dim3(grid1(pl.BH * (pl.Cp / 64))), dim3(256), lds_t, s, a);
+    hipLaunchKernelGGL(k_lin_bwd_state, dim3(grid1(pl.BH * (pl.d / 16))), dim3(256), lds_s, s, a);
+    dWC = a.dWp;
+    dMC = a.dMp;
+  }
+  hipLaunchKernelGGL(k_lin_bwd_scalars, dim3(grid1(pl.BH * pl.nC)), dim3(64), 0, s, sh, pl.mode,
+                     eta, alpha, beta, static_cast<const float*>(wsf(bp.sw)),
+                     static_cast<const float*>(wsf(bp.sm)), static_cast<const float*>(wsf(bp.dots)),
+                     reinterpret_cast<double*>(ws + bp.bcp), deta, dalpha, dbeta);
   return hipGetLastError() == hipSuccess ? E2TTT_OK : E2TTT_EHIP;
 }
 

@@ -234,6 +234,43 @@ E2TTT_API e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* 
                                          void* workspace, size_t workspace_bytes,
                                          void* stream);
 
+/* Outer-loop backward of e2ttt_chunk_forward (the gradients a model needs to
+ * train through the chunk update; the throughput claims of B.5 "Throughput
+ * and Inference Cost" of the E2-TTT paper are training throughput).  Given
+ * the same inputs as the forward and the gradients dout = dl/dout, dW_end =
+ * dl/dW_end, dM_end = dl/dM_end of a scalar loss l, it writes dl/dq, dl/dk,
+ * dl/dv, dl/deta, dl/dalpha, dl/dbeta, dl/dW0, dl/dM0 through the whole chunk
+ * recurrence: the readout at the chunk-start weights (Eq. 6), the per-token
+ * descent directions at those weights (§3), the two weighted aggregations and
+ * the chunk coefficients (§3.2, App. A), the scalar kernels' suffix products
+ * and the affine reverse scan (App. A.2), and the decay coupling of Eq. 14
+ * (or alpha taken as gamma).  Chunk-end states of every chunk are recomputed
+ * by a forward pass inside the call.
+ *
+ * Supported: kind E2TTT_LINEAR, io_dtype E2TTT_F32, flags 0, dim a multiple of
+ * 16 up to 64 (else EUNSUPPORTED).  Layouts as the forward: q, k, v, dout,
+ * dq, dk, dv [B,H,L,dim] fp32; eta, alpha, beta, deta, dalpha, dbeta [B,H,L];
+ * W0, M0, dW_end, dM_end, dW0, dM0 [B,H,dim*dim] row-major.  dW_end and
+ * dM_end may be NULL (zero gradients).  All pointers are device pointers owned
+ * by the caller, 16-byte aligned (workspace 256); inputs are read-only; no
+ * output may overlap another output, the workspace or any input (EINVAL).
+ * L = 0 writes dW0 = dW_end, dM0 = dM_end only.  The workspace holds at least
+ * e2ttt_backward_workspace_bytes() bytes (EWORKSPACE).  Asynchronous on
+ * `stream`; nothing is launched when an argument check fails.  Sums over
+ * tokens and state blocks run in a fixed order, so repeated calls give
+ * identical bits. */
+E2TTT_API e2ttt_status e2ttt_backward_workspace_bytes(const e2ttt_problem* prob,
+                                                      size_t* bytes);
+E2TTT_API e2ttt_status e2ttt_chunk_backward(const e2ttt_problem* prob, const void* q,
+                                            const void* k, const void* v, const float* eta,
+                                            const float* alpha, const float* beta,
+                                            const float* W0, const float* M0, const void* dout,
+                                            const float* dW_end, const float* dM_end, void* dq,
+                                            void* dk, void* dv, float* deta, float* dalpha,
+                                            float* dbeta, float* dW0, float* dM0,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

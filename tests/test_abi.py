@@ -210,3 +210,58 @@ def test_decode_host_checks():
     # null tensors are rejected before anything touches a device
     st = cwu.lib().e2ttt_decode_step(ctypes.byref(base), *([None] * 10), 0, None, 0, None)
     assert st == cwu.EINVAL
+
+
+def bwd_fake_args(prob):
+    f = Fake()
+    B, H, L, d = prob.batch, prob.heads, prob.seq_len, prob.dim
+    nx, ns, np_ = B * H * L * d * 4, B * H * L * 4, B * H * d * d * 4
+    a = dict(q=f(nx), k=f(nx), v=f(nx), eta=f(ns), alpha=f(ns), beta=f(ns), W0=f(np_),
+             M0=f(np_), dout=f(nx), dW_end=f(np_), dM_end=f(np_), dq=f(nx), dk=f(nx), dv=f(nx),
+             deta=f(ns), dalpha=f(ns), dbeta=f(ns), dW0=f(np_), dM0=f(np_))
+    nws = cwu.backward_workspace_bytes(prob)
+    a["workspace"] = f(nws)
+    a["nws"] = nws
+    return a
+
+
+def bwd_call(prob, a):
+    return cwu.chunk_backward(prob, a["q"], a["k"], a["v"], a["eta"], a["alpha"], a["beta"],
+                              a["W0"], a["M0"], a["dout"], a["dW_end"], a["dM_end"], a["dq"],
+                              a["dk"], a["dv"], a["deta"], a["dalpha"], a["dbeta"], a["dW0"],
+                              a["dM0"], a["workspace"], a["nws"], stream=0, check=False)
+
+
+def test_backward_support_and_workspace():
+    lin = linear()
+    n = cwu.backward_workspace_bytes(lin)
+    assert n > cwu.workspace_bytes(lin) and n % 256 == 0
+    assert cwu.backward_workspace_bytes(linear(seq_len=0)) == 0
+    for bad in (swiglu(), linear(io_dtype=cwu.BF16), linear(dim=128),
+                linear(flags=cwu.FLAG_CHUNK_AVERAGED_DECAY), linear(flags=cwu.FLAG_QK_SILU_L2)):
+        with pytest.raises(cwu.E2tttError) as e:
+            cwu.backward_workspace_bytes(bad)
+        assert e.value.status == cwu.EUNSUPPORTED
+    assert cwu.lib().e2ttt_backward_workspace_bytes(ctypes.byref(lin), None) == cwu.EINVAL
+
+
+@pytest.mark.parametrize("mutate,expected", [
+    (lambda a: a.update(q=None), cwu.EINVAL),
+    (lambda a: a.update(dout=None), cwu.EINVAL),
+    (lambda a: a.update(dW0=None), cwu.EINVAL),
+    (lambda a: a.update(deta=None), cwu.EINVAL),
+    (lambda a: a.update(workspace=None), cwu.EINVAL),
+    (lambda a: a.update(dk=a["dk"] + 4), cwu.EINVAL),            # misaligned
+    (lambda a: a.update(workspace=a["workspace"] + 16), cwu.EINVAL),
+    (lambda a: a.update(nws=a["nws"] - 256), cwu.EWORKSPACE),
+    (lambda a: a.update(dq=a["q"]), cwu.EINVAL),                  # output over an input
+    (lambda a: a.update(dW0=a["dW_end"]), cwu.EINVAL),            # in-place not allowed
+    (lambda a: a.update(dM0=a["dW0"]), cwu.EINVAL),               # outputs alias
+    (lambda a: a.update(workspace=a["dv"]), cwu.EINVAL),
+])
+def test_backward_host_errors(mutate, expected):
+    prob = linear()
+    a = bwd_fake_args(prob)
+    mutate(a)
+    assert bwd_call(prob, a) == expected
+    assert bwd_call(swiglu(), bwd_fake_args(linear())) == cwu.EUNSUPPORTED

@@ -237,6 +237,65 @@ def decode_bench(w, reps=200):
             "tokens_per_s": B * H / (t * 1e-6), "gbs": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS}
 
 
+def backward_bench(with_oracle, reps=50):
+    """The outer-loop backward (e2ttt_chunk_backward) on the linear workload's
+    shape (d = 64, fp32; seeded synthetic inputs and upstream gradients),
+    timed per call with events.  Algorithmic flops per token: the forward
+    re-run (8 d^2) and the backward's matrix-vector and outer products (e, u, m,
+    dq, three for dk, two for the state adjoint: 18 d^2).  At this size the
+    call is latency-bound; the line reports its time beside the main metric,
+    not as it.  With ``with_oracle``, the oracle's reverse mode is timed on the
+    host for the same problem."""
+    import numpy as np
+    import torch
+    import chunk_weight_update_amd as cwu
+    from chunk_weight_update_amd.inputs import WORKLOADS, make_workload_inputs
+    w = WORKLOADS["linear-d64-b1h1-l256-c64-fp32"]
+    inp = make_workload_inputs(w, seed=0, m0_scale=0.01)
+    rng = np.random.default_rng(1000)
+    B, H, L, d = w.B, w.H, w.L, w.d
+    up = [rng.standard_normal(s).astype(np.float32)
+          for s in ((B, H, L, d), (B, H, d * d), (B, H, d * d))]
+    names = ("q", "k", "v", "eta", "alpha", "beta", "W0", "M0")
+    t = {n: torch.from_numpy(np.ascontiguousarray(inp[n], dtype=np.float32)).cuda() for n in names}
+    dout, dW, dM = (torch.from_numpy(a).cuda() for a in up)
+    g = {n: torch.empty_like(t[n]) for n in names}
+    prob = cwu.make_problem(w.kind, B, H, L, d, 0, w.C, w.io, 0)
+    ws = torch.empty(cwu.backward_workspace_bytes(prob), dtype=torch.uint8, device="cuda")
+
+    def call():
+        cwu.chunk_backward(prob, *[t[n] for n in names], dout, dW, dM,
+                           *[g[n] for n in names], ws)
+    for _ in range(10):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 26.0 * d * d * L * B * H
+    out = {"label": "outer-loop backward of the chunk forward, linear learner "
+                    "(not the main metric)",
+           "config": w.describe(), "ms_per_call": ms, "tokens_per_s": B * L / (ms * 1e-3),
+           "tflops_algorithmic": flops / (ms * 1e-3) / 1e12,
+           "bound": "latency (16.8 MFLOP per call)"}
+    if with_oracle:
+        import oracle
+        oracle.build(force=False)
+        t0 = time.perf_counter()
+        oracle.chunk_backward(w.kind, inp["q64"], inp["k64"], inp["v64"], inp["eta"],
+                              inp["alpha"], inp["beta"], inp["W0"], inp["M0"], up[0], up[1],
+                              up[2], w.C)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": B * L / dt, "unit": "tokens/s", "cores": 1,
+                               "kind": "oracle", "sample": "the whole problem, one run "
+                               "(fp64 reverse mode of the literal recurrence, one thread)"}
+    return out
+
+
 def algorithmic_flops(w):
     if w.kind == 0:
         return 8.0 * w.d * w.d * w.L * w.B * w.H
@@ -416,6 +475,8 @@ def main():
         log(f"bench: decode step {line['decode']}")
         line["scan_microbench"] = scan_microbench()
         log(f"bench: scan microbenchmark {line['scan_microbench']}")
+        line["backward"] = backward_bench(not args.no_cpu_baseline)
+        log(f"bench: linear backward {line['backward']}")
     if not args.no_cpu_baseline:
         log("bench: timing the fp64 oracle on the host cores")
         line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)

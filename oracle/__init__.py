@@ -66,7 +66,7 @@ def _load():
             P = ctypes.POINTER(ctypes.c_double)
             i64 = ctypes.c_int64
             lib.oracle_chunk_forward.argtypes = (
-                [ctypes.c_int, ctypes.c_int] + [i64] * 6 + [P] * 11 + [ctypes.c_int] * 2)
+                [ctypes.c_int, ctypes.c_int] + [i64] * 6 + [P] * 11 + [ctypes.c_int] * 3)
             lib.oracle_chunk_forward.restype = ctypes.c_int
             lib.oracle_token_descent.argtypes = [ctypes.c_int, i64, i64, P, P, P, P]
             lib.oracle_token_descent.restype = ctypes.c_int
@@ -104,11 +104,14 @@ def set_threads(n: int) -> None:
 
 
 def chunk_forward(kind, q, k, v, eta, alpha, beta, W0, M0, chunk, hidden=0,
-                  decay_mode=GAMMA_1_MINUS_ETA_ALPHA, averaged=False, qk_norm=False):
+                  decay_mode=GAMMA_1_MINUS_ETA_ALPHA, averaged=False, qk_norm=False,
+                  row_norm=False):
     """Run the literal recurrence.  q,k,v: [B,H,L,d]; eta/alpha/beta: [B,H,L];
     W0, M0: [B,H,P].  averaged: the chunk-averaged variant (beta, gamma
     replaced by their means over each chunk).  qk_norm: the q/k prologue (SiLU,
-    then L2 normalisation per token) before use.  Returns (out [B,H,L,d],
+    then L2 normalisation per token) before use.  row_norm: every row of every
+    fast-weight matrix divided by its L2 norm after each chunk (the
+    chunk-boundary stabiliser of App. B.1).  Returns (out [B,H,L,d],
     Wend, Mend), all float64."""
     lib = _load()
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -126,7 +129,7 @@ def chunk_forward(kind, q, k, v, eta, alpha, beta, W0, M0, chunk, hidden=0,
                                   _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
                                   _ptr(alpha), _ptr(beta), _ptr(W0), _ptr(M0),
                                   _ptr(out), _ptr(Wend), _ptr(Mend), int(bool(averaged)),
-                                  int(bool(qk_norm)))
+                                  int(bool(qk_norm)), int(bool(row_norm)))
     if rc != 0:
         raise RuntimeError(f"oracle_chunk_forward failed with code {rc}")
     return out, Wend, Mend

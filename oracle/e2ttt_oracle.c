@@ -42,6 +42,14 @@
  *     chunk's tokens (of gamma_t, after Eq. 14), and otherwise the same
  *     recurrence.
  *
+ *   - Option (row_norm != 0): the stabiliser of App. B.1 ("Training
+ *     Details"), L2 normalisation of the fast-weight matrices at each chunk
+ *     boundary, following LaCT.  The pages name neither the axis nor an
+ *     epsilon; this divides every row of every fast-weight matrix (linear W;
+ *     SwiGLU W1, W3 and W2, rows as stored, i.e. one row per output unit) by
+ *     max(||row||_2, 1e-12) after each chunk's update, the last chunk
+ *     included.  M is left as it is.
+ *
  * The recurrence is run literally, token by token, on every state entry.
  * Each entry's recurrence involves only that entry, so the loops are ordered
  * state-row outer, token inner; this performs the identical sequence of fp64
@@ -187,6 +195,25 @@ int oracle_fast_forward(int kind, int64_t d, int64_t h, const double* W,
   return 0;
 }
 
+/* Divide each row of each fast-weight matrix of one unit's state by
+ * max(||row||_2, 1e-12) (the chunk-boundary normalisation option). */
+static void normalise_rows(int kind, int64_t d, int64_t h, double* W) {
+  int64_t nrows, len;
+  for (int part = 0; part < (kind == OR_LINEAR ? 1 : 2); ++part) {
+    double* base;
+    if (kind == OR_LINEAR) { base = W; nrows = d; len = d; }
+    else if (part == 0) { base = W; nrows = 2 * h; len = d; }   /* W1, W3 */
+    else { base = W + 2 * h * d; nrows = d; len = h; }          /* W2 */
+    for (int64_t r = 0; r < nrows; ++r) {
+      double ss = 0.0;
+      for (int64_t j = 0; j < len; ++j) ss += base[r * len + j] * base[r * len + j];
+      double nrm = sqrt(ss);
+      if (nrm < 1e-12) nrm = 1e-12;
+      for (int64_t j = 0; j < len; ++j) base[r * len + j] /= nrm;
+    }
+  }
+}
+
 /*
  * The chunk forward over a whole sequence, literal recurrence.
  *   q, k, v, out : [B, H, L, d]      eta, alpha, beta : [B, H, L]
@@ -194,7 +221,7 @@ int oracle_fast_forward(int kind, int64_t d, int64_t h, const double* W,
  * Chunks are consecutive runs of C tokens; a final run shorter than C (when
  * C does not divide L) is a chunk of its own.  L == 0 copies the state.
  * averaged != 0 selects the chunk-averaged variant, qk_norm != 0 the q/k
- * prologue (see the header).
+ * prologue, row_norm != 0 the chunk-boundary normalisation (see the header).
  * Returns 0 on success, nonzero on bad arguments or allocation failure.
  */
 int oracle_chunk_forward(int kind, int decay_mode, int64_t B, int64_t H,
@@ -203,7 +230,7 @@ int oracle_chunk_forward(int kind, int decay_mode, int64_t B, int64_t H,
                          const double* eta, const double* alpha,
                          const double* beta, const double* W0,
                          const double* M0, double* out, double* Wend,
-                         double* Mend, int averaged, int qk_norm) {
+                         double* Mend, int averaged, int qk_norm, int row_norm) {
   if (kind != OR_LINEAR && kind != OR_SWIGLU) return 1;
   if (decay_mode != OR_GAMMA_1_MINUS_ETA_ALPHA &&
       decay_mode != OR_ALPHA_IS_GAMMA)
@@ -346,6 +373,7 @@ int oracle_chunk_forward(int kind, int decay_mode, int64_t B, int64_t H,
           }
         }
       }
+      if (row_norm) normalise_rows(kind, d, h, W);
     }
     free(Ws); free(fe); free(fu1); free(fu3); free(fz); free(gam); free(bet);
     free(qn); free(kn);

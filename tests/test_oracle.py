@@ -396,3 +396,42 @@ def test_qk_prologue_is_silu_then_l2_normalisation(kind, d, h):
                                         C, h)
     assert _rel(out, out2) <= 1e-13 and _rel(Wend, W2) <= 1e-13 and _rel(Mend, M2) <= 1e-13
     assert np.all(out[0, 0, 2] == 0.0)
+
+
+def _normalise_rows_np(kind, W, d, h):
+    """Rows of every fast-weight matrix divided by max(||row||, 1e-12) (numpy)."""
+    W = np.array(W, dtype=np.float64)
+    parts = [(0, d, d)] if kind == oracle.LINEAR else [(0, 2 * h, d), (2 * h * d, d, h)]
+    for off, rows, cols in parts:
+        blk = W[..., off:off + rows * cols].reshape(W.shape[:-1] + (rows, cols))
+        nrm = np.maximum(np.linalg.norm(blk, axis=-1, keepdims=True), 1e-12)
+        W[..., off:off + rows * cols] = (blk / nrm).reshape(W.shape[:-1] + (rows * cols,))
+    return W
+
+
+@pytest.mark.parametrize("kind,d,h", [(oracle.LINEAR, 4, 0), (oracle.SWIGLU, 3, 5)])
+@pytest.mark.parametrize("C,L", [(3, 10), (4, 4), (1, 3)])
+def test_row_norm_is_chunkwise_row_normalisation(kind, d, h, C, L):
+    """Chunk-boundary normalisation (App. B.1): the run with the option equals
+    chunk-by-chunk runs without it, with every fast-weight row divided by its
+    norm (numpy) between chunks and after the last; readouts of later chunks
+    see the normalised weights, and M is untouched by the normalisation."""
+    rng = np.random.default_rng(31 + C + L + d)
+    q, k, v, eta, alpha, beta, W0, M0 = _rand_problem(rng, kind, L, d, h)
+    out, We, Me = oracle.chunk_forward(kind, q, k, v, eta, alpha, beta, W0, M0, C, h,
+                                       row_norm=True)
+    W, M, outs = W0, M0, []
+    for t0 in range(0, L, C):
+        sl = slice(t0, min(L, t0 + C))
+        o, W, M = oracle.chunk_forward(kind, q[:, :, sl], k[:, :, sl], v[:, :, sl],
+                                       eta[:, :, sl], alpha[:, :, sl], beta[:, :, sl], W, M,
+                                       C, h)
+        W = _normalise_rows_np(kind, W, d, h)
+        outs.append(o)
+    assert _rel(out, np.concatenate(outs, axis=2)) <= 1e-13
+    assert _rel(We, W) <= 1e-13
+    assert _rel(Me, M) <= 1e-13
+    assert np.allclose(_normalise_rows_np(kind, We, d, h), We, rtol=0, atol=1e-14)
+    # the option changes the result (the normalisation is not a no-op here)
+    _, W_plain, _ = oracle.chunk_forward(kind, q, k, v, eta, alpha, beta, W0, M0, C, h)
+    assert _rel(We, W_plain) > 1e-3

@@ -26,6 +26,7 @@ GAMMA_1_MINUS_ETA_ALPHA, ALPHA_IS_GAMMA = 0, 1
 FLAG_COMPENSATED_WEIGHTS = 1
 FLAG_CHUNK_AVERAGED_DECAY = 2
 FLAG_QK_SILU_L2 = 4
+FLAG_POST_CHUNK_ROW_L2 = 8
 
 
 class Problem(ctypes.Structure):

@@ -44,6 +44,7 @@ struct Plan {
   int kind, io, mode, krep;
   int averaged = 0;  // chunk-averaged beta, gamma (E2TTT_FLAG_CHUNK_AVERAGED_DECAY)
   int qknorm = 0;    // SiLU + L2 prologue on q, k (E2TTT_FLAG_QK_SILU_L2)
+  int rownorm = 0;   // chunk-boundary row normalisation (E2TTT_FLAG_POST_CHUNK_ROW_L2)
   bool fused;   // two-kernel chunk step (SwiGLU, d = 128, bf16 io)
   int rbA;      // phase A rows per workgroup (32 or 64; LDS-streamed variant)
   int wpuA;     // register-resident phase A: workgroups per unit (0: not used)
@@ -64,7 +65,8 @@ e2ttt_status check_problem(const e2ttt_problem* p) {
     return E2TTT_EINVAL;
   if ((p->flags & ~static_cast<uint32_t>(E2TTT_FLAG_COMPENSATED_WEIGHTS |
                                          E2TTT_FLAG_CHUNK_AVERAGED_DECAY |
-                                         E2TTT_FLAG_QK_SILU_L2)) != 0u)
+                                         E2TTT_FLAG_QK_SILU_L2 |
+                                         E2TTT_FLAG_POST_CHUNK_ROW_L2)) != 0u)
     return E2TTT_EINVAL;
   if (p->reserved != 0u) return E2TTT_EINVAL;
   if (p->batch < 1 || p->heads < 1 || p->seq_len < 0 || p->dim < 1 || p->chunk < 1)
@@ -102,6 +104,7 @@ e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
   q.kind = p->kind; q.io = p->io_dtype; q.mode = p->decay_mode;
   q.averaged = (p->flags & E2TTT_FLAG_CHUNK_AVERAGED_DECAY) ? 1 : 0;
   q.qknorm = (p->flags & E2TTT_FLAG_QK_SILU_L2) ? 1 : 0;
+  q.rownorm = (p->flags & E2TTT_FLAG_POST_CHUNK_ROW_L2) ? 1 : 0;
   q.nC = q.L > 0 ? (q.L + q.C - 1) / q.C : 0;
   q.P = q.kind == E2TTT_LINEAR ? q.d * q.d : 3 * q.d * q.h;
   const size_t f4 = 4;
@@ -252,6 +255,19 @@ void set_lds_attributes() {
 }
 
 unsigned grid1(int64_t n) { return static_cast<unsigned>(n); }
+
+// Chunk-boundary normalisation of the chunk-end weights, then (SwiGLU, when a
+// chunk follows) the next chunk's operand shadows rebuilt from them.
+template <typename T>
+void launch_rownorm(const Plan& q, const Shape& s, float* Wend, bool more, T* w13s, T* w2s,
+                    T* w2ts, hipStream_t st) {
+  const int64_t rows = q.BH * (q.h == 0 ? q.d : 2 * q.h + q.d);
+  hipLaunchKernelGGL(k_row_l2norm, dim3(grid1((rows + 3) / 4)), dim3(256), 0, st, Wend, q.BH,
+                     q.d, q.h);
+  if (q.h != 0 && more)
+    hipLaunchKernelGGL(k_prep_shadow<T>, dim3(grid1(shadow_blocks(s))), dim3(256), 0, st, s,
+                       static_cast<const float*>(Wend), w13s, w2s, w2ts);
+}
 
 // Optional event bracketing of one kernel class (benchmark instrumentation).
 struct Instr {
@@ -423,6 +439,7 @@ void launch_swiglu(const Plan& q, const void* qv, const void* kv, const void* vv
                    st, s, ri, static_cast<int>(r == q.nC - 1), ut, kt, gt, zt, coef, Win, Min,
                    Wend, Mend, w13s, w2s, w2ts);
     }
+    if (q.rownorm) launch_rownorm<T>(q, s, Wend, r + 1 < q.nC, w13s, w2s, w2ts, st);
   }
 }
 
@@ -492,6 +509,8 @@ void launch_fused(const Plan& q, const void* qv, const void* kv, const void* vv,
     if (q.nsplitB > 1)
       E2TTT_LAUNCH(I, E2TTT_KERNEL_STATE, k_state_epi, dim3(grid1(q.BH * (q.h / 64) * 24)),
                    dim3(256), 0, st, a);
+    if (q.rownorm)
+      launch_rownorm<bf16_t>(q, s, Wend, r + 1 < q.nC, a.w13s, a.w2s, a.w2ts, st);
   }
 }
 
@@ -521,6 +540,8 @@ void launch_linear(const Plan& q, const void* qv, const void* kv, const void* vv
                  dim3(256), lds_f, st, s, ri, Q, K, V, Win, kw, km, O, gw, gm);
     E2TTT_LAUNCH(I, E2TTT_KERNEL_LINEAR_AGG, k_lin_agg<IO>, dim3(grid1(q.BH * (q.d / 16))),
                  dim3(256), lds_a, st, s, ri, K, gw, gm, coef, Win, Min, Wend, Mend);
+    if (q.rownorm)
+      launch_rownorm<float>(q, s, Wend, false, nullptr, nullptr, nullptr, st);
   }
 }
 
@@ -737,7 +758,8 @@ e2ttt_status e2ttt_decode_workspace_bytes(const e2ttt_problem* prob, size_t* byt
   if (!bytes) return E2TTT_EINVAL;
   const e2ttt_status st = check_problem(prob);
   if (st != E2TTT_OK) return st;
-  if (prob->flags & E2TTT_FLAG_CHUNK_AVERAGED_DECAY) return E2TTT_EUNSUPPORTED;
+  if (prob->flags & (E2TTT_FLAG_CHUNK_AVERAGED_DECAY | E2TTT_FLAG_POST_CHUNK_ROW_L2))
+    return E2TTT_EUNSUPPORTED;
   const int64_t h = prob->kind == E2TTT_LINEAR ? 0 : prob->hidden;
   *bytes = decode_ws_total(prob, prob->batch * prob->heads, prob->dim, h);
   return E2TTT_OK;
@@ -750,7 +772,8 @@ e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* q, const v
                                void* stream) {
   e2ttt_status st = check_problem(prob);
   if (st != E2TTT_OK) return st;
-  if (prob->flags & E2TTT_FLAG_CHUNK_AVERAGED_DECAY) return E2TTT_EUNSUPPORTED;
+  if (prob->flags & (E2TTT_FLAG_CHUNK_AVERAGED_DECAY | E2TTT_FLAG_POST_CHUNK_ROW_L2))
+    return E2TTT_EUNSUPPORTED;
   const int64_t BH = prob->batch * prob->heads, d = prob->dim;
   const int64_t h = prob->kind == E2TTT_LINEAR ? 0 : prob->hidden;
   const int64_t P = h == 0 ? d * d : 3 * d * h;

@@ -934,6 +934,37 @@ __global__ __launch_bounds__(256) void k_lin_agg(Shape s, int r, const IO* __res
   }
 }
 
+// Chunk-boundary normalisation (App. B.1): every row of every fast-weight
+// matrix of every unit divided by max(||row||_2, 1e-12), in place.  Rows of a
+// unit: linear, d rows of d; SwiGLU, the 2h rows of [W1; W3] (d entries), then
+// the d rows of W2 (h entries).  One wave per row; each lane sums its strided
+// entries in order, the wave adds them by a fixed shuffle tree into lane 0,
+// and lane 0's norm is broadcast, so the result does not depend on timing.
+__global__ __launch_bounds__(256) void k_row_l2norm(float* W, int64_t BH, int64_t d, int64_t h) {
+  const int lane = threadIdx.x & 63;
+  const int64_t rows_u = h == 0 ? d : 2 * h + d;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= BH * rows_u) return;  // whole waves leave together
+  const int64_t u = row / rows_u, r = row % rows_u;
+  const int64_t P = h == 0 ? d * d : 3 * d * h;
+  float* base;
+  int64_t len;
+  if (h == 0 || r < 2 * h) {
+    base = W + u * P + r * d;
+    len = d;
+  } else {
+    base = W + u * P + 2 * h * d + (r - 2 * h) * h;
+    len = h;
+  }
+  float ss = 0.0f;
+  for (int64_t j = lane; j < len; j += 64) ss += base[j] * base[j];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_down(ss, off);
+  ss = __shfl(ss, 0);
+  const float nrm = fmaxf(sqrtf(ss), 1e-12f);
+  for (int64_t j = lane; j < len; j += 64) base[j] = base[j] / nrm;
+}
+
 __global__ __launch_bounds__(256) void k_copy2(const float* __restrict__ a,
                                                const float* __restrict__ b, float* ao, float* bo,
                                                int64_t n) {

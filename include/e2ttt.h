@@ -97,7 +97,17 @@ enum {
    * rounded to io_dtype) before using them.  Applies to e2ttt_chunk_forward,
    * its timed twin and e2ttt_decode_step; the workspace grows by the two
    * normalised copies. */
-  E2TTT_FLAG_QK_SILU_L2 = 4u
+  E2TTT_FLAG_QK_SILU_L2 = 4u,
+  /* Chunk-boundary normalisation of the fast weights ("Rethinking
+   * Expressivity and Efficiency in Test-Time Training", App. B.1 Training
+   * Details, a stabiliser taken over from LaCT): after every chunk's update,
+   * the last one included, each row of each fast-weight matrix (linear W;
+   * SwiGLU W1, W3, W2, rows as stored) is divided by max(||row||_2, 1e-12),
+   * in fp32 with a fixed summation order.  M is not changed.  The next
+   * chunk's readout and descent directions use the normalised W.  Applies to
+   * e2ttt_chunk_forward and its timed twin; e2ttt_decode_step and
+   * e2ttt_chunk_backward return EUNSUPPORTED for it. */
+  E2TTT_FLAG_POST_CHUNK_ROW_L2 = 8u
 };
 
 /* Problem description.  struct_size must equal sizeof(e2ttt_problem). */

@@ -75,7 +75,9 @@ def test_status_strings():
     (swiglu(decay_mode=3), cwu.EINVAL),
     (swiglu(flags=cwu.FLAG_CHUNK_AVERAGED_DECAY), cwu.OK),
     (swiglu(flags=cwu.FLAG_QK_SILU_L2), cwu.OK),
-    (swiglu(flags=8), cwu.EINVAL),
+    (swiglu(flags=cwu.FLAG_POST_CHUNK_ROW_L2), cwu.OK),
+    (linear(flags=cwu.FLAG_POST_CHUNK_ROW_L2), cwu.OK),
+    (swiglu(flags=16), cwu.EINVAL),
     (linear(hidden=3), cwu.EINVAL),
     (swiglu(dim=96), cwu.EUNSUPPORTED),
     (swiglu(hidden=200), cwu.EUNSUPPORTED),
@@ -207,6 +209,8 @@ def test_decode_host_checks():
     assert n >= 4 * B * H * (6 * h + d) and n % 256 == 0
     with pytest.raises(cwu.E2tttError):
         cwu.decode_workspace_bytes(swiglu(flags=cwu.FLAG_CHUNK_AVERAGED_DECAY))
+    with pytest.raises(cwu.E2tttError):
+        cwu.decode_workspace_bytes(swiglu(flags=cwu.FLAG_POST_CHUNK_ROW_L2))
     # null tensors are rejected before anything touches a device
     st = cwu.lib().e2ttt_decode_step(ctypes.byref(base), *([None] * 10), 0, None, 0, None)
     assert st == cwu.EINVAL
@@ -238,7 +242,8 @@ def test_backward_support_and_workspace():
     assert n > cwu.workspace_bytes(lin) and n % 256 == 0
     assert cwu.backward_workspace_bytes(linear(seq_len=0)) == 0
     for bad in (swiglu(), linear(io_dtype=cwu.BF16), linear(dim=128),
-                linear(flags=cwu.FLAG_CHUNK_AVERAGED_DECAY), linear(flags=cwu.FLAG_QK_SILU_L2)):
+                linear(flags=cwu.FLAG_CHUNK_AVERAGED_DECAY), linear(flags=cwu.FLAG_QK_SILU_L2),
+                linear(flags=cwu.FLAG_POST_CHUNK_ROW_L2)):
         with pytest.raises(cwu.E2tttError) as e:
             cwu.backward_workspace_bytes(bad)
         assert e.value.status == cwu.EUNSUPPORTED

@@ -45,7 +45,7 @@ def check(kind, B, H, L, d, h, C, io, seed=0, regime="default", m0_scale=0.0, de
     prob = problem_for(kind, B, H, L, d, h, C, io, decay_mode, flags)
     out, W, M = run_gpu(prob, to_device(inp, io))
     ro, rW, rM = run_oracle(kind, inp, C, h, decay_mode, averaged=bool(flags & 2),
-                            qk_norm=bool(flags & 4))
+                            qk_norm=bool(flags & 4), row_norm=bool(flags & 8))
     e = (rel_fro(out, ro), rel_fro(W, rW), rel_fro(M, rM))
     log(f"  rel_fro out={e[0]:.3e} W={e[1]:.3e} M={e[2]:.3e}")
     t = tol or TOL[io]
@@ -171,6 +171,23 @@ def test_chunk_averaged_forward(kind, B, H, L, d, h, C, io, regime):
     import chunk_weight_update_amd as cwu
     check(kind, B, H, L, d, h, C, io, seed=8, regime=regime,
           m0_scale=M0.get(regime, 0.0), flags=cwu.FLAG_CHUNK_AVERAGED_DECAY)
+
+
+@pytest.mark.parametrize("kind,B,H,L,d,h,C,io,regime,flags", [
+    (LINEAR, 1, 2, 600, 64, 0, 128, F32, "default", 0),        # ragged last chunk
+    (SWIGLU, 1, 2, 600, 128, 256, 256, F32, "nearunit", 0),    # generic fp32 path
+    (SWIGLU, 2, 2, 512, 128, 256, 128, BF16, "nearunit", 0),   # fused path, 4 chunks
+    (SWIGLU, 4, 9, 1024, 128, 256, 512, BF16, "nearunit", 0),  # fused path, unsplit phase B
+    (SWIGLU, 1, 1, 700, 256, 512, 256, BF16, "nearunit", 0),   # 256-tile generic path
+    (SWIGLU, 2, 2, 512, 128, 256, 128, BF16, "nearunit", 1),   # with hi/lo weight operands
+])
+def test_post_chunk_row_normalisation_forward(kind, B, H, L, d, h, C, io, regime, flags):
+    """Rows of the fast weights divided by their L2 norm after every chunk
+    (App. B.1); the next chunk's readout, descent directions and operand
+    shadows use the normalised weights."""
+    import chunk_weight_update_amd as cwu
+    check(kind, B, H, L, d, h, C, io, seed=12, regime=regime,
+          m0_scale=M0.get(regime, 0.0), flags=cwu.FLAG_POST_CHUNK_ROW_L2 | flags)
 
 
 @pytest.mark.parametrize("kind,B,H,L,d,h,C,io,regime", [

@@ -21,7 +21,7 @@
 // scalar scan (App. A.2's suffix products and the affine reverse scan of P),
 // which runs forward in token order (k_lin_bwd_scalars).
 //
-//   k_lin_bwd_tok     per 64-token tile: e, u, m, de, dK^W, dK^M, dv, dq, dk
+//   k_lin_bwd_tok     per 16 tokens: e, u, m, de, dK^W, dK^M, dv, dq, dk
 //   k_lin_bwd_state   per 16-row block of the state: dWs, dMs and the block's
 //                     partial sums of dcW, dcM, dcWM (added later in block
 //                     order, so results do not depend on scheduling)
@@ -58,102 +58,130 @@ struct LinBwdArgs {
   float* dMp;
 };
 
-// LDS floats of k_lin_bwd_tok: three d x (d+1) matrices and six 64 x (d+1)
-// token tiles.
+// LDS floats of k_lin_bwd_tok: three d x (d+1) matrices and four
+// LIN_BWD_TB x (d+1) token tiles.
+constexpr int LIN_BWD_TB = 16;  // tokens per workgroup
 __host__ __device__ constexpr int64_t lin_bwd_tok_lds_floats(int64_t d) {
-  return (3 * d + 6 * 64) * (d + 1);
+  return (3 * d + 4 * LIN_BWD_TB) * (d + 1);
 }
 
+// One workgroup per 16 tokens of a chunk; d = 16 R.  Thread (token pr =
+// tid / 16, g = tid % 16) owns rows g, g+16, .. (phase 1) and columns g,
+// g+16, .. (phase 2), so each thread runs 3R or 4R independent dot products
+// with compile-time trip counts.
+template <int R>
 __global__ __launch_bounds__(256) void k_lin_bwd_tok(LinBwdArgs a) {
+  constexpr int d = 16 * R, D1 = d + 1, TB = LIN_BWD_TB;
   extern __shared__ float lsm[];
   const Shape& s = a.s;
-  const int d = static_cast<int>(s.d), D1 = d + 1;
   float* Wl = lsm;             // Ws
   float* dWl = Wl + d * D1;    // dW_C
   float* dMl = dWl + d * D1;   // dM_C
   float* Kt = dMl + d * D1;    // k rows of the tile
-  float* Xt = Kt + 64 * D1;    // v rows, then dout rows
-  float* Et = Xt + 64 * D1;    // e
-  float* Dt = Et + 64 * D1;    // de
-  float* Pw = Dt + 64 * D1;    // e_i u_i
-  float* Pm = Pw + 64 * D1;    // e_i m_i
-  const int64_t ntm = s.Cp / 64;
+  float* Xt = Kt + TB * D1;    // v rows, then dout rows
+  float* Et = Xt + TB * D1;    // e
+  float* Dt = Et + TB * D1;    // de
+  const int64_t ntm = s.Cp / TB;
   const int64_t mt = blockIdx.x % ntm, u = blockIdx.x / ntm;
-  const int64_t p0 = mt * 64;
+  const int64_t p0 = mt * TB;
   const int64_t tok0 = static_cast<int64_t>(a.r) * s.C;
   const int64_t nv = n_valid(s, a.r);
-  const int64_t P = static_cast<int64_t>(d) * d;
+  constexpr int64_t P = static_cast<int64_t>(d) * d;
   const int64_t seg = u * s.nC + a.r;
+#pragma unroll 8
   for (int idx = threadIdx.x; idx < d * d; idx += 256) {
     const int o = (idx / d) * D1 + idx % d;
     Wl[o] = a.Ws[u * P + idx];
     dWl[o] = a.dWC[u * P + idx];
     dMl[o] = a.dMC[u * P + idx];
   }
-  for (int idx = threadIdx.x; idx < 64 * d; idx += 256) {
+#pragma unroll 8
+  for (int idx = threadIdx.x; idx < TB * d; idx += 256) {
     const int pr = idx / d, c = idx % d;
     const int64_t p = p0 + pr;
     const bool ok = p < nv;
-    const int64_t g = (u * s.L + tok0 + p) * d + c;
-    Kt[pr * D1 + c] = ok ? a.k[g] : 0.0f;
-    Xt[pr * D1 + c] = ok ? a.v[g] : 0.0f;
+    const int64_t gi = (u * s.L + tok0 + p) * d + c;
+    Kt[pr * D1 + c] = ok ? a.k[gi] : 0.0f;
+    Xt[pr * D1 + c] = ok ? a.v[gi] : 0.0f;
   }
   __syncthreads();
-  const float* kwr = a.kw + seg * s.Cp;
-  const float* kmr = a.km + seg * s.Cp;
-  // Token pr, output row i: e, u, m and de.
-  for (int idx = threadIdx.x; idx < 64 * d; idx += 256) {
-    const int pr = idx / d, i = idx % d;
-    const int64_t p = p0 + pr;
-    float y = 0.0f, uu = 0.0f, mm = 0.0f;
+  const int pr = threadIdx.x >> 4, g = threadIdx.x & 15;
+  const int64_t p = p0 + pr;
+  const float kwv = p < nv ? a.kw[seg * s.Cp + p] : 0.0f;
+  const float kmv = p < nv ? a.km[seg * s.Cp + p] : 0.0f;
+  // Phase 1, rows i = g + 16 r: e, u, m, de and this thread's share of
+  // dK^W = e . u and dK^M = e . m.
+  {
+    float y[R], uu[R], mm[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) { y[r] = 0.0f; uu[r] = 0.0f; mm[r] = 0.0f; }
+#pragma unroll 8
     for (int j = 0; j < d; ++j) {
       const float kj = Kt[pr * D1 + j];
-      y += Wl[i * D1 + j] * kj;
-      uu += dWl[i * D1 + j] * kj;
-      mm += dMl[i * D1 + j] * kj;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int i = g + 16 * r;
+        y[r] += Wl[i * D1 + j] * kj;
+        uu[r] += dWl[i * D1 + j] * kj;
+        mm[r] += dMl[i * D1 + j] * kj;
+      }
     }
-    const float e = Xt[pr * D1 + i] - y;
-    const float kwv = p < nv ? kwr[p] : 0.0f, kmv = p < nv ? kmr[p] : 0.0f;
-    const float de = kwv * uu + kmv * mm;
-    Et[pr * D1 + i] = e;
-    Dt[pr * D1 + i] = de;
-    Pw[pr * D1 + i] = e * uu;
-    Pm[pr * D1 + i] = e * mm;
-    a.de[(u * s.Cp + p) * d + i] = de;
-    if (p < nv) a.dv[(u * s.L + tok0 + p) * d + i] = de;
+    float pw = 0.0f, pm = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int i = g + 16 * r;
+      const float e = Xt[pr * D1 + i] - y[r];
+      const float de = kwv * uu[r] + kmv * mm[r];
+      Et[pr * D1 + i] = e;
+      Dt[pr * D1 + i] = de;
+      pw += e * uu[r];
+      pm += e * mm[r];
+      a.de[(u * s.Cp + p) * d + i] = de;
+      if (p < nv) a.dv[(u * s.L + tok0 + p) * d + i] = de;
+    }
+    // The token's 16 threads are 16 consecutive lanes: a fixed tree into g = 0.
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) {
+      pw += __shfl_down(pw, off, 16);
+      pm += __shfl_down(pm, off, 16);
+    }
+    if (g == 0) {
+      a.sw[seg * s.Cp + p] = pw;
+      a.sm[seg * s.Cp + p] = pm;
+    }
   }
   __syncthreads();
-  // dK^W, dK^M of each token, summed in row order.
-  if (threadIdx.x < 128) {
-    const int pr = threadIdx.x & 63;
-    const float* src = threadIdx.x < 64 ? Pw : Pm;
-    float acc = 0.0f;
-    for (int i = 0; i < d; ++i) acc += src[pr * D1 + i];
-    (threadIdx.x < 64 ? a.sw : a.sm)[seg * s.Cp + p0 + pr] = acc;
-  }
-  for (int idx = threadIdx.x; idx < 64 * d; idx += 256) {
-    const int pr = idx / d, c = idx % d;
-    const int64_t p = p0 + pr;
-    Xt[pr * D1 + c] = p < nv ? a.dout[(u * s.L + tok0 + p) * d + c] : 0.0f;
+#pragma unroll 8
+  for (int idx = threadIdx.x; idx < TB * d; idx += 256) {
+    const int rr = idx / d, c = idx % d;
+    const int64_t pp = p0 + rr;
+    Xt[rr * D1 + c] = pp < nv ? a.dout[(u * s.L + tok0 + pp) * d + c] : 0.0f;
   }
   __syncthreads();
-  // Token pr, input column j: dq and dk.
-  for (int idx = threadIdx.x; idx < 64 * d; idx += 256) {
-    const int pr = idx / d, j = idx % d;
-    const int64_t p = p0 + pr;
-    float gq = 0.0f, gw = 0.0f, gm = 0.0f, gd = 0.0f;
-    for (int i = 0; i < d; ++i) {
+  // Phase 2, columns j = g + 16 c: dq and dk.
+  float gq[R], gw[R], gm[R], gd[R];
+#pragma unroll
+  for (int c = 0; c < R; ++c) { gq[c] = 0.0f; gw[c] = 0.0f; gm[c] = 0.0f; gd[c] = 0.0f; }
+#pragma unroll 8
+  for (int i = 0; i < d; ++i) {
+    const float ei = Et[pr * D1 + i], oi = Xt[pr * D1 + i], di = Dt[pr * D1 + i];
+#pragma unroll
+    for (int c = 0; c < R; ++c) {
+      const int j = g + 16 * c;
       const float wij = Wl[i * D1 + j];
-      const float ei = Et[pr * D1 + i];
-      gq += wij * Xt[pr * D1 + i];
-      gw += dWl[i * D1 + j] * ei;
-      gm += dMl[i * D1 + j] * ei;
-      gd += wij * Dt[pr * D1 + i];
+      gq[c] += wij * oi;
+      gd[c] += wij * di;
+      gw[c] += dWl[i * D1 + j] * ei;
+      gm[c] += dMl[i * D1 + j] * ei;
     }
-    if (p < nv) {
-      const int64_t g = (u * s.L + tok0 + p) * d + j;
-      a.dq[g] = gq;
-      a.dk[g] = kwr[p] * gw + kmr[p] * gm - gd;
+  }
+  if (p < nv) {
+#pragma unroll
+    for (int c = 0; c < R; ++c) {
+      const int j = g + 16 * c;
+      const int64_t gi = (u * s.L + tok0 + p) * d + j;
+      a.dq[gi] = gq[c];
+      a.dk[gi] = kwv * gw[c] + kmv * gm[c] - gd[c];
     }
   }
 }
@@ -163,30 +191,35 @@ __host__ __device__ constexpr int64_t lin_bwd_state_lds_floats(int64_t d) {
   return 2 * 64 * 16 + 2 * 64 * d + 3 * 256;
 }
 
+template <int R>
 __global__ __launch_bounds__(256) void k_lin_bwd_state(LinBwdArgs a) {
+  constexpr int d = 16 * R;
   extern __shared__ float lsm[];
   const Shape& s = a.s;
-  const int d = static_cast<int>(s.d);
   float* so = lsm;              // [64][16] dout, this block's rows
   float* sd = so + 64 * 16;     // [64][16] de, this block's rows
   float* sq = sd + 64 * 16;     // [64][d]
   float* sk = sq + 64 * d;      // [64][d]
   float* red = sk + 64 * d;     // [3][256]
-  const int nrb = d / 16;
+  constexpr int nrb = R;
   const int64_t rb = blockIdx.x % nrb, u = blockIdx.x / nrb;
   const int64_t tok0 = static_cast<int64_t>(a.r) * s.C;
   const int64_t nv = n_valid(s, a.r);
-  const int64_t P = static_cast<int64_t>(d) * d;
-  const int nper = d / 16;  // state entries per thread (16 d / 256)
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  constexpr int64_t P = static_cast<int64_t>(d) * d;
+  constexpr int nper = R;  // state entries per thread (16 d / 256)
+  float acc[nper];
+#pragma unroll
+  for (int e = 0; e < nper; ++e) acc[e] = 0.0f;
   for (int64_t pb = 0; pb < s.Cp; pb += 64) {
     __syncthreads();
+#pragma unroll 8
     for (int idx = threadIdx.x; idx < 64 * 16; idx += 256) {
       const int pr = idx / 16, i = idx % 16;
       const int64_t p = pb + pr;
       so[idx] = p < nv ? a.dout[(u * s.L + tok0 + p) * d + rb * 16 + i] : 0.0f;
       sd[idx] = a.de[(u * s.Cp + p) * d + rb * 16 + i];
     }
+#pragma unroll 8
     for (int idx = threadIdx.x; idx < 64 * d; idx += 256) {
       const int pr = idx / d, c = idx % d;
       const int64_t p = pb + pr;
@@ -195,18 +228,25 @@ __global__ __launch_bounds__(256) void k_lin_bwd_state(LinBwdArgs a) {
       sk[idx] = ok ? a.k[(u * s.L + tok0 + p) * d + c] : 0.0f;
     }
     __syncthreads();
-    for (int e = 0; e < nper; ++e) {
-      const int ent = threadIdx.x + 256 * e;
-      const int i = ent / d, j = ent % d;
-      float t = 0.0f;
-      for (int pr = 0; pr < 64; ++pr)
-        t += so[pr * 16 + i] * sq[pr * d + j] - sd[pr * 16 + i] * sk[pr * d + j];
-      acc[e] += t;
+    float t[nper];
+#pragma unroll
+    for (int e = 0; e < nper; ++e) t[e] = 0.0f;
+#pragma unroll 16
+    for (int pr = 0; pr < 64; ++pr) {
+#pragma unroll
+      for (int e = 0; e < nper; ++e) {
+        const int ent = threadIdx.x + 256 * e;
+        const int i = ent / d, j = ent % d;
+        t[e] += so[pr * 16 + i] * sq[pr * d + j] - sd[pr * 16 + i] * sk[pr * d + j];
+      }
     }
+#pragma unroll
+    for (int e = 0; e < nper; ++e) acc[e] += t[e];
   }
   const float* cf = a.coef + (u * s.nC + a.r) * 4;
   const float cW = cf[0], cM = cf[1], cWM = cf[2];
   float pw = 0.0f, pm = 0.0f, pwm = 0.0f;
+#pragma unroll
   for (int e = 0; e < nper; ++e) {
     const int ent = threadIdx.x + 256 * e;
     const int64_t off = u * P + (rb * 16 + ent / d) * d + ent % d;

@@ -248,7 +248,8 @@ void set_lds_attributes() {
       reinterpret_cast<const void*>(&k_phaseB<2>), reinterpret_cast<const void*>(&k_phaseA2<32>),
       reinterpret_cast<const void*>(&k_phaseA2<64>), reinterpret_cast<const void*>(&k_agg256),
       reinterpret_cast<const void*>(&k_fwd13_256), reinterpret_cast<const void*>(&k_fwd2_256),
-      reinterpret_cast<const void*>(&k_lin_bwd_tok)};
+      reinterpret_cast<const void*>(&k_lin_bwd_tok<1>), reinterpret_cast<const void*>(&k_lin_bwd_tok<2>),
+      reinterpret_cast<const void*>(&k_lin_bwd_tok<3>), reinterpret_cast<const void*>(&k_lin_bwd_tok<4>)};
   for (const void* f : fused_kernels)
     (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   g_attr_done.store(1, std::memory_order_release);
@@ -530,13 +531,14 @@ void launch_linear(const Plan& q, const void* qv, const void* kv, const void* vv
   float* gw = reinterpret_cast<float*>(ws + q.gw);
   float* gm = reinterpret_cast<float*>(ws + q.gm);
   launch_scan(q, eta, alpha, beta, kw, km, q.nC * q.Cp, q.Cp, q.Cp, coef, 4, st, I);
-  const size_t lds_f = static_cast<size_t>(q.d * (q.d + 1) + 64 * (q.d + 1)) * sizeof(float);
+  const size_t lds_f = static_cast<size_t>(q.d * (q.d + 1) + LIN_FWD_TB * (q.d + 1)) * sizeof(float);
   const size_t lds_a = static_cast<size_t>(2 * 64 * 16 + 64 * q.d) * sizeof(float);
   for (int64_t r = 0; r < q.nC; ++r) {
     const float* Win = r == 0 ? W0 : Wend;
     const float* Min = r == 0 ? M0 : Mend;
     const int ri = static_cast<int>(r);
-    E2TTT_LAUNCH(I, E2TTT_KERNEL_LINEAR_FWD, k_lin_fwd<IO>, dim3(grid1(q.BH * (2 * q.Cp / 64))),
+    E2TTT_LAUNCH(I, E2TTT_KERNEL_LINEAR_FWD, k_lin_fwd<IO>,
+                 dim3(grid1(q.BH * (2 * q.Cp / LIN_FWD_TB))),
                  dim3(256), lds_f, st, s, ri, Q, K, V, Win, kw, km, O, gw, gm);
     E2TTT_LAUNCH(I, E2TTT_KERNEL_LINEAR_AGG, k_lin_agg<IO>, dim3(grid1(q.BH * (q.d / 16))),
                  dim3(256), lds_a, st, s, ri, K, gw, gm, coef, Win, Min, Wend, Mend);
@@ -964,11 +966,11 @@ e2ttt_status e2ttt_chunk_backward(const e2ttt_problem* prob, const void* q, cons
   auto Mst = [&](int64_t r) -> float* { return wsf(bp.mst) + r * nP; };
   auto Win = [&](int64_t r) -> const float* { return r == 0 ? W0 : Wst(r); };
   auto Min = [&](int64_t r) -> const float* { return r == 0 ? M0 : Mst(r); };
-  const size_t lds_f = static_cast<size_t>(pl.d * (pl.d + 1) + 64 * (pl.d + 1)) * sizeof(float);
+  const size_t lds_f = static_cast<size_t>(pl.d * (pl.d + 1) + LIN_FWD_TB * (pl.d + 1)) * sizeof(float);
   const size_t lds_a = static_cast<size_t>(2 * 64 * 16 + 64 * pl.d) * sizeof(float);
   for (int64_t r = 0; r + 1 < pl.nC; ++r) {
     const int ri = static_cast<int>(r);
-    hipLaunchKernelGGL(k_lin_fwd<float>, dim3(grid1(pl.BH * (2 * pl.Cp / 64))), dim3(256), lds_f,
+    hipLaunchKernelGGL(k_lin_fwd<float>, dim3(grid1(pl.BH * (2 * pl.Cp / LIN_FWD_TB))), dim3(256), lds_f,
                        s, sh, ri, Q, K, V, Win(r), kw, km, static_cast<float*>(dq),
                        wsf(pl.gw), wsf(pl.gm));
     hipLaunchKernelGGL(k_lin_agg<float>, dim3(grid1(pl.BH * (pl.d / 16))), dim3(256), lds_a, s,
@@ -1004,8 +1006,13 @@ e2ttt_status e2ttt_chunk_backward(const e2ttt_problem* prob, const void* q, cons
       a.dWp = dWC == wsf(bp.dwa) ? wsf(bp.dwb) : wsf(bp.dwa);
       a.dMp = dMC == wsf(bp.dma) ? wsf(bp.dmb) : wsf(bp.dma);
     }
-    hipLaunchKernelGGL(k_lin_bwd_tok, dim3(grid1(pl.BH * (pl.Cp / 64))), dim3(256), lds_t, s, a);
-    hipLaunchKernelGGL(k_lin_bwd_state, dim3(grid1(pl.BH * (pl.d / 16))), dim3(256), lds_s, s, a);
+    const int R = static_cast<int>(pl.d / 16);
+    void (*ktok)(LinBwdArgs) = R == 1 ? k_lin_bwd_tok<1> : R == 2 ? k_lin_bwd_tok<2>
+                               : R == 3 ? k_lin_bwd_tok<3> : k_lin_bwd_tok<4>;
+    void (*kst)(LinBwdArgs) = R == 1 ? k_lin_bwd_state<1> : R == 2 ? k_lin_bwd_state<2>
+                              : R == 3 ? k_lin_bwd_state<3> : k_lin_bwd_state<4>;
+    hipLaunchKernelGGL(ktok, dim3(grid1(pl.BH * (pl.Cp / LIN_BWD_TB))), dim3(256), lds_t, s, a);
+    hipLaunchKernelGGL(kst, dim3(grid1(pl.BH * R)), dim3(256), lds_s, s, a);
     dWC = a.dWp;
     dMC = a.dMp;
   }

@@ -835,6 +835,10 @@ __global__ __launch_bounds__(256) void k_agg(Shape s, int r, int last, const T* 
 // Linear learner f_W(x) = W x (fp32 arithmetic; io fp32 or bf16).
 // fwd: Y = X W^T for X = [K; Q] rows of chunk r; readout or scaled residuals
 // gw = K^W g, gm = K^M g with g = v - W k (fp32, [BH][Cp][d]).
+// A workgroup takes LIN_FWD_TB rows; thread (row tid/16, g = tid%16) owns
+// the outputs g, g+16, .. (up to 8 independent dot products, so the LDS reads
+// of one step serve several accumulators).
+constexpr int LIN_FWD_TB = 16;
 template <typename IO>
 __global__ __launch_bounds__(256) void k_lin_fwd(Shape s, int r, const IO* __restrict__ q,
                                                  const IO* __restrict__ k,
@@ -843,37 +847,54 @@ __global__ __launch_bounds__(256) void k_lin_fwd(Shape s, int r, const IO* __res
                                                  const float* __restrict__ kw,
                                                  const float* __restrict__ km, IO* out,
                                                  float* gw, float* gm) {
+  constexpr int TB = LIN_FWD_TB;
   extern __shared__ float lsm[];
   const int64_t d = s.d;
+  const int D1 = static_cast<int>(d) + 1;
   float* Ws = lsm;                 // [d][d+1]
-  float* Xs = lsm + d * (d + 1);   // [64][d+1]
-  const int64_t ntm = 2 * s.Cp / 64, mtK = s.Cp / 64;
+  float* Xs = lsm + d * D1;        // [TB][d+1]
+  const int64_t ntm = 2 * s.Cp / TB, mtK = s.Cp / TB;
   const int64_t mt = blockIdx.x % ntm, u = blockIdx.x / ntm;
   const bool isQ = mt >= mtK;
-  const int64_t p0 = (mt - (isQ ? mtK : 0)) * 64;
+  const int64_t p0 = (mt - (isQ ? mtK : 0)) * TB;
   const int64_t tok0 = static_cast<int64_t>(r) * s.C;
   const int64_t nv = n_valid(s, r);
   const IO* X = (isQ ? q : k) + (u * s.L + tok0) * d;
+#pragma unroll 8
   for (int64_t idx = threadIdx.x; idx < d * d; idx += 256)
-    Ws[(idx / d) * (d + 1) + idx % d] = Wst[u * d * d + idx];
-  for (int64_t idx = threadIdx.x; idx < 64 * d; idx += 256) {
+    Ws[(idx / d) * D1 + idx % d] = Wst[u * d * d + idx];
+#pragma unroll 8
+  for (int64_t idx = threadIdx.x; idx < TB * d; idx += 256) {
     const int64_t pr = idx / d, c = idx % d, p = p0 + pr;
-    Xs[pr * (d + 1) + c] = p < nv ? to_f32<IO>(X[p * d + c]) : 0.0f;
+    Xs[pr * D1 + c] = p < nv ? to_f32<IO>(X[p * d + c]) : 0.0f;
   }
   __syncthreads();
-  const float* kwr = kw + (u * s.nC + r) * s.Cp;
-  const float* kmr = km + (u * s.nC + r) * s.Cp;
-  for (int64_t idx = threadIdx.x; idx < 64 * d; idx += 256) {
-    const int64_t pr = idx / d, c = idx % d, p = p0 + pr;
-    float y = 0.0f;
-    for (int64_t kk = 0; kk < d; ++kk) y += Xs[pr * (d + 1) + kk] * Ws[c * (d + 1) + kk];
+  const int R = static_cast<int>(d / 16);  // outputs per thread (d <= 128)
+  const int pr = threadIdx.x >> 4, g = threadIdx.x & 15;
+  const int64_t p = p0 + pr;
+  float y[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) y[c] = 0.0f;
+#pragma unroll 4
+  for (int kk = 0; kk < static_cast<int>(d); ++kk) {
+    const float x = Xs[pr * D1 + kk];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      if (c < R) y[c] += x * Ws[(g + 16 * c) * D1 + kk];
+  }
+  const float kwv = p < nv ? kw[(u * s.nC + r) * s.Cp + p] : 0.0f;
+  const float kmv = p < nv ? km[(u * s.nC + r) * s.Cp + p] : 0.0f;
+#pragma unroll
+  for (int c8 = 0; c8 < 8; ++c8) {
+    if (c8 >= R) break;
+    const int64_t c = g + 16 * c8;
     if (isQ) {
-      if (p < nv) out[(u * s.L + tok0 + p) * d + c] = from_f32<IO>(y);
+      if (p < nv) out[(u * s.L + tok0 + p) * d + c] = from_f32<IO>(y[c8]);
     } else {
       const float vin = p < nv ? to_f32<IO>(v[(u * s.L + tok0 + p) * d + c]) : 0.0f;
-      const float g = vin - y;
-      gw[(u * s.Cp + p) * d + c] = kwr[p] * g;
-      gm[(u * s.Cp + p) * d + c] = kmr[p] * g;
+      const float gg = vin - y[c8];
+      gw[(u * s.Cp + p) * d + c] = kwv * gg;
+      gm[(u * s.Cp + p) * d + c] = kmv * gg;
     }
   }
 }

@@ -44,14 +44,12 @@ struct Tile256 {
 // loader256_chunk(i).  rowp[i] points at that row's chunk (k offset 0).
 struct Loader256 {
   const bf16_t* rowp[4];
-  __device__ __forceinline__ void issue(int64_t k0, char* slab) const {
+  // Load i of this wave for the slab starting at token k0 into `slab`.
+  __device__ __forceinline__ void issue1(int i, int64_t k0, char* slab) const {
     const int wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(
-          static_cast<const void*>(rowp[i] + k0),
-          (__attribute__((address_space(3))) void*)(slab + (4 * wave + i) * 1024),
-          16, 0, 0);
+    __builtin_amdgcn_global_load_lds(
+        static_cast<const void*>(rowp[i] + k0),
+        (__attribute__((address_space(3))) void*)(slab + (4 * wave + i) * 1024), 16, 0, 0);
   }
 };
 
@@ -134,11 +132,7 @@ __device__ __forceinline__ void gemm_tile256(f32x16_t (&acc)[4][4], const Loader
   // Load q (0..7) of a slab: operand q / 4, piece q % 4 of the wave's rows.
   auto load = [&](int slab, int q) {
     char* st = lds + (slab % NST) * 2 * SB;
-    const Loader256& l = q < 4 ? la : lb;
-    __builtin_amdgcn_global_load_lds(
-        static_cast<const void*>(l.rowp[q & 3] + k0 + static_cast<int64_t>(slab) * BK),
-        (__attribute__((address_space(3))) void*)(st + (q < 4 ? 0 : SB) + (4 * wave + (q & 3)) * 1024),
-        16, 0, 0);
+    (q < 4 ? la : lb).issue1(q & 3, k0 + static_cast<int64_t>(slab) * BK, st + (q < 4 ? 0 : SB));
   };
   auto body = [&](int s, bool refill) {
     const char* As = lds + (s % NST) * 2 * SB + wm * 128 * 64;

@@ -180,6 +180,9 @@ def test_chunk_averaged_forward(kind, B, H, L, d, h, C, io, regime):
     (SWIGLU, 4, 9, 1024, 128, 256, 512, BF16, "nearunit", 0),  # fused path, unsplit phase B
     (SWIGLU, 1, 1, 700, 256, 512, 256, BF16, "nearunit", 0),   # 256-tile generic path
     (SWIGLU, 2, 2, 512, 128, 256, 128, BF16, "nearunit", 1),   # with hi/lo weight operands
+    (SWIGLU, 2, 2, 512, 128, 256, 128, BF16, "nearunit", 6),   # with chunk averaging, q/k prologue
+    (LINEAR, 1, 2, 300, 32, 0, 64, F32, "default", 6),         # the same on the linear learner
+    (SWIGLU, 1, 1, 512, 256, 512, 256, BF16, "nearunit", 6),   # the same on the 256-tile path
 ])
 def test_post_chunk_row_normalisation_forward(kind, B, H, L, d, h, C, io, regime, flags):
     """Rows of the fast weights divided by their L2 norm after every chunk

@@ -350,7 +350,7 @@ def main():
                          "many MiB 5 times (the known-size reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the (batch, head) units would shard across GPUs with no communication); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)

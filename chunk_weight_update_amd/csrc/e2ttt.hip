@@ -760,8 +760,7 @@ e2ttt_status e2ttt_decode_workspace_bytes(const e2ttt_problem* prob, size_t* byt
   if (!bytes) return E2TTT_EINVAL;
   const e2ttt_status st = check_problem(prob);
   if (st != E2TTT_OK) return st;
-  if (prob->flags & (E2TTT_FLAG_CHUNK_AVERAGED_DECAY | E2TTT_FLAG_POST_CHUNK_ROW_L2))
-    return E2TTT_EUNSUPPORTED;
+  if (prob->flags & E2TTT_FLAG_CHUNK_AVERAGED_DECAY) return E2TTT_EUNSUPPORTED;
   const int64_t h = prob->kind == E2TTT_LINEAR ? 0 : prob->hidden;
   *bytes = decode_ws_total(prob, prob->batch * prob->heads, prob->dim, h);
   return E2TTT_OK;
@@ -774,8 +773,7 @@ e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* q, const v
                                void* stream) {
   e2ttt_status st = check_problem(prob);
   if (st != E2TTT_OK) return st;
-  if (prob->flags & (E2TTT_FLAG_CHUNK_AVERAGED_DECAY | E2TTT_FLAG_POST_CHUNK_ROW_L2))
-    return E2TTT_EUNSUPPORTED;
+  if (prob->flags & E2TTT_FLAG_CHUNK_AVERAGED_DECAY) return E2TTT_EUNSUPPORTED;
   const int64_t BH = prob->batch * prob->heads, d = prob->dim;
   const int64_t h = prob->kind == E2TTT_LINEAR ? 0 : prob->hidden;
   const int64_t P = h == 0 ? d * d : 3 * d * h;
@@ -838,6 +836,13 @@ e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* q, const v
                          static_cast<const float*>(part));
     }
     hipLaunchKernelGGL(k_dec_update<T>, dim3(gu), dim3(256), 0, s, a, K);
+    if (chunk_end && (prob->flags & E2TTT_FLAG_POST_CHUNK_ROW_L2)) {
+      // chunk boundary: rows of W normalised, then W0 <- W again
+      const int64_t rows = BH * (h == 0 ? d : 2 * h + d);
+      hipLaunchKernelGGL(k_row_l2norm, dim3(grid1((rows + 3) / 4)), dim3(256), 0, s, W, BH, d, h);
+      hipLaunchKernelGGL(k_copy_or_zero, dim3(grid1((BH * P + 255) / 256)), dim3(256), 0, s,
+                         static_cast<const float*>(W), W0, BH * P);
+    }
   };
   if (prob->io_dtype == E2TTT_BF16) run(bf16_t{});
   else run(float{});

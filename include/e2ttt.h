@@ -105,8 +105,8 @@ enum {
    * SwiGLU W1, W3, W2, rows as stored) is divided by max(||row||_2, 1e-12),
    * in fp32 with a fixed summation order.  M is not changed.  The next
    * chunk's readout and descent directions use the normalised W.  Applies to
-   * e2ttt_chunk_forward and its timed twin; e2ttt_decode_step and
-   * e2ttt_chunk_backward return EUNSUPPORTED for it. */
+   * e2ttt_chunk_forward, its timed twin and e2ttt_decode_step (at a call with
+   * chunk_end set); e2ttt_chunk_backward returns EUNSUPPORTED for it. */
   E2TTT_FLAG_POST_CHUNK_ROW_L2 = 8u
 };
 

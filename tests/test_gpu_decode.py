@@ -75,3 +75,27 @@ def test_decode_with_qk_prologue():
     e = (rel_fro(out, ro), rel_fro(W, rW), rel_fro(M, rM))
     log(f"  rel_fro out={e[0]:.3e} W={e[1]:.3e} M={e[2]:.3e}")
     assert e[0] <= 1e-2 and e[1] <= 5e-3 and e[2] <= 5e-3, e
+
+
+@pytest.mark.parametrize("kind,B,H,L,d,h,C,io,regime", [
+    (LINEAR, 1, 2, 40, 64, 0, 16, F32, "default"),
+    (SWIGLU, 2, 2, 40, 128, 256, 16, BF16, "nearunit"),     # ragged
+])
+def test_decode_with_row_normalisation(kind, B, H, L, d, h, C, io, regime):
+    """Chunk-boundary row normalisation at every call with chunk_end set,
+    against the oracle's chunk forward with the same option."""
+    import chunk_weight_update_amd as cwu
+    import oracle
+    log(f"decode with row normalisation kind={kind} B={B} H={H} L={L} C={C} io={io}")
+    inp = make_inputs(kind, B, H, L, d, h, io, seed=15, regime=regime,
+                      m0_scale=1e-6 if regime == "nearunit" else 0.01)
+    prob = problem_for(kind, B, H, L, d, h, C, io, 0, cwu.FLAG_POST_CHUNK_ROW_L2)
+    out, W, M, W0 = run_decode(prob, to_device(inp, io), L, C)
+    ro, rW, rM = oracle.chunk_forward(kind, inp["q64"], inp["k64"], inp["v64"], inp["eta"],
+                                      inp["alpha"], inp["beta"], inp["W0"], inp["M0"], C, h,
+                                      row_norm=True)
+    e = (rel_fro(out, ro), rel_fro(W, rW), rel_fro(M, rM))
+    log(f"  rel_fro out={e[0]:.3e} W={e[1]:.3e} M={e[2]:.3e}")
+    t = TOL[io]
+    assert e[0] <= t[0] and e[1] <= t[1] and e[2] <= t[2], e
+    assert np.array_equal(W0, W)

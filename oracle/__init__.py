@@ -75,7 +75,7 @@ def _load():
             lib.oracle_scalar_kernels.argtypes = [ctypes.c_int, i64, i64] + [P] * 6 + [ctypes.c_int]
             lib.oracle_scalar_kernels.restype = ctypes.c_int
             lib.oracle_chunk_backward.argtypes = (
-                [ctypes.c_int, ctypes.c_int] + [i64] * 5 + [P] * 19)
+                [ctypes.c_int, ctypes.c_int] + [i64] * 6 + [P] * 19)
             lib.oracle_chunk_backward.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -175,8 +175,8 @@ def scalar_kernels(eta, alpha, beta, decay_mode=GAMMA_1_MINUS_ETA_ALPHA, average
 
 
 def chunk_backward(kind, q, k, v, eta, alpha, beta, W0, M0, dout, dWend, dMend, chunk,
-                   decay_mode=GAMMA_1_MINUS_ETA_ALPHA):
-    """Reverse mode of ``chunk_forward`` (linear learner): gradients of
+                   decay_mode=GAMMA_1_MINUS_ETA_ALPHA, hidden=0):
+    """Reverse mode of ``chunk_forward`` (linear and SwiGLU learners): gradients of
     <dout, out> + <dWend, Wend> + <dMend, Mend> with respect to every input.
     dWend / dMend may be None (zero).  Returns a dict with keys q, k, v, eta,
     alpha, beta, W0, M0 (float64 arrays of the inputs' shapes)."""
@@ -185,7 +185,7 @@ def chunk_backward(kind, q, k, v, eta, alpha, beta, W0, M0, dout, dWend, dMend, 
     eta, alpha, beta = _f64(eta), _f64(alpha), _f64(beta)
     W0, M0, dout = _f64(W0), _f64(M0), _f64(dout)
     B, H, L, d = q.shape
-    P = state_size(kind, d, 0)
+    P = state_size(kind, d, hidden)
     assert k.shape == q.shape and v.shape == q.shape and dout.shape == q.shape
     assert eta.shape == (B, H, L) and alpha.shape == (B, H, L) and beta.shape == (B, H, L)
     assert W0.shape == (B, H, P) and M0.shape == (B, H, P)
@@ -196,7 +196,7 @@ def chunk_backward(kind, q, k, v, eta, alpha, beta, W0, M0, dout, dWend, dMend, 
          (("q", q), ("k", k), ("v", v), ("eta", eta), ("alpha", alpha), ("beta", beta),
           ("W0", W0), ("M0", M0))}
     rc = lib.oracle_chunk_backward(
-        kind, decay_mode, B, H, L, d, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
+        kind, decay_mode, B, H, L, d, hidden, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
         _ptr(alpha), _ptr(beta), _ptr(W0), _ptr(M0), _ptr(dout),
         _ptr(dWp) if dWp is not None else null, _ptr(dMp) if dMp is not None else null,
         _ptr(g["q"]), _ptr(g["k"]), _ptr(g["v"]), _ptr(g["eta"]), _ptr(g["alpha"]),

@@ -463,34 +463,214 @@ int oracle_scalar_kernels(int decay_mode, int64_t nseg, int64_t n,
 }
 
 /*
- * Reverse mode of the chunk forward for the linear learner (the outer-loop
- * backward): the gradient of a scalar loss
+ * Reverse mode of G = descent(Ws; k, v) for one token: given the adjoint dG
+ * (P entries, packed as the state), adds the contributions to dk, dv and dWs.
+ * It walks the steps of descent_factors backwards:
+ *   linear : e = v - Ws k,  G = e k^T
+ *            de = dG k,  dk += dG^T e - Ws^T de,  dv += de,  dWs -= de k^T
+ *   SwiGLU : a1 = W1 k, a3 = W3 k, z = silu(a1) a3, e = v - W2 z, w = W2^T e,
+ *            u1 = w a3 silu'(a1), u3 = w silu(a1),
+ *            G1 = u1 k^T, G3 = u3 k^T, G2 = e z^T;
+ *            each intermediate's adjoint is the sum over its uses, with
+ *            silu''(a) = s (1 - s) (2 + a (1 - 2 s)), s = sigma(a).
+ * scratch holds at least 16 h + 4 d doubles.
+ */
+static void descent_vjp(int kind, int64_t d, int64_t h, const double* Ws,
+                        const double* k, const double* v, const double* dG,
+                        double* dk, double* dv, double* dWs, double* scratch) {
+  if (kind == OR_LINEAR) {
+    double* e = scratch;
+    double* de = scratch + d;
+    for (int64_t i = 0; i < d; ++i) {
+      double y = 0.0;
+      for (int64_t j = 0; j < d; ++j) y += Ws[i * d + j] * k[j];
+      e[i] = v[i] - y;
+      double s = 0.0;
+      for (int64_t j = 0; j < d; ++j) s += dG[i * d + j] * k[j];
+      de[i] = s;
+    }
+    for (int64_t j = 0; j < d; ++j) {
+      double s1 = 0.0, s2 = 0.0;
+      for (int64_t i = 0; i < d; ++i) {
+        s1 += dG[i * d + j] * e[i];
+        s2 += Ws[i * d + j] * de[i];
+      }
+      dk[j] += s1 - s2;
+    }
+    for (int64_t i = 0; i < d; ++i) {
+      dv[i] += de[i];
+      for (int64_t j = 0; j < d; ++j) dWs[i * d + j] -= de[i] * k[j];
+    }
+    return;
+  }
+  const double* W1 = Ws;
+  const double* W3 = Ws + h * d;
+  const double* W2 = Ws + 2 * h * d;
+  const double* D1 = dG;
+  const double* D3 = dG + h * d;
+  const double* D2 = dG + 2 * h * d;
+  double* dW1 = dWs;
+  double* dW3 = dWs + h * d;
+  double* dW2 = dWs + 2 * h * d;
+  double *a1 = scratch, *a3 = a1 + h, *z = a3 + h, *w = z + h, *sl = w + h,
+         *sp = sl + h, *spp = sp + h, *u1 = spp + h, *u3 = u1 + h, *du1 = u3 + h,
+         *du3 = du1 + h, *dz = du3 + h, *dw = dz + h, *da1 = dw + h, *da3 = da1 + h;
+  double *y = scratch + 16 * h, *e = y + d, *de = e + d;
+  fast_forward(OR_SWIGLU, d, h, Ws, k, a1, a3, z, y);
+  for (int64_t o = 0; o < d; ++o) e[o] = v[o] - y[o];
+  for (int64_t i = 0; i < h; ++i) {
+    double s = 0.0;
+    for (int64_t o = 0; o < d; ++o) s += W2[o * h + i] * e[o];
+    w[i] = s;
+    const double sg = sigm(a1[i]);
+    sl[i] = a1[i] * sg;
+    sp[i] = sg * (1.0 + a1[i] * (1.0 - sg));
+    spp[i] = sg * (1.0 - sg) * (2.0 + a1[i] * (1.0 - 2.0 * sg));
+    u1[i] = w[i] * a3[i] * sp[i];
+    u3[i] = w[i] * sl[i];
+  }
+  /* G1 = u1 k^T, G3 = u3 k^T */
+  for (int64_t i = 0; i < h; ++i) {
+    double s1 = 0.0, s3 = 0.0;
+    for (int64_t j = 0; j < d; ++j) {
+      s1 += D1[i * d + j] * k[j];
+      s3 += D3[i * d + j] * k[j];
+    }
+    du1[i] = s1;
+    du3[i] = s3;
+  }
+  for (int64_t j = 0; j < d; ++j) {
+    double s = 0.0;
+    for (int64_t i = 0; i < h; ++i) s += D1[i * d + j] * u1[i] + D3[i * d + j] * u3[i];
+    dk[j] += s;
+  }
+  /* G2 = e z^T */
+  for (int64_t o = 0; o < d; ++o) {
+    double s = 0.0;
+    for (int64_t i = 0; i < h; ++i) s += D2[o * h + i] * z[i];
+    de[o] = s;
+  }
+  for (int64_t i = 0; i < h; ++i) {
+    double s = 0.0;
+    for (int64_t o = 0; o < d; ++o) s += D2[o * h + i] * e[o];
+    dz[i] = s;
+  }
+  /* u1 = w a3 silu'(a1), u3 = w silu(a1) */
+  for (int64_t i = 0; i < h; ++i) {
+    dw[i] = du3[i] * sl[i] + du1[i] * a3[i] * sp[i];
+    da1[i] = du3[i] * w[i] * sp[i] + du1[i] * w[i] * a3[i] * spp[i];
+    da3[i] = du1[i] * w[i] * sp[i];
+  }
+  /* w = W2^T e */
+  for (int64_t o = 0; o < d; ++o) {
+    double s = 0.0;
+    for (int64_t i = 0; i < h; ++i) {
+      s += W2[o * h + i] * dw[i];
+      dW2[o * h + i] += e[o] * dw[i];
+    }
+    de[o] += s;
+  }
+  /* e = v - y, y = W2 z */
+  for (int64_t o = 0; o < d; ++o) {
+    dv[o] += de[o];
+    for (int64_t i = 0; i < h; ++i) dW2[o * h + i] -= de[o] * z[i];
+  }
+  for (int64_t i = 0; i < h; ++i) {
+    double s = 0.0;
+    for (int64_t o = 0; o < d; ++o) s += W2[o * h + i] * de[o];
+    dz[i] -= s;
+  }
+  /* z = silu(a1) a3, a1 = W1 k, a3 = W3 k */
+  for (int64_t i = 0; i < h; ++i) {
+    da1[i] += dz[i] * a3[i] * sp[i];
+    da3[i] += dz[i] * sl[i];
+    for (int64_t j = 0; j < d; ++j) {
+      dW1[i * d + j] += da1[i] * k[j];
+      dW3[i * d + j] += da3[i] * k[j];
+    }
+  }
+  for (int64_t j = 0; j < d; ++j) {
+    double s = 0.0;
+    for (int64_t i = 0; i < h; ++i) s += W1[i * d + j] * da1[i] + W3[i * d + j] * da3[i];
+    dk[j] += s;
+  }
+}
+
+/* Reverse mode of the readout o = f_Ws(x): adds the contributions of the
+ * output adjoint dy to dx and dWs.  scratch holds at least 8 h + d doubles. */
+static void readout_vjp(int kind, int64_t d, int64_t h, const double* Ws,
+                        const double* x, const double* dy, double* dx, double* dWs,
+                        double* scratch) {
+  if (kind == OR_LINEAR) {
+    for (int64_t j = 0; j < d; ++j) {
+      double s = 0.0;
+      for (int64_t i = 0; i < d; ++i) s += Ws[i * d + j] * dy[i];
+      dx[j] += s;
+    }
+    for (int64_t i = 0; i < d; ++i)
+      for (int64_t j = 0; j < d; ++j) dWs[i * d + j] += dy[i] * x[j];
+    return;
+  }
+  const double* W1 = Ws;
+  const double* W3 = Ws + h * d;
+  const double* W2 = Ws + 2 * h * d;
+  double* dW1 = dWs;
+  double* dW3 = dWs + h * d;
+  double* dW2 = dWs + 2 * h * d;
+  double *a1 = scratch, *a3 = a1 + h, *z = a3 + h, *dz = z + h, *da1 = dz + h,
+         *da3 = da1 + h, *y = scratch + 8 * h;
+  fast_forward(OR_SWIGLU, d, h, Ws, x, a1, a3, z, y);
+  for (int64_t i = 0; i < h; ++i) {
+    double s = 0.0;
+    for (int64_t o = 0; o < d; ++o) s += W2[o * h + i] * dy[o];
+    dz[i] = s;
+    const double sg = sigm(a1[i]);
+    da1[i] = s * a3[i] * (sg * (1.0 + a1[i] * (1.0 - sg)));
+    da3[i] = s * (a1[i] * sg);
+  }
+  for (int64_t o = 0; o < d; ++o)
+    for (int64_t i = 0; i < h; ++i) dW2[o * h + i] += dy[o] * z[i];
+  for (int64_t i = 0; i < h; ++i)
+    for (int64_t j = 0; j < d; ++j) {
+      dW1[i * d + j] += da1[i] * x[j];
+      dW3[i * d + j] += da3[i] * x[j];
+    }
+  for (int64_t j = 0; j < d; ++j) {
+    double s = 0.0;
+    for (int64_t i = 0; i < h; ++i) s += W1[i * d + j] * da1[i] + W3[i * d + j] * da3[i];
+    dx[j] += s;
+  }
+}
+
+/*
+ * Reverse mode of the chunk forward (the outer-loop backward), linear and
+ * SwiGLU learners: the gradient of a scalar loss
  *     l = <dout, out> + <dWend, Wend> + <dMend, Mend>
  * with respect to every input of oracle_chunk_forward.  It differentiates the
  * same literal recurrence, one token at a time in reverse:
  *   - the chunk-start states (W, M) of every chunk are recorded by a forward
  *     pass; each chunk is re-run to record the state before each token;
  *   - token t of a chunk with frozen weights Ws did
- *         e = v_t - Ws k_t,  G = e k_t^T,
+ *         G = descent(Ws; k_t, v_t),
  *         M <- beta_t M + eta_t G,  W <- gamma_t W + M,
  *     so with (dW, dM) the adjoint of the state after the token:
  *         dMt    = dM + dW                      (W used the new M)
  *         dgamma = <dW, W_before>,  dbeta = <dMt, M_before>
  *         deta  += <dMt, G>,        dG = eta_t dMt
- *         de = dG k_t,  dk_t += dG^T e - Ws^T de,  dv_t += de,
- *         dWs   -= de k_t^T
+ *         (dk_t, dv_t, dWs) += reverse mode of descent at dG (descent_vjp)
  *         dW <- gamma_t dW,  dM <- beta_t dMt;
- *   - the readout o_t = Ws q_t adds dq_t = Ws^T do_t and dWs += do_t q_t^T;
+ *   - the readout o_t = f_Ws(q_t) adds its reverse mode to dq_t and dWs;
  *   - Ws is the state at the chunk start, so dW += dWs before the previous
  *     chunk is processed;
  *   - gamma_t = 1 - eta_t alpha_t (Eq. 14): deta_t -= alpha_t dgamma,
  *     dalpha_t = -eta_t dgamma; with alpha taken as gamma, dalpha_t = dgamma.
- * The chunk-averaged variant and the q/k prologue are not covered.
- * dWend or dMend may be NULL (zero).  Returns 0 on success, 1 on bad
- * arguments, 2 on allocation failure, 3 for a learner other than linear.
+ * The chunk-averaged variant and the q/k and row-normalisation options are
+ * not covered.  dWend or dMend may be NULL (zero).  h is the SwiGLU hidden
+ * width (ignored for linear).  Returns 0 on success, 1 on bad arguments,
+ * 2 on allocation failure, 3 for an unknown learner.
  */
 int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
-                          int64_t L, int64_t d, int64_t C,
+                          int64_t L, int64_t d, int64_t h, int64_t C,
                           const double* q, const double* k, const double* v,
                           const double* eta, const double* alpha,
                           const double* beta, const double* W0,
@@ -499,14 +679,16 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
                           double* dq, double* dk, double* dv, double* deta,
                           double* dalpha, double* dbeta, double* dW0,
                           double* dM0) {
-  if (kind != OR_LINEAR) return 3;
+  if (kind != OR_LINEAR && kind != OR_SWIGLU) return 3;
   if (decay_mode != OR_GAMMA_1_MINUS_ETA_ALPHA &&
       decay_mode != OR_ALPHA_IS_GAMMA)
     return 1;
   if (B < 0 || H < 0 || L < 0 || d <= 0 || C <= 0) return 1;
-  const int64_t P = d * d;
+  if (kind == OR_SWIGLU && h <= 0) return 1;
+  const int64_t P = state_size(kind, d, h);
   const int64_t nC = (L + C - 1) / C;
   const int64_t Cmax = C < L ? C : (L > 0 ? L : 1);
+  const int64_t nscr = 16 * (kind == OR_LINEAR ? 1 : h) + 4 * d;
 
   for (int64_t u = 0; u < B * H; ++u) {
     const double* qu = q + u * L * d;
@@ -529,17 +711,19 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
     double* Mst = (double*)malloc(sizeof(double) * (size_t)((nC > 0 ? nC : 1) * P));
     double* Wb = (double*)malloc(sizeof(double) * (size_t)(Cmax * P));
     double* Mb = (double*)malloc(sizeof(double) * (size_t)(Cmax * P));
-    double* e = (double*)malloc(sizeof(double) * (size_t)(Cmax * d));
+    double* Gt = (double*)malloc(sizeof(double) * (size_t)(Cmax * P));
     double* W = (double*)malloc(sizeof(double) * (size_t)P);
     double* M = (double*)malloc(sizeof(double) * (size_t)P);
     double* dW = (double*)malloc(sizeof(double) * (size_t)P);
     double* dM = (double*)malloc(sizeof(double) * (size_t)P);
     double* dMt = (double*)malloc(sizeof(double) * (size_t)P);
+    double* dG = (double*)malloc(sizeof(double) * (size_t)P);
     double* dWs = (double*)malloc(sizeof(double) * (size_t)P);
-    double* de = (double*)malloc(sizeof(double) * (size_t)d);
-    if (!Wst || !Mst || !Wb || !Mb || !e || !W || !M || !dW || !dM || !dMt || !dWs || !de) {
-      free(Wst); free(Mst); free(Wb); free(Mb); free(e); free(W); free(M);
-      free(dW); free(dM); free(dMt); free(dWs); free(de);
+    double* scr = (double*)malloc(sizeof(double) * (size_t)nscr);
+    if (!Wst || !Mst || !Wb || !Mb || !Gt || !W || !M || !dW || !dM || !dMt || !dG ||
+        !dWs || !scr) {
+      free(Wst); free(Mst); free(Wb); free(Mb); free(Gt); free(W); free(M);
+      free(dW); free(dM); free(dMt); free(dG); free(dWs); free(scr);
       return 2;
     }
 
@@ -554,14 +738,10 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
       for (int64_t t = 0; t < n; ++t) {
         const int64_t tt = t0 + t;
         const double g = decay_factor(decay_mode, etu[tt], alu[tt]);
-        for (int64_t i = 0; i < d; ++i) {
-          double y = 0.0;
-          for (int64_t j = 0; j < d; ++j) y += Ws[i * d + j] * ku[tt * d + j];
-          const double ei = vu[tt * d + i] - y;
-          for (int64_t j = 0; j < d; ++j) {
-            M[i * d + j] = beu[tt] * M[i * d + j] + etu[tt] * (ei * ku[tt * d + j]);
-            W[i * d + j] = g * W[i * d + j] + M[i * d + j];
-          }
+        oracle_token_descent(kind, d, h, Ws, ku + tt * d, vu + tt * d, Gt);
+        for (int64_t i = 0; i < P; ++i) {
+          M[i] = beu[tt] * M[i] + etu[tt] * Gt[i];
+          W[i] = g * W[i] + M[i];
         }
       }
     }
@@ -574,7 +754,7 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
     for (int64_t r = nC - 1; r >= 0; --r) {
       const int64_t t0 = r * C, n = (L - t0) < C ? (L - t0) : C;
       const double* Ws = Wst + r * P;
-      /* Re-run the chunk, recording the state before each token. */
+      /* Re-run the chunk, recording the state before each token and G. */
       memcpy(W, Ws, sizeof(double) * (size_t)P);
       memcpy(M, Mst + r * P, sizeof(double) * (size_t)P);
       for (int64_t t = 0; t < n; ++t) {
@@ -582,14 +762,11 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
         const double g = decay_factor(decay_mode, etu[tt], alu[tt]);
         memcpy(Wb + t * P, W, sizeof(double) * (size_t)P);
         memcpy(Mb + t * P, M, sizeof(double) * (size_t)P);
-        for (int64_t i = 0; i < d; ++i) {
-          double y = 0.0;
-          for (int64_t j = 0; j < d; ++j) y += Ws[i * d + j] * ku[tt * d + j];
-          e[t * d + i] = vu[tt * d + i] - y;
-          for (int64_t j = 0; j < d; ++j) {
-            M[i * d + j] = beu[tt] * M[i * d + j] + etu[tt] * (e[t * d + i] * ku[tt * d + j]);
-            W[i * d + j] = g * W[i * d + j] + M[i * d + j];
-          }
+        double* G = Gt + t * P;
+        oracle_token_descent(kind, d, h, Ws, ku + tt * d, vu + tt * d, G);
+        for (int64_t i = 0; i < P; ++i) {
+          M[i] = beu[tt] * M[i] + etu[tt] * G[i];
+          W[i] = g * W[i] + M[i];
         }
       }
       for (int64_t i = 0; i < P; ++i) dWs[i] = 0.0;
@@ -597,32 +774,17 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
         const int64_t tt = t0 + t;
         const double et = etu[tt];
         const double g = decay_factor(decay_mode, et, alu[tt]);
-        const double* kt = ku + tt * d;
-        const double* ev = e + t * d;
+        const double* G = Gt + t * P;
         double dgam = 0.0, dbet = 0.0, detd = 0.0;
         for (int64_t i = 0; i < P; ++i) {
           dMt[i] = dM[i] + dW[i];
           dgam += dW[i] * Wb[t * P + i];
           dbet += dMt[i] * Mb[t * P + i];
+          detd += dMt[i] * G[i];
+          dG[i] = et * dMt[i];
         }
-        for (int64_t i = 0; i < d; ++i) {
-          double s = 0.0; /* (dMt k)_i */
-          for (int64_t j = 0; j < d; ++j) s += dMt[i * d + j] * kt[j];
-          detd += ev[i] * s;
-          de[i] = et * s;
-        }
-        for (int64_t j = 0; j < d; ++j) {
-          double s1 = 0.0, s2 = 0.0; /* (dMt^T e)_j and (Ws^T de)_j */
-          for (int64_t i = 0; i < d; ++i) {
-            s1 += dMt[i * d + j] * ev[i];
-            s2 += Ws[i * d + j] * de[i];
-          }
-          dku[tt * d + j] += et * s1 - s2;
-        }
-        for (int64_t i = 0; i < d; ++i) {
-          dvu[tt * d + i] += de[i];
-          for (int64_t j = 0; j < d; ++j) dWs[i * d + j] -= de[i] * kt[j];
-        }
+        descent_vjp(kind, d, h, Ws, ku + tt * d, vu + tt * d, dG, dku + tt * d,
+                    dvu + tt * d, dWs, scr);
         for (int64_t i = 0; i < P; ++i) {
           dW[i] = g * dW[i];
           dM[i] = beu[tt] * dMt[i];
@@ -636,23 +798,17 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
           dalu[tt] += dgam;
         }
       }
-      /* Readout o_t = Ws q_t. */
+      /* Readout o_t = f_Ws(q_t). */
       for (int64_t t = 0; t < n; ++t) {
         const int64_t tt = t0 + t;
-        for (int64_t j = 0; j < d; ++j) {
-          double s = 0.0;
-          for (int64_t i = 0; i < d; ++i) s += Ws[i * d + j] * dou[tt * d + i];
-          dqu[tt * d + j] += s;
-        }
-        for (int64_t i = 0; i < d; ++i)
-          for (int64_t j = 0; j < d; ++j) dWs[i * d + j] += dou[tt * d + i] * qu[tt * d + j];
+        readout_vjp(kind, d, h, Ws, qu + tt * d, dou + tt * d, dqu + tt * d, dWs, scr);
       }
       for (int64_t i = 0; i < P; ++i) dW[i] += dWs[i];
     }
     memcpy(dW0 + u * P, dW, sizeof(double) * (size_t)P);
     memcpy(dM0 + u * P, dM, sizeof(double) * (size_t)P);
-    free(Wst); free(Mst); free(Wb); free(Mb); free(e); free(W); free(M);
-    free(dW); free(dM); free(dMt); free(dWs); free(de);
+    free(Wst); free(Mst); free(Wb); free(Mb); free(Gt); free(W); free(M);
+    free(dW); free(dM); free(dMt); free(dG); free(dWs); free(scr);
   }
   return 0;
 }

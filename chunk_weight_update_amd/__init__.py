@@ -234,7 +234,8 @@ def chunk_backward(prob: Problem, q, k, v, eta, alpha, beta, W0, M0, dout, dW_en
                    dq, dk, dv, deta, dalpha, dbeta, dW0, dM0, workspace,
                    workspace_nbytes: Optional[int] = None, stream=None,
                    check: bool = True) -> int:
-    """Call ``e2ttt_chunk_backward`` (linear learner): gradients of a loss
+    """Call ``e2ttt_chunk_backward`` (linear and SwiGLU learners, fp32):
+    gradients of a loss
     with respect to every input of the chunk forward, given its gradients
     dout, dW_end, dM_end (the last two may be None).  Returns the status;
     raises on failure when ``check``."""

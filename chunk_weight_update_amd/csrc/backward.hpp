@@ -301,8 +301,8 @@ __global__ __launch_bounds__(64) void k_lin_bwd_scalars(Shape s, int mode, const
                                                         const float* __restrict__ sw,
                                                         const float* __restrict__ sm,
                                                         const float* __restrict__ dots,
-                                                        double* bcp, float* deta, float* dalpha,
-                                                        float* dbeta) {
+                                                        int nrb, double* bcp, float* deta,
+                                                        float* dalpha, float* dbeta) {
   const int64_t seg = blockIdx.x;
   const int64_t u = seg / s.nC;
   const int r = static_cast<int>(seg % s.nC);
@@ -353,7 +353,6 @@ __global__ __launch_bounds__(64) void k_lin_bwd_scalars(Shape s, int mode, const
   }
   __syncthreads();  // every lane's b, c, P written (read back below across lanes)
   // Chunk-coefficient adjoints: block partials added in block order.
-  const int nrb = static_cast<int>(s.d / 16);
   double dcW = 0.0, dcM = 0.0, dcWM = 0.0;
   for (int rb = 0; rb < nrb; ++rb) {
     dcW += dots[(seg * nrb + rb) * 4 + 0];

@@ -22,6 +22,7 @@
 #include "fused.hpp"
 #include "decode.hpp"
 #include "backward.hpp"
+#include "swiglu_backward.hpp"
 
 using namespace e2ttt;
 
@@ -860,10 +861,15 @@ struct BwdPlan {
   Plan f;
   size_t wst, mst;            // chunk-start states of chunks 1 .. nC-1 (slot r), [nC][BH][P]
   size_t dwa, dwb, dma, dmb;  // state adjoints, two of each in turn, [BH][P]
-  size_t de;                  // [BH][Cp][d]
+  size_t de;                  // linear: [BH][Cp][d]
   size_t sw, sm;              // dK^W, dK^M, [BH][nC][Cp]
-  size_t dots;                // [BH][nC][d/16][4]
+  size_t dots;                // [BH][nC][nrb][4]
   size_t bcp;                 // fp64 b, c, P, [BH][nC][Cp][3]
+  int64_t nrb;                // partial-sum blocks of the chunk-coefficient dots
+  // SwiGLU, one chunk at a time, token-major [BH][Cp][width]:
+  size_t hk, hq, tw, tm, du, uw, um, da, daq;  // width 2h
+  size_t zk, zq, wv, dzq, r2w, r2m, dwv, dza;  // width h
+  size_t e, s2w, s2m, dea;                     // width d
   size_t total;
 };
 
@@ -871,24 +877,240 @@ e2ttt_status make_bwd_plan(const e2ttt_problem* p, BwdPlan* bp) {
   const e2ttt_status st = make_plan(p, &bp->f);
   if (st != E2TTT_OK) return st;
   const Plan& q = bp->f;
-  if (q.kind != E2TTT_LINEAR || q.io != E2TTT_F32 || p->flags != 0u || q.d > 64)
-    return E2TTT_EUNSUPPORTED;
+  if (q.io != E2TTT_F32 || p->flags != 0u) return E2TTT_EUNSUPPORTED;
+  if (q.kind == E2TTT_LINEAR && q.d > 64) return E2TTT_EUNSUPPORTED;
+  if (q.kind == E2TTT_SWIGLU && q.BH > 65535) return E2TTT_EUNSUPPORTED;  // grid z
   size_t o = align256(q.total);
   auto take = [&](size_t bytes) { const size_t at = o; o = align256(o + bytes); return at; };
   const size_t np = 4 * static_cast<size_t>(q.BH * q.P);
+  bp->nrb = q.kind == E2TTT_LINEAR ? q.d / 16 : (q.P + SWB_STATE_ELEMS - 1) / SWB_STATE_ELEMS;
   bp->wst = take(np * q.nC);
   bp->mst = take(np * q.nC);
   bp->dwa = take(np);
   bp->dwb = take(np);
   bp->dma = take(np);
   bp->dmb = take(np);
-  bp->de = take(4 * static_cast<size_t>(q.BH * q.Cp * q.d));
   bp->sw = take(4 * static_cast<size_t>(q.BH * q.nC * q.Cp));
   bp->sm = take(4 * static_cast<size_t>(q.BH * q.nC * q.Cp));
-  bp->dots = take(4 * static_cast<size_t>(q.BH * q.nC * (q.d / 16) * 4));
+  bp->dots = take(4 * static_cast<size_t>(q.BH * q.nC * bp->nrb * 4));
   bp->bcp = take(8 * static_cast<size_t>(q.BH * q.nC * q.Cp * 3));
+  const size_t rows = 4 * static_cast<size_t>(q.BH * q.Cp);
+  if (q.kind == E2TTT_LINEAR) {
+    bp->de = take(rows * q.d);
+  } else {
+    for (size_t* b : {&bp->hk, &bp->hq, &bp->tw, &bp->tm, &bp->du, &bp->uw, &bp->um, &bp->da,
+                      &bp->daq})
+      *b = take(rows * 2 * q.h);
+    for (size_t* b : {&bp->zk, &bp->zq, &bp->wv, &bp->dzq, &bp->r2w, &bp->r2m, &bp->dwv,
+                      &bp->dza})
+      *b = take(rows * q.h);
+    for (size_t* b : {&bp->e, &bp->s2w, &bp->s2m, &bp->dea}) *b = take(rows * q.d);
+  }
   bp->total = q.L == 0 ? 0 : o;
   return E2TTT_OK;
+}
+
+// Batched fp32 GEMM over the BH units (grid z).
+void gemm_f32(const GemmF32& g, int64_t BH, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0) return;
+  const dim3 grid(static_cast<unsigned>((g.N + GF_T - 1) / GF_T),
+                  static_cast<unsigned>((g.M + GF_T - 1) / GF_T), static_cast<unsigned>(BH));
+  hipLaunchKernelGGL(k_gemm_f32, grid, dim3(256), 0, s, g);
+}
+
+GemmF32 gf(int64_t M, int64_t N, int64_t K, const float* A, int64_t sAb, int64_t sAm,
+           int64_t sAk, const float* B, int64_t sBb, int64_t sBk, int64_t sBn, const float* D,
+           int64_t sDb, int64_t ldd, float* C, int64_t sCb, int64_t ldc, float alpha = 1.0f) {
+  return GemmF32{M, N, K, A, sAb, sAm, sAk, B, sBb, sBk, sBn, D, sDb, ldd, C, sCb, ldc, alpha};
+}
+
+// The SwiGLU learner's backward (fp32): forward re-run for the chunk-start
+// states, then the chunks in reverse, each as the GEMMs and per-token steps
+// listed in swiglu_backward.hpp.  The scalar kernels, the chunk
+// coefficients and the adjoint buffers are set up by the caller.
+void swiglu_backward(const BwdPlan& bp, char* ws, const float* Q, const float* K,
+                     const float* V, const float* W0, const float* M0, const float* DO,
+                     const float* dWC, const float* dMC, float* dq, float* dk, float* dv,
+                     float* dW0, float* dM0, hipStream_t s) {
+  const Plan& q = bp.f;
+  auto wsf = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  const Shape sh{q.BH, q.L, q.d, q.h, q.C, q.Cp, q.nC, q.krep};
+  const int64_t BH = q.BH, L = q.L, d = q.d, h = q.h, Cp = q.Cp, P = q.P, nP = BH * P;
+  const int64_t Ld = L * d;
+  float* kw = wsf(q.kw);
+  float* km = wsf(q.km);
+  float* coef = wsf(q.coef);
+  auto Wst = [&](int64_t r) -> float* { return wsf(bp.wst) + r * nP; };
+  auto Mst = [&](int64_t r) -> float* { return wsf(bp.mst) + r * nP; };
+  auto Win = [&](int64_t r) -> const float* { return r == 0 ? W0 : Wst(r); };
+  auto Min = [&](int64_t r) -> const float* { return r == 0 ? M0 : Mst(r); };
+  // Forward re-run (the generic chunk kernels; the readout goes to dq, which
+  // the backward overwrites for every token).
+  {
+    float* kt = wsf(q.kt);
+    float* w13s = wsf(q.w13s);
+    float* w2s = wsf(q.w2s);
+    float* w2ts = wsf(q.w2ts);
+    float* zrow = wsf(q.zrow);
+    float* a1s = wsf(q.a1s);
+    float* a3s = wsf(q.a3s);
+    float* grow = wsf(q.grow);
+    float* ut = wsf(q.ut);
+    float* gt = wsf(q.gt);
+    float* zt = wsf(q.zt);
+    if (q.nC > 1) {
+      hipLaunchKernelGGL((k_prep_kt<float, false>),
+                         dim3(grid1(BH * q.nC * (Cp / 64) * (d / 64))), dim3(256), 0, s, sh, K, kt);
+      hipLaunchKernelGGL(k_prep_shadow<float>, dim3(grid1(shadow_blocks(sh))), dim3(256), 0, s,
+                         sh, W0, w13s, w2s, w2ts);
+    }
+    const int64_t na = (4 * h / 128) * (d / 128), nb = (2 * d / 128) * (h / 128);
+    for (int64_t r = 0; r + 1 < q.nC; ++r) {
+      const int ri = static_cast<int>(r);
+      hipLaunchKernelGGL(k_fwd13<float>, dim3(grid1(BH * (2 * Cp / 128) * (2 * h / 128))),
+                         dim3(256), 0, s, sh, ri, Q, K, w13s, zrow, a1s, a3s, zt);
+      hipLaunchKernelGGL(k_fwd2<float>, dim3(grid1(BH * (2 * Cp / 128) * (d / 128))), dim3(256),
+                         0, s, sh, ri, V, dq, zrow, w2s, kw, km, grow, gt);
+      hipLaunchKernelGGL(k_bwd<float>, dim3(grid1(BH * (Cp / 128) * (h / 128))), dim3(256), 0,
+                         s, sh, ri, grow, w2ts, a1s, a3s, kw, km, ut);
+      hipLaunchKernelGGL(k_agg<float>, dim3(grid1(BH * (na + nb))), dim3(256), 0, s, sh, ri, 0,
+                         ut, kt, gt, zt, coef, Win(r), Min(r), Wst(r + 1), Mst(r + 1), w13s,
+                         w2s, w2ts);
+    }
+  }
+  float *HK = wsf(bp.hk), *HQ = wsf(bp.hq), *TW = wsf(bp.tw), *TM = wsf(bp.tm),
+        *DU = wsf(bp.du), *UW = wsf(bp.uw), *UM = wsf(bp.um), *DA = wsf(bp.da),
+        *DAQ = wsf(bp.daq), *ZK = wsf(bp.zk), *ZQ = wsf(bp.zq), *WV = wsf(bp.wv),
+        *DZQ = wsf(bp.dzq), *R2W = wsf(bp.r2w), *R2M = wsf(bp.r2m), *DW = wsf(bp.dwv),
+        *DZA = wsf(bp.dza), *E = wsf(bp.e), *S2W = wsf(bp.s2w), *S2M = wsf(bp.s2m),
+        *DEA = wsf(bp.dea);
+  const int64_t b2 = Cp * 2 * h, b1 = Cp * h, bd = Cp * d;  // unit strides of the buffers
+  const int64_t o2 = 2 * h * d;                              // offset of W2 in a state
+  for (int64_t r = q.nC - 1; r >= 0; --r) {
+    const int ri = static_cast<int>(r);
+    const int64_t t0 = r * q.C, n = (L - t0) < q.C ? (L - t0) : q.C;
+    const float *Kr = K + t0 * d, *Qr = Q + t0 * d, *Vr = V + t0 * d, *DOr = DO + t0 * d;
+    float *dqr = dq + t0 * d, *dkr = dk + t0 * d, *dvr = dv + t0 * d;
+    const float* Ws = Win(r);
+    const float* Ms = Min(r);
+    float* dWp;
+    float* dMp;
+    if (r == 0) {
+      dWp = dW0;
+      dMp = dM0;
+    } else {
+      dWp = dWC == wsf(bp.dwa) ? wsf(bp.dwb) : wsf(bp.dwa);
+      dMp = dMC == wsf(bp.dma) ? wsf(bp.dmb) : wsf(bp.dma);
+    }
+    // Forward quantities at Ws.
+    gemm_f32(gf(n, 2 * h, d, Kr, Ld, d, 1, Ws, P, 1, d, nullptr, 0, 0, HK, b2, 2 * h), BH, s);
+    gemm_f32(gf(n, 2 * h, d, Qr, Ld, d, 1, Ws, P, 1, d, nullptr, 0, 0, HQ, b2, 2 * h), BH, s);
+    const unsigned gact = grid1((BH * n * h + 255) / 256);
+    hipLaunchKernelGGL(k_swb_act, dim3(gact), dim3(256), 0, s, BH, n, h, Cp, HK, ZK);
+    hipLaunchKernelGGL(k_swb_act, dim3(gact), dim3(256), 0, s, BH, n, h, Cp, HQ, ZQ);
+    gemm_f32(gf(n, d, h, ZK, b1, h, 1, Ws + o2, P, 1, h, Vr, Ld, d, E, bd, d, -1.0f), BH, s);
+    gemm_f32(gf(n, h, d, E, bd, d, 1, Ws + o2, P, h, 1, nullptr, 0, 0, WV, b1, h), BH, s);
+    gemm_f32(gf(n, h, d, DOr, Ld, d, 1, Ws + o2, P, h, 1, nullptr, 0, 0, DZQ, b1, h), BH, s);
+    // Products with the chunk-end adjoints.
+    gemm_f32(gf(n, 2 * h, d, Kr, Ld, d, 1, dWC, P, 1, d, nullptr, 0, 0, TW, b2, 2 * h), BH, s);
+    gemm_f32(gf(n, 2 * h, d, Kr, Ld, d, 1, dMC, P, 1, d, nullptr, 0, 0, TM, b2, 2 * h), BH, s);
+    gemm_f32(gf(n, d, h, ZK, b1, h, 1, dWC + o2, P, 1, h, nullptr, 0, 0, S2W, bd, d), BH, s);
+    gemm_f32(gf(n, d, h, ZK, b1, h, 1, dMC + o2, P, 1, h, nullptr, 0, 0, S2M, bd, d), BH, s);
+    gemm_f32(gf(n, h, d, E, bd, d, 1, dWC + o2, P, h, 1, nullptr, 0, 0, R2W, b1, h), BH, s);
+    gemm_f32(gf(n, h, d, E, bd, d, 1, dMC + o2, P, h, 1, nullptr, 0, 0, R2M, b1, h), BH, s);
+    if (n > 0) {
+      SwbTokArgs ta;
+      ta.n = n; ta.d = d; ta.h = h; ta.Cp = Cp; ta.nC = q.nC; ta.r = ri;
+      ta.HK = HK; ta.WV = WV; ta.E = E; ta.TW = TW; ta.TM = TM; ta.SW = S2W; ta.SM = S2M;
+      ta.RW = R2W; ta.RM = R2M; ta.kw = kw; ta.km = km;
+      ta.sw = wsf(bp.sw); ta.sm = wsf(bp.sm); ta.DU = DU; ta.DW = DW; ta.DEA = DEA;
+      ta.DZA = DZA; ta.UW = UW; ta.UM = UM;
+      hipLaunchKernelGGL(k_swb_tok, dim3(grid1(BH * n)), dim3(256), 0, s, ta);
+    }
+    // de (= dv) and dz.
+    gemm_f32(gf(n, d, h, DW, b1, h, 1, Ws + o2, P, 1, h, DEA, bd, d, dvr, Ld, d), BH, s);
+    gemm_f32(gf(n, h, d, dvr, Ld, d, 1, Ws + o2, P, h, 1, DZA, b1, h, DZA, b1, h, -1.0f), BH, s);
+    hipLaunchKernelGGL(k_swb_da, dim3(gact), dim3(256), 0, s, BH, n, h, Cp, HK, WV, DU, DZA,
+                       HQ, DZQ, DA, DAQ);
+    // dk, dq.
+    gemm_f32(gf(n, d, 2 * h, DA, b2, 2 * h, 1, Ws, P, d, 1, nullptr, 0, 0, dkr, Ld, d), BH, s);
+    gemm_f32(gf(n, d, 2 * h, UW, b2, 2 * h, 1, dWC, P, d, 1, dkr, Ld, d, dkr, Ld, d), BH, s);
+    gemm_f32(gf(n, d, 2 * h, UM, b2, 2 * h, 1, dMC, P, d, 1, dkr, Ld, d, dkr, Ld, d), BH, s);
+    gemm_f32(gf(n, d, 2 * h, DAQ, b2, 2 * h, 1, Ws, P, d, 1, nullptr, 0, 0, dqr, Ld, d), BH, s);
+    // Previous chunk's state adjoints: state terms, then the token sums.
+    hipLaunchKernelGGL(k_swb_state, dim3(grid1(BH * bp.nrb)), dim3(256), 0, s, P, bp.nrb, q.nC,
+                       ri, coef, Ws, Ms, dWC, dMC, dWp, dMp, wsf(bp.dots));
+    gemm_f32(gf(2 * h, d, n, DA, b2, 1, 2 * h, Kr, Ld, d, 1, dWp, P, d, dWp, P, d), BH, s);
+    gemm_f32(gf(2 * h, d, n, DAQ, b2, 1, 2 * h, Qr, Ld, d, 1, dWp, P, d, dWp, P, d), BH, s);
+    gemm_f32(gf(d, h, n, E, bd, 1, d, DW, b1, h, 1, dWp + o2, P, h, dWp + o2, P, h), BH, s);
+    gemm_f32(gf(d, h, n, dvr, Ld, 1, d, ZK, b1, h, 1, dWp + o2, P, h, dWp + o2, P, h, -1.0f),
+             BH, s);
+    gemm_f32(gf(d, h, n, DOr, Ld, 1, d, ZQ, b1, h, 1, dWp + o2, P, h, dWp + o2, P, h), BH, s);
+    dWC = dWp;
+    dMC = dMp;
+  }
+}
+
+// The linear learner's backward (fp32): forward re-run for the chunk-start
+// states, then the chunks in reverse (backward.hpp).
+void linear_backward(const BwdPlan& bp, char* ws, const float* Q, const float* K,
+                     const float* V, const float* W0, const float* M0, const float* DO,
+                     const float* dWC, const float* dMC, float* dq, float* dk, float* dv,
+                     float* dW0, float* dM0, hipStream_t s) {
+  const Plan& pl = bp.f;
+  auto wsf = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  const Shape sh{pl.BH, pl.L, pl.d, 0, pl.C, pl.Cp, pl.nC, 1};
+  const int64_t nP = pl.BH * pl.P;
+  float* kw = wsf(pl.kw);
+  float* km = wsf(pl.km);
+  float* coef = wsf(pl.coef);
+  // Forward re-run for the chunk-start states (the readout goes to dq, which
+  // the backward overwrites for every token).
+  auto Wst = [&](int64_t r) -> float* { return wsf(bp.wst) + r * nP; };
+  auto Mst = [&](int64_t r) -> float* { return wsf(bp.mst) + r * nP; };
+  auto Win = [&](int64_t r) -> const float* { return r == 0 ? W0 : Wst(r); };
+  auto Min = [&](int64_t r) -> const float* { return r == 0 ? M0 : Mst(r); };
+  const size_t lds_f = static_cast<size_t>(pl.d * (pl.d + 1) + LIN_FWD_TB * (pl.d + 1)) * sizeof(float);
+  const size_t lds_a = static_cast<size_t>(2 * 64 * 16 + 64 * pl.d) * sizeof(float);
+  for (int64_t r = 0; r + 1 < pl.nC; ++r) {
+    const int ri = static_cast<int>(r);
+    hipLaunchKernelGGL(k_lin_fwd<float>, dim3(grid1(pl.BH * (2 * pl.Cp / LIN_FWD_TB))), dim3(256), lds_f,
+                       s, sh, ri, Q, K, V, Win(r), kw, km, dq, wsf(pl.gw), wsf(pl.gm));
+    hipLaunchKernelGGL(k_lin_agg<float>, dim3(grid1(pl.BH * (pl.d / 16))), dim3(256), lds_a, s,
+                       sh, ri, K, wsf(pl.gw), wsf(pl.gm), coef, Win(r), Min(r), Wst(r + 1),
+                       Mst(r + 1));
+  }
+  // Reverse chunk loop.
+  const size_t lds_t = static_cast<size_t>(lin_bwd_tok_lds_floats(pl.d)) * sizeof(float);
+  const size_t lds_s = static_cast<size_t>(lin_bwd_state_lds_floats(pl.d)) * sizeof(float);
+  for (int64_t r = pl.nC - 1; r >= 0; --r) {
+    LinBwdArgs a;
+    a.s = sh;
+    a.r = static_cast<int>(r);
+    a.mode = pl.mode;
+    a.q = Q; a.k = K; a.v = V; a.dout = DO;
+    a.Ws = Win(r); a.Ms = Min(r);
+    a.dWC = dWC; a.dMC = dMC;
+    a.kw = kw; a.km = km; a.coef = coef;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.de = wsf(bp.de); a.sw = wsf(bp.sw); a.sm = wsf(bp.sm); a.dots = wsf(bp.dots);
+    if (r == 0) {
+      a.dWp = dW0;
+      a.dMp = dM0;
+    } else {
+      a.dWp = dWC == wsf(bp.dwa) ? wsf(bp.dwb) : wsf(bp.dwa);
+      a.dMp = dMC == wsf(bp.dma) ? wsf(bp.dmb) : wsf(bp.dma);
+    }
+    const int R = static_cast<int>(pl.d / 16);
+    void (*ktok)(LinBwdArgs) = R == 1 ? k_lin_bwd_tok<1> : R == 2 ? k_lin_bwd_tok<2>
+                               : R == 3 ? k_lin_bwd_tok<3> : k_lin_bwd_tok<4>;
+    void (*kst)(LinBwdArgs) = R == 1 ? k_lin_bwd_state<1> : R == 2 ? k_lin_bwd_state<2>
+                              : R == 3 ? k_lin_bwd_state<3> : k_lin_bwd_state<4>;
+    hipLaunchKernelGGL(ktok, dim3(grid1(pl.BH * (pl.Cp / LIN_BWD_TB))), dim3(256), lds_t, s, a);
+    hipLaunchKernelGGL(kst, dim3(grid1(pl.BH * R)), dim3(256), lds_s, s, a);
+    dWC = a.dWp;
+    dMC = a.dMp;
+  }
 }
 
 }  // namespace
@@ -965,24 +1187,6 @@ e2ttt_status e2ttt_chunk_backward(const e2ttt_problem* prob, const void* q, cons
   float* coef = wsf(pl.coef);
   Instr none;
   launch_scan(pl, eta, alpha, beta, kw, km, pl.nC * pl.Cp, pl.Cp, pl.Cp, coef, 4, s, none);
-  // Forward re-run for the chunk-start states (the readout goes to dq, which
-  // the backward overwrites for every token).
-  auto Wst = [&](int64_t r) -> float* { return wsf(bp.wst) + r * nP; };
-  auto Mst = [&](int64_t r) -> float* { return wsf(bp.mst) + r * nP; };
-  auto Win = [&](int64_t r) -> const float* { return r == 0 ? W0 : Wst(r); };
-  auto Min = [&](int64_t r) -> const float* { return r == 0 ? M0 : Mst(r); };
-  const size_t lds_f = static_cast<size_t>(pl.d * (pl.d + 1) + LIN_FWD_TB * (pl.d + 1)) * sizeof(float);
-  const size_t lds_a = static_cast<size_t>(2 * 64 * 16 + 64 * pl.d) * sizeof(float);
-  for (int64_t r = 0; r + 1 < pl.nC; ++r) {
-    const int ri = static_cast<int>(r);
-    hipLaunchKernelGGL(k_lin_fwd<float>, dim3(grid1(pl.BH * (2 * pl.Cp / LIN_FWD_TB))), dim3(256), lds_f,
-                       s, sh, ri, Q, K, V, Win(r), kw, km, static_cast<float*>(dq),
-                       wsf(pl.gw), wsf(pl.gm));
-    hipLaunchKernelGGL(k_lin_agg<float>, dim3(grid1(pl.BH * (pl.d / 16))), dim3(256), lds_a, s,
-                       sh, ri, K, wsf(pl.gw), wsf(pl.gm), coef, Win(r), Min(r), Wst(r + 1),
-                       Mst(r + 1));
-  }
-  // Reverse chunk loop.
   const float* dWC = dW_end;
   const float* dMC = dM_end;
   if (!dWC || !dMC) {  // absent state gradients: zeros in the first adjoint pair
@@ -991,40 +1195,17 @@ e2ttt_status e2ttt_chunk_backward(const e2ttt_problem* prob, const void* q, cons
     dWC = wsf(bp.dwb);
     dMC = wsf(bp.dmb);
   }
-  const size_t lds_t = static_cast<size_t>(lin_bwd_tok_lds_floats(pl.d)) * sizeof(float);
-  const size_t lds_s = static_cast<size_t>(lin_bwd_state_lds_floats(pl.d)) * sizeof(float);
-  for (int64_t r = pl.nC - 1; r >= 0; --r) {
-    LinBwdArgs a;
-    a.s = sh;
-    a.r = static_cast<int>(r);
-    a.mode = pl.mode;
-    a.q = Q; a.k = K; a.v = V; a.dout = static_cast<const float*>(dout);
-    a.Ws = Win(r); a.Ms = Min(r);
-    a.dWC = dWC; a.dMC = dMC;
-    a.kw = kw; a.km = km; a.coef = coef;
-    a.dq = static_cast<float*>(dq); a.dk = static_cast<float*>(dk); a.dv = static_cast<float*>(dv);
-    a.de = wsf(bp.de); a.sw = wsf(bp.sw); a.sm = wsf(bp.sm); a.dots = wsf(bp.dots);
-    if (r == 0) {
-      a.dWp = dW0;
-      a.dMp = dM0;
-    } else {
-      a.dWp = dWC == wsf(bp.dwa) ? wsf(bp.dwb) : wsf(bp.dwa);
-      a.dMp = dMC == wsf(bp.dma) ? wsf(bp.dmb) : wsf(bp.dma);
-    }
-    const int R = static_cast<int>(pl.d / 16);
-    void (*ktok)(LinBwdArgs) = R == 1 ? k_lin_bwd_tok<1> : R == 2 ? k_lin_bwd_tok<2>
-                               : R == 3 ? k_lin_bwd_tok<3> : k_lin_bwd_tok<4>;
-    void (*kst)(LinBwdArgs) = R == 1 ? k_lin_bwd_state<1> : R == 2 ? k_lin_bwd_state<2>
-                              : R == 3 ? k_lin_bwd_state<3> : k_lin_bwd_state<4>;
-    hipLaunchKernelGGL(ktok, dim3(grid1(pl.BH * (pl.Cp / LIN_BWD_TB))), dim3(256), lds_t, s, a);
-    hipLaunchKernelGGL(kst, dim3(grid1(pl.BH * R)), dim3(256), lds_s, s, a);
-    dWC = a.dWp;
-    dMC = a.dMp;
-  }
+  void (*run)(const BwdPlan&, char*, const float*, const float*, const float*, const float*,
+              const float*, const float*, const float*, const float*, float*, float*, float*,
+              float*, float*, hipStream_t) =
+      pl.kind == E2TTT_SWIGLU ? swiglu_backward : linear_backward;
+  run(bp, ws, Q, K, V, W0, M0, static_cast<const float*>(dout), dWC, dMC,
+      static_cast<float*>(dq), static_cast<float*>(dk), static_cast<float*>(dv), dW0, dM0, s);
   hipLaunchKernelGGL(k_lin_bwd_scalars, dim3(grid1(pl.BH * pl.nC)), dim3(64), 0, s, sh, pl.mode,
                      eta, alpha, beta, static_cast<const float*>(wsf(bp.sw)),
                      static_cast<const float*>(wsf(bp.sm)), static_cast<const float*>(wsf(bp.dots)),
-                     reinterpret_cast<double*>(ws + bp.bcp), deta, dalpha, dbeta);
+                     static_cast<int>(bp.nrb), reinterpret_cast<double*>(ws + bp.bcp), deta,
+                     dalpha, dbeta);
   return hipGetLastError() == hipSuccess ? E2TTT_OK : E2TTT_EHIP;
 }
 

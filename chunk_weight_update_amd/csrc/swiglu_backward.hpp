@@ -1,0 +1,255 @@
+// Outer-loop backward of the chunk update for the three-matrix SwiGLU learner
+// f(x) = W2 (silu(W1 x) * (W3 x)) ("Rethinking Expressivity and Efficiency in
+// Test-Time Training", §5.2 and App. B.5 for the learner; §3.2 and Appendix A
+// for the chunk closed form), fp32.
+//
+// Chunk r with start state (Ws, Ms) produces (§3.2)
+//   W_C = cW Ws + cWM Ms + sum_t K^W_t G_t,   M_C = cM Ms + sum_t K^M_t G_t,
+//   out_t = f_Ws(q_t),
+// with G_t the descent direction at the frozen Ws: for
+//   a1 = W1 k, a3 = W3 k, z = silu(a1) a3, e = v - W2 z, w = W2^T e,
+//   G_W1 = u1 k^T (u1 = w a3 silu'(a1)), G_W3 = u3 k^T (u3 = w silu(a1)),
+//   G_W2 = e z^T.
+// Given the adjoints dW_C, dM_C of the chunk-end state, the adjoint of G_t is
+// the per-token matrix A_t = K^W_t dW_C + K^M_t dM_C, never formed: every
+// product with it is a product with dW_C and dM_C, combined per token.
+//   dK^W_t = <dW_C, G_t> = u1.(dW1_C k) + u3.(dW3_C k) + e.(dW2_C z)
+//   du1 = A1 k, du3 = A3 k, de = A2 z + W2 dw, dz = A2^T e - W2^T de,
+//   dw = du3 silu(a1) + du1 a3 silu'(a1),
+//   da1 = du3 w silu' + du1 w a3 silu'' + dz a3 silu',  da3 = du1 w silu' + dz silu,
+//   dk = W1^T da1 + W3^T da3 + A1^T u1 + A3^T u3,  dv = de,
+//   dWs += [da1; da3] k^T (W1, W3) and e dw^T - de z^T (W2), summed over tokens,
+// plus the readout's reverse mode (dq, dWs) and the state terms
+//   dW_prev = cW dW_C + dWs,  dM_prev = cWM dW_C + cM dM_C,
+//   dcW = <dW_C, Ws>, dcM = <dM_C, Ms>, dcWM = <dW_C, Ms>.
+// The scalar adjoints (deta, dalpha, dbeta) follow from dK^W, dK^M and the
+// three dots exactly as for the linear learner.
+//
+// Every product over tokens or features is a call of one batched, strided
+// fp32 GEMM (64 x 64 tiles through LDS); the per-token steps are small
+// elementwise kernels.  Only the chunk's n valid tokens enter any product.
+#pragma once
+
+#include "kernels.hpp"
+
+namespace e2ttt {
+
+// C[b](m, n) = D[b](m, n) + alpha * sum_k A[b](m, k) B[b](k, n), m < M, n < N,
+// with A(m, k) at A + b*sAb + m*sAm + k*sAk, B(k, n) at B + b*sBb + k*sBk +
+// n*sBn, C and D row-major with leading dimensions ldc, ldd.  D may be null
+// (zero) or equal to C.
+struct GemmF32 {
+  int64_t M, N, K;
+  const float* A;
+  int64_t sAb, sAm, sAk;
+  const float* B;
+  int64_t sBb, sBk, sBn;
+  const float* D;
+  int64_t sDb, ldd;
+  float* C;
+  int64_t sCb, ldc;
+  float alpha;
+};
+
+constexpr int GF_T = 64, GF_K = 16;
+
+__global__ __launch_bounds__(256) void k_gemm_f32(GemmF32 g) {
+  __shared__ float As[GF_K][GF_T + 4], Bs[GF_K][GF_T + 4];
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
+  const int64_t b = blockIdx.z;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * GF_T;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * GF_T;
+  const float* A = g.A + b * g.sAb;
+  const float* B = g.B + b * g.sBb;
+  const bool aK = g.sAk == 1;  // k contiguous in A: threads run along k
+  const bool bN = g.sBn == 1;  // n contiguous in B: threads run along n
+  float acc[4][4] = {};
+  for (int64_t k0 = 0; k0 < g.K; k0 += GF_K) {
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      const int e = tid + 256 * l;
+      const int mm = aK ? e / GF_K : e % GF_T, kk = aK ? e % GF_K : e / GF_T;
+      const int64_t m = m0 + mm, k = k0 + kk;
+      As[kk][mm] = (m < g.M && k < g.K) ? A[m * g.sAm + k * g.sAk] : 0.0f;
+      const int nn = bN ? e % GF_T : e / GF_K, kb = bN ? e / GF_T : e % GF_K;
+      const int64_t n = n0 + nn, kq = k0 + kb;
+      Bs[kb][nn] = (n < g.N && kq < g.K) ? B[kq * g.sBk + n * g.sBn] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < GF_K; ++kk) {
+      float a[4], bb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty + 16 * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bb[j] = Bs[kk][tx + 16 * j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * bb[j];
+    }
+    __syncthreads();
+  }
+  float* C = g.C + b * g.sCb;
+  const float* D = g.D ? g.D + b * g.sDb : nullptr;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = m0 + ty + 16 * i;
+    if (m >= g.M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = n0 + tx + 16 * j;
+      if (n >= g.N) continue;
+      const float base = D ? D[m * g.ldd + n] : 0.0f;
+      C[m * g.ldc + n] = base + g.alpha * acc[i][j];
+    }
+  }
+}
+
+__device__ __forceinline__ float sig_acc(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// Z = silu(a1) * a3 for n rows of H = [a1 | a3] (row length 2h), per unit.
+__global__ __launch_bounds__(256) void k_swb_act(int64_t BH, int64_t n, int64_t h,
+                                                 int64_t ustride, const float* __restrict__ H,
+                                                 float* __restrict__ Z) {
+  const int64_t per = n * h;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= BH * per) return;
+  const int64_t u = i / per, rem = i % per, t = rem / h, j = rem % h;
+  const float* hr = H + u * ustride * 2 * h + t * 2 * h;
+  const float a1 = hr[j], a3 = hr[h + j];
+  Z[u * ustride * h + t * h + j] = a1 * sig_acc(a1) * a3;
+}
+
+struct SwbTokArgs {
+  int64_t n, d, h, Cp, nC;
+  int r;
+  const float *HK, *WV, *E, *TW, *TM, *SW, *SM, *RW, *RM, *kw, *km;
+  float *sw, *sm, *DU, *DW, *DEA, *DZA, *UW, *UM;
+};
+
+// One workgroup per (unit, token): dK^W, dK^M and the token's adjoint vectors.
+__global__ __launch_bounds__(256) void k_swb_tok(SwbTokArgs a) {
+  __shared__ float red[2][256];
+  const int64_t u = blockIdx.x / a.n, t = blockIdx.x % a.n;
+  const int tid = threadIdx.x;
+  const int64_t h = a.h, d = a.d;
+  const int64_t rh = (u * a.Cp + t) * h, r2 = 2 * rh, rd = (u * a.Cp + t) * d;
+  const int64_t seg = u * a.nC + a.r;
+  const float kwt = a.kw[seg * a.Cp + t], kmt = a.km[seg * a.Cp + t];
+  float pW = 0.0f, pM = 0.0f;
+  for (int64_t i = tid; i < h; i += 256) {
+    const float a1 = a.HK[r2 + i], a3 = a.HK[r2 + h + i], w = a.WV[rh + i];
+    const float sg = sig_acc(a1), sl = a1 * sg, sp = sg * (1.0f + a1 * (1.0f - sg));
+    const float u1 = w * a3 * sp, u3 = w * sl;
+    const float tw1 = a.TW[r2 + i], tw3 = a.TW[r2 + h + i];
+    const float tm1 = a.TM[r2 + i], tm3 = a.TM[r2 + h + i];
+    pW += u1 * tw1 + u3 * tw3;
+    pM += u1 * tm1 + u3 * tm3;
+    const float du1 = kwt * tw1 + kmt * tm1, du3 = kwt * tw3 + kmt * tm3;
+    a.DU[r2 + i] = du1;
+    a.DU[r2 + h + i] = du3;
+    a.DW[rh + i] = du3 * sl + du1 * a3 * sp;
+    a.UW[r2 + i] = kwt * u1;
+    a.UW[r2 + h + i] = kwt * u3;
+    a.UM[r2 + i] = kmt * u1;
+    a.UM[r2 + h + i] = kmt * u3;
+    a.DZA[rh + i] = kwt * a.RW[rh + i] + kmt * a.RM[rh + i];
+  }
+  for (int64_t o = tid; o < d; o += 256) {
+    const float e = a.E[rd + o], sw = a.SW[rd + o], sm = a.SM[rd + o];
+    pW += e * sw;
+    pM += e * sm;
+    a.DEA[rd + o] = kwt * sw + kmt * sm;
+  }
+  red[0][tid] = pW;
+  red[1][tid] = pM;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) {
+      red[0][tid] += red[0][tid + off];
+      red[1][tid] += red[1][tid + off];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    a.sw[seg * a.Cp + t] = red[0][0];
+    a.sm[seg * a.Cp + t] = red[1][0];
+  }
+}
+
+// [da1 | da3] of the key rows (from a1, a3, w, du1, du3, dz) and of the query
+// rows (readout: from a1, a3 and dz = W2^T dout).
+__global__ __launch_bounds__(256) void k_swb_da(int64_t BH, int64_t n, int64_t h, int64_t Cp,
+                                                const float* __restrict__ HK,
+                                                const float* __restrict__ WV,
+                                                const float* __restrict__ DU,
+                                                const float* __restrict__ DZ,
+                                                const float* __restrict__ HQ,
+                                                const float* __restrict__ DZQ,
+                                                float* __restrict__ DA, float* __restrict__ DAQ) {
+  const int64_t per = n * h;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= BH * per) return;
+  const int64_t u = i / per, rem = i % per, t = rem / h, j = rem % h;
+  const int64_t rh = (u * Cp + t) * h, r2 = 2 * rh;
+  {
+    const float a1 = HK[r2 + j], a3 = HK[r2 + h + j], w = WV[rh + j];
+    const float du1 = DU[r2 + j], du3 = DU[r2 + h + j], dz = DZ[rh + j];
+    const float sg = sig_acc(a1), sl = a1 * sg, sp = sg * (1.0f + a1 * (1.0f - sg));
+    const float spp = sg * (1.0f - sg) * (2.0f + a1 * (1.0f - 2.0f * sg));
+    DA[r2 + j] = du3 * w * sp + du1 * w * a3 * spp + dz * a3 * sp;
+    DA[r2 + h + j] = du1 * w * sp + dz * sl;
+  }
+  {
+    const float a1 = HQ[r2 + j], a3 = HQ[r2 + h + j], dz = DZQ[rh + j];
+    const float sg = sig_acc(a1), sl = a1 * sg, sp = sg * (1.0f + a1 * (1.0f - sg));
+    DAQ[r2 + j] = dz * a3 * sp;
+    DAQ[r2 + h + j] = dz * sl;
+  }
+}
+
+constexpr int SWB_STATE_ELEMS = 1024;  // state entries per workgroup of k_swb_state
+
+// dW_prev = cW dW_C, dM_prev = cWM dW_C + cM dM_C (the token sums are added
+// afterwards), and this block's partial sums of <dW_C, Ws>, <dM_C, Ms>,
+// <dW_C, Ms> (added in block order later, so results do not depend on
+// scheduling).  Grid: BH * nrb workgroups, nrb = ceil(P / 1024).
+__global__ __launch_bounds__(256) void k_swb_state(int64_t P, int64_t nrb, int64_t nC, int r,
+                                                   const float* __restrict__ coef,
+                                                   const float* __restrict__ Ws,
+                                                   const float* __restrict__ Ms,
+                                                   const float* __restrict__ dWC,
+                                                   const float* __restrict__ dMC, float* dWp,
+                                                   float* dMp, float* __restrict__ dots) {
+  __shared__ float red[3][256];
+  const int64_t u = blockIdx.x / nrb, rb = blockIdx.x % nrb;
+  const int tid = threadIdx.x;
+  const float* cf = coef + (u * nC + r) * 4;
+  const float cW = cf[0], cM = cf[1], cWM = cf[2];
+  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f;
+  for (int l = 0; l < SWB_STATE_ELEMS / 256; ++l) {
+    const int64_t p = rb * SWB_STATE_ELEMS + l * 256 + tid;
+    if (p >= P) break;
+    const int64_t x = u * P + p;
+    const float dw = dWC[x], dm = dMC[x], ws = Ws[x], ms = Ms[x];
+    s0 += dw * ws;
+    s1 += dm * ms;
+    s2 += dw * ms;
+    dWp[x] = cW * dw;
+    dMp[x] = cWM * dw + cM * dm;
+  }
+  red[0][tid] = s0;
+  red[1][tid] = s1;
+  red[2][tid] = s2;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off)
+      for (int c = 0; c < 3; ++c) red[c][tid] += red[c][tid + off];
+    __syncthreads();
+  }
+  if (tid < 3) dots[((u * nC + r) * nrb + rb) * 4 + tid] = red[tid][0];
+}
+
+}  // namespace e2ttt

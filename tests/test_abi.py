@@ -218,7 +218,8 @@ def test_decode_host_checks():
 def bwd_fake_args(prob):
     f = Fake()
     B, H, L, d = prob.batch, prob.heads, prob.seq_len, prob.dim
-    nx, ns, np_ = B * H * L * d * 4, B * H * L * 4, B * H * d * d * 4
+    P = d * d if prob.kind == cwu.LINEAR else 3 * d * prob.hidden
+    nx, ns, np_ = B * H * L * d * 4, B * H * L * 4, B * H * P * 4
     a = dict(q=f(nx), k=f(nx), v=f(nx), eta=f(ns), alpha=f(ns), beta=f(ns), W0=f(np_),
              M0=f(np_), dout=f(nx), dW_end=f(np_), dM_end=f(np_), dq=f(nx), dk=f(nx), dv=f(nx),
              deta=f(ns), dalpha=f(ns), dbeta=f(ns), dW0=f(np_), dM0=f(np_))
@@ -240,7 +241,12 @@ def test_backward_support_and_workspace():
     n = cwu.backward_workspace_bytes(lin)
     assert n > cwu.workspace_bytes(lin) and n % 256 == 0
     assert cwu.backward_workspace_bytes(linear(seq_len=0)) == 0
-    for bad in (swiglu(), linear(io_dtype=cwu.BF16), linear(dim=128),
+    sw = swiglu(io_dtype=cwu.F32)
+    n = cwu.backward_workspace_bytes(sw)
+    assert n > cwu.workspace_bytes(sw) and n % 256 == 0
+    assert cwu.backward_workspace_bytes(swiglu(io_dtype=cwu.F32, seq_len=0)) == 0
+    for bad in (swiglu(), swiglu(io_dtype=cwu.F32, flags=cwu.FLAG_POST_CHUNK_ROW_L2),
+                linear(io_dtype=cwu.BF16), linear(dim=128),
                 linear(flags=cwu.FLAG_CHUNK_AVERAGED_DECAY), linear(flags=cwu.FLAG_QK_SILU_L2),
                 linear(flags=cwu.FLAG_POST_CHUNK_ROW_L2)):
         with pytest.raises(cwu.E2tttError) as e:
@@ -264,8 +270,8 @@ def test_backward_support_and_workspace():
     (lambda a: a.update(workspace=a["dv"]), cwu.EINVAL),
 ])
 def test_backward_host_errors(mutate, expected):
-    prob = linear()
-    a = bwd_fake_args(prob)
-    mutate(a)
-    assert bwd_call(prob, a) == expected
+    for prob in (linear(), swiglu(io_dtype=cwu.F32, seq_len=300, batch=1, heads=2)):
+        a = bwd_fake_args(prob)
+        mutate(a)
+        assert bwd_call(prob, a) == expected
     assert bwd_call(swiglu(), bwd_fake_args(linear())) == cwu.EUNSUPPORTED

@@ -296,6 +296,71 @@ def backward_bench(with_oracle, reps=50):
     return out
 
 
+def backward_bench_swiglu(with_oracle, reps=10):
+    """The outer-loop backward of the SwiGLU learner on the main workload's
+    shape (B = 2, H = 4, L = 4096, C = 512, d = 128, h = 256) with fp32
+    inputs (the backward's one supported io type), timed per call with events.
+    Algorithmic flops per token: the forward re-run (26 d h) and the
+    backward's products (64 d h: the learner's forward at the chunk-start
+    weights for keys and queries, eight products with the chunk-end adjoints,
+    the two W2 products of the error's adjoint, four for dk and dq, five
+    token sums for the state adjoint).  With ``with_oracle``, the oracle's
+    reverse mode is timed on the host on a sample: the first unit, first 1024
+    tokens (two chunks)."""
+    import numpy as np
+    import torch
+    import chunk_weight_update_amd as cwu
+    from chunk_weight_update_amd.inputs import F32, SWIGLU, make_inputs
+    B, H, L, d, h, C = 2, 4, 4096, 128, 256, 512
+    P = 3 * d * h
+    inp = make_inputs(SWIGLU, B, H, L, d, h, F32, seed=0, m0_scale=0.01)
+    rng = np.random.default_rng(1000)
+    up = [rng.standard_normal(s).astype(np.float32)
+          for s in ((B, H, L, d), (B, H, P), (B, H, P))]
+    names = ("q", "k", "v", "eta", "alpha", "beta", "W0", "M0")
+    t = {n: torch.from_numpy(np.ascontiguousarray(inp[n], dtype=np.float32)).cuda() for n in names}
+    dout, dW, dM = (torch.from_numpy(a).cuda() for a in up)
+    g = {n: torch.empty_like(t[n]) for n in names}
+    prob = cwu.make_problem(SWIGLU, B, H, L, d, h, C, F32, 0)
+    ws = torch.empty(cwu.backward_workspace_bytes(prob), dtype=torch.uint8, device="cuda")
+
+    def call():
+        cwu.chunk_backward(prob, *[t[n] for n in names], dout, dW, dM,
+                           *[g[n] for n in names], ws)
+    for _ in range(3):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 90.0 * d * h * L * B * H
+    out = {"label": "outer-loop backward of the chunk forward, SwiGLU learner, fp32 "
+                    "(not the main metric)",
+           "config": {"workload": f"swiglu-d{d}h{h}-b{B}h{H}-l{L}-c{C}-fp32"},
+           "ms_per_call": ms, "tokens_per_s": B * H * L / (ms * 1e-3),
+           "tflops_algorithmic": flops / (ms * 1e-3) / 1e12,
+           "frac_of_fp32_vector_peak": flops / (ms * 1e-3) / 157.3e12}
+    if with_oracle:
+        import oracle
+        oracle.build(force=False)
+        n = 1024
+        sl = (slice(0, 1), slice(0, 1), slice(0, n))
+        t0 = time.perf_counter()
+        oracle.chunk_backward(SWIGLU, inp["q64"][sl], inp["k64"][sl], inp["v64"][sl],
+                              inp["eta"][sl], inp["alpha"][sl], inp["beta"][sl],
+                              inp["W0"][:1, :1], inp["M0"][:1, :1], up[0][sl], up[1][:1, :1],
+                              up[2][:1, :1], C, hidden=h)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": n / dt, "unit": "tokens/s", "cores": 1,
+                               "kind": "oracle", "sample": f"unit 0, tokens 0..{n - 1} "
+                               "(fp64 reverse mode of the literal recurrence, one thread)"}
+    return out
+
+
 def algorithmic_flops(w):
     if w.kind == 0:
         return 8.0 * w.d * w.d * w.L * w.B * w.H
@@ -476,6 +541,7 @@ def main():
         line["scan_microbench"] = scan_microbench()
         log(f"bench: scan microbenchmark {line['scan_microbench']}")
         line["backward"] = backward_bench(not args.no_cpu_baseline)
+        line["backward_swiglu"] = backward_bench_swiglu(not args.no_cpu_baseline)
         log(f"bench: linear backward {line['backward']}")
     if not args.no_cpu_baseline:
         log("bench: timing the fp64 oracle on the host cores")

@@ -26,8 +26,8 @@
 // three dots exactly as for the linear learner.
 //
 // Every product over tokens or features is a call of one batched, strided
-// fp32 GEMM (64 x 64 tiles through LDS); the per-token steps are small
-// elementwise kernels.  Only the chunk's n valid tokens enter any product.
+// fp32 GEMM (64 x 64 tiles through LDS, fp32 MFMA); the per-token steps are
+// small elementwise kernels.  Only the chunk's n valid tokens enter any product.
 #pragma once
 
 #include "kernels.hpp"
@@ -53,10 +53,17 @@ struct GemmF32 {
 
 constexpr int GF_T = 64, GF_K = 16;
 
+// 64 x 64 output tile, 256 threads = 4 waves in a 2 x 2 grid, each wave one
+// 32 x 32 block on v_mfma_f32_32x32x2f32.  K advances in slabs of 16 staged
+// through LDS (k-major, so both operands are read as 32 consecutive floats per
+// lane half); the next slab's global loads are in flight during the current
+// slab's MFMAs.  Loads run along whichever of an operand's two strides is 1,
+// so row- and column-major operands are both read in full cache lines.
 __global__ __launch_bounds__(256) void k_gemm_f32(GemmF32 g) {
   __shared__ float As[GF_K][GF_T + 4], Bs[GF_K][GF_T + 4];
   const int tid = threadIdx.x;
-  const int tx = tid & 15, ty = tid >> 4;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, hf = lane >> 5;
   const int64_t b = blockIdx.z;
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * GF_T;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * GF_T;
@@ -64,46 +71,60 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmF32 g) {
   const float* B = g.B + b * g.sBb;
   const bool aK = g.sAk == 1;  // k contiguous in A: threads run along k
   const bool bN = g.sBn == 1;  // n contiguous in B: threads run along n
-  float acc[4][4] = {};
-  for (int64_t k0 = 0; k0 < g.K; k0 += GF_K) {
+  float ra[4], rb[4];
+  auto fetch = [&](int64_t k0) {
 #pragma unroll
     for (int l = 0; l < 4; ++l) {
       const int e = tid + 256 * l;
       const int mm = aK ? e / GF_K : e % GF_T, kk = aK ? e % GF_K : e / GF_T;
       const int64_t m = m0 + mm, k = k0 + kk;
-      As[kk][mm] = (m < g.M && k < g.K) ? A[m * g.sAm + k * g.sAk] : 0.0f;
+      ra[l] = (m < g.M && k < g.K) ? A[m * g.sAm + k * g.sAk] : 0.0f;
       const int nn = bN ? e % GF_T : e / GF_K, kb = bN ? e / GF_T : e % GF_K;
       const int64_t n = n0 + nn, kq = k0 + kb;
-      Bs[kb][nn] = (n < g.N && kq < g.K) ? B[kq * g.sBk + n * g.sBn] : 0.0f;
+      rb[l] = (n < g.N && kq < g.K) ? B[kq * g.sBk + n * g.sBn] : 0.0f;
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      const int e = tid + 256 * l;
+      As[aK ? e % GF_K : e / GF_T][aK ? e / GF_K : e % GF_T] = ra[l];
+      Bs[bN ? e / GF_T : e % GF_K][bN ? e % GF_T : e / GF_K] = rb[l];
+    }
+  };
+  f32x16_t acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  fetch(0);
+  stash();
+  __syncthreads();
+  for (int64_t k0 = 0; k0 < g.K; k0 += GF_K) {
+    const bool more = k0 + GF_K < g.K;
+    if (more) fetch(k0 + GF_K);
+#pragma unroll
+    for (int ks = 0; ks < GF_K / 2; ++ks) {
+      const int k = 2 * ks + hf;
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[k][32 * wm + l32], Bs[k][32 * wn + l32], acc,
+                                                 0, 0, 0);
     }
     __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < GF_K; ++kk) {
-      float a[4], bb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty + 16 * i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bb[j] = Bs[kk][tx + 16 * j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * bb[j];
+    if (more) {
+      stash();
+      __syncthreads();
     }
-    __syncthreads();
   }
+  // Lane l, register v holds row 8 (v / 4) + 4 hf + v % 4, column l % 32 of
+  // the wave's block.
   float* C = g.C + b * g.sCb;
   const float* D = g.D ? g.D + b * g.sDb : nullptr;
+  const int64_t n = n0 + 32 * wn + l32;
+  if (n >= g.N) return;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t m = m0 + ty + 16 * i;
+  for (int v = 0; v < 16; ++v) {
+    const int64_t m = m0 + 32 * wm + 8 * (v / 4) + 4 * hf + (v % 4);
     if (m >= g.M) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + tx + 16 * j;
-      if (n >= g.N) continue;
-      const float base = D ? D[m * g.ldd + n] : 0.0f;
-      C[m * g.ldc + n] = base + g.alpha * acc[i][j];
-    }
+    const float base = D ? D[m * g.ldd + n] : 0.0f;
+    C[m * g.ldc + n] = base + g.alpha * acc[v];
   }
 }
 

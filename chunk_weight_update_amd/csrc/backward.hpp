@@ -32,6 +32,14 @@
 
 namespace e2ttt {
 
+// dst[i] = src[i] converted (bf16 <-> fp32; fp32 -> bf16 rounds to nearest even).
+template <typename S, typename D>
+__global__ __launch_bounds__(256) void k_convert(const S* __restrict__ src, D* __restrict__ dst,
+                                                 int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) dst[i] = from_f32<D>(to_f32<S>(src[i]));
+}
+
 struct LinBwdArgs {
   Shape s;
   int r;     // chunk index

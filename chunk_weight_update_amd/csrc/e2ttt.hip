@@ -870,14 +870,27 @@ struct BwdPlan {
   size_t hk, hq, tw, tm, du, uw, um, da, daq;  // width 2h
   size_t zk, zq, wv, dzq, r2w, r2m, dwv, dza;  // width h
   size_t e, s2w, s2m, dea;                     // width d
+  // bf16 io: fp32 copies of q, k, v, dout and fp32 dq, dk, dv, [BH][L][d]
+  bool bf16io;
+  size_t xq, xk, xv, xdo, xdq, xdk, xdv;
   size_t total;
 };
 
 e2ttt_status make_bwd_plan(const e2ttt_problem* p, BwdPlan* bp) {
-  const e2ttt_status st = make_plan(p, &bp->f);
+  // The backward computes in fp32; bf16 io is converted at the boundary, so
+  // the inner plan (and the forward re-run) is the fp32 one.
+  e2ttt_problem pf;
+  if (p && p->struct_size == sizeof(e2ttt_problem)) {
+    pf = *p;
+    pf.io_dtype = E2TTT_F32;
+  }
+  const e2ttt_status st = make_plan(p && p->struct_size == sizeof(e2ttt_problem) ? &pf : p,
+                                    &bp->f);
   if (st != E2TTT_OK) return st;
+  if (p->io_dtype != E2TTT_F32 && p->io_dtype != E2TTT_BF16) return E2TTT_EINVAL;
+  bp->bf16io = p->io_dtype == E2TTT_BF16;
   const Plan& q = bp->f;
-  if (q.io != E2TTT_F32 || p->flags != 0u) return E2TTT_EUNSUPPORTED;
+  if (p->flags != 0u) return E2TTT_EUNSUPPORTED;
   if (q.kind == E2TTT_LINEAR && q.d > 64) return E2TTT_EUNSUPPORTED;
   if (q.kind == E2TTT_SWIGLU && q.BH > 65535) return E2TTT_EUNSUPPORTED;  // grid z
   size_t o = align256(q.total);
@@ -906,6 +919,9 @@ e2ttt_status make_bwd_plan(const e2ttt_problem* p, BwdPlan* bp) {
       *b = take(rows * q.h);
     for (size_t* b : {&bp->e, &bp->s2w, &bp->s2m, &bp->dea}) *b = take(rows * q.d);
   }
+  if (bp->bf16io)
+    for (size_t* b : {&bp->xq, &bp->xk, &bp->xv, &bp->xdo, &bp->xdq, &bp->xdk, &bp->xdv})
+      *b = take(4 * static_cast<size_t>(q.BH * q.L * q.d));
   bp->total = q.L == 0 ? 0 : o;
   return E2TTT_OK;
 }
@@ -1148,7 +1164,7 @@ e2ttt_status e2ttt_chunk_backward(const e2ttt_problem* prob, const void* q, cons
     if (p && !aligned(p, 16)) return E2TTT_EINVAL;
   if (workspace && !aligned(workspace, 256)) return E2TTT_EINVAL;
   if (!empty && workspace_bytes < bp.total) return E2TTT_EWORKSPACE;
-  const size_t nx = static_cast<size_t>(pl.BH * pl.L * pl.d) * 4;
+  const size_t nx = static_cast<size_t>(pl.BH * pl.L * pl.d) * (bp.bf16io ? 2 : 4);
   const size_t ns = static_cast<size_t>(pl.BH * pl.L) * 4;
   const size_t np = static_cast<size_t>(pl.BH * pl.P) * 4;
   const Range in[] = {rng(q, nx), rng(k, nx), rng(v, nx), rng(eta, ns), rng(alpha, ns),
@@ -1182,6 +1198,22 @@ e2ttt_status e2ttt_chunk_backward(const e2ttt_problem* prob, const void* q, cons
   const float* Q = static_cast<const float*>(q);
   const float* K = static_cast<const float*>(k);
   const float* V = static_cast<const float*>(v);
+  const float* DO = static_cast<const float*>(dout);
+  float* dQ = static_cast<float*>(dq);
+  float* dK = static_cast<float*>(dk);
+  float* dV = static_cast<float*>(dv);
+  const int64_t nxe = pl.BH * pl.L * pl.d;
+  const unsigned gx = grid1((nxe + 255) / 256);
+  if (bp.bf16io) {  // widen the bf16 inputs; the outputs are rounded back at the end
+    const bf16_t* src[] = {static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                           static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(dout)};
+    const size_t dst[] = {bp.xq, bp.xk, bp.xv, bp.xdo};
+    for (int i = 0; i < 4; ++i)
+      hipLaunchKernelGGL((k_convert<bf16_t, float>), dim3(gx), dim3(256), 0, s, src[i],
+                         wsf(dst[i]), nxe);
+    Q = wsf(bp.xq); K = wsf(bp.xk); V = wsf(bp.xv); DO = wsf(bp.xdo);
+    dQ = wsf(bp.xdq); dK = wsf(bp.xdk); dV = wsf(bp.xdv);
+  }
   float* kw = wsf(pl.kw);
   float* km = wsf(pl.km);
   float* coef = wsf(pl.coef);
@@ -1199,8 +1231,14 @@ e2ttt_status e2ttt_chunk_backward(const e2ttt_problem* prob, const void* q, cons
               const float*, const float*, const float*, const float*, float*, float*, float*,
               float*, float*, hipStream_t) =
       pl.kind == E2TTT_SWIGLU ? swiglu_backward : linear_backward;
-  run(bp, ws, Q, K, V, W0, M0, static_cast<const float*>(dout), dWC, dMC,
-      static_cast<float*>(dq), static_cast<float*>(dk), static_cast<float*>(dv), dW0, dM0, s);
+  run(bp, ws, Q, K, V, W0, M0, DO, dWC, dMC, dQ, dK, dV, dW0, dM0, s);
+  if (bp.bf16io) {
+    bf16_t* dst[] = {static_cast<bf16_t*>(dq), static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv)};
+    const float* src[] = {dQ, dK, dV};
+    for (int i = 0; i < 3; ++i)
+      hipLaunchKernelGGL((k_convert<float, bf16_t>), dim3(gx), dim3(256), 0, s, src[i], dst[i],
+                         nxe);
+  }
   hipLaunchKernelGGL(k_lin_bwd_scalars, dim3(grid1(pl.BH * pl.nC)), dim3(64), 0, s, sh, pl.mode,
                      eta, alpha, beta, static_cast<const float*>(wsf(bp.sw)),
                      static_cast<const float*>(wsf(bp.sm)), static_cast<const float*>(wsf(bp.dots)),

@@ -261,10 +261,12 @@ E2TTT_API e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* 
  * weights through the learner (§5.2, App. B.5), so its reverse mode carries
  * the second-order terms of f = W2 (silu(W1 x) * (W3 x)) as well.
  *
- * Supported: io_dtype E2TTT_F32, flags 0, and kind E2TTT_LINEAR with dim a
- * multiple of 16 up to 64, or E2TTT_SWIGLU with the forward's (dim, hidden)
- * set and at most 65535 batch*heads units (else EUNSUPPORTED).  Layouts as
- * the forward: q, k, v, dout, dq, dk, dv [B,H,L,dim] fp32; eta, alpha, beta,
+ * Supported: flags 0, and kind E2TTT_LINEAR with dim a multiple of 16 up to
+ * 64, or E2TTT_SWIGLU with the forward's (dim, hidden) set and at most 65535
+ * batch*heads units (else EUNSUPPORTED).  The arithmetic is fp32 (the forward
+ * re-run too); with io_dtype E2TTT_BF16, q, k, v, dout are widened on entry
+ * and dq, dk, dv rounded to nearest even on exit.  Layouts as the forward: q,
+ * k, v, dout, dq, dk, dv [B,H,L,dim] of io_dtype; eta, alpha, beta,
  * deta, dalpha, dbeta [B,H,L]; W0, M0, dW_end, dM_end, dW0, dM0 [B,H,P] packed
  * as the forward's state (P = dim*dim, or 3*dim*hidden).  dW_end and
  * dM_end may be NULL (zero gradients).  All pointers are device pointers owned

@@ -245,8 +245,9 @@ def test_backward_support_and_workspace():
     n = cwu.backward_workspace_bytes(sw)
     assert n > cwu.workspace_bytes(sw) and n % 256 == 0
     assert cwu.backward_workspace_bytes(swiglu(io_dtype=cwu.F32, seq_len=0)) == 0
-    for bad in (swiglu(), swiglu(io_dtype=cwu.F32, flags=cwu.FLAG_POST_CHUNK_ROW_L2),
-                linear(io_dtype=cwu.BF16), linear(dim=128),
+    for ok in (swiglu(), linear(io_dtype=cwu.BF16)):  # bf16 io: widened at the boundary
+        assert cwu.backward_workspace_bytes(ok) > 0
+    for bad in (swiglu(io_dtype=cwu.F32, flags=cwu.FLAG_POST_CHUNK_ROW_L2), linear(dim=128),
                 linear(flags=cwu.FLAG_CHUNK_AVERAGED_DECAY), linear(flags=cwu.FLAG_QK_SILU_L2),
                 linear(flags=cwu.FLAG_POST_CHUNK_ROW_L2)):
         with pytest.raises(cwu.E2tttError) as e:
@@ -270,8 +271,10 @@ def test_backward_support_and_workspace():
     (lambda a: a.update(workspace=a["dv"]), cwu.EINVAL),
 ])
 def test_backward_host_errors(mutate, expected):
-    for prob in (linear(), swiglu(io_dtype=cwu.F32, seq_len=300, batch=1, heads=2)):
+    for prob in (linear(), swiglu(io_dtype=cwu.F32, seq_len=300, batch=1, heads=2),
+                 swiglu(seq_len=100, batch=1, heads=1)):
         a = bwd_fake_args(prob)
         mutate(a)
         assert bwd_call(prob, a) == expected
-    assert bwd_call(swiglu(), bwd_fake_args(linear())) == cwu.EUNSUPPORTED
+    bad = swiglu(flags=cwu.FLAG_POST_CHUNK_ROW_L2)
+    assert bwd_call(bad, bwd_fake_args(linear())) == cwu.EUNSUPPORTED

@@ -55,6 +55,12 @@ def test_swiglu_backward_matches_oracle(B, H, L, C, mode, regime):
     check(B, H, L, 128, 256, C, mode, regime)
 
 
+def test_swiglu_backward_large_state():
+    """The large-state learner's shape (d = 768, h = 1536) on a short sequence
+    (the oracle's reverse mode stores the state before every token)."""
+    check(1, 1, 20, 768, 1536, 8, seed=2)
+
+
 def test_swiglu_backward_without_state_gradients():
     check(1, 1, 160, 128, 256, 64, seed=4, with_state=False)
 
@@ -68,3 +74,59 @@ def test_swiglu_backward_is_deterministic():
     b = run_backward(prob, inp, dout, dW, dM)
     for n in NAMES:
         assert np.array_equal(a[n], b[n]), n
+
+
+# --------------------------------------------------------------------------
+# bf16 io: q, k, v, dout in and dq, dk, dv out as bf16 (the state tensors and
+# per-token scalars stay fp32).  The library widens the inputs and computes in
+# fp32, so the fp32 outputs keep the fp32 bar; the bf16 outputs carry one
+# rounding each (at most 2^-9 relative) and take the bf16 output bar.
+
+BF16_OUT_TOL = 1e-2
+BF16_OUT = ("q", "k", "v")
+
+
+def check_bf16(kind, B, H, L, d, h, C, mode=0, regime="default", seed=0):
+    import torch
+    import oracle
+    import chunk_weight_update_amd as cwu
+    from chunk_weight_update_amd.inputs import BF16, bf16_bits_to_f32, f32_to_bf16_bits
+    log(f"bf16-io backward case kind={kind} B={B} H={H} L={L} d={d} h={h} C={C} mode={mode} "
+        f"regime={regime} seed={seed}")
+    inp = make_inputs(kind, B, H, L, d, h, BF16, seed=seed, regime=regime, m0_scale=0.01)
+    P = d * d if kind == oracle.LINEAR else 3 * d * h
+    rng = np.random.default_rng(seed + 3000)
+    do_bits = f32_to_bf16_bits(rng.standard_normal((B, H, L, d)).astype(np.float32))
+    dout64 = bf16_bits_to_f32(do_bits).astype(np.float64)
+    dW = rng.standard_normal((B, H, P)).astype(np.float32)
+    dM = rng.standard_normal((B, H, P)).astype(np.float32)
+    prob = problem_for(kind, B, H, L, d, h, C, BF16, decay_mode=mode)
+    dev = "cuda"
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+    t = {n: bf(inp[n]) for n in ("q", "k", "v")}
+    for n in ("eta", "alpha", "beta", "W0", "M0"):
+        t[n] = torch.from_numpy(np.ascontiguousarray(inp[n], dtype=np.float32)).to(dev)
+    g = {n: torch.full_like(t[n], float("nan")) for n in NAMES}
+    ws = torch.empty(max(cwu.backward_workspace_bytes(prob), 256), dtype=torch.uint8, device=dev)
+    cwu.chunk_backward(prob, *[t[n] for n in NAMES], bf(do_bits), torch.from_numpy(dW).to(dev),
+                       torch.from_numpy(dM).to(dev), *[g[n] for n in NAMES], ws)
+    torch.cuda.synchronize()
+    got = {n: g[n].float().cpu().numpy().astype(np.float64) for n in NAMES}
+    ref = oracle.chunk_backward(kind, inp["q64"], inp["k64"], inp["v64"], inp["eta"],
+                                inp["alpha"], inp["beta"], inp["W0"], inp["M0"], dout64, dW, dM,
+                                C, decay_mode=mode, hidden=h)
+    errs = {n: rel_fro(got[n], ref[n]) for n in NAMES}
+    log("  rel_fro " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    for n in NAMES:
+        assert np.all(np.isfinite(got[n])), n
+        assert errs[n] <= (BF16_OUT_TOL if n in BF16_OUT else TOL), (n, errs[n])
+
+
+@pytest.mark.parametrize("kind,B,H,L,d,h,C,mode", [
+    (SWIGLU, 1, 2, 300, 128, 256, 128, 0),   # the bf16 workloads' learner, ragged last chunk
+    (0, 2, 2, 200, 64, 0, 64, 1),            # linear learner, alpha taken as gamma
+])
+def test_backward_bf16_io_matches_oracle(kind, B, H, L, d, h, C, mode):
+    check_bf16(kind, B, H, L, d, h, C, mode)

@@ -49,6 +49,13 @@ struct GemmF32 {
   float* C;
   int64_t sCb, ldc;
   float alpha;
+  // Split of K over nsplit workgroups (grid z = unit * nsplit + split), each
+  // taking kchunk (a multiple of 16) of K and writing its alpha-scaled partial
+  // to part[(unit * nsplit + split) * M * N + m * N + n]; k_gemm_split_sum then
+  // adds D and the splits in split order into C.  nsplit = 1: direct.
+  int nsplit;
+  int64_t kchunk;
+  float* part;
 };
 
 constexpr int GF_T = 64, GF_K = 16;
@@ -64,7 +71,10 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmF32 g) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, hf = lane >> 5;
-  const int64_t b = blockIdx.z;
+  const int64_t b = blockIdx.z / g.nsplit;
+  const int sp = static_cast<int>(blockIdx.z % g.nsplit);
+  const int64_t kb = sp * g.kchunk;
+  const int64_t ke = g.nsplit == 1 ? g.K : (kb + g.kchunk < g.K ? kb + g.kchunk : g.K);
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * GF_T;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * GF_T;
   const float* A = g.A + b * g.sAb;
@@ -78,10 +88,10 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmF32 g) {
       const int e = tid + 256 * l;
       const int mm = aK ? e / GF_K : e % GF_T, kk = aK ? e % GF_K : e / GF_T;
       const int64_t m = m0 + mm, k = k0 + kk;
-      ra[l] = (m < g.M && k < g.K) ? A[m * g.sAm + k * g.sAk] : 0.0f;
+      ra[l] = (m < g.M && k < ke) ? A[m * g.sAm + k * g.sAk] : 0.0f;
       const int nn = bN ? e % GF_T : e / GF_K, kb = bN ? e / GF_T : e % GF_K;
       const int64_t n = n0 + nn, kq = k0 + kb;
-      rb[l] = (n < g.N && kq < g.K) ? B[kq * g.sBk + n * g.sBn] : 0.0f;
+      rb[l] = (n < g.N && kq < ke) ? B[kq * g.sBk + n * g.sBn] : 0.0f;
     }
   };
   auto stash = [&]() {
@@ -95,11 +105,11 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmF32 g) {
   f32x16_t acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-  fetch(0);
+  fetch(kb);
   stash();
   __syncthreads();
-  for (int64_t k0 = 0; k0 < g.K; k0 += GF_K) {
-    const bool more = k0 + GF_K < g.K;
+  for (int64_t k0 = kb; k0 < ke; k0 += GF_K) {
+    const bool more = k0 + GF_K < ke;
     if (more) fetch(k0 + GF_K);
 #pragma unroll
     for (int ks = 0; ks < GF_K / 2; ++ks) {
@@ -115,10 +125,19 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmF32 g) {
   }
   // Lane l, register v holds row 8 (v / 4) + 4 hf + v % 4, column l % 32 of
   // the wave's block.
-  float* C = g.C + b * g.sCb;
-  const float* D = g.D ? g.D + b * g.sDb : nullptr;
   const int64_t n = n0 + 32 * wn + l32;
   if (n >= g.N) return;
+  if (g.nsplit > 1) {
+    float* Pp = g.part + blockIdx.z * g.M * g.N;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t m = m0 + 32 * wm + 8 * (v / 4) + 4 * hf + (v % 4);
+      if (m < g.M) Pp[m * g.N + n] = g.alpha * acc[v];
+    }
+    return;
+  }
+  float* C = g.C + b * g.sCb;
+  const float* D = g.D ? g.D + b * g.sDb : nullptr;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int64_t m = m0 + 32 * wm + 8 * (v / 4) + 4 * hf + (v % 4);
@@ -126,6 +145,17 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmF32 g) {
     const float base = D ? D[m * g.ldd + n] : 0.0f;
     C[m * g.ldc + n] = base + g.alpha * acc[v];
   }
+}
+
+// C = D + the nsplit partials of a K-split product, added in split order.
+__global__ __launch_bounds__(256) void k_gemm_split_sum(GemmF32 g, int64_t BH) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t MN = g.M * g.N;
+  if (i >= BH * MN) return;
+  const int64_t b = i / MN, e = i % MN, m = e / g.N, n = e % g.N;
+  float acc = g.D ? g.D[b * g.sDb + m * g.ldd + n] : 0.0f;
+  for (int sp = 0; sp < g.nsplit; ++sp) acc += g.part[(b * g.nsplit + sp) * MN + e];
+  g.C[b * g.sCb + m * g.ldc + n] = acc;
 }
 
 __device__ __forceinline__ float sig_acc(float x) { return 1.0f / (1.0f + expf(-x)); }

@@ -338,8 +338,30 @@ def backward_bench_swiglu(with_oracle, reps=10):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     flops = 90.0 * d * h * L * B * H
+    # The same backward given the chunk-start states kept by the forward
+    # (e2ttt_chunk_forward_states), which skips the forward re-run.
+    nC = (L + C - 1) // C
+    Wk = torch.empty((nC - 1, B, H, P), device="cuda")
+    Mk = torch.empty((nC - 1, B, H, P), device="cuda")
+    fws = torch.empty(cwu.workspace_bytes(prob), dtype=torch.uint8, device="cuda")
+    o_, We_, Me_ = (torch.empty_like(t["q"]), torch.empty_like(t["W0"]), torch.empty_like(t["W0"]))
+    cwu.chunk_forward_states(prob, *[t[n] for n in names], o_, We_, Me_, Wk, Mk, fws)
+
+    def call_kept():
+        cwu.chunk_backward(prob, *[t[n] for n in names], dout, dW, dM,
+                           *[g[n] for n in names], ws, W_starts=Wk, M_starts=Mk)
+    for _ in range(3):
+        call_kept()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        call_kept()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_kept = e0.elapsed_time(e1) / reps
     out = {"label": "outer-loop backward of the chunk forward, SwiGLU learner, fp32 "
                     "(not the main metric)",
+           "ms_per_call_with_kept_states": ms_kept,
            "config": {"workload": f"swiglu-d{d}h{h}-b{B}h{H}-l{L}-c{C}-fp32"},
            "ms_per_call": ms, "tokens_per_s": B * H * L / (ms * 1e-3),
            "tflops_algorithmic": flops / (ms * 1e-3) / 1e12,

@@ -66,7 +66,8 @@ _lib = None
 EXPORTED = ("e2ttt_validate", "e2ttt_workspace_bytes", "e2ttt_chunk_forward",
             "e2ttt_scalar_kernels", "e2ttt_chunk_forward_timed", "e2ttt_status_string",
             "e2ttt_decode_workspace_bytes", "e2ttt_decode_step",
-            "e2ttt_backward_workspace_bytes", "e2ttt_chunk_backward")
+            "e2ttt_backward_workspace_bytes", "e2ttt_chunk_backward",
+            "e2ttt_chunk_forward_states", "e2ttt_chunk_backward_states")
 
 # e2ttt_kernel_class
 KERNEL_SCAN, KERNEL_PREP, KERNEL_FWD13, KERNEL_FWD2, KERNEL_BWD, KERNEL_AGG = range(6)
@@ -112,6 +113,10 @@ def lib() -> ctypes.CDLL:
             L.e2ttt_backward_workspace_bytes.restype = ctypes.c_int
             L.e2ttt_chunk_backward.argtypes = [P] + [vp] * 20 + [ctypes.c_size_t, vp]
             L.e2ttt_chunk_backward.restype = ctypes.c_int
+            L.e2ttt_chunk_forward_states.argtypes = [P] + [vp] * 14 + [ctypes.c_size_t, vp]
+            L.e2ttt_chunk_forward_states.restype = ctypes.c_int
+            L.e2ttt_chunk_backward_states.argtypes = [P] + [vp] * 22 + [ctypes.c_size_t, vp]
+            L.e2ttt_chunk_backward_states.restype = ctypes.c_int
             L.e2ttt_status_string.argtypes = [ctypes.c_int]
             L.e2ttt_status_string.restype = ctypes.c_char_p
             _lib = L
@@ -164,6 +169,24 @@ def chunk_forward(prob: Problem, q, k, v, eta, alpha, beta, W0, M0, out, W_end, 
         int(workspace_nbytes), _stream(stream))
     if check and st != OK:
         raise E2tttError(st, "e2ttt_chunk_forward")
+    return st
+
+
+def chunk_forward_states(prob: Problem, q, k, v, eta, alpha, beta, W0, M0, out, W_end,
+                         M_end, W_starts, M_starts, workspace,
+                         workspace_nbytes: Optional[int] = None, stream=None,
+                         check: bool = True) -> int:
+    """Call ``e2ttt_chunk_forward_states``: chunk_forward that also writes the
+    states at the starts of chunks 1 .. nC-1 ([nC-1, B, H, P] fp32 each), for
+    e2ttt_chunk_backward_states.  Returns the status."""
+    if workspace_nbytes is None:
+        workspace_nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().e2ttt_chunk_forward_states(
+        ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(alpha), _ptr(beta),
+        _ptr(W0), _ptr(M0), _ptr(out), _ptr(W_end), _ptr(M_end), _ptr(W_starts), _ptr(M_starts),
+        _ptr(workspace), int(workspace_nbytes), _stream(stream))
+    if check and st != OK:
+        raise E2tttError(st, "e2ttt_chunk_forward_states")
     return st
 
 
@@ -233,21 +256,32 @@ def backward_workspace_bytes(prob: Problem) -> int:
 def chunk_backward(prob: Problem, q, k, v, eta, alpha, beta, W0, M0, dout, dW_end, dM_end,
                    dq, dk, dv, deta, dalpha, dbeta, dW0, dM0, workspace,
                    workspace_nbytes: Optional[int] = None, stream=None,
-                   check: bool = True) -> int:
-    """Call ``e2ttt_chunk_backward`` (linear and SwiGLU learners, fp32):
-    gradients of a loss
-    with respect to every input of the chunk forward, given its gradients
-    dout, dW_end, dM_end (the last two may be None).  Returns the status;
-    raises on failure when ``check``."""
+                   check: bool = True, W_starts=None, M_starts=None) -> int:
+    """Call ``e2ttt_chunk_backward`` (linear and SwiGLU learners, fp32 or bf16
+    io): gradients of a loss with respect to every input of the chunk
+    forward, given its gradients dout, dW_end, dM_end (the last two may be
+    None).  With ``W_starts``/``M_starts`` (the chunk-start states kept by
+    ``chunk_forward_states``) it calls ``e2ttt_chunk_backward_states``, which
+    skips the forward re-run.  Returns the status; raises on failure when
+    ``check``."""
     if workspace_nbytes is None:
         workspace_nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().e2ttt_chunk_backward(
-        ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(alpha), _ptr(beta),
-        _ptr(W0), _ptr(M0), _ptr(dout), _ptr(dW_end), _ptr(dM_end), _ptr(dq), _ptr(dk),
-        _ptr(dv), _ptr(deta), _ptr(dalpha), _ptr(dbeta), _ptr(dW0), _ptr(dM0), _ptr(workspace),
-        int(workspace_nbytes), _stream(stream))
+    if W_starts is None and M_starts is None:
+        name = "e2ttt_chunk_backward"
+        st = lib().e2ttt_chunk_backward(
+            ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(alpha), _ptr(beta),
+            _ptr(W0), _ptr(M0), _ptr(dout), _ptr(dW_end), _ptr(dM_end), _ptr(dq), _ptr(dk),
+            _ptr(dv), _ptr(deta), _ptr(dalpha), _ptr(dbeta), _ptr(dW0), _ptr(dM0),
+            _ptr(workspace), int(workspace_nbytes), _stream(stream))
+    else:
+        name = "e2ttt_chunk_backward_states"
+        st = lib().e2ttt_chunk_backward_states(
+            ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(alpha), _ptr(beta),
+            _ptr(W0), _ptr(M0), _ptr(W_starts), _ptr(M_starts), _ptr(dout), _ptr(dW_end),
+            _ptr(dM_end), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(deta), _ptr(dalpha), _ptr(dbeta),
+            _ptr(dW0), _ptr(dM0), _ptr(workspace), int(workspace_nbytes), _stream(stream))
     if check and st != OK:
-        raise E2tttError(st, "e2ttt_chunk_backward")
+        raise E2tttError(st, name)
     return st
 
 

@@ -53,6 +53,9 @@ struct Plan {
   bool tile256 = false;  // generic path: forward GEMMs on 256x256 tiles
   int nsplitB;  // phase B token split (1: fused state epilogue)
   size_t opsz;  // bytes per GEMM operand element (2 for bf16, 4 for fp32)
+  // Optional output: the states at the starts of chunks 1 .. nC-1, [nC-1][BH][P] each.
+  float* saveW;
+  float* saveM;
   // workspace offsets (bytes)
   size_t kw, km, coef, kt, w13s, w2s, w2ts, zrow, a1s, a3s, grow, ut, gt, zt, gw, gm, gbf, gft,
       part, part256, qn, kn, total;
@@ -325,6 +328,14 @@ ScanArgs scan_args(const Plan& q, const float* eta, const float* alpha, const fl
   return sa;
 }
 
+// After chunk r: keep a copy of the state that chunk r+1 starts from.
+void save_state(const Plan& q, int64_t r, const float* Wend, const float* Mend, hipStream_t st) {
+  if (!q.saveW || r + 1 >= q.nC) return;
+  const int64_t n = q.BH * q.P;
+  hipLaunchKernelGGL(k_copy2, dim3(grid1((n + 255) / 256)), dim3(256), 0, st, Wend, Mend,
+                     q.saveW + r * n, q.saveM + r * n, n);
+}
+
 void launch_scan(const Plan& q, const float* eta, const float* alpha, const float* beta,
                  float* kw, float* km, int64_t ustride, int64_t rstride, int64_t pad,
                  float* coef, int cstride, hipStream_t st, Instr& I) {
@@ -442,6 +453,7 @@ void launch_swiglu(const Plan& q, const void* qv, const void* kv, const void* vv
                    Wend, Mend, w13s, w2s, w2ts);
     }
     if (q.rownorm) launch_rownorm<T>(q, s, Wend, r + 1 < q.nC, w13s, w2s, w2ts, st);
+    save_state(q, r, Wend, Mend, st);
   }
 }
 
@@ -513,6 +525,7 @@ void launch_fused(const Plan& q, const void* qv, const void* kv, const void* vv,
                    dim3(256), 0, st, a);
     if (q.rownorm)
       launch_rownorm<bf16_t>(q, s, Wend, r + 1 < q.nC, a.w13s, a.w2s, a.w2ts, st);
+    save_state(q, r, Wend, Mend, st);
   }
 }
 
@@ -545,6 +558,7 @@ void launch_linear(const Plan& q, const void* qv, const void* kv, const void* vv
                  dim3(256), lds_a, st, s, ri, K, gw, gm, coef, Win, Min, Wend, Mend);
     if (q.rownorm)
       launch_rownorm<float>(q, s, Wend, false, nullptr, nullptr, nullptr, st);
+    save_state(q, r, Wend, Mend, st);
   }
 }
 
@@ -582,10 +596,14 @@ e2ttt_status forward_impl(const e2ttt_problem* prob, const void* q, const void* 
                           const float* eta, const float* alpha, const float* beta,
                           const float* W0, const float* M0, void* out, float* W_end,
                           float* M_end, void* workspace, size_t workspace_bytes, void* stream,
-                          Instr& I) {
+                          Instr& I, float* W_starts = nullptr, float* M_starts = nullptr,
+                          bool want_starts = false) {
   Plan pl;
   e2ttt_status status = make_plan(prob, &pl);
   if (status != E2TTT_OK) return status;
+  const bool keep = want_starts && pl.nC > 1;
+  if (keep && (!W_starts || !M_starts || !aligned(W_starts, 16) || !aligned(M_starts, 16)))
+    return E2TTT_EINVAL;
   if (!W0 || !M0 || !W_end || !M_end) return E2TTT_EINVAL;
   const bool empty = pl.L == 0;
   if (!empty && (!q || !k || !v || !eta || !alpha || !beta || !out)) return E2TTT_EINVAL;
@@ -604,9 +622,11 @@ e2ttt_status forward_impl(const e2ttt_problem* prob, const void* q, const void* 
                       rng(beta, ns), rng(W0, np), rng(M0, np)};
   const Range o_out = rng(out, nx), o_w = rng(W_end, np), o_m = rng(M_end, np),
               o_ws = rng(workspace, empty ? 0 : pl.total);
-  const Range outs[] = {o_out, o_w, o_m, o_ws};
-  for (int a = 0; a < 4; ++a) {
-    for (int b = a + 1; b < 4; ++b)
+  const size_t nst = keep ? np * static_cast<size_t>(pl.nC - 1) : 0;
+  const Range outs[] = {o_out, o_w, o_m, o_ws, rng(keep ? W_starts : nullptr, nst),
+                        rng(keep ? M_starts : nullptr, nst)};
+  for (int a = 0; a < 6; ++a) {
+    for (int b = a + 1; b < 6; ++b)
       if (overlap(outs[a], outs[b])) return E2TTT_EINVAL;
     for (int i = 0; i < 8; ++i) {
       if (!overlap(outs[a], in[i])) continue;
@@ -621,6 +641,10 @@ e2ttt_status forward_impl(const e2ttt_problem* prob, const void* q, const void* 
   set_lds_attributes();
   (void)hipGetLastError();  // clear a stale error so only our launches are reported
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (keep) {
+    pl.saveW = W_starts;
+    pl.saveM = M_starts;
+  }
   if (empty) {
     if (W_end != W0 || M_end != M0) {
       const int64_t n = pl.BH * pl.P;
@@ -679,6 +703,17 @@ e2ttt_status e2ttt_chunk_forward(const e2ttt_problem* prob, const void* q, const
   Instr none;
   return forward_impl(prob, q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end, workspace,
                       workspace_bytes, stream, none);
+}
+
+e2ttt_status e2ttt_chunk_forward_states(const e2ttt_problem* prob, const void* q,
+                                        const void* k, const void* v, const float* eta,
+                                        const float* alpha, const float* beta, const float* W0,
+                                        const float* M0, void* out, float* W_end, float* M_end,
+                                        float* W_starts, float* M_starts, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  Instr none;
+  return forward_impl(prob, q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end, workspace,
+                      workspace_bytes, stream, none, W_starts, M_starts, true);
 }
 
 e2ttt_status e2ttt_chunk_forward_timed(const e2ttt_problem* prob, const void* q, const void* k,
@@ -965,7 +1000,8 @@ GemmF32 gf(int64_t M, int64_t N, int64_t K, const float* A, int64_t sAb, int64_t
 void swiglu_backward(const BwdPlan& bp, char* ws, const float* Q, const float* K,
                      const float* V, const float* W0, const float* M0, const float* DO,
                      const float* dWC, const float* dMC, float* dq, float* dk, float* dv,
-                     float* dW0, float* dM0, hipStream_t s) {
+                     float* dW0, float* dM0, const float* Wsv, const float* Msv,
+                     hipStream_t s) {
   const Plan& q = bp.f;
   auto wsf = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   const Shape sh{q.BH, q.L, q.d, q.h, q.C, q.Cp, q.nC, q.krep};
@@ -976,11 +1012,16 @@ void swiglu_backward(const BwdPlan& bp, char* ws, const float* Q, const float* K
   float* coef = wsf(q.coef);
   auto Wst = [&](int64_t r) -> float* { return wsf(bp.wst) + r * nP; };
   auto Mst = [&](int64_t r) -> float* { return wsf(bp.mst) + r * nP; };
-  auto Win = [&](int64_t r) -> const float* { return r == 0 ? W0 : Wst(r); };
-  auto Min = [&](int64_t r) -> const float* { return r == 0 ? M0 : Mst(r); };
+  // Chunk-start states: the caller's (from e2ttt_chunk_forward_states) or re-run.
+  auto Win = [&](int64_t r) -> const float* {
+    return r == 0 ? W0 : Wsv ? Wsv + (r - 1) * nP : Wst(r);
+  };
+  auto Min = [&](int64_t r) -> const float* {
+    return r == 0 ? M0 : Msv ? Msv + (r - 1) * nP : Mst(r);
+  };
   // Forward re-run (the generic chunk kernels; the readout goes to dq, which
-  // the backward overwrites for every token).
-  {
+  // the backward overwrites for every token), unless the states were given.
+  if (!Wsv) {
     float* kt = wsf(q.kt);
     float* w13s = wsf(q.w13s);
     float* w2s = wsf(q.w2s);
@@ -1090,7 +1131,8 @@ void swiglu_backward(const BwdPlan& bp, char* ws, const float* Q, const float* K
 void linear_backward(const BwdPlan& bp, char* ws, const float* Q, const float* K,
                      const float* V, const float* W0, const float* M0, const float* DO,
                      const float* dWC, const float* dMC, float* dq, float* dk, float* dv,
-                     float* dW0, float* dM0, hipStream_t s) {
+                     float* dW0, float* dM0, const float* Wsv, const float* Msv,
+                     hipStream_t s) {
   const Plan& pl = bp.f;
   auto wsf = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   const Shape sh{pl.BH, pl.L, pl.d, 0, pl.C, pl.Cp, pl.nC, 1};
@@ -1102,11 +1144,16 @@ void linear_backward(const BwdPlan& bp, char* ws, const float* Q, const float* K
   // the backward overwrites for every token).
   auto Wst = [&](int64_t r) -> float* { return wsf(bp.wst) + r * nP; };
   auto Mst = [&](int64_t r) -> float* { return wsf(bp.mst) + r * nP; };
-  auto Win = [&](int64_t r) -> const float* { return r == 0 ? W0 : Wst(r); };
-  auto Min = [&](int64_t r) -> const float* { return r == 0 ? M0 : Mst(r); };
+  // Chunk-start states: the caller's (from e2ttt_chunk_forward_states) or re-run.
+  auto Win = [&](int64_t r) -> const float* {
+    return r == 0 ? W0 : Wsv ? Wsv + (r - 1) * nP : Wst(r);
+  };
+  auto Min = [&](int64_t r) -> const float* {
+    return r == 0 ? M0 : Msv ? Msv + (r - 1) * nP : Mst(r);
+  };
   const size_t lds_f = static_cast<size_t>(pl.d * (pl.d + 1) + LIN_FWD_TB * (pl.d + 1)) * sizeof(float);
   const size_t lds_a = static_cast<size_t>(2 * 64 * 16 + 64 * pl.d) * sizeof(float);
-  for (int64_t r = 0; r + 1 < pl.nC; ++r) {
+  for (int64_t r = 0; !Wsv && r + 1 < pl.nC; ++r) {
     const int ri = static_cast<int>(r);
     hipLaunchKernelGGL(k_lin_fwd<float>, dim3(grid1(pl.BH * (2 * pl.Cp / LIN_FWD_TB))), dim3(256), lds_f,
                        s, sh, ri, Q, K, V, Win(r), kw, km, dq, wsf(pl.gw), wsf(pl.gm));
@@ -1160,18 +1207,23 @@ e2ttt_status e2ttt_backward_workspace_bytes(const e2ttt_problem* prob, size_t* b
   return E2TTT_OK;
 }
 
-e2ttt_status e2ttt_chunk_backward(const e2ttt_problem* prob, const void* q, const void* k,
-                                  const void* v, const float* eta, const float* alpha,
-                                  const float* beta, const float* W0, const float* M0,
-                                  const void* dout, const float* dW_end, const float* dM_end,
-                                  void* dq, void* dk, void* dv, float* deta, float* dalpha,
-                                  float* dbeta, float* dW0, float* dM0, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+namespace {
+
+e2ttt_status backward_impl(const e2ttt_problem* prob, const void* q, const void* k,
+                           const void* v, const float* eta, const float* alpha,
+                           const float* beta, const float* W0, const float* M0,
+                           const void* dout, const float* dW_end, const float* dM_end,
+                           const float* W_starts, const float* M_starts, void* dq, void* dk,
+                           void* dv, float* deta, float* dalpha, float* dbeta, float* dW0,
+                           float* dM0, void* workspace, size_t workspace_bytes, void* stream) {
   BwdPlan bp;
   e2ttt_status st = make_bwd_plan(prob, &bp);
   if (st != E2TTT_OK) return st;
   const Plan& pl = bp.f;
   const bool empty = pl.L == 0;
+  if ((W_starts == nullptr) != (M_starts == nullptr)) return E2TTT_EINVAL;
+  const bool keep = W_starts && pl.nC > 1;  // caller-kept chunk-start states
+  if (keep && (!aligned(W_starts, 16) || !aligned(M_starts, 16))) return E2TTT_EINVAL;
   if (!W0 || !M0 || !dW0 || !dM0) return E2TTT_EINVAL;
   if (!empty && (!q || !k || !v || !eta || !alpha || !beta || !dout || !dq || !dk || !dv ||
                  !deta || !dalpha || !dbeta || !workspace))
@@ -1185,13 +1237,15 @@ e2ttt_status e2ttt_chunk_backward(const e2ttt_problem* prob, const void* q, cons
   const size_t nx = static_cast<size_t>(pl.BH * pl.L * pl.d) * (bp.bf16io ? 2 : 4);
   const size_t ns = static_cast<size_t>(pl.BH * pl.L) * 4;
   const size_t np = static_cast<size_t>(pl.BH * pl.P) * 4;
+  const size_t nst = keep ? np * static_cast<size_t>(pl.nC - 1) : 0;
   const Range in[] = {rng(q, nx), rng(k, nx), rng(v, nx), rng(eta, ns), rng(alpha, ns),
                       rng(beta, ns), rng(W0, np), rng(M0, np), rng(dout, nx),
-                      rng(dW_end, np), rng(dM_end, np)};
+                      rng(dW_end, np), rng(dM_end, np), rng(keep ? W_starts : nullptr, nst),
+                      rng(keep ? M_starts : nullptr, nst)};
   const Range outs[] = {rng(dq, nx), rng(dk, nx), rng(dv, nx), rng(deta, ns),
                         rng(dalpha, ns), rng(dbeta, ns), rng(dW0, np), rng(dM0, np),
                         rng(workspace, empty ? 0 : bp.total)};
-  constexpr int NO = 9, NI = 11;
+  constexpr int NO = 9, NI = 13;
   for (int a = 0; a < NO; ++a) {
     for (int b = a + 1; b < NO; ++b)
       if (overlap(outs[a], outs[b])) return E2TTT_EINVAL;
@@ -1247,9 +1301,10 @@ e2ttt_status e2ttt_chunk_backward(const e2ttt_problem* prob, const void* q, cons
   }
   void (*run)(const BwdPlan&, char*, const float*, const float*, const float*, const float*,
               const float*, const float*, const float*, const float*, float*, float*, float*,
-              float*, float*, hipStream_t) =
+              float*, float*, const float*, const float*, hipStream_t) =
       pl.kind == E2TTT_SWIGLU ? swiglu_backward : linear_backward;
-  run(bp, ws, Q, K, V, W0, M0, DO, dWC, dMC, dQ, dK, dV, dW0, dM0, s);
+  run(bp, ws, Q, K, V, W0, M0, DO, dWC, dMC, dQ, dK, dV, dW0, dM0, keep ? W_starts : nullptr,
+      keep ? M_starts : nullptr, s);
   if (bp.bf16io) {
     bf16_t* dst[] = {static_cast<bf16_t*>(dq), static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv)};
     const float* src[] = {dQ, dK, dV};
@@ -1263,6 +1318,34 @@ e2ttt_status e2ttt_chunk_backward(const e2ttt_problem* prob, const void* q, cons
                      static_cast<int>(bp.nrb), reinterpret_cast<double*>(ws + bp.bcp), deta,
                      dalpha, dbeta);
   return hipGetLastError() == hipSuccess ? E2TTT_OK : E2TTT_EHIP;
+}
+
+}  // namespace
+
+e2ttt_status e2ttt_chunk_backward(const e2ttt_problem* prob, const void* q, const void* k,
+                                  const void* v, const float* eta, const float* alpha,
+                                  const float* beta, const float* W0, const float* M0,
+                                  const void* dout, const float* dW_end, const float* dM_end,
+                                  void* dq, void* dk, void* dv, float* deta, float* dalpha,
+                                  float* dbeta, float* dW0, float* dM0, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return backward_impl(prob, q, k, v, eta, alpha, beta, W0, M0, dout, dW_end, dM_end, nullptr,
+                       nullptr, dq, dk, dv, deta, dalpha, dbeta, dW0, dM0, workspace,
+                       workspace_bytes, stream);
+}
+
+e2ttt_status e2ttt_chunk_backward_states(const e2ttt_problem* prob, const void* q,
+                                         const void* k, const void* v, const float* eta,
+                                         const float* alpha, const float* beta, const float* W0,
+                                         const float* M0, const float* W_starts,
+                                         const float* M_starts, const void* dout,
+                                         const float* dW_end, const float* dM_end, void* dq,
+                                         void* dk, void* dv, float* deta, float* dalpha,
+                                         float* dbeta, float* dW0, float* dM0, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  return backward_impl(prob, q, k, v, eta, alpha, beta, W0, M0, dout, dW_end, dM_end, W_starts,
+                       M_starts, dq, dk, dv, deta, dalpha, dbeta, dW0, dM0, workspace,
+                       workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -154,6 +154,23 @@ E2TTT_API e2ttt_status e2ttt_chunk_forward(const e2ttt_problem* prob, const void
                                  float* M_end, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/* e2ttt_chunk_forward that also keeps, for training, the state each chunk
+ * starts from (the chunk-to-chunk carry of §3.2: (W_C, M_C) of chunk r is the
+ * start of chunk r+1), so that e2ttt_chunk_backward_states need not recompute
+ * them.  W_starts, M_starts: [nC-1][B,H,P] fp32 (nC = ceil(L / chunk)); slot
+ * r - 1 holds the state at the start of chunk r, after the chunk-boundary
+ * normalisation when that flag is set.  Both must be non-null, 16-byte aligned
+ * and overlap nothing else when nC > 1 (EINVAL); with nC <= 1 they are not
+ * touched.  Everything else as e2ttt_chunk_forward, same workspace. */
+E2TTT_API e2ttt_status e2ttt_chunk_forward_states(const e2ttt_problem* prob, const void* q,
+                                                  const void* k, const void* v,
+                                                  const float* eta, const float* alpha,
+                                                  const float* beta, const float* W0,
+                                                  const float* M0, void* out, float* W_end,
+                                                  float* M_end, float* W_starts,
+                                                  float* M_starts, void* workspace,
+                                                  size_t workspace_bytes, void* stream);
+
 /* The per-token scalar kernels alone (§3.2, App. A.2-A.3), for every chunk:
  *   k_w[b,h,t] = K^W_t = eta_t * beta~_t * R_t  (weight kernel)
  *   k_m[b,h,t] = K^M_t = eta_t * beta~_t        (momentum kernel)
@@ -288,6 +305,24 @@ E2TTT_API e2ttt_status e2ttt_chunk_backward(const e2ttt_problem* prob, const voi
                                             float* dbeta, float* dW0, float* dM0,
                                             void* workspace, size_t workspace_bytes,
                                             void* stream);
+
+/* e2ttt_chunk_backward given the chunk-start states kept by
+ * e2ttt_chunk_forward_states for the same problem and inputs (read-only, must
+ * not overlap an output; EINVAL when only one of the two is null).  The
+ * forward re-run is skipped; the gradients are those of the forward whose
+ * states were kept (for bf16 io that is the bf16 forward, rather than the fp32
+ * re-run).  Both null: identical to e2ttt_chunk_backward.  Same workspace. */
+E2TTT_API e2ttt_status e2ttt_chunk_backward_states(const e2ttt_problem* prob, const void* q,
+                                                   const void* k, const void* v,
+                                                   const float* eta, const float* alpha,
+                                                   const float* beta, const float* W0,
+                                                   const float* M0, const float* W_starts,
+                                                   const float* M_starts, const void* dout,
+                                                   const float* dW_end, const float* dM_end,
+                                                   void* dq, void* dk, void* dv, float* deta,
+                                                   float* dalpha, float* dbeta, float* dW0,
+                                                   float* dM0, void* workspace,
+                                                   size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

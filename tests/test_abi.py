@@ -278,3 +278,32 @@ def test_backward_host_errors(mutate, expected):
         assert bwd_call(prob, a) == expected
     bad = swiglu(flags=cwu.FLAG_POST_CHUNK_ROW_L2)
     assert bwd_call(bad, bwd_fake_args(linear())) == cwu.EUNSUPPORTED
+
+
+def test_state_keeping_entry_points_host_checks():
+    """e2ttt_chunk_forward_states needs both state buffers when there is more
+    than one chunk; e2ttt_chunk_backward_states takes both or neither; kept
+    states may not overlap an output."""
+    f = Fake()
+    prob = linear()  # L = 256, C = 64: 4 chunks, 3 kept states
+    B, H, L, d = prob.batch, prob.heads, prob.seq_len, prob.dim
+    nx, ns, np_ = B * H * L * d * 4, B * H * L * 4, B * H * d * d * 4
+    args = [f(nx), f(nx), f(nx), f(ns), f(ns), f(ns), f(np_), f(np_), f(nx), f(np_), f(np_)]
+    Ws, Ms = f(3 * np_), f(3 * np_)
+    nws = cwu.workspace_bytes(prob)
+    ws = f(nws)
+    call = lambda W, M: cwu.chunk_forward_states(prob, *args, W, M, ws, nws, stream=0,
+                                                 check=False)
+    assert call(None, Ms) == cwu.EINVAL
+    assert call(Ws, None) == cwu.EINVAL
+    assert call(Ws, Ws + 16) == cwu.EINVAL          # the two overlap
+    assert call(Ws, args[9]) == cwu.EINVAL          # M_starts over W_end
+    a = bwd_fake_args(prob)
+    bcall = lambda W, M: cwu.chunk_backward(
+        prob, a["q"], a["k"], a["v"], a["eta"], a["alpha"], a["beta"], a["W0"], a["M0"],
+        a["dout"], a["dW_end"], a["dM_end"], a["dq"], a["dk"], a["dv"], a["deta"],
+        a["dalpha"], a["dbeta"], a["dW0"], a["dM0"], a["workspace"], a["nws"], stream=0,
+        check=False, W_starts=W, M_starts=M)
+    assert bcall(Ws, None) == cwu.EINVAL
+    assert bcall(a["dq"], Ms) == cwu.EINVAL         # kept states over an output
+    assert bcall(Ws + 4, Ms) == cwu.EINVAL          # misaligned

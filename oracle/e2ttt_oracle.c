@@ -86,6 +86,34 @@ static void silu_l2_rows(double* x, int64_t L, int64_t d) {
   }
 }
 
+/* Reverse mode of silu_l2_rows: g holds, per row, the adjoint of the
+ * normalised vector y = s / max(||s||, 1e-12), s = silu(x); it is replaced by
+ * the adjoint of the raw x.  With n = ||s|| > 1e-12:
+ *   ds = (g - y (y . g)) / n,   dx = ds * silu'(x),  silu'(x) = sigma (1 + x (1 - sigma));
+ * below the floor the divisor is the constant 1e-12 and ds = g / 1e-12. */
+static void silu_l2_rows_vjp(const double* x, double* g, int64_t L, int64_t d) {
+  for (int64_t t = 0; t < L; ++t) {
+    const double* xr = x + t * d;
+    double* gr = g + t * d;
+    double ss = 0.0;
+    for (int64_t i = 0; i < d; ++i) {
+      const double si = xr[i] * sigm(xr[i]);
+      ss += si * si;
+    }
+    const double n = sqrt(ss);
+    const double den = n < 1e-12 ? 1e-12 : n;
+    double dot = 0.0;
+    if (n >= 1e-12)
+      for (int64_t i = 0; i < d; ++i) dot += (xr[i] * sigm(xr[i]) / den) * gr[i];
+    for (int64_t i = 0; i < d; ++i) {
+      const double sg = sigm(xr[i]);
+      const double yi = xr[i] * sg / den;
+      const double ds = (gr[i] - (n >= 1e-12 ? yi * dot : 0.0)) / den;
+      gr[i] = ds * (sg * (1.0 + xr[i] * (1.0 - sg)));
+    }
+  }
+}
+
 /* gamma_t from the per-token scalars (Eq. 14, or alpha taken as gamma). */
 static double decay_factor(int decay_mode, double eta, double alpha) {
   if (decay_mode == OR_ALPHA_IS_GAMMA) return alpha;
@@ -664,8 +692,10 @@ static void readout_vjp(int kind, int64_t d, int64_t h, const double* Ws,
  *     chunk is processed;
  *   - gamma_t = 1 - eta_t alpha_t (Eq. 14): deta_t -= alpha_t dgamma,
  *     dalpha_t = -eta_t dgamma; with alpha taken as gamma, dalpha_t = dgamma.
- * The chunk-averaged variant and the q/k and row-normalisation options are
- * not covered.  dWend or dMend may be NULL (zero).  h is the SwiGLU hidden
+ * With qk_norm != 0 the q/k prologue (SiLU, then L2 per token) runs first, as
+ * in the forward, and dq, dk are mapped back through it (silu_l2_rows_vjp).
+ * The chunk-averaged variant and the row-normalisation option are not
+ * covered.  dWend or dMend may be NULL (zero).  h is the SwiGLU hidden
  * width (ignored for linear).  Returns 0 on success, 1 on bad arguments,
  * 2 on allocation failure, 3 for an unknown learner.
  */
@@ -678,7 +708,7 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
                           const double* dWend, const double* dMend,
                           double* dq, double* dk, double* dv, double* deta,
                           double* dalpha, double* dbeta, double* dW0,
-                          double* dM0) {
+                          double* dM0, int qk_norm) {
   if (kind != OR_LINEAR && kind != OR_SWIGLU) return 3;
   if (decay_mode != OR_GAMMA_1_MINUS_ETA_ALPHA &&
       decay_mode != OR_ALPHA_IS_GAMMA)
@@ -690,9 +720,22 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
   const int64_t Cmax = C < L ? C : (L > 0 ? L : 1);
   const int64_t nscr = 16 * (kind == OR_LINEAR ? 1 : h) + 4 * d;
 
+  double* qkn = NULL; /* normalised q | k of one unit (q/k prologue) */
+  if (qk_norm && L > 0) {
+    qkn = (double*)malloc(sizeof(double) * (size_t)(2 * L * d));
+    if (!qkn) return 2;
+  }
   for (int64_t u = 0; u < B * H; ++u) {
     const double* qu = q + u * L * d;
     const double* ku = k + u * L * d;
+    if (qkn) {
+      memcpy(qkn, qu, sizeof(double) * (size_t)(L * d));
+      memcpy(qkn + L * d, ku, sizeof(double) * (size_t)(L * d));
+      silu_l2_rows(qkn, L, d);
+      silu_l2_rows(qkn + L * d, L, d);
+      qu = qkn;
+      ku = qkn + L * d;
+    }
     const double* vu = v + u * L * d;
     const double* etu = eta + u * L;
     const double* alu = alpha + u * L;
@@ -723,7 +766,7 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
     if (!Wst || !Mst || !Wb || !Mb || !Gt || !W || !M || !dW || !dM || !dMt || !dG ||
         !dWs || !scr) {
       free(Wst); free(Mst); free(Wb); free(Mb); free(Gt); free(W); free(M);
-      free(dW); free(dM); free(dMt); free(dG); free(dWs); free(scr);
+      free(dW); free(dM); free(dMt); free(dG); free(dWs); free(scr); free(qkn);
       return 2;
     }
 
@@ -807,8 +850,13 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
     }
     memcpy(dW0 + u * P, dW, sizeof(double) * (size_t)P);
     memcpy(dM0 + u * P, dM, sizeof(double) * (size_t)P);
+    if (qkn) { /* back through the prologue, from the raw inputs */
+      silu_l2_rows_vjp(q + u * L * d, dqu, L, d);
+      silu_l2_rows_vjp(k + u * L * d, dku, L, d);
+    }
     free(Wst); free(Mst); free(Wb); free(Mb); free(Gt); free(W); free(M);
     free(dW); free(dM); free(dMt); free(dG); free(dWs); free(scr);
   }
+  free(qkn);
   return 0;
 }

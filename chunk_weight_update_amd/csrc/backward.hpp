@@ -40,6 +40,50 @@ __global__ __launch_bounds__(256) void k_convert(const S* __restrict__ src, D* _
   if (i < n) dst[i] = from_f32<D>(to_f32<S>(src[i]));
 }
 
+// Reverse mode of the q/k prologue (SiLU, then L2 per token, §4): dy is the
+// adjoint of y = s / max(||s||, 1e-12), s = silu(x); writes the adjoint of x:
+//   dx = (dy - y (y . dy)) / ||s|| * silu'(x)   (dy / 1e-12 * silu'(x) below the floor).
+// One wave per row, as the forward prologue (rows of up to 1024 features).
+__global__ __launch_bounds__(256) void k_qk_norm_bwd(const float* __restrict__ x,
+                                                     const float* __restrict__ dy,
+                                                     float* __restrict__ dx, int64_t rows,
+                                                     int64_t d) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float* xr = x + row * d;
+  const float* gr = dy + row * d;
+  float* outr = dx + row * d;
+  float s[16], g[16];
+  float ss = 0.0f, sg = 0.0f;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const int64_t e = lane + 64 * m;
+    const float v = e < d ? xr[e] : 0.0f;
+    s[m] = v * sigmoidf_(v);
+    g[m] = e < d ? gr[e] : 0.0f;
+    ss = fmaf(s[m], s[m], ss);
+    sg = fmaf(s[m], g[m], sg);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    ss += __shfl_xor(ss, off, 64);
+    sg += __shfl_xor(sg, off, 64);
+  }
+  const float n = sqrtf(ss);
+  const bool above = n >= 1e-12f;
+  const float inv = 1.0f / (above ? n : 1e-12f);
+  const float dot = above ? sg * inv : 0.0f;  // y . dy
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const int64_t e = lane + 64 * m;
+    if (e >= d) continue;
+    const float v = xr[e], sgm = sigmoidf_(v);
+    const float ds = (g[m] - s[m] * inv * dot) * inv;
+    outr[e] = ds * (sgm * (1.0f + v * (1.0f - sgm)));
+  }
+}
+
 struct LinBwdArgs {
   Shape s;
   int r;     // chunk index

@@ -909,6 +909,9 @@ struct BwdPlan {
   // bf16 io: fp32 copies of q, k, v, dout and fp32 dq, dk, dv, [BH][L][d]
   bool bf16io;
   size_t xq, xk, xv, xdo, xdq, xdk, xdv;
+  // q/k prologue: normalised q, k and their adjoints, fp32 [BH][L][d]
+  bool qknorm;
+  size_t nq, nk, dnq, dnk;
   size_t total;
 };
 
@@ -926,7 +929,8 @@ e2ttt_status make_bwd_plan(const e2ttt_problem* p, BwdPlan* bp) {
   if (p->io_dtype != E2TTT_F32 && p->io_dtype != E2TTT_BF16) return E2TTT_EINVAL;
   bp->bf16io = p->io_dtype == E2TTT_BF16;
   const Plan& q = bp->f;
-  if (p->flags != 0u) return E2TTT_EUNSUPPORTED;
+  if ((p->flags & ~static_cast<uint32_t>(E2TTT_FLAG_QK_SILU_L2)) != 0u) return E2TTT_EUNSUPPORTED;
+  bp->qknorm = q.qknorm != 0;
   if (q.kind == E2TTT_LINEAR && q.d > 64) return E2TTT_EUNSUPPORTED;
   if (q.kind == E2TTT_SWIGLU && q.BH > 65535) return E2TTT_EUNSUPPORTED;  // grid z
   size_t o = align256(q.total);
@@ -959,6 +963,9 @@ e2ttt_status make_bwd_plan(const e2ttt_problem* p, BwdPlan* bp) {
   }
   if (bp->bf16io)
     for (size_t* b : {&bp->xq, &bp->xk, &bp->xv, &bp->xdo, &bp->xdq, &bp->xdk, &bp->xdv})
+      *b = take(4 * static_cast<size_t>(q.BH * q.L * q.d));
+  if (bp->qknorm)
+    for (size_t* b : {&bp->nq, &bp->nk, &bp->dnq, &bp->dnk})
       *b = take(4 * static_cast<size_t>(q.BH * q.L * q.d));
   bp->total = q.L == 0 ? 0 : o;
   return E2TTT_OK;
@@ -1303,8 +1310,31 @@ e2ttt_status backward_impl(const e2ttt_problem* prob, const void* q, const void*
               const float*, const float*, const float*, const float*, float*, float*, float*,
               float*, float*, const float*, const float*, hipStream_t) =
       pl.kind == E2TTT_SWIGLU ? swiglu_backward : linear_backward;
+  const float* Qraw = Q;
+  const float* Kraw = K;
+  float* dQout = dQ;
+  float* dKout = dK;
+  const unsigned gqk = grid1((pl.BH * pl.L + 3) / 4);
+  if (bp.qknorm) {  // the prologue as in the forward; its reverse mode after the run
+    hipLaunchKernelGGL(k_qk_norm<float>, dim3(gqk), dim3(256), 0, s, Qraw, wsf(bp.nq),
+                       pl.BH * pl.L, pl.d);
+    hipLaunchKernelGGL(k_qk_norm<float>, dim3(gqk), dim3(256), 0, s, Kraw, wsf(bp.nk),
+                       pl.BH * pl.L, pl.d);
+    Q = wsf(bp.nq);
+    K = wsf(bp.nk);
+    dQ = wsf(bp.dnq);
+    dK = wsf(bp.dnk);
+  }
   run(bp, ws, Q, K, V, W0, M0, DO, dWC, dMC, dQ, dK, dV, dW0, dM0, keep ? W_starts : nullptr,
       keep ? M_starts : nullptr, s);
+  if (bp.qknorm) {
+    hipLaunchKernelGGL(k_qk_norm_bwd, dim3(gqk), dim3(256), 0, s, Qraw, dQ, dQout,
+                       pl.BH * pl.L, pl.d);
+    hipLaunchKernelGGL(k_qk_norm_bwd, dim3(gqk), dim3(256), 0, s, Kraw, dK, dKout,
+                       pl.BH * pl.L, pl.d);
+    dQ = dQout;
+    dK = dKout;
+  }
   if (bp.bf16io) {
     bf16_t* dst[] = {static_cast<bf16_t*>(dq), static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv)};
     const float* src[] = {dQ, dK, dV};

@@ -27,17 +27,22 @@ def _upstream(B, H, L, d, h, seed, with_state=True):
     return dout, dW, dM
 
 
-def check(B, H, L, d, h, C, mode=0, regime="default", seed=0, with_state=True):
+def check(B, H, L, d, h, C, mode=0, regime="default", seed=0, with_state=True, kind=SWIGLU,
+          flags=0):
     import oracle
     log(f"swiglu backward case B={B} H={H} L={L} d={d} h={h} C={C} mode={mode} "
         f"regime={regime} seed={seed} state_grads={with_state}")
-    inp = make_inputs(SWIGLU, B, H, L, d, h, F32, seed=seed, regime=regime, m0_scale=0.01)
-    dout, dW, dM = _upstream(B, H, L, d, h, seed, with_state)
-    prob = problem_for(SWIGLU, B, H, L, d, h, C, F32, decay_mode=mode)
+    inp = make_inputs(kind, B, H, L, d, h, F32, seed=seed, regime=regime, m0_scale=0.01)
+    P = d * d if kind == oracle.LINEAR else 3 * d * h
+    rng = np.random.default_rng(seed + 2000)
+    dout = rng.standard_normal((B, H, L, d)).astype(np.float32)
+    dW = rng.standard_normal((B, H, P)).astype(np.float32) if with_state else None
+    dM = rng.standard_normal((B, H, P)).astype(np.float32) if with_state else None
+    prob = problem_for(kind, B, H, L, d, h, C, F32, decay_mode=mode, flags=flags)
     got = run_backward(prob, inp, dout, dW, dM)
-    ref = oracle.chunk_backward(oracle.SWIGLU, inp["q64"], inp["k64"], inp["v64"], inp["eta"],
+    ref = oracle.chunk_backward(kind, inp["q64"], inp["k64"], inp["v64"], inp["eta"],
                                 inp["alpha"], inp["beta"], inp["W0"], inp["M0"], dout, dW, dM,
-                                C, decay_mode=mode, hidden=h)
+                                C, decay_mode=mode, hidden=h, qk_norm=bool(flags & 4))
     errs = {n: rel_fro(got[n], ref[n]) for n in NAMES}
     log("  rel_fro " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
     for n in NAMES:
@@ -59,6 +64,12 @@ def test_swiglu_backward_large_state():
     """The large-state learner's shape (d = 768, h = 1536) on a short sequence
     (the oracle's reverse mode stores the state before every token)."""
     check(1, 1, 20, 768, 1536, 8, seed=2)
+
+
+@pytest.mark.parametrize("kind,L,d,h,C", [(SWIGLU, 300, 128, 256, 128), (0, 200, 64, 0, 64)])
+def test_backward_through_qk_prologue(kind, L, d, h, C):
+    """E2TTT_FLAG_QK_SILU_L2: dq, dk taken back through SiLU + L2 per token."""
+    check(1, 2, L, d, h, C, seed=7, kind=kind, flags=4)
 
 
 def test_swiglu_backward_without_state_gradients():

@@ -694,8 +694,10 @@ static void readout_vjp(int kind, int64_t d, int64_t h, const double* Ws,
  *     dalpha_t = -eta_t dgamma; with alpha taken as gamma, dalpha_t = dgamma.
  * With qk_norm != 0 the q/k prologue (SiLU, then L2 per token) runs first, as
  * in the forward, and dq, dk are mapped back through it (silu_l2_rows_vjp).
- * The chunk-averaged variant and the row-normalisation option are not
- * covered.  dWend or dMend may be NULL (zero).  h is the SwiGLU hidden
+ * With averaged != 0 (the chunk-averaged variant) every token of a chunk uses
+ * the chunk means of beta and gamma, so the per-token adjoints of the two
+ * means are summed over the chunk and each token's beta and gamma receive
+ * 1/n of the sums.  The row-normalisation option is not covered.  dWend or dMend may be NULL (zero).  h is the SwiGLU hidden
  * width (ignored for linear).  Returns 0 on success, 1 on bad arguments,
  * 2 on allocation failure, 3 for an unknown learner.
  */
@@ -708,7 +710,7 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
                           const double* dWend, const double* dMend,
                           double* dq, double* dk, double* dv, double* deta,
                           double* dalpha, double* dbeta, double* dW0,
-                          double* dM0, int qk_norm) {
+                          double* dM0, int qk_norm, int averaged) {
   if (kind != OR_LINEAR && kind != OR_SWIGLU) return 3;
   if (decay_mode != OR_GAMMA_1_MINUS_ETA_ALPHA &&
       decay_mode != OR_ALPHA_IS_GAMMA)
@@ -719,11 +721,36 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
   const int64_t nC = (L + C - 1) / C;
   const int64_t Cmax = C < L ? C : (L > 0 ? L : 1);
   const int64_t nscr = 16 * (kind == OR_LINEAR ? 1 : h) + 4 * d;
+  /* The momentum and decay factors each token of a chunk uses. */
+  double* fb = (double*)malloc(sizeof(double) * (size_t)Cmax);
+  double* fg = (double*)malloc(sizeof(double) * (size_t)Cmax);
+  if (!fb || !fg) {
+    free(fb); free(fg);
+    return 2;
+  }
+#define CHUNK_FACTORS(t0_, n_)                                                     \
+  do {                                                                             \
+    double sb_ = 0.0, sg_ = 0.0;                                                   \
+    for (int64_t t_ = 0; t_ < (n_); ++t_) {                                        \
+      fb[t_] = beu[(t0_) + t_];                                                    \
+      fg[t_] = decay_factor(decay_mode, etu[(t0_) + t_], alu[(t0_) + t_]);         \
+      sb_ += fb[t_];                                                               \
+      sg_ += fg[t_];                                                               \
+    }                                                                              \
+    if (averaged)                                                                  \
+      for (int64_t t_ = 0; t_ < (n_); ++t_) {                                      \
+        fb[t_] = sb_ / (double)(n_);                                               \
+        fg[t_] = sg_ / (double)(n_);                                               \
+      }                                                                            \
+  } while (0)
 
   double* qkn = NULL; /* normalised q | k of one unit (q/k prologue) */
   if (qk_norm && L > 0) {
     qkn = (double*)malloc(sizeof(double) * (size_t)(2 * L * d));
-    if (!qkn) return 2;
+    if (!qkn) {
+      free(fb); free(fg);
+      return 2;
+    }
   }
   for (int64_t u = 0; u < B * H; ++u) {
     const double* qu = q + u * L * d;
@@ -767,6 +794,7 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
         !dWs || !scr) {
       free(Wst); free(Mst); free(Wb); free(Mb); free(Gt); free(W); free(M);
       free(dW); free(dM); free(dMt); free(dG); free(dWs); free(scr); free(qkn);
+      free(fb); free(fg);
       return 2;
     }
 
@@ -778,13 +806,13 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
       memcpy(Wst + r * P, W, sizeof(double) * (size_t)P);
       memcpy(Mst + r * P, M, sizeof(double) * (size_t)P);
       const double* Ws = Wst + r * P;
+      CHUNK_FACTORS(t0, n);
       for (int64_t t = 0; t < n; ++t) {
         const int64_t tt = t0 + t;
-        const double g = decay_factor(decay_mode, etu[tt], alu[tt]);
         oracle_token_descent(kind, d, h, Ws, ku + tt * d, vu + tt * d, Gt);
         for (int64_t i = 0; i < P; ++i) {
-          M[i] = beu[tt] * M[i] + etu[tt] * Gt[i];
-          W[i] = g * W[i] + M[i];
+          M[i] = fb[t] * M[i] + etu[tt] * Gt[i];
+          W[i] = fg[t] * W[i] + M[i];
         }
       }
     }
@@ -800,23 +828,24 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
       /* Re-run the chunk, recording the state before each token and G. */
       memcpy(W, Ws, sizeof(double) * (size_t)P);
       memcpy(M, Mst + r * P, sizeof(double) * (size_t)P);
+      CHUNK_FACTORS(t0, n);
       for (int64_t t = 0; t < n; ++t) {
         const int64_t tt = t0 + t;
-        const double g = decay_factor(decay_mode, etu[tt], alu[tt]);
         memcpy(Wb + t * P, W, sizeof(double) * (size_t)P);
         memcpy(Mb + t * P, M, sizeof(double) * (size_t)P);
         double* G = Gt + t * P;
         oracle_token_descent(kind, d, h, Ws, ku + tt * d, vu + tt * d, G);
         for (int64_t i = 0; i < P; ++i) {
-          M[i] = beu[tt] * M[i] + etu[tt] * G[i];
-          W[i] = g * W[i] + M[i];
+          M[i] = fb[t] * M[i] + etu[tt] * G[i];
+          W[i] = fg[t] * W[i] + M[i];
         }
       }
       for (int64_t i = 0; i < P; ++i) dWs[i] = 0.0;
+      double sum_dbet = 0.0, sum_dgam = 0.0; /* adjoints of the chunk means */
       for (int64_t t = n - 1; t >= 0; --t) {
         const int64_t tt = t0 + t;
         const double et = etu[tt];
-        const double g = decay_factor(decay_mode, et, alu[tt]);
+        const double g = fg[t];
         const double* G = Gt + t * P;
         double dgam = 0.0, dbet = 0.0, detd = 0.0;
         for (int64_t i = 0; i < P; ++i) {
@@ -830,9 +859,14 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
                     dvu + tt * d, dWs, scr);
         for (int64_t i = 0; i < P; ++i) {
           dW[i] = g * dW[i];
-          dM[i] = beu[tt] * dMt[i];
+          dM[i] = fb[t] * dMt[i];
         }
         detu[tt] += detd;
+        if (averaged) {
+          sum_dbet += dbet;
+          sum_dgam += dgam;
+          continue;
+        }
         dbeu[tt] += dbet;
         if (decay_mode == OR_GAMMA_1_MINUS_ETA_ALPHA) {
           detu[tt] -= alu[tt] * dgam;
@@ -841,6 +875,18 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
           dalu[tt] += dgam;
         }
       }
+      if (averaged) /* each token's beta, gamma enters its chunk mean with weight 1/n */
+        for (int64_t t = 0; t < n; ++t) {
+          const int64_t tt = t0 + t;
+          const double dg = sum_dgam / (double)n;
+          dbeu[tt] += sum_dbet / (double)n;
+          if (decay_mode == OR_GAMMA_1_MINUS_ETA_ALPHA) {
+            detu[tt] -= alu[tt] * dg;
+            dalu[tt] += -etu[tt] * dg;
+          } else {
+            dalu[tt] += dg;
+          }
+        }
       /* Readout o_t = f_Ws(q_t). */
       for (int64_t t = 0; t < n; ++t) {
         const int64_t tt = t0 + t;
@@ -858,5 +904,8 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
     free(dW); free(dM); free(dMt); free(dG); free(dWs); free(scr);
   }
   free(qkn);
+  free(fb);
+  free(fg);
+#undef CHUNK_FACTORS
   return 0;
 }

@@ -353,8 +353,9 @@ __global__ __launch_bounds__(64) void k_lin_bwd_scalars(Shape s, int mode, const
                                                         const float* __restrict__ sw,
                                                         const float* __restrict__ sm,
                                                         const float* __restrict__ dots,
-                                                        int nrb, double* bcp, float* deta,
-                                                        float* dalpha, float* dbeta) {
+                                                        int nrb, int averaged, double* bcp,
+                                                        float* deta, float* dalpha,
+                                                        float* dbeta) {
   const int64_t seg = blockIdx.x;
   const int64_t u = seg / s.nC;
   const int r = static_cast<int>(seg % s.nC);
@@ -364,16 +365,36 @@ __global__ __launch_bounds__(64) void k_lin_bwd_scalars(Shape s, int mode, const
   const int64_t tpl = (n + 63) / 64;
   const int64_t lo = lane * tpl, hi = (lo + tpl < n ? lo + tpl : n);  // [lo, hi)
   double* B3 = bcp + seg * s.Cp * 3;
-  auto gam = [&](int64_t i) -> double {
+  auto gam_tok = [&](int64_t i) -> double {
     const double e = eta[t0 + i], al = alpha[t0 + i];
     return mode == 0 ? 1.0 - e * al : al;
   };
+  // Chunk-averaged variant: every token uses the segment means (summed by the
+  // wave in a fixed order).
+  double mbeta = 0.0, mgam = 0.0;
+  if (averaged) {
+    double sb = 0.0, sg = 0.0;
+    for (int64_t i = lo; i < hi; ++i) {
+      sb += beta[t0 + i];
+      sg += gam_tok(i);
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+      sb += __shfl_xor(sb, off, 64);
+      sg += __shfl_xor(sg, off, 64);
+    }
+    mbeta = sb / static_cast<double>(n);
+    mgam = sg / static_cast<double>(n);
+  }
+  auto bet = [&](int64_t i) -> double {
+    return averaged ? mbeta : static_cast<double>(beta[t0 + i]);
+  };
+  auto gam = [&](int64_t i) -> double { return averaged ? mgam : gam_tok(i); };
   // Suffix scan of the maps T_j, j = 1 .. n-1 (B, G, Z): (b, c, P) ->
   // (B b, G c, Z c + B P); F after E = (B_F B_E, G_F G_E, Z_F G_E + B_F Z_E).
   double mB = 1.0, mG = 1.0, mZ = 0.0;  // this lane's composition, T_lo after ... after T_hi-1
   for (int64_t j = hi - 1; j >= lo; --j) {
     if (j < 1) continue;
-    const double bj = beta[t0 + j], gj = gam(j);
+    const double bj = bet(j), gj = gam(j);
     // (T_j after current): current applied first
     const double nB = bj * mB, nG = gj * mG, nZ = gj * mG + bj * mZ;
     mB = nB; mG = nG; mZ = nZ;
@@ -398,7 +419,7 @@ __global__ __launch_bounds__(64) void k_lin_bwd_scalars(Shape s, int mode, const
     B3[3 * i + 1] = vc;
     B3[3 * i + 2] = vP;
     if (i >= 1) {  // v_{i-1} = T_i(v_i)
-      const double bi = beta[t0 + i], gi = gam(i);
+      const double bi = bet(i), gi = gam(i);
       const double nb = bi * vb, nc = gi * vc, nP = gi * vc + bi * vP;
       vb = nb; vc = nc; vP = nP;
     }
@@ -412,7 +433,7 @@ __global__ __launch_bounds__(64) void k_lin_bwd_scalars(Shape s, int mode, const
     dcWM += dots[(seg * nrb + rb) * 4 + 2];
   }
   const double b0 = B3[0], c0 = B3[1], P0 = B3[2];
-  const double beta0 = beta[t0], gamma0 = gam(0);
+  const double beta0 = bet(0), gamma0 = gam(0);
   auto seedP = [&](int64_t i) -> double {
     double v = static_cast<double>(eta[t0 + i]) * sw[seg * s.Cp + i];
     if (i == 0) v += dcWM * beta0;
@@ -426,7 +447,7 @@ __global__ __launch_bounds__(64) void k_lin_bwd_scalars(Shape s, int mode, const
   // Pass 1: prefix carries of TP and Tb (multiplier beta_i).
   AffD fP{1.0, 0.0}, fb{1.0, 0.0};
   for (int64_t i = lo; i < hi; ++i) {
-    const double bi = beta[t0 + i];
+    const double bi = bet(i);
     fP = aff_after(fP, AffD{bi, seedP(i)});
     fb = aff_after(fb, AffD{bi, seedb(i)});
   }
@@ -444,27 +465,18 @@ __global__ __launch_bounds__(64) void k_lin_bwd_scalars(Shape s, int mode, const
   {
     double TP = cP;
     for (int64_t i = lo; i < hi; ++i) {
-      const double bi = beta[t0 + i];
+      const double bi = bet(i);
       TP = seedP(i) + bi * TP;
       fc = aff_after(fc, AffD{gam(i), TP + (i == 0 ? dcW * gamma0 : 0.0)});
     }
   }
   const double cc = prefix(fc);
-  // Pass 3: outputs.
-  double TP = cP, Tb = cb, Tc = cc;  // values at i-1
-  for (int64_t i = lo; i < hi; ++i) {
-    const double bi = beta[t0 + i], gi = gam(i);
-    const double b_i = B3[3 * i], c_i = B3[3 * i + 1], P_i = B3[3 * i + 2];
-    double dbe, dga;
-    if (i == 0) {
-      dbe = dcM * b0 + dcWM * P0;
-      dga = dcW * c0;
-    } else {
-      dbe = TP * P_i + Tb * b_i;
-      dga = Tc * c_i;
-    }
+  // Pass 3: outputs.  deta has the kernels' direct term (K^W = eta P, K^M =
+  // eta b) and, through Eq. 14, the decay's.
+  auto write_tok = [&](int64_t i, double dbe, double dga, double P_i, double b_i) {
     const double e = eta[t0 + i];
-    double det = static_cast<double>(sw[seg * s.Cp + i]) * P_i + static_cast<double>(sm[seg * s.Cp + i]) * b_i;
+    double det = static_cast<double>(sw[seg * s.Cp + i]) * P_i +
+                 static_cast<double>(sm[seg * s.Cp + i]) * b_i;
     double dal;
     if (mode == 0) {
       det -= static_cast<double>(alpha[t0 + i]) * dga;
@@ -475,9 +487,38 @@ __global__ __launch_bounds__(64) void k_lin_bwd_scalars(Shape s, int mode, const
     deta[t0 + i] = static_cast<float>(det);
     dalpha[t0 + i] = static_cast<float>(dal);
     dbeta[t0 + i] = static_cast<float>(dbe);
+  };
+  double sdbe = 0.0, sdga = 0.0;
+  double TP = cP, Tb = cb, Tc = cc;  // values at i-1
+  for (int64_t i = lo; i < hi; ++i) {
+    const double bi = bet(i), gi = gam(i);
+    const double b_i = B3[3 * i], c_i = B3[3 * i + 1], P_i = B3[3 * i + 2];
+    double dbe, dga;
+    if (i == 0) {
+      dbe = dcM * b0 + dcWM * P0;
+      dga = dcW * c0;
+    } else {
+      dbe = TP * P_i + Tb * b_i;
+      dga = Tc * c_i;
+    }
+    if (averaged) {  // the adjoints of the two means; distributed below
+      sdbe += dbe;
+      sdga += dga;
+    } else {
+      write_tok(i, dbe, dga, P_i, b_i);
+    }
     TP = seedP(i) + bi * TP;
     Tb = seedb(i) + bi * Tb;
     Tc = TP + (i == 0 ? dcW * gamma0 : 0.0) + gi * Tc;
+  }
+  if (averaged) {  // each token's beta and gamma enter the means with weight 1/n
+    for (int off = 32; off >= 1; off >>= 1) {
+      sdbe += __shfl_xor(sdbe, off, 64);
+      sdga += __shfl_xor(sdga, off, 64);
+    }
+    const double inv_n = 1.0 / static_cast<double>(n);
+    for (int64_t i = lo; i < hi; ++i)
+      write_tok(i, sdbe * inv_n, sdga * inv_n, B3[3 * i + 2], B3[3 * i]);
   }
 }
 

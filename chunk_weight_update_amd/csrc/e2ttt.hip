@@ -929,7 +929,9 @@ e2ttt_status make_bwd_plan(const e2ttt_problem* p, BwdPlan* bp) {
   if (p->io_dtype != E2TTT_F32 && p->io_dtype != E2TTT_BF16) return E2TTT_EINVAL;
   bp->bf16io = p->io_dtype == E2TTT_BF16;
   const Plan& q = bp->f;
-  if ((p->flags & ~static_cast<uint32_t>(E2TTT_FLAG_QK_SILU_L2)) != 0u) return E2TTT_EUNSUPPORTED;
+  if ((p->flags & ~static_cast<uint32_t>(E2TTT_FLAG_QK_SILU_L2 |
+                                         E2TTT_FLAG_CHUNK_AVERAGED_DECAY)) != 0u)
+    return E2TTT_EUNSUPPORTED;
   bp->qknorm = q.qknorm != 0;
   if (q.kind == E2TTT_LINEAR && q.d > 64) return E2TTT_EUNSUPPORTED;
   if (q.kind == E2TTT_SWIGLU && q.BH > 65535) return E2TTT_EUNSUPPORTED;  // grid z
@@ -1345,8 +1347,8 @@ e2ttt_status backward_impl(const e2ttt_problem* prob, const void* q, const void*
   hipLaunchKernelGGL(k_lin_bwd_scalars, dim3(grid1(pl.BH * pl.nC)), dim3(64), 0, s, sh, pl.mode,
                      eta, alpha, beta, static_cast<const float*>(wsf(bp.sw)),
                      static_cast<const float*>(wsf(bp.sm)), static_cast<const float*>(wsf(bp.dots)),
-                     static_cast<int>(bp.nrb), reinterpret_cast<double*>(ws + bp.bcp), deta,
-                     dalpha, dbeta);
+                     static_cast<int>(bp.nrb), pl.averaged, reinterpret_cast<double*>(ws + bp.bcp),
+                     deta, dalpha, dbeta);
   return hipGetLastError() == hipSuccess ? E2TTT_OK : E2TTT_EHIP;
 }
 

@@ -278,8 +278,10 @@ E2TTT_API e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* 
  * weights through the learner (§5.2, App. B.5), so its reverse mode carries
  * the second-order terms of f = W2 (silu(W1 x) * (W3 x)) as well.
  *
- * Supported: flags 0 or E2TTT_FLAG_QK_SILU_L2 (the prologue is recomputed and
- * dq, dk are taken back through it to the raw q, k), and kind E2TTT_LINEAR
+ * Supported: flags 0, E2TTT_FLAG_QK_SILU_L2 (the prologue is recomputed and
+ * dq, dk are taken back through it to the raw q, k) and
+ * E2TTT_FLAG_CHUNK_AVERAGED_DECAY (each token's beta and gamma receive 1/n of
+ * the adjoints of its chunk's means), and kind E2TTT_LINEAR
  * with dim a multiple of 16 up to 64, or E2TTT_SWIGLU with the forward's (dim, hidden) set and at most 65535
  * batch*heads units (else EUNSUPPORTED).  The arithmetic is fp32 (the forward
  * re-run too); with io_dtype E2TTT_BF16, q, k, v, dout are widened on entry

@@ -248,8 +248,8 @@ def test_backward_support_and_workspace():
     for ok in (swiglu(), linear(io_dtype=cwu.BF16),  # bf16 io: widened at the boundary
                linear(flags=cwu.FLAG_QK_SILU_L2), swiglu(flags=cwu.FLAG_QK_SILU_L2)):
         assert cwu.backward_workspace_bytes(ok) > 0
+    assert cwu.backward_workspace_bytes(linear(flags=cwu.FLAG_CHUNK_AVERAGED_DECAY)) > 0
     for bad in (swiglu(io_dtype=cwu.F32, flags=cwu.FLAG_POST_CHUNK_ROW_L2), linear(dim=128),
-                linear(flags=cwu.FLAG_CHUNK_AVERAGED_DECAY),
                 linear(flags=cwu.FLAG_POST_CHUNK_ROW_L2)):
         with pytest.raises(cwu.E2tttError) as e:
             cwu.backward_workspace_bytes(bad)

@@ -42,7 +42,8 @@ def check(B, H, L, d, h, C, mode=0, regime="default", seed=0, with_state=True, k
     got = run_backward(prob, inp, dout, dW, dM)
     ref = oracle.chunk_backward(kind, inp["q64"], inp["k64"], inp["v64"], inp["eta"],
                                 inp["alpha"], inp["beta"], inp["W0"], inp["M0"], dout, dW, dM,
-                                C, decay_mode=mode, hidden=h, qk_norm=bool(flags & 4))
+                                C, decay_mode=mode, hidden=h, qk_norm=bool(flags & 4),
+                                averaged=bool(flags & 2))
     errs = {n: rel_fro(got[n], ref[n]) for n in NAMES}
     log("  rel_fro " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
     for n in NAMES:
@@ -70,6 +71,14 @@ def test_swiglu_backward_large_state():
 def test_backward_through_qk_prologue(kind, L, d, h, C):
     """E2TTT_FLAG_QK_SILU_L2: dq, dk taken back through SiLU + L2 per token."""
     check(1, 2, L, d, h, C, seed=7, kind=kind, flags=4)
+
+
+@pytest.mark.parametrize("kind,L,d,h,C,mode", [(SWIGLU, 300, 128, 256, 128, 0),
+                                               (0, 1000, 64, 0, 512, 1)])
+def test_backward_chunk_averaged(kind, L, d, h, C, mode):
+    """E2TTT_FLAG_CHUNK_AVERAGED_DECAY: the adjoints of the chunk means of beta
+    and gamma, shared out over the chunk's tokens."""
+    check(1, 2, L, d, h, C, mode=mode, seed=8, kind=kind, flags=2)
 
 
 def test_swiglu_backward_without_state_gradients():

@@ -87,16 +87,16 @@ enum {
    * chunk the per-token momentum factors beta_t and decay factors gamma_t
    * (after decay_mode) are replaced by their arithmetic means over the
    * chunk's tokens before the scalar kernels are formed; eta_t stays per
-   * token.  Applies to e2ttt_chunk_forward, its timed twin and
-   * e2ttt_scalar_kernels, for every kind and dtype. */
+   * token.  Applies to e2ttt_chunk_forward, its timed twin,
+   * e2ttt_scalar_kernels and the backward, for every kind and dtype. */
   E2TTT_FLAG_CHUNK_AVERAGED_DECAY = 2u,
   /* The TTT branch's input prologue ("Rethinking Expressivity and
    * Efficiency in Test-Time Training", §4 Overall Architecture): q and k are
    * passed as raw projections, and the library applies SiLU and then L2
    * normalisation to every token's vector (x / max(||x||, 1e-12), in fp32,
    * rounded to io_dtype) before using them.  Applies to e2ttt_chunk_forward,
-   * its timed twin and e2ttt_decode_step; the workspace grows by the two
-   * normalised copies. */
+   * its timed twin, e2ttt_decode_step and the backward (which takes dq, dk
+   * back through it); the workspace grows by the two normalised copies. */
   E2TTT_FLAG_QK_SILU_L2 = 4u,
   /* Chunk-boundary normalisation of the fast weights ("Rethinking
    * Expressivity and Efficiency in Test-Time Training", App. B.1 Training

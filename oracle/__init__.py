@@ -75,7 +75,7 @@ def _load():
             lib.oracle_scalar_kernels.argtypes = [ctypes.c_int, i64, i64] + [P] * 6 + [ctypes.c_int]
             lib.oracle_scalar_kernels.restype = ctypes.c_int
             lib.oracle_chunk_backward.argtypes = (
-                [ctypes.c_int, ctypes.c_int] + [i64] * 6 + [P] * 19 + [ctypes.c_int] * 2)
+                [ctypes.c_int, ctypes.c_int] + [i64] * 6 + [P] * 19 + [ctypes.c_int] * 3)
             lib.oracle_chunk_backward.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -175,7 +175,8 @@ def scalar_kernels(eta, alpha, beta, decay_mode=GAMMA_1_MINUS_ETA_ALPHA, average
 
 
 def chunk_backward(kind, q, k, v, eta, alpha, beta, W0, M0, dout, dWend, dMend, chunk,
-                   decay_mode=GAMMA_1_MINUS_ETA_ALPHA, hidden=0, qk_norm=False, averaged=False):
+                   decay_mode=GAMMA_1_MINUS_ETA_ALPHA, hidden=0, qk_norm=False, averaged=False,
+                   row_norm=False):
     """Reverse mode of ``chunk_forward`` (linear and SwiGLU learners): gradients of
     <dout, out> + <dWend, Wend> + <dMend, Mend> with respect to every input.
     dWend / dMend may be None (zero).  Returns a dict with keys q, k, v, eta,
@@ -200,7 +201,8 @@ def chunk_backward(kind, q, k, v, eta, alpha, beta, W0, M0, dout, dWend, dMend, 
         _ptr(alpha), _ptr(beta), _ptr(W0), _ptr(M0), _ptr(dout),
         _ptr(dWp) if dWp is not None else null, _ptr(dMp) if dMp is not None else null,
         _ptr(g["q"]), _ptr(g["k"]), _ptr(g["v"]), _ptr(g["eta"]), _ptr(g["alpha"]),
-        _ptr(g["beta"]), _ptr(g["W0"]), _ptr(g["M0"]), int(bool(qk_norm)), int(bool(averaged)))
+        _ptr(g["beta"]), _ptr(g["W0"]), _ptr(g["M0"]), int(bool(qk_norm)), int(bool(averaged)),
+        int(bool(row_norm)))
     if rc != 0:
         raise RuntimeError(f"oracle_chunk_backward failed with code {rc}")
     return g

@@ -242,6 +242,36 @@ static void normalise_rows(int kind, int64_t d, int64_t h, double* W) {
   }
 }
 
+/* Reverse mode of normalise_rows: g holds the adjoint of the normalised W
+ * and is replaced by the adjoint of W before normalisation (Wpre).  Per row
+ * r with norm n: dr = (g - y (y . g)) / n, y = r / n; below the 1e-12 floor
+ * the divisor is constant and dr = g / 1e-12. */
+static void normalise_rows_vjp(int kind, int64_t d, int64_t h, const double* Wpre,
+                               double* g) {
+  int64_t nrows, len;
+  for (int part = 0; part < (kind == OR_LINEAR ? 1 : 2); ++part) {
+    const double* base;
+    double* gb;
+    if (kind == OR_LINEAR) { base = Wpre; gb = g; nrows = d; len = d; }
+    else if (part == 0) { base = Wpre; gb = g; nrows = 2 * h; len = d; }
+    else { base = Wpre + 2 * h * d; gb = g + 2 * h * d; nrows = d; len = h; }
+    for (int64_t r = 0; r < nrows; ++r) {
+      const double* w = base + r * len;
+      double* gr = gb + r * len;
+      double ss = 0.0;
+      for (int64_t j = 0; j < len; ++j) ss += w[j] * w[j];
+      const double n = sqrt(ss);
+      if (n < 1e-12) {
+        for (int64_t j = 0; j < len; ++j) gr[j] /= 1e-12;
+        continue;
+      }
+      double dot = 0.0;
+      for (int64_t j = 0; j < len; ++j) dot += (w[j] / n) * gr[j];
+      for (int64_t j = 0; j < len; ++j) gr[j] = (gr[j] - (w[j] / n) * dot) / n;
+    }
+  }
+}
+
 /*
  * The chunk forward over a whole sequence, literal recurrence.
  *   q, k, v, out : [B, H, L, d]      eta, alpha, beta : [B, H, L]
@@ -697,7 +727,10 @@ static void readout_vjp(int kind, int64_t d, int64_t h, const double* Ws,
  * With averaged != 0 (the chunk-averaged variant) every token of a chunk uses
  * the chunk means of beta and gamma, so the per-token adjoints of the two
  * means are summed over the chunk and each token's beta and gamma receive
- * 1/n of the sums.  The row-normalisation option is not covered.  dWend or dMend may be NULL (zero).  h is the SwiGLU hidden
+ * 1/n of the sums.  With row_norm != 0 (chunk-boundary normalisation) the
+ * forward normalises W after every chunk, the last included, so before a
+ * chunk is walked in reverse the adjoint of its normalised end state is taken
+ * back through the normalisation (normalise_rows_vjp) at the state before it.  dWend or dMend may be NULL (zero).  h is the SwiGLU hidden
  * width (ignored for linear).  Returns 0 on success, 1 on bad arguments,
  * 2 on allocation failure, 3 for an unknown learner.
  */
@@ -710,7 +743,7 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
                           const double* dWend, const double* dMend,
                           double* dq, double* dk, double* dv, double* deta,
                           double* dalpha, double* dbeta, double* dW0,
-                          double* dM0, int qk_norm, int averaged) {
+                          double* dM0, int qk_norm, int averaged, int row_norm) {
   if (kind != OR_LINEAR && kind != OR_SWIGLU) return 3;
   if (decay_mode != OR_GAMMA_1_MINUS_ETA_ALPHA &&
       decay_mode != OR_ALPHA_IS_GAMMA)
@@ -815,6 +848,7 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
           W[i] = fg[t] * W[i] + M[i];
         }
       }
+      if (row_norm) normalise_rows(kind, d, h, W);
     }
 
     /* Backward. */
@@ -840,6 +874,7 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
           W[i] = fg[t] * W[i] + M[i];
         }
       }
+      if (row_norm) normalise_rows_vjp(kind, d, h, W, dW); /* W: the chunk end, before it */
       for (int64_t i = 0; i < P; ++i) dWs[i] = 0.0;
       double sum_dbet = 0.0, sum_dgam = 0.0; /* adjoints of the chunk means */
       for (int64_t t = n - 1; t >= 0; --t) {

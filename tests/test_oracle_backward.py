@@ -344,3 +344,33 @@ def test_backward_chunk_averaged_matches_finite_differences(kind, mode):
         fd = (loss(xp) - loss(xm)) / (2 * eps)
         an = float((g[name] * dl).sum())
         assert abs(fd - an) <= 2e-7 * max(1.0, abs(an)), (name, fd, an)
+
+
+@pytest.mark.parametrize("kind", [oracle.LINEAR, oracle.SWIGLU])
+def test_backward_row_normalisation_matches_finite_differences(kind):
+    """Chunk-boundary normalisation: W normalised after every chunk (the last
+    included); the adjoint goes back through each normalisation."""
+    rng = np.random.default_rng(700 + kind)
+    B, H, L, d, hd, C = 1, 2, 8, 3, 4, 3
+    if kind == oracle.LINEAR:
+        x, hd, P = _problem(rng, B, H, L, d, 0), 0, d * d
+    else:
+        x, P = _problem_sw(rng, B, H, L, d, hd, 0), 3 * d * hd
+    dout = rng.standard_normal((B, H, L, d))
+    dWe = rng.standard_normal((B, H, P))
+    dMe = rng.standard_normal((B, H, P))
+    g = oracle.chunk_backward(kind, *[x[n] for n in NAMES], dout, dWe, dMe, C, hidden=hd,
+                              row_norm=True)
+
+    def loss(xx):
+        o, We, Me = oracle.chunk_forward(kind, *[xx[n] for n in NAMES], C, hidden=hd,
+                                         row_norm=True)
+        return float((dout * o).sum() + (dWe * We).sum() + (dMe * Me).sum())
+    eps = 1e-6
+    for name in NAMES:
+        dl = rng.standard_normal(x[name].shape)
+        xp = dict(x); xp[name] = x[name] + eps * dl
+        xm = dict(x); xm[name] = x[name] - eps * dl
+        fd = (loss(xp) - loss(xm)) / (2 * eps)
+        an = float((g[name] * dl).sum())
+        assert abs(fd - an) <= 2e-7 * max(1.0, abs(an)), (name, fd, an)

@@ -84,6 +84,49 @@ __global__ __launch_bounds__(256) void k_qk_norm_bwd(const float* __restrict__ x
   }
 }
 
+// Reverse mode of k_row_l2norm: g is the adjoint of the normalised rows,
+// Wpre the state before normalisation; writes the adjoint of Wpre:
+//   dr = (g - y (y . g)) / n,  y = r / n  (g / 1e-12 below the floor).
+// Rows and waves as k_row_l2norm; dW may not alias g.
+__global__ __launch_bounds__(256) void k_row_l2norm_bwd(const float* __restrict__ Wpre,
+                                                        const float* __restrict__ g,
+                                                        float* __restrict__ dW, int64_t BH,
+                                                        int64_t d, int64_t h) {
+  const int lane = threadIdx.x & 63;
+  const int64_t rows_u = h == 0 ? d : 2 * h + d;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= BH * rows_u) return;  // whole waves leave together
+  const int64_t u = row / rows_u, r = row % rows_u;
+  const int64_t P = h == 0 ? d * d : 3 * d * h;
+  int64_t off, len;
+  if (h == 0 || r < 2 * h) {
+    off = u * P + r * d;
+    len = d;
+  } else {
+    off = u * P + 2 * h * d + (r - 2 * h) * h;
+    len = h;
+  }
+  float ss = 0.0f, wg = 0.0f;
+  for (int64_t j = lane; j < len; j += 64) {
+    const float w = Wpre[off + j];
+    ss = fmaf(w, w, ss);
+    wg = fmaf(w, g[off + j], wg);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    ss += __shfl_down(ss, o);
+    wg += __shfl_down(wg, o);
+  }
+  ss = __shfl(ss, 0);
+  wg = __shfl(wg, 0);
+  const float n = sqrtf(ss);
+  const bool above = n >= 1e-12f;
+  const float inv = 1.0f / (above ? n : 1e-12f);
+  const float dot = above ? wg * inv : 0.0f;  // y . g
+  for (int64_t j = lane; j < len; j += 64)
+    dW[off + j] = (g[off + j] - Wpre[off + j] * inv * dot) * inv;
+}
+
 struct LinBwdArgs {
   Shape s;
   int r;     // chunk index

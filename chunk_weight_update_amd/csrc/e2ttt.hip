@@ -912,6 +912,10 @@ struct BwdPlan {
   // q/k prologue: normalised q, k and their adjoints, fp32 [BH][L][d]
   bool qknorm;
   size_t nq, nk, dnq, dnk;
+  // chunk-boundary row normalisation: each chunk's end state before it,
+  // [nC][BH][P], and the adjoint taken back through it, [BH][P]
+  bool rownorm;
+  size_t wpre, dwn;
   size_t total;
 };
 
@@ -929,10 +933,10 @@ e2ttt_status make_bwd_plan(const e2ttt_problem* p, BwdPlan* bp) {
   if (p->io_dtype != E2TTT_F32 && p->io_dtype != E2TTT_BF16) return E2TTT_EINVAL;
   bp->bf16io = p->io_dtype == E2TTT_BF16;
   const Plan& q = bp->f;
-  if ((p->flags & ~static_cast<uint32_t>(E2TTT_FLAG_QK_SILU_L2 |
-                                         E2TTT_FLAG_CHUNK_AVERAGED_DECAY)) != 0u)
-    return E2TTT_EUNSUPPORTED;
+  // Every flag of the forward is supported (the compensated-weights option
+  // only concerns bf16 matrix operands; the backward computes in fp32).
   bp->qknorm = q.qknorm != 0;
+  bp->rownorm = q.rownorm != 0;
   if (q.kind == E2TTT_LINEAR && q.d > 64) return E2TTT_EUNSUPPORTED;
   if (q.kind == E2TTT_SWIGLU && q.BH > 65535) return E2TTT_EUNSUPPORTED;  // grid z
   size_t o = align256(q.total);
@@ -969,6 +973,10 @@ e2ttt_status make_bwd_plan(const e2ttt_problem* p, BwdPlan* bp) {
   if (bp->qknorm)
     for (size_t* b : {&bp->nq, &bp->nk, &bp->dnq, &bp->dnk})
       *b = take(4 * static_cast<size_t>(q.BH * q.L * q.d));
+  if (bp->rownorm) {
+    bp->wpre = take(np * q.nC);
+    bp->dwn = take(np);
+  }
   bp->total = q.L == 0 ? 0 : o;
   return E2TTT_OK;
 }
@@ -1042,24 +1050,36 @@ void swiglu_backward(const BwdPlan& bp, char* ws, const float* Q, const float* K
     float* ut = wsf(q.ut);
     float* gt = wsf(q.gt);
     float* zt = wsf(q.zt);
-    if (q.nC > 1) {
+    // With row normalisation every chunk is re-run (the last one's end state
+    // before normalisation is needed too); each end state is kept before it
+    // is normalised into the next chunk's start (and its operand shadows).
+    const bool rn = bp.rownorm;
+    if (q.nC > 1 || rn) {
       hipLaunchKernelGGL((k_prep_kt<float, false>),
                          dim3(grid1(BH * q.nC * (Cp / 64) * (d / 64))), dim3(256), 0, s, sh, K, kt);
       hipLaunchKernelGGL(k_prep_shadow<float>, dim3(grid1(shadow_blocks(sh))), dim3(256), 0, s,
                          sh, W0, w13s, w2s, w2ts);
     }
     const int64_t na = (4 * h / 128) * (d / 128), nb = (2 * d / 128) * (h / 128);
-    for (int64_t r = 0; r + 1 < q.nC; ++r) {
+    for (int64_t r = 0; r + (rn ? 0 : 1) < q.nC; ++r) {
       const int ri = static_cast<int>(r);
+      const bool more = r + 1 < q.nC;
+      float* Wout = rn ? wsf(bp.wpre) + r * nP : Wst(r + 1);
+      float* Mout = more ? Mst(r + 1) : wsf(bp.dwn);  // the last M is not needed
       hipLaunchKernelGGL(k_fwd13<float>, dim3(grid1(BH * (2 * Cp / 128) * (2 * h / 128))),
                          dim3(256), 0, s, sh, ri, Q, K, w13s, zrow, a1s, a3s, zt);
       hipLaunchKernelGGL(k_fwd2<float>, dim3(grid1(BH * (2 * Cp / 128) * (d / 128))), dim3(256),
                          0, s, sh, ri, V, dq, zrow, w2s, kw, km, grow, gt);
       hipLaunchKernelGGL(k_bwd<float>, dim3(grid1(BH * (Cp / 128) * (h / 128))), dim3(256), 0,
                          s, sh, ri, grow, w2ts, a1s, a3s, kw, km, ut);
-      hipLaunchKernelGGL(k_agg<float>, dim3(grid1(BH * (na + nb))), dim3(256), 0, s, sh, ri, 0,
-                         ut, kt, gt, zt, coef, Win(r), Min(r), Wst(r + 1), Mst(r + 1), w13s,
-                         w2s, w2ts);
+      hipLaunchKernelGGL(k_agg<float>, dim3(grid1(BH * (na + nb))), dim3(256), 0, s, sh, ri,
+                         rn ? 1 : 0, ut, kt, gt, zt, coef, Win(r), Min(r), Wout, Mout, w13s, w2s,
+                         w2ts);
+      if (rn && more) {
+        hipLaunchKernelGGL(k_copy_or_zero, dim3(grid1((nP + 255) / 256)), dim3(256), 0, s,
+                           static_cast<const float*>(Wout), Wst(r + 1), nP);
+        launch_rownorm<float>(q, sh, Wst(r + 1), true, w13s, w2s, w2ts, s);
+      }
     }
   }
   float *HK = wsf(bp.hk), *HQ = wsf(bp.hq), *TW = wsf(bp.tw), *TM = wsf(bp.tm),
@@ -1070,9 +1090,16 @@ void swiglu_backward(const BwdPlan& bp, char* ws, const float* Q, const float* K
         *DEA = wsf(bp.dea), *PART = wsf(bp.gpart);
   const int64_t b2 = Cp * 2 * h, b1 = Cp * h, bd = Cp * d;  // unit strides of the buffers
   const int64_t o2 = 2 * h * d;                              // offset of W2 in a state
+  const int64_t nrows = BH * (2 * h + d);
   for (int64_t r = q.nC - 1; r >= 0; --r) {
     const int ri = static_cast<int>(r);
     const int64_t t0 = r * q.C, n = (L - t0) < q.C ? (L - t0) : q.C;
+    if (bp.rownorm) {  // back through this chunk's normalisation
+      hipLaunchKernelGGL(k_row_l2norm_bwd, dim3(grid1((nrows + 3) / 4)), dim3(256), 0, s,
+                         static_cast<const float*>(wsf(bp.wpre) + r * nP), dWC, wsf(bp.dwn), BH,
+                         d, h);
+      dWC = wsf(bp.dwn);
+    }
     const float *Kr = K + t0 * d, *Qr = Q + t0 * d, *Vr = V + t0 * d, *DOr = DO + t0 * d;
     float *dqr = dq + t0 * d, *dkr = dk + t0 * d, *dvr = dv + t0 * d;
     const float* Ws = Win(r);
@@ -1162,18 +1189,37 @@ void linear_backward(const BwdPlan& bp, char* ws, const float* Q, const float* K
   };
   const size_t lds_f = static_cast<size_t>(pl.d * (pl.d + 1) + LIN_FWD_TB * (pl.d + 1)) * sizeof(float);
   const size_t lds_a = static_cast<size_t>(2 * 64 * 16 + 64 * pl.d) * sizeof(float);
-  for (int64_t r = 0; !Wsv && r + 1 < pl.nC; ++r) {
+  // With row normalisation every chunk is re-run (the last one's end state
+  // before normalisation is needed too) and each end state is kept before
+  // being normalised into the next chunk's start.
+  const bool rn = bp.rownorm;
+  const int64_t rows = pl.BH * pl.d;
+  for (int64_t r = 0; !Wsv && r + (rn ? 0 : 1) < pl.nC; ++r) {
     const int ri = static_cast<int>(r);
+    const bool more = r + 1 < pl.nC;
+    float* Wout = rn ? wsf(bp.wpre) + r * nP : Wst(r + 1);
+    float* Mout = more ? Mst(r + 1) : wsf(bp.dwn);  // the last M is not needed
     hipLaunchKernelGGL(k_lin_fwd<float>, dim3(grid1(pl.BH * (2 * pl.Cp / LIN_FWD_TB))), dim3(256), lds_f,
                        s, sh, ri, Q, K, V, Win(r), kw, km, dq, wsf(pl.gw), wsf(pl.gm));
     hipLaunchKernelGGL(k_lin_agg<float>, dim3(grid1(pl.BH * (pl.d / 16))), dim3(256), lds_a, s,
-                       sh, ri, K, wsf(pl.gw), wsf(pl.gm), coef, Win(r), Min(r), Wst(r + 1),
-                       Mst(r + 1));
+                       sh, ri, K, wsf(pl.gw), wsf(pl.gm), coef, Win(r), Min(r), Wout, Mout);
+    if (rn && more) {
+      hipLaunchKernelGGL(k_copy_or_zero, dim3(grid1((nP + 255) / 256)), dim3(256), 0, s,
+                         static_cast<const float*>(Wout), Wst(r + 1), nP);
+      hipLaunchKernelGGL(k_row_l2norm, dim3(grid1((rows + 3) / 4)), dim3(256), 0, s, Wst(r + 1),
+                         pl.BH, pl.d, int64_t(0));
+    }
   }
   // Reverse chunk loop.
   const size_t lds_t = static_cast<size_t>(lin_bwd_tok_lds_floats(pl.d)) * sizeof(float);
   const size_t lds_s = static_cast<size_t>(lin_bwd_state_lds_floats(pl.d)) * sizeof(float);
   for (int64_t r = pl.nC - 1; r >= 0; --r) {
+    if (rn) {  // back through this chunk's normalisation
+      hipLaunchKernelGGL(k_row_l2norm_bwd, dim3(grid1((rows + 3) / 4)), dim3(256), 0, s,
+                         static_cast<const float*>(wsf(bp.wpre) + r * nP), dWC, wsf(bp.dwn),
+                         pl.BH, pl.d, int64_t(0));
+      dWC = wsf(bp.dwn);
+    }
     LinBwdArgs a;
     a.s = sh;
     a.r = static_cast<int>(r);
@@ -1233,6 +1279,9 @@ e2ttt_status backward_impl(const e2ttt_problem* prob, const void* q, const void*
   if ((W_starts == nullptr) != (M_starts == nullptr)) return E2TTT_EINVAL;
   const bool keep = W_starts && pl.nC > 1;  // caller-kept chunk-start states
   if (keep && (!aligned(W_starts, 16) || !aligned(M_starts, 16))) return E2TTT_EINVAL;
+  // The reverse of the row normalisation needs each chunk's end state before
+  // it, which the kept (normalised) states do not carry.
+  if (keep && bp.rownorm) return E2TTT_EUNSUPPORTED;
   if (!W0 || !M0 || !dW0 || !dM0) return E2TTT_EINVAL;
   if (!empty && (!q || !k || !v || !eta || !alpha || !beta || !dout || !dq || !dk || !dv ||
                  !deta || !dalpha || !dbeta || !workspace))

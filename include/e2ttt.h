@@ -106,7 +106,7 @@ enum {
    * in fp32 with a fixed summation order.  M is not changed.  The next
    * chunk's readout and descent directions use the normalised W.  Applies to
    * e2ttt_chunk_forward, its timed twin and e2ttt_decode_step (at a call with
-   * chunk_end set); e2ttt_chunk_backward returns EUNSUPPORTED for it. */
+   * chunk_end set), and the backward (through every normalisation). */
   E2TTT_FLAG_POST_CHUNK_ROW_L2 = 8u
 };
 
@@ -278,10 +278,14 @@ E2TTT_API e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* 
  * weights through the learner (§5.2, App. B.5), so its reverse mode carries
  * the second-order terms of f = W2 (silu(W1 x) * (W3 x)) as well.
  *
- * Supported: flags 0, E2TTT_FLAG_QK_SILU_L2 (the prologue is recomputed and
- * dq, dk are taken back through it to the raw q, k) and
- * E2TTT_FLAG_CHUNK_AVERAGED_DECAY (each token's beta and gamma receive 1/n of
- * the adjoints of its chunk's means), and kind E2TTT_LINEAR
+ * Flags: E2TTT_FLAG_QK_SILU_L2 (the prologue is recomputed and dq, dk are
+ * taken back through it to the raw q, k), E2TTT_FLAG_CHUNK_AVERAGED_DECAY
+ * (each token's beta and gamma receive 1/n of the adjoints of its chunk's
+ * means), E2TTT_FLAG_POST_CHUNK_ROW_L2 (the adjoint goes back through every
+ * chunk's normalisation; the states are then always recomputed, so
+ * e2ttt_chunk_backward_states returns EUNSUPPORTED for it) and
+ * E2TTT_FLAG_COMPENSATED_WEIGHTS (no effect: the arithmetic is fp32).
+ * Supported: kind E2TTT_LINEAR
  * with dim a multiple of 16 up to 64, or E2TTT_SWIGLU with the forward's (dim, hidden) set and at most 65535
  * batch*heads units (else EUNSUPPORTED).  The arithmetic is fp32 (the forward
  * re-run too); with io_dtype E2TTT_BF16, q, k, v, dout are widened on entry

@@ -249,8 +249,9 @@ def test_backward_support_and_workspace():
                linear(flags=cwu.FLAG_QK_SILU_L2), swiglu(flags=cwu.FLAG_QK_SILU_L2)):
         assert cwu.backward_workspace_bytes(ok) > 0
     assert cwu.backward_workspace_bytes(linear(flags=cwu.FLAG_CHUNK_AVERAGED_DECAY)) > 0
-    for bad in (swiglu(io_dtype=cwu.F32, flags=cwu.FLAG_POST_CHUNK_ROW_L2), linear(dim=128),
-                linear(flags=cwu.FLAG_POST_CHUNK_ROW_L2)):
+    assert cwu.backward_workspace_bytes(swiglu(flags=cwu.FLAG_POST_CHUNK_ROW_L2)) > 0
+    assert cwu.backward_workspace_bytes(swiglu(flags=cwu.FLAG_COMPENSATED_WEIGHTS)) > 0
+    for bad in (linear(dim=128), linear(dim=80)):
         with pytest.raises(cwu.E2tttError) as e:
             cwu.backward_workspace_bytes(bad)
         assert e.value.status == cwu.EUNSUPPORTED
@@ -277,7 +278,7 @@ def test_backward_host_errors(mutate, expected):
         a = bwd_fake_args(prob)
         mutate(a)
         assert bwd_call(prob, a) == expected
-    bad = swiglu(flags=cwu.FLAG_POST_CHUNK_ROW_L2)
+    bad = linear(dim=128)
     assert bwd_call(bad, bwd_fake_args(linear())) == cwu.EUNSUPPORTED
 
 
@@ -308,3 +309,18 @@ def test_state_keeping_entry_points_host_checks():
     assert bcall(Ws, None) == cwu.EINVAL
     assert bcall(a["dq"], Ms) == cwu.EINVAL         # kept states over an output
     assert bcall(Ws + 4, Ms) == cwu.EINVAL          # misaligned
+
+
+def test_backward_kept_states_with_row_normalisation_unsupported():
+    """The reverse of the row normalisation needs each chunk's end state before
+    it; the kept (normalised) states do not carry it."""
+    f = Fake()
+    prob = linear(flags=cwu.FLAG_POST_CHUNK_ROW_L2)
+    a = bwd_fake_args(prob)
+    np_ = prob.dim * prob.dim * 4
+    st = cwu.chunk_backward(
+        prob, a["q"], a["k"], a["v"], a["eta"], a["alpha"], a["beta"], a["W0"], a["M0"],
+        a["dout"], a["dW_end"], a["dM_end"], a["dq"], a["dk"], a["dv"], a["deta"], a["dalpha"],
+        a["dbeta"], a["dW0"], a["dM0"], a["workspace"], a["nws"], stream=0, check=False,
+        W_starts=f(3 * np_), M_starts=f(3 * np_))
+    assert st == cwu.EUNSUPPORTED

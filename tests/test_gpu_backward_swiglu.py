@@ -43,7 +43,7 @@ def check(B, H, L, d, h, C, mode=0, regime="default", seed=0, with_state=True, k
     ref = oracle.chunk_backward(kind, inp["q64"], inp["k64"], inp["v64"], inp["eta"],
                                 inp["alpha"], inp["beta"], inp["W0"], inp["M0"], dout, dW, dM,
                                 C, decay_mode=mode, hidden=h, qk_norm=bool(flags & 4),
-                                averaged=bool(flags & 2))
+                                averaged=bool(flags & 2), row_norm=bool(flags & 8))
     errs = {n: rel_fro(got[n], ref[n]) for n in NAMES}
     log("  rel_fro " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
     for n in NAMES:
@@ -79,6 +79,17 @@ def test_backward_chunk_averaged(kind, L, d, h, C, mode):
     """E2TTT_FLAG_CHUNK_AVERAGED_DECAY: the adjoints of the chunk means of beta
     and gamma, shared out over the chunk's tokens."""
     check(1, 2, L, d, h, C, mode=mode, seed=8, kind=kind, flags=2)
+
+
+@pytest.mark.parametrize("kind,L,d,h,C,flags", [(SWIGLU, 300, 128, 256, 128, 8),
+                                                (0, 200, 64, 0, 64, 8),
+                                                (SWIGLU, 100, 128, 256, 128, 8),   # one chunk
+                                                (SWIGLU, 260, 128, 256, 128, 14)])  # all three
+def test_backward_row_normalisation(kind, L, d, h, C, flags):
+    """E2TTT_FLAG_POST_CHUNK_ROW_L2: the adjoint goes back through every
+    chunk's normalisation, the last one included (alone and with the
+    averaged variant and the q/k prologue)."""
+    check(1, 2, L, d, h, C, seed=9, kind=kind, flags=flags)
 
 
 def test_swiglu_backward_without_state_gradients():

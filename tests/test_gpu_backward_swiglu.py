@@ -161,3 +161,26 @@ def check_bf16(kind, B, H, L, d, h, C, mode=0, regime="default", seed=0):
 ])
 def test_backward_bf16_io_matches_oracle(kind, B, H, L, d, h, C, mode):
     check_bf16(kind, B, H, L, d, h, C, mode)
+
+
+def test_swiglu_backward_bench_shape_sampled_units():
+    """The bench's backward shape (B2 x H4, L4096, C512, d128/h256, fp32) in
+    its launch configuration; units are independent, so the oracle's reverse
+    mode is run on two sampled (batch, head) units and compared unit by unit."""
+    import oracle
+    B, H, L, d, h, C = 2, 4, 4096, 128, 256, 512
+    log(f"bench-shape backward B={B} H={H} L={L} C={C}, oracle on units (0,0) and (1,3)")
+    inp = make_inputs(SWIGLU, B, H, L, d, h, F32, seed=0, m0_scale=0.01)
+    dout, dW, dM = _upstream(B, H, L, d, h, 0)
+    prob = problem_for(SWIGLU, B, H, L, d, h, C, F32)
+    got = run_backward(prob, inp, dout, dW, dM)
+    for (bi, hi) in ((0, 0), (1, 3)):
+        sl = (slice(bi, bi + 1), slice(hi, hi + 1))
+        ref = oracle.chunk_backward(oracle.SWIGLU, inp["q64"][sl], inp["k64"][sl],
+                                    inp["v64"][sl], inp["eta"][sl], inp["alpha"][sl],
+                                    inp["beta"][sl], inp["W0"][sl], inp["M0"][sl], dout[sl],
+                                    dW[sl], dM[sl], C, hidden=h)
+        errs = {n: rel_fro(got[n][sl], ref[n]) for n in NAMES}
+        log(f"  unit ({bi},{hi}) rel_fro " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+        for n in NAMES:
+            assert errs[n] <= TOL, (bi, hi, n, errs[n])

@@ -42,7 +42,9 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow
 
 struct Plan {
   int64_t B, H, BH, L, d, h, C, Cp, nC, P;
-  int kind, io, mode, krep;
+  int kind, io, mode;
+  int krep;   // operand shadow layout: 1 = bf16 weights, 2 = bf16 hi/lo pairs
+  int krepA;  // fused path: phase A products on hi only (1) or on hi/lo (2)
   int averaged = 0;  // chunk-averaged beta, gamma (E2TTT_FLAG_CHUNK_AVERAGED_DECAY)
   int qknorm = 0;    // SiLU + L2 prologue on q, k (E2TTT_FLAG_QK_SILU_L2)
   int rownorm = 0;   // chunk-boundary row normalisation (E2TTT_FLAG_POST_CHUNK_ROW_L2)
@@ -70,7 +72,10 @@ e2ttt_status check_problem(const e2ttt_problem* p) {
   if ((p->flags & ~static_cast<uint32_t>(E2TTT_FLAG_COMPENSATED_WEIGHTS |
                                          E2TTT_FLAG_CHUNK_AVERAGED_DECAY |
                                          E2TTT_FLAG_QK_SILU_L2 |
-                                         E2TTT_FLAG_POST_CHUNK_ROW_L2)) != 0u)
+                                         E2TTT_FLAG_POST_CHUNK_ROW_L2 |
+                                         E2TTT_FLAG_PLAIN_BF16_WEIGHTS)) != 0u)
+    return E2TTT_EINVAL;
+  if ((p->flags & E2TTT_FLAG_COMPENSATED_WEIGHTS) && (p->flags & E2TTT_FLAG_PLAIN_BF16_WEIGHTS))
     return E2TTT_EINVAL;
   if (p->reserved != 0u) return E2TTT_EINVAL;
   if (p->batch < 1 || p->heads < 1 || p->seq_len < 0 || p->dim < 1 || p->chunk < 1)
@@ -127,8 +132,12 @@ e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
     q.fused = true;
     q.Cp = (q.C + 127) / 128 * 128;
     q.opsz = 2;
-    q.krep = (p->flags & E2TTT_FLAG_COMPENSATED_WEIGHTS) ? 2 : 1;
-    q.rbA = (q.krep == 2 || q.BH * (2 * q.Cp / 64) >= 512) ? 64 : 32;
+    // Weight operands: hi/lo shadows and phase B (the products that feed the
+    // chunk-end state) on the pair, unless plain bf16 is asked for; phase A
+    // (readout and residuals) on the pair only with compensated weights.
+    q.krep = (p->flags & E2TTT_FLAG_PLAIN_BF16_WEIGHTS) ? 1 : 2;
+    q.krepA = (p->flags & E2TTT_FLAG_COMPENSATED_WEIGHTS) ? 2 : 1;
+    q.rbA = (q.krepA == 2 || q.BH * (2 * q.Cp / 64) >= 512) ? 64 : 32;
     // Register-resident phase A (plain bf16 operands, h = 128 or 256): about
     // one workgroup per CU, each taking a contiguous run of one unit's 32-row
     // tiles (the count divides the unit's tiles so none is left empty).  Used
@@ -137,7 +146,7 @@ e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
     // overlaps the second hidden block's weights with the first block's
     // compute, is faster (measured).
     q.wpuA = 0;
-    if (q.krep == 1 && (q.h == 128 || q.h == 256)) {
+    if (q.krepA == 1 && (q.h == 128 || q.h == 256)) {
       const int64_t ntA = 2 * q.Cp / 32;
       int64_t w = (kCUs + q.BH - 1) / q.BH;
       if (w > ntA) w = ntA;
@@ -167,6 +176,7 @@ e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
     q.Cp = (q.C + 127) / 128 * 128;
     q.opsz = q.io == E2TTT_BF16 ? 2 : 4;
     q.krep = (q.io == E2TTT_BF16 && (p->flags & E2TTT_FLAG_COMPENSATED_WEIGHTS)) ? 2 : 1;
+    q.krepA = q.krep;
     const size_t T = q.opsz;
     q.kw = take(f4 * q.BH * q.nC * q.Cp);
     q.km = take(f4 * q.BH * q.nC * q.Cp);
@@ -506,9 +516,9 @@ void launch_fused(const Plan& q, const void* qv, const void* kv, const void* vv,
     a.last = static_cast<int>(r == q.nC - 1);
     a.Win = r == 0 ? W0 : Wend;
     a.Min = r == 0 ? M0 : Mend;
-    void (*kA)(FusedArgs) = q.krep == 2 ? k_phaseA<64, 2>
+    void (*kA)(FusedArgs) = q.krepA == 2 ? k_phaseA<64, 2>
                            : (q.rbA == 64 ? k_phaseA<64, 1> : k_phaseA<32, 1>);
-    const size_t ldsA = q.krep == 2 ? PhaseACfg<64, 2>::LDS_BYTES
+    const size_t ldsA = q.krepA == 2 ? PhaseACfg<64, 2>::LDS_BYTES
                         : (q.rbA == 64 ? PhaseACfg<64, 1>::LDS_BYTES : PhaseACfg<32, 1>::LDS_BYTES);
     void (*kB)(FusedArgs) = q.krep == 2 ? k_phaseB<2> : k_phaseB<1>;
     if (q.wpuA > 0) {

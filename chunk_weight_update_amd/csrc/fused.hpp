@@ -205,9 +205,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   const int64_t tok0 = static_cast<int64_t>(a.r) * a.C;
   const int64_t nv = fused_nvalid(a);
   const bf16_t* X = (isQ ? a.q : a.k) + (u * a.L + tok0) * FD;
-  const bf16_t* W13 = a.w13s + u * 2 * a.h * P::KD;
-  const bf16_t* W2 = a.w2s + u * FD * (KREP * a.h);
-  const int64_t w2ld = KREP * a.h;
+  // Shadow row strides follow the layout (a.krep); with KREP = 1 and a
+  // hi/lo layout only the hi halves are read.
+  const int64_t ld13 = a.krep * FD;
+  const bf16_t* W13 = a.w13s + u * 2 * a.h * ld13;
+  const bf16_t* W2 = a.w2s + u * FD * (a.krep * a.h);
+  const int64_t w2ld = a.krep * a.h;
   const int nhb = static_cast<int>(a.h / P::HBK);
 
   const int wave = threadIdx.x >> 6;
@@ -216,7 +219,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   TileCopy<RB, FD, 256> cx;
   TileCopy<P::NS, P::KD, 256> c13;
   auto w13_rows = [&](int hb) {
-    return [=](int rr) -> const bf16_t* { return W13 + (static_cast<int64_t>(hb) * P::NS + rr) * P::KD; };
+    return [=](int rr) -> const bf16_t* { return W13 + (static_cast<int64_t>(hb) * P::NS + rr) * ld13; };
   };
 
   cx.load([&](int rr) -> const bf16_t* { return p0 + rr < nv ? X + (p0 + rr) * FD : nullptr; }, X);
@@ -451,21 +454,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   bf16x8_t w13[MB][2][8];  // [m-block][W1, W3][d k-block]
   bf16x8_t w2[4][KB2];     // [d m-block of 32][hidden k-block of 16]
   {
-    const bf16_t* W13 = a.w13s + u * 2 * a.h * FD;
+    // Shadow rows hold [hi | lo] when the layout carries pairs (a.krep = 2);
+    // this kernel multiplies the hi halves only.
+    const int64_t ld13 = a.krep * FD, ld2 = a.krep * a.h;
+    const bf16_t* W13 = a.w13s + u * 2 * a.h * ld13;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int64_t i = wave * HW + 32 * mb + l32;  // hidden unit of this lane
-      const bf16_t* r1 = W13 + (64 * (i / 32) + i % 32) * FD + 8 * hf;
+      const bf16_t* r1 = W13 + (64 * (i / 32) + i % 32) * ld13 + 8 * hf;
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) {
         w13[mb][0][kb] = *reinterpret_cast<const bf16x8_t*>(r1 + 16 * kb);
-        w13[mb][1][kb] = *reinterpret_cast<const bf16x8_t*>(r1 + 32 * FD + 16 * kb);
+        w13[mb][1][kb] = *reinterpret_cast<const bf16x8_t*>(r1 + 32 * ld13 + 16 * kb);
       }
     }
-    const bf16_t* W2 = a.w2s + u * FD * a.h;
+    const bf16_t* W2 = a.w2s + u * FD * ld2;
 #pragma unroll
     for (int jm = 0; jm < 4; ++jm) {
-      const bf16_t* rj = W2 + (32 * jm + l32) * a.h + wave * HW;
+      const bf16_t* rj = W2 + (32 * jm + l32) * ld2 + wave * HW;
 #pragma unroll
       for (int kb = 0; kb < KB2; ++kb) {
         const bf16x4_t lo = *reinterpret_cast<const bf16x4_t*>(rj + 16 * kb + 4 * hf);

@@ -74,6 +74,10 @@ WORKLOADS = {w.name: w for w in [
              F32, "nearunit"),
     Workload("swiglu-d128h256-b2h4-l4096-c512-bf16-nearunit", SWIGLU, 2, 4, 4096, 128, 256, 512, BF16,
              "nearunit"),
+    Workload("swiglu-d128h256-b1h16-l32768-c2048-bf16-nearunit", SWIGLU, 1, 16, 32768, 128, 256,
+             2048, BF16, "nearunit"),
+    Workload("swiglu-d768h1536-b1h1-l24576-c8192-bf16-nearunit", SWIGLU, 1, 1, 24576, 768, 1536,
+             8192, BF16, "nearunit"),
 ]}
 
 # The workload the benchmark line is quoted on.

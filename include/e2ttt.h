@@ -12,7 +12,10 @@
  *     kernels K^M_t = eta_t*beta~_t and K^W_t = eta_t*beta~_t*R_t of §3.2:
  *         M_C = cM*M_0 + sum_t K^M_t G_t
  *         W_C = cW*W_0 + cWM*M_0 + sum_t K^W_t G_t
- *     with beta~_t, gamma~_t suffix products taken in log space (App. A.2);
+ *     with beta~_t, gamma~_t the suffix products of beta and gamma over the
+ *     chunk's later tokens (App. A.2 forms them in log space; here they are
+ *     fp64 products of linear maps in a suffix scan, see
+ *     e2ttt_scalar_kernels);
  *   - gamma_t = 1 - eta_t*alpha_t (Eq. 14, App. A.3), or gamma_t = alpha_t
  *     with E2TTT_ALPHA_IS_GAMMA;
  *   - the readout is o_t = f_{W_0}(q_t) with the chunk-start weights (Eq. 6);
@@ -74,16 +77,26 @@ typedef enum {
   E2TTT_ALPHA_IS_GAMMA = 1           /* gamma = alpha                  */
 } e2ttt_decay_mode;
 
-/* Bits of e2ttt_problem.flags. */
+/* Bits of e2ttt_problem.flags.
+ *
+ * Precision of the fast-weight operands (SwiGLU, bf16 io).  The matrix cores
+ * take bf16 operands; the fast weights are fp32.  A weight rounded to bf16
+ * carries 8 mantissa bits; a hi/lo pair (W = hi + lo, both multiplied against
+ * the same activations) carries ~16.  By default, with d = 128, the products
+ * that feed the chunk-end state (the recomputed W1 x, W3 x and the W2^T g of
+ * the backward at W_0) use the hi/lo pair and the readout's forward uses hi
+ * only: the state's error per chunk is then ~1.6e-3 instead of ~2.4e-3,
+ * which matters when every chunk rebuilds the state from gradients that are
+ * polynomial in W_0, so that relative errors roughly double from chunk to
+ * chunk.  The other shapes use plain bf16 weights unless the
+ * compensated flag is set. */
 enum {
-  /* SwiGLU with bf16 io: feed the fast weights to the matrix cores as a
-   * bf16 hi/lo pair (W = hi + lo, both operands multiplied against the same
-   * activations) in the forward and backward products.  The weight operand
-   * then carries ~16 mantissa bits instead of 8, at about 1.5x the
-   * matrix-core work of the whole call.  Ignored for fp32 io and LINEAR. */
+  /* SwiGLU with bf16 io: the hi/lo pair in every forward and backward
+   * product (the readout's too), at about 1.7x the matrix-core work of
+   * plain bf16 weights.  Ignored for fp32 io and LINEAR. */
   E2TTT_FLAG_COMPENSATED_WEIGHTS = 1u,
   /* The chunk-averaged variant ("Rethinking Expressivity and Efficiency in
-   * Test-Time Training", §4.3 Table 5 and App. B.3 Table 8): within each
+   * Test-Time Training", §5.4 Table 5 and App. B.3 Table 8): within each
    * chunk the per-token momentum factors beta_t and decay factors gamma_t
    * (after decay_mode) are replaced by their arithmetic means over the
    * chunk's tokens before the scalar kernels are formed; eta_t stays per
@@ -107,7 +120,13 @@ enum {
    * chunk's readout and descent directions use the normalised W.  Applies to
    * e2ttt_chunk_forward, its timed twin and e2ttt_decode_step (at a call with
    * chunk_end set), and the backward (through every normalisation). */
-  E2TTT_FLAG_POST_CHUNK_ROW_L2 = 8u
+  E2TTT_FLAG_POST_CHUNK_ROW_L2 = 8u,
+  /* SwiGLU with bf16 io and d = 128: plain bf16 fast-weight operands in every
+   * product (the fastest setting; ~2.4e-3 relative error on the chunk-end
+   * state per chunk).  Exclusive with E2TTT_FLAG_COMPENSATED_WEIGHTS
+   * (EINVAL when both are set); no effect on other shapes, fp32 io, LINEAR,
+   * the decode step and the backward, which use their weights in fp32. */
+  E2TTT_FLAG_PLAIN_BF16_WEIGHTS = 16u
 };
 
 /* Problem description.  struct_size must equal sizeof(e2ttt_problem). */

@@ -35,7 +35,7 @@
  *     Architecture"): SiLU applied to q_t and k_t, then L2 normalisation of
  *     each token's vector, before anything else uses them.  The pages give no
  *     epsilon; this divides by max(||x||, 1e-12).
- *   - Variant (averaged != 0): the chunk-averaged ablation of §4.3 (Table 5)
+ *   - Variant (averaged != 0): the chunk-averaged ablation of §5.4 (Table 5)
  *     and App. B.3 (Table 8), where the per-token momentum and decay factors
  *     beta_t, gamma_t of a chunk are collapsed to chunk-level scalars.  The
  *     pages do not say which average; this takes the arithmetic mean over the

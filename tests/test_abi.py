@@ -77,7 +77,9 @@ def test_status_strings():
     (swiglu(flags=cwu.FLAG_QK_SILU_L2), cwu.OK),
     (swiglu(flags=cwu.FLAG_POST_CHUNK_ROW_L2), cwu.OK),
     (linear(flags=cwu.FLAG_POST_CHUNK_ROW_L2), cwu.OK),
-    (swiglu(flags=16), cwu.EINVAL),
+    (swiglu(flags=cwu.FLAG_PLAIN_BF16_WEIGHTS), cwu.OK),
+    (swiglu(flags=cwu.FLAG_PLAIN_BF16_WEIGHTS | cwu.FLAG_COMPENSATED_WEIGHTS), cwu.EINVAL),
+    (swiglu(flags=32), cwu.EINVAL),
     (linear(hidden=3), cwu.EINVAL),
     (swiglu(dim=96), cwu.EUNSUPPORTED),
     (swiglu(hidden=200), cwu.EUNSUPPORTED),
@@ -104,7 +106,13 @@ def test_struct_size_and_reserved_checked():
 def test_workspace_bytes():
     n = cwu.workspace_bytes(swiglu())
     assert n > 0 and n % 256 == 0
-    assert cwu.workspace_bytes(swiglu(flags=cwu.FLAG_COMPENSATED_WEIGHTS)) > n
+    # d = 128 bf16: the default shadows carry hi/lo pairs (as with compensated
+    # weights); plain bf16 weights need half of that shadow space
+    assert cwu.workspace_bytes(swiglu(flags=cwu.FLAG_COMPENSATED_WEIGHTS)) == n
+    assert cwu.workspace_bytes(swiglu(flags=cwu.FLAG_PLAIN_BF16_WEIGHTS)) < n
+    big = dict(dim=768, hidden=1536, chunk=8192, seq_len=57344, batch=1, heads=1)
+    assert (cwu.workspace_bytes(swiglu(flags=cwu.FLAG_COMPENSATED_WEIGHTS, **big))
+            > cwu.workspace_bytes(swiglu(**big)))
     assert cwu.workspace_bytes(swiglu(io_dtype=cwu.F32)) > n
     assert cwu.workspace_bytes(swiglu(seq_len=0)) == 0
     with pytest.raises(cwu.E2tttError):

@@ -15,7 +15,7 @@ Two properties of the SwiGLU dynamics decide how a workload can be compared:
   chunk-start state (rounded to fp32, exactly what the GPU is given), for
   every chunk whose start state is representable; the full trajectory is
   checked for finiteness, for the first chunk's readout, and (2 chunks) at
-  the full bar with compensated weight operands.
+  the full bar with the default flags.
 * Near-unit scalars (App. A.3 regime (i), eta_base = 1e-2, alpha_base =
   1e-1 of App. B.3) keep the state O(1): the whole trajectory is compared.
 """
@@ -154,9 +154,34 @@ def test_two_chunk_workload_full_bar_with_compensated_weights():
     full_compare(w, flags=cwu.FLAG_COMPENSATED_WEIGHTS)
 
 
-def test_two_chunk_workload_plain_bf16_reported():
-    """Plain bf16 operands on the two-chunk workload: the second chunk inherits
-    the first chunk's ~3e-3 and doubles it (quadratic dynamics), landing near
-    the 5e-3 bar; the bound checked here is the derived 1e-2."""
+def test_two_chunk_workload_default_flags_full_bar():
+    """The two-chunk workload (B8 x H16, C = 2048) over its whole trajectory
+    with the default flags, at the full bf16 bar.  Under the default scalars
+    each chunk rebuilds the state from gradients polynomial in its start
+    state, so chunk 0's error roughly doubles in chunk 1; the default keeps
+    the products that feed the state on hi/lo weight pairs, which keeps the
+    end state under 5e-3 (plain bf16 weights: ~5.4e-3)."""
     w = WORKLOADS["swiglu-d128h256-b8h16-l4096-c2048-bf16"]
-    full_compare(w, tol=(1e-2, 1e-2, 1e-2))
+    full_compare(w)
+
+
+def test_two_chunk_workload_plain_bf16_weights_reported():
+    """The opt-out (plain bf16 weights in every product): the second chunk
+    inherits the first chunk's ~2.4e-3 and roughly doubles it, landing just
+    above the 5e-3 bar; checked against the derived bound 1e-2."""
+    w = WORKLOADS["swiglu-d128h256-b8h16-l4096-c2048-bf16"]
+    full_compare(w, flags=cwu.FLAG_PLAIN_BF16_WEIGHTS, tol=(1e-2, 1e-2, 1e-2))
+
+
+@pytest.mark.parametrize("name", [
+    "swiglu-d128h256-b1h16-l32768-c2048-bf16-nearunit",
+    "swiglu-d768h1536-b1h1-l24576-c8192-bf16-nearunit",
+])
+def test_nearunit_multichunk_full_trajectory(name):
+    """Whole trajectories in one call at the layer shapes of the long-prefill
+    workload (B1 x H16, L = 32768, C = 2048: 16 chunks on the fused path with
+    the token-split phase B and the split-sum state epilogue) and of the
+    large-state workload (d = 768, h = 1536, C = 8192, three chunks: the
+    256-tile path with the split aggregation), with the near-unit scalars so
+    that the carried state stays within fp32's range; full bf16 bar."""
+    full_compare(WORKLOADS[name])

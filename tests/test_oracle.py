@@ -321,7 +321,7 @@ def test_planted_mistakes_are_caught():
     assert _rel(mutated(use_decay=False), Wref) > 1e-3
 
 
-# --- Chunk-averaged variant (the ablation of §4.3 / App. B.3 of the E2-TTT
+# --- Chunk-averaged variant (the ablation of §5.4 / App. B.3 of the E2-TTT
 # page: per-token beta_t, gamma_t collapsed to chunk-level scalars; reading:
 # arithmetic means over the chunk's tokens).
 

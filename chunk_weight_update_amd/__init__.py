@@ -68,7 +68,10 @@ EXPORTED = ("e2ttt_validate", "e2ttt_workspace_bytes", "e2ttt_chunk_forward",
             "e2ttt_scalar_kernels", "e2ttt_chunk_forward_timed", "e2ttt_status_string",
             "e2ttt_decode_workspace_bytes", "e2ttt_decode_step",
             "e2ttt_backward_workspace_bytes", "e2ttt_chunk_backward",
-            "e2ttt_chunk_forward_states", "e2ttt_chunk_backward_states")
+            "e2ttt_chunk_forward_states", "e2ttt_chunk_backward_states",
+            "e2ttt_chunk_forward_noalloc")
+# Scratch size built into e2ttt_chunk_forward_noalloc (E2TTT_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # e2ttt_kernel_class
 KERNEL_SCAN, KERNEL_PREP, KERNEL_FWD13, KERNEL_FWD2, KERNEL_BWD, KERNEL_AGG = range(6)
@@ -98,6 +101,8 @@ def lib() -> ctypes.CDLL:
             L.e2ttt_workspace_bytes.restype = ctypes.c_int
             L.e2ttt_chunk_forward.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t, vp]
             L.e2ttt_chunk_forward.restype = ctypes.c_int
+            L.e2ttt_chunk_forward_noalloc.argtypes = [P] + [vp] * 12
+            L.e2ttt_chunk_forward_noalloc.restype = ctypes.c_int
             L.e2ttt_chunk_forward_timed.argtypes = ([P] + [vp] * 12 + [ctypes.c_size_t, vp] +
                                                     [ctypes.c_int, ctypes.POINTER(vp),
                                                      ctypes.c_int,
@@ -170,6 +175,19 @@ def chunk_forward(prob: Problem, q, k, v, eta, alpha, beta, W0, M0, out, W_end, 
         int(workspace_nbytes), _stream(stream))
     if check and st != OK:
         raise E2tttError(st, "e2ttt_chunk_forward")
+    return st
+
+
+def chunk_forward_noalloc(prob: Problem, q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end,
+                          stream=None, check: bool = True) -> int:
+    """Call ``e2ttt_chunk_forward_noalloc``: chunk_forward on the library's
+    built-in per-GPU scratch instead of a caller workspace.  Returns the
+    status; raises E2tttError on failure when ``check``."""
+    st = lib().e2ttt_chunk_forward_noalloc(
+        ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(alpha), _ptr(beta),
+        _ptr(W0), _ptr(M0), _ptr(out), _ptr(W_end), _ptr(M_end), _stream(stream))
+    if check and st != OK:
+        raise E2tttError(st, "e2ttt_chunk_forward_noalloc")
     return st
 
 

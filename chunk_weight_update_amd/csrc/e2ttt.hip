@@ -15,6 +15,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "e2ttt.h"
 #include "kernels.hpp"
@@ -703,6 +704,37 @@ e2ttt_status forward_impl(const e2ttt_problem* prob, const void* q, const void* 
 
 }  // namespace
 
+// Scratch of e2ttt_chunk_forward_noalloc: one array per GPU, in the code
+// object, so that the entry point needs no allocation.  Host code never uses
+// the array's name as an address (that is a host-side stand-in): the device
+// address of each GPU's copy is looked up once per device with
+// hipGetSymbolAddress and kept.
+static_assert(E2TTT_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) unsigned char scratch[E2TTT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];  // per device; guarded by g_scratch_mu
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device, with that device current).
+e2ttt_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return E2TTT_EHIP;
+  if (dev < 0 || dev >= 64) return E2TTT_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return E2TTT_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return E2TTT_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 e2ttt_status e2ttt_chunk_forward(const e2ttt_problem* prob, const void* q, const void* k,
@@ -724,6 +756,26 @@ e2ttt_status e2ttt_chunk_forward_states(const e2ttt_problem* prob, const void* q
   Instr none;
   return forward_impl(prob, q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end, workspace,
                       workspace_bytes, stream, none, W_starts, M_starts, true);
+}
+
+e2ttt_status e2ttt_chunk_forward_noalloc(const e2ttt_problem* prob, const void* q,
+                                         const void* k, const void* v, const float* eta,
+                                         const float* alpha, const float* beta,
+                                         const float* W0, const float* M0, void* out,
+                                         float* W_end, float* M_end, void* stream) {
+  Plan pl;
+  const e2ttt_status st = make_plan(prob, &pl);
+  if (st != E2TTT_OK) return st;
+  if (pl.total > E2TTT_NOALLOC_SCRATCH_BYTES) return E2TTT_EWORKSPACE;
+  void* ws = nullptr;
+  if (pl.total > 0) {
+    const e2ttt_status sa = scratch_address(&ws);
+    if (sa != E2TTT_OK) return sa;
+  }
+  Instr none;
+  return forward_impl(prob, q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end, ws,
+                      pl.total > 0 ? static_cast<size_t>(E2TTT_NOALLOC_SCRATCH_BYTES) : 0,
+                      stream, none);
 }
 
 e2ttt_status e2ttt_chunk_forward_timed(const e2ttt_problem* prob, const void* q, const void* k,

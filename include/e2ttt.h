@@ -190,6 +190,27 @@ E2TTT_API e2ttt_status e2ttt_chunk_forward_states(const e2ttt_problem* prob, con
                                                   float* M_starts, void* workspace,
                                                   size_t workspace_bytes, void* stream);
 
+/* e2ttt_chunk_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, results and checks as e2ttt_chunk_forward,
+ * minus the workspace: the call uses a scratch array of
+ * E2TTT_NOALLOC_SCRATCH_BYTES built into the library, one per GPU (each GPU
+ * holds it from the library's load until the process ends), and calls no
+ * allocating routine.  Problems whose e2ttt_workspace_bytes() exceeds that
+ * size return E2TTT_EWORKSPACE (nothing launched).  The array is shared by
+ * every call on one GPU and keeps the last call's contents (the forward
+ * treats it as uninitialised scratch): calls that may overlap in time on one
+ * GPU, on different streams or from different threads, race and must be
+ * serialised by the caller.  The device address of a GPU's array is looked
+ * up at the first call on that GPU (E2TTT_EHIP if that fails). */
+#define E2TTT_NOALLOC_SCRATCH_BYTES (64u << 20)
+E2TTT_API e2ttt_status e2ttt_chunk_forward_noalloc(const e2ttt_problem* prob, const void* q,
+                                                   const void* k, const void* v,
+                                                   const float* eta, const float* alpha,
+                                                   const float* beta, const float* W0,
+                                                   const float* M0, void* out, float* W_end,
+                                                   float* M_end, void* stream);
+
 /* The per-token scalar kernels alone (§3.2, App. A.2-A.3), for every chunk:
  *   k_w[b,h,t] = K^W_t = eta_t * beta~_t * R_t  (weight kernel)
  *   k_m[b,h,t] = K^M_t = eta_t * beta~_t        (momentum kernel)

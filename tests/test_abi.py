@@ -332,3 +332,16 @@ def test_backward_kept_states_with_row_normalisation_unsupported():
         a["dbeta"], a["dW0"], a["dM0"], a["workspace"], a["nws"], stream=0, check=False,
         W_starts=f(3 * np_), M_starts=f(3 * np_))
     assert st == cwu.EUNSUPPORTED
+
+
+def test_noalloc_size_and_problem_checked_on_the_host():
+    """e2ttt_chunk_forward_noalloc checks the problem and the scratch size
+    before any HIP call: EWORKSPACE for a problem whose workspace exceeds the
+    built-in scratch, EINVAL for a malformed problem."""
+    L = cwu.lib()
+    big = swiglu(batch=8, heads=16, chunk=2048)
+    assert cwu.workspace_bytes(big) > cwu.NOALLOC_SCRATCH_BYTES
+    args = [None] * 11 + [None]
+    assert L.e2ttt_chunk_forward_noalloc(ctypes.byref(big), *args) == cwu.EWORKSPACE
+    assert L.e2ttt_chunk_forward_noalloc(ctypes.byref(swiglu(chunk=0)), *args) == cwu.EINVAL
+    assert cwu.workspace_bytes(swiglu()) <= cwu.NOALLOC_SCRATCH_BYTES

@@ -3,18 +3,27 @@
 
 One step = one e2ttt_chunk_forward over the whole workload (all batch x head
 units, all chunks: scan, forward at W_0, readout, backward, both scaled
-aggregations, chunk-end states), inputs already resident in HBM.
+aggregations, chunk-end states), inputs already resident in HBM.  The
+default workload is the largest layer of the set: one head, SwiGLU fast
+weight d = 768 / h = 1536 (3.5M state entries), 57,344 tokens in chunks of
+8,192, bf16 q/k/v, fp32 states.
 
 Prints ONE JSON line:
-  value         tokens/s = batch * seq_len / (time per step), N = 1 GPU
+  value         tokens/s = batch * seq_len / (time per step), N = 1 GPU,
+                over K back-to-back steps; per_call_ms gives the median,
+                p10 and p90 of the single calls (an event between calls)
   roofline      dominant kernel: algorithmic flops per launch / its average
                 launch duration (HIP events recorded at the start and end of
                 every launch of that kernel by e2ttt_chunk_forward_timed, in
-                a second timed pass of the same steps) against the published
+                a second pass of the same steps) against the published
                 peak; traffic = HBM bytes per launch from the committed
                 rocprofv3 counter summary when it matches the current code
   cpu_baseline  the fp64 oracle timed on this host's cores on a bounded
-                sample of the same workload, scaled to tokens/s
+                sample of the same workload (the first chunk of the first
+                units), scaled to tokens/s
+  parity        rel_fro of out, W_end, M_end against that oracle sample
+  system        CPU model, ROCm version, device name and compute units
+  other_configs the other workloads' timings (shorter runs)
 """
 from __future__ import annotations
 
@@ -365,7 +374,7 @@ def backward_bench_swiglu(with_oracle, reps=10):
            "config": {"workload": f"swiglu-d{d}h{h}-b{B}h{H}-l{L}-c{C}-fp32"},
            "ms_per_call": ms, "tokens_per_s": B * H * L / (ms * 1e-3),
            "tflops_algorithmic": flops / (ms * 1e-3) / 1e12,
-           "frac_of_fp32_vector_peak": flops / (ms * 1e-3) / 157.3e12}
+           "frac_of_fp32_matrix_peak": flops / (ms * 1e-3) / (PEAK_FP32_TFLOPS * 1e12)}
     if with_oracle:
         import oracle
         oracle.build(force=False)
@@ -389,70 +398,38 @@ def algorithmic_flops(w):
     return 26.0 * w.d * w.h * w.L * w.B * w.H
 
 
-def cpu_baseline(w, inp, budget_s):
-    """Time the fp64 oracle on a bounded sample: the first n (b, h) units of
-    the workload over the full sequence, n chosen so that it runs for about
-    budget_s; scaled to workload tokens/s."""
-    import numpy as np
+def system_info():
+    """Host CPU model, usable threads, ROCm version, device name and CU count."""
+    import torch
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    rocm = None
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        try:
+            with open(path) as f:
+                rocm = f.read().strip()
+                break
+        except OSError:
+            continue
+    prop = torch.cuda.get_device_properties(0)
+    return {"cpu_model": cpu, "cpu_threads_usable": len(os.sched_getaffinity(0)),
+            "rocm_version": rocm, "hip_runtime": torch.version.hip, "torch": torch.__version__,
+            "device_name": prop.name, "gcn_arch": getattr(prop, "gcnArchName", None),
+            "compute_units": prop.multi_processor_count,
+            "peaks": {"bf16_mfma_tflops": PEAK_BF16_TFLOPS, "fp32_mfma_tflops": PEAK_FP32_TFLOPS,
+                      "hbm_gbs": PEAK_HBM_GBS}}
 
-    import oracle
-    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
-    oracle.set_threads(cores)
-    oracle.build(force=False)
-    BH = w.B * w.H
 
-    def run_units(n):
-        sl = lambda a: a.reshape((BH,) + a.shape[2:])[:n][None]
-        t0 = time.perf_counter()
-        oracle.chunk_forward(w.kind, sl(inp["q64"]), sl(inp["k64"]), sl(inp["v64"]),
-                             sl(inp["eta"]), sl(inp["alpha"]), sl(inp["beta"]), sl(inp["W0"]),
-                             sl(inp["M0"]), w.C, w.h)
-        return time.perf_counter() - t0
-
-    t1 = run_units(1)
-    n = int(max(1, min(BH, budget_s / max(t1, 1e-6))))
-    tn = run_units(n) if n > 1 else t1
-    t_full = tn * BH / n
-    return {"value": w.B * w.L / t_full, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} of {BH} (batch, head) units x all {w.L} tokens "
-                      f"({tn:.1f} s fp64, literal token-wise recurrence), scaled to the "
-                      f"whole workload"}
-
-
-def main():
-    ap = argparse.ArgumentParser(description=__doc__)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=None)
-    ap.add_argument("--flags", type=int, default=0, help="e2ttt_problem.flags")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-kernel-timing", action="store_true",
-                    help="skip the per-kernel event pass (for profiler runs)")
-    ap.add_argument("--no-scan-microbench", action="store_true",
-                    help="skip the 2^26-token scan microbenchmark")
-    ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="after the timed steps, run a plain device-to-device copy of this "
-                         "many MiB 5 times (the known-size reference for HBM byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(the (batch, head) units would shard across GPUs with no communication); "
-              "run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
-
+def device_inputs(w, inp, dev="cuda:0"):
     import numpy as np
     import torch
-
-    import chunk_weight_update_amd as cwu
-    from chunk_weight_update_amd.inputs import BENCH_WORKLOAD, WORKLOADS, make_workload_inputs
-
-    w = WORKLOADS[args.workload or BENCH_WORKLOAD]
-    torch.cuda.set_device(0)
-    log(f"bench: workload {w.name}")
-    inp = make_workload_inputs(w, seed=0)
-    dev = "cuda:0"
     t = {}
     for n in ("q", "k", "v"):
         a = np.ascontiguousarray(inp[n])
@@ -460,44 +437,23 @@ def main():
                 else torch.from_numpy(a)).to(dev)
     for n in ("eta", "alpha", "beta", "W0", "M0"):
         t[n] = torch.from_numpy(inp[n]).to(dev)
-    prob = cwu.make_problem(w.kind, w.B, w.H, w.L, w.d, w.h, w.C, w.io, 0, args.flags)
-    run = cwu.ChunkForward(prob, device=dev)
-    call_args = (t["q"], t["k"], t["v"], t["eta"], t["alpha"], t["beta"], t["W0"], t["M0"])
+    return t
 
-    for _ in range(args.warmup):
-        run(*call_args)
-    torch.cuda.synchronize()
-    log(f"bench: warmup {args.warmup} done")
 
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
-        run(*call_args)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    tokens = w.B * w.L
-    value = tokens / (ms * 1e-3)
-    log(f"bench: {args.steps} steps, {ms:.4f} ms/step, {value:.4g} tokens/s")
+def percentile(xs, p):
+    xs = sorted(xs)
+    if not xs:
+        return None
+    k = (len(xs) - 1) * p / 100.0
+    lo, hi = int(k), min(int(k) + 1, len(xs) - 1)
+    return xs[lo] + (xs[hi] - xs[lo]) * (k - lo)
 
-    if args.copy_calibration_mib > 0:
-        nbytes = args.copy_calibration_mib << 20
-        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"bench: copy calibration, 5 x {nbytes} bytes device to device")
-        del src, dst
 
-    if args.no_kernel_timing:
-        print(json.dumps({"metric": "TTT-layer fwd tokens/sec on 1 MI355X; MFMA util % of bf16 peak",
-                          "value": value, "unit": "tokens/s", "ms_per_step": ms,
-                          "config": w.describe()}), flush=True)
-        return
-    # Second timed pass: per-kernel-class launch durations with HIP events.
+def kernel_pass(w, prob, run, call_args, steps):
+    """Per-kernel-class launch durations: e2ttt_chunk_forward_timed records
+    HIP events at the start and end of every launch of one class."""
+    import chunk_weight_update_amd as cwu
+    import torch
     ev = HipEvents()
     classes = ([cwu.KERNEL_SCAN, cwu.KERNEL_LINEAR_FWD, cwu.KERNEL_LINEAR_AGG] if w.kind == 0
                else [cwu.KERNEL_SCAN, cwu.KERNEL_PREP, cwu.KERNEL_FWD13, cwu.KERNEL_FWD2,
@@ -505,7 +461,7 @@ def main():
                      cwu.KERNEL_STATE, cwu.KERNEL_PROLOGUE])
     per_step_launches = 2 * max(w.n_chunks, 2) + 2
     kernels = {}
-    steps_k = max(1, min(args.steps, 10))
+    steps_k = max(1, min(steps, 10))
     for cls in classes:
         evs = ev.create(2 * per_step_launches * steps_k)
         per = []
@@ -531,32 +487,228 @@ def main():
             "ms_per_step": avg_ms * launches_per_step,
             ("tflops" if unit == "flop" else "gbs"): rate / (1e12 if unit == "flop" else 1e9),
             "work_per_launch": per_launch, "work_unit": unit}
-        log(f"bench: kernel {cwu.KERNEL_NAMES[cls]}: {launches_per_step:g} launches/step, "
-            f"avg {avg_ms * 1e3:.1f} us, {kernels[cwu.KERNEL_NAMES[cls]]}")
+    return kernels
 
+
+def roofline_of(w, kernels):
     peak_mfma = PEAK_BF16_TFLOPS if w.io == 1 else PEAK_FP32_TFLOPS
     dom_name = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     dk = kernels[dom_name]
     traffic = measured_traffic(dom_name, w.name)
     if dk["work_unit"] == "flop":
-        roof = {"kernel": dom_name, "bound": "mfma", "achieved": dk["tflops"],
+        return {"kernel": dom_name, "bound": "mfma", "achieved": dk["tflops"],
                 "peak": peak_mfma, "unit": "TFLOP/s", "frac": dk["tflops"] / peak_mfma,
                 "traffic": traffic}
-    else:
-        roof = {"kernel": dom_name, "bound": "hbm", "achieved": dk["gbs"], "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": dk["gbs"] / PEAK_HBM_GBS, "traffic": traffic}
-    flops = algorithmic_flops(w)
+    return {"kernel": dom_name, "bound": "hbm", "achieved": dk["gbs"], "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": dk["gbs"] / PEAK_HBM_GBS, "traffic": traffic}
+
+
+def run_workload(w, steps, warmup, flags=0, kernel_timing=True, inp=None):
+    """Time `steps` back-to-back e2ttt_chunk_forward calls of workload `w`
+    (inputs resident in HBM), with an event between consecutive calls, so
+    both the whole timed region and every single call are measured."""
+    import chunk_weight_update_amd as cwu
+    import torch
+    from chunk_weight_update_amd.inputs import make_workload_inputs
+    if inp is None:
+        inp = make_workload_inputs(w, seed=0)
+    t = device_inputs(w, inp)
+    prob = cwu.make_problem(w.kind, w.B, w.H, w.L, w.d, w.h, w.C, w.io, 0, flags)
+    run = cwu.ChunkForward(prob, device="cuda:0")
+    call_args = (t["q"], t["k"], t["v"], t["eta"], t["alpha"], t["beta"], t["W0"], t["M0"])
+    for _ in range(warmup):
+        run(*call_args)
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(steps):
+        run(*call_args)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    ms = evs[0].elapsed_time(evs[-1]) / steps
+    per_call = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    res = {"config": w.describe() | {"flags": flags}, "ms_per_step": ms,
+           "value": w.B * w.L / (ms * 1e-3),
+           "per_call_ms": {"median": percentile(per_call, 50), "p10": percentile(per_call, 10),
+                           "p90": percentile(per_call, 90), "n": steps},
+           "tflops_algorithmic": algorithmic_flops(w) / (ms * 1e-3) / 1e12}
+    res["mfma_util_pct_of_bf16_peak"] = 100.0 * res["tflops_algorithmic"] / PEAK_BF16_TFLOPS
+    if kernel_timing:
+        res["kernels"] = kernel_pass(w, prob, run, call_args, steps)
+        res["roofline"] = roofline_of(w, res["kernels"])
+    res["_run"] = (run, t, prob)
+    return res
+
+
+def oracle_sample(w, inp, budget_s):
+    """The fp64 oracle on the first chunk of the first n (b, h) units (n
+    chosen so that it runs for about budget_s): timed for the CPU baseline,
+    and kept as the reference for the parity figures of the bench line."""
+    import oracle
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    oracle.set_threads(cores)
+    oracle.build(force=False)
+    BH = w.B * w.H
+    C = min(w.C, w.L)
+
+    def sl(a, n):
+        a = a.reshape((BH,) + a.shape[2:])[:n][None]
+        return a[..., :C, :] if a.ndim == 4 else (a[..., :C] if a.shape[-1] == w.L else a)
+
+    def run_units(n):
+        t0 = time.perf_counter()
+        ref = oracle.chunk_forward(w.kind, sl(inp["q64"], n), sl(inp["k64"], n),
+                                   sl(inp["v64"], n), sl(inp["eta"], n), sl(inp["alpha"], n),
+                                   sl(inp["beta"], n), sl(inp["W0"], n), sl(inp["M0"], n),
+                                   w.C, w.h)
+        return time.perf_counter() - t0, ref
+
+    t1, ref = run_units(1)
+    n = int(max(1, min(BH, budget_s / max(t1, 1e-6))))
+    tn, ref = run_units(n) if n > 1 else (t1, ref)
+    # A sample well under the budget is repeated (up to 3 runs, median).
+    times = [tn]
+    while len(times) < 3 and sum(times) + tn <= budget_s:
+        times.append(run_units(n)[0])
+    times.sort()
+    return {"n_units": n, "tokens": C, "seconds": times[len(times) // 2], "runs": len(times),
+            "cores": cores, "ref": ref, "slice": sl}
+
+
+def parity_on_sample(w, res, smp, inp):
+    """rel_fro of the timed call's first-chunk outputs, and of a first-chunk
+    call's end states, against the oracle sample (the first chunk of the
+    first n units: the whole chunk from W_0)."""
+    import numpy as np
+    import torch
+    import chunk_weight_update_amd as cwu
+    run, t, prob = res["_run"]
+    n, C, sl = smp["n_units"], smp["tokens"], smp["slice"]
+    ro, rW, rM = smp["ref"]
+    BH = w.B * w.H
+
+    def f64(x):
+        return x.detach().float().cpu().numpy().astype(np.float64)
+
+    def rel(x, r):
+        return float(np.linalg.norm((x - r).ravel()) / np.linalg.norm(r.ravel()))
+    out_timed = f64(run.out).reshape((BH, w.L, w.d))[:n, :C][None]
+    sub = {k: sl(inp[k], n) for k in ("q", "k", "v", "eta", "alpha", "beta", "W0", "M0")}
+    ts = device_inputs(w, sub)
+    p1 = cwu.make_problem(w.kind, 1, n, C, w.d, w.h, w.C, w.io, 0)
+    r1 = cwu.ChunkForward(p1, device="cuda:0")
+    o1, W1, M1 = r1(ts["q"], ts["k"], ts["v"], ts["eta"], ts["alpha"], ts["beta"], ts["W0"],
+                    ts["M0"])
+    torch.cuda.synchronize()
+    return {"sample": f"first chunk ({C} tokens) of {n} of {BH} (batch, head) units, from W_0",
+            "out_timed_call": rel(out_timed, ro), "out": rel(f64(o1), ro),
+            "W_end": rel(f64(W1), rW), "M_end": rel(f64(M1), rM),
+            "tolerance": {"out": 1e-2, "W_end": 5e-3, "M_end": 5e-3} if w.io == 1
+            else {"out": 1e-5, "W_end": 1e-5, "M_end": 1e-5}}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--flags", type=int, default=0, help="e2ttt_problem.flags")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true",
+                    help="skip the per-kernel event pass (for profiler runs)")
+    ap.add_argument("--no-scan-microbench", action="store_true",
+                    help="skip the side measurements (scan microbenchmark, decode, backward)")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the other workloads' short timings")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed steps, run a plain device-to-device copy of this "
+                         "many MiB 5 times (the known-size reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the (batch, head) units would shard across GPUs with no communication); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from chunk_weight_update_amd.inputs import BENCH_WORKLOAD, WORKLOADS, make_workload_inputs
+
+    w = WORKLOADS[args.workload or BENCH_WORKLOAD]
+    torch.cuda.set_device(0)
+    log(f"bench: workload {w.name}")
+    inp = make_workload_inputs(w, seed=0)
+    res = run_workload(w, args.steps, args.warmup, args.flags,
+                       kernel_timing=not args.no_kernel_timing, inp=inp)
+    log(f"bench: {args.steps} steps, {res['ms_per_step']:.4f} ms/step, "
+        f"{res['value']:.4g} tokens/s, per call {res['per_call_ms']}")
+
+    if args.copy_calibration_mib > 0:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"bench: copy calibration, 5 x {nbytes} bytes device to device")
+        del src, dst
+
+    metric = "TTT-layer fwd tokens/sec on 1 MI355X; MFMA util % of bf16 peak"
+    if args.no_kernel_timing:
+        print(json.dumps({"metric": metric, "value": res["value"], "unit": "tokens/s",
+                          "ms_per_step": res["ms_per_step"], "config": res["config"]}),
+              flush=True)
+        return
+    for k, v in res["kernels"].items():
+        log(f"bench: kernel {k}: {v}")
     line = {
-        "metric": "TTT-layer fwd tokens/sec on 1 MI355X; MFMA util % of bf16 peak",
-        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16" if w.io == 1 else "fp32", "data": "synthetic",
-        "config": w.describe() | {"flags": args.flags},
-        "mfma_util_pct_of_bf16_peak": 100.0 * flops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
-        "tflops_algorithmic": flops / (ms * 1e-3) / 1e12,
-        "roofline": roof,
-        "kernels": kernels,
+        "metric": metric, "value": res["value"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.io == 1 else "fp32", "data": "synthetic",
+        "config": res["config"],
+        "per_call_ms": res["per_call_ms"],
+        "mfma_util_pct_of_bf16_peak": res["mfma_util_pct_of_bf16_peak"],
+        "tflops_algorithmic": res["tflops_algorithmic"],
+        "roofline": res["roofline"],
+        "kernels": res["kernels"],
+        "system": system_info(),
     }
+    if not args.no_cpu_baseline:
+        log("bench: fp64 oracle on a sample of the workload (host cores)")
+        smp = oracle_sample(w, inp, args.cpu_seconds)
+        line["parity"] = parity_on_sample(w, res, smp, inp)
+        log(f"bench: parity on the sample {line['parity']}")
+        line["cpu_baseline"] = {
+            # token-heads per second on the sample -> tokens per second of
+            # the workload (each token carries H heads)
+            "value": smp["n_units"] * smp["tokens"] / smp["seconds"] / w.H,
+            "unit": "tokens/s", "cores": smp["cores"], "kind": "oracle",
+            "sample": f"first chunk ({smp['tokens']} tokens) of {smp['n_units']} of "
+                      f"{w.B * w.H} (batch, head) units from W_0, {smp['seconds']:.1f} s fp64 "
+                      f"(median of {smp['runs']} runs) "
+                      f"(literal token-wise recurrence), scaled to the whole workload's "
+                      f"tokens/s"}
+    else:
+        line["cpu_baseline"] = None
+    del res["_run"]
+    if not args.no_other_configs and args.workload is None:
+        others = {}
+        for name in ("linear-d64-b1h1-l256-c64-fp32", "swiglu-d128h256-b2h4-l4096-c512-bf16",
+                     "swiglu-d128h256-b8h16-l4096-c2048-bf16",
+                     "swiglu-d128h256-b1h16-l32768-c2048-bf16"):
+            wo = WORKLOADS[name]
+            ro = run_workload(wo, 20, 5)
+            del ro["_run"]
+            others[name] = {k: ro[k] for k in ("ms_per_step", "value", "per_call_ms",
+                                                "tflops_algorithmic", "roofline")}
+            log(f"bench: other workload {name}: {others[name]}")
+            torch.cuda.empty_cache()
+        line["other_configs"] = others
     if not args.no_scan_microbench:
         line["decode"] = decode_bench(w)
         log(f"bench: decode step {line['decode']}")
@@ -565,11 +717,6 @@ def main():
         line["backward"] = backward_bench(not args.no_cpu_baseline)
         line["backward_swiglu"] = backward_bench_swiglu(not args.no_cpu_baseline)
         log(f"bench: linear backward {line['backward']}")
-    if not args.no_cpu_baseline:
-        log("bench: timing the fp64 oracle on the host cores")
-        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
-    else:
-        line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
 
 

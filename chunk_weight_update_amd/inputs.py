@@ -81,7 +81,7 @@ WORKLOADS = {w.name: w for w in [
 ]}
 
 # The workload the benchmark line is quoted on.
-BENCH_WORKLOAD = "swiglu-d128h256-b2h4-l4096-c512-bf16"
+BENCH_WORKLOAD = "swiglu-d768h1536-b1h1-l57344-c8192-bf16"
 
 
 def _sig(z: np.ndarray) -> np.ndarray:

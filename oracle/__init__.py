@@ -89,6 +89,14 @@ def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
+def _variant(averaged: bool, lact: bool) -> int:
+    """Variant code of the C functions: 0 the E2-TTT recurrence, 1 its
+    chunk-averaged ablation, 2 the LaCT rule."""
+    if averaged and lact:
+        raise ValueError("averaged and lact are exclusive")
+    return 2 if lact else int(bool(averaged))
+
+
 def state_size(kind: int, d: int, h: int) -> int:
     return d * d if kind == LINEAR else 3 * d * h
 
@@ -105,10 +113,12 @@ def set_threads(n: int) -> None:
 
 def chunk_forward(kind, q, k, v, eta, alpha, beta, W0, M0, chunk, hidden=0,
                   decay_mode=GAMMA_1_MINUS_ETA_ALPHA, averaged=False, qk_norm=False,
-                  row_norm=False):
+                  row_norm=False, lact=False):
     """Run the literal recurrence.  q,k,v: [B,H,L,d]; eta/alpha/beta: [B,H,L];
     W0, M0: [B,H,P].  averaged: the chunk-averaged variant (beta, gamma
-    replaced by their means over each chunk).  qk_norm: the q/k prologue (SiLU,
+    replaced by their means over each chunk).  lact: the LaCT rule instead
+    (one step per chunk on the eta-weighted sum of the descent directions,
+    with the chunk means of beta and gamma; exclusive with averaged).  qk_norm: the q/k prologue (SiLU,
     then L2 normalisation per token) before use.  row_norm: every row of every
     fast-weight matrix divided by its L2 norm after each chunk (the
     chunk-boundary stabiliser of App. B.1).  Returns (out [B,H,L,d],
@@ -128,8 +138,9 @@ def chunk_forward(kind, q, k, v, eta, alpha, beta, W0, M0, chunk, hidden=0,
     rc = lib.oracle_chunk_forward(kind, decay_mode, B, H, L, d, hidden, chunk,
                                   _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
                                   _ptr(alpha), _ptr(beta), _ptr(W0), _ptr(M0),
-                                  _ptr(out), _ptr(Wend), _ptr(Mend), int(bool(averaged)),
-                                  int(bool(qk_norm)), int(bool(row_norm)))
+                                  _ptr(out), _ptr(Wend), _ptr(Mend),
+                                  _variant(averaged, lact), int(bool(qk_norm)),
+                                  int(bool(row_norm)))
     if rc != 0:
         raise RuntimeError(f"oracle_chunk_forward failed with code {rc}")
     return out, Wend, Mend
@@ -157,7 +168,8 @@ def fast_forward(kind, W, x, d, hidden=0):
     return y
 
 
-def scalar_kernels(eta, alpha, beta, decay_mode=GAMMA_1_MINUS_ETA_ALPHA, averaged=False):
+def scalar_kernels(eta, alpha, beta, decay_mode=GAMMA_1_MINUS_ETA_ALPHA, averaged=False,
+                   lact=False):
     """Impulse-response kernels of each segment.  eta/alpha/beta: [nseg, n].
     Returns kw [nseg,n], km [nseg,n], coef [nseg,3] = (cW, cM, cWM)."""
     lib = _load()
@@ -168,7 +180,7 @@ def scalar_kernels(eta, alpha, beta, decay_mode=GAMMA_1_MINUS_ETA_ALPHA, average
     coef = np.empty((nseg, 3), dtype=np.float64)
     rc = lib.oracle_scalar_kernels(decay_mode, nseg, n, _ptr(eta), _ptr(alpha),
                                    _ptr(beta), _ptr(kw), _ptr(km), _ptr(coef),
-                                   int(bool(averaged)))
+                                   _variant(averaged, lact))
     if rc != 0:
         raise RuntimeError(f"oracle_scalar_kernels failed with code {rc}")
     return kw, km, coef

@@ -42,6 +42,20 @@
  *     chunk's tokens (of gamma_t, after Eq. 14), and otherwise the same
  *     recurrence.
  *
+ *   - Variant (averaged == 2): the LaCT update rule as §3.2 ("Two scalar
+ *     kernels with distinct temporal weighting") sets it against E2-TTT
+ *     (Eq. 5, whose display is missing from the page): the gradient term
+ *     carries only eta_t, with neither the momentum suffix product nor the
+ *     weight-decay ratio sum, and the momentum factor is collapsed to a chunk
+ *     average; §1 describes LaCT as one fast-weight update per chunk from the
+ *     gradient of a summed loss.  Reading taken: per chunk, with bbar and
+ *     gbar the means of beta_t and gamma_t (after Eq. 14) over the chunk's
+ *     tokens,
+ *         M_C = bbar * M_0 + sum_t eta_t G_t
+ *         W_C = gbar * W_0 + M_C
+ *     i.e. the recurrence's step taken once, on the eta-weighted sum of the
+ *     chunk's descent directions (all evaluated at W_0); readout as above.
+ *
  *   - Option (row_norm != 0): the stabiliser of App. B.1 ("Training
  *     Details"), L2 normalisation of the fast-weight matrices at each chunk
  *     boundary, following LaCT.  The pages name neither the axis nor an
@@ -278,7 +292,8 @@ static void normalise_rows_vjp(int kind, int64_t d, int64_t h, const double* Wpr
  *   W0, M0, Wend, Mend : [B, H, P]
  * Chunks are consecutive runs of C tokens; a final run shorter than C (when
  * C does not divide L) is a chunk of its own.  L == 0 copies the state.
- * averaged != 0 selects the chunk-averaged variant, qk_norm != 0 the q/k
+ * averaged == 1 selects the chunk-averaged variant, averaged == 2 the LaCT
+ * rule, qk_norm != 0 the q/k
  * prologue, row_norm != 0 the chunk-boundary normalisation (see the header).
  * Returns 0 on success, nonzero on bad arguments or allocation failure.
  */
@@ -295,6 +310,7 @@ int oracle_chunk_forward(int kind, int decay_mode, int64_t B, int64_t H,
     return 1;
   if (B < 0 || H < 0 || L < 0 || d <= 0 || C <= 0) return 1;
   if (kind == OR_SWIGLU && h <= 0) return 1;
+  if (averaged < 0 || averaged > 2) return 1;
   const int64_t P = state_size(kind, d, h);
   const int64_t hh = kind == OR_LINEAR ? 1 : h;
   const int64_t Cmax = C < L ? C : (L > 0 ? L : 1);
@@ -366,7 +382,7 @@ int oracle_chunk_forward(int kind, int decay_mode, int64_t B, int64_t H,
         gam[t] = decay_factor(decay_mode, etu[t0 + t], alu[t0 + t]);
         bet[t] = beu[t0 + t];
       }
-      if (averaged) { /* chunk-level scalars: the means over the chunk */
+      if (averaged) { /* chunk-level scalars: the means over the chunk (both variants) */
         double sb = 0.0, sgm = 0.0;
         for (int64_t t = 0; t < n; ++t) {
           sb += bet[t];
@@ -418,6 +434,16 @@ int oracle_chunk_forward(int kind, int decay_mode, int64_t B, int64_t H,
           w = W + 2 * h * d + (r - 2 * h) * h;
           m = M + 2 * h * d + (r - 2 * h) * h;
         }
+        if (averaged == 2) { /* LaCT rule: one step on the eta-weighted sum */
+          for (int64_t j = 0; j < nc; ++j) {
+            double gs = 0.0;
+            for (int64_t t = 0; t < n; ++t)
+              gs += etu[t0 + t] * (left[t * lstride + lidx] * right[t * rstride + j]);
+            m[j] = bet[0] * m[j] + gs;          /* bet[], gam[] hold the means */
+            w[j] = gam[0] * w[j] + m[j];
+          }
+          continue;
+        }
         for (int64_t t = 0; t < n; ++t) {
           const double bt = bet[t];
           const double et = etu[t0 + t];
@@ -451,7 +477,8 @@ int oracle_chunk_forward(int kind, int decay_mode, int64_t B, int64_t H,
  *   coef[2] = cWM : W_C when M_0 = 1 (W_0 = 0, G = 0)
  * Arrays are [nseg, n] with nseg segments of n tokens; coef is [nseg, 3].
  * O(n^2) per segment: each impulse is propagated literally to the chunk end.
- * averaged != 0: beta and gamma replaced by their segment means first.
+ * averaged != 0: beta and gamma replaced by their segment means first;
+ * averaged == 2: the LaCT rule's single chunk step applied to each impulse.
  */
 int oracle_scalar_kernels(int decay_mode, int64_t nseg, int64_t n,
                           const double* eta, const double* alpha,
@@ -490,6 +517,21 @@ int oracle_scalar_kernels(int decay_mode, int64_t nseg, int64_t n,
         b[s] = sb;
         g[s] = sgm;
       }
+    }
+    if (averaged == 2) { /* LaCT rule: M_C = bbar M_0 + sum eta G, W_C = gbar W_0 + M_C */
+      const double bb = n > 0 ? b[0] : 1.0, gg = n > 0 ? g[0] : 1.0;
+      for (int64_t t = 0; t < n; ++t) {
+        const double m = bb * 0.0 + e[t] * 1.0;
+        kw[sg * n + t] = gg * 0.0 + m;
+        km[sg * n + t] = m;
+      }
+      double m = bb * 0.0 + 0.0; /* W_0 impulse */
+      coef[sg * 3 + 0] = gg * 1.0 + m;
+      m = bb * 1.0 + 0.0;        /* M_0 impulse */
+      coef[sg * 3 + 1] = m;
+      coef[sg * 3 + 2] = gg * 0.0 + m;
+      free(b); free(g);
+      continue;
     }
     for (int64_t t = 0; t < n; ++t) {
       /* token t receives the impulse: M = beta*0 + eta*1, W = gamma*0 + M */
@@ -744,6 +786,7 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
                           double* dq, double* dk, double* dv, double* deta,
                           double* dalpha, double* dbeta, double* dW0,
                           double* dM0, int qk_norm, int averaged, int row_norm) {
+  if (averaged < 0 || averaged > 1) return 1; /* the LaCT rule has no reverse mode here */
   if (kind != OR_LINEAR && kind != OR_SWIGLU) return 3;
   if (decay_mode != OR_GAMMA_1_MINUS_ETA_ALPHA &&
       decay_mode != OR_ALPHA_IS_GAMMA)

@@ -28,6 +28,7 @@ FLAG_CHUNK_AVERAGED_DECAY = 2
 FLAG_QK_SILU_L2 = 4
 FLAG_POST_CHUNK_ROW_L2 = 8
 FLAG_PLAIN_BF16_WEIGHTS = 16
+FLAG_LACT_RULE = 32
 
 
 class Problem(ctypes.Structure):

@@ -47,6 +47,7 @@ struct Plan {
   int krep;   // operand shadow layout: 1 = bf16 weights, 2 = bf16 hi/lo pairs
   int krepA;  // fused path: phase A products on hi only (1) or on hi/lo (2)
   int averaged = 0;  // chunk-averaged beta, gamma (E2TTT_FLAG_CHUNK_AVERAGED_DECAY)
+  int lact = 0;      // the LaCT rule's kernels (E2TTT_FLAG_LACT_RULE)
   int qknorm = 0;    // SiLU + L2 prologue on q, k (E2TTT_FLAG_QK_SILU_L2)
   int rownorm = 0;   // chunk-boundary row normalisation (E2TTT_FLAG_POST_CHUNK_ROW_L2)
   bool fused;   // two-kernel chunk step (SwiGLU, d = 128, bf16 io)
@@ -74,7 +75,10 @@ e2ttt_status check_problem(const e2ttt_problem* p) {
                                          E2TTT_FLAG_CHUNK_AVERAGED_DECAY |
                                          E2TTT_FLAG_QK_SILU_L2 |
                                          E2TTT_FLAG_POST_CHUNK_ROW_L2 |
-                                         E2TTT_FLAG_PLAIN_BF16_WEIGHTS)) != 0u)
+                                         E2TTT_FLAG_PLAIN_BF16_WEIGHTS |
+                                         E2TTT_FLAG_LACT_RULE)) != 0u)
+    return E2TTT_EINVAL;
+  if ((p->flags & E2TTT_FLAG_LACT_RULE) && (p->flags & E2TTT_FLAG_CHUNK_AVERAGED_DECAY))
     return E2TTT_EINVAL;
   if ((p->flags & E2TTT_FLAG_COMPENSATED_WEIGHTS) && (p->flags & E2TTT_FLAG_PLAIN_BF16_WEIGHTS))
     return E2TTT_EINVAL;
@@ -113,6 +117,7 @@ e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
   q.d = p->dim; q.h = p->hidden; q.C = p->chunk;
   q.kind = p->kind; q.io = p->io_dtype; q.mode = p->decay_mode;
   q.averaged = (p->flags & E2TTT_FLAG_CHUNK_AVERAGED_DECAY) ? 1 : 0;
+  q.lact = (p->flags & E2TTT_FLAG_LACT_RULE) ? 1 : 0;
   q.qknorm = (p->flags & E2TTT_FLAG_QK_SILU_L2) ? 1 : 0;
   q.rownorm = (p->flags & E2TTT_FLAG_POST_CHUNK_ROW_L2) ? 1 : 0;
   q.nC = q.L > 0 ? (q.L + q.C - 1) / q.C : 0;
@@ -333,6 +338,7 @@ ScanArgs scan_args(const Plan& q, const float* eta, const float* alpha, const fl
   ScanArgs sa;
   sa.eta = eta; sa.alpha = alpha; sa.beta = beta;
   sa.L = q.L; sa.C = q.C; sa.nC = q.nC; sa.mode = q.mode; sa.averaged = q.averaged;
+  sa.lact = q.lact;
   sa.kw = kw; sa.km = km;
   sa.ustride = ustride; sa.rstride = rstride; sa.pad = pad;
   sa.coef = coef; sa.cstride = cstride;
@@ -858,7 +864,8 @@ e2ttt_status e2ttt_decode_workspace_bytes(const e2ttt_problem* prob, size_t* byt
   if (!bytes) return E2TTT_EINVAL;
   const e2ttt_status st = check_problem(prob);
   if (st != E2TTT_OK) return st;
-  if (prob->flags & E2TTT_FLAG_CHUNK_AVERAGED_DECAY) return E2TTT_EUNSUPPORTED;
+  if (prob->flags & (E2TTT_FLAG_CHUNK_AVERAGED_DECAY | E2TTT_FLAG_LACT_RULE))
+    return E2TTT_EUNSUPPORTED;
   const int64_t h = prob->kind == E2TTT_LINEAR ? 0 : prob->hidden;
   *bytes = decode_ws_total(prob, prob->batch * prob->heads, prob->dim, h);
   return E2TTT_OK;
@@ -871,7 +878,8 @@ e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* q, const v
                                void* stream) {
   e2ttt_status st = check_problem(prob);
   if (st != E2TTT_OK) return st;
-  if (prob->flags & E2TTT_FLAG_CHUNK_AVERAGED_DECAY) return E2TTT_EUNSUPPORTED;
+  if (prob->flags & (E2TTT_FLAG_CHUNK_AVERAGED_DECAY | E2TTT_FLAG_LACT_RULE))
+    return E2TTT_EUNSUPPORTED;
   const int64_t BH = prob->batch * prob->heads, d = prob->dim;
   const int64_t h = prob->kind == E2TTT_LINEAR ? 0 : prob->hidden;
   const int64_t P = h == 0 ? d * d : 3 * d * h;
@@ -997,6 +1005,7 @@ e2ttt_status make_bwd_plan(const e2ttt_problem* p, BwdPlan* bp) {
   const Plan& q = bp->f;
   // Every flag of the forward is supported (the compensated-weights option
   // only concerns bf16 matrix operands; the backward computes in fp32).
+  if (q.lact) return E2TTT_EUNSUPPORTED;  // no reverse mode of the LaCT rule
   bp->qknorm = q.qknorm != 0;
   bp->rownorm = q.rownorm != 0;
   if (q.kind == E2TTT_LINEAR && q.d > 64) return E2TTT_EUNSUPPORTED;

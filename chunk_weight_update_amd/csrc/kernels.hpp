@@ -107,6 +107,7 @@ struct ScanArgs {
   int64_t L, C, nC;
   int mode;
   int averaged;  // beta, gamma replaced by their segment means
+  int lact;      // the LaCT rule: K^W = K^M = eta, (cW, cM, cWM) = segment means
   float* kw;
   float* km;
   int64_t ustride, rstride, pad;
@@ -166,7 +167,7 @@ __device__ __forceinline__ void scan_segment(int64_t seg, const ScanArgs& sa) {
   // fp64 by a fixed-order block reduction (lane 0 of each wave, then the
   // waves in order), so every thread holds the same two values.
   double bbar = 0.0, gbar = 0.0;
-  if (sa.averaged) {
+  if (sa.averaged || sa.lact) {
     __shared__ double s_red[2][NW];
     double sb = 0.0, sg = 0.0;
     for (int64_t i = tid; i < n; i += NT) {
@@ -192,6 +193,23 @@ __device__ __forceinline__ void scan_segment(int64_t seg, const ScanArgs& sa) {
     }
     bbar = sb / static_cast<double>(n);
     gbar = sg / static_cast<double>(n);
+  }
+  // The LaCT rule (one step per chunk on the eta-weighted gradient sum, with
+  // the chunk means of beta and gamma): K^W = K^M = eta, cW = mean(gamma),
+  // cM = cWM = mean(beta).  No scan.
+  if (sa.lact) {
+    for (int64_t i = tid; i < n; i += NT) {
+      const float e = e_g[i];
+      kw_o[i] = e;
+      km_o[i] = e;
+    }
+    if (tid == 0 && n > 0) {
+      float* cf = sa.coef + (u * sa.nC + r) * sa.cstride;
+      cf[0] = static_cast<float>(gbar);
+      cf[1] = static_cast<float>(bbar);
+      cf[2] = static_cast<float>(bbar);
+    }
+    return;
   }
 
   ScanVec vin = {1.0, 1.0, 1.0};  // v at the last token of the current round

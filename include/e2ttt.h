@@ -126,7 +126,22 @@ enum {
    * state per chunk).  Exclusive with E2TTT_FLAG_COMPENSATED_WEIGHTS
    * (EINVAL when both are set); no effect on other shapes, fp32 io, LINEAR,
    * the decode step and the backward, which use their weights in fp32. */
-  E2TTT_FLAG_PLAIN_BF16_WEIGHTS = 16u
+  E2TTT_FLAG_PLAIN_BF16_WEIGHTS = 16u,
+  /* The LaCT rule ("Rethinking Expressivity and Efficiency in Test-Time
+   * Training", §3.2 "Two scalar kernels with distinct temporal weighting",
+   * Eq. 5, and §1): one update per chunk from the eta-weighted sum of the
+   * chunk's descent directions, with the momentum and decay factors
+   * collapsed to their chunk means:
+   *     M_C = mean(beta) M_0 + sum_t eta_t G_t,  W_C = mean(gamma) W_0 + M_C
+   * (gamma after decay_mode; G_t at W_0; readout as the default).  The
+   * display of Eq. 5 is missing from the page; this is the reading of its
+   * description there (no momentum suffix product, no decay ratio sum).
+   * Same kernels as the default rule, only the scalar kernels differ:
+   * K^W = K^M = eta, (cW, cM, cWM) = (mean gamma, mean beta, mean beta).
+   * Applies to e2ttt_chunk_forward (and its twins) and e2ttt_scalar_kernels;
+   * EINVAL together with E2TTT_FLAG_CHUNK_AVERAGED_DECAY; EUNSUPPORTED for
+   * e2ttt_decode_step and the backward. */
+  E2TTT_FLAG_LACT_RULE = 32u
 };
 
 /* Problem description.  struct_size must equal sizeof(e2ttt_problem). */

@@ -56,9 +56,10 @@ def run_gpu(prob, t, stream=None):
             M.cpu().numpy().astype(np.float64))
 
 
-def run_oracle(kind, inp, C, h, decay_mode=0, averaged=False, qk_norm=False, row_norm=False):
+def run_oracle(kind, inp, C, h, decay_mode=0, averaged=False, qk_norm=False, row_norm=False,
+               lact=False):
     import oracle
     return oracle.chunk_forward(kind, inp["q64"], inp["k64"], inp["v64"], inp["eta"],
                                 inp["alpha"], inp["beta"], inp["W0"], inp["M0"], C, h,
                                 decay_mode=decay_mode, averaged=averaged, qk_norm=qk_norm,
-                                row_norm=row_norm)
+                                row_norm=row_norm, lact=lact)

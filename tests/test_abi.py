@@ -79,7 +79,10 @@ def test_status_strings():
     (linear(flags=cwu.FLAG_POST_CHUNK_ROW_L2), cwu.OK),
     (swiglu(flags=cwu.FLAG_PLAIN_BF16_WEIGHTS), cwu.OK),
     (swiglu(flags=cwu.FLAG_PLAIN_BF16_WEIGHTS | cwu.FLAG_COMPENSATED_WEIGHTS), cwu.EINVAL),
-    (swiglu(flags=32), cwu.EINVAL),
+    (swiglu(flags=cwu.FLAG_LACT_RULE), cwu.OK),
+    (linear(flags=cwu.FLAG_LACT_RULE), cwu.OK),
+    (swiglu(flags=cwu.FLAG_LACT_RULE | cwu.FLAG_CHUNK_AVERAGED_DECAY), cwu.EINVAL),
+    (swiglu(flags=64), cwu.EINVAL),
     (linear(hidden=3), cwu.EINVAL),
     (swiglu(dim=96), cwu.EUNSUPPORTED),
     (swiglu(hidden=200), cwu.EUNSUPPORTED),
@@ -217,6 +220,8 @@ def test_decode_host_checks():
     assert n >= 4 * B * H * (6 * h + d) and n % 256 == 0
     with pytest.raises(cwu.E2tttError):
         cwu.decode_workspace_bytes(swiglu(flags=cwu.FLAG_CHUNK_AVERAGED_DECAY))
+    with pytest.raises(cwu.E2tttError):
+        cwu.decode_workspace_bytes(swiglu(flags=cwu.FLAG_LACT_RULE))
     assert cwu.decode_workspace_bytes(swiglu(flags=cwu.FLAG_POST_CHUNK_ROW_L2)) == n
     # null tensors are rejected before anything touches a device
     st = cwu.lib().e2ttt_decode_step(ctypes.byref(base), *([None] * 10), 0, None, 0, None)
@@ -259,6 +264,8 @@ def test_backward_support_and_workspace():
     assert cwu.backward_workspace_bytes(linear(flags=cwu.FLAG_CHUNK_AVERAGED_DECAY)) > 0
     assert cwu.backward_workspace_bytes(swiglu(flags=cwu.FLAG_POST_CHUNK_ROW_L2)) > 0
     assert cwu.backward_workspace_bytes(swiglu(flags=cwu.FLAG_COMPENSATED_WEIGHTS)) > 0
+    with pytest.raises(cwu.E2tttError):
+        cwu.backward_workspace_bytes(linear(flags=cwu.FLAG_LACT_RULE))
     for bad in (linear(dim=128), linear(dim=80)):
         with pytest.raises(cwu.E2tttError) as e:
             cwu.backward_workspace_bytes(bad)

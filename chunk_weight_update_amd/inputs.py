@@ -162,3 +162,30 @@ def make_workload_inputs(w: Workload, seed: int = 0, m0_scale: float = 0.0,
     """Inputs shaped like workload ``w`` (optionally with fewer tokens/units)."""
     return make_inputs(w.kind, B or w.B, H or w.H, w.L if L is None else L, w.d, w.h,
                        w.io, seed=seed, regime=w.regime, m0_scale=m0_scale)
+
+
+def make_head_inputs(B: int, L: int, D: int, H: int, io: int, seed: int = 0,
+                     ) -> Dict[str, np.ndarray]:
+    """Inputs of the per-token scalar heads (numpy PCG64, in this order):
+      x [B, L, D] ~ N(0, 1), the layer input (unit-variance hidden states);
+      w [3H, D] ~ N(0, 1/D), the eta, alpha and beta head weights, so that
+        every pre-activation <w, x> is ~ N(0, 1) like the workloads' z draws;
+      bias [3H] ~ N(0, 0.25).
+    x and w are rounded to bf16 (RNE) for bf16 problems; the bias stays fp32.
+    Returns the io representations (x, w) and their fp64 widenings (x64,
+    w64), and bias (fp32)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, L, D)).astype(np.float32)
+    w = (rng.standard_normal((3 * H, D)) / np.sqrt(D)).astype(np.float32)
+    bias = (0.5 * rng.standard_normal(3 * H)).astype(np.float32)
+    out: Dict[str, np.ndarray] = {"bias": bias}
+    for name, a in (("x", x), ("w", w)):
+        if io == BF16:
+            bits = f32_to_bf16_bits(a)
+            out[name] = bits
+            out[name + "64"] = bf16_bits_to_f32(bits).astype(np.float64)
+        else:
+            out[name] = a
+            out[name + "64"] = a.astype(np.float64)
+    return out
+

@@ -77,6 +77,8 @@ def _load():
             lib.oracle_chunk_backward.argtypes = (
                 [ctypes.c_int, ctypes.c_int] + [i64] * 6 + [P] * 19 + [ctypes.c_int] * 3)
             lib.oracle_chunk_backward.restype = ctypes.c_int
+            lib.oracle_scalar_heads.argtypes = [i64] * 4 + [P] * 3 + [ctypes.c_double] * 2 + [P] * 3
+            lib.oracle_scalar_heads.restype = ctypes.c_int
             _lib = lib
     return _lib
 
@@ -218,3 +220,23 @@ def chunk_backward(kind, q, k, v, eta, alpha, beta, W0, M0, dout, dWend, dMend, 
     if rc != 0:
         raise RuntimeError(f"oracle_chunk_backward failed with code {rc}")
     return g
+
+
+def scalar_heads(x, w, bias, heads, eta_base, alpha_base):
+    """The per-token scalar heads: x [B, L, D] layer input, w [3H, D] (eta,
+    alpha, beta heads in that order), bias [3H].  Returns eta, alpha, beta
+    [B, H, L] (float64): eta_base * sigma(.), alpha_base * sigma(.), sigma(.)."""
+    lib = _load()
+    x, w, bias = _f64(x), _f64(w), _f64(bias)
+    B, L, D = x.shape
+    H = int(heads)
+    assert w.shape == (3 * H, D) and bias.shape == (3 * H,)
+    eta = np.empty((B, H, L))
+    alpha = np.empty((B, H, L))
+    beta = np.empty((B, H, L))
+    rc = lib.oracle_scalar_heads(B, L, D, H, _ptr(x), _ptr(w), _ptr(bias), float(eta_base),
+                                 float(alpha_base), _ptr(eta), _ptr(alpha), _ptr(beta))
+    if rc != 0:
+        raise RuntimeError(f"oracle_scalar_heads failed with code {rc}")
+    return eta, alpha, beta
+

@@ -56,6 +56,17 @@
  *     i.e. the recurrence's step taken once, on the eta-weighted sum of the
  *     chunk's descent directions (all evaluated at W_0); readout as above.
  *
+ *   - Scalar heads (oracle_scalar_heads): §4 ("Overall Architecture",
+ *     "Input-Dependent Dynamics") predicts eta_t, beta_t and alpha_t from the
+ *     layer input x_t by lightweight linear heads (Eqs. 12-14, App. B.4), and
+ *     App. B.3 says eta_base and alpha_base scale per-token sigmoid gates.
+ *     Eq. 13 (beta's "timescale parameterization", App. A.3) is missing from
+ *     the page; the reading taken is a plain sigmoid gate.  Per TTT head h:
+ *         eta_t   = eta_base   * sigma(<w_eta_h,   x_t> + b_eta_h)
+ *         alpha_t = alpha_base * sigma(<w_alpha_h, x_t> + b_alpha_h)
+ *         beta_t  =              sigma(<w_beta_h,  x_t> + b_beta_h)
+ *     and gamma_t = 1 - eta_t alpha_t (Eq. 14) downstream.
+ *
  *   - Option (row_norm != 0): the stabiliser of App. B.1 ("Training
  *     Details"), L2 normalisation of the fast-weight matrices at each chunk
  *     boundary, following LaCT.  The pages name neither the axis nor an
@@ -985,5 +996,33 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
   free(fb);
   free(fg);
 #undef CHUNK_FACTORS
+  return 0;
+}
+
+/*
+ * The per-token scalar heads (see the header): x [B, L, D] is the layer
+ * input, w [3H, D] the head weights in the order (eta heads 0..H-1, alpha
+ * heads, beta heads), bias [3H].  Writes eta, alpha, beta [B, H, L].
+ * Returns 0 on success, 1 on bad arguments.
+ */
+int oracle_scalar_heads(int64_t B, int64_t L, int64_t D, int64_t H, const double* x,
+                        const double* w, const double* bias, double eta_base,
+                        double alpha_base, double* eta, double* alpha, double* beta) {
+  if (B < 0 || L < 0 || D <= 0 || H <= 0) return 1;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < B * L; ++n) {
+    const int64_t b = n / L, t = n % L;
+    const double* xt = x + n * D;
+    for (int64_t c = 0; c < 3 * H; ++c) {
+      double z = 0.0;
+      for (int64_t j = 0; j < D; ++j) z += w[c * D + j] * xt[j];
+      const double s = sigm(z + bias[c]);
+      const int64_t head = c % H;
+      const int64_t o = (b * H + head) * L + t;
+      if (c < H) eta[o] = eta_base * s;
+      else if (c < 2 * H) alpha[o] = alpha_base * s;
+      else beta[o] = s;
+    }
+  }
   return 0;
 }

@@ -246,6 +246,37 @@ def decode_bench(w, reps=200):
             "tokens_per_s": B * H / (t * 1e-6), "gbs": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS}
 
 
+def heads_bench(reps=20):
+    """e2ttt_scalar_heads on the 1.3B-shaped layer (batch 8, 4096 tokens,
+    model dim 2048, 16 TTT heads, bf16 input and head weights; seeded
+    synthetic).  Algorithmic bytes: x and the head weights read once, the
+    three scalars written (12 B per token-head).  HBM-bound."""
+    import torch
+    import chunk_weight_update_amd as cwu
+    B, L, D, H = 8, 4096, 2048, 16
+    g = torch.Generator(device="cuda").manual_seed(2)
+    x = torch.randn((B, L, D), generator=g, device="cuda").to(torch.bfloat16)
+    w = (torch.randn((3 * H, D), generator=g, device="cuda") / D ** 0.5).to(torch.bfloat16)
+    bias = 0.5 * torch.randn((3 * H,), generator=g, device="cuda")
+    out = [torch.empty((B, H, L), device="cuda") for _ in range(3)]
+    prob = cwu.make_problem(cwu.SWIGLU, B, H, L, 128, 256, 2048, cwu.BF16)
+    for _ in range(3):
+        cwu.scalar_heads(prob, x, D, w, bias, 0.01, 0.1, *out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        cwu.scalar_heads(prob, x, D, w, bias, 0.01, 0.1, *out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = 2.0 * B * L * D + 2.0 * 3 * H * D + 12.0 * B * H * L
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"label": "per-token scalar heads, batch 8 x 4096 tokens, model dim 2048, 16 heads, "
+                     "bf16 (not the main metric)", "us": ms * 1e3, "gbs": gbs,
+            "frac_of_hbm_peak": gbs / PEAK_HBM_GBS, "bound": "hbm"}
+
+
 def backward_bench(with_oracle, reps=50):
     """The outer-loop backward (e2ttt_chunk_backward) on the linear workload's
     shape (d = 64, fp32; seeded synthetic inputs and upstream gradients),
@@ -714,6 +745,8 @@ def main():
         log(f"bench: decode step {line['decode']}")
         line["scan_microbench"] = scan_microbench()
         log(f"bench: scan microbenchmark {line['scan_microbench']}")
+        line["scalar_heads"] = heads_bench()
+        log(f"bench: scalar heads {line['scalar_heads']}")
         line["backward"] = backward_bench(not args.no_cpu_baseline)
         line["backward_swiglu"] = backward_bench_swiglu(not args.no_cpu_baseline)
         log(f"bench: linear backward {line['backward']}")

@@ -70,7 +70,7 @@ EXPORTED = ("e2ttt_validate", "e2ttt_workspace_bytes", "e2ttt_chunk_forward",
             "e2ttt_decode_workspace_bytes", "e2ttt_decode_step",
             "e2ttt_backward_workspace_bytes", "e2ttt_chunk_backward",
             "e2ttt_chunk_forward_states", "e2ttt_chunk_backward_states",
-            "e2ttt_chunk_forward_noalloc")
+            "e2ttt_chunk_forward_noalloc", "e2ttt_scalar_heads")
 # Scratch size built into e2ttt_chunk_forward_noalloc (E2TTT_NOALLOC_SCRATCH_BYTES).
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -102,6 +102,9 @@ def lib() -> ctypes.CDLL:
             L.e2ttt_workspace_bytes.restype = ctypes.c_int
             L.e2ttt_chunk_forward.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t, vp]
             L.e2ttt_chunk_forward.restype = ctypes.c_int
+            L.e2ttt_scalar_heads.argtypes = ([P, vp, ctypes.c_int64, vp, vp, ctypes.c_float,
+                                              ctypes.c_float] + [vp] * 4)
+            L.e2ttt_scalar_heads.restype = ctypes.c_int
             L.e2ttt_chunk_forward_noalloc.argtypes = [P] + [vp] * 12
             L.e2ttt_chunk_forward_noalloc.restype = ctypes.c_int
             L.e2ttt_chunk_forward_timed.argtypes = ([P] + [vp] * 12 + [ctypes.c_size_t, vp] +
@@ -237,6 +240,19 @@ def scalar_kernels(prob: Problem, eta, alpha, beta, k_w, k_m, chunk_coef, stream
                                     _ptr(k_w), _ptr(k_m), _ptr(chunk_coef), _stream(stream))
     if check and st != OK:
         raise E2tttError(st, "e2ttt_scalar_kernels")
+    return st
+
+
+def scalar_heads(prob: Problem, x, model_dim: int, w_heads, b_heads, eta_base: float,
+                 alpha_base: float, eta, alpha, beta, stream=None, check: bool = True) -> int:
+    """Call ``e2ttt_scalar_heads``: eta, alpha, beta [B, H, L] from the layer
+    input x [B, L, model_dim] and the head weights w_heads [3H, model_dim],
+    b_heads [3H].  Returns the status; raises on failure when ``check``."""
+    st = lib().e2ttt_scalar_heads(ctypes.byref(prob), _ptr(x), int(model_dim), _ptr(w_heads),
+                                  _ptr(b_heads), float(eta_base), float(alpha_base), _ptr(eta),
+                                  _ptr(alpha), _ptr(beta), _stream(stream))
+    if check and st != OK:
+        raise E2tttError(st, "e2ttt_scalar_heads")
     return st
 
 

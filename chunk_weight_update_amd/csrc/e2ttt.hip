@@ -24,6 +24,7 @@
 #include "decode.hpp"
 #include "backward.hpp"
 #include "swiglu_backward.hpp"
+#include "heads.hpp"
 
 using namespace e2ttt;
 
@@ -272,6 +273,10 @@ void set_lds_attributes() {
       reinterpret_cast<const void*>(&k_lin_bwd_tok<3>), reinterpret_cast<const void*>(&k_lin_bwd_tok<4>)};
   for (const void* f : fused_kernels)
     (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_heads<float>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_heads<bf16_t>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   g_attr_done.store(1, std::memory_order_release);
 }
 
@@ -782,6 +787,52 @@ e2ttt_status e2ttt_chunk_forward_noalloc(const e2ttt_problem* prob, const void* 
   return forward_impl(prob, q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end, ws,
                       pl.total > 0 ? static_cast<size_t>(E2TTT_NOALLOC_SCRATCH_BYTES) : 0,
                       stream, none);
+}
+
+e2ttt_status e2ttt_scalar_heads(const e2ttt_problem* prob, const void* x, int64_t model_dim,
+                                const void* w_heads, const float* b_heads, float eta_base,
+                                float alpha_base, float* eta, float* alpha, float* beta,
+                                void* stream) {
+  const e2ttt_status st = check_problem(prob);
+  if (st != E2TTT_OK) return st;
+  const int64_t B = prob->batch, H = prob->heads, L = prob->seq_len, D = model_dim;
+  if (D < 64 || D % 64 != 0 || D > 65536 || H > 64) return E2TTT_EUNSUPPORTED;
+  int64_t N;
+  if (!mul_ok(B, L, &N) || N / HeadsCfg<float>::ROWS >= (int64_t(1) << 31))
+    return E2TTT_EUNSUPPORTED;
+  if (L == 0) return E2TTT_OK;
+  if (!x || !w_heads || !b_heads || !eta || !alpha || !beta) return E2TTT_EINVAL;
+  if (!aligned(x, 16) || !aligned(w_heads, 16) || !aligned(b_heads, 4) || !aligned(eta, 4) ||
+      !aligned(alpha, 4) || !aligned(beta, 4))
+    return E2TTT_EINVAL;
+  const size_t el = prob->io_dtype == E2TTT_BF16 ? 2 : 4;
+  const size_t ns = static_cast<size_t>(B * H * L) * 4;
+  const Range in[] = {rng(x, static_cast<size_t>(N * D) * el),
+                      rng(w_heads, static_cast<size_t>(3 * H * D) * el),
+                      rng(b_heads, static_cast<size_t>(3 * H) * 4)};
+  const Range outs[] = {rng(eta, ns), rng(alpha, ns), rng(beta, ns)};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return E2TTT_EINVAL;
+    for (int j = 0; j < 3; ++j)
+      if (overlap(outs[i], in[j])) return E2TTT_EINVAL;
+  }
+  const e2ttt_status ds = device_ok();
+  if (ds != E2TTT_OK) return ds;
+  set_lds_attributes();
+  (void)hipGetLastError();
+  HeadsArgs ha;
+  ha.x = x; ha.w = w_heads; ha.bias = b_heads;
+  ha.N = N; ha.L = L; ha.D = D; ha.H = static_cast<int>(H);
+  ha.eta_base = eta_base; ha.alpha_base = alpha_base;
+  ha.eta = eta; ha.alpha = alpha; ha.beta = beta;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const unsigned grid = grid1((N + HeadsCfg<float>::ROWS - 1) / HeadsCfg<float>::ROWS);
+  if (prob->io_dtype == E2TTT_BF16)
+    hipLaunchKernelGGL(k_heads<bf16_t>, dim3(grid), dim3(256), HeadsCfg<bf16_t>::LDS_BYTES, hs, ha);
+  else
+    hipLaunchKernelGGL(k_heads<float>, dim3(grid), dim3(256), HeadsCfg<float>::LDS_BYTES, hs, ha);
+  return hipGetLastError() == hipSuccess ? E2TTT_OK : E2TTT_EHIP;
 }
 
 e2ttt_status e2ttt_chunk_forward_timed(const e2ttt_problem* prob, const void* q, const void* k,

@@ -244,6 +244,31 @@ E2TTT_API e2ttt_status e2ttt_scalar_kernels(const e2ttt_problem* prob, const flo
                                   float* k_w, float* k_m, float* chunk_coef,
                                   void* stream);
 
+/* The per-token scalar heads of the TTT branch ("Rethinking Expressivity
+ * and Efficiency in Test-Time Training", §4 Overall Architecture and
+ * Input-Dependent Dynamics; App. B.3, B.4): linear heads on the layer input
+ * give the inputs eta, alpha, beta of e2ttt_chunk_forward.  For token t of
+ * batch b and TTT head h (H = prob->heads):
+ *   eta[b,h,t]   = eta_base   * sigmoid(<w_heads[h],      x[b,t]> + b_heads[h])
+ *   alpha[b,h,t] = alpha_base * sigmoid(<w_heads[H + h],  x[b,t]> + b_heads[H + h])
+ *   beta[b,h,t]  =              sigmoid(<w_heads[2H + h], x[b,t]> + b_heads[2H + h])
+ * (App. B.3: the base scalars scale the sigmoid gates; Eq. 13, beta's
+ * timescale form, is missing from the page and taken as a plain sigmoid
+ * gate; gamma follows from eta and alpha downstream by Eq. 14.)
+ * x [B, L, model_dim] and w_heads [3H, model_dim] are of io_dtype, b_heads
+ * [3H] fp32; eta, alpha, beta [B, H, L] fp32 (the layout the forward takes).
+ * The products accumulate in fp32 on the matrix cores; x is read once for
+ * all heads.  Only batch, heads, seq_len and io_dtype of `prob` are used
+ * (the rest must validate).  Supported: model_dim a multiple of 64 in
+ * [64, 65536], H <= 64 (else EUNSUPPORTED).  x and w_heads 16-byte aligned,
+ * the rest 4-byte aligned; outputs must not overlap each other or the inputs
+ * (EINVAL).  L = 0 does nothing.  Asynchronous on `stream`. */
+E2TTT_API e2ttt_status e2ttt_scalar_heads(const e2ttt_problem* prob, const void* x,
+                                          int64_t model_dim, const void* w_heads,
+                                          const float* b_heads, float eta_base,
+                                          float alpha_base, float* eta, float* alpha,
+                                          float* beta, void* stream);
+
 /* Kernel classes of the chunk forward, for e2ttt_chunk_forward_timed. */
 typedef enum {
   E2TTT_KERNEL_SCAN = 0,       /* scalar kernels, all chunks (one launch)    */

@@ -352,3 +352,20 @@ def test_noalloc_size_and_problem_checked_on_the_host():
     assert L.e2ttt_chunk_forward_noalloc(ctypes.byref(big), *args) == cwu.EWORKSPACE
     assert L.e2ttt_chunk_forward_noalloc(ctypes.byref(swiglu(chunk=0)), *args) == cwu.EINVAL
     assert cwu.workspace_bytes(swiglu()) <= cwu.NOALLOC_SCRATCH_BYTES
+
+
+def test_scalar_heads_checked_on_the_host():
+    """e2ttt_scalar_heads rejects unsupported model dims and head counts, and
+    null or misaligned pointers, before any HIP call."""
+    L = cwu.lib()
+    p = swiglu()
+    assert L.e2ttt_scalar_heads(ctypes.byref(p), None, 96, None, None, 0.01, 0.1,
+                                None, None, None, None) == cwu.EUNSUPPORTED
+    assert L.e2ttt_scalar_heads(ctypes.byref(swiglu(heads=65)), None, 512, None, None, 0.01,
+                                0.1, None, None, None, None) == cwu.EUNSUPPORTED
+    assert L.e2ttt_scalar_heads(ctypes.byref(p), None, 512, None, None, 0.01, 0.1,
+                                None, None, None, None) == cwu.EINVAL
+    assert L.e2ttt_scalar_heads(ctypes.byref(swiglu(seq_len=0)), None, 512, None, None, 0.01,
+                                0.1, None, None, None, None) == cwu.OK
+    assert L.e2ttt_scalar_heads(ctypes.byref(swiglu(chunk=0)), None, 512, None, None, 0.01,
+                                0.1, None, None, None, None) == cwu.EINVAL

@@ -12,7 +12,8 @@ Recipe (all draws from numpy's PCG64 ``default_rng(seed)``, in this order):
      scalars are sigmoid transforms of them (``SCALARS`` below), stored fp32.
   3. Fast weights, per tensor over all (b, h): W1 [B,H,h,d], W3 [B,H,h,d],
      W2 [B,H,d,h] ~ N(0, 1/fan_in) (fan_in = d for W1, W3 and the linear W;
-     h for W2), fp32, packed [W1 | W3 | W2] per (b, h).
+     h for W2), fp32, packed [W1 | W3 | W2] per (b, h); the MLP learner
+     draws W1 then W2, packed [W1 | W2].
   4. M0 = 0, or with ``m0_scale`` > 0: M0 ~ N(0, m0_scale/fan_in) drawn in the
      same tensor order, so the M0 terms of the chunk-end state are exercised.
 
@@ -30,6 +31,7 @@ import numpy as np
 
 LINEAR = 0
 SWIGLU = 1
+MLP = 2
 F32 = 0
 BF16 = 1
 
@@ -49,7 +51,9 @@ class Workload:
 
     @property
     def P(self) -> int:
-        return self.d * self.d if self.kind == LINEAR else 3 * self.d * self.h
+        if self.kind == LINEAR:
+            return self.d * self.d
+        return (2 if self.kind == MLP else 3) * self.d * self.h
 
     @property
     def n_chunks(self) -> int:
@@ -57,7 +61,7 @@ class Workload:
 
     def describe(self) -> Dict:
         return {"workload": self.name,
-                "learner": "linear" if self.kind == LINEAR else "swiglu",
+                "learner": {LINEAR: "linear", SWIGLU: "swiglu", MLP: "mlp"}[self.kind],
                 "batch": self.B, "heads": self.H, "seq_len": self.L,
                 "dim": self.d, "hidden": self.h, "chunk": self.C,
                 "io_dtype": "bf16" if self.io == BF16 else "fp32",
@@ -145,6 +149,10 @@ def make_inputs(kind: int, B: int, H: int, L: int, d: int, h: int, io: int,
             return (rng.standard_normal((B, H, d, d)) * np.sqrt(scale / d)
                     ).reshape(B, H, d * d).astype(np.float32)
         W1 = rng.standard_normal((B, H, h, d)) * np.sqrt(scale / d)
+        if kind == MLP:  # [W1 | W2]
+            W2 = rng.standard_normal((B, H, d, h)) * np.sqrt(scale / h)
+            return np.concatenate([W1.reshape(B, H, -1), W2.reshape(B, H, -1)],
+                                  axis=-1).astype(np.float32)
         W3 = rng.standard_normal((B, H, h, d)) * np.sqrt(scale / d)
         W2 = rng.standard_normal((B, H, d, h)) * np.sqrt(scale / h)
         return np.concatenate([W1.reshape(B, H, -1), W3.reshape(B, H, -1),

@@ -40,6 +40,7 @@ _lib = None
 
 LINEAR = 0
 SWIGLU = 1
+MLP = 2
 GAMMA_1_MINUS_ETA_ALPHA = 0
 ALPHA_IS_GAMMA = 1
 
@@ -100,7 +101,7 @@ def _variant(averaged: bool, lact: bool) -> int:
 
 
 def state_size(kind: int, d: int, h: int) -> int:
-    return d * d if kind == LINEAR else 3 * d * h
+    return d * d if kind == LINEAR else (2 if kind == MLP else 3) * d * h
 
 
 def set_threads(n: int) -> None:

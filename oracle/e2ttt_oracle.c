@@ -28,9 +28,13 @@
  *   - Output: o_t = f_{W_0}(q_t), the chunk-start weights (Eq. 6, §3.2).
  *   - (W_C, M_C) of chunk r is (W_0, M_0) of chunk r+1 (§3 notation, §3.2
  *     "Cross-chunk equivalence ... follows by induction").
- *   - Inner learners: linear f_W(x) = W x (§2) and the three-matrix SwiGLU
+ *   - Inner learners: linear f_W(x) = W x (§2), the three-matrix SwiGLU
  *     f(x) = W2 (silu(W1 x) * (W3 x)) (§5.2, App. B.5 "three-matrix
- *     fast-weight network").
+ *     fast-weight network"), and the MLP learner of E2-TTT_MLP (§5, App.
+ *     B.3 Table 11, App. B.5: a smaller fast-weight network than the
+ *     SwiGLU's; its activation is not named on the page).  Reading taken:
+ *     the two-matrix f(x) = W2 silu(W1 x), the SwiGLU without its gate
+ *     branch, state packed [W1 (h x d) | W2 (d x h)].
  *   - Option (qk_norm != 0): the TTT branch's input prologue of §4 ("Overall
  *     Architecture"): SiLU applied to q_t and k_t, then L2 normalisation of
  *     each token's vector, before anything else uses them.  The pages give no
@@ -91,7 +95,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_LINEAR = 0, OR_SWIGLU = 1 };
+enum { OR_LINEAR = 0, OR_SWIGLU = 1, OR_MLP = 2 };
 enum { OR_GAMMA_1_MINUS_ETA_ALPHA = 0, OR_ALPHA_IS_GAMMA = 1 };
 
 static double sigm(double x) { return 1.0 / (1.0 + exp(-x)); }
@@ -146,11 +150,17 @@ static double decay_factor(int decay_mode, double eta, double alpha) {
 }
 
 static int64_t state_size(int kind, int64_t d, int64_t h) {
-  return kind == OR_LINEAR ? d * d : 3 * d * h;
+  return kind == OR_LINEAR ? d * d : kind == OR_MLP ? 2 * d * h : 3 * d * h;
+}
+
+/* Offset of W2 in a unit's packed state (SwiGLU: after W1, W3; MLP: after W1). */
+static int64_t w2_offset(int kind, int64_t d, int64_t h) {
+  return kind == OR_MLP ? h * d : 2 * h * d;
 }
 
 /* y = f_W(x).  For SwiGLU also returns the hidden pre-activations a1 = W1 x,
- * a3 = W3 x and z = silu(a1) * a3 (any of them may be NULL for linear). */
+ * a3 = W3 x and z = silu(a1) * a3 (any of them may be NULL for linear); for
+ * the MLP a1 = W1 x, z = silu(a1) and a3 = 1 (no gate branch). */
 static void fast_forward(int kind, int64_t d, int64_t h, const double* W,
                          const double* x, double* a1, double* a3, double* z,
                          double* y) {
@@ -164,8 +174,17 @@ static void fast_forward(int kind, int64_t d, int64_t h, const double* W,
   }
   const double* W1 = W;
   const double* W3 = W + h * d;
-  const double* W2 = W + 2 * h * d;
-  for (int64_t i = 0; i < h; ++i) {
+  const double* W2 = W + w2_offset(kind, d, h);
+  if (kind == OR_MLP) {
+    for (int64_t i = 0; i < h; ++i) {
+      double s1 = 0.0;
+      for (int64_t j = 0; j < d; ++j) s1 += W1[i * d + j] * x[j];
+      a1[i] = s1;
+      a3[i] = 1.0;
+      z[i] = s1 * sigm(s1);
+    }
+  }
+  for (int64_t i = 0; kind == OR_SWIGLU && i < h; ++i) {
     double s1 = 0.0, s3 = 0.0;
     for (int64_t j = 0; j < d; ++j) {
       s1 += W1[i * d + j] * x[j];
@@ -188,6 +207,7 @@ static void fast_forward(int kind, int64_t d, int64_t h, const double* W,
  *            G_W3 = u3 k^T,            u3 = (W2^T e) * silu(a1)    (h)
  *            G_W1 = u1 k^T,            u1 = (W2^T e) * a3 * silu'(a1)
  *   with silu'(a) = sigma(a) (1 + a (1 - sigma(a))).
+ *   MLP    : G_W2 = e z^T, G_W1 = u1 k^T with z = silu(a1), a3 = 1 above.
  * Chain rule of the loss of §2 through the learner; z is also returned. */
 static void descent_factors(int kind, int64_t d, int64_t h, const double* W,
                             const double* k, const double* v, double* e,
@@ -196,7 +216,7 @@ static void descent_factors(int kind, int64_t d, int64_t h, const double* W,
   fast_forward(kind, d, h, W, k, a1, a3, z, y);
   for (int64_t i = 0; i < d; ++i) e[i] = v[i] - y[i];
   if (kind == OR_LINEAR) return;
-  const double* W2 = W + 2 * h * d;
+  const double* W2 = W + w2_offset(kind, d, h);
   for (int64_t j = 0; j < h; ++j) {
     double dz = 0.0;
     for (int64_t i = 0; i < d; ++i) dz += W2[i * h + j] * e[i];
@@ -210,7 +230,7 @@ static void descent_factors(int kind, int64_t d, int64_t h, const double* W,
  * the state).  Exposed for the gradient checks of the test suite. */
 int oracle_token_descent(int kind, int64_t d, int64_t h, const double* W,
                          const double* k, const double* v, double* G) {
-  if (kind != OR_LINEAR && kind != OR_SWIGLU) return 1;
+  if (kind != OR_LINEAR && kind != OR_SWIGLU && kind != OR_MLP) return 1;
   int64_t hh = kind == OR_LINEAR ? 1 : h;
   double* buf = (double*)malloc(sizeof(double) * (size_t)(2 * d + 5 * hh));
   if (!buf) return 2;
@@ -223,11 +243,11 @@ int oracle_token_descent(int kind, int64_t d, int64_t h, const double* W,
   } else {
     double* G1 = G;
     double* G3 = G + h * d;
-    double* G2 = G + 2 * h * d;
+    double* G2 = G + w2_offset(kind, d, h);
     for (int64_t i = 0; i < h; ++i)
       for (int64_t j = 0; j < d; ++j) {
         G1[i * d + j] = u1[i] * k[j];
-        G3[i * d + j] = u3[i] * k[j];
+        if (kind == OR_SWIGLU) G3[i * d + j] = u3[i] * k[j];
       }
     for (int64_t i = 0; i < d; ++i)
       for (int64_t j = 0; j < h; ++j) G2[i * h + j] = e[i] * z[j];
@@ -239,7 +259,7 @@ int oracle_token_descent(int kind, int64_t d, int64_t h, const double* W,
 /* y = f_W(x) for one vector (readout check helper). */
 int oracle_fast_forward(int kind, int64_t d, int64_t h, const double* W,
                         const double* x, double* y) {
-  if (kind != OR_LINEAR && kind != OR_SWIGLU) return 1;
+  if (kind != OR_LINEAR && kind != OR_SWIGLU && kind != OR_MLP) return 1;
   int64_t hh = kind == OR_LINEAR ? 1 : h;
   double* buf = (double*)malloc(sizeof(double) * (size_t)(3 * hh));
   if (!buf) return 2;
@@ -255,8 +275,8 @@ static void normalise_rows(int kind, int64_t d, int64_t h, double* W) {
   for (int part = 0; part < (kind == OR_LINEAR ? 1 : 2); ++part) {
     double* base;
     if (kind == OR_LINEAR) { base = W; nrows = d; len = d; }
-    else if (part == 0) { base = W; nrows = 2 * h; len = d; }   /* W1, W3 */
-    else { base = W + 2 * h * d; nrows = d; len = h; }          /* W2 */
+    else if (part == 0) { base = W; nrows = kind == OR_MLP ? h : 2 * h; len = d; } /* W1 (, W3) */
+    else { base = W + w2_offset(kind, d, h); nrows = d; len = h; }                 /* W2 */
     for (int64_t r = 0; r < nrows; ++r) {
       double ss = 0.0;
       for (int64_t j = 0; j < len; ++j) ss += base[r * len + j] * base[r * len + j];
@@ -315,7 +335,7 @@ int oracle_chunk_forward(int kind, int decay_mode, int64_t B, int64_t H,
                          const double* beta, const double* W0,
                          const double* M0, double* out, double* Wend,
                          double* Mend, int averaged, int qk_norm, int row_norm) {
-  if (kind != OR_LINEAR && kind != OR_SWIGLU) return 1;
+  if (kind != OR_LINEAR && kind != OR_SWIGLU && kind != OR_MLP) return 1;
   if (decay_mode != OR_GAMMA_1_MINUS_ETA_ALPHA &&
       decay_mode != OR_ALPHA_IS_GAMMA)
     return 1;
@@ -416,7 +436,7 @@ int oracle_chunk_forward(int kind, int decay_mode, int64_t B, int64_t H,
         nrows = d;
         ncols = d;
       } else {
-        nrows = 2 * h + d;
+        nrows = (kind == OR_MLP ? h : 2 * h) + d;
         ncols = 0; /* per row, below */
       }
 #pragma omp parallel for schedule(dynamic, 4)
@@ -435,6 +455,11 @@ int oracle_chunk_forward(int kind, int decay_mode, int64_t B, int64_t H,
           left = fu1; lidx = r; lstride = hh;
           right = ku + t0 * d; rstride = d; nc = d;
           w = W + r * d; m = M + r * d;
+        } else if (kind == OR_MLP) { /* W2 row r-h */
+          left = fe; lidx = r - h; lstride = d;
+          right = fz; rstride = hh; nc = h;
+          w = W + h * d + (r - h) * h;
+          m = M + h * d + (r - h) * h;
         } else if (r < 2 * h) { /* W3 row r-h */
           left = fu3; lidx = r - h; lstride = hh;
           right = ku + t0 * d; rstride = d; nc = d;

@@ -29,9 +29,12 @@ import torch
 
 
 def learner_forward(kind, W, x, d, h):
-    """f_W(x) on torch fp64 tensors; W is the packed state vector."""
+    """f_W(x) on torch fp64 tensors; W is the packed state vector (kind 0
+    linear, 1 SwiGLU [W1 | W3 | W2], 2 MLP [W1 | W2] = W2 silu(W1 x))."""
     if kind == 0:
         return W.reshape(d, d) @ x
+    if kind == 2:
+        return W[h * d:].reshape(d, h) @ torch.nn.functional.silu(W[: h * d].reshape(h, d) @ x)
     W1 = W[: h * d].reshape(h, d)
     W3 = W[h * d: 2 * h * d].reshape(h, d)
     W2 = W[2 * h * d:].reshape(d, h)

@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libe2ttt.so")
 
 OK, EINVAL, EWORKSPACE, EUNSUPPORTED, EHIP = 0, 1, 2, 3, 4
-LINEAR, SWIGLU = 0, 1
+LINEAR, SWIGLU, MLP = 0, 1, 2
 F32, BF16 = 0, 1
 GAMMA_1_MINUS_ETA_ALPHA, ALPHA_IS_GAMMA = 0, 1
 FLAG_COMPENSATED_WEIGHTS = 1
@@ -147,6 +147,11 @@ def workspace_bytes(prob: Problem) -> int:
     if st != OK:
         raise E2tttError(st, "e2ttt_workspace_bytes")
     return int(n.value)
+
+
+def state_size(kind: int, d: int, h: int) -> int:
+    """Floats of one (batch, head) state: d*d (linear), 3dh (SwiGLU), 2dh (MLP)."""
+    return d * d if kind == LINEAR else (2 if kind == MLP else 3) * d * h
 
 
 def _ptr(t) -> Optional[int]:
@@ -329,7 +334,7 @@ class ChunkForward:
         import torch
         self.prob = prob
         B, H, L, d = prob.batch, prob.heads, prob.seq_len, prob.dim
-        P = d * d if prob.kind == LINEAR else 3 * d * prob.hidden
+        P = state_size(prob.kind, d, prob.hidden)
         io = torch.bfloat16 if prob.io_dtype == BF16 else torch.float32
         self.out = torch.empty((B, H, L, d), dtype=io, device=device)
         self.W_end = torch.empty((B, H, P), dtype=torch.float32, device=device)

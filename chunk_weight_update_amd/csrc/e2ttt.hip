@@ -63,12 +63,13 @@ struct Plan {
   float* saveM;
   // workspace offsets (bytes)
   size_t kw, km, coef, kt, w13s, w2s, w2ts, zrow, a1s, a3s, grow, ut, gt, zt, gw, gm, gbf, gft,
-      part, part256, qn, kn, total;
+      part, part256, qn, kn, wx, mx, total;
 };
 
 e2ttt_status check_problem(const e2ttt_problem* p) {
   if (!p || p->struct_size != sizeof(e2ttt_problem)) return E2TTT_EINVAL;
-  if (p->kind != E2TTT_LINEAR && p->kind != E2TTT_SWIGLU) return E2TTT_EINVAL;
+  if (p->kind != E2TTT_LINEAR && p->kind != E2TTT_SWIGLU && p->kind != E2TTT_MLP)
+    return E2TTT_EINVAL;
   if (p->io_dtype != E2TTT_F32 && p->io_dtype != E2TTT_BF16) return E2TTT_EINVAL;
   if (p->decay_mode != E2TTT_GAMMA_1_MINUS_ETA_ALPHA && p->decay_mode != E2TTT_ALPHA_IS_GAMMA)
     return E2TTT_EINVAL;
@@ -100,7 +101,7 @@ e2ttt_status check_problem(const e2ttt_problem* p) {
   if (!mul_ok(p->batch, p->heads, &bh) || !mul_ok(bh, p->seq_len + kMaxChunk, &bhl) ||
       !mul_ok(bhl, 4 * p->dim, &tot))
     return E2TTT_EUNSUPPORTED;
-  if (p->kind == E2TTT_SWIGLU) {
+  if (p->kind != E2TTT_LINEAR) {
     int64_t a, b;
     if (!mul_ok(bh, 12 * p->dim, &a) || !mul_ok(a, p->hidden, &b)) return E2TTT_EUNSUPPORTED;
     if (!mul_ok(bhl, 4 * p->hidden, &a)) return E2TTT_EUNSUPPORTED;
@@ -122,7 +123,7 @@ e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
   q.qknorm = (p->flags & E2TTT_FLAG_QK_SILU_L2) ? 1 : 0;
   q.rownorm = (p->flags & E2TTT_FLAG_POST_CHUNK_ROW_L2) ? 1 : 0;
   q.nC = q.L > 0 ? (q.L + q.C - 1) / q.C : 0;
-  q.P = q.kind == E2TTT_LINEAR ? q.d * q.d : 3 * q.d * q.h;
+  q.P = q.kind == E2TTT_LINEAR ? q.d * q.d : (q.kind == E2TTT_MLP ? 2 : 3) * q.d * q.h;
   const size_t f4 = 4;
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o = align256(o + bytes); return at; };
@@ -135,7 +136,7 @@ e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
     q.coef = take(f4 * q.BH * q.nC * 4);
     q.gw = take(f4 * q.BH * q.Cp * q.d);
     q.gm = take(f4 * q.BH * q.Cp * q.d);
-  } else if (q.io == E2TTT_BF16 && q.d == FD) {
+  } else if (q.kind == E2TTT_SWIGLU && q.io == E2TTT_BF16 && q.d == FD) {
     q.fused = true;
     q.Cp = (q.C + 127) / 128 * 128;
     q.opsz = 2;
@@ -213,7 +214,11 @@ e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
       // (S divides the slab count, so every split has at least one slab)
       while (S < 8 && tiles * S * 2 <= kCUs && (q.Cp / 32) % (S * 2) == 0) S *= 2;
       q.nsplitAgg = S;
-      q.part256 = take(f4 * static_cast<size_t>(S) * 2 * q.BH * q.P);
+      q.part256 = take(f4 * static_cast<size_t>(S) * 2 * q.BH * 3 * q.d * q.h);
+    }
+    if (q.kind == E2TTT_MLP) {  // the state in the SwiGLU layout, W3 = 0
+      q.wx = take(f4 * q.BH * 3 * q.d * q.h);
+      q.mx = take(f4 * q.BH * 3 * q.d * q.h);
     }
   }
   if (q.qknorm) {  // normalised copies of q and k
@@ -388,7 +393,8 @@ void launch_agg256(const Plan& q, const Shape& s, int r, int last, const T* ut, 
                  dim3(256), Tile256::LDS_BYTES, st, s, q.nsplitAgg, ut, kt, gt, zt, r, part);
     void (*kred)(Shape, int, int, int, const float*, const float*, const float*, const float*,
                  float*, float*, T*, T*, T*) = k_agg_reduce<T>;
-    E2TTT_LAUNCH(I, E2TTT_KERNEL_STATE, kred, dim3(grid1((q.BH * q.P / 4 + 255) / 256)),
+    // (the kernels' state layout [W1 | W3 | W2]: 3dh per unit, also for the MLP)
+    E2TTT_LAUNCH(I, E2TTT_KERNEL_STATE, kred, dim3(grid1((q.BH * 3 * q.d * q.h / 4 + 255) / 256)),
                  dim3(256), 0, st, s, q.nsplitAgg, r, last, part, coef, Win, Min, Wend, Mend,
                  w13s, w2s, w2ts);
   }
@@ -426,6 +432,7 @@ void launch_swiglu(const Plan& q, const void* qv, const void* kv, const void* vv
   const T* V = static_cast<const T*>(vv);
   T* O = static_cast<T*>(outv);
   Shape s{q.BH, q.L, q.d, q.h, q.C, q.Cp, q.nC, q.krep};
+  s.gated = q.kind == E2TTT_MLP ? 0 : 1;
   float* kw = reinterpret_cast<float*>(ws + q.kw);
   float* km = reinterpret_cast<float*>(ws + q.km);
   float* coef = reinterpret_cast<float*>(ws + q.coef);
@@ -624,6 +631,7 @@ e2ttt_status forward_impl(const e2ttt_problem* prob, const void* q, const void* 
   e2ttt_status status = make_plan(prob, &pl);
   if (status != E2TTT_OK) return status;
   const bool keep = want_starts && pl.nC > 1;
+  if (want_starts && pl.kind == E2TTT_MLP) return E2TTT_EUNSUPPORTED;
   if (keep && (!W_starts || !M_starts || !aligned(W_starts, 16) || !aligned(M_starts, 16)))
     return E2TTT_EINVAL;
   if (!W0 || !M0 || !W_end || !M_end) return E2TTT_EINVAL;
@@ -703,6 +711,23 @@ e2ttt_status forward_impl(const e2ttt_problem* prob, const void* q, const void* 
         launch_linear<float>(pl, q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end, ws, st, I);
     } else if (pl.fused) {
       launch_fused(pl, q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end, ws, st, I);
+    } else if (pl.kind == E2TTT_MLP) {
+      // The SwiGLU kernels on the state in their layout with W3 = 0 (the
+      // gate held at one), advanced in place, then copied back.
+      float* Wx = reinterpret_cast<float*>(ws + pl.wx);
+      float* Mx = reinterpret_cast<float*>(ws + pl.mx);
+      const int64_t n4 = pl.BH * 3 * pl.d * pl.h / 4;
+      const unsigned gx = grid1((n4 + 255) / 256);
+      hipLaunchKernelGGL(k_mlp_state, dim3(gx), dim3(256), 0, st, W0, Wx, pl.BH, pl.d, pl.h, 1);
+      hipLaunchKernelGGL(k_mlp_state, dim3(gx), dim3(256), 0, st, M0, Mx, pl.BH, pl.d, pl.h, 1);
+      if (pl.io == E2TTT_BF16)
+        launch_swiglu<bf16_t>(pl, q, k, v, eta, alpha, beta, Wx, Mx, out, Wx, Mx, ws, st, I);
+      else
+        launch_swiglu<float>(pl, q, k, v, eta, alpha, beta, Wx, Mx, out, Wx, Mx, ws, st, I);
+      hipLaunchKernelGGL(k_mlp_state, dim3(gx), dim3(256), 0, st, Wx, W_end, pl.BH, pl.d, pl.h,
+                         0);
+      hipLaunchKernelGGL(k_mlp_state, dim3(gx), dim3(256), 0, st, Mx, M_end, pl.BH, pl.d, pl.h,
+                         0);
     } else {
       if (pl.io == E2TTT_BF16)
         launch_swiglu<bf16_t>(pl, q, k, v, eta, alpha, beta, W0, M0, out, W_end, M_end, ws, st, I);
@@ -917,6 +942,7 @@ e2ttt_status e2ttt_decode_workspace_bytes(const e2ttt_problem* prob, size_t* byt
   if (st != E2TTT_OK) return st;
   if (prob->flags & (E2TTT_FLAG_CHUNK_AVERAGED_DECAY | E2TTT_FLAG_LACT_RULE))
     return E2TTT_EUNSUPPORTED;
+  if (prob->kind == E2TTT_MLP) return E2TTT_EUNSUPPORTED;
   const int64_t h = prob->kind == E2TTT_LINEAR ? 0 : prob->hidden;
   *bytes = decode_ws_total(prob, prob->batch * prob->heads, prob->dim, h);
   return E2TTT_OK;
@@ -931,6 +957,7 @@ e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* q, const v
   if (st != E2TTT_OK) return st;
   if (prob->flags & (E2TTT_FLAG_CHUNK_AVERAGED_DECAY | E2TTT_FLAG_LACT_RULE))
     return E2TTT_EUNSUPPORTED;
+  if (prob->kind == E2TTT_MLP) return E2TTT_EUNSUPPORTED;
   const int64_t BH = prob->batch * prob->heads, d = prob->dim;
   const int64_t h = prob->kind == E2TTT_LINEAR ? 0 : prob->hidden;
   const int64_t P = h == 0 ? d * d : 3 * d * h;
@@ -1057,6 +1084,7 @@ e2ttt_status make_bwd_plan(const e2ttt_problem* p, BwdPlan* bp) {
   // Every flag of the forward is supported (the compensated-weights option
   // only concerns bf16 matrix operands; the backward computes in fp32).
   if (q.lact) return E2TTT_EUNSUPPORTED;  // no reverse mode of the LaCT rule
+  if (q.kind == E2TTT_MLP) return E2TTT_EUNSUPPORTED;
   bp->qknorm = q.qknorm != 0;
   bp->rownorm = q.rownorm != 0;
   if (q.kind == E2TTT_LINEAR && q.d > 64) return E2TTT_EUNSUPPORTED;

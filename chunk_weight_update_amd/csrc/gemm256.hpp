@@ -419,7 +419,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int off = ps.row(mi, v) * h + j;
-        const float a1 = acc[mi][2 * pr][v], a3 = acc[mi][2 * pr + 1][v];
+        const float a1 = acc[mi][2 * pr][v], a3 = s.gated ? acc[mi][2 * pr + 1][v] : 1.0f;
         const float z = a1 * sigmoidf_(a1) * a3;
         zv[v] = z;
         zq[off] = f2bf(z);

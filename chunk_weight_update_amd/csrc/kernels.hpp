@@ -41,6 +41,10 @@ namespace e2ttt {
 struct Shape {
   int64_t BH, L, d, h, C, Cp, nC;
   int krep;
+  // 0 for the MLP learner on these kernels: the gate branch's pre-activation
+  // A3 is taken as 1 (its weights are zero) and its gradient dA3 as 0, so
+  // z = silu(A1), dA1 = dZ silu'(A1) and W3 stays zero.
+  int gated = 1;
 };
 
 __device__ __forceinline__ int64_t n_valid(const Shape& s, int r) {
@@ -530,6 +534,28 @@ __global__ __launch_bounds__(256) void k_prologue(ScanArgs sa, Shape s, const bf
   else prep_shadow_block<bf16_t>(s, b - nscan - nkt, W0, w13s, w2s, w2ts);
 }
 
+// The MLP learner's state [W1 | W2] (2dh per unit) to the SwiGLU layout
+// [W1 | W3 = 0 | W2] (3dh) of the kernels (expand != 0), or back.  Four
+// entries per thread; grid over the 3dh layout.
+__global__ __launch_bounds__(256) void k_mlp_state(const float* __restrict__ src,
+                                                   float* __restrict__ dst, int64_t BH,
+                                                   int64_t d, int64_t h, int expand) {
+  const int64_t hd = h * d, n4 = BH * 3 * hd / 4;
+  const int64_t i4 = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i4 >= n4) return;
+  const int64_t u = (4 * i4) / (3 * hd), o = (4 * i4) % (3 * hd);  // o in the 3dh layout
+  const bool isW3 = o >= hd && o < 2 * hd;
+  const int64_t oc = o < hd ? o : o - hd;                          // offset in the 2dh layout
+  if (expand) {
+    f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+    if (!isW3) x = *reinterpret_cast<const f32x4_t*>(src + u * 2 * hd + oc);
+    *reinterpret_cast<f32x4_t*>(dst + u * 3 * hd + o) = x;
+  } else if (!isW3) {
+    *reinterpret_cast<f32x4_t*>(dst + u * 2 * hd + oc) =
+        *reinterpret_cast<const f32x4_t*>(src + u * 3 * hd + o);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // fwd13: [K;Q] rows x shadow W13 -> A1, A3 -> Z.
 template <typename T>
@@ -565,7 +591,7 @@ __global__ __launch_bounds__(256) void k_fwd13(Shape s, int r, const T* __restri
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int64_t p = p0 + ps.row(mi, v);
-      const float a1 = acc[mi][0][v], a3 = acc[mi][1][v];
+      const float a1 = acc[mi][0][v], a3 = s.gated ? acc[mi][1][v] : 1.0f;
       const float z = a1 * sigmoidf_(a1) * a3;
       zv[mi][0][v] = z;
       zrow[(u * 2 * s.Cp + (isQ ? s.Cp : 0) + p) * s.h + j] = from_f32<T>(z);
@@ -747,7 +773,7 @@ __global__ __launch_bounds__(256) void k_bwd(Shape s, int r, const T* __restrict
         const float a3 = a3s[(u * s.Cp + p) * s.h + j];
         const float sg = sigmoidf_(a1);
         const float dz = acc[mi][ni][vv];
-        d3[mi][ni][vv] = dz * (a1 * sg);
+        d3[mi][ni][vv] = s.gated ? dz * (a1 * sg) : 0.0f;
         d1[mi][ni][vv] = dz * a3 * (sg * (1.0f + a1 * (1.0f - sg)));
       }
   T* ubase = ut + u * 4 * s.h * s.Cp + p0;

@@ -26,11 +26,22 @@
  *   E2TTT_SWIGLU : f(x) = W2 (silu(W1 x) * (W3 x)); the state of one
  *                  (batch, head) is packed [W1 (h x d) | W3 (h x d) | W2 (d x h)],
  *                  each row-major, P = 3*d*h floats.
+ *   E2TTT_MLP    : f(x) = W2 silu(W1 x), the smaller fast-weight network of
+ *                  E2-TTT_MLP (§5, App. B.3 Table 11, App. B.5; the page
+ *                  names no activation: SiLU, the SwiGLU's, is taken);
+ *                  packed [W1 (h x d) | W2 (d x h)], P = 2*d*h floats.  It
+ *                  runs on the SwiGLU kernels with the gate branch held at
+ *                  one (an internal copy of the state carries W3 = 0 and the
+ *                  gate's pre-activation is replaced by 1, its gradient by
+ *                  0).  Supported by e2ttt_chunk_forward, its timed and
+ *                  allocation-free twins and e2ttt_scalar_kernels; the
+ *                  kept-states forward, the decode step and the backward
+ *                  return EUNSUPPORTED.
  *
  * Layouts (all contiguous, row-major):
  *   q, k, v, out          [B, H, L, d]   io_dtype (fp32 or bf16)
  *   eta, alpha, beta      [B, H, L]      fp32
- *   W0, M0, W_end, M_end  [B, H, P]      fp32   (P = d*d or 3*d*h)
+ *   W0, M0, W_end, M_end  [B, H, P]      fp32   (P = d*d, 3*d*h or 2*d*h)
  * Chunks are consecutive runs of C tokens from the start of the sequence; if
  * C does not divide L the last chunk is shorter (same recurrence, fewer
  * tokens).  L == 0 copies (W0, M0) to (W_end, M_end).
@@ -70,7 +81,7 @@ typedef enum {
   E2TTT_EHIP = 4          /* a HIP runtime call or kernel launch failed */
 } e2ttt_status;
 
-typedef enum { E2TTT_LINEAR = 0, E2TTT_SWIGLU = 1 } e2ttt_fast_weight;
+typedef enum { E2TTT_LINEAR = 0, E2TTT_SWIGLU = 1, E2TTT_MLP = 2 } e2ttt_fast_weight;
 typedef enum { E2TTT_F32 = 0, E2TTT_BF16 = 1 } e2ttt_dtype;
 typedef enum {
   E2TTT_GAMMA_1_MINUS_ETA_ALPHA = 0, /* gamma = 1 - eta*alpha (Eq. 14) */
@@ -163,7 +174,7 @@ typedef struct {
 /* Host-only argument check (no HIP call).  Returns E2TTT_OK if the problem is
  * well formed and supported:
  *   LINEAR : 16 <= d <= 128, d % 16 == 0, io fp32 or bf16.
- *   SWIGLU : d % 128 == 0, h % 128 == 0, d <= 1024, h <= 4096, io fp32 or bf16.
+ *   SWIGLU, MLP : d % 128 == 0, h % 128 == 0, d <= 1024, h <= 4096, io fp32 or bf16.
  *   Both   : 1 <= C <= 12288.
  * EINVAL for malformed values, EUNSUPPORTED for well-formed but uncompiled. */
 E2TTT_API e2ttt_status e2ttt_validate(const e2ttt_problem* prob);

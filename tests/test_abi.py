@@ -71,6 +71,10 @@ def test_status_strings():
     (swiglu(chunk=0), cwu.EINVAL),
     (swiglu(hidden=0), cwu.EINVAL),
     (swiglu(kind=7), cwu.EINVAL),
+    (swiglu(kind=cwu.MLP), cwu.OK),
+    (swiglu(kind=cwu.MLP, dim=768, hidden=1536, chunk=8192, seq_len=57344, batch=1, heads=1),
+     cwu.OK),
+    (swiglu(kind=cwu.MLP, dim=96), cwu.EUNSUPPORTED),
     (swiglu(io_dtype=5), cwu.EINVAL),
     (swiglu(decay_mode=3), cwu.EINVAL),
     (swiglu(flags=cwu.FLAG_CHUNK_AVERAGED_DECAY), cwu.OK),
@@ -369,3 +373,14 @@ def test_scalar_heads_checked_on_the_host():
                                 0.1, None, None, None, None) == cwu.OK
     assert L.e2ttt_scalar_heads(ctypes.byref(swiglu(chunk=0)), None, 512, None, None, 0.01,
                                 0.1, None, None, None, None) == cwu.EINVAL
+
+
+def test_mlp_learner_entry_points():
+    """The MLP learner: its own (larger, SwiGLU-layout) forward workspace;
+    EUNSUPPORTED for the decode step and the backward."""
+    assert cwu.workspace_bytes(swiglu(kind=cwu.MLP)) > cwu.workspace_bytes(
+        swiglu(kind=cwu.MLP, seq_len=0))
+    with pytest.raises(cwu.E2tttError):
+        cwu.decode_workspace_bytes(swiglu(kind=cwu.MLP))
+    with pytest.raises(cwu.E2tttError):
+        cwu.backward_workspace_bytes(swiglu(kind=cwu.MLP, io_dtype=cwu.F32))

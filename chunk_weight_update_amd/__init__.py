@@ -17,7 +17,9 @@ import threading
 from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libe2ttt.so")
+# E2TTT_LIBRARY selects another build of the same library (the sanitizer
+# build of the host code); it must exist like the default one.
+LIB_PATH = os.environ.get("E2TTT_LIBRARY") or os.path.join(_HERE, "libe2ttt.so")
 
 OK, EINVAL, EWORKSPACE, EUNSUPPORTED, EHIP = 0, 1, 2, 3, 4
 LINEAR, SWIGLU, MLP = 0, 1, 2

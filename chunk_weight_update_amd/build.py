@@ -9,9 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libe2ttt.so")
-SOURCES = [os.path.join(CSRC, "e2ttt.hip")]
-DEPS = SOURCES + [os.path.join(CSRC, f) for f in ("common.hpp", "kernels.hpp")] + [
-    os.path.join(ROOT, "include", "e2ttt.h")]
+SOURCES = [os.path.join(CSRC, "e2ttt.hip")]  # includes every csrc/*.hpp and include/e2ttt.h
 
 
 def hipcc() -> str:
@@ -36,12 +34,6 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     return LIB
 
-
-def is_stale() -> bool:
-    if not os.path.exists(LIB):
-        return True
-    t = os.path.getmtime(LIB)
-    return any(os.path.getmtime(p) > t for p in DEPS)
 
 
 if __name__ == "__main__":

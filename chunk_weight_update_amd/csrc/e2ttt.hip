@@ -96,7 +96,8 @@ e2ttt_status check_problem(const e2ttt_problem* p) {
       return E2TTT_EUNSUPPORTED;
   }
   if (p->chunk > kMaxChunk) return E2TTT_EUNSUPPORTED;
-  // Every element count must fit comfortably in int64 and every grid in 2^31.
+  // Every element count must fit comfortably in int64 (the grids are checked
+  // against the dispatch limit in make_plan).
   int64_t bh, bhl, tot;
   if (!mul_ok(p->batch, p->heads, &bh) || !mul_ok(bh, p->seq_len + kMaxChunk, &bhl) ||
       !mul_ok(bhl, 4 * p->dim, &tot))
@@ -227,6 +228,25 @@ e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
     q.kn = take(nx);
   }
   q.total = q.L == 0 ? 0 : o;  // an empty sequence only copies the state
+  // Every 1-D launch of the plan must fit one dispatch: blocks * 256
+  // work-items below 2^32.  The largest grids of each path:
+  int64_t worst = q.BH * q.nC;                          // scan
+  auto upd = [&](int64_t blocks) { worst = blocks > worst ? blocks : worst; };
+  upd(q.BH * q.P / 256 + 1);                            // state copies
+  if (q.qknorm) upd(q.BH * q.L / 4 + 1);                // q/k prologue, 4 rows per block
+  if (q.kind == E2TTT_LINEAR) {
+    upd(q.BH * (2 * q.Cp / 16));                        // linear forward
+    upd(q.BH * q.d / 4 + 1);                            // row normalisation
+  } else {
+    upd(q.BH * q.nC * (q.Cp / 64) * (q.d / 64));        // K^T staging
+    upd(q.BH * 3 * (q.d / 64) * (q.h / 64));            // operand shadows
+    upd(q.BH * (2 * q.Cp / 32));                        // phase A (32-row tiles)
+    upd(q.BH * (q.h / 64) * 24);                        // split-sum state epilogue
+    upd(q.BH * (2 * q.Cp / 128) * (2 * q.h / 128));     // fwd13 (128-row tiles)
+    upd(q.BH * 3 * q.d * q.h / 1024 + 1);               // agg reduce, MLP state copies
+    upd(q.BH * (2 * q.h + q.d) / 4 + 1);                // row normalisation
+  }
+  if (worst > static_cast<int64_t>(UINT32_MAX / 256u)) return E2TTT_EUNSUPPORTED;
   return E2TTT_OK;
 }
 
@@ -596,7 +616,11 @@ void launch_linear(const Plan& q, const void* qv, const void* kv, const void* vv
 extern "C" {
 
 const char* e2ttt_status_string(e2ttt_status s) {
-  switch (s) {
+  // A C caller may pass any int; read the bits as one (an out-of-range value
+  // of the C++ enum type would be undefined).
+  int v = 0;
+  std::memcpy(&v, &s, sizeof(v));
+  switch (v) {
     case E2TTT_OK: return "E2TTT_OK";
     case E2TTT_EINVAL: return "E2TTT_EINVAL: invalid argument";
     case E2TTT_EWORKSPACE: return "E2TTT_EWORKSPACE: workspace too small";

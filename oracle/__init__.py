@@ -34,7 +34,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "e2ttt_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# E2TTT_ORACLE_LIBRARY selects a prebuilt oracle library (the sanitizer
+# build); it is then loaded as it is, never rebuilt.
+_LIB_ENV = os.environ.get("E2TTT_ORACLE_LIBRARY")
+_LIB = _LIB_ENV or os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
 
@@ -60,8 +63,8 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB) or (
-                    os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
+            if not _LIB_ENV and (not os.path.exists(_LIB) or (
+                    os.path.getmtime(_LIB) < os.path.getmtime(_SRC))):
                 build()
             lib = ctypes.CDLL(_LIB)
             P = ctypes.POINTER(ctypes.c_double)

@@ -11,10 +11,12 @@
  *  Training", E2-TTT, as served by paperpeel.com, unless noted):
  *
  *   - The state is the fast weight W and a momentum buffer M of the same shape
- *     ("W_t denotes the full collection of fast-weight tensors", §2).
+ *     (§2: for a learner with several weight tensors the state symbol stands
+ *     for all of them).
  *   - Within chunk r all per-token gradients are evaluated at the chunk-start
- *     weights W_0 (§1, §3, App. A.5 "evaluated at the frozen W_0").
- *   - The token-wise state recurrence (Eq. 7, the "optimisation-style view" of
+ *     weights W_0 (§1, §3; App. A.5 takes every gradient of a chunk at the frozen
+ *     chunk-start weights).
+ *   - The token-wise state recurrence (Eq. 7, in the optimisation-style reading of
  *     App. A.5: momentum factor beta_t, L2 decay factor gamma_t) is taken as
  *         M_t = beta_t * M_{t-1} + eta_t * G_t
  *         W_t = gamma_t * W_{t-1} + M_t
@@ -27,7 +29,7 @@
  *     summed over the d outputs (§2).
  *   - Output: o_t = f_{W_0}(q_t), the chunk-start weights (Eq. 6, §3.2).
  *   - (W_C, M_C) of chunk r is (W_0, M_0) of chunk r+1 (§3 notation, §3.2
- *     "Cross-chunk equivalence ... follows by induction").
+ *     where equivalence across chunks follows by induction).
  *   - Inner learners: linear f_W(x) = W x (§2), the three-matrix SwiGLU
  *     f(x) = W2 (silu(W1 x) * (W3 x)) (§5.2, App. B.5 "three-matrix
  *     fast-weight network"), and the MLP learner of E2-TTT_MLP (§5, App.
@@ -64,7 +66,7 @@
  *     "Input-Dependent Dynamics") predicts eta_t, beta_t and alpha_t from the
  *     layer input x_t by lightweight linear heads (Eqs. 12-14, App. B.4), and
  *     App. B.3 says eta_base and alpha_base scale per-token sigmoid gates.
- *     Eq. 13 (beta's "timescale parameterization", App. A.3) is missing from
+ *     Eq. 13 (the timescale form of beta that App. A.3 mentions) is missing from
  *     the page; the reading taken is a plain sigmoid gate.  Per TTT head h:
  *         eta_t   = eta_base   * sigma(<w_eta_h,   x_t> + b_eta_h)
  *         alpha_t = alpha_base * sigma(<w_alpha_h, x_t> + b_alpha_h)

@@ -384,3 +384,15 @@ def test_mlp_learner_entry_points():
         cwu.decode_workspace_bytes(swiglu(kind=cwu.MLP))
     with pytest.raises(cwu.E2tttError):
         cwu.backward_workspace_bytes(swiglu(kind=cwu.MLP, io_dtype=cwu.F32))
+
+
+def test_problems_beyond_the_dispatch_limit_are_unsupported():
+    """A launch of more than 2^32 work-items cannot be dispatched: such
+    problems are EUNSUPPORTED before anything is enqueued (here the q/k
+    prologue over 2^27 rows, which needs 2^33 work-items), while the same
+    sequence without it fits."""
+    big = linear(dim=16, seq_len=1 << 27, chunk=64)
+    assert cwu.validate(big) == cwu.OK
+    assert cwu.workspace_bytes(big) > 0
+    with pytest.raises(cwu.E2tttError):
+        cwu.workspace_bytes(linear(dim=16, seq_len=1 << 27, chunk=64, flags=cwu.FLAG_QK_SILU_L2))

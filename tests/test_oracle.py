@@ -3,14 +3,14 @@
 Each test ties the oracle to a fact fixed by E2-TTT ("Rethinking
 Expressivity and Efficiency in Test-Time Training") or by mathematics:
   - the kernel formulas of §3.2 in their ratio-sum form (closed_form_np.py)
-    reproduce the literal recurrence ("exactly reproduces the chunk-end
-    fast-weight and momentum states", abstract, §3.2);
+    reproduce the literal recurrence (the abstract and §3.2 claim the
+    chunk-end weight and momentum of the token recurrence exactly);
   - per-token descent directions equal torch autograd and finite differences;
   - with no momentum (beta = 0) and no decay (gamma = 1) the chunk update is
     a plain summed-gradient step at W_0 (the LaCT-style update of §3.2);
   - gamma = 0 makes W_t = M_t (App. A.3, aggressive-decay limit);
-  - C = 1 is token-wise online descent with momentum (App. B.3, "C -> 1
-    recovers the token-wise update exactly");
+  - C = 1 is token-wise online descent with momentum (App. B.3: in the
+    limit of one-token chunks the update is the token-wise one);
   - constant scalars give geometric-series kernels (App. A.3 regimes);
   - readout with the chunk-start weights (Eq. 6);
   - linearity of the linear learner in (W_0, M_0, v);

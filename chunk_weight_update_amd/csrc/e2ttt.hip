@@ -414,7 +414,7 @@ void launch_agg256(const Plan& q, const Shape& s, int r, int last, const T* ut, 
     void (*kred)(Shape, int, int, int, const float*, const float*, const float*, const float*,
                  float*, float*, T*, T*, T*) = k_agg_reduce<T>;
     // (the kernels' state layout [W1 | W3 | W2]: 3dh per unit, also for the MLP)
-    E2TTT_LAUNCH(I, E2TTT_KERNEL_STATE, kred, dim3(grid1((q.BH * 3 * q.d * q.h / 4 + 255) / 256)),
+    E2TTT_LAUNCH(I, E2TTT_KERNEL_STATE, kred, dim3(grid1(agg_reduce_blocks(s))),
                  dim3(256), 0, st, s, q.nsplitAgg, r, last, part, coef, Win, Min, Wend, Mend,
                  w13s, w2s, w2ts);
   }

@@ -264,8 +264,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
-// Chunk-end state from the split partials: 4 entries per thread (16-byte
-// vectors), grid (BH * P / 4 + 255) / 256.
+// Chunk-end state from the split partials (the S partials added in split
+// order), plus the operand shadows of the next chunk's weights.  Blocks
+// [0, nA) take the W1/W3 entries of all units, 4 consecutive entries per
+// thread (16-byte state accesses, 8-byte shadow stores of one shadow row);
+// the other blocks take one 64 x 64 tile of a unit's W2 each, so that the
+// transposed shadow W2^T is written in rows through LDS.
+__host__ __device__ inline int64_t agg_reduce_blocks_a(const Shape& s) { return (s.BH * 2 * s.h * s.d / 4 + 255) / 256; }
+__host__ __device__ inline int64_t agg_reduce_blocks(const Shape& s) {
+  return agg_reduce_blocks_a(s) + s.BH * (s.d / 64) * (s.h / 64);
+}
+
+template <typename T>
+__device__ __forceinline__ void put4_shadow(T* hi, int kr, int64_t lo_off, const f32x4_t& w) {
+  const float x[4] = {w[0], w[1], w[2], w[3]};
+  split_store4<T>(x, hi, kr == 2 ? hi + lo_off : nullptr);
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_agg_reduce(Shape s, int nsplit, int r, int last,
                                                     const float* __restrict__ part,
@@ -273,31 +288,72 @@ __global__ __launch_bounds__(256) void k_agg_reduce(Shape s, int nsplit, int r, 
                                                     const float* Win, const float* Min,
                                                     float* Wout, float* Mout, T* w13s, T* w2s,
                                                     T* w2ts) {
-  const int64_t P = 3 * s.d * s.h;
-  const int64_t q4 = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (q4 * 4 >= s.BH * P) return;
-  const int64_t u = (q4 * 4) / P, e = (q4 * 4) % P;
-  const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(Win + u * P + e);
-  const f32x4_t m0 = *reinterpret_cast<const f32x4_t*>(Min + u * P + e);
-  f32x4_t aw = *reinterpret_cast<const f32x4_t*>(part + u * P + e);
-  f32x4_t am = *reinterpret_cast<const f32x4_t*>(part + (s.BH + u) * P + e);
-  for (int sp = 1; sp < nsplit; ++sp) {
-    aw += *reinterpret_cast<const f32x4_t*>(part + ((sp * 2) * s.BH + u) * P + e);
-    am += *reinterpret_cast<const f32x4_t*>(part + ((sp * 2 + 1) * s.BH + u) * P + e);
-  }
-  const float* cf = coef + (u * s.nC + r) * 4;
-  const float cW = cf[0], cM = cf[1], cWM = cf[2];
-  f32x4_t wn, mn;
+  __shared__ float tT[64 * 65];
+  const int64_t d = s.d, h = s.h, hd = h * d, P = 3 * hd;
+  const int kr = s.krep;
+  const int64_t nA = agg_reduce_blocks_a(s);
+  const int64_t blk = blockIdx.x;
+  // Four entries e .. e+3 of unit u: partial sums, chunk-end values.
+  auto entry4 = [&](int64_t u, int64_t e, f32x4_t& wn) {
+    const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(Win + u * P + e);
+    const f32x4_t m0 = *reinterpret_cast<const f32x4_t*>(Min + u * P + e);
+    f32x4_t aw = *reinterpret_cast<const f32x4_t*>(part + u * P + e);
+    f32x4_t am = *reinterpret_cast<const f32x4_t*>(part + (s.BH + u) * P + e);
+    for (int sp = 1; sp < nsplit; ++sp) {
+      aw += *reinterpret_cast<const f32x4_t*>(part + ((sp * 2) * s.BH + u) * P + e);
+      am += *reinterpret_cast<const f32x4_t*>(part + ((sp * 2 + 1) * s.BH + u) * P + e);
+    }
+    const float* cf = coef + (u * s.nC + r) * 4;
+    const float cW = cf[0], cM = cf[1], cWM = cf[2];
+    f32x4_t mn;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    wn[i] = cW * w0[i] + cWM * m0[i] + aw[i];
-    mn[i] = cM * m0[i] + am[i];
+    for (int i = 0; i < 4; ++i) {
+      wn[i] = cW * w0[i] + cWM * m0[i] + aw[i];
+      mn[i] = cM * m0[i] + am[i];
+    }
+    *reinterpret_cast<f32x4_t*>(Wout + u * P + e) = wn;
+    *reinterpret_cast<f32x4_t*>(Mout + u * P + e) = mn;
+  };
+  if (blk < nA) {  // W1 / W3
+    const int64_t q4 = blk * 256 + threadIdx.x;
+    if (q4 * 4 >= s.BH * 2 * hd) return;
+    const int64_t u = (q4 * 4) / (2 * hd), e = (q4 * 4) % (2 * hd);
+    f32x4_t wn;
+    entry4(u, e, wn);
+    if (last) return;
+    const int isW3 = e >= hd;
+    const int64_t oo = isW3 ? e - hd : e;
+    const int64_t sr = oo / d, c = oo % d;
+    const int64_t srow = 64 * (sr / 32) + 32 * isW3 + sr % 32;
+    put4_shadow<T>(w13s + (u * 2 * h + srow) * (kr * d) + c, kr, d, wn);
+    return;
   }
-  *reinterpret_cast<f32x4_t*>(Wout + u * P + e) = wn;
-  *reinterpret_cast<f32x4_t*>(Mout + u * P + e) = mn;
-  if (!last) {
+  // W2: tile (J0 .. J0+63 rows = output units, I0 .. I0+63 cols = hidden units)
+  const int64_t tb = blk - nA;
+  const int64_t tpu = (d / 64) * (h / 64);
+  const int64_t u = tb / tpu, t = tb % tpu;
+  const int64_t J0 = 64 * (t / (h / 64)), I0 = 64 * (t % (h / 64));
+  const int tid = threadIdx.x, rr = tid >> 4, c0 = 4 * (tid & 15);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) write_shadow<T>(s, u, e + i, wn[i], w13s, w2s, w2ts);
+  for (int k = 0; k < 4; ++k) {
+    const int jr = rr + 16 * k;
+    f32x4_t wn;
+    entry4(u, 2 * hd + (J0 + jr) * h + I0 + c0, wn);
+    if (!last) {
+      put4_shadow<T>(w2s + (u * d + J0 + jr) * (kr * h) + I0 + c0, kr, h, wn);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tT[(c0 + e) * 65 + jr] = wn[e];
+    }
+  }
+  if (last) return;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {  // W2^T row I0 + ir, columns J0 + c0 ..
+    const int ir = rr + 16 * k;
+    f32x4_t w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = tT[ir * 65 + c0 + e];
+    put4_shadow<T>(w2ts + (u * h + I0 + ir) * (kr * d) + J0 + c0, kr, d, w);
   }
 }
 

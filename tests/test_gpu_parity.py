@@ -277,6 +277,14 @@ def test_swiglu_bf16_d256_tiled_aggregation(L, C):
           m0_scale=M0["nearunit"])
 
 
+def test_swiglu_bf16_d256_tiled_aggregation_compensated():
+    """The split-sum state epilogue writing hi/lo operand shadows (compensated
+    weights): the 256-tile aggregation with the 128-tile forward products."""
+    import chunk_weight_update_amd as cwu
+    check(SWIGLU, 2, 1, 700, 256, 512, 256, BF16, seed=10, regime="nearunit",
+          m0_scale=M0["nearunit"], flags=cwu.FLAG_COMPENSATED_WEIGHTS)
+
+
 def test_swiglu_alpha_is_gamma_fp32():
     check(SWIGLU, 1, 2, 384, 128, 128, 128, F32, seed=5, regime="nearunit",
           m0_scale=M0["nearunit"], decay_mode=1)

@@ -185,65 +185,72 @@ def scan_microbench(reps=10):
             "gbs": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS}
 
 
-def decode_bench(w, reps=200):
-    """The decode step (one token of every unit per call, e2ttt_decode_step)
-    on the workload's B, H, d, h and io dtype, seeded synthetic inputs.
-    Algorithmic bytes per step and unit: W0 read once, W and M read and
-    written (5 P fp32), plus q, k, v, out.  Reported beside the main metric,
-    not as it."""
+def decode_bench(B, H, d, h, C, io, n_tok=64):
+    """The decode step (e2ttt_decode_step, one token of every unit per call,
+    the state update amortised over the chunk) on seeded synthetic inputs:
+    the per-token cost from a graph of n_tok calls inside a chunk (replayed,
+    so the host's per-call cost is excluded), the chunk-end call (buffered
+    tokens aggregated into the state) separately, and the amortised time per
+    token = per-token + (chunk end - per-token) / C.  Algorithmic bytes per
+    token and unit: the chunk-start weights read once (4 P) plus q, k, v,
+    out."""
     import torch
     import chunk_weight_update_amd as cwu
-    B, H, d, h = w.B, w.H, w.d, w.h
-    io = torch.bfloat16 if w.io == 1 else torch.float32
-    P = d * d if w.kind == 0 else 3 * d * h
+    dt = torch.bfloat16 if io == 1 else torch.float32
+    kind = cwu.SWIGLU
+    P = 3 * d * h
     g = torch.Generator(device="cuda").manual_seed(1)
     x = [torch.nn.functional.normalize(torch.randn((B, H, d), generator=g, device="cuda"),
-                                       dim=-1).to(io) for _ in range(3)]
+                                       dim=-1).to(dt) for _ in range(3)]
     eta = 0.1 * torch.sigmoid(torch.randn((B, H), generator=g, device="cuda"))
     alpha = 1.0 - 0.05 * torch.sigmoid(torch.randn((B, H), generator=g, device="cuda"))
     beta = 0.9 * torch.sigmoid(torch.randn((B, H), generator=g, device="cuda"))
-    W0 = torch.randn((B, H, P), generator=g, device="cuda") * (1.0 / d) ** 0.5
-    W, M = W0.clone(), torch.zeros_like(W0)
+    W = torch.randn((B, H, P), generator=g, device="cuda") * (1.0 / d) ** 0.5
+    M = torch.zeros_like(W)
     out = torch.empty_like(x[0])
-    prob = cwu.make_problem(w.kind, B, H, w.C, d, h, w.C, w.io, 0)
+    prob = cwu.make_problem(kind, B, H, C, d, h, C, io, 0)
     ws = torch.empty(cwu.decode_workspace_bytes(prob), dtype=torch.uint8, device="cuda")
-    for _ in range(20):
-        cwu.decode_step(prob, *x, eta, alpha, beta, W0, W, M, out, False, ws)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def step(pos, end):
+        cwu.decode_step(prob, *x, eta, alpha, beta, W, M, out, pos, end, ws)
+    for p_ in range(8):
+        step(p_, False)
     torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for p_ in range(n_tok):
+            step(p_, False)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(reps):
-        cwu.decode_step(prob, *x, eta, alpha, beta, W0, W, M, out, False, ws)
+    for _ in range(4):
+        graph.replay()
     e1.record()
     torch.cuda.synchronize()
-    us_eager = e0.elapsed_time(e1) / reps * 1e3  # includes the host's per-call cost
-    # Device time per step: 50 steps captured in a graph (the step makes no
-    # allocation and no memset, so it captures), replayed.
-    us = None
-    try:
-        steps = 50
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for _ in range(steps):
-                cwu.decode_step(prob, *x, eta, alpha, beta, W0, W, M, out, False, ws)
-        graph.replay()
+    us_tok = e0.elapsed_time(e1) / (4 * n_tok) * 1e3
+    W0 = W.clone()
+    reps = 3
+    times = []
+    for _ in range(reps):
+        W.copy_(W0)
+        M.zero_()
         torch.cuda.synchronize()
         e0.record()
-        for _ in range(4):
-            graph.replay()
+        step(C - 1, True)
         e1.record()
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) / (4 * steps) * 1e3
-    except Exception as exc:  # report the eager rate only
-        log(f"bench: decode graph capture unavailable ({exc})")
-    t = us if us is not None else us_eager
-    nbytes = B * H * (20.0 * P + 4 * d * (2 if w.io == 1 else 4))
-    gbs = nbytes / (t * 1e-6) / 1e9
-    return {"label": "decode step, one token per (b,h) unit per call (not the main metric)",
-            "shape": {"batch": B, "heads": H, "dim": d, "hidden": h},
-            "us_per_step": t, "us_per_step_eager_calls": us_eager,
-            "timing": "graph replay" if us is not None else "eager calls",
-            "tokens_per_s": B * H / (t * 1e-6), "gbs": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS}
+        times.append(e0.elapsed_time(e1) * 1e3)
+    us_end = sorted(times)[reps // 2]
+    us_amort = us_tok + max(us_end - us_tok, 0.0) / C
+    nbytes = B * H * (4.0 * P + 4 * d * (2 if io == 1 else 4))
+    return {"shape": {"batch": B, "heads": H, "dim": d, "hidden": h, "chunk": C,
+                      "io": "bf16" if io == 1 else "fp32"},
+            "us_per_token_in_chunk": us_tok, "us_chunk_end_call": us_end,
+            "us_per_token_amortised": us_amort, "tokens_per_s": B * H / (us_amort * 1e-6),
+            "gbs_per_token": nbytes / (us_tok * 1e-6) / 1e9,
+            "frac_of_hbm_peak": nbytes / (us_tok * 1e-6) / 1e9 / PEAK_HBM_GBS,
+            "timing": f"graph of {n_tok} in-chunk calls; chunk-end call eager (median of {reps})"}
 
 
 def heads_bench(reps=20):
@@ -741,8 +748,14 @@ def main():
             torch.cuda.empty_cache()
         line["other_configs"] = others
     if not args.no_scan_microbench:
-        line["decode"] = decode_bench(w)
+        line["decode"] = {
+            "label": "decode step, one token per (b,h) unit per call, state update once per "
+                     "chunk (not the main metric)",
+            "shapes": ([decode_bench(w.B, w.H, w.d, w.h, w.C, w.io)] if w.kind == 1 else []) + [
+                       decode_bench(2, 4, 128, 256, 512, 1),
+                       decode_bench(8, 16, 128, 256, 2048, 1)]}
         log(f"bench: decode step {line['decode']}")
+        torch.cuda.empty_cache()
         line["scan_microbench"] = scan_microbench()
         log(f"bench: scan microbenchmark {line['scan_microbench']}")
         line["scalar_heads"] = heads_bench()

@@ -118,8 +118,8 @@ def lib() -> ctypes.CDLL:
             L.e2ttt_scalar_kernels.restype = ctypes.c_int
             L.e2ttt_decode_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
             L.e2ttt_decode_workspace_bytes.restype = ctypes.c_int
-            L.e2ttt_decode_step.argtypes = [P] + [vp] * 10 + [ctypes.c_int, vp, ctypes.c_size_t,
-                                                              vp]
+            L.e2ttt_decode_step.argtypes = ([P] + [vp] * 9 + [ctypes.c_int64, ctypes.c_int, vp,
+                                                                ctypes.c_size_t, vp])
             L.e2ttt_decode_step.restype = ctypes.c_int
             L.e2ttt_backward_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
             L.e2ttt_backward_workspace_bytes.restype = ctypes.c_int
@@ -271,17 +271,19 @@ def decode_workspace_bytes(prob: Problem) -> int:
     return int(n.value)
 
 
-def decode_step(prob: Problem, q, k, v, eta, alpha, beta, W0, W, M, out, chunk_end: bool,
+def decode_step(prob: Problem, q, k, v, eta, alpha, beta, W, M, out, pos: int, chunk_end: bool,
                 workspace, workspace_nbytes: Optional[int] = None, stream=None,
                 check: bool = True) -> int:
-    """Call ``e2ttt_decode_step``: one token of every (b, h) unit; W0, W, M
-    are updated in place.  Returns the status; raises on failure when
-    ``check``."""
+    """Call ``e2ttt_decode_step``: the token at position ``pos`` of the current
+    chunk for every (b, h) unit; W, M (the chunk-start state) are replaced by
+    the chunk-end state when ``chunk_end``.  The workspace must be the same,
+    unmodified, for all calls of a chunk.  Returns the status; raises on
+    failure when ``check``."""
     if workspace_nbytes is None:
         workspace_nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().e2ttt_decode_step(
         ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(alpha), _ptr(beta),
-        _ptr(W0), _ptr(W), _ptr(M), _ptr(out), int(bool(chunk_end)), _ptr(workspace),
+        _ptr(W), _ptr(M), _ptr(out), int(pos), int(bool(chunk_end)), _ptr(workspace),
         int(workspace_nbytes), _stream(stream))
     if check and st != OK:
         raise E2tttError(st, "e2ttt_decode_step")

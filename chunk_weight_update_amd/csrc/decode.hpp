@@ -1,17 +1,17 @@
-// decode.hpp -- one token of the fast-weight recurrence for every (b, h)
-// unit: the streaming / decode use of the method of "Rethinking
-// Expressivity and Efficiency in Test-Time Training" (E2-TTT).
+// decode.hpp -- streaming / decode use of the chunk update of "Rethinking
+// Expressivity and Efficiency in Test-Time Training" (E2-TTT): one token of
+// every (b, h) unit per call, with the state update amortised over the chunk.
 //
-// Within a chunk the readout uses the chunk-start weights W_0 (Eq. 6, §3.2),
-// the token's descent direction G_t = -grad_W 0.5||f_W(k_t) - v_t||^2 is
-// taken at W_0 as well (§1, §3), and the state follows the token-wise
-// recurrence whose chunk-end values the closed form reproduces (§3.2,
-// App. A.5):
-//   M <- beta_t M + eta_t G_t,   W <- gamma_t W + M,
-// with gamma_t = 1 - eta_t alpha_t (Eq. 14) or alpha_t itself.  After the
-// last token of a chunk the running W becomes the next chunk's W_0 (§3.2,
-// induction over chunks).  Running the step over a sequence therefore gives
-// the same outputs and chunk-end states as the chunk forward.
+// Within a chunk the readout uses the chunk-start weights W_0 (Eq. 6, §3.2)
+// and the token's descent direction G_t is taken at W_0 as well (§1, §3), so
+// a token needs only W_0: its output and the rank-one factors of G_t are
+// computed at once, and the factors (with the token's key and scalars) go
+// into the chunk's slot of a buffer.  At the chunk's last token the chunk-end
+// pair (W_C, M_C) is formed from the buffered tokens exactly as the chunk
+// forward forms it (§3.2, App. A: the scalar kernels by the suffix scan, then
+// the two weighted aggregations), and it becomes the next chunk's start (App.
+// B.5 notes that this per-chunk bookkeeping is amortised over the chunk's
+// tokens).
 //
 // Per token and unit (SwiGLU, f(x) = W2 (silu(W1 x) * W3 x)):
 //   k_dec_fwd13 : a1 = W1 x, a3 = W3 x, z = silu(a1) a3 for x = q and x = k
@@ -19,12 +19,12 @@
 //   k_dec_bwd   : partial dz = W2^T g per block of 64 rows of W2
 //   k_dec_dact  : dz (partials added in block order); dA3 = dz silu(a1),
 //                 dA1 = dz a3 silu'(a1)
-//   k_dec_update: G_W1 = dA1 k^T, G_W3 = dA3 k^T, G_W2 = g z(k)^T and the
-//                 recurrence on every state entry (16-byte vectors)
-// Linear learner (f(x) = W x): k_dec_lin_fwd (y, out, g) and k_dec_update
-// with G = g k^T.  All arithmetic is fp32 on the fp32 state; the per-token
-// dot products reduce over lanes (fixed shuffle order), so results do not
-// depend on scheduling.
+//   k_dec_stash : k, z(k), dA1, dA3, g and the scalars into the chunk slot
+// Linear learner (f(x) = W x): k_dec_lin_fwd (y, out, g) and k_dec_stash.
+// At the chunk end: the scan over the buffered scalars, k_dec_pack (the
+// scaled aggregation operands, feature-major) and the chunk forward's fp32
+// aggregation kernel.  All arithmetic is fp32 on the fp32 state; per-token
+// dot products reduce over lanes in a fixed shuffle order.
 #pragma once
 #include "common.hpp"
 
@@ -32,14 +32,7 @@ namespace e2ttt {
 
 struct DecodeArgs {
   int64_t BH, d, h;   // h = 0 for the linear learner
-  int mode;           // decay_mode
-  int chunk_end;      // nonzero: W_0 <- W after the update
-  const float* eta;   // [BH]
-  const float* alpha;
-  const float* beta;
-  float* W0;          // [BH][P] chunk-start weights
-  float* W;           // [BH][P] running weights
-  float* M;           // [BH][P] running momentum
+  const float* W0;    // [BH][P] chunk-start weights
   float* zq;          // workspace [BH][h]: z of the query
   float* zk;          // [BH][h]: z of the key
   float* a1k;         // [BH][h]
@@ -47,6 +40,31 @@ struct DecodeArgs {
   float* dA1;         // [BH][h]
   float* dA3;         // [BH][h]
   float* g;           // [BH][d]: v - f_{W_0}(k)
+};
+
+// The chunk buffer of the decode workspace (fp32).  Slot t of a chunk holds
+// token t.  SwiGLU: feature-major rows of cb slots, as the aggregation
+// reads them; linear: token-major.
+struct DecodeBuf {
+  int64_t cb;          // slots (the chunk length rounded up to the tile)
+  float* eb;           // [BH][cb] eta, alpha, beta of the buffered tokens
+  float* ab;
+  float* bb;
+  float* kt;           // SwiGLU [BH][d][cb]: keys
+  float* zt;           // [BH][h][cb]: z(k)
+  float* d1;           // [BH][h][cb]: dA1
+  float* d3;           // [BH][h][cb]: dA3
+  float* gb;           // [BH][d][cb]: g
+  float* kb;           // linear [BH][cb][d]: keys
+  float* gl;           // [BH][cb][d]: g
+  // chunk-end operands
+  float* kw;           // [BH][cb] K^W, K^M (zero past the chunk's tokens)
+  float* km;
+  float* coef;         // [BH][4] cW, cM, cWM
+  float* ut;           // SwiGLU [BH][4h][cb]: K^W dA1, K^M dA1 | K^W dA3, K^M dA3 (32-row interleave)
+  float* gt;           // [BH][2d][cb]: K^W g, K^M g (32-row interleave)
+  float* gw;           // linear [BH][cb][d]: K^W g
+  float* gm;           // [BH][cb][d]: K^M g
 };
 
 __device__ __forceinline__ float wave_sum(float x) {
@@ -237,66 +255,90 @@ __global__ __launch_bounds__(256) void k_dec_lin_fwd(DecodeArgs a, const T* __re
   }
 }
 
-// The recurrence on every state entry, four consecutive entries per thread:
-// M <- beta M + eta G, W <- gamma W + M (and W_0 <- W at a chunk end).
-// Grid ceil(BH * P / 4 / 256); P % 4 == 0 and every row is a multiple of 4.
+// Token `pos` of the chunk into the buffer: the scalars, and (SwiGLU) k,
+// z(k), dA1, dA3, g feature-major, or (linear) k, g token-major.  One block
+// per (unit, group of 256 entries); grid BH * ceil((3 + 3h + 2d) / 256).
 template <typename T>
-__global__ __launch_bounds__(256) void k_dec_update(DecodeArgs a, const T* __restrict__ k) {
-  const int64_t d = a.d, h = a.h;
-  const int64_t P = h == 0 ? d * d : 3 * d * h;
-  const int64_t e4 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
-  if (e4 >= a.BH * P) return;
-  const int64_t u = e4 / P, o = e4 % P;
-  const float et = a.eta[u], al = a.alpha[u], bt = a.beta[u];
-  // gamma in fp64 from the fp32 inputs (the product is exact), one rounding.
-  const float gt = a.mode == 1 ? al
-                   : static_cast<float>(1.0 - static_cast<double>(et) * static_cast<double>(al));
-  float left;        // the left factor of this row of G
-  float right[4];    // the right factors of the four entries
-  // Four consecutive entries of k (vector load; their index is a multiple
-  // of 4 and rows of k are multiples of 16 elements).
-  auto k4 = [&](int64_t idx) {
-    if constexpr (sizeof(T) == 2) {
-      const uint2 p = *reinterpret_cast<const uint2*>(k + idx);
-      right[0] = bf2f(static_cast<bf16_t>(p.x & 0xffffu));
-      right[1] = bf2f(static_cast<bf16_t>(p.x >> 16));
-      right[2] = bf2f(static_cast<bf16_t>(p.y & 0xffffu));
-      right[3] = bf2f(static_cast<bf16_t>(p.y >> 16));
-    } else {
-      const f32x4_t p = *reinterpret_cast<const f32x4_t*>(k + idx);
-#pragma unroll
-      for (int x = 0; x < 4; ++x) right[x] = p[x];
-    }
-  };
-  if (h == 0) {      // linear: G = g k^T
-    const int64_t i = o / d, j = o % d;
-    left = a.g[u * d + i];
-    k4(u * d + j);
-  } else if (o < 2 * h * d) {  // W1 or W3 row i: G = dA k^T
-    const bool w3 = o >= h * d;
-    const int64_t oo = w3 ? o - h * d : o;
-    const int64_t i = oo / d, j = oo % d;
-    left = (w3 ? a.dA3 : a.dA1)[u * h + i];
-    k4(u * d + j);
-  } else {           // W2 row j: G = g z(k)^T
-    const int64_t oo = o - 2 * h * d;
-    const int64_t j = oo / h, i = oo % h;
-    left = a.g[u * d + j];
-    const f32x4_t z = *reinterpret_cast<const f32x4_t*>(a.zk + u * h + i);
-#pragma unroll
-    for (int x = 0; x < 4; ++x) right[x] = z[x];
+__global__ __launch_bounds__(256) void k_dec_stash(DecodeArgs a, DecodeBuf b, int64_t pos,
+                                                   const T* __restrict__ k,
+                                                   const float* __restrict__ eta,
+                                                   const float* __restrict__ alpha,
+                                                   const float* __restrict__ beta) {
+  const int64_t d = a.d, h = a.h, cb = b.cb;
+  const int64_t per = 3 + 3 * h + 2 * d;
+  const int64_t nblk = (per + 255) / 256;
+  const int64_t u = blockIdx.x / nblk;
+  const int64_t e = (blockIdx.x % nblk) * 256 + threadIdx.x;
+  if (e >= per) return;
+  if (e < 3) {
+    const float* src = e == 0 ? eta : e == 1 ? alpha : beta;
+    float* dst = e == 0 ? b.eb : e == 1 ? b.ab : b.bb;
+    dst[u * cb + pos] = src[u];
+    return;
   }
-  const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(a.W + e4);
-  const f32x4_t m0 = *reinterpret_cast<const f32x4_t*>(a.M + e4);
-  f32x4_t wn, mn;
-#pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    mn[x] = fmaf(bt, m0[x], et * (left * right[x]));
-    wn[x] = fmaf(gt, w0[x], mn[x]);
+  int64_t x = e - 3;
+  if (h == 0) {  // linear: k then g, token-major
+    if (x < d) b.kb[(u * cb + pos) * d + x] = to_f32<T>(k[u * d + x]);
+    else if (x < 2 * d) b.gl[(u * cb + pos) * d + (x - d)] = a.g[u * d + (x - d)];
+    return;
   }
-  *reinterpret_cast<f32x4_t*>(a.M + e4) = mn;
-  *reinterpret_cast<f32x4_t*>(a.W + e4) = wn;
-  if (a.chunk_end) *reinterpret_cast<f32x4_t*>(a.W0 + e4) = wn;
+  if (x < d) { b.kt[(u * d + x) * cb + pos] = to_f32<T>(k[u * d + x]); return; }
+  x -= d;
+  if (x < d) { b.gb[(u * d + x) * cb + pos] = a.g[u * d + x]; return; }
+  x -= d;
+  const int64_t which = x / h, j = x % h;  // 0: z, 1: dA1, 2: dA3
+  const float* src = which == 0 ? a.zk : which == 1 ? a.dA1 : a.dA3;
+  float* dst = which == 0 ? b.zt : which == 1 ? b.d1 : b.d3;
+  dst[(u * h + j) * cb + pos] = src[u * h + j];
+}
+
+// Chunk end, SwiGLU: the scaled aggregation operands of the n buffered tokens
+// (zero in the slots past them), and the key and z rows' slots past them
+// zeroed (stale or unset slots must not reach the products).  One block per
+// (unit, operand row), threads along the slots; grid BH * (5h + 3d).
+__global__ __launch_bounds__(256) void k_dec_pack(DecodeArgs a, DecodeBuf b, int64_t n) {
+  const int64_t d = a.d, h = a.h, cb = b.cb;
+  const int64_t rows = 5 * h + 3 * d;
+  const int64_t u = blockIdx.x / rows;
+  int64_t R = blockIdx.x % rows;
+  const float* kwu = b.kw + u * cb;
+  const float* kmu = b.km + u * cb;
+  if (R < 4 * h) {  // ut row R
+    const bool a3 = R >= 2 * h;
+    const int64_t Rp = a3 ? R - 2 * h : R;
+    const bool isM = (Rp % 64) >= 32;
+    const int64_t j = 64 * (Rp / 64) / 2 + Rp % 32;
+    const float* src = (a3 ? b.d3 : b.d1) + (u * h + j) * cb;
+    const float* ks = isM ? kmu : kwu;
+    float* dst = b.ut + (u * 4 * h + R) * cb;
+    for (int64_t t = threadIdx.x; t < cb; t += 256) dst[t] = t < n ? ks[t] * src[t] : 0.0f;
+    return;
+  }
+  R -= 4 * h;
+  if (R < 2 * d) {  // gt row R
+    const bool isM = (R % 64) >= 32;
+    const int64_t i = 64 * (R / 64) / 2 + R % 32;
+    const float* src = b.gb + (u * d + i) * cb;
+    const float* ks = isM ? kmu : kwu;
+    float* dst = b.gt + (u * 2 * d + R) * cb;
+    for (int64_t t = threadIdx.x; t < cb; t += 256) dst[t] = t < n ? ks[t] * src[t] : 0.0f;
+    return;
+  }
+  R -= 2 * d;
+  float* row = R < d ? b.kt + (u * d + R) * cb : b.zt + (u * h + (R - d)) * cb;
+  for (int64_t t = n + threadIdx.x; t < cb; t += 256) row[t] = 0.0f;
+}
+
+// Chunk end, linear learner: K^W g and K^M g of the buffered tokens, zero
+// past them.  Grid ceil(BH * cb * d / 256).
+__global__ __launch_bounds__(256) void k_dec_pack_lin(DecodeArgs a, DecodeBuf b, int64_t n) {
+  const int64_t d = a.d, cb = b.cb;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= a.BH * cb * d) return;
+  const int64_t u = e / (cb * d), t = (e / d) % cb;
+  const float g = t < n ? b.gl[e] : 0.0f;
+  b.gw[e] = t < n ? b.kw[u * cb + t] * g : 0.0f;
+  b.gm[e] = t < n ? b.km[u * cb + t] * g : 0.0f;
 }
 
 }  // namespace e2ttt

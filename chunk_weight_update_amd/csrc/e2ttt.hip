@@ -372,6 +372,7 @@ ScanArgs scan_args(const Plan& q, const float* eta, const float* alpha, const fl
   sa.kw = kw; sa.km = km;
   sa.ustride = ustride; sa.rstride = rstride; sa.pad = pad;
   sa.coef = coef; sa.cstride = cstride;
+  sa.istride = q.L;
   return sa;
 }
 
@@ -941,19 +942,65 @@ e2ttt_status e2ttt_scalar_kernels(const e2ttt_problem* prob, const float* eta,
 
 namespace {
 
-// Decode workspace: z(q), z(k), A1(k), A3(k), dA1, dA3 [BH][h], g [BH][d]
-// and the W2^T g partials [d/64][BH][h], fp32.
-size_t decode_ws_bytes(int64_t BH, int64_t d, int64_t h) {
-  return align256(4 * static_cast<size_t>(BH) * static_cast<size_t>(6 * h + d + (d / 64) * h));
+// Decode workspace: the per-token scratch (z of q and k, a1, a3, dA1, dA3 of
+// k [BH][h]; g [BH][d]; the W2^T g partials [d/64][BH][h]), then the chunk
+// buffer of the buffered tokens and the chunk-end operands (DecodeBuf), then,
+// with the q/k prologue, the normalised q and k of the token.  All fp32
+// except those two (io dtype); sub-buffers 256-byte aligned.
+struct DecodeLayout {
+  int64_t BH, d, h, C, cb;
+  size_t eb, ab, bb, kt, zt, d1, d3, gb, kb, gl, kw, km, coef, ut, gt, gw, gm, qn, kn, total;
+};
+
+DecodeLayout decode_layout(const e2ttt_problem* p) {
+  DecodeLayout L;
+  std::memset(&L, 0, sizeof(L));
+  L.BH = p->batch * p->heads;
+  L.d = p->dim;
+  L.h = p->kind == E2TTT_LINEAR ? 0 : p->hidden;
+  L.C = p->chunk;
+  L.cb = L.h == 0 ? (L.C + 63) / 64 * 64 : (L.C + 127) / 128 * 128;
+  const size_t BH = static_cast<size_t>(L.BH), d = static_cast<size_t>(L.d),
+               h = static_cast<size_t>(L.h), cb = static_cast<size_t>(L.cb);
+  size_t o = align256(4 * BH * (6 * h + d + (d / 64) * h));
+  auto take = [&](size_t bytes) { const size_t at = o; o = align256(o + bytes); return at; };
+  L.eb = take(4 * BH * cb);
+  L.ab = take(4 * BH * cb);
+  L.bb = take(4 * BH * cb);
+  if (h != 0) {
+    L.kt = take(4 * BH * d * cb);
+    L.gb = take(4 * BH * d * cb);
+    L.zt = take(4 * BH * h * cb);
+    L.d1 = take(4 * BH * h * cb);
+    L.d3 = take(4 * BH * h * cb);
+    L.ut = take(4 * BH * 4 * h * cb);
+    L.gt = take(4 * BH * 2 * d * cb);
+  } else {
+    L.kb = take(4 * BH * cb * d);
+    L.gl = take(4 * BH * cb * d);
+    L.gw = take(4 * BH * cb * d);
+    L.gm = take(4 * BH * cb * d);
+  }
+  L.kw = take(4 * BH * cb);
+  L.km = take(4 * BH * cb);
+  L.coef = take(4 * BH * 4);
+  if (p->flags & E2TTT_FLAG_QK_SILU_L2) {
+    const size_t nx = BH * d * (p->io_dtype == E2TTT_BF16 ? 2 : 4);
+    L.qn = take(nx);
+    L.kn = take(nx);
+  }
+  L.total = o;
+  return L;
 }
 
-// With the q/k prologue: the normalised q and k of the token follow, io
-// dtype, each 256-byte aligned.
-size_t decode_ws_total(const e2ttt_problem* p, int64_t BH, int64_t d, int64_t h) {
-  size_t n = decode_ws_bytes(BH, d, h);
-  if (p->flags & E2TTT_FLAG_QK_SILU_L2)
-    n += 2 * align256(static_cast<size_t>(BH * d) * (p->io_dtype == E2TTT_BF16 ? 2 : 4));
-  return n;
+e2ttt_status decode_check(const e2ttt_problem* prob) {
+  const e2ttt_status st = check_problem(prob);
+  if (st != E2TTT_OK) return st;
+  if (prob->flags & (E2TTT_FLAG_CHUNK_AVERAGED_DECAY | E2TTT_FLAG_LACT_RULE))
+    return E2TTT_EUNSUPPORTED;
+  if (prob->kind == E2TTT_MLP) return E2TTT_EUNSUPPORTED;
+  if (prob->kind == E2TTT_LINEAR && prob->dim > 128) return E2TTT_EUNSUPPORTED;
+  return E2TTT_OK;
 }
 
 }  // namespace
@@ -962,69 +1009,70 @@ extern "C" {
 
 e2ttt_status e2ttt_decode_workspace_bytes(const e2ttt_problem* prob, size_t* bytes) {
   if (!bytes) return E2TTT_EINVAL;
-  const e2ttt_status st = check_problem(prob);
+  const e2ttt_status st = decode_check(prob);
   if (st != E2TTT_OK) return st;
-  if (prob->flags & (E2TTT_FLAG_CHUNK_AVERAGED_DECAY | E2TTT_FLAG_LACT_RULE))
-    return E2TTT_EUNSUPPORTED;
-  if (prob->kind == E2TTT_MLP) return E2TTT_EUNSUPPORTED;
-  const int64_t h = prob->kind == E2TTT_LINEAR ? 0 : prob->hidden;
-  *bytes = decode_ws_total(prob, prob->batch * prob->heads, prob->dim, h);
+  *bytes = decode_layout(prob).total;
   return E2TTT_OK;
 }
 
 e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* q, const void* k,
                                const void* v, const float* eta, const float* alpha,
-                               const float* beta, float* W0, float* W, float* M, void* out,
+                               const float* beta, float* W, float* M, void* out, int64_t pos,
                                int chunk_end, void* workspace, size_t workspace_bytes,
                                void* stream) {
-  e2ttt_status st = check_problem(prob);
+  e2ttt_status st = decode_check(prob);
   if (st != E2TTT_OK) return st;
-  if (prob->flags & (E2TTT_FLAG_CHUNK_AVERAGED_DECAY | E2TTT_FLAG_LACT_RULE))
-    return E2TTT_EUNSUPPORTED;
-  if (prob->kind == E2TTT_MLP) return E2TTT_EUNSUPPORTED;
-  const int64_t BH = prob->batch * prob->heads, d = prob->dim;
-  const int64_t h = prob->kind == E2TTT_LINEAR ? 0 : prob->hidden;
+  const DecodeLayout Lw = decode_layout(prob);
+  const int64_t BH = Lw.BH, d = Lw.d, h = Lw.h, cb = Lw.cb;
   const int64_t P = h == 0 ? d * d : 3 * d * h;
-  const size_t need = decode_ws_total(prob, BH, d, h);
-  if (!q || !k || !v || !eta || !alpha || !beta || !W0 || !W || !M || !out || !workspace)
+  if (pos < 0 || pos >= prob->chunk) return E2TTT_EINVAL;
+  if (pos == prob->chunk - 1 && !chunk_end) return E2TTT_EINVAL;  // the last slot ends the chunk
+  if (!q || !k || !v || !eta || !alpha || !beta || !W || !M || !out || !workspace)
     return E2TTT_EINVAL;
-  const void* p16[] = {q, k, v, eta, alpha, beta, W0, W, M, out};
+  const void* p16[] = {q, k, v, eta, alpha, beta, W, M, out};
   for (const void* p : p16)
     if (!aligned(p, 16)) return E2TTT_EINVAL;
   if (!aligned(workspace, 256)) return E2TTT_EINVAL;
-  if (workspace_bytes < need) return E2TTT_EWORKSPACE;
+  if (workspace_bytes < Lw.total) return E2TTT_EWORKSPACE;
   const size_t iosz = prob->io_dtype == E2TTT_BF16 ? 2 : 4;
   const size_t nx = static_cast<size_t>(BH * d) * iosz, ns = static_cast<size_t>(BH) * 4,
                np = static_cast<size_t>(BH * P) * 4;
   const Range in[] = {rng(q, nx), rng(k, nx), rng(v, nx), rng(eta, ns), rng(alpha, ns),
                       rng(beta, ns)};
-  const Range outs[] = {rng(W0, np), rng(W, np), rng(M, np), rng(out, nx), rng(workspace, need)};
-  for (int a = 0; a < 5; ++a) {
-    for (int b = a + 1; b < 5; ++b)
+  const Range outs[] = {rng(W, np), rng(M, np), rng(out, nx), rng(workspace, Lw.total)};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = a + 1; b < 4; ++b)
       if (overlap(outs[a], outs[b])) return E2TTT_EINVAL;
     for (int i = 0; i < 6; ++i)
       if (overlap(outs[a], in[i])) return E2TTT_EINVAL;
   }
   st = device_ok();
   if (st != E2TTT_OK) return st;
+  set_lds_attributes();
   (void)hipGetLastError();
   hipStream_t s = static_cast<hipStream_t>(stream);
+  char* wb = static_cast<char*>(workspace);
   float* ws = static_cast<float*>(workspace);
+  auto F = [&](size_t off) { return off ? reinterpret_cast<float*>(wb + off) : nullptr; };
   DecodeArgs a;
-  a.BH = BH; a.d = d; a.h = h; a.mode = prob->decay_mode; a.chunk_end = chunk_end != 0;
-  a.eta = eta; a.alpha = alpha; a.beta = beta;
-  a.W0 = W0; a.W = W; a.M = M;
+  a.BH = BH; a.d = d; a.h = h;
+  a.W0 = W;
   a.zq = ws; a.zk = ws + BH * h; a.a1k = ws + 2 * BH * h; a.a3k = ws + 3 * BH * h;
   a.dA1 = ws + 4 * BH * h; a.dA3 = ws + 5 * BH * h; a.g = ws + 6 * BH * h;
-  const unsigned gu = grid1((BH * P / 4 + 255) / 256);
+  DecodeBuf b;
+  b.cb = cb;
+  b.eb = F(Lw.eb); b.ab = F(Lw.ab); b.bb = F(Lw.bb);
+  b.kt = F(Lw.kt); b.zt = F(Lw.zt); b.d1 = F(Lw.d1); b.d3 = F(Lw.d3); b.gb = F(Lw.gb);
+  b.kb = F(Lw.kb); b.gl = F(Lw.gl);
+  b.kw = F(Lw.kw); b.km = F(Lw.km); b.coef = F(Lw.coef);
+  b.ut = F(Lw.ut); b.gt = F(Lw.gt); b.gw = F(Lw.gw); b.gm = F(Lw.gm);
   auto run = [&](auto tag) {
     typedef decltype(tag) T;
     const T* Q = static_cast<const T*>(q);
     const T* K = static_cast<const T*>(k);
     if (prob->flags & E2TTT_FLAG_QK_SILU_L2) {
-      char* xb = static_cast<char*>(workspace) + decode_ws_bytes(BH, d, h);
-      T* qn = reinterpret_cast<T*>(xb);
-      T* kn = reinterpret_cast<T*>(xb + align256(static_cast<size_t>(BH * d) * sizeof(T)));
+      T* qn = reinterpret_cast<T*>(wb + Lw.qn);
+      T* kn = reinterpret_cast<T*>(wb + Lw.kn);
       hipLaunchKernelGGL(k_qk_norm<T>, dim3(grid1((BH + 3) / 4)), dim3(256), 0, s, Q, qn, BH, d);
       hipLaunchKernelGGL(k_qk_norm<T>, dim3(grid1((BH + 3) / 4)), dim3(256), 0, s, K, kn, BH, d);
       Q = qn;
@@ -1032,6 +1080,7 @@ e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* q, const v
     }
     const T* V = static_cast<const T*>(v);
     T* O = static_cast<T*>(out);
+    // The token: readout and descent factors at the chunk-start weights.
     if (h == 0) {
       hipLaunchKernelGGL(k_dec_lin_fwd<T>, dim3(grid1(BH)), dim3(256), 0, s, a, Q, K, V, O);
     } else {
@@ -1043,13 +1092,46 @@ e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* q, const v
       hipLaunchKernelGGL(k_dec_dact, dim3(grid1((BH * h + 255) / 256)), dim3(256), 0, s, a,
                          static_cast<const float*>(part));
     }
-    hipLaunchKernelGGL(k_dec_update<T>, dim3(gu), dim3(256), 0, s, a, K);
-    if (chunk_end && (prob->flags & E2TTT_FLAG_POST_CHUNK_ROW_L2)) {
-      // chunk boundary: rows of W normalised, then W0 <- W again
+    const int64_t nblk = (3 + 3 * h + 2 * d + 255) / 256;
+    hipLaunchKernelGGL(k_dec_stash<T>, dim3(grid1(BH * nblk)), dim3(256), 0, s, a, b, pos, K,
+                       eta, alpha, beta);
+    if (!chunk_end) return;
+    // Chunk end: the scalar kernels of the buffered tokens, the weighted
+    // aggregations, (W, M) <- (W_C, M_C).
+    const int64_t n = pos + 1;
+    ScanArgs sa;
+    sa.eta = b.eb; sa.alpha = b.ab; sa.beta = b.bb;
+    sa.L = n; sa.C = n; sa.nC = 1; sa.mode = prob->decay_mode; sa.averaged = 0; sa.lact = 0;
+    sa.kw = b.kw; sa.km = b.km; sa.ustride = cb; sa.rstride = 0; sa.pad = cb;
+    sa.coef = b.coef; sa.cstride = 4; sa.istride = cb;
+    const int tpt = scan_tpt(n);
+    void (*fs)(ScanArgs) = tpt == 1 ? k_scan<256, 1, 1> : tpt == 2 ? k_scan<256, 2, 1>
+                           : tpt == 4 ? k_scan<256, 4, 1> : k_scan<256, 8, 1>;
+    hipLaunchKernelGGL(fs, dim3(grid1(BH)), dim3(256), 0, s, sa);
+    if (h == 0) {
+      hipLaunchKernelGGL(k_dec_pack_lin, dim3(grid1((BH * cb * d + 255) / 256)), dim3(256), 0, s,
+                         a, b, n);
+      Shape sh{BH, cb, d, 0, n, cb, 1, 1};
+      const size_t lds = static_cast<size_t>(2 * 64 * 16 + 64 * d) * sizeof(float);
+      hipLaunchKernelGGL(k_lin_agg<float>, dim3(grid1(BH * (d / 16))), dim3(256), lds, s, sh, 0,
+                         static_cast<const float*>(b.kb), static_cast<const float*>(b.gw),
+                         static_cast<const float*>(b.gm), static_cast<const float*>(b.coef),
+                         static_cast<const float*>(W), static_cast<const float*>(M), W, M);
+    } else {
+      hipLaunchKernelGGL(k_dec_pack, dim3(grid1(BH * (5 * h + 3 * d))), dim3(256), 0, s, a, b,
+                         n);
+      Shape sh{BH, cb, d, h, cb, cb, 1, 1};
+      const int64_t na = (4 * h / 128) * (d / 128), nbk = (2 * d / 128) * (h / 128);
+      hipLaunchKernelGGL(k_agg<float>, dim3(grid1(BH * (na + nbk))), dim3(256), 0, s, sh, 0, 1,
+                         static_cast<const float*>(b.ut), static_cast<const float*>(b.kt),
+                         static_cast<const float*>(b.gt), static_cast<const float*>(b.zt),
+                         static_cast<const float*>(b.coef), static_cast<const float*>(W),
+                         static_cast<const float*>(M), W, M, static_cast<float*>(nullptr),
+                         static_cast<float*>(nullptr), static_cast<float*>(nullptr));
+    }
+    if (prob->flags & E2TTT_FLAG_POST_CHUNK_ROW_L2) {
       const int64_t rows = BH * (h == 0 ? d : 2 * h + d);
       hipLaunchKernelGGL(k_row_l2norm, dim3(grid1((rows + 3) / 4)), dim3(256), 0, s, W, BH, d, h);
-      hipLaunchKernelGGL(k_copy_or_zero, dim3(grid1((BH * P + 255) / 256)), dim3(256), 0, s,
-                         static_cast<const float*>(W), W0, BH * P);
     }
   };
   if (prob->io_dtype == E2TTT_BF16) run(bf16_t{});

@@ -117,6 +117,7 @@ struct ScanArgs {
   int64_t ustride, rstride, pad;
   float* coef;
   int cstride;
+  int64_t istride;  // row stride of eta, alpha, beta per unit (L for [B,H,L] inputs)
 };
 
 // VW consecutive floats at p (p aligned to VW floats).
@@ -157,9 +158,9 @@ __device__ __forceinline__ void scan_segment(int64_t seg, const ScanArgs& sa) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t t0 = static_cast<int64_t>(r) * sa.C;
   const int64_t n = (sa.L - t0) < sa.C ? (sa.L - t0) : sa.C;
-  const float* e_g = sa.eta + u * sa.L + t0;
-  const float* a_g = sa.alpha + u * sa.L + t0;
-  const float* b_g = sa.beta + u * sa.L + t0;
+  const float* e_g = sa.eta + u * sa.istride + t0;
+  const float* a_g = sa.alpha + u * sa.istride + t0;
+  const float* b_g = sa.beta + u * sa.istride + t0;
   float* kw_o = sa.kw + u * sa.ustride + r * sa.rstride;
   float* km_o = sa.km + u * sa.ustride + r * sa.rstride;
   for (int64_t i = n + tid; i < sa.pad; i += NT) {

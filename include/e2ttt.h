@@ -325,30 +325,46 @@ E2TTT_API const char* e2ttt_status_string(e2ttt_status status);
 
 /* Streaming / decode use ("Rethinking Expressivity and Efficiency in
  * Test-Time Training": readout at the chunk-start weights, Eq. 6 and §3.2;
- * gradients at the chunk-start weights, §1 and §3; the token-wise state
- * recurrence whose chunk-end values the closed form reproduces, §3.2 and
- * App. A.5).  One call processes ONE token of every (b, h) unit:
- *   out = f_{W0}(q);  G = -grad_W 0.5 ||f_W(k) - v||^2 at W = W0;
- *   M <- beta M + eta G;  W <- gamma W + M   (gamma by decay_mode);
- *   and, when chunk_end != 0, W0 <- W (the next chunk starts from it).
- * Calling it for the tokens of a sequence in order, with chunk_end set on
+ * gradients at the chunk-start weights, §1 and §3; the chunk-end pair of the
+ * token recurrence by the closed form, §3.2 and App. A; App. B.5: the
+ * per-chunk bookkeeping is amortised over the chunk's tokens).  One call
+ * processes ONE token of every (b, h) unit, the token at position `pos` of
+ * the current chunk (0 <= pos < prob->chunk):
+ *   out = f_W(q) with W the chunk-start weights;
+ *   the token's descent factors at W, its key and its scalars are buffered
+ *   in the workspace, slot pos;
+ *   at a call with chunk_end != 0 the buffered tokens 0 .. pos are applied
+ *   at once: (W, M) <- (W_C, M_C) of the chunk recurrence
+ *     M <- beta M + eta G,  W <- gamma W + M  (gamma by decay_mode)
+ *   exactly as e2ttt_chunk_forward forms them (scalar kernels, then the two
+ *   weighted aggregations, fp32), then the chunk-boundary row normalisation
+ *   when that flag is set.
+ * So between chunk ends W and M hold the state at the chunk's start.  Calling
+ * it for the tokens of a sequence in order, pos = t mod C, with chunk_end on
  * every C-th token and on the last, gives the outputs and end states of
- * e2ttt_chunk_forward on that sequence (up to rounding).
+ * e2ttt_chunk_forward on that sequence (up to rounding).  chunk_end must be
+ * set at pos = C - 1 (EINVAL otherwise).  The workspace carries the chunk's
+ * buffered tokens from call to call: every call of a chunk must get the same
+ * workspace, unmodified; its size (e2ttt_decode_workspace_bytes) grows with
+ * the chunk length: (7h + 4d + 5) floats per slot and unit for SwiGLU,
+ * (4d + 5) for the linear learner.
+ * Per token the call reads W (about 4P bytes) and writes a few vectors; the
+ * full state is read and written once per chunk.
  * Shapes: q, k, v, out [B,H,d] io_dtype (this token); eta, alpha, beta [B,H]
- * fp32; W0, W, M [B,H,P] fp32, updated in place (W0 only at a chunk end).
- * Only batch, heads, dim, hidden, kind, io_dtype and decay_mode of `prob` are
- * used (the rest must still validate); E2TTT_FLAG_CHUNK_AVERAGED_DECAY gives
- * EUNSUPPORTED (chunk means need the whole chunk), the compensated-weights
- * flag is ignored (the state is used in fp32).  W0, W, M, out and the
- * workspace must not overlap one another or the inputs (EINVAL).  All
- * tensor pointers 16-byte aligned, the workspace 256-byte aligned with at
- * least e2ttt_decode_workspace_bytes() bytes (EWORKSPACE).  Asynchronous on
+ * fp32; W, M [B,H,P] fp32, updated in place at a chunk end.  Used from `prob`:
+ * batch, heads, dim, hidden, chunk, kind, io_dtype, decay_mode and the flags
+ * (seq_len must still validate).  E2TTT_FLAG_CHUNK_AVERAGED_DECAY,
+ * E2TTT_FLAG_LACT_RULE and the MLP learner give EUNSUPPORTED; the weight
+ * precision flags have no effect (fp32 throughout).  W, M, out and the
+ * workspace must not overlap one another or the inputs (EINVAL).  All tensor
+ * pointers 16-byte aligned, the workspace 256-byte aligned with at least
+ * e2ttt_decode_workspace_bytes() bytes (EWORKSPACE).  Asynchronous on
  * `stream`; nothing is launched when an argument check fails. */
 E2TTT_API e2ttt_status e2ttt_decode_workspace_bytes(const e2ttt_problem* prob, size_t* bytes);
 E2TTT_API e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* q,
                                          const void* k, const void* v, const float* eta,
-                                         const float* alpha, const float* beta, float* W0,
-                                         float* W, float* M, void* out, int chunk_end,
+                                         const float* alpha, const float* beta, float* W,
+                                         float* M, void* out, int64_t pos, int chunk_end,
                                          void* workspace, size_t workspace_bytes,
                                          void* stream);
 

@@ -217,19 +217,34 @@ def test_timed_entry_host_errors():
 
 
 def test_decode_host_checks():
-    """Host-side checks of the decode entry points (no device call)."""
+    """Host-side checks of the decode entry points (no device call): the
+    workspace holds the chunk buffer (grows with the chunk length), and bad
+    positions or null tensors are rejected before anything touches a device."""
     base = swiglu()
     n = cwu.decode_workspace_bytes(base)
-    B, H, d, h = base.batch, base.heads, base.dim, base.hidden
-    assert n >= 4 * B * H * (6 * h + d) and n % 256 == 0
+    B, H, d, h, C = base.batch, base.heads, base.dim, base.hidden, base.chunk
+    assert n >= 4 * B * H * (7 * h + 4 * d) * C and n % 256 == 0
+    assert cwu.decode_workspace_bytes(swiglu(chunk=2 * C)) > n
+    lin = linear()
+    assert cwu.decode_workspace_bytes(lin) >= 4 * 4 * lin.dim * lin.chunk
     with pytest.raises(cwu.E2tttError):
         cwu.decode_workspace_bytes(swiglu(flags=cwu.FLAG_CHUNK_AVERAGED_DECAY))
     with pytest.raises(cwu.E2tttError):
         cwu.decode_workspace_bytes(swiglu(flags=cwu.FLAG_LACT_RULE))
     assert cwu.decode_workspace_bytes(swiglu(flags=cwu.FLAG_POST_CHUNK_ROW_L2)) == n
-    # null tensors are rejected before anything touches a device
-    st = cwu.lib().e2ttt_decode_step(ctypes.byref(base), *([None] * 10), 0, None, 0, None)
-    assert st == cwu.EINVAL
+    step = cwu.lib().e2ttt_decode_step
+    f = Fake()
+    nx, ns, np_ = B * H * d * 2, B * H * 4, B * H * 3 * d * h * 4
+    args = [f(nx), f(nx), f(nx), f(ns), f(ns), f(ns), f(np_), f(np_), f(nx)]
+    ws = f(n)
+    # null tensors
+    assert step(ctypes.byref(base), *([None] * 9), 0, 0, None, 0, None) == cwu.EINVAL
+    # positions outside the chunk, and the chunk's last slot without chunk_end
+    assert step(ctypes.byref(base), *args, -1, 0, ws, n, None) == cwu.EINVAL
+    assert step(ctypes.byref(base), *args, C, 1, ws, n, None) == cwu.EINVAL
+    assert step(ctypes.byref(base), *args, C - 1, 0, ws, n, None) == cwu.EINVAL
+    # a workspace too small for the chunk buffer
+    assert step(ctypes.byref(base), *args, 0, 0, ws, n - 256, None) == cwu.EWORKSPACE
 
 
 def bwd_fake_args(prob):

@@ -1,9 +1,12 @@
-"""Decode step (one token of the recurrence per call) against the oracle.
+"""Decode step (one token per call, the state update amortised over the
+chunk) against the oracle.
 
-Running e2ttt_decode_step over every token of a sequence, with chunk_end on
-every C-th token and on the last, must give the chunk forward's outputs and
-end states: the oracle's literal recurrence (readout and gradients at the
-chunk-start weights, token-wise momentum/decay update) is the reference."""
+Running e2ttt_decode_step over every token of a sequence, position t mod C
+within the chunk, with chunk_end on every C-th token and on the last, must
+give the chunk forward's outputs and end states: the oracle's literal
+recurrence (readout and gradients at the chunk-start weights, token-wise
+momentum/decay update) is the reference.  The chunk-end update is fp32, so
+the states meet 1e-5 for both io types."""
 import numpy as np
 import pytest
 
@@ -15,11 +18,9 @@ pytestmark = pytest.mark.gpu
 TOL = {F32: (1e-5, 1e-5, 1e-5), BF16: (1e-2, 1e-5, 1e-5)}
 
 
-def run_decode(prob, t, L, C):
+def run_decode(prob, t, L, C, check_mid_chunk=False):
     import torch
     import chunk_weight_update_amd as cwu
-    B, H, _, d = t["q"].shape
-    W0 = t["W0"].clone()
     W = t["W0"].clone()
     M = t["M0"].clone()
     outs = torch.empty_like(t["q"])
@@ -27,13 +28,17 @@ def run_decode(prob, t, L, C):
     ws = torch.empty(cwu.decode_workspace_bytes(prob), dtype=torch.uint8, device="cuda")
     for s in range(L):
         col = lambda x: x[:, :, s].clone()  # fresh, aligned (a [1,1] slice is a view)
+        end = (s + 1) % C == 0 or s == L - 1
+        before = (W.clone(), M.clone()) if check_mid_chunk and not end else None
         cwu.decode_step(prob, col(t["q"]), col(t["k"]), col(t["v"]), col(t["eta"]),
-                        col(t["alpha"]), col(t["beta"]), W0, W, M, out_t,
-                        (s + 1) % C == 0 or s == L - 1, ws)
+                        col(t["alpha"]), col(t["beta"]), W, M, out_t, s % C, end, ws)
         outs[:, :, s] = out_t
+        if before is not None:  # between chunk ends the state is the chunk start's
+            torch.cuda.synchronize()
+            assert torch.equal(before[0], W) and torch.equal(before[1], M)
     torch.cuda.synchronize()
     return (outs.float().cpu().numpy().astype(np.float64), W.cpu().numpy().astype(np.float64),
-            M.cpu().numpy().astype(np.float64), W0.cpu().numpy().astype(np.float64))
+            M.cpu().numpy().astype(np.float64))
 
 
 @pytest.mark.parametrize("kind,B,H,L,d,h,C,io,regime", [
@@ -42,20 +47,20 @@ def run_decode(prob, t, L, C):
     (SWIGLU, 1, 2, 48, 128, 256, 16, F32, "nearunit"),
     (SWIGLU, 2, 2, 40, 128, 256, 16, BF16, "nearunit"),     # ragged
     (SWIGLU, 1, 1, 24, 256, 512, 8, BF16, "default"),
+    (SWIGLU, 1, 2, 300, 128, 256, 128, BF16, "nearunit"),   # chunks past one 128-slot tile
 ])
 def test_decode_matches_oracle(kind, B, H, L, d, h, C, io, regime):
     log(f"decode kind={kind} B={B} H={H} L={L} d={d} h={h} C={C} io={io} {regime}")
     inp = make_inputs(kind, B, H, L, d, h, io, seed=9, regime=regime,
                       m0_scale=1e-6 if regime == "nearunit" else 0.01)
     prob = problem_for(kind, B, H, L, d, h, C, io)
-    out, W, M, W0 = run_decode(prob, to_device(inp, io), L, C)
+    out, W, M = run_decode(prob, to_device(inp, io), L, C, check_mid_chunk=True)
     ro, rW, rM = run_oracle(kind, inp, C, h)
     e = (rel_fro(out, ro), rel_fro(W, rW), rel_fro(M, rM))
     log(f"  rel_fro out={e[0]:.3e} W={e[1]:.3e} M={e[2]:.3e}")
     t = TOL[io]
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(W)) and np.all(np.isfinite(M))
     assert e[0] <= t[0] and e[1] <= t[1] and e[2] <= t[2], e
-    assert np.array_equal(W0, W)  # the last token closed the chunk: W0 <- W
 
 
 def test_decode_with_qk_prologue():
@@ -67,7 +72,7 @@ def test_decode_with_qk_prologue():
     inp = raw_projections(make_inputs(kind, B, H, L, d, h, io, seed=13, regime="nearunit",
                                       m0_scale=1e-6), io, 13)
     prob = problem_for(kind, B, H, L, d, h, C, io, 0, cwu.FLAG_QK_SILU_L2)
-    out, W, M, _ = run_decode(prob, to_device(inp, io), L, C)
+    out, W, M = run_decode(prob, to_device(inp, io), L, C)
     import oracle
     ro, rW, rM = oracle.chunk_forward(kind, inp["q64"], inp["k64"], inp["v64"], inp["eta"],
                                       inp["alpha"], inp["beta"], inp["W0"], inp["M0"], C, h,
@@ -90,7 +95,7 @@ def test_decode_with_row_normalisation(kind, B, H, L, d, h, C, io, regime):
     inp = make_inputs(kind, B, H, L, d, h, io, seed=15, regime=regime,
                       m0_scale=1e-6 if regime == "nearunit" else 0.01)
     prob = problem_for(kind, B, H, L, d, h, C, io, 0, cwu.FLAG_POST_CHUNK_ROW_L2)
-    out, W, M, W0 = run_decode(prob, to_device(inp, io), L, C)
+    out, W, M = run_decode(prob, to_device(inp, io), L, C)
     ro, rW, rM = oracle.chunk_forward(kind, inp["q64"], inp["k64"], inp["v64"], inp["eta"],
                                       inp["alpha"], inp["beta"], inp["W0"], inp["M0"], C, h,
                                       row_norm=True)
@@ -98,4 +103,3 @@ def test_decode_with_row_normalisation(kind, B, H, L, d, h, C, io, regime):
     log(f"  rel_fro out={e[0]:.3e} W={e[1]:.3e} M={e[2]:.3e}")
     t = TOL[io]
     assert e[0] <= t[0] and e[1] <= t[1] and e[2] <= t[2], e
-    assert np.array_equal(W0, W)

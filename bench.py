@@ -743,7 +743,9 @@ def main():
             ro = run_workload(wo, 20, 5)
             del ro["_run"]
             others[name] = {k: ro[k] for k in ("ms_per_step", "value", "per_call_ms",
-                                                "tflops_algorithmic", "roofline")}
+                                                "tflops_algorithmic",
+                                                "mfma_util_pct_of_bf16_peak", "roofline")}
+            others[name]["config"] = wo.describe()
             log(f"bench: other workload {name}: {others[name]}")
             torch.cuda.empty_cache()
         line["other_configs"] = others

@@ -194,17 +194,21 @@ e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
     q.w13s = take(T * q.BH * 2 * q.h * q.krep * q.d);
     q.w2s = take(T * q.BH * q.d * q.krep * q.h);
     q.w2ts = take(T * q.BH * q.h * q.krep * q.d);
+    // Plain bf16 operands with d, h and the padded chunk multiples of 256:
+    // the forward GEMMs (fwd13, fwd2) run on 256x256 tiles, and the backward
+    // recomputes A1, A3 instead of keeping an fp32 copy.
+    q.tile256 = q.io == E2TTT_BF16 && q.krep == 1 && q.d % 256 == 0 && q.h % 256 == 0 &&
+                q.Cp % 256 == 0;
     q.zrow = take(T * q.BH * 2 * q.Cp * q.h);
-    q.a1s = take(f4 * q.BH * q.Cp * q.h);
-    q.a3s = take(f4 * q.BH * q.Cp * q.h);
+    q.a1s = q.a3s = 0;
+    if (!q.tile256) {
+      q.a1s = take(f4 * q.BH * q.Cp * q.h);
+      q.a3s = take(f4 * q.BH * q.Cp * q.h);
+    }
     q.grow = take(T * q.BH * q.Cp * q.d);
     q.ut = take(T * q.BH * 4 * q.h * q.Cp);
     q.gt = take(T * q.BH * 2 * q.d * q.Cp);
     q.zt = take(T * q.BH * q.h * q.Cp);
-    // Plain bf16 operands with d, h and the padded chunk multiples of 256:
-    // the forward GEMMs (fwd13, fwd2) run on 256x256 tiles.
-    q.tile256 = q.io == E2TTT_BF16 && q.krep == 1 && q.d % 256 == 0 && q.h % 256 == 0 &&
-                q.Cp % 256 == 0;
     // bf16 operands with d, h multiples of 256: the aggregation runs on
     // 256x256 tiles; the chunk's token slabs are split so that the grid comes
     // close to one workgroup per CU, and k_agg_reduce adds the splits.
@@ -294,6 +298,7 @@ void set_lds_attributes() {
       reinterpret_cast<const void*>(&k_phaseB<2>), reinterpret_cast<const void*>(&k_phaseA2<32>),
       reinterpret_cast<const void*>(&k_phaseA2<64>), reinterpret_cast<const void*>(&k_agg256),
       reinterpret_cast<const void*>(&k_fwd13_256), reinterpret_cast<const void*>(&k_fwd2_256),
+      reinterpret_cast<const void*>(&k_bwd256),
       reinterpret_cast<const void*>(&k_lin_bwd_tok<1>), reinterpret_cast<const void*>(&k_lin_bwd_tok<2>),
       reinterpret_cast<const void*>(&k_lin_bwd_tok<3>), reinterpret_cast<const void*>(&k_lin_bwd_tok<4>)};
   for (const void* f : fused_kernels)
@@ -424,22 +429,20 @@ void launch_agg256(const Plan& q, const Shape& s, int r, int last, const T* ut, 
 // Forward GEMMs of one chunk on 256x256 tiles (plain bf16), then the backward.
 template <typename T>
 void launch_fwd_bwd256(const Plan& q, const Shape& s, int r, const T* Q, const T* K, const T* V,
-                       T* O, const T* w13s, const T* w2s, const T* w2ts, T* zrow, float* a1s,
-                       float* a3s, T* zt, const float* kw, const float* km, T* grow, T* gt, T* ut,
-                       hipStream_t st, Instr& I) {
+                       T* O, const T* w13s, const T* w2s, const T* w2ts, T* zrow, T* zt,
+                       const float* kw, const float* km, T* grow, T* gt, T* ut, hipStream_t st,
+                       Instr& I) {
   static_assert(sizeof(T) == 2 || sizeof(T) == 4, "operand type");
   if constexpr (sizeof(T) == 2) {
     E2TTT_LAUNCH(I, E2TTT_KERNEL_FWD13, k_fwd13_256,
                  dim3(grid1(q.BH * (2 * q.Cp / 256) * (2 * q.h / 256))), dim3(256),
-                 Tile256::LDS_BYTES, st, s, r, Q, K, w13s, zrow, a1s, a3s, zt);
+                 Tile256::LDS_BYTES, st, s, r, Q, K, w13s, zrow, zt);
     E2TTT_LAUNCH(I, E2TTT_KERNEL_FWD2, k_fwd2_256,
                  dim3(grid1(q.BH * (2 * q.Cp / 256) * (q.d / 256))), dim3(256), Tile256::LDS_BYTES,
                  st, s, r, V, O, zrow, w2s, kw, km, grow, gt);
-    // The backward stays on 128x128 tiles: its epilogue is memory-bound (fp32
-    // A1, A3 in, four scaled outputs out), and the 128-tile kernel overlaps
-    // it with other workgroups' MFMAs (measured faster at d = 768).
-    E2TTT_LAUNCH(I, E2TTT_KERNEL_BWD, k_bwd<T>, dim3(grid1(q.BH * (q.Cp / 128) * (q.h / 128))),
-                 dim3(256), 0, st, s, r, grow, w2ts, a1s, a3s, kw, km, ut);
+    E2TTT_LAUNCH(I, E2TTT_KERNEL_BWD, k_bwd256,
+                 dim3(grid1(q.BH * (q.Cp / Bwd256::BM) * (q.h / Bwd256::BN))), dim3(256),
+                 Bwd256::LDS_BYTES, st, s, r, K, grow, w13s, w2ts, kw, km, ut);
   }
 }
 
@@ -481,8 +484,8 @@ void launch_swiglu(const Plan& q, const void* qv, const void* kv, const void* vv
     const float* Min = r == 0 ? M0 : Mend;
     const int ri = static_cast<int>(r);
     if (q.tile256) {
-      launch_fwd_bwd256(q, s, ri, Q, K, V, O, w13s, w2s, w2ts, zrow, a1s, a3s, zt, kw, km, grow,
-                        gt, ut, st, I);
+      launch_fwd_bwd256(q, s, ri, Q, K, V, O, w13s, w2s, w2ts, zrow, zt, kw, km, grow, gt, ut,
+                        st, I);
     } else {
       E2TTT_LAUNCH(I, E2TTT_KERNEL_FWD13, k_fwd13<T>,
                    dim3(grid1(q.BH * (2 * q.Cp / 128) * (2 * q.h / 128))), dim3(256), 0, st, s,

@@ -427,10 +427,11 @@ __device__ __forceinline__ void for_bands(F&& f) {
 
 // fwd13: [K; Q] rows x [W1; W3]^T (w13s rows interleaved in blocks of 32, so
 // accumulator blocks 2*pr and 2*pr+1 are A1 and A3 of the same 32 hidden
-// units) -> Z = silu(A1) A3 row-major, A1 and A3 (fp32) and Z^T for K rows.
+// units) -> Z = silu(A1) A3 row-major, and Z^T for K rows (the backward
+// recomputes A1 and A3).
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_fwd13_256(
     Shape s, int r, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-    const bf16_t* __restrict__ w13s, bf16_t* zrow, float* a1s, float* a3s, bf16_t* zt) {
+    const bf16_t* __restrict__ w13s, bf16_t* zrow, bf16_t* zt) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   const int64_t ntn = 2 * s.h / 256, ntm = 2 * s.Cp / 256, mtK = s.Cp / 256;
   int64_t bid = xcd_logical_block();
@@ -458,8 +459,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int h = static_cast<int>(s.h);
   // Row p0 of this tile in each output; offsets below are 32-bit.
   bf16_t* zq = zrow + (u * 2 * s.Cp + (isQ ? s.Cp : 0) + p0) * s.h + nt * 128;
-  float* a1u = a1s + (u * s.Cp + p0) * s.h + nt * 128;
-  float* a3u = a3s + (u * s.Cp + p0) * s.h + nt * 128;
   // Each band in two pieces (one per 32 hidden units), kept apart by
   // scheduling barriers so that only one piece's values are live at a time.
   auto band = [&](auto MI, auto KROWS) {
@@ -479,10 +478,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const float z = a1 * sigmoidf_(a1) * a3;
         zv[v] = z;
         zq[off] = f2bf(z);
-        if constexpr (krows) {
-          a1u[off] = a1;
-          a3u[off] = a3;
-        }
       }
       if constexpr (krows) {
 #pragma unroll
@@ -611,6 +606,230 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
   if (nvt == 256) for_bands([&](auto MI) { band(MI, Flag<true>{}); });
   else for_bands([&](auto MI) { band(MI, Flag<false>{}); });
+}
+
+// ---------------------------------------------------------------------------
+// Backward of the 256 path: dZ = g W2 together with the pre-activations
+// A1 = k W1^T, A3 = k W3^T, recomputed from the bf16 operands the forward
+// used (same products, same k order and fragment layout as k_fwd13_256, so
+// the values are the forward's own), then dA1, dA3 scaled by both kernels
+// into the feature-major operands of the aggregation.  Recomputing costs
+// 4dh flop per token; an fp32 copy of A1, A3 written by the forward and read
+// back here costs 16 bytes per token and hidden unit of memory traffic,
+// which at d = 768 takes longer than the products.
+//
+// Tile: 256 tokens x 64 hidden units of one unit.  Each of the 4 waves takes
+// 64 tokens (accumulator blocks mi = 0, 1) and all 64 units (jb = 0, 1) of
+// the three products: 12 blocks, 192 accumulator registers.  A stage holds
+// one 32-deep slab of 704 rows of 64 bytes: g rows 0..255, k rows 256..511,
+// W2^T rows of the 64 units 512..575, then their 128 w13s rows 576..703
+// (W1 and W3 in blocks of 32), stored with the swizzle of the 256 engine.
+// Loads go straight to LDS, three stages deep.
+struct Bwd256 {
+  static constexpr int BM = 256, BN = 64, BK = 32, NST = 3;
+  static constexpr int ROWS = 2 * BM + 3 * BN;          // 704
+  static constexpr int STAGE = ROWS * 64;               // 44 KB
+  static constexpr int LOADS = ROWS / 16 / 4;           // direct loads per wave per slab: 11
+  static constexpr size_t LDS_BYTES = static_cast<size_t>(NST) * STAGE;  // 132 KB
+};
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_bwd256(
+    Shape s, int r, const bf16_t* __restrict__ k, const bf16_t* __restrict__ grow,
+    const bf16_t* __restrict__ w13s, const bf16_t* __restrict__ w2ts,
+    const float* __restrict__ kw, const float* __restrict__ km, bf16_t* ut) {
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  constexpr int NST = Bwd256::NST, SB = Bwd256::STAGE, NL = Bwd256::LOADS;
+  const int64_t ntn = s.h / Bwd256::BN, ntm = s.Cp / Bwd256::BM;
+  int64_t bid = xcd_logical_block();  // the hidden tiles of a token block share one L2
+  const int64_t nt = bid % ntn; bid /= ntn;
+  const int64_t mt = bid % ntm;
+  const int64_t u = bid / ntm;
+  const int64_t p0 = mt * Bwd256::BM, j0 = nt * Bwd256::BN;
+  const int64_t tok0 = static_cast<int64_t>(r) * s.C;
+  const int64_t nv = n_valid(s, r);
+  const int64_t d = s.d;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+  // Source of this lane's piece for load i: stage row R = 16*(4i + wave) +
+  // lane/4, physical piece lane%4 = logical k-chunk (lane%4) ^ swz256(R).
+  const bf16_t* src[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int R = 16 * (4 * i + wave) + (lane >> 2);
+    const int c8 = 8 * ((lane & 3) ^ swz256(R));
+    const bf16_t* row;
+    if (R < 256) {
+      row = grow + (u * s.Cp + p0 + R) * d;
+    } else if (R < 512) {
+      const int64_t p = p0 + R - 256;
+      row = p < nv ? k + (u * s.L + tok0 + p) * d : kZeroRow256;
+    } else if (R < 576) {
+      row = w2ts + (u * s.h + j0 + R - 512) * d;
+    } else {
+      row = w13s + (u * 2 * s.h + 2 * j0 + R - 576) * d;
+    }
+    src[i] = row + c8;
+  }
+  auto load = [&](int slab, int i) {
+    char* st = smem_raw + (slab % NST) * SB;
+    __builtin_amdgcn_global_load_lds(
+        static_cast<const void*>(src[i] + static_cast<int64_t>(slab) * Bwd256::BK),
+        (__attribute__((address_space(3))) void*)(st + (4 * i + wave) * 1024), 16, 0, 0);
+  };
+
+  // The epilogue's per-token kernels, loaded now so that their latency
+  // overlaps the main loop: token p0 + 64*wave + 32*mi + 8*vq + 4*hf + e.
+  f32x4_t kw4[2][4], km4[2][4];
+  {
+    const float* kwr = kw + (u * s.nC + r) * s.Cp + p0 + 64 * wave + 4 * (lane >> 5);
+    const float* kmr = km + (u * s.nC + r) * s.Cp + p0 + 64 * wave + 4 * (lane >> 5);
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int vq = 0; vq < 4; ++vq) {
+        kw4[mi][vq] = *reinterpret_cast<const f32x4_t*>(kwr + 32 * mi + 8 * vq);
+        km4[mi][vq] = *reinterpret_cast<const f32x4_t*>(kmr + 32 * mi + 8 * vq);
+      }
+  }
+  f32x16_t dz[2][2], a1[2][2], a3[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) { dz[i][j][v] = 0.0f; a1[i][j][v] = 0.0f; a3[i][j][v] = 0.0f; }
+
+  const int r32 = lane & 31, hf = lane >> 5, sw = swz256(r32);
+  const int off0 = r32 * 64 + ((hf ^ sw) << 4), off1 = r32 * 64 + (((2 + hf) ^ sw) << 4);
+  const int ns = static_cast<int>(d / Bwd256::BK);
+  // Fragment set of one 16-deep step: g and k blocks of this wave's tokens,
+  // W2^T, W1, W3 blocks of the tile's units, in the order the MFMAs use them.
+  struct Frags { bf16x8_t g[2], kk[2], w2[2], w1[2], w3[2]; };
+  auto rd = [&](const char* st, int off, int rowbase) {
+    return *reinterpret_cast<const bf16x8_t*>(st + rowbase * 64 + off);
+  };
+  auto read_frags = [&](Frags& f, const char* st, int ks) {
+    const int off = ks ? off1 : off0;
+    f.g[0] = rd(st, off, 64 * wave);
+    f.w2[0] = rd(st, off, 512);
+    f.w2[1] = rd(st, off, 544);
+    f.g[1] = rd(st, off, 64 * wave + 32);
+    f.kk[0] = rd(st, off, 256 + 64 * wave);
+    f.w1[0] = rd(st, off, 576);
+    f.w1[1] = rd(st, off, 640);
+    f.kk[1] = rd(st, off, 256 + 64 * wave + 32);
+    f.w3[0] = rd(st, off, 608);
+    f.w3[1] = rd(st, off, 672);
+  };
+  // The 12 MFMAs of one step; load slots spread the slab's refill among them.
+  auto step = [&](const Frags& f, auto&& between) {
+#pragma unroll
+    for (int m = 0; m < 12; ++m) {
+      const int prod = m / 4, mi = (m >> 1) & 1, jb = m & 1;
+      if (prod == 0) dz[mi][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.g[mi], f.w2[jb], dz[mi][jb], 0, 0, 0);
+      else if (prod == 1) a1[mi][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.kk[mi], f.w1[jb], a1[mi][jb], 0, 0, 0);
+      else a3[mi][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.kk[mi], f.w3[jb], a3[mi][jb], 0, 0, 0);
+      between(m);
+    }
+  };
+  auto body = [&](int sl, bool refill) {
+    const char* st = smem_raw + (sl % NST) * SB;
+    Frags f0, f1;
+    read_frags(f0, st, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    step(f0, [&](int m) {
+      if (m == 1) read_frags(f1, st, 1);
+      if (refill && m >= 2 && m < 2 + 5) load(sl + NST - 1, m - 2);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    step(f1, [&](int m) {
+      if (refill && m < NL - 5) load(sl + NST - 1, m + 5);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+#pragma unroll
+  for (int p = 0; p < NST - 1; ++p)
+    if (p < ns)
+#pragma unroll
+      for (int i = 0; i < NL; ++i) load(p, i);
+  int sl = 0;
+  for (; sl < ns - (NST - 1); ++sl) {
+    wait_vmcnt<NL * (NST - 2)>();
+    barrier_nofence();
+    body(sl, true);
+  }
+  for (; sl < ns; ++sl) {
+    if (sl < ns - 1) wait_vmcnt<NL>();
+    else wait_vmcnt<0>();
+    barrier_nofence();
+    body(sl, false);
+  }
+
+  // Epilogue: lane values of block (mi, jb), register v: token
+  // p0 + 64*wave + 32*mi + 8*(v/4) + 4*hf + v%4, unit j0 + 32*jb + r32.  The
+  // four scaled outputs of the tile (o = dA1 K^W, dA1 K^M, dA3 K^W, dA3 K^M)
+  // are staged in LDS as [o][unit][256 tokens + 8] bf16 (the stages are
+  // free: every wave has passed the last slab's barrier and read its
+  // fragments), four tokens per 8-byte write, then copied out in whole
+  // 512-byte rows: ut row (W1 | W3 family) + 64*(j/32) + (0 | 32 for K^M) +
+  // j%32, tokens p0 .. p0+255.  (Direct 8-byte stores from the accumulator
+  // layout touch 32 rows per instruction and measured twice as slow.)
+  constexpr int SW = Bwd256::BM + 8;  // staged row, bf16
+  static_assert(4 * Bwd256::BN * SW * 2 <= static_cast<int>(Bwd256::LDS_BYTES), "staging fits");
+  bf16_t* stg = reinterpret_cast<bf16_t*>(smem_raw);
+  __syncthreads();  // every wave's last fragment reads are done
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+      pin_acc(dz[mi][jb]);
+      pin_acc(a1[mi][jb]);
+      pin_acc(a3[mi][jb]);
+    }
+#pragma unroll
+    for (int vq = 0; vq < 4; ++vq) {
+      const int tk = 32 * mi + 8 * vq + 4 * hf;
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        float x1w[4], x1m[4], x3w[4], x3m[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = 4 * vq + e;
+          const float A1 = a1[mi][jb][v];
+          const float A3 = s.gated ? a3[mi][jb][v] : 1.0f;
+          const float dzv = dz[mi][jb][v];
+          const float sg = sigmoidf_(A1);
+          const float d3 = s.gated ? dzv * (A1 * sg) : 0.0f;
+          const float d1 = dzv * A3 * (sg * (1.0f + A1 * (1.0f - sg)));
+          x1w[e] = kw4[mi][vq][e] * d1;
+          x1m[e] = km4[mi][vq][e] * d1;
+          x3w[e] = kw4[mi][vq][e] * d3;
+          x3m[e] = km4[mi][vq][e] * d3;
+        }
+        const int jj = 32 * jb + r32, col = 64 * wave + tk;
+        auto put = [&](int o, const float (&x)[4]) {
+          *reinterpret_cast<uint2*>(stg + (o * Bwd256::BN + jj) * SW + col) =
+              make_uint2(f2bf(x[0]) | (static_cast<uint32_t>(f2bf(x[1])) << 16),
+                         f2bf(x[2]) | (static_cast<uint32_t>(f2bf(x[3])) << 16));
+        };
+        put(0, x1w);
+        put(1, x1m);
+        put(2, x3w);
+        put(3, x3m);
+      }
+    }
+  }
+  __syncthreads();
+  bf16_t* ub = ut + u * 4 * s.h * s.Cp + p0;
+  constexpr int VPR = Bwd256::BM / 8;  // 16-byte pieces per row
+  for (int idx = threadIdx.x; idx < 4 * Bwd256::BN * VPR; idx += 256) {
+    const int row = idx / VPR, c = idx % VPR;
+    const int o = row / Bwd256::BN, jj = row % Bwd256::BN;
+    const int64_t j = j0 + jj;
+    const int64_t dst = (o >= 2 ? 2 * s.h : 0) + 64 * (j / 32) + (o & 1 ? 32 : 0) + j % 32;
+    *reinterpret_cast<uint4*>(ub + dst * s.Cp + 8 * c) =
+        *reinterpret_cast<const uint4*>(stg + row * SW + 8 * c);
+  }
 }
 
 }  // namespace e2ttt

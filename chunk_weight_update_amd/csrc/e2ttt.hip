@@ -438,7 +438,7 @@ void launch_fwd_bwd256(const Plan& q, const Shape& s, int r, const T* Q, const T
                  dim3(grid1(q.BH * (2 * q.Cp / 256) * (2 * q.h / 256))), dim3(256),
                  Tile256::LDS_BYTES, st, s, r, Q, K, w13s, zrow, zt);
     E2TTT_LAUNCH(I, E2TTT_KERNEL_FWD2, k_fwd2_256,
-                 dim3(grid1(q.BH * (2 * q.Cp / 256) * (q.d / 256))), dim3(256), Tile256::LDS_BYTES,
+                 dim3(grid1(q.BH * (2 * q.Cp / 256) * (q.d / 256))), dim3(256), Fwd2Epi::LDS_BYTES,
                  st, s, r, V, O, zrow, w2s, kw, km, grow, gt);
     E2TTT_LAUNCH(I, E2TTT_KERNEL_BWD, k_bwd256,
                  dim3(grid1(q.BH * (q.Cp / Bwd256::BM) * (q.h / Bwd256::BN))), dim3(256),

@@ -498,6 +498,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // fwd2: Z rows x W2^T -> Y; the readout for Q rows, g = v - Y for K rows
 // (row-major) and K^W g, K^M g feature-major (rows 64*(i/32) + i%32, +32 for
 // the momentum copy).
+//
+// Epilogue, one accumulator band at a time (band mi = tile rows 32*mi +
+// [0,32) of both wave rows; band row br = 32*wm + [0,32)): the band's rows
+// of v come straight into LDS (512-byte rows, in pairs padded to 1056 bytes
+// so that the two lane halves, 4 rows apart, read distinct banks), the next
+// band's while this one is computed; each lane reads its values of v there
+// and writes g back in place; g and the readout leave in whole rows, and the
+// two scaled copies of g go through the transposing band buffers.  The
+// chunk's kernels for the tile's 256 tokens sit in LDS as well.
+struct Fwd2Epi {
+  static constexpr int PAIR = 1056;                    // two 512-byte rows + pad
+  static constexpr int GBUF = 32 * PAIR;               // one band of v / g: 64 rows
+  static constexpr int TBUF = 256 * 72 * 2;            // one transposed band (band_put)
+  static constexpr int G0 = 0, G1 = GBUF, TW = 2 * GBUF, TM = TW + TBUF, KS = TM + TBUF;
+  static constexpr size_t LDS_BYTES = KS + 2 * 256 * 4;  // + K^W, K^M of the tile: 140 KB
+  static_assert(LDS_BYTES >= Tile256::LDS_BYTES, "the main loop's stages fit");
+  __device__ static int off(int br, int c) { return (br >> 1) * PAIR + (br & 1) * 512 + 2 * c; }
+};
+
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_fwd2_256(
     Shape s, int r, const bf16_t* __restrict__ v, bf16_t* out, const bf16_t* __restrict__ zrow,
     const bf16_t* __restrict__ w2s, const float* __restrict__ kw, const float* __restrict__ km,
@@ -523,89 +542,118 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   gemm_tile256(acc, la, lb, 0, s.h, smem_raw);
 
   const Acc256Pos ps;
-  const int d = static_cast<int>(s.d);
+  const int64_t d = s.d;
   const int nvt = static_cast<int>(nv - p0 < 256 ? nv - p0 : 256);  // valid rows of the tile
+  using E = Fwd2Epi;
+  // Tile row of band row br in band mi.
+  auto trow = [](int mi, int br) { return 128 * (br >> 5) + 32 * mi + (br & 31); };
+  // Band row of this lane's register vv.
+  auto brow = [&](int vv) { return 32 * ps.wm + 8 * (vv >> 2) + 4 * ps.hf + (vv & 3); };
+  // Copy band mi's 64 rows from G out to dst + tile row * d (rows below
+  // `valid` only), 16 bytes per thread and step; 8 steps per thread.
+  auto rows_out = [&](int mi, const char* G, bf16_t* dst, int valid) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = threadIdx.x + 256 * i;
+      const int k = idx >> 6, rr = (idx >> 5) & 1, c16 = idx & 31;
+      const int tr = trow(mi, 2 * k + rr);
+      const uint4 x = *reinterpret_cast<const uint4*>(G + k * E::PAIR + rr * 512 + 16 * c16);
+      if (tr < valid) *reinterpret_cast<uint4*>(dst + tr * d + 8 * c16) = x;
+    }
+  };
   if (isQ) {
-    bf16_t* o = out + (u * s.L + tok0) * s.d + nt * 256;
-    auto band = [&](auto MI, auto FULL) {
+    bf16_t* o = out + (u * s.L + tok0 + p0) * d + nt * 256;
+    char* G = smem_raw + E::G0;
+    auto band = [&](auto MI) {
       constexpr int mi = decltype(MI)::value;
+      __syncthreads();  // the main loop's stages, or the previous band's rows, are free
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni) {
         pin_acc(acc[mi][ni]);
 #pragma unroll
-        for (int vv = 0; vv < 16; ++vv) {
-          const int pr = ps.row(mi, vv);
-          if (decltype(FULL)::value || pr < nvt)
-            o[(p0 + pr) * s.d + ps.col(ni)] = f2bf(acc[mi][ni][vv]);
-        }
+        for (int vv = 0; vv < 16; ++vv)
+          *reinterpret_cast<bf16_t*>(G + E::off(brow(vv), ps.col(ni))) = f2bf(acc[mi][ni][vv]);
         __builtin_amdgcn_sched_barrier(0);
       }
+      __syncthreads();
+      rows_out(mi, G, o, nvt);
     };
-    if (nvt == 256) for_bands([&](auto MI) { band(MI, Flag<true>{}); });
-    else for_bands([&](auto MI) { band(MI, Flag<false>{}); });
+    for_bands(band);
     return;
   }
-  bf16_t* lds = reinterpret_cast<bf16_t*>(smem_raw);
-  bf16_t* ldsM = lds + 256 * 72;
-  const bf16_t* vs = v + (u * s.L + tok0 + p0) * s.d + nt * 256;
-  bf16_t* gr = grow + (u * s.Cp + p0) * s.d + nt * 256;
-  const float* kwr = kw + (u * s.nC + r) * s.Cp + p0;
-  const float* kmr = km + (u * s.nC + r) * s.Cp + p0;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const bf16_t* vs = v + (u * s.L + tok0 + p0) * d + nt * 256;
+  bf16_t* gr = grow + (u * s.Cp + p0) * d + nt * 256;
   bf16_t* gbase = gt + u * 2 * s.d * s.Cp + p0;
-  auto band = [&](auto MI, auto FULL) {
-    constexpr int mi = decltype(MI)::value;
-    constexpr bool full = decltype(FULL)::value;
-    // All loads of the band first (v as bf16, the kernels): grow may alias v
-    // as far as the compiler knows.  Rows past the valid tokens read row 0
-    // and use 0.  Then one piece per accumulator column block, kept apart by
-    // scheduling barriers.
-    bf16_t vb[4][16];
-    float kwv[16], kmv[16];
+  bf16_t* tW = reinterpret_cast<bf16_t*>(smem_raw + E::TW);
+  bf16_t* tM = reinterpret_cast<bf16_t*>(smem_raw + E::TM);
+  const float* kws = reinterpret_cast<const float*>(smem_raw + E::KS);
+  const float* kms = kws + 256;
+  // Band mi's v rows into G: wave w loads row pairs w, w+4, ..., w+28 (lane
+  // l: row 2k + l/32, bytes 16*(l%32)); rows past the valid tokens read zeros.
+  auto load_v = [&](int mi, char* G) {
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int vv = 0; vv < 16; ++vv) {
-        const int pr = ps.row(mi, vv);
-        vb[ni][vv] = vs[(full || pr < nvt ? pr : 0) * d + ps.col(ni)];
-      }
-#pragma unroll
-    for (int vv = 0; vv < 16; ++vv) {
-      kwv[vv] = kwr[ps.row(mi, vv)];
-      kmv[vv] = kmr[ps.row(mi, vv)];
+    for (int i = 0; i < 8; ++i) {
+      const int k = 4 * i + wave;
+      const int tr = trow(mi, 2 * k + (lane >> 5));
+      const bf16_t* src = (tr < nvt ? vs + tr * d : kZeroRow256) + 8 * (lane & 31);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
+                                       (__attribute__((address_space(3))) void*)(G + k * E::PAIR),
+                                       16, 0, 0);
     }
-    __syncthreads();  // the previous band has been copied out
+  };
+  __syncthreads();  // the main loop's stages are free
+  if (wave < 2) {   // K^W (wave 0), K^M (wave 1) of the tile's tokens: 1 KB each
+    const float* src = (wave == 0 ? kw : km) + (u * s.nC + r) * s.Cp + p0 + 4 * lane;
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
+                                     (__attribute__((address_space(3))) void*)(smem_raw + E::KS + 1024 * wave),
+                                     16, 0, 0);
+  }
+  load_v(0, smem_raw + E::G0);
+  auto band = [&](auto MI) {
+    constexpr int mi = decltype(MI)::value;
+    char* G = smem_raw + ((mi & 1) ? E::G1 : E::G0);
+    if constexpr (mi > 0) barrier_nofence();  // band mi-1's rows have been copied out
+    if constexpr (mi < 3) load_v(mi + 1, smem_raw + ((mi & 1) ? E::G0 : E::G1));
+    // Band mi's rows (and the kernels) have landed: after them this wave
+    // issued band mi-1's 24 stores and band mi+1's 8 loads.
+    wait_vmcnt<(mi > 0 ? 24 : 0) + (mi < 3 ? 8 : 0)>();
+    barrier_nofence();
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
       pin_acc(acc[mi][ni]);
+      const int c = ps.col(ni);
       float g[16];
 #pragma unroll
       for (int vv = 0; vv < 16; ++vv) {
-        const int pr = ps.row(mi, vv);
-        g[vv] = (full || pr < nvt ? bf2f(vb[ni][vv]) : 0.0f) - acc[mi][ni][vv];
-        gr[pr * d + ps.col(ni)] = f2bf(g[vv]);
+        bf16_t* e = reinterpret_cast<bf16_t*>(G + E::off(brow(vv), c));
+        g[vv] = bf2f(*e) - acc[mi][ni][vv];
+        *e = f2bf(g[vv]);
       }
-      const int c = ps.col(ni);
 #pragma unroll
       for (int vq = 0; vq < 4; ++vq) {
-        band_put(lds, c, ps, vq, kwv[4 * vq] * g[4 * vq], kwv[4 * vq + 1] * g[4 * vq + 1],
-                 kwv[4 * vq + 2] * g[4 * vq + 2], kwv[4 * vq + 3] * g[4 * vq + 3]);
-        band_put(ldsM, c, ps, vq, kmv[4 * vq] * g[4 * vq], kmv[4 * vq + 1] * g[4 * vq + 1],
-                 kmv[4 * vq + 2] * g[4 * vq + 2], kmv[4 * vq + 3] * g[4 * vq + 3]);
+        const int t0 = 128 * ps.wm + 32 * mi + 8 * vq + 4 * ps.hf;
+        const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(kws + t0);
+        const f32x4_t m4 = *reinterpret_cast<const f32x4_t*>(kms + t0);
+        band_put(tW, c, ps, vq, w4[0] * g[4 * vq], w4[1] * g[4 * vq + 1], w4[2] * g[4 * vq + 2],
+                 w4[3] * g[4 * vq + 3]);
+        band_put(tM, c, ps, vq, m4[0] * g[4 * vq], m4[1] * g[4 * vq + 1], m4[2] * g[4 * vq + 2],
+                 m4[3] * g[4 * vq + 3]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
-    band_copy(lds, 256, [&](int c) {
+    rows_out(mi, G, gr, 256);
+    band_copy(tW, 256, [&](int c) {
       const int64_t i = nt * 256 + c;
       return gbase + (64 * (i / 32) + i % 32) * s.Cp + 32 * mi;
     });
-    band_copy(ldsM, 256, [&](int c) {
+    band_copy(tM, 256, [&](int c) {
       const int64_t i = nt * 256 + c;
       return gbase + (64 * (i / 32) + 32 + i % 32) * s.Cp + 32 * mi;
     });
   };
-  if (nvt == 256) for_bands([&](auto MI) { band(MI, Flag<true>{}); });
-  else for_bands([&](auto MI) { band(MI, Flag<false>{}); });
+  for_bands(band);
 }
 
 // ---------------------------------------------------------------------------

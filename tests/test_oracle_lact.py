@@ -28,7 +28,16 @@ import torch
 import oracle
 from closed_form_np import learner_forward
 
-torch.set_default_dtype(torch.float64)
+
+
+@pytest.fixture(autouse=True)
+def _float64_default():
+    """torch's default dtype is float64 inside this module's tests only (set
+    at import it would leak into every module collected after this one)."""
+    prev = torch.get_default_dtype()
+    torch.set_default_dtype(torch.float64)
+    yield
+    torch.set_default_dtype(prev)
 
 
 def _problem(rng, kind, L, d, h, m0=True):

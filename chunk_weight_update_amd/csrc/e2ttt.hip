@@ -303,10 +303,12 @@ void set_lds_attributes() {
       reinterpret_cast<const void*>(&k_lin_bwd_tok<3>), reinterpret_cast<const void*>(&k_lin_bwd_tok<4>)};
   for (const void* f : fused_kernels)
     (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_heads<float>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_heads<bf16_t>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  const void* heads_kernels[] = {
+      reinterpret_cast<const void*>(&k_heads<float, 3>), reinterpret_cast<const void*>(&k_heads<float, 6>),
+      reinterpret_cast<const void*>(&k_heads<float, 12>), reinterpret_cast<const void*>(&k_heads<bf16_t, 3>),
+      reinterpret_cast<const void*>(&k_heads<bf16_t, 6>), reinterpret_cast<const void*>(&k_heads<bf16_t, 12>)};
+  for (const void* f : heads_kernels)
+    (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   g_attr_done.store(1, std::memory_order_release);
 }
 
@@ -851,7 +853,7 @@ e2ttt_status e2ttt_scalar_heads(const e2ttt_problem* prob, const void* x, int64_
   const int64_t B = prob->batch, H = prob->heads, L = prob->seq_len, D = model_dim;
   if (D < 64 || D % 64 != 0 || D > 65536 || H > 64) return E2TTT_EUNSUPPORTED;
   int64_t N;
-  if (!mul_ok(B, L, &N) || N / HeadsCfg<float>::ROWS >= (int64_t(1) << 31))
+  if (!mul_ok(B, L, &N) || N / kHeadsRows >= (int64_t(1) << 31))
     return E2TTT_EUNSUPPORTED;
   if (L == 0) return E2TTT_OK;
   if (!x || !w_heads || !b_heads || !eta || !alpha || !beta) return E2TTT_EINVAL;
@@ -880,11 +882,27 @@ e2ttt_status e2ttt_scalar_heads(const e2ttt_problem* prob, const void* x, int64_
   ha.eta_base = eta_base; ha.alpha_base = alpha_base;
   ha.eta = eta; ha.alpha = alpha; ha.beta = beta;
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  const unsigned grid = grid1((N + HeadsCfg<float>::ROWS - 1) / HeadsCfg<float>::ROWS);
-  if (prob->io_dtype == E2TTT_BF16)
-    hipLaunchKernelGGL(k_heads<bf16_t>, dim3(grid), dim3(256), HeadsCfg<bf16_t>::LDS_BYTES, hs, ha);
-  else
-    hipLaunchKernelGGL(k_heads<float>, dim3(grid), dim3(256), HeadsCfg<float>::LDS_BYTES, hs, ha);
+  const unsigned grid = grid1((N + kHeadsRows - 1) / kHeadsRows);
+  const int nb = static_cast<int>((3 * H + 15) / 16);
+  auto launch = [&](auto tag, auto nbt) {
+    typedef decltype(tag) T;
+    constexpr int NBT = decltype(nbt)::value;
+    void (*f)(HeadsArgs) = k_heads<T, NBT>;
+    constexpr size_t lds = HeadsCfg<T, NBT>::LDS_BYTES;
+    hipLaunchKernelGGL(f, dim3(grid), dim3(256), lds, hs, ha);
+  };
+  using I3 = std::integral_constant<int, 3>;
+  using I6 = std::integral_constant<int, 6>;
+  using I12 = std::integral_constant<int, 12>;
+  if (prob->io_dtype == E2TTT_BF16) {
+    if (nb <= 3) launch(bf16_t{}, I3{});
+    else if (nb <= 6) launch(bf16_t{}, I6{});
+    else launch(bf16_t{}, I12{});
+  } else {
+    if (nb <= 3) launch(float{}, I3{});
+    else if (nb <= 6) launch(float{}, I6{});
+    else launch(float{}, I12{});
+  }
   return hipGetLastError() == hipSuccess ? E2TTT_OK : E2TTT_EHIP;
 }
 

@@ -688,10 +688,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   constexpr int NST = Bwd256::NST, SB = Bwd256::STAGE, NL = Bwd256::LOADS;
   const int64_t ntn = s.h / Bwd256::BN, ntm = s.Cp / Bwd256::BM;
-  int64_t bid = xcd_logical_block();  // the hidden tiles of a token block share one L2
-  const int64_t nt = bid % ntn; bid /= ntn;
-  const int64_t mt = bid % ntm;
-  const int64_t u = bid / ntm;
+  // XCD-aware numbering, then groups of 4 token blocks x all hidden tiles
+  // with the token block fastest: the 32 workgroups an XCD runs at a time
+  // share 4 token panels and 8 weight panels in its L2 (measured 2% faster
+  // than hidden tiles fastest, whose 24 weight panels per token block do not
+  // stay in L2).
+  int64_t bid = xcd_logical_block();
+  const int64_t GT = ntm % 4 == 0 ? 4 : 1;
+  const int64_t u = bid / (ntm * ntn);
+  bid %= ntm * ntn;
+  const int64_t wi = bid % (GT * ntn);
+  const int64_t nt = wi / GT;
+  const int64_t mt = bid / (GT * ntn) * GT + wi % GT;
   const int64_t p0 = mt * Bwd256::BM, j0 = nt * Bwd256::BN;
   const int64_t tok0 = static_cast<int64_t>(r) * s.C;
   const int64_t nv = n_valid(s, r);

@@ -17,9 +17,9 @@
 //   k_dec_fwd13 : a1 = W1 x, a3 = W3 x, z = silu(a1) a3 for x = q and x = k
 //   k_dec_fwd2  : y = W2 z; out = y(q); g = v - y(k)
 //   k_dec_bwd   : partial dz = W2^T g per block of 64 rows of W2
-//   k_dec_dact  : dz (partials added in block order); dA3 = dz silu(a1),
-//                 dA1 = dz a3 silu'(a1)
-//   k_dec_stash : k, z(k), dA1, dA3, g and the scalars into the chunk slot
+//   k_dec_stash : dz (partials added in block order); dA3 = dz silu(a1),
+//                 dA1 = dz a3 silu'(a1); k, z(k), dA1, dA3, g and the
+//                 scalars into the chunk slot
 // Linear learner (f(x) = W x): k_dec_lin_fwd (y, out, g) and k_dec_stash.
 // At the chunk end: the scan over the buffered scalars, k_dec_pack (the
 // scaled aggregation operands, feature-major) and the chunk forward's fp32
@@ -35,10 +35,8 @@ struct DecodeArgs {
   const float* W0;    // [BH][P] chunk-start weights
   float* zq;          // workspace [BH][h]: z of the query
   float* zk;          // [BH][h]: z of the key
-  float* a1k;         // [BH][h]
+  float* a1k;         // [BH][h]: the key's pre-activations
   float* a3k;         // [BH][h]
-  float* dA1;         // [BH][h]
-  float* dA3;         // [BH][h]
   float* g;           // [BH][d]: v - f_{W_0}(k)
 };
 
@@ -74,70 +72,76 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // Rows of a [rows][n] fp32 matrix dotted with lane-strided vectors: lane l
-// holds x[l + 64 m] (m < n/64, n % 64 == 0).  R rows per wave, all loads of
-// the wave issued before any reduction.
-template <int R, int NX, int MAXM>
+// holds x[l + 64 m] (m < M; zero for l + 64 m >= n, n % 64 == 0, n <= 64 M).
+// Every load of the wave is issued before any product, unconditionally: the
+// chunks past n read a clamped in-range element, which meets x = 0.  (A load
+// under a runtime condition makes the compiler wait for each one in turn.)
+template <int R, int NX, int M>
 __device__ __forceinline__ void wave_dots(const float* const (&rows)[R], int64_t n,
-                                          const float (&x)[NX][MAXM], float (&out)[R][NX]) {
+                                          const float (&x)[NX][M], float (&out)[R][NX]) {
   const int lane = threadIdx.x & 63;
-  const int nm = static_cast<int>(n / 64);
+  float w[M][R];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int64_t e0 = lane + 64 * m;
+    const int64_t e = e0 < n ? e0 : n - 1;
+#pragma unroll
+    for (int r = 0; r < R; ++r) w[m][r] = rows[r][e];
+  }
   float acc[R][NX];
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int c = 0; c < NX; ++c) acc[r][c] = 0.0f;
 #pragma unroll
-  for (int m = 0; m < MAXM; ++m) {
-    if (m < nm) {
-      float w[R];
+  for (int m = 0; m < M; ++m)
 #pragma unroll
-      for (int r = 0; r < R; ++r) w[r] = rows[r][lane + 64 * m];
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int c = 0; c < NX; ++c) acc[r][c] = fmaf(w[r], x[c][m], acc[r][c]);
-    }
-  }
+      for (int c = 0; c < NX; ++c) acc[r][c] = fmaf(w[m][r], x[c][m], acc[r][c]);
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int c = 0; c < NX; ++c) out[r][c] = wave_sum(acc[r][c]);
 }
 
-// W1 and W3 rows of 4 hidden units per wave (16 per workgroup) dotted with q
-// and k.  Grid BH * (h / 16); d <= 1024.
-template <typename T>
+// Smallest of 2, 4, 8, ... >= n / 64: the chunk count a wave_dots instance
+// covers.
+__host__ __device__ inline int dot_chunks(int64_t n) {
+  int m = 2;
+  while (64 * static_cast<int64_t>(m) < n) m *= 2;
+  return m;
+}
+
+// W1 and W3 rows of 2 hidden units per wave (8 per workgroup) dotted with q
+// and k.  Grid BH * (h / 8); d <= 64 M.
+template <typename T, int M>
 __global__ __launch_bounds__(256) void k_dec_fwd13(DecodeArgs a, const T* __restrict__ q,
                                                    const T* __restrict__ k) {
-  const int64_t nb = a.h / 16, u = blockIdx.x / nb, ib = blockIdx.x % nb;
+  const int64_t nb = a.h / 8, u = blockIdx.x / nb, ib = blockIdx.x % nb;
   const int64_t d = a.d, h = a.h;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float x[2][16];
+  float x[2][M];
 #pragma unroll
-  for (int m = 0; m < 16; ++m) {
+  for (int m = 0; m < M; ++m) {
     const int64_t e = lane + 64 * m;
     x[0][m] = e < d ? to_f32<T>(q[u * d + e]) : 0.0f;
     x[1][m] = e < d ? to_f32<T>(k[u * d + e]) : 0.0f;
   }
   const float* Wu = a.W0 + u * 3 * d * h;
-  const int64_t i0 = ib * 16 + wave * 4;
-  const float* rows[8];
+  const int64_t i0 = ib * 8 + wave * 2;
+  const float* rows[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  for (int r = 0; r < 2; ++r) {
     rows[r] = Wu + (i0 + r) * d;              // W1
-    rows[4 + r] = Wu + h * d + (i0 + r) * d;  // W3
+    rows[2 + r] = Wu + h * d + (i0 + r) * d;  // W3
   }
-  float s[8][2];
-  wave_dots<8, 2, 16>(rows, d, x, s);
-  if (lane < 4) {
-    const int r = lane;
-    float s1q = s[0][0], s3q = s[4][0], s1k = s[0][1], s3k = s[4][1];
-#pragma unroll
-    for (int rr = 1; rr < 4; ++rr)
-      if (r == rr) {
-        s1q = s[rr][0]; s3q = s[4 + rr][0]; s1k = s[rr][1]; s3k = s[4 + rr][1];
-      }
-    const int64_t i = u * h + i0 + r;
+  float s[4][2];
+  wave_dots<4, 2, M>(rows, d, x, s);
+  if (lane < 2) {
+    const float s1q = lane ? s[1][0] : s[0][0], s3q = lane ? s[3][0] : s[2][0];
+    const float s1k = lane ? s[1][1] : s[0][1], s3k = lane ? s[3][1] : s[2][1];
+    const int64_t i = u * h + i0 + lane;
     a.zq[i] = s1q * sigmoidf_(s1q) * s3q;
     a.zk[i] = s1k * sigmoidf_(s1k) * s3k;
     a.a1k[i] = s1k;
@@ -145,39 +149,30 @@ __global__ __launch_bounds__(256) void k_dec_fwd13(DecodeArgs a, const T* __rest
   }
 }
 
-// W2 rows of 4 outputs per wave (16 per workgroup): y = W2 z for both z; the
-// readout and the residual g.  Grid BH * (d / 16); h <= 4096.
-template <typename T>
+// One W2 row per wave (4 per workgroup): y = W2 z for both z; the readout
+// and the residual g.  Grid BH * (d / 4); h <= 64 M.
+template <typename T, int M>
 __global__ __launch_bounds__(256) void k_dec_fwd2(DecodeArgs a, const T* __restrict__ v,
                                                   T* __restrict__ out) {
-  const int64_t nb = a.d / 16, u = blockIdx.x / nb, jb = blockIdx.x % nb;
+  const int64_t nb = a.d / 4, u = blockIdx.x / nb, jb = blockIdx.x % nb;
   const int64_t d = a.d, h = a.h;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float z[2][64];
+  float z[2][M];
 #pragma unroll
-  for (int m = 0; m < 64; ++m) {
-    const int64_t e = lane + 64 * m;
-    z[0][m] = e < h ? a.zq[u * h + e] : 0.0f;
-    z[1][m] = e < h ? a.zk[u * h + e] : 0.0f;
+  for (int m = 0; m < M; ++m) {
+    const int64_t e0 = lane + 64 * m;
+    const int64_t e = e0 < h ? e0 : h - 1;
+    const float zq = a.zq[u * h + e], zk = a.zk[u * h + e];
+    z[0][m] = e0 < h ? zq : 0.0f;
+    z[1][m] = e0 < h ? zk : 0.0f;
   }
-  const float* W2 = a.W0 + u * 3 * d * h + 2 * h * d;
-  const int64_t j0 = jb * 16 + wave * 4;
-  const float* rows[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) rows[r] = W2 + (j0 + r) * h;
-  float y[4][2];
-  wave_dots<4, 2, 64>(rows, h, z, y);
-  if (lane < 4) {
-    float yq = y[0][0], yk = y[0][1];
-#pragma unroll
-    for (int rr = 1; rr < 4; ++rr)
-      if (lane == rr) {
-        yq = y[rr][0];
-        yk = y[rr][1];
-      }
-    const int64_t j = u * d + j0 + lane;
-    out[j] = from_f32<T>(yq);
-    a.g[j] = to_f32<T>(v[j]) - yk;
+  const int64_t j = jb * 4 + wave;
+  const float* rows[1] = {a.W0 + u * 3 * d * h + 2 * h * d + j * h};
+  float y[1][2];
+  wave_dots<1, 2, M>(rows, h, z, y);
+  if (lane == 0) {
+    out[u * d + j] = from_f32<T>(y[0][0]);
+    a.g[u * d + j] = to_f32<T>(v[u * d + j]) - y[0][1];
   }
 }
 
@@ -207,20 +202,6 @@ __global__ __launch_bounds__(256) void k_dec_bwd(DecodeArgs a, float* __restrict
   if (wave == 0)
     part[(jb * a.BH + u) * h + ib * 64 + lane] =
         ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
-}
-
-// dz from the d/64 partials (in block order), then dA1, dA3.  Grid
-// ceil(BH * h / 256).
-__global__ __launch_bounds__(256) void k_dec_dact(DecodeArgs a, const float* __restrict__ part) {
-  const int64_t n = a.BH * a.h;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= n) return;
-  float dz = part[i];
-  for (int64_t jb = 1; jb < a.d / 64; ++jb) dz += part[jb * n + i];
-  const float a1 = a.a1k[i], a3 = a.a3k[i];
-  const float sg = sigmoidf_(a1);
-  a.dA3[i] = dz * (a1 * sg);
-  a.dA1[i] = dz * a3 * (sg * (1.0f + a1 * (1.0f - sg)));
 }
 
 // Linear learner: y = W x for q and k, 4 waves over the d rows of one unit.
@@ -256,14 +237,17 @@ __global__ __launch_bounds__(256) void k_dec_lin_fwd(DecodeArgs a, const T* __re
 }
 
 // Token `pos` of the chunk into the buffer: the scalars, and (SwiGLU) k,
-// z(k), dA1, dA3, g feature-major, or (linear) k, g token-major.  One block
-// per (unit, group of 256 entries); grid BH * ceil((3 + 3h + 2d) / 256).
+// z(k), dA1, dA3, g feature-major, or (linear) k, g token-major.  dA1, dA3
+// come from dz, the d/64 partials of k_dec_bwd added in block order, and the
+// key's pre-activations: dA3 = dz silu(a1), dA1 = dz a3 silu'(a1).  One
+// block per (unit, group of 256 entries); grid BH * ceil((3 + 3h + 2d) / 256).
 template <typename T>
 __global__ __launch_bounds__(256) void k_dec_stash(DecodeArgs a, DecodeBuf b, int64_t pos,
                                                    const T* __restrict__ k,
                                                    const float* __restrict__ eta,
                                                    const float* __restrict__ alpha,
-                                                   const float* __restrict__ beta) {
+                                                   const float* __restrict__ beta,
+                                                   const float* __restrict__ part) {
   const int64_t d = a.d, h = a.h, cb = b.cb;
   const int64_t per = 3 + 3 * h + 2 * d;
   const int64_t nblk = (per + 255) / 256;
@@ -287,9 +271,25 @@ __global__ __launch_bounds__(256) void k_dec_stash(DecodeArgs a, DecodeBuf b, in
   if (x < d) { b.gb[(u * d + x) * cb + pos] = a.g[u * d + x]; return; }
   x -= d;
   const int64_t which = x / h, j = x % h;  // 0: z, 1: dA1, 2: dA3
-  const float* src = which == 0 ? a.zk : which == 1 ? a.dA1 : a.dA3;
-  float* dst = which == 0 ? b.zt : which == 1 ? b.d1 : b.d3;
-  dst[(u * h + j) * cb + pos] = src[u * h + j];
+  const int64_t i = u * h + j;
+  if (which == 0) {
+    b.zt[i * cb + pos] = a.zk[i];
+    return;
+  }
+  // dz: the partials in block order, loaded four at a time.
+  const int64_t n = a.BH * h, nj = d / 64;
+  float dz = part[i];
+  int64_t jb = 1;
+  for (; jb + 4 <= nj; jb += 4) {
+    const float p0 = part[jb * n + i], p1 = part[(jb + 1) * n + i];
+    const float p2 = part[(jb + 2) * n + i], p3 = part[(jb + 3) * n + i];
+    dz = (((dz + p0) + p1) + p2) + p3;
+  }
+  for (; jb < nj; ++jb) dz += part[jb * n + i];
+  const float a1 = a.a1k[i], a3 = a.a3k[i];
+  const float sg = sigmoidf_(a1);
+  if (which == 1) b.d1[i * cb + pos] = dz * a3 * (sg * (1.0f + a1 * (1.0f - sg)));
+  else b.d3[i * cb + pos] = dz * (a1 * sg);
 }
 
 // Chunk end, SwiGLU: the scaled aggregation operands of the n buffered tokens

@@ -963,8 +963,8 @@ e2ttt_status e2ttt_scalar_kernels(const e2ttt_problem* prob, const float* eta,
 
 namespace {
 
-// Decode workspace: the per-token scratch (z of q and k, a1, a3, dA1, dA3 of
-// k [BH][h]; g [BH][d]; the W2^T g partials [d/64][BH][h]), then the chunk
+// Decode workspace: the per-token scratch (z of q and k, a1, a3 of k
+// [BH][h]; g [BH][d]; the W2^T g partials [d/64][BH][h]), then the chunk
 // buffer of the buffered tokens and the chunk-end operands (DecodeBuf), then,
 // with the q/k prologue, the normalised q and k of the token.  All fp32
 // except those two (io dtype); sub-buffers 256-byte aligned.
@@ -983,7 +983,7 @@ DecodeLayout decode_layout(const e2ttt_problem* p) {
   L.cb = L.h == 0 ? (L.C + 63) / 64 * 64 : (L.C + 127) / 128 * 128;
   const size_t BH = static_cast<size_t>(L.BH), d = static_cast<size_t>(L.d),
                h = static_cast<size_t>(L.h), cb = static_cast<size_t>(L.cb);
-  size_t o = align256(4 * BH * (6 * h + d + (d / 64) * h));
+  size_t o = align256(4 * BH * (4 * h + d + (d / 64) * h));  // zq, zk, a1k, a3k, g, dz partials
   auto take = [&](size_t bytes) { const size_t at = o; o = align256(o + bytes); return at; };
   L.eb = take(4 * BH * cb);
   L.ab = take(4 * BH * cb);
@@ -1079,7 +1079,7 @@ e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* q, const v
   a.BH = BH; a.d = d; a.h = h;
   a.W0 = W;
   a.zq = ws; a.zk = ws + BH * h; a.a1k = ws + 2 * BH * h; a.a3k = ws + 3 * BH * h;
-  a.dA1 = ws + 4 * BH * h; a.dA3 = ws + 5 * BH * h; a.g = ws + 6 * BH * h;
+  a.g = ws + 4 * BH * h;
   DecodeBuf b;
   b.cb = cb;
   b.eb = F(Lw.eb); b.ab = F(Lw.ab); b.bb = F(Lw.bb);
@@ -1102,20 +1102,27 @@ e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* q, const v
     const T* V = static_cast<const T*>(v);
     T* O = static_cast<T*>(out);
     // The token: readout and descent factors at the chunk-start weights.
+    float* part = ws + 4 * BH * h + BH * d;  // k_dec_bwd's partials of dz
     if (h == 0) {
       hipLaunchKernelGGL(k_dec_lin_fwd<T>, dim3(grid1(BH)), dim3(256), 0, s, a, Q, K, V, O);
     } else {
-      float* part = ws + 6 * BH * h + BH * d;
-      hipLaunchKernelGGL(k_dec_fwd13<T>, dim3(grid1(BH * (h / 16))), dim3(256), 0, s, a, Q, K);
-      hipLaunchKernelGGL(k_dec_fwd2<T>, dim3(grid1(BH * (d / 16))), dim3(256), 0, s, a, V, O);
+      // (d <= 1024, h <= 4096: the dot products take 2 .. 16 and 2 .. 64
+      // chunks of 64 per lane)
+      const int md = dot_chunks(d), mh = dot_chunks(h);
+      void (*f13)(DecodeArgs, const T*, const T*) =
+          md <= 2 ? k_dec_fwd13<T, 2> : md <= 4 ? k_dec_fwd13<T, 4>
+          : md <= 8 ? k_dec_fwd13<T, 8> : k_dec_fwd13<T, 16>;
+      void (*f2)(DecodeArgs, const T*, T*) =
+          mh <= 2 ? k_dec_fwd2<T, 2> : mh <= 4 ? k_dec_fwd2<T, 4> : mh <= 8 ? k_dec_fwd2<T, 8>
+          : mh <= 16 ? k_dec_fwd2<T, 16> : mh <= 32 ? k_dec_fwd2<T, 32> : k_dec_fwd2<T, 64>;
+      hipLaunchKernelGGL(f13, dim3(grid1(BH * (h / 8))), dim3(256), 0, s, a, Q, K);
+      hipLaunchKernelGGL(f2, dim3(grid1(BH * (d / 4))), dim3(256), 0, s, a, V, O);
       hipLaunchKernelGGL(k_dec_bwd, dim3(grid1(BH * (h / 64) * (d / 64))), dim3(256), 0, s, a,
                          part);
-      hipLaunchKernelGGL(k_dec_dact, dim3(grid1((BH * h + 255) / 256)), dim3(256), 0, s, a,
-                         static_cast<const float*>(part));
     }
     const int64_t nblk = (3 + 3 * h + 2 * d + 255) / 256;
     hipLaunchKernelGGL(k_dec_stash<T>, dim3(grid1(BH * nblk)), dim3(256), 0, s, a, b, pos, K,
-                       eta, alpha, beta);
+                       eta, alpha, beta, static_cast<const float*>(part));
     if (!chunk_end) return;
     // Chunk end: the scalar kernels of the buffered tokens, the weighted
     // aggregations, (W, M) <- (W_C, M_C).

@@ -13,7 +13,10 @@
 // B.5 notes that this per-chunk bookkeeping is amortised over the chunk's
 // tokens).
 //
-// Per token and unit (SwiGLU, f(x) = W2 (silu(W1 x) * W3 x)):
+// Per token and unit (SwiGLU, f(x) = W2 (silu(W1 x) * W3 x); the MLP learner
+// f(x) = W2 silu(W1 x) on the same kernels with a3 = 1 and dA3 = 0, its
+// [W1 | W2] state read in place and, at a chunk end, updated through the
+// [W1 | W3 = 0 | W2] layout of the aggregation):
 //   k_dec_fwd13 : a1 = W1 x, a3 = W3 x, z = silu(a1) a3 for x = q and x = k
 //   k_dec_fwd2  : y = W2 z; out = y(q); g = v - y(k)
 //   k_dec_bwd   : partial dz = W2^T g per block of 64 rows of W2
@@ -32,6 +35,8 @@ namespace e2ttt {
 
 struct DecodeArgs {
   int64_t BH, d, h;   // h = 0 for the linear learner
+  int64_t P;          // state entries per unit: [W1 | W3 | W2] 3dh, the MLP's [W1 | W2] 2dh
+  int gated;          // 0 for the MLP learner: no W3, a3 = 1, dA3 = 0
   const float* W0;    // [BH][P] chunk-start weights
   float* zq;          // workspace [BH][h]: z of the query
   float* zk;          // [BH][h]: z of the key
@@ -114,7 +119,7 @@ __host__ __device__ inline int dot_chunks(int64_t n) {
 }
 
 // W1 and W3 rows of 2 hidden units per wave (8 per workgroup) dotted with q
-// and k.  Grid BH * (h / 8); d <= 64 M.
+// and k (the MLP learner: W1 only, a3 = 1).  Grid BH * (h / 8); d <= 64 M.
 template <typename T, int M>
 __global__ __launch_bounds__(256) void k_dec_fwd13(DecodeArgs a, const T* __restrict__ q,
                                                    const T* __restrict__ k) {
@@ -128,19 +133,20 @@ __global__ __launch_bounds__(256) void k_dec_fwd13(DecodeArgs a, const T* __rest
     x[0][m] = e < d ? to_f32<T>(q[u * d + e]) : 0.0f;
     x[1][m] = e < d ? to_f32<T>(k[u * d + e]) : 0.0f;
   }
-  const float* Wu = a.W0 + u * 3 * d * h;
+  const float* Wu = a.W0 + u * a.P;
   const int64_t i0 = ib * 8 + wave * 2;
   const float* rows[4];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    rows[r] = Wu + (i0 + r) * d;              // W1
-    rows[2 + r] = Wu + h * d + (i0 + r) * d;  // W3
+    rows[r] = Wu + (i0 + r) * d;                                // W1
+    rows[2 + r] = a.gated ? Wu + h * d + (i0 + r) * d : rows[r];  // W3 (MLP: unused)
   }
   float s[4][2];
   wave_dots<4, 2, M>(rows, d, x, s);
   if (lane < 2) {
-    const float s1q = lane ? s[1][0] : s[0][0], s3q = lane ? s[3][0] : s[2][0];
-    const float s1k = lane ? s[1][1] : s[0][1], s3k = lane ? s[3][1] : s[2][1];
+    const float s1q = lane ? s[1][0] : s[0][0], s1k = lane ? s[1][1] : s[0][1];
+    const float s3q = a.gated ? (lane ? s[3][0] : s[2][0]) : 1.0f;
+    const float s3k = a.gated ? (lane ? s[3][1] : s[2][1]) : 1.0f;
     const int64_t i = u * h + i0 + lane;
     a.zq[i] = s1q * sigmoidf_(s1q) * s3q;
     a.zk[i] = s1k * sigmoidf_(s1k) * s3k;
@@ -167,7 +173,7 @@ __global__ __launch_bounds__(256) void k_dec_fwd2(DecodeArgs a, const T* __restr
     z[1][m] = e0 < h ? zk : 0.0f;
   }
   const int64_t j = jb * 4 + wave;
-  const float* rows[1] = {a.W0 + u * 3 * d * h + 2 * h * d + j * h};
+  const float* rows[1] = {a.W0 + u * a.P + (a.P - h * d) + j * h};  // W2 row j
   float y[1][2];
   wave_dots<1, 2, M>(rows, h, z, y);
   if (lane == 0) {
@@ -186,7 +192,7 @@ __global__ __launch_bounds__(256) void k_dec_bwd(DecodeArgs a, float* __restrict
   const int64_t ib = rest % nib, u = rest / nib;
   const int64_t d = a.d, h = a.h;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const float* W2 = a.W0 + u * 3 * d * h + 2 * h * d + ib * 64 + lane;
+  const float* W2 = a.W0 + u * a.P + (a.P - h * d) + ib * 64 + lane;
   const int64_t j0 = jb * 64 + wave * 16;
   float w[16], gv[16];
 #pragma unroll
@@ -289,7 +295,7 @@ __global__ __launch_bounds__(256) void k_dec_stash(DecodeArgs a, DecodeBuf b, in
   const float a1 = a.a1k[i], a3 = a.a3k[i];
   const float sg = sigmoidf_(a1);
   if (which == 1) b.d1[i * cb + pos] = dz * a3 * (sg * (1.0f + a1 * (1.0f - sg)));
-  else b.d3[i * cb + pos] = dz * (a1 * sg);
+  else b.d3[i * cb + pos] = a.gated ? dz * (a1 * sg) : 0.0f;
 }
 
 // Chunk end, SwiGLU: the scaled aggregation operands of the n buffered tokens

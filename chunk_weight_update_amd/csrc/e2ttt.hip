@@ -970,7 +970,8 @@ namespace {
 // except those two (io dtype); sub-buffers 256-byte aligned.
 struct DecodeLayout {
   int64_t BH, d, h, C, cb;
-  size_t eb, ab, bb, kt, zt, d1, d3, gb, kb, gl, kw, km, coef, ut, gt, gw, gm, qn, kn, total;
+  size_t eb, ab, bb, kt, zt, d1, d3, gb, kb, gl, kw, km, coef, ut, gt, gw, gm, wx, mx, qn, kn,
+      total;
 };
 
 DecodeLayout decode_layout(const e2ttt_problem* p) {
@@ -1005,6 +1006,10 @@ DecodeLayout decode_layout(const e2ttt_problem* p) {
   L.kw = take(4 * BH * cb);
   L.km = take(4 * BH * cb);
   L.coef = take(4 * BH * 4);
+  if (p->kind == E2TTT_MLP) {  // the state in the aggregation's layout at a chunk end
+    L.wx = take(4 * BH * 3 * d * h);
+    L.mx = take(4 * BH * 3 * d * h);
+  }
   if (p->flags & E2TTT_FLAG_QK_SILU_L2) {
     const size_t nx = BH * d * (p->io_dtype == E2TTT_BF16 ? 2 : 4);
     L.qn = take(nx);
@@ -1017,9 +1022,6 @@ DecodeLayout decode_layout(const e2ttt_problem* p) {
 e2ttt_status decode_check(const e2ttt_problem* prob) {
   const e2ttt_status st = check_problem(prob);
   if (st != E2TTT_OK) return st;
-  if (prob->flags & (E2TTT_FLAG_CHUNK_AVERAGED_DECAY | E2TTT_FLAG_LACT_RULE))
-    return E2TTT_EUNSUPPORTED;
-  if (prob->kind == E2TTT_MLP) return E2TTT_EUNSUPPORTED;
   if (prob->kind == E2TTT_LINEAR && prob->dim > 128) return E2TTT_EUNSUPPORTED;
   return E2TTT_OK;
 }
@@ -1045,7 +1047,7 @@ e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* q, const v
   if (st != E2TTT_OK) return st;
   const DecodeLayout Lw = decode_layout(prob);
   const int64_t BH = Lw.BH, d = Lw.d, h = Lw.h, cb = Lw.cb;
-  const int64_t P = h == 0 ? d * d : 3 * d * h;
+  const int64_t P = h == 0 ? d * d : (prob->kind == E2TTT_MLP ? 2 : 3) * d * h;
   if (pos < 0 || pos >= prob->chunk) return E2TTT_EINVAL;
   if (pos == prob->chunk - 1 && !chunk_end) return E2TTT_EINVAL;  // the last slot ends the chunk
   if (!q || !k || !v || !eta || !alpha || !beta || !W || !M || !out || !workspace)
@@ -1077,6 +1079,8 @@ e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* q, const v
   auto F = [&](size_t off) { return off ? reinterpret_cast<float*>(wb + off) : nullptr; };
   DecodeArgs a;
   a.BH = BH; a.d = d; a.h = h;
+  a.P = P;
+  a.gated = prob->kind == E2TTT_MLP ? 0 : 1;
   a.W0 = W;
   a.zq = ws; a.zk = ws + BH * h; a.a1k = ws + 2 * BH * h; a.a3k = ws + 3 * BH * h;
   a.g = ws + 4 * BH * h;
@@ -1129,7 +1133,11 @@ e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* q, const v
     const int64_t n = pos + 1;
     ScanArgs sa;
     sa.eta = b.eb; sa.alpha = b.ab; sa.beta = b.bb;
-    sa.L = n; sa.C = n; sa.nC = 1; sa.mode = prob->decay_mode; sa.averaged = 0; sa.lact = 0;
+    // (the chunk-averaged variant and the LaCT rule differ from the default
+    // rule only in these kernels and coefficients: the buffered tokens' means)
+    sa.L = n; sa.C = n; sa.nC = 1; sa.mode = prob->decay_mode;
+    sa.averaged = (prob->flags & E2TTT_FLAG_CHUNK_AVERAGED_DECAY) ? 1 : 0;
+    sa.lact = (prob->flags & E2TTT_FLAG_LACT_RULE) ? 1 : 0;
     sa.kw = b.kw; sa.km = b.km; sa.ustride = cb; sa.rstride = 0; sa.pad = cb;
     sa.coef = b.coef; sa.cstride = 4; sa.istride = cb;
     const int tpt = scan_tpt(n);
@@ -1148,17 +1156,37 @@ e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* q, const v
     } else {
       hipLaunchKernelGGL(k_dec_pack, dim3(grid1(BH * (5 * h + 3 * d))), dim3(256), 0, s, a, b,
                          n);
+      // The MLP's [W1 | W2] state goes through the [W1 | W3 = 0 | W2] layout
+      // of the aggregation (its W3 aggregates are zero: dA3 = 0).
+      const bool mlp = prob->kind == E2TTT_MLP;
+      float* Ws = mlp ? F(Lw.wx) : W;
+      float* Ms = mlp ? F(Lw.mx) : M;
+      const unsigned gx = grid1((BH * 3 * d * h / 4 + 255) / 256);
+      if (mlp) {
+        hipLaunchKernelGGL(k_mlp_state, dim3(gx), dim3(256), 0, s, W, Ws, BH, d, h, 1);
+        hipLaunchKernelGGL(k_mlp_state, dim3(gx), dim3(256), 0, s, M, Ms, BH, d, h, 1);
+      }
       Shape sh{BH, cb, d, h, cb, cb, 1, 1};
       const int64_t na = (4 * h / 128) * (d / 128), nbk = (2 * d / 128) * (h / 128);
       hipLaunchKernelGGL(k_agg<float>, dim3(grid1(BH * (na + nbk))), dim3(256), 0, s, sh, 0, 1,
                          static_cast<const float*>(b.ut), static_cast<const float*>(b.kt),
                          static_cast<const float*>(b.gt), static_cast<const float*>(b.zt),
-                         static_cast<const float*>(b.coef), static_cast<const float*>(W),
-                         static_cast<const float*>(M), W, M, static_cast<float*>(nullptr),
+                         static_cast<const float*>(b.coef), static_cast<const float*>(Ws),
+                         static_cast<const float*>(Ms), Ws, Ms, static_cast<float*>(nullptr),
                          static_cast<float*>(nullptr), static_cast<float*>(nullptr));
+      if (prob->flags & E2TTT_FLAG_POST_CHUNK_ROW_L2) {
+        const int64_t rows = BH * (2 * h + d);
+        hipLaunchKernelGGL(k_row_l2norm, dim3(grid1((rows + 3) / 4)), dim3(256), 0, s, Ws, BH, d,
+                           h);
+      }
+      if (mlp) {
+        hipLaunchKernelGGL(k_mlp_state, dim3(gx), dim3(256), 0, s, Ws, W, BH, d, h, 0);
+        hipLaunchKernelGGL(k_mlp_state, dim3(gx), dim3(256), 0, s, Ms, M, BH, d, h, 0);
+      }
+      return;
     }
     if (prob->flags & E2TTT_FLAG_POST_CHUNK_ROW_L2) {
-      const int64_t rows = BH * (h == 0 ? d : 2 * h + d);
+      const int64_t rows = BH * d;
       hipLaunchKernelGGL(k_row_l2norm, dim3(grid1((rows + 3) / 4)), dim3(256), 0, s, W, BH, d, h);
     }
   };

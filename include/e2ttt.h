@@ -112,7 +112,8 @@ enum {
    * (after decay_mode) are replaced by their arithmetic means over the
    * chunk's tokens before the scalar kernels are formed; eta_t stays per
    * token.  Applies to e2ttt_chunk_forward, its timed twin,
-   * e2ttt_scalar_kernels and the backward, for every kind and dtype. */
+   * e2ttt_scalar_kernels, e2ttt_decode_step (the means over the buffered
+   * tokens at each chunk end) and the backward, for every kind and dtype. */
   E2TTT_FLAG_CHUNK_AVERAGED_DECAY = 2u,
   /* The TTT branch's input prologue ("Rethinking Expressivity and
    * Efficiency in Test-Time Training", §4 Overall Architecture): q and k are
@@ -149,9 +150,9 @@ enum {
    * description there (no momentum suffix product, no decay ratio sum).
    * Same kernels as the default rule, only the scalar kernels differ:
    * K^W = K^M = eta, (cW, cM, cWM) = (mean gamma, mean beta, mean beta).
-   * Applies to e2ttt_chunk_forward (and its twins) and e2ttt_scalar_kernels;
-   * EINVAL together with E2TTT_FLAG_CHUNK_AVERAGED_DECAY; EUNSUPPORTED for
-   * e2ttt_decode_step and the backward. */
+   * Applies to e2ttt_chunk_forward (and its twins), e2ttt_scalar_kernels and
+   * e2ttt_decode_step (the update at each chunk end); EINVAL together with
+   * E2TTT_FLAG_CHUNK_AVERAGED_DECAY; EUNSUPPORTED for the backward. */
   E2TTT_FLAG_LACT_RULE = 32u
 };
 
@@ -353,9 +354,11 @@ E2TTT_API const char* e2ttt_status_string(e2ttt_status status);
  * Shapes: q, k, v, out [B,H,d] io_dtype (this token); eta, alpha, beta [B,H]
  * fp32; W, M [B,H,P] fp32, updated in place at a chunk end.  Used from `prob`:
  * batch, heads, dim, hidden, chunk, kind, io_dtype, decay_mode and the flags
- * (seq_len must still validate).  E2TTT_FLAG_CHUNK_AVERAGED_DECAY,
- * E2TTT_FLAG_LACT_RULE and the MLP learner give EUNSUPPORTED; the weight
- * precision flags have no effect (fp32 throughout).  W, M, out and the
+ * (seq_len must still validate).  With E2TTT_FLAG_CHUNK_AVERAGED_DECAY or
+ * E2TTT_FLAG_LACT_RULE the chunk-end update takes the means over the
+ * buffered tokens, as the chunk forward does over a chunk's tokens.  The MLP
+ * learner gives EUNSUPPORTED; the weight precision flags have no effect
+ * (fp32 throughout).  W, M, out and the
  * workspace must not overlap one another or the inputs (EINVAL).  All tensor
  * pointers 16-byte aligned, the workspace 256-byte aligned with at least
  * e2ttt_decode_workspace_bytes() bytes (EWORKSPACE).  Asynchronous on

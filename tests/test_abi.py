@@ -227,10 +227,11 @@ def test_decode_host_checks():
     assert cwu.decode_workspace_bytes(swiglu(chunk=2 * C)) > n
     lin = linear()
     assert cwu.decode_workspace_bytes(lin) >= 4 * 4 * lin.dim * lin.chunk
+    assert cwu.decode_workspace_bytes(swiglu(flags=cwu.FLAG_CHUNK_AVERAGED_DECAY)) == n
+    assert cwu.decode_workspace_bytes(swiglu(flags=cwu.FLAG_LACT_RULE)) == n
     with pytest.raises(cwu.E2tttError):
-        cwu.decode_workspace_bytes(swiglu(flags=cwu.FLAG_CHUNK_AVERAGED_DECAY))
-    with pytest.raises(cwu.E2tttError):
-        cwu.decode_workspace_bytes(swiglu(flags=cwu.FLAG_LACT_RULE))
+        cwu.decode_workspace_bytes(swiglu(flags=cwu.FLAG_LACT_RULE |
+                                          cwu.FLAG_CHUNK_AVERAGED_DECAY))
     assert cwu.decode_workspace_bytes(swiglu(flags=cwu.FLAG_POST_CHUNK_ROW_L2)) == n
     step = cwu.lib().e2ttt_decode_step
     f = Fake()
@@ -392,11 +393,13 @@ def test_scalar_heads_checked_on_the_host():
 
 def test_mlp_learner_entry_points():
     """The MLP learner: its own (larger, SwiGLU-layout) forward workspace;
-    EUNSUPPORTED for the decode step and the backward."""
+    the decode step's workspace adds the state in that layout (for the
+    chunk-end update); EUNSUPPORTED for the backward."""
     assert cwu.workspace_bytes(swiglu(kind=cwu.MLP)) > cwu.workspace_bytes(
         swiglu(kind=cwu.MLP, seq_len=0))
-    with pytest.raises(cwu.E2tttError):
-        cwu.decode_workspace_bytes(swiglu(kind=cwu.MLP))
+    p = swiglu(kind=cwu.MLP)
+    assert cwu.decode_workspace_bytes(p) >= (cwu.decode_workspace_bytes(swiglu()) +
+                                             2 * 4 * p.batch * p.heads * 3 * p.dim * p.hidden)
     with pytest.raises(cwu.E2tttError):
         cwu.backward_workspace_bytes(swiglu(kind=cwu.MLP, io_dtype=cwu.F32))
 

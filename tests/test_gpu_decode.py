@@ -10,7 +10,7 @@ the states meet 1e-5 for both io types."""
 import numpy as np
 import pytest
 
-from chunk_weight_update_amd.inputs import BF16, F32, LINEAR, SWIGLU, make_inputs
+from chunk_weight_update_amd.inputs import BF16, F32, LINEAR, MLP, SWIGLU, make_inputs
 from gpu_util import log, problem_for, rel_fro, run_oracle, to_device
 
 pytestmark = pytest.mark.gpu
@@ -102,4 +102,57 @@ def test_decode_with_row_normalisation(kind, B, H, L, d, h, C, io, regime):
     e = (rel_fro(out, ro), rel_fro(W, rW), rel_fro(M, rM))
     log(f"  rel_fro out={e[0]:.3e} W={e[1]:.3e} M={e[2]:.3e}")
     t = TOL[io]
+    assert e[0] <= t[0] and e[1] <= t[1] and e[2] <= t[2], e
+
+
+@pytest.mark.parametrize("variant", ["averaged", "lact"])
+@pytest.mark.parametrize("kind,B,H,L,d,h,C,io,regime", [
+    (LINEAR, 1, 2, 40, 64, 0, 16, F32, "default"),          # ragged last chunk
+    (SWIGLU, 2, 2, 40, 128, 256, 16, BF16, "nearunit"),     # ragged
+    (SWIGLU, 1, 1, 24, 256, 512, 8, F32, "nearunit"),
+])
+def test_decode_variants(variant, kind, B, H, L, d, h, C, io, regime):
+    """The chunk-averaged variant and the LaCT rule change only the chunk-end
+    kernels and coefficients (means over the buffered tokens, the last chunk
+    ragged); token by token against the oracle's chunk forward with the same
+    option."""
+    import chunk_weight_update_amd as cwu
+    flag = cwu.FLAG_CHUNK_AVERAGED_DECAY if variant == "averaged" else cwu.FLAG_LACT_RULE
+    log(f"decode {variant} kind={kind} B={B} H={H} L={L} d={d} C={C} io={io}")
+    inp = make_inputs(kind, B, H, L, d, h, io, seed=17, regime=regime,
+                      m0_scale=1e-6 if regime == "nearunit" else 0.01)
+    prob = problem_for(kind, B, H, L, d, h, C, io, 0, flag)
+    out, W, M = run_decode(prob, to_device(inp, io), L, C, check_mid_chunk=True)
+    ro, rW, rM = run_oracle(kind, inp, C, h, averaged=variant == "averaged",
+                            lact=variant == "lact")
+    e = (rel_fro(out, ro), rel_fro(W, rW), rel_fro(M, rM))
+    log(f"  rel_fro out={e[0]:.3e} W={e[1]:.3e} M={e[2]:.3e}")
+    t = TOL[io]
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(W)) and np.all(np.isfinite(M))
+    assert e[0] <= t[0] and e[1] <= t[1] and e[2] <= t[2], e
+
+
+@pytest.mark.parametrize("kind,B,H,L,d,h,C,io,flags", [
+    (MLP, 1, 2, 48, 128, 256, 16, F32, 0),
+    (MLP, 2, 2, 40, 128, 256, 16, BF16, 0),       # ragged last chunk
+    (MLP, 1, 1, 24, 256, 512, 8, F32, 8),         # with row normalisation
+    (MLP, 1, 2, 40, 128, 256, 16, F32, 32),       # the LaCT rule
+])
+def test_decode_mlp_learner(kind, B, H, L, d, h, C, io, flags):
+    """The MLP learner f(x) = W2 silu(W1 x), token by token: its [W1 | W2]
+    state read in place by the per-token kernels (a3 = 1, dA3 = 0) and
+    updated at each chunk end through the [W1 | W3 = 0 | W2] layout of the
+    aggregation; against the oracle's MLP chunk forward."""
+    import chunk_weight_update_amd as cwu
+    log(f"decode MLP B={B} H={H} L={L} d={d} h={h} C={C} io={io} flags={flags}")
+    inp = make_inputs(kind, B, H, L, d, h, io, seed=19, regime="nearunit", m0_scale=1e-6)
+    prob = problem_for(kind, B, H, L, d, h, C, io, 0, flags)
+    out, W, M = run_decode(prob, to_device(inp, io), L, C, check_mid_chunk=True)
+    ro, rW, rM = run_oracle(kind, inp, C, h, row_norm=bool(flags & cwu.FLAG_POST_CHUNK_ROW_L2),
+                            lact=bool(flags & cwu.FLAG_LACT_RULE))
+    e = (rel_fro(out, ro), rel_fro(W, rW), rel_fro(M, rM))
+    log(f"  rel_fro out={e[0]:.3e} W={e[1]:.3e} M={e[2]:.3e}")
+    t = TOL[io]
+    assert W.shape[-1] == 2 * d * h
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(W)) and np.all(np.isfinite(M))
     assert e[0] <= t[0] and e[1] <= t[1] and e[2] <= t[2], e

@@ -269,7 +269,7 @@ def test_swiglu_bf16_register_resident_phase_a():
           m0_scale=M0["nearunit"])
 
 
-@pytest.mark.parametrize("L,C", [(700, 256), (512, 512)])
+@pytest.mark.parametrize("L,C", [(700, 256), (512, 512), (600, 200)])
 def test_swiglu_bf16_d256_tiled_aggregation(L, C):
     """d = 256, h = 512 bf16: the 256x256-tile aggregation with a token
     split and the split-sum state epilogue (generic path)."""

@@ -383,10 +383,19 @@ ScanArgs scan_args(const Plan& q, const float* eta, const float* alpha, const fl
   return sa;
 }
 
-// After chunk r: keep a copy of the state that chunk r+1 starts from.
+// After chunk r: keep a copy of the state that chunk r+1 starts from (the
+// MLP learner's from the kernels' [W1 | W3 | W2] layout back to [W1 | W2]).
 void save_state(const Plan& q, int64_t r, const float* Wend, const float* Mend, hipStream_t st) {
   if (!q.saveW || r + 1 >= q.nC) return;
   const int64_t n = q.BH * q.P;
+  if (q.kind == E2TTT_MLP) {
+    const unsigned gx = grid1((q.BH * 3 * q.d * q.h / 4 + 255) / 256);
+    hipLaunchKernelGGL(k_mlp_state, dim3(gx), dim3(256), 0, st, Wend, q.saveW + r * n, q.BH,
+                       q.d, q.h, 0);
+    hipLaunchKernelGGL(k_mlp_state, dim3(gx), dim3(256), 0, st, Mend, q.saveM + r * n, q.BH,
+                       q.d, q.h, 0);
+    return;
+  }
   hipLaunchKernelGGL(k_copy2, dim3(grid1((n + 255) / 256)), dim3(256), 0, st, Wend, Mend,
                      q.saveW + r * n, q.saveM + r * n, n);
 }
@@ -661,7 +670,6 @@ e2ttt_status forward_impl(const e2ttt_problem* prob, const void* q, const void* 
   e2ttt_status status = make_plan(prob, &pl);
   if (status != E2TTT_OK) return status;
   const bool keep = want_starts && pl.nC > 1;
-  if (want_starts && pl.kind == E2TTT_MLP) return E2TTT_EUNSUPPORTED;
   if (keep && (!W_starts || !M_starts || !aligned(W_starts, 16) || !aligned(M_starts, 16)))
     return E2TTT_EINVAL;
   if (!W0 || !M0 || !W_end || !M_end) return E2TTT_EINVAL;

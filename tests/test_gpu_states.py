@@ -10,7 +10,7 @@ forward: checked against the oracle at the bf16 bars."""
 import numpy as np
 import pytest
 
-from chunk_weight_update_amd.inputs import BF16, F32, LINEAR, SWIGLU, make_inputs
+from chunk_weight_update_amd.inputs import BF16, F32, LINEAR, MLP, SWIGLU, make_inputs
 from gpu_util import log, problem_for, rel_fro, to_device
 
 pytestmark = pytest.mark.gpu
@@ -22,7 +22,7 @@ def _forward_states(prob, t):
     import torch
     import chunk_weight_update_amd as cwu
     B, H, L, d = prob.batch, prob.heads, prob.seq_len, prob.dim
-    P = d * d if prob.kind == LINEAR else 3 * d * prob.hidden
+    P = d * d if prob.kind == LINEAR else (2 if prob.kind == MLP else 3) * d * prob.hidden
     nC = (L + prob.chunk - 1) // prob.chunk
     io = torch.bfloat16 if prob.io_dtype == BF16 else torch.float32
     out = torch.empty((B, H, L, d), dtype=io, device="cuda")
@@ -40,6 +40,8 @@ def _forward_states(prob, t):
     (SWIGLU, 2, 4, 1100, 128, 256, 256, BF16),   # fused path, ragged last chunk
     (SWIGLU, 1, 2, 700, 128, 256, 256, F32),     # generic fp32 path
     (LINEAR, 1, 3, 300, 64, 0, 64, F32),         # linear path
+    (MLP, 1, 2, 700, 128, 256, 256, F32),        # MLP learner, its [W1 | W2] states
+    (MLP, 1, 1, 700, 256, 512, 256, BF16),       # MLP learner on the 256-tile path
 ])
 def test_kept_states_equal_prefix_runs(kind, B, H, L, d, h, C, io):
     import torch

@@ -457,7 +457,25 @@ def system_info():
         except OSError:
             continue
     prop = torch.cuda.get_device_properties(0)
+    # The achievable HBM ceiling: a plain 1 GiB device-to-device copy (read +
+    # write bytes over time), median of 5.
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    copy_gbs = 2 * (1 << 30) / (percentile(times, 50) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
     return {"cpu_model": cpu, "cpu_threads_usable": len(os.sched_getaffinity(0)),
+            "hbm_copy_gbs_measured": copy_gbs,
             "rocm_version": rocm, "hip_runtime": torch.version.hip, "torch": torch.__version__,
             "device_name": prop.name, "gcn_arch": getattr(prop, "gcnArchName", None),
             "compute_units": prop.multi_processor_count,
@@ -740,12 +758,22 @@ def main():
                      "swiglu-d128h256-b8h16-l4096-c2048-bf16",
                      "swiglu-d128h256-b1h16-l32768-c2048-bf16"):
             wo = WORKLOADS[name]
-            ro = run_workload(wo, 20, 5)
-            del ro["_run"]
+            inp_o = make_workload_inputs(wo, seed=0)
+            ro = run_workload(wo, 50, 5, inp=inp_o)  # 50 timed calls for the smaller workloads
             others[name] = {k: ro[k] for k in ("ms_per_step", "value", "per_call_ms",
                                                 "tflops_algorithmic",
                                                 "mfma_util_pct_of_bf16_peak", "roofline")}
             others[name]["config"] = wo.describe()
+            if not args.no_cpu_baseline:  # a short oracle sample: parity and CPU baseline
+                smp = oracle_sample(wo, inp_o, 3.0)
+                others[name]["parity"] = parity_on_sample(wo, ro, smp, inp_o)
+                others[name]["cpu_baseline"] = {
+                    "value": smp["n_units"] * smp["tokens"] / smp["seconds"] / wo.H,
+                    "unit": "tokens/s", "cores": smp["cores"], "kind": "oracle",
+                    "sample": f"first chunk ({smp['tokens']} tokens) of {smp['n_units']} of "
+                              f"{wo.B * wo.H} units from W_0, {smp['seconds']:.2f} s fp64"}
+            del ro["_run"]
+            del inp_o
             log(f"bench: other workload {name}: {others[name]}")
             torch.cuda.empty_cache()
         line["other_configs"] = others

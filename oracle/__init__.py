@@ -194,11 +194,13 @@ def scalar_kernels(eta, alpha, beta, decay_mode=GAMMA_1_MINUS_ETA_ALPHA, average
 
 def chunk_backward(kind, q, k, v, eta, alpha, beta, W0, M0, dout, dWend, dMend, chunk,
                    decay_mode=GAMMA_1_MINUS_ETA_ALPHA, hidden=0, qk_norm=False, averaged=False,
-                   row_norm=False):
-    """Reverse mode of ``chunk_forward`` (linear and SwiGLU learners): gradients of
+                   row_norm=False, lact=False):
+    """Reverse mode of ``chunk_forward`` (linear, SwiGLU and MLP learners; the
+    default rule, the chunk-averaged variant or the LaCT rule): gradients of
     <dout, out> + <dWend, Wend> + <dMend, Mend> with respect to every input.
     dWend / dMend may be None (zero).  Returns a dict with keys q, k, v, eta,
     alpha, beta, W0, M0 (float64 arrays of the inputs' shapes)."""
+    assert not (averaged and lact), "the LaCT rule and the chunk-averaged variant are exclusive"
     lib = _load()
     q, k, v = _f64(q), _f64(k), _f64(v)
     eta, alpha, beta = _f64(eta), _f64(alpha), _f64(beta)
@@ -219,8 +221,8 @@ def chunk_backward(kind, q, k, v, eta, alpha, beta, W0, M0, dout, dWend, dMend, 
         _ptr(alpha), _ptr(beta), _ptr(W0), _ptr(M0), _ptr(dout),
         _ptr(dWp) if dWp is not None else null, _ptr(dMp) if dMp is not None else null,
         _ptr(g["q"]), _ptr(g["k"]), _ptr(g["v"]), _ptr(g["eta"]), _ptr(g["alpha"]),
-        _ptr(g["beta"]), _ptr(g["W0"]), _ptr(g["M0"]), int(bool(qk_norm)), int(bool(averaged)),
-        int(bool(row_norm)))
+        _ptr(g["beta"]), _ptr(g["W0"]), _ptr(g["M0"]), int(bool(qk_norm)),
+        2 if lact else int(bool(averaged)), int(bool(row_norm)))
     if rc != 0:
         raise RuntimeError(f"oracle_chunk_backward failed with code {rc}")
     return g

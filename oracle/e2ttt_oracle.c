@@ -300,8 +300,10 @@ static void normalise_rows_vjp(int kind, int64_t d, int64_t h, const double* Wpr
     const double* base;
     double* gb;
     if (kind == OR_LINEAR) { base = Wpre; gb = g; nrows = d; len = d; }
-    else if (part == 0) { base = Wpre; gb = g; nrows = 2 * h; len = d; }
-    else { base = Wpre + 2 * h * d; gb = g + 2 * h * d; nrows = d; len = h; }
+    else if (part == 0) { base = Wpre; gb = g; nrows = kind == OR_MLP ? h : 2 * h; len = d; }
+    else {
+      base = Wpre + w2_offset(kind, d, h); gb = g + w2_offset(kind, d, h); nrows = d; len = h;
+    }
     for (int64_t r = 0; r < nrows; ++r) {
       const double* w = base + r * len;
       double* gr = gb + r * len;
@@ -641,20 +643,23 @@ static void descent_vjp(int kind, int64_t d, int64_t h, const double* Ws,
     }
     return;
   }
+  /* The MLP learner (gated == 0) is the same walk with a3 = 1 held
+   * constant: no W3, no u3 (G has no W3 block) and no adjoint of a3. */
+  const int gated = kind == OR_SWIGLU;
   const double* W1 = Ws;
   const double* W3 = Ws + h * d;
-  const double* W2 = Ws + 2 * h * d;
+  const double* W2 = Ws + w2_offset(kind, d, h);
   const double* D1 = dG;
   const double* D3 = dG + h * d;
-  const double* D2 = dG + 2 * h * d;
+  const double* D2 = dG + w2_offset(kind, d, h);
   double* dW1 = dWs;
   double* dW3 = dWs + h * d;
-  double* dW2 = dWs + 2 * h * d;
+  double* dW2 = dWs + w2_offset(kind, d, h);
   double *a1 = scratch, *a3 = a1 + h, *z = a3 + h, *w = z + h, *sl = w + h,
          *sp = sl + h, *spp = sp + h, *u1 = spp + h, *u3 = u1 + h, *du1 = u3 + h,
          *du3 = du1 + h, *dz = du3 + h, *dw = dz + h, *da1 = dw + h, *da3 = da1 + h;
   double *y = scratch + 16 * h, *e = y + d, *de = e + d;
-  fast_forward(OR_SWIGLU, d, h, Ws, k, a1, a3, z, y);
+  fast_forward(kind, d, h, Ws, k, a1, a3, z, y);
   for (int64_t o = 0; o < d; ++o) e[o] = v[o] - y[o];
   for (int64_t i = 0; i < h; ++i) {
     double s = 0.0;
@@ -672,14 +677,15 @@ static void descent_vjp(int kind, int64_t d, int64_t h, const double* Ws,
     double s1 = 0.0, s3 = 0.0;
     for (int64_t j = 0; j < d; ++j) {
       s1 += D1[i * d + j] * k[j];
-      s3 += D3[i * d + j] * k[j];
+      if (gated) s3 += D3[i * d + j] * k[j];
     }
     du1[i] = s1;
     du3[i] = s3;
   }
   for (int64_t j = 0; j < d; ++j) {
     double s = 0.0;
-    for (int64_t i = 0; i < h; ++i) s += D1[i * d + j] * u1[i] + D3[i * d + j] * u3[i];
+    for (int64_t i = 0; i < h; ++i)
+      s += D1[i * d + j] * u1[i] + (gated ? D3[i * d + j] * u3[i] : 0.0);
     dk[j] += s;
   }
   /* G2 = e z^T */
@@ -724,12 +730,13 @@ static void descent_vjp(int kind, int64_t d, int64_t h, const double* Ws,
     da3[i] += dz[i] * sl[i];
     for (int64_t j = 0; j < d; ++j) {
       dW1[i * d + j] += da1[i] * k[j];
-      dW3[i * d + j] += da3[i] * k[j];
+      if (gated) dW3[i * d + j] += da3[i] * k[j];
     }
   }
   for (int64_t j = 0; j < d; ++j) {
     double s = 0.0;
-    for (int64_t i = 0; i < h; ++i) s += W1[i * d + j] * da1[i] + W3[i * d + j] * da3[i];
+    for (int64_t i = 0; i < h; ++i)
+      s += W1[i * d + j] * da1[i] + (gated ? W3[i * d + j] * da3[i] : 0.0);
     dk[j] += s;
   }
 }
@@ -749,15 +756,16 @@ static void readout_vjp(int kind, int64_t d, int64_t h, const double* Ws,
       for (int64_t j = 0; j < d; ++j) dWs[i * d + j] += dy[i] * x[j];
     return;
   }
+  const int gated = kind == OR_SWIGLU; /* the MLP: a3 = 1, no W3 */
   const double* W1 = Ws;
   const double* W3 = Ws + h * d;
-  const double* W2 = Ws + 2 * h * d;
+  const double* W2 = Ws + w2_offset(kind, d, h);
   double* dW1 = dWs;
   double* dW3 = dWs + h * d;
-  double* dW2 = dWs + 2 * h * d;
+  double* dW2 = dWs + w2_offset(kind, d, h);
   double *a1 = scratch, *a3 = a1 + h, *z = a3 + h, *dz = z + h, *da1 = dz + h,
          *da3 = da1 + h, *y = scratch + 8 * h;
-  fast_forward(OR_SWIGLU, d, h, Ws, x, a1, a3, z, y);
+  fast_forward(kind, d, h, Ws, x, a1, a3, z, y);
   for (int64_t i = 0; i < h; ++i) {
     double s = 0.0;
     for (int64_t o = 0; o < d; ++o) s += W2[o * h + i] * dy[o];
@@ -771,18 +779,19 @@ static void readout_vjp(int kind, int64_t d, int64_t h, const double* Ws,
   for (int64_t i = 0; i < h; ++i)
     for (int64_t j = 0; j < d; ++j) {
       dW1[i * d + j] += da1[i] * x[j];
-      dW3[i * d + j] += da3[i] * x[j];
+      if (gated) dW3[i * d + j] += da3[i] * x[j];
     }
   for (int64_t j = 0; j < d; ++j) {
     double s = 0.0;
-    for (int64_t i = 0; i < h; ++i) s += W1[i * d + j] * da1[i] + W3[i * d + j] * da3[i];
+    for (int64_t i = 0; i < h; ++i)
+      s += W1[i * d + j] * da1[i] + (gated ? W3[i * d + j] * da3[i] : 0.0);
     dx[j] += s;
   }
 }
 
 /*
- * Reverse mode of the chunk forward (the outer-loop backward), linear and
- * SwiGLU learners: the gradient of a scalar loss
+ * Reverse mode of the chunk forward (the outer-loop backward), linear,
+ * SwiGLU and MLP learners: the gradient of a scalar loss
  *     l = <dout, out> + <dWend, Wend> + <dMend, Mend>
  * with respect to every input of oracle_chunk_forward.  It differentiates the
  * same literal recurrence, one token at a time in reverse:
@@ -807,7 +816,11 @@ static void readout_vjp(int kind, int64_t d, int64_t h, const double* Ws,
  * With averaged != 0 (the chunk-averaged variant) every token of a chunk uses
  * the chunk means of beta and gamma, so the per-token adjoints of the two
  * means are summed over the chunk and each token's beta and gamma receive
- * 1/n of the sums.  With row_norm != 0 (chunk-boundary normalisation) the
+ * 1/n of the sums.  With averaged == 2 (the LaCT rule) a chunk is one step,
+ * M_C = bbar M_s + sum_t eta_t G_t, W_C = gbar W_s + M_C, walked backwards
+ * as a whole (the adjoints of the means again shared out by 1/n).  The MLP
+ * learner takes the SwiGLU walk with a3 = 1 held constant (no W3 block).
+ * With row_norm != 0 (chunk-boundary normalisation) the
  * forward normalises W after every chunk, the last included, so before a
  * chunk is walked in reverse the adjoint of its normalised end state is taken
  * back through the normalisation (normalise_rows_vjp) at the state before it.  dWend or dMend may be NULL (zero).  h is the SwiGLU hidden
@@ -824,13 +837,13 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
                           double* dq, double* dk, double* dv, double* deta,
                           double* dalpha, double* dbeta, double* dW0,
                           double* dM0, int qk_norm, int averaged, int row_norm) {
-  if (averaged < 0 || averaged > 1) return 1; /* the LaCT rule has no reverse mode here */
-  if (kind != OR_LINEAR && kind != OR_SWIGLU) return 3;
+  if (averaged < 0 || averaged > 2) return 1;
+  if (kind != OR_LINEAR && kind != OR_SWIGLU && kind != OR_MLP) return 3;
   if (decay_mode != OR_GAMMA_1_MINUS_ETA_ALPHA &&
       decay_mode != OR_ALPHA_IS_GAMMA)
     return 1;
   if (B < 0 || H < 0 || L < 0 || d <= 0 || C <= 0) return 1;
-  if (kind == OR_SWIGLU && h <= 0) return 1;
+  if (kind != OR_LINEAR && h <= 0) return 1;
   const int64_t P = state_size(kind, d, h);
   const int64_t nC = (L + C - 1) / C;
   const int64_t Cmax = C < L ? C : (L > 0 ? L : 1);
@@ -921,12 +934,22 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
       memcpy(Mst + r * P, M, sizeof(double) * (size_t)P);
       const double* Ws = Wst + r * P;
       CHUNK_FACTORS(t0, n);
-      for (int64_t t = 0; t < n; ++t) {
-        const int64_t tt = t0 + t;
-        oracle_token_descent(kind, d, h, Ws, ku + tt * d, vu + tt * d, Gt);
-        for (int64_t i = 0; i < P; ++i) {
-          M[i] = fb[t] * M[i] + etu[tt] * Gt[i];
-          W[i] = fg[t] * W[i] + M[i];
+      if (averaged == 2) { /* LaCT: M <- bbar M + sum eta G, W <- gbar W + M */
+        for (int64_t i = 0; i < P; ++i) M[i] *= fb[0];
+        for (int64_t t = 0; t < n; ++t) {
+          const int64_t tt = t0 + t;
+          oracle_token_descent(kind, d, h, Ws, ku + tt * d, vu + tt * d, Gt);
+          for (int64_t i = 0; i < P; ++i) M[i] += etu[tt] * Gt[i];
+        }
+        for (int64_t i = 0; i < P; ++i) W[i] = fg[0] * W[i] + M[i];
+      } else {
+        for (int64_t t = 0; t < n; ++t) {
+          const int64_t tt = t0 + t;
+          oracle_token_descent(kind, d, h, Ws, ku + tt * d, vu + tt * d, Gt);
+          for (int64_t i = 0; i < P; ++i) {
+            M[i] = fb[t] * M[i] + etu[tt] * Gt[i];
+            W[i] = fg[t] * W[i] + M[i];
+          }
         }
       }
       if (row_norm) normalise_rows(kind, d, h, W);
@@ -940,6 +963,67 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
     for (int64_t r = nC - 1; r >= 0; --r) {
       const int64_t t0 = r * C, n = (L - t0) < C ? (L - t0) : C;
       const double* Ws = Wst + r * P;
+      if (averaged == 2) {
+        /* LaCT: M_C = bbar M_s + sum_t eta_t G_t, W_C = gbar W_s + M_C with
+         * the chunk means bbar, gbar.  With (dW, dM) the adjoint of
+         * (W_C, M_C): dMt = dM + dW, dgbar = <dW, W_s>, dbbar = <dMt, M_s>,
+         * deta_t += <dMt, G_t>, dG_t = eta_t dMt; dW <- gbar dW,
+         * dM <- bbar dMt; each token's beta, gamma gets 1/n of dbbar, dgbar. */
+        const double* Msr = Mst + r * P;
+        CHUNK_FACTORS(t0, n);
+        if (row_norm) { /* the chunk end before its normalisation */
+          memcpy(W, Ws, sizeof(double) * (size_t)P);
+          memcpy(M, Msr, sizeof(double) * (size_t)P);
+          for (int64_t i = 0; i < P; ++i) M[i] *= fb[0];
+          for (int64_t t = 0; t < n; ++t) {
+            const int64_t tt = t0 + t;
+            oracle_token_descent(kind, d, h, Ws, ku + tt * d, vu + tt * d, Gt);
+            for (int64_t i = 0; i < P; ++i) M[i] += etu[tt] * Gt[i];
+          }
+          for (int64_t i = 0; i < P; ++i) W[i] = fg[0] * W[i] + M[i];
+          normalise_rows_vjp(kind, d, h, W, dW);
+        }
+        double dgb = 0.0, dbb = 0.0;
+        for (int64_t i = 0; i < P; ++i) {
+          dMt[i] = dM[i] + dW[i];
+          dgb += dW[i] * Ws[i];
+          dbb += dMt[i] * Msr[i];
+          dWs[i] = 0.0;
+        }
+        for (int64_t t = 0; t < n; ++t) {
+          const int64_t tt = t0 + t;
+          oracle_token_descent(kind, d, h, Ws, ku + tt * d, vu + tt * d, Gt);
+          double detd = 0.0;
+          for (int64_t i = 0; i < P; ++i) {
+            detd += dMt[i] * Gt[i];
+            dG[i] = etu[tt] * dMt[i];
+          }
+          detu[tt] += detd;
+          descent_vjp(kind, d, h, Ws, ku + tt * d, vu + tt * d, dG, dku + tt * d,
+                      dvu + tt * d, dWs, scr);
+        }
+        for (int64_t i = 0; i < P; ++i) {
+          dW[i] = fg[0] * dW[i];
+          dM[i] = fb[0] * dMt[i];
+        }
+        for (int64_t t = 0; t < n; ++t) {
+          const int64_t tt = t0 + t;
+          const double dg = dgb / (double)n;
+          dbeu[tt] += dbb / (double)n;
+          if (decay_mode == OR_GAMMA_1_MINUS_ETA_ALPHA) {
+            detu[tt] -= alu[tt] * dg;
+            dalu[tt] += -etu[tt] * dg;
+          } else {
+            dalu[tt] += dg;
+          }
+        }
+        for (int64_t t = 0; t < n; ++t) {
+          const int64_t tt = t0 + t;
+          readout_vjp(kind, d, h, Ws, qu + tt * d, dou + tt * d, dqu + tt * d, dWs, scr);
+        }
+        for (int64_t i = 0; i < P; ++i) dW[i] += dWs[i];
+        continue;
+      }
       /* Re-run the chunk, recording the state before each token and G. */
       memcpy(W, Ws, sizeof(double) * (size_t)P);
       memcpy(M, Mst + r * P, sizeof(double) * (size_t)P);

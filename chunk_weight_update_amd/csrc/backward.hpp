@@ -408,6 +408,35 @@ __global__ __launch_bounds__(64) void k_lin_bwd_scalars(Shape s, int mode, const
   const int64_t tpl = (n + 63) / 64;
   const int64_t lo = lane * tpl, hi = (lo + tpl < n ? lo + tpl : n);  // [lo, hi)
   double* B3 = bcp + seg * s.Cp * 3;
+  if (averaged == 2) {
+    // The LaCT rule: K^W = K^M = eta and (cW, cM, cWM) = (mean gamma, mean
+    // beta, mean beta), so deta = dK^W + dK^M directly, and every token's
+    // beta and gamma get 1/n of the adjoints of the means (gamma through
+    // Eq. 14 as below).
+    double dcW = 0.0, dcM = 0.0, dcWM = 0.0;
+    for (int rb = 0; rb < nrb; ++rb) {
+      dcW += dots[(seg * nrb + rb) * 4 + 0];
+      dcM += dots[(seg * nrb + rb) * 4 + 1];
+      dcWM += dots[(seg * nrb + rb) * 4 + 2];
+    }
+    const double inv_n = 1.0 / static_cast<double>(n > 0 ? n : 1);
+    const double dgb = dcW * inv_n, dbb = (dcM + dcWM) * inv_n;
+    for (int64_t i = lo; i < hi; ++i) {
+      const double e = eta[t0 + i];
+      double det = static_cast<double>(sw[seg * s.Cp + i]) + static_cast<double>(sm[seg * s.Cp + i]);
+      double dal;
+      if (mode == 0) {
+        det -= static_cast<double>(alpha[t0 + i]) * dgb;
+        dal = -e * dgb;
+      } else {
+        dal = dgb;
+      }
+      deta[t0 + i] = static_cast<float>(det);
+      dalpha[t0 + i] = static_cast<float>(dal);
+      dbeta[t0 + i] = static_cast<float>(dbb);
+    }
+    return;
+  }
   auto gam_tok = [&](int64_t i) -> double {
     const double e = eta[t0 + i], al = alpha[t0 + i];
     return mode == 0 ? 1.0 - e * al : al;

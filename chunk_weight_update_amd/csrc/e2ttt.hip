@@ -1253,7 +1253,6 @@ e2ttt_status make_bwd_plan(const e2ttt_problem* p, BwdPlan* bp) {
   const Plan& q = bp->f;
   // Every flag of the forward is supported (the compensated-weights option
   // only concerns bf16 matrix operands; the backward computes in fp32).
-  if (q.lact) return E2TTT_EUNSUPPORTED;  // no reverse mode of the LaCT rule
   if (q.kind == E2TTT_MLP) return E2TTT_EUNSUPPORTED;
   bp->qknorm = q.qknorm != 0;
   bp->rownorm = q.rownorm != 0;
@@ -1716,8 +1715,8 @@ e2ttt_status backward_impl(const e2ttt_problem* prob, const void* q, const void*
   hipLaunchKernelGGL(k_lin_bwd_scalars, dim3(grid1(pl.BH * pl.nC)), dim3(64), 0, s, sh, pl.mode,
                      eta, alpha, beta, static_cast<const float*>(wsf(bp.sw)),
                      static_cast<const float*>(wsf(bp.sm)), static_cast<const float*>(wsf(bp.dots)),
-                     static_cast<int>(bp.nrb), pl.averaged, reinterpret_cast<double*>(ws + bp.bcp),
-                     deta, dalpha, dbeta);
+                     static_cast<int>(bp.nrb), pl.lact ? 2 : pl.averaged,
+                     reinterpret_cast<double*>(ws + bp.bcp), deta, dalpha, dbeta);
   return hipGetLastError() == hipSuccess ? E2TTT_OK : E2TTT_EHIP;
 }
 

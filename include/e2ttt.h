@@ -150,9 +150,11 @@ enum {
    * description there (no momentum suffix product, no decay ratio sum).
    * Same kernels as the default rule, only the scalar kernels differ:
    * K^W = K^M = eta, (cW, cM, cWM) = (mean gamma, mean beta, mean beta).
-   * Applies to e2ttt_chunk_forward (and its twins), e2ttt_scalar_kernels and
-   * e2ttt_decode_step (the update at each chunk end); EINVAL together with
-   * E2TTT_FLAG_CHUNK_AVERAGED_DECAY; EUNSUPPORTED for the backward. */
+   * Applies to e2ttt_chunk_forward (and its twins), e2ttt_scalar_kernels,
+   * e2ttt_decode_step (the update at each chunk end) and the backward (deta
+   * takes the adjoints of both kernels; each token's beta and gamma get 1/n
+   * of the adjoints of the means); EINVAL together with
+   * E2TTT_FLAG_CHUNK_AVERAGED_DECAY. */
   E2TTT_FLAG_LACT_RULE = 32u
 };
 
@@ -391,7 +393,8 @@ E2TTT_API e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* 
  * Flags: E2TTT_FLAG_QK_SILU_L2 (the prologue is recomputed and dq, dk are
  * taken back through it to the raw q, k), E2TTT_FLAG_CHUNK_AVERAGED_DECAY
  * (each token's beta and gamma receive 1/n of the adjoints of its chunk's
- * means), E2TTT_FLAG_POST_CHUNK_ROW_L2 (the adjoint goes back through every
+ * means), E2TTT_FLAG_LACT_RULE (deta takes dK^W + dK^M, the means' adjoints
+ * shared out as for the averaged variant), E2TTT_FLAG_POST_CHUNK_ROW_L2 (the adjoint goes back through every
  * chunk's normalisation; the states are then always recomputed, so
  * e2ttt_chunk_backward_states returns EUNSUPPORTED for it) and
  * E2TTT_FLAG_COMPENSATED_WEIGHTS (no effect: the arithmetic is fp32).

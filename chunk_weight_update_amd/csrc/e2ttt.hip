@@ -1212,6 +1212,12 @@ namespace {
 // per-token adjoint terms (byte offsets, 256-aligned).
 struct BwdPlan {
   Plan f;
+  // State length per unit inside the backward: the caller's P, except for the
+  // MLP learner, whose states and adjoints are carried in the SwiGLU layout
+  // [W1 | W3 = 0 | W2] (3dh) and expanded / compacted at the boundary.
+  int64_t P;
+  bool mlp;
+  size_t w0x, m0x, dw0x, dm0x;  // MLP: expanded W0, M0 and the adjoints of them, [BH][3dh]
   size_t wst, mst;            // chunk-start states of chunks 1 .. nC-1 (slot r), [nC][BH][P]
   size_t dwa, dwb, dma, dmb;  // state adjoints, two of each in turn, [BH][P]
   size_t de;                  // linear: [BH][Cp][d]
@@ -1253,15 +1259,16 @@ e2ttt_status make_bwd_plan(const e2ttt_problem* p, BwdPlan* bp) {
   const Plan& q = bp->f;
   // Every flag of the forward is supported (the compensated-weights option
   // only concerns bf16 matrix operands; the backward computes in fp32).
-  if (q.kind == E2TTT_MLP) return E2TTT_EUNSUPPORTED;
+  bp->mlp = q.kind == E2TTT_MLP;
+  bp->P = bp->mlp ? 3 * q.d * q.h : q.P;
   bp->qknorm = q.qknorm != 0;
   bp->rownorm = q.rownorm != 0;
   if (q.kind == E2TTT_LINEAR && q.d > 64) return E2TTT_EUNSUPPORTED;
   if (q.kind == E2TTT_SWIGLU && q.BH > 65535) return E2TTT_EUNSUPPORTED;  // grid z
   size_t o = align256(q.total);
   auto take = [&](size_t bytes) { const size_t at = o; o = align256(o + bytes); return at; };
-  const size_t np = 4 * static_cast<size_t>(q.BH * q.P);
-  bp->nrb = q.kind == E2TTT_LINEAR ? q.d / 16 : (q.P + SWB_STATE_ELEMS - 1) / SWB_STATE_ELEMS;
+  const size_t np = 4 * static_cast<size_t>(q.BH * bp->P);
+  bp->nrb = q.kind == E2TTT_LINEAR ? q.d / 16 : (bp->P + SWB_STATE_ELEMS - 1) / SWB_STATE_ELEMS;
   bp->wst = take(np * q.nC);
   bp->mst = take(np * q.nC);
   bp->dwa = take(np);
@@ -1296,6 +1303,8 @@ e2ttt_status make_bwd_plan(const e2ttt_problem* p, BwdPlan* bp) {
     bp->wpre = take(np * q.nC);
     bp->dwn = take(np);
   }
+  if (bp->mlp)
+    for (size_t* b : {&bp->w0x, &bp->m0x, &bp->dw0x, &bp->dm0x}) *b = take(np);
   bp->total = q.L == 0 ? 0 : o;
   return E2TTT_OK;
 }
@@ -1340,8 +1349,9 @@ void swiglu_backward(const BwdPlan& bp, char* ws, const float* Q, const float* K
                      hipStream_t s) {
   const Plan& q = bp.f;
   auto wsf = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
-  const Shape sh{q.BH, q.L, q.d, q.h, q.C, q.Cp, q.nC, q.krep};
-  const int64_t BH = q.BH, L = q.L, d = q.d, h = q.h, Cp = q.Cp, P = q.P, nP = BH * P;
+  Shape sh{q.BH, q.L, q.d, q.h, q.C, q.Cp, q.nC, q.krep};
+  sh.gated = bp.mlp ? 0 : 1;
+  const int64_t BH = q.BH, L = q.L, d = q.d, h = q.h, Cp = q.Cp, P = bp.P, nP = BH * P;
   const int64_t Ld = L * d;
   float* kw = wsf(q.kw);
   float* km = wsf(q.km);
@@ -1436,8 +1446,8 @@ void swiglu_backward(const BwdPlan& bp, char* ws, const float* Q, const float* K
     gemm_f32(gf(n, 2 * h, d, Kr, Ld, d, 1, Ws, P, 1, d, nullptr, 0, 0, HK, b2, 2 * h), BH, PART, s);
     gemm_f32(gf(n, 2 * h, d, Qr, Ld, d, 1, Ws, P, 1, d, nullptr, 0, 0, HQ, b2, 2 * h), BH, PART, s);
     const unsigned gact = grid1((BH * n * h + 255) / 256);
-    hipLaunchKernelGGL(k_swb_act, dim3(gact), dim3(256), 0, s, BH, n, h, Cp, HK, ZK);
-    hipLaunchKernelGGL(k_swb_act, dim3(gact), dim3(256), 0, s, BH, n, h, Cp, HQ, ZQ);
+    hipLaunchKernelGGL(k_swb_act, dim3(gact), dim3(256), 0, s, BH, n, h, Cp, sh.gated, HK, ZK);
+    hipLaunchKernelGGL(k_swb_act, dim3(gact), dim3(256), 0, s, BH, n, h, Cp, sh.gated, HQ, ZQ);
     gemm_f32(gf(n, d, h, ZK, b1, h, 1, Ws + o2, P, 1, h, Vr, Ld, d, E, bd, d, -1.0f), BH, PART, s);
     gemm_f32(gf(n, h, d, E, bd, d, 1, Ws + o2, P, h, 1, nullptr, 0, 0, WV, b1, h), BH, PART, s);
     gemm_f32(gf(n, h, d, DOr, Ld, d, 1, Ws + o2, P, h, 1, nullptr, 0, 0, DZQ, b1, h), BH, PART, s);
@@ -1450,7 +1460,7 @@ void swiglu_backward(const BwdPlan& bp, char* ws, const float* Q, const float* K
     gemm_f32(gf(n, h, d, E, bd, d, 1, dMC + o2, P, h, 1, nullptr, 0, 0, R2M, b1, h), BH, PART, s);
     if (n > 0) {
       SwbTokArgs ta;
-      ta.n = n; ta.d = d; ta.h = h; ta.Cp = Cp; ta.nC = q.nC; ta.r = ri;
+      ta.n = n; ta.d = d; ta.h = h; ta.Cp = Cp; ta.nC = q.nC; ta.r = ri; ta.gated = sh.gated;
       ta.HK = HK; ta.WV = WV; ta.E = E; ta.TW = TW; ta.TM = TM; ta.SW = S2W; ta.SM = S2M;
       ta.RW = R2W; ta.RM = R2M; ta.kw = kw; ta.km = km;
       ta.sw = wsf(bp.sw); ta.sm = wsf(bp.sm); ta.DU = DU; ta.DW = DW; ta.DEA = DEA;
@@ -1460,8 +1470,8 @@ void swiglu_backward(const BwdPlan& bp, char* ws, const float* Q, const float* K
     // de (= dv) and dz.
     gemm_f32(gf(n, d, h, DW, b1, h, 1, Ws + o2, P, 1, h, DEA, bd, d, dvr, Ld, d), BH, PART, s);
     gemm_f32(gf(n, h, d, dvr, Ld, d, 1, Ws + o2, P, h, 1, DZA, b1, h, DZA, b1, h, -1.0f), BH, PART, s);
-    hipLaunchKernelGGL(k_swb_da, dim3(gact), dim3(256), 0, s, BH, n, h, Cp, HK, WV, DU, DZA,
-                       HQ, DZQ, DA, DAQ);
+    hipLaunchKernelGGL(k_swb_da, dim3(gact), dim3(256), 0, s, BH, n, h, Cp, sh.gated, HK, WV,
+                       DU, DZA, HQ, DZQ, DA, DAQ);
     // dk, dq.
     gemm_f32(gf(n, d, 2 * h, DA, b2, 2 * h, 1, Ws, P, d, 1, nullptr, 0, 0, dkr, Ld, d), BH, PART, s);
     gemm_f32(gf(n, d, 2 * h, UW, b2, 2 * h, 1, dWC, P, d, 1, dkr, Ld, d, dkr, Ld, d), BH, PART, s);
@@ -1670,7 +1680,45 @@ e2ttt_status backward_impl(const e2ttt_problem* prob, const void* q, const void*
   launch_scan(pl, eta, alpha, beta, kw, km, pl.nC * pl.Cp, pl.Cp, pl.Cp, coef, 4, s, none);
   const float* dWC = dW_end;
   const float* dMC = dM_end;
-  if (!dWC || !dMC) {  // absent state gradients: zeros in the first adjoint pair
+  const float* W0r = W0;
+  const float* M0r = M0;
+  float* dW0r = dW0;
+  float* dM0r = dM0;
+  const float* Wkeep = keep ? W_starts : nullptr;
+  const float* Mkeep = keep ? M_starts : nullptr;
+  if (bp.mlp) {
+    // The MLP learner's states, their adjoints and any kept chunk-start
+    // states in the SwiGLU layout with W3 = 0 (absent adjoints as zeros); the
+    // kept state of chunk r + 1 goes to slot r + 1 of the re-run's buffers.
+    const int64_t nP3 = pl.BH * bp.P;
+    const unsigned gx3 = grid1((nP3 / 4 + 255) / 256);
+    auto expand = [&](const float* src, float* dst) {
+      if (src)
+        hipLaunchKernelGGL(k_mlp_state, dim3(gx3), dim3(256), 0, s, src, dst, pl.BH, pl.d, pl.h,
+                           1);
+      else
+        hipLaunchKernelGGL(k_copy_or_zero, dim3(grid1((nP3 + 255) / 256)), dim3(256), 0, s,
+                           static_cast<const float*>(nullptr), dst, nP3);
+    };
+    expand(W0, wsf(bp.w0x));
+    expand(M0, wsf(bp.m0x));
+    expand(dW_end, wsf(bp.dwb));
+    expand(dM_end, wsf(bp.dmb));
+    W0r = wsf(bp.w0x);
+    M0r = wsf(bp.m0x);
+    dWC = wsf(bp.dwb);
+    dMC = wsf(bp.dmb);
+    dW0r = wsf(bp.dw0x);
+    dM0r = wsf(bp.dm0x);
+    if (keep) {
+      for (int64_t r = 0; r + 1 < pl.nC; ++r) {
+        expand(W_starts + r * nP, wsf(bp.wst) + (r + 1) * nP3);
+        expand(M_starts + r * nP, wsf(bp.mst) + (r + 1) * nP3);
+      }
+      Wkeep = wsf(bp.wst) + nP3;
+      Mkeep = wsf(bp.mst) + nP3;
+    }
+  } else if (!dWC || !dMC) {  // absent state gradients: zeros in the first adjoint pair
     hipLaunchKernelGGL(k_copy_or_zero, dim3(gP), dim3(256), 0, s, dW_end, wsf(bp.dwb), nP);
     hipLaunchKernelGGL(k_copy_or_zero, dim3(gP), dim3(256), 0, s, dM_end, wsf(bp.dmb), nP);
     dWC = wsf(bp.dwb);
@@ -1679,7 +1727,7 @@ e2ttt_status backward_impl(const e2ttt_problem* prob, const void* q, const void*
   void (*run)(const BwdPlan&, char*, const float*, const float*, const float*, const float*,
               const float*, const float*, const float*, const float*, float*, float*, float*,
               float*, float*, const float*, const float*, hipStream_t) =
-      pl.kind == E2TTT_SWIGLU ? swiglu_backward : linear_backward;
+      pl.kind == E2TTT_LINEAR ? linear_backward : swiglu_backward;
   const float* Qraw = Q;
   const float* Kraw = K;
   float* dQout = dQ;
@@ -1695,8 +1743,14 @@ e2ttt_status backward_impl(const e2ttt_problem* prob, const void* q, const void*
     dQ = wsf(bp.dnq);
     dK = wsf(bp.dnk);
   }
-  run(bp, ws, Q, K, V, W0, M0, DO, dWC, dMC, dQ, dK, dV, dW0, dM0, keep ? W_starts : nullptr,
-      keep ? M_starts : nullptr, s);
+  run(bp, ws, Q, K, V, W0r, M0r, DO, dWC, dMC, dQ, dK, dV, dW0r, dM0r, Wkeep, Mkeep, s);
+  if (bp.mlp) {  // the adjoints of W0, M0 back in the caller's [W1 | W2] layout
+    const unsigned gx3 = grid1((pl.BH * bp.P / 4 + 255) / 256);
+    hipLaunchKernelGGL(k_mlp_state, dim3(gx3), dim3(256), 0, s,
+                       static_cast<const float*>(dW0r), dW0, pl.BH, pl.d, pl.h, 0);
+    hipLaunchKernelGGL(k_mlp_state, dim3(gx3), dim3(256), 0, s,
+                       static_cast<const float*>(dM0r), dM0, pl.BH, pl.d, pl.h, 0);
+  }
   if (bp.qknorm) {
     hipLaunchKernelGGL(k_qk_norm_bwd, dim3(gqk), dim3(256), 0, s, Qraw, dQ, dQout,
                        pl.BH * pl.L, pl.d);

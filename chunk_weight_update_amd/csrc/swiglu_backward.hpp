@@ -160,22 +160,29 @@ __global__ __launch_bounds__(256) void k_gemm_split_sum(GemmF32 g, int64_t BH) {
 
 __device__ __forceinline__ float sig_acc(float x) { return 1.0f / (1.0f + expf(-x)); }
 
-// Z = silu(a1) * a3 for n rows of H = [a1 | a3] (row length 2h), per unit.
+// The two-matrix MLP learner f(x) = W2 silu(W1 x) (§5.2) runs through the same
+// steps on the state laid out as [W1 | W3 = 0 | W2] with gated = 0: the gate
+// a3 is held at one, so u3, du3 and da3 are zero and the W3 block of every
+// state adjoint stays zero.
+
+// Z = silu(a1) * a3 for n rows of H = [a1 | a3] (row length 2h), per unit
+// (a3 = 1 when gated = 0).
 __global__ __launch_bounds__(256) void k_swb_act(int64_t BH, int64_t n, int64_t h,
-                                                 int64_t ustride, const float* __restrict__ H,
+                                                 int64_t ustride, int gated,
+                                                 const float* __restrict__ H,
                                                  float* __restrict__ Z) {
   const int64_t per = n * h;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= BH * per) return;
   const int64_t u = i / per, rem = i % per, t = rem / h, j = rem % h;
   const float* hr = H + u * ustride * 2 * h + t * 2 * h;
-  const float a1 = hr[j], a3 = hr[h + j];
+  const float a1 = hr[j], a3 = gated ? hr[h + j] : 1.0f;
   Z[u * ustride * h + t * h + j] = a1 * sig_acc(a1) * a3;
 }
 
 struct SwbTokArgs {
   int64_t n, d, h, Cp, nC;
-  int r;
+  int r, gated;
   const float *HK, *WV, *E, *TW, *TM, *SW, *SM, *RW, *RM, *kw, *km;
   float *sw, *sm, *DU, *DW, *DEA, *DZA, *UW, *UM;
 };
@@ -191,14 +198,15 @@ __global__ __launch_bounds__(256) void k_swb_tok(SwbTokArgs a) {
   const float kwt = a.kw[seg * a.Cp + t], kmt = a.km[seg * a.Cp + t];
   float pW = 0.0f, pM = 0.0f;
   for (int64_t i = tid; i < h; i += 256) {
-    const float a1 = a.HK[r2 + i], a3 = a.HK[r2 + h + i], w = a.WV[rh + i];
+    const float a1 = a.HK[r2 + i], a3 = a.gated ? a.HK[r2 + h + i] : 1.0f, w = a.WV[rh + i];
     const float sg = sig_acc(a1), sl = a1 * sg, sp = sg * (1.0f + a1 * (1.0f - sg));
-    const float u1 = w * a3 * sp, u3 = w * sl;
+    const float u1 = w * a3 * sp, u3 = a.gated ? w * sl : 0.0f;
     const float tw1 = a.TW[r2 + i], tw3 = a.TW[r2 + h + i];
     const float tm1 = a.TM[r2 + i], tm3 = a.TM[r2 + h + i];
     pW += u1 * tw1 + u3 * tw3;
     pM += u1 * tm1 + u3 * tm3;
-    const float du1 = kwt * tw1 + kmt * tm1, du3 = kwt * tw3 + kmt * tm3;
+    const float du1 = kwt * tw1 + kmt * tm1;
+    const float du3 = a.gated ? kwt * tw3 + kmt * tm3 : 0.0f;
     a.DU[r2 + i] = du1;
     a.DU[r2 + h + i] = du3;
     a.DW[rh + i] = du3 * sl + du1 * a3 * sp;
@@ -231,8 +239,9 @@ __global__ __launch_bounds__(256) void k_swb_tok(SwbTokArgs a) {
 }
 
 // [da1 | da3] of the key rows (from a1, a3, w, du1, du3, dz) and of the query
-// rows (readout: from a1, a3 and dz = W2^T dout).
+// rows (readout: from a1, a3 and dz = W2^T dout); da3 = 0 when gated = 0.
 __global__ __launch_bounds__(256) void k_swb_da(int64_t BH, int64_t n, int64_t h, int64_t Cp,
+                                                int gated,
                                                 const float* __restrict__ HK,
                                                 const float* __restrict__ WV,
                                                 const float* __restrict__ DU,
@@ -246,18 +255,18 @@ __global__ __launch_bounds__(256) void k_swb_da(int64_t BH, int64_t n, int64_t h
   const int64_t u = i / per, rem = i % per, t = rem / h, j = rem % h;
   const int64_t rh = (u * Cp + t) * h, r2 = 2 * rh;
   {
-    const float a1 = HK[r2 + j], a3 = HK[r2 + h + j], w = WV[rh + j];
+    const float a1 = HK[r2 + j], a3 = gated ? HK[r2 + h + j] : 1.0f, w = WV[rh + j];
     const float du1 = DU[r2 + j], du3 = DU[r2 + h + j], dz = DZ[rh + j];
     const float sg = sig_acc(a1), sl = a1 * sg, sp = sg * (1.0f + a1 * (1.0f - sg));
     const float spp = sg * (1.0f - sg) * (2.0f + a1 * (1.0f - 2.0f * sg));
     DA[r2 + j] = du3 * w * sp + du1 * w * a3 * spp + dz * a3 * sp;
-    DA[r2 + h + j] = du1 * w * sp + dz * sl;
+    DA[r2 + h + j] = gated ? du1 * w * sp + dz * sl : 0.0f;
   }
   {
-    const float a1 = HQ[r2 + j], a3 = HQ[r2 + h + j], dz = DZQ[rh + j];
+    const float a1 = HQ[r2 + j], a3 = gated ? HQ[r2 + h + j] : 1.0f, dz = DZQ[rh + j];
     const float sg = sig_acc(a1), sl = a1 * sg, sp = sg * (1.0f + a1 * (1.0f - sg));
     DAQ[r2 + j] = dz * a3 * sp;
-    DAQ[r2 + h + j] = dz * sl;
+    DAQ[r2 + h + j] = gated ? dz * sl : 0.0f;
   }
 }
 

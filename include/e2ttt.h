@@ -33,10 +33,8 @@
  *                  runs on the SwiGLU kernels with the gate branch held at
  *                  one (an internal copy of the state carries W3 = 0 and the
  *                  gate's pre-activation is replaced by 1, its gradient by
- *                  0).  Supported by e2ttt_chunk_forward, its timed and
- *                  allocation-free twins and e2ttt_scalar_kernels; the
- *                  kept-states forward, the decode step and the backward
- *                  return EUNSUPPORTED.
+ *                  0).  Supported by every entry point; the states and
+ *                  their adjoints at the boundary are always [W1 | W2].
  *
  * Layouts (all contiguous, row-major):
  *   q, k, v, out          [B, H, L, d]   io_dtype (fp32 or bf16)
@@ -358,9 +356,8 @@ E2TTT_API const char* e2ttt_status_string(e2ttt_status status);
  * batch, heads, dim, hidden, chunk, kind, io_dtype, decay_mode and the flags
  * (seq_len must still validate).  With E2TTT_FLAG_CHUNK_AVERAGED_DECAY or
  * E2TTT_FLAG_LACT_RULE the chunk-end update takes the means over the
- * buffered tokens, as the chunk forward does over a chunk's tokens.  The MLP
- * learner gives EUNSUPPORTED; the weight precision flags have no effect
- * (fp32 throughout).  W, M, out and the
+ * buffered tokens, as the chunk forward does over a chunk's tokens.  The
+ * weight precision flags have no effect (fp32 throughout).  W, M, out and the
  * workspace must not overlap one another or the inputs (EINVAL).  All tensor
  * pointers 16-byte aligned, the workspace 256-byte aligned with at least
  * e2ttt_decode_workspace_bytes() bytes (EWORKSPACE).  Asynchronous on
@@ -386,9 +383,11 @@ E2TTT_API e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* 
  * (or alpha taken as gamma).  Chunk-end states of every chunk are recomputed
  * by a forward pass inside the call.
  *
- * For the SwiGLU learner the descent direction depends on the chunk-start
- * weights through the learner (§5.2, App. B.5), so its reverse mode carries
- * the second-order terms of f = W2 (silu(W1 x) * (W3 x)) as well.
+ * For the SwiGLU and MLP learners the descent direction depends on the
+ * chunk-start weights through the learner (§5.2, App. B.5), so its reverse
+ * mode carries the second-order terms of f = W2 (silu(W1 x) * (W3 x)) (or of
+ * W2 silu(W1 x)) as well; the MLP learner's is the SwiGLU one with the gate
+ * held at one, on an internal [W1 | 0 | W2] copy of the states and adjoints.
  *
  * Flags: E2TTT_FLAG_QK_SILU_L2 (the prologue is recomputed and dq, dk are
  * taken back through it to the raw q, k), E2TTT_FLAG_CHUNK_AVERAGED_DECAY
@@ -399,13 +398,14 @@ E2TTT_API e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* 
  * e2ttt_chunk_backward_states returns EUNSUPPORTED for it) and
  * E2TTT_FLAG_COMPENSATED_WEIGHTS (no effect: the arithmetic is fp32).
  * Supported: kind E2TTT_LINEAR
- * with dim a multiple of 16 up to 64, or E2TTT_SWIGLU with the forward's (dim, hidden) set and at most 65535
- * batch*heads units (else EUNSUPPORTED).  The arithmetic is fp32 (the forward
+ * with dim a multiple of 16 up to 64, or E2TTT_SWIGLU / E2TTT_MLP with the
+ * forward's (dim, hidden) set and at most 65535 batch*heads units (else
+ * EUNSUPPORTED).  The arithmetic is fp32 (the forward
  * re-run too); with io_dtype E2TTT_BF16, q, k, v, dout are widened on entry
  * and dq, dk, dv rounded to nearest even on exit.  Layouts as the forward: q,
  * k, v, dout, dq, dk, dv [B,H,L,dim] of io_dtype; eta, alpha, beta,
  * deta, dalpha, dbeta [B,H,L]; W0, M0, dW_end, dM_end, dW0, dM0 [B,H,P] packed
- * as the forward's state (P = dim*dim, or 3*dim*hidden).  dW_end and
+ * as the forward's state (P = dim*dim, 3*dim*hidden or 2*dim*hidden).  dW_end and
  * dM_end may be NULL (zero gradients).  All pointers are device pointers owned
  * by the caller, 16-byte aligned (workspace 256); inputs are read-only; no
  * output may overlap another output, the workspace or any input (EINVAL).

@@ -11,7 +11,7 @@ Frobenius error of the fp64 oracle."""
 import numpy as np
 import pytest
 
-from chunk_weight_update_amd.inputs import F32, SWIGLU, make_inputs
+from chunk_weight_update_amd.inputs import F32, MLP, SWIGLU, make_inputs
 from gpu_util import log, problem_for, rel_fro
 from test_gpu_backward import NAMES, TOL, run_backward
 
@@ -30,10 +30,10 @@ def _upstream(B, H, L, d, h, seed, with_state=True):
 def check(B, H, L, d, h, C, mode=0, regime="default", seed=0, with_state=True, kind=SWIGLU,
           flags=0, tol=None):
     import oracle
-    log(f"swiglu backward case B={B} H={H} L={L} d={d} h={h} C={C} mode={mode} "
-        f"regime={regime} seed={seed} state_grads={with_state}")
+    log(f"backward case kind={kind} B={B} H={H} L={L} d={d} h={h} C={C} mode={mode} "
+        f"regime={regime} seed={seed} state_grads={with_state} flags={flags}")
     inp = make_inputs(kind, B, H, L, d, h, F32, seed=seed, regime=regime, m0_scale=0.01)
-    P = d * d if kind == oracle.LINEAR else 3 * d * h
+    P = oracle.state_size(kind, d, h)
     rng = np.random.default_rng(seed + 2000)
     dout = rng.standard_normal((B, H, L, d)).astype(np.float32)
     dW = rng.standard_normal((B, H, P)).astype(np.float32) if with_state else None
@@ -126,7 +126,7 @@ def check_bf16(kind, B, H, L, d, h, C, mode=0, regime="default", seed=0):
     log(f"bf16-io backward case kind={kind} B={B} H={H} L={L} d={d} h={h} C={C} mode={mode} "
         f"regime={regime} seed={seed}")
     inp = make_inputs(kind, B, H, L, d, h, BF16, seed=seed, regime=regime, m0_scale=0.01)
-    P = d * d if kind == oracle.LINEAR else 3 * d * h
+    P = oracle.state_size(kind, d, h)
     rng = np.random.default_rng(seed + 3000)
     do_bits = f32_to_bf16_bits(rng.standard_normal((B, H, L, d)).astype(np.float32))
     dout64 = bf16_bits_to_f32(do_bits).astype(np.float64)
@@ -159,6 +159,7 @@ def check_bf16(kind, B, H, L, d, h, C, mode=0, regime="default", seed=0):
 @pytest.mark.parametrize("kind,B,H,L,d,h,C,mode", [
     (SWIGLU, 1, 2, 300, 128, 256, 128, 0),   # the bf16 workloads' learner, ragged last chunk
     (0, 2, 2, 200, 64, 0, 64, 1),            # linear learner, alpha taken as gamma
+    (MLP, 1, 2, 300, 128, 256, 128, 0),      # MLP learner
 ])
 def test_backward_bf16_io_matches_oracle(kind, B, H, L, d, h, C, mode):
     check_bf16(kind, B, H, L, d, h, C, mode)
@@ -211,3 +212,70 @@ def test_backward_lact_rule_with_row_normalisation():
     every other gradient to the fp32 bar."""
     check(1, 2, 200, 128, 256, 64, 0, seed=11, kind=SWIGLU, flags=32 | 8,
           tol={"alpha": 1e-4, "beta": 1e-4})
+
+
+# --------------------------------------------------------------------------
+# The MLP learner f(x) = W2 silu(W1 x): the SwiGLU backward with the gate held
+# at one, on an internal [W1 | 0 | W2] copy of the states and adjoints; the
+# caller's states and gradients are [W1 | W2].
+
+@pytest.mark.parametrize("B,H,L,C,mode,regime,flags", [
+    (1, 2, 300, 128, 0, "default", 0),    # ragged last chunk, two units
+    (1, 1, 256, 256, 1, "default", 0),    # alpha taken as gamma, one chunk
+    (2, 1, 200, 64, 0, "default", 0),     # chunk below the 128-row tile
+    (1, 1, 5, 1, 0, "default", 0),        # chunks of one token
+    (1, 2, 300, 128, 0, "default", 4),    # q/k prologue
+    (1, 2, 300, 128, 1, "default", 2),    # chunk-averaged variant
+    (1, 2, 260, 128, 0, "default", 8),    # chunk-boundary row normalisation
+    (1, 2, 300, 128, 0, "default", 32),   # LaCT rule
+])
+def test_mlp_backward_matches_oracle(B, H, L, C, mode, regime, flags):
+    check(B, H, L, 128, 256, C, mode, regime, seed=13, kind=MLP, flags=flags)
+
+
+def test_mlp_backward_without_state_gradients():
+    check(1, 1, 160, 128, 256, 64, seed=14, with_state=False, kind=MLP)
+
+
+def test_mlp_backward_large_state():
+    """The MLP learner at the large-state shape (d = 768, h = 1536), short sequence."""
+    check(1, 1, 20, 768, 1536, 8, seed=15, kind=MLP)
+
+
+def test_mlp_backward_near_unit_retention():
+    """The MLP learner under near-unit retention (beta ~ 0.995, eta ~ 0.005):
+    over 200 tokens the momentum piles up and the gradients reach ~1e10 in
+    norm, so the problem itself is ill-conditioned.  Its condition is measured
+    here on the oracle: one fp32-sized relative perturbation (6e-8) of M0 moves
+    the fp64 gradients by s ~ 2e-6 relative, about 30 times the perturbation.
+    An fp32 evaluation rounds every intermediate state of the chain, so its
+    error is a sum of many such responses: the bar is the larger of the fp32
+    bar and 10 s per gradient (the case is checked to be this badly
+    conditioned: some s above 1e-6), with q, whose gradient needs no reverse
+    chain, at the fp32 bar."""
+    import oracle
+    B, H, L, d, h, C, seed = 2, 1, 200, 128, 256, 64, 13
+    inp = make_inputs(MLP, B, H, L, d, h, F32, seed=seed, regime="nearunit", m0_scale=0.01)
+    P = oracle.state_size(MLP, d, h)
+    rng = np.random.default_rng(seed + 2000)
+    dout = rng.standard_normal((B, H, L, d)).astype(np.float32)
+    dW = rng.standard_normal((B, H, P)).astype(np.float32)
+    dM = rng.standard_normal((B, H, P)).astype(np.float32)
+
+    def ref(M0):
+        return oracle.chunk_backward(MLP, inp["q64"], inp["k64"], inp["v64"], inp["eta"],
+                                     inp["alpha"], inp["beta"], inp["W0"], M0, dout, dW, dM, C,
+                                     hidden=h)
+    r0 = ref(inp["M0"])
+    pert = np.random.default_rng(99).standard_normal(inp["M0"].shape)
+    r1 = ref(np.asarray(inp["M0"], dtype=np.float64) * (1 + 6e-8 * pert))
+    sens = {n: rel_fro(r1[n], r0[n]) for n in NAMES}
+    log("  oracle sensitivity " + " ".join(f"{n}={e:.1e}" for n, e in sens.items()))
+    got = run_backward(problem_for(MLP, B, H, L, d, h, C, F32), inp, dout, dW, dM)
+    errs = {n: rel_fro(got[n], r0[n]) for n in NAMES}
+    log("  rel_fro " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    assert max(sens.values()) > 1e-6, sens
+    for n in NAMES:
+        assert np.all(np.isfinite(got[n])), n
+        bar = TOL if n == "q" else max(TOL, 10 * sens[n])
+        assert errs[n] <= bar, (n, errs[n], bar)

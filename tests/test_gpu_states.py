@@ -80,6 +80,7 @@ def _backward(prob, t, dout, dW, dM, Ws=None, Ms=None):
 @pytest.mark.parametrize("kind,B,H,L,d,h,C", [
     (SWIGLU, 1, 2, 300, 128, 256, 128),
     (LINEAR, 2, 1, 200, 64, 0, 64),
+    (MLP, 1, 2, 300, 128, 256, 128),     # kept [W1 | W2] states, expanded inside
 ])
 def test_backward_with_kept_states_matches_recompute(kind, B, H, L, d, h, C):
     import torch
@@ -88,7 +89,7 @@ def test_backward_with_kept_states_matches_recompute(kind, B, H, L, d, h, C):
     t = to_device(inp, F32)
     prob = problem_for(kind, B, H, L, d, h, C, F32)
     _, _, _, Ws, Ms = _forward_states(prob, t)
-    P = d * d if kind == LINEAR else 3 * d * h
+    P = d * d if kind == LINEAR else (2 if kind == MLP else 3) * d * h
     gen = torch.Generator(device="cuda").manual_seed(3)
     dout = torch.randn(B, H, L, d, device="cuda", generator=gen)
     dW = torch.randn(B, H, P, device="cuda", generator=gen)

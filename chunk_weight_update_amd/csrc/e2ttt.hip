@@ -62,7 +62,7 @@ struct Plan {
   float* saveW;
   float* saveM;
   // workspace offsets (bytes)
-  size_t kw, km, coef, kt, w13s, w2s, w2ts, zrow, a1s, a3s, grow, ut, gt, zt, gw, gm, gbf, gft,
+  size_t kw, km, coef, kt, w13s, w2s, w2ts, zrow, a1s, a3s, fac, grow, ut, gt, zt, gw, gm, gbf, gft,
       part, part256, qn, kn, wx, mx, total;
 };
 
@@ -196,12 +196,14 @@ e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
     q.w2ts = take(T * q.BH * q.h * q.krep * q.d);
     // Plain bf16 operands with d, h and the padded chunk multiples of 256:
     // the forward GEMMs (fwd13, fwd2) run on 256x256 tiles, and the backward
-    // recomputes A1, A3 instead of keeping an fp32 copy.
+    // takes the SiLU factors as bf16 pairs instead of an fp32 copy of A1, A3.
     q.tile256 = q.io == E2TTT_BF16 && q.krep == 1 && q.d % 256 == 0 && q.h % 256 == 0 &&
                 q.Cp % 256 == 0;
     q.zrow = take(T * q.BH * 2 * q.Cp * q.h);
-    q.a1s = q.a3s = 0;
-    if (!q.tile256) {
+    q.a1s = q.a3s = q.fac = 0;
+    if (q.tile256) {
+      q.fac = take(f4 * q.BH * q.Cp * q.h);
+    } else {
       q.a1s = take(f4 * q.BH * q.Cp * q.h);
       q.a3s = take(f4 * q.BH * q.Cp * q.h);
     }
@@ -298,7 +300,7 @@ void set_lds_attributes() {
       reinterpret_cast<const void*>(&k_phaseB<2>), reinterpret_cast<const void*>(&k_phaseA2<32>),
       reinterpret_cast<const void*>(&k_phaseA2<64>), reinterpret_cast<const void*>(&k_agg256),
       reinterpret_cast<const void*>(&k_fwd13_256), reinterpret_cast<const void*>(&k_fwd2_256),
-      reinterpret_cast<const void*>(&k_bwd256),
+      reinterpret_cast<const void*>(&k_bwd256<4>), reinterpret_cast<const void*>(&k_bwd256<6>),
       reinterpret_cast<const void*>(&k_lin_bwd_tok<1>), reinterpret_cast<const void*>(&k_lin_bwd_tok<2>),
       reinterpret_cast<const void*>(&k_lin_bwd_tok<3>), reinterpret_cast<const void*>(&k_lin_bwd_tok<4>)};
   for (const void* f : fused_kernels)
@@ -441,19 +443,27 @@ void launch_agg256(const Plan& q, const Shape& s, int r, int last, const T* ut, 
 template <typename T>
 void launch_fwd_bwd256(const Plan& q, const Shape& s, int r, const T* Q, const T* K, const T* V,
                        T* O, const T* w13s, const T* w2s, const T* w2ts, T* zrow, T* zt,
-                       const float* kw, const float* km, T* grow, T* gt, T* ut, hipStream_t st,
-                       Instr& I) {
+                       const float* kw, const float* km, T* grow, T* gt, T* ut, uint32_t* fac,
+                       hipStream_t st, Instr& I) {
   static_assert(sizeof(T) == 2 || sizeof(T) == 4, "operand type");
   if constexpr (sizeof(T) == 2) {
     E2TTT_LAUNCH(I, E2TTT_KERNEL_FWD13, k_fwd13_256,
                  dim3(grid1(q.BH * (2 * q.Cp / 256) * (2 * q.h / 256))), dim3(256),
-                 Tile256::LDS_BYTES, st, s, r, Q, K, w13s, zrow, zt);
+                 Tile256::LDS_BYTES, st, s, r, Q, K, w13s, zrow, zt, fac);
     E2TTT_LAUNCH(I, E2TTT_KERNEL_FWD2, k_fwd2_256,
                  dim3(grid1(q.BH * (2 * q.Cp / 256) * (q.d / 256))), dim3(256), Fwd2Epi::LDS_BYTES,
                  st, s, r, V, O, zrow, w2s, kw, km, grow, gt);
-    E2TTT_LAUNCH(I, E2TTT_KERNEL_BWD, k_bwd256,
-                 dim3(grid1(q.BH * (q.Cp / Bwd256::BM) * (q.h / Bwd256::BN))), dim3(256),
-                 Bwd256::LDS_BYTES, st, s, r, K, grow, w13s, w2ts, kw, km, ut);
+    // 192 hidden units per backward tile where h allows (one workgroup per
+    // CU at d = 768, h = 1536), else 128.
+    if (q.h % 192 == 0) {
+      E2TTT_LAUNCH(I, E2TTT_KERNEL_BWD, k_bwd256<6>,
+                   dim3(grid1(q.BH * (q.Cp / 256) * (q.h / 192))), dim3(256),
+                   Bwd256<6>::LDS_BYTES, st, s, r, grow, w2ts, fac, kw, km, ut);
+    } else {
+      E2TTT_LAUNCH(I, E2TTT_KERNEL_BWD, k_bwd256<4>,
+                   dim3(grid1(q.BH * (q.Cp / 256) * (q.h / 128))), dim3(256),
+                   Bwd256<4>::LDS_BYTES, st, s, r, grow, w2ts, fac, kw, km, ut);
+    }
   }
 }
 
@@ -496,7 +506,7 @@ void launch_swiglu(const Plan& q, const void* qv, const void* kv, const void* vv
     const int ri = static_cast<int>(r);
     if (q.tile256) {
       launch_fwd_bwd256(q, s, ri, Q, K, V, O, w13s, w2s, w2ts, zrow, zt, kw, km, grow, gt, ut,
-                        st, I);
+                        reinterpret_cast<uint32_t*>(ws + q.fac), st, I);
     } else {
       E2TTT_LAUNCH(I, E2TTT_KERNEL_FWD13, k_fwd13<T>,
                    dim3(grid1(q.BH * (2 * q.Cp / 128) * (2 * q.h / 128))), dim3(256), 0, st, s,

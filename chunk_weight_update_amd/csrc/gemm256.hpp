@@ -425,21 +425,34 @@ __device__ __forceinline__ void for_bands(F&& f) {
   f(Band<3>{});
 }
 
+// The SiLU factors of the backward, f1 = A3 silu'(A1) and f3 = silu(A1), of
+// K row t and hidden unit j, as one 32-bit word (bf16 f1 in the low half, f3
+// in the high half), stored in the accumulator layout of 32 x 32 blocks: the
+// block of tokens 32*tb .. +31 and units 32*hb .. +31 of unit u is 1024
+// consecutive words, word 256*(v/4) + 4*lane + v%4 for the lane and register
+// v that hold (t, j) in a 32x32 MFMA output.  The forward writes and the
+// backward reads each block with the same lanes, in 1 KB vectors.
+__device__ __forceinline__ int64_t fac_block(const Shape& s, int64_t u, int64_t tb, int64_t hb) {
+  return ((u * (s.Cp / 32) + tb) * (s.h / 32) + hb) * 1024;
+}
+
 // fwd13: [K; Q] rows x [W1; W3]^T (w13s rows interleaved in blocks of 32, so
 // accumulator blocks 2*pr and 2*pr+1 are A1 and A3 of the same 32 hidden
-// units) -> Z = silu(A1) A3 row-major, and Z^T for K rows (the backward
-// recomputes A1 and A3).
+// units) -> Z = silu(A1) A3 row-major, and for K rows Z^T and the SiLU
+// factors of the backward.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_fwd13_256(
     Shape s, int r, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-    const bf16_t* __restrict__ w13s, bf16_t* zrow, bf16_t* zt) {
+    const bf16_t* __restrict__ w13s, bf16_t* zrow, bf16_t* zt, uint32_t* fac) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  const int64_t ntn = 2 * s.h / 256, ntm = 2 * s.Cp / 256, mtK = s.Cp / 256;
+  const int64_t ntn = 2 * s.h / 256, ntm = 2 * s.Cp / 256;
   int64_t bid = xcd_logical_block();
   const int64_t nt = bid % ntn; bid /= ntn;
-  const int64_t mt = bid % ntm;
+  // K and Q row blocks alternate in the numbering, so that every XCD gets
+  // as many of the K blocks (whose epilogue writes more) as of the Q blocks.
+  const int64_t tq = bid % ntm;
   const int64_t u = bid / ntm;
-  const bool isQ = mt >= mtK;
-  const int64_t p0 = (mt - (isQ ? mtK : 0)) * 256;
+  const bool isQ = tq & 1;
+  const int64_t p0 = (tq >> 1) * 256;
   const int64_t tok0 = static_cast<int64_t>(r) * s.C;
   const int64_t nv = n_valid(s, r);
   const bf16_t* X = (isQ ? q : k) + (u * s.L + tok0) * s.d;
@@ -456,40 +469,70 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   const Acc256Pos ps;
   bf16_t* lds = reinterpret_cast<bf16_t*>(smem_raw);
+  // The band's Z rows, row-major: [64 band rows][128 units + 8] bf16, after
+  // the transposed band buffer (128 x 72 bf16).
+  constexpr int ZRW = 136;
+  bf16_t* zr = lds + 128 * 72;
   const int h = static_cast<int>(s.h);
   // Row p0 of this tile in each output; offsets below are 32-bit.
   bf16_t* zq = zrow + (u * 2 * s.Cp + (isQ ? s.Cp : 0) + p0) * s.h + nt * 128;
+  // LDS writes visible to the workgroup; vector memory left in flight.
+  auto barrier_lds = [] {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    barrier_nofence();
+  };
   // Each band in two pieces (one per 32 hidden units), kept apart by
   // scheduling barriers so that only one piece's values are live at a time.
+  // Z leaves in whole 256-byte row pieces from the staged rows; for K rows Z^T
+  // leaves through the transposed buffer, and the SiLU factors go straight
+  // out (1 KB per instruction).
   auto band = [&](auto MI, auto KROWS) {
     constexpr int mi = decltype(MI)::value;
     constexpr bool krows = decltype(KROWS)::value;
-    if constexpr (krows) __syncthreads();  // the previous Z^T band has been copied out
+    barrier_lds();  // the previous band's staged rows have been copied out
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
       const int j = ps.wn * 64 + pr * 32 + ps.r32;  // hidden unit - nt*128
       pin_acc(acc[mi][2 * pr]);
       pin_acc(acc[mi][2 * pr + 1]);
       float zv[16];
+      uint32_t fw[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int off = ps.row(mi, v) * h + j;
         const float a1 = acc[mi][2 * pr][v], a3 = s.gated ? acc[mi][2 * pr + 1][v] : 1.0f;
-        const float z = a1 * sigmoidf_(a1) * a3;
+        const float sg = sigmoidf_(a1), sl = a1 * sg;
+        const float z = sl * a3;
         zv[v] = z;
-        zq[off] = f2bf(z);
+        zr[(32 * ps.wm + 8 * (v >> 2) + 4 * ps.hf + (v & 3)) * ZRW + j] = f2bf(z);
+        if constexpr (krows)
+          fw[v] = f2bf(a3 * (sg * (1.0f + a1 * (1.0f - sg)))) |
+                  (static_cast<uint32_t>(f2bf(sl)) << 16);
       }
       if constexpr (krows) {
 #pragma unroll
         for (int vq = 0; vq < 4; ++vq)
           band_put(lds, j, ps, vq, zv[4 * vq], zv[4 * vq + 1], zv[4 * vq + 2], zv[4 * vq + 3]);
+        const int64_t tb = (p0 + 128 * ps.wm + 32 * mi) / 32;
+        const int64_t hb = nt * 4 + 2 * ps.wn + pr;
+        uint32_t* fb = fac + fac_block(s, u, tb, hb) + 4 * ps.lane;
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq)
+          *reinterpret_cast<uint4*>(fb + 256 * vq) =
+              make_uint4(fw[4 * vq], fw[4 * vq + 1], fw[4 * vq + 2], fw[4 * vq + 3]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (krows) {  // Z^T band: 128 hidden rows x 64 tokens
-      __syncthreads();
-      band_copy(lds, 128, [&](int c) { return zt + (u * s.h + nt * 128 + c) * s.Cp + p0 + 32 * mi; });
+    barrier_lds();
+    // Band row br is tile row 128*(br/32) + 32*mi + br%32.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = threadIdx.x + 256 * i, br = idx >> 4, c = idx & 15;
+      const int tr = 128 * (br >> 5) + 32 * mi + (br & 31);
+      *reinterpret_cast<uint4*>(zq + tr * h + 8 * c) =
+          *reinterpret_cast<const uint4*>(zr + br * ZRW + 8 * c);
     }
+    if constexpr (krows)  // Z^T band: 128 hidden rows x 64 tokens
+      band_copy(lds, 128, [&](int c) { return zt + (u * s.h + nt * 128 + c) * s.Cp + p0 + 32 * mi; });
   };
   if (isQ) for_bands([&](auto MI) { band(MI, Flag<false>{}); });
   else for_bands([&](auto MI) { band(MI, Flag<true>{}); });
@@ -525,10 +568,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int64_t ntn = s.d / 256, ntm = 2 * s.Cp / 256, mtK = s.Cp / 256;
   int64_t bid = xcd_logical_block();
   const int64_t nt = bid % ntn; bid /= ntn;
-  const int64_t mt = bid % ntm;
+  // K and Q row blocks alternate in the numbering, so that every XCD gets
+  // as many of the K blocks (whose epilogue writes more) as of the Q blocks.
+  const int64_t tq = bid % ntm;
   const int64_t u = bid / ntm;
-  const bool isQ = mt >= mtK;
-  const int64_t p0 = (mt - (isQ ? mtK : 0)) * 256;
+  const bool isQ = tq & 1;
+  const int64_t mt = (tq >> 1) + (isQ ? mtK : 0);  // row block of [K; Q]
+  const int64_t p0 = (tq >> 1) * 256;
   const int64_t tok0 = static_cast<int64_t>(r) * s.C;
   const int64_t nv = n_valid(s, r);
   Loader256 la, lb;
@@ -657,42 +703,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ---------------------------------------------------------------------------
-// Backward of the 256 path: dZ = g W2 together with the pre-activations
-// A1 = k W1^T, A3 = k W3^T, recomputed from the bf16 operands the forward
-// used (same products, same k order and fragment layout as k_fwd13_256, so
-// the values are the forward's own), then dA1, dA3 scaled by both kernels
-// into the feature-major operands of the aggregation.  Recomputing costs
-// 4dh flop per token; an fp32 copy of A1, A3 written by the forward and read
-// back here costs 16 bytes per token and hidden unit of memory traffic,
-// which at d = 768 takes longer than the products.
+// Backward of the 256 path: dZ = g W2 on the tile's tokens and hidden units,
+// then dA1 = dZ f1 and dA3 = dZ f3 with the SiLU factors that k_fwd13_256
+// stored for the same K rows (bf16), scaled by both kernels into the
+// feature-major operands of the aggregation.  Storing the factors costs 4
+// bytes per token and hidden unit written and read; recomputing A1 and A3
+// here instead cost twice the products of dZ (4dh flop per token) on top.
 //
-// Tile: 256 tokens x 64 hidden units of one unit.  Each of the 4 waves takes
-// 64 tokens (accumulator blocks mi = 0, 1) and all 64 units (jb = 0, 1) of
-// the three products: 12 blocks, 192 accumulator registers.  A stage holds
-// one 32-deep slab of 704 rows of 64 bytes: g rows 0..255, k rows 256..511,
-// W2^T rows of the 64 units 512..575, then their 128 w13s rows 576..703
-// (W1 and W3 in blocks of 32), stored with the swizzle of the 256 engine.
-// Loads go straight to LDS, three stages deep.
+// Tile: 256 tokens x 32*NB hidden units of one unit.  Each of the 4 waves
+// takes 64 tokens (accumulator blocks mi = 0, 1) and all 32*NB units (jb =
+// 0 .. NB-1): 2*NB blocks, 32*NB accumulator registers.  A stage holds one
+// 32-deep slab of 256 + 32*NB rows of 64 bytes: g rows 0..255, then the W2^T
+// rows of the units, stored with the swizzle of the 256 engine.  Loads go
+// straight to LDS, NST stages deep.
+template <int NB>
 struct Bwd256 {
-  static constexpr int BM = 256, BN = 64, BK = 32, NST = 3;
-  static constexpr int ROWS = 2 * BM + 3 * BN;          // 704
-  static constexpr int STAGE = ROWS * 64;               // 44 KB
-  static constexpr int LOADS = ROWS / 16 / 4;           // direct loads per wave per slab: 11
-  static constexpr size_t LDS_BYTES = static_cast<size_t>(NST) * STAGE;  // 132 KB
+  static_assert(NB % 2 == 0 && NB >= 2 && NB <= 6, "units per tile");
+  static constexpr int BM = 256, BN = 32 * NB, BK = 32, NST = 4;
+  static constexpr int ROWS = BM + BN;
+  static constexpr int STAGE = ROWS * 64;
+  static constexpr int LOADS = ROWS / 64;        // direct loads per wave per slab
+  static constexpr int SW = BM + 8;              // staged output row, bf16
+  static constexpr int STG = 4 * 64 * SW * 2;    // one epilogue pass: 4 outputs x 64 units
+  static constexpr int KS = NST * STAGE > STG ? NST * STAGE : STG;  // K^W, K^M of the tile
+  static constexpr size_t LDS_BYTES = static_cast<size_t>(KS) + 2 * BM * 4;
 };
 
+template <int NB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_bwd256(
-    Shape s, int r, const bf16_t* __restrict__ k, const bf16_t* __restrict__ grow,
-    const bf16_t* __restrict__ w13s, const bf16_t* __restrict__ w2ts,
-    const float* __restrict__ kw, const float* __restrict__ km, bf16_t* ut) {
+    Shape s, int r, const bf16_t* __restrict__ grow, const bf16_t* __restrict__ w2ts,
+    const uint32_t* __restrict__ fac, const float* __restrict__ kw,
+    const float* __restrict__ km, bf16_t* ut) {
+  using B = Bwd256<NB>;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  constexpr int NST = Bwd256::NST, SB = Bwd256::STAGE, NL = Bwd256::LOADS;
-  const int64_t ntn = s.h / Bwd256::BN, ntm = s.Cp / Bwd256::BM;
+  constexpr int NST = B::NST, SB = B::STAGE, NL = B::LOADS;
+  const int64_t ntn = s.h / B::BN, ntm = s.Cp / B::BM;
   // XCD-aware numbering, then groups of 4 token blocks x all hidden tiles
-  // with the token block fastest: the 32 workgroups an XCD runs at a time
-  // share 4 token panels and 8 weight panels in its L2 (measured 2% faster
-  // than hidden tiles fastest, whose 24 weight panels per token block do not
-  // stay in L2).
+  // with the token block fastest, so that the workgroups an XCD runs at a
+  // time share a few token and weight panels in its L2.
   int64_t bid = xcd_logical_block();
   const int64_t GT = ntm % 4 == 0 ? 4 : 1;
   const int64_t u = bid / (ntm * ntn);
@@ -700,9 +748,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int64_t wi = bid % (GT * ntn);
   const int64_t nt = wi / GT;
   const int64_t mt = bid / (GT * ntn) * GT + wi % GT;
-  const int64_t p0 = mt * Bwd256::BM, j0 = nt * Bwd256::BN;
-  const int64_t tok0 = static_cast<int64_t>(r) * s.C;
-  const int64_t nv = n_valid(s, r);
+  const int64_t p0 = mt * B::BM, j0 = nt * B::BN;
   const int64_t d = s.d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
@@ -713,78 +759,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int i = 0; i < NL; ++i) {
     const int R = 16 * (4 * i + wave) + (lane >> 2);
     const int c8 = 8 * ((lane & 3) ^ swz256(R));
-    const bf16_t* row;
-    if (R < 256) {
-      row = grow + (u * s.Cp + p0 + R) * d;
-    } else if (R < 512) {
-      const int64_t p = p0 + R - 256;
-      row = p < nv ? k + (u * s.L + tok0 + p) * d : kZeroRow256;
-    } else if (R < 576) {
-      row = w2ts + (u * s.h + j0 + R - 512) * d;
-    } else {
-      row = w13s + (u * 2 * s.h + 2 * j0 + R - 576) * d;
-    }
+    const bf16_t* row = R < B::BM ? grow + (u * s.Cp + p0 + R) * d
+                                  : w2ts + (u * s.h + j0 + R - B::BM) * d;
     src[i] = row + c8;
   }
   auto load = [&](int slab, int i) {
     char* st = smem_raw + (slab % NST) * SB;
     __builtin_amdgcn_global_load_lds(
-        static_cast<const void*>(src[i] + static_cast<int64_t>(slab) * Bwd256::BK),
+        static_cast<const void*>(src[i] + static_cast<int64_t>(slab) * B::BK),
         (__attribute__((address_space(3))) void*)(st + (4 * i + wave) * 1024), 16, 0, 0);
   };
+  // The tile's K^W, K^M (one token per thread), stored in LDS past the
+  // stages for the epilogue.
+  const float kwt = kw[(u * s.nC + r) * s.Cp + p0 + threadIdx.x];
+  const float kmt = km[(u * s.nC + r) * s.Cp + p0 + threadIdx.x];
 
-  // The epilogue's per-token kernels, loaded now so that their latency
-  // overlaps the main loop: token p0 + 64*wave + 32*mi + 8*vq + 4*hf + e.
-  f32x4_t kw4[2][4], km4[2][4];
-  {
-    const float* kwr = kw + (u * s.nC + r) * s.Cp + p0 + 64 * wave + 4 * (lane >> 5);
-    const float* kmr = km + (u * s.nC + r) * s.Cp + p0 + 64 * wave + 4 * (lane >> 5);
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int vq = 0; vq < 4; ++vq) {
-        kw4[mi][vq] = *reinterpret_cast<const f32x4_t*>(kwr + 32 * mi + 8 * vq);
-        km4[mi][vq] = *reinterpret_cast<const f32x4_t*>(kmr + 32 * mi + 8 * vq);
-      }
-  }
-  f32x16_t dz[2][2], a1[2][2], a3[2][2];
+  f32x16_t dz[2][NB];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) { dz[i][j][v] = 0.0f; a1[i][j][v] = 0.0f; a3[i][j][v] = 0.0f; }
+      for (int v = 0; v < 16; ++v) dz[i][j][v] = 0.0f;
 
   const int r32 = lane & 31, hf = lane >> 5, sw = swz256(r32);
   const int off0 = r32 * 64 + ((hf ^ sw) << 4), off1 = r32 * 64 + (((2 + hf) ^ sw) << 4);
-  const int ns = static_cast<int>(d / Bwd256::BK);
-  // Fragment set of one 16-deep step: g and k blocks of this wave's tokens,
-  // W2^T, W1, W3 blocks of the tile's units, in the order the MFMAs use them.
-  struct Frags { bf16x8_t g[2], kk[2], w2[2], w1[2], w3[2]; };
+  const int ns = static_cast<int>(d / B::BK);
+  // Fragment set of one 16-deep step: g blocks of this wave's tokens, then
+  // the W2^T blocks of the tile's units.
+  struct Frags { bf16x8_t g[2], w2[NB]; };
   auto rd = [&](const char* st, int off, int rowbase) {
     return *reinterpret_cast<const bf16x8_t*>(st + rowbase * 64 + off);
   };
   auto read_frags = [&](Frags& f, const char* st, int ks) {
     const int off = ks ? off1 : off0;
     f.g[0] = rd(st, off, 64 * wave);
-    f.w2[0] = rd(st, off, 512);
-    f.w2[1] = rd(st, off, 544);
+    f.w2[0] = rd(st, off, B::BM);
     f.g[1] = rd(st, off, 64 * wave + 32);
-    f.kk[0] = rd(st, off, 256 + 64 * wave);
-    f.w1[0] = rd(st, off, 576);
-    f.w1[1] = rd(st, off, 640);
-    f.kk[1] = rd(st, off, 256 + 64 * wave + 32);
-    f.w3[0] = rd(st, off, 608);
-    f.w3[1] = rd(st, off, 672);
+#pragma unroll
+    for (int jb = 1; jb < NB; ++jb) f.w2[jb] = rd(st, off, B::BM + 32 * jb);
   };
-  // The 12 MFMAs of one step; load slots spread the slab's refill among them.
+  // The 2*NB MFMAs of one step; the slab's refill loads go one every LSTEP
+  // MFMAs from the third of the slab's 4*NB on.
+  constexpr int LSTEP = (4 * NB - 2) / NL;
+  static_assert(LSTEP >= 1 && 2 + LSTEP * (NL - 1) < 4 * NB, "load slots");
   auto step = [&](const Frags& f, auto&& between) {
 #pragma unroll
-    for (int m = 0; m < 12; ++m) {
-      const int prod = m / 4, mi = (m >> 1) & 1, jb = m & 1;
-      if (prod == 0) dz[mi][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.g[mi], f.w2[jb], dz[mi][jb], 0, 0, 0);
-      else if (prod == 1) a1[mi][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.kk[mi], f.w1[jb], a1[mi][jb], 0, 0, 0);
-      else a3[mi][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.kk[mi], f.w3[jb], a3[mi][jb], 0, 0, 0);
+    for (int m = 0; m < 2 * NB; ++m) {
+      const int mi = m & 1, jb = m >> 1;
+      dz[mi][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.g[mi], f.w2[jb], dz[mi][jb], 0, 0, 0);
       between(m);
     }
   };
@@ -793,99 +816,140 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     Frags f0, f1;
     read_frags(f0, st, 0);
     __builtin_amdgcn_sched_barrier(0);
+    auto slot = [&](int g) {  // global MFMA index g of the slab
+      if (refill && g >= 2 && (g - 2) % LSTEP == 0 && (g - 2) / LSTEP < NL)
+        load(sl + NST - 1, (g - 2) / LSTEP);
+      __builtin_amdgcn_sched_barrier(0);
+    };
     step(f0, [&](int m) {
       if (m == 1) read_frags(f1, st, 1);
-      if (refill && m >= 2 && m < 2 + 5) load(sl + NST - 1, m - 2);
-      __builtin_amdgcn_sched_barrier(0);
+      slot(m);
     });
-    step(f1, [&](int m) {
-      if (refill && m < NL - 5) load(sl + NST - 1, m + 5);
-      __builtin_amdgcn_sched_barrier(0);
-    });
+    step(f1, [&](int m) { slot(2 * NB + m); });
   };
+  using Fac = uint4[2][2][4];
+  auto fac_load = [&](Fac& f, int p) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int j2 = 0; j2 < 2; ++j2) {
+        const int64_t tb = (p0 + 64 * wave + 32 * mi) / 32, hb = (j0 + 64 * p + 32 * j2) / 32;
+        const uint32_t* fb = fac + fac_block(s, u, tb, hb) + 4 * lane;
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq) f[mi][j2][vq] = *reinterpret_cast<const uint4*>(fb + 256 * vq);
+      }
+  };
+  Fac fa, fb;
+  // d is a multiple of 256 on this path, so ns >= 8 > NST - 1.
 #pragma unroll
   for (int p = 0; p < NST - 1; ++p)
-    if (p < ns)
 #pragma unroll
-      for (int i = 0; i < NL; ++i) load(p, i);
+    for (int i = 0; i < NL; ++i) load(p, i);
   int sl = 0;
   for (; sl < ns - (NST - 1); ++sl) {
     wait_vmcnt<NL * (NST - 2)>();
     barrier_nofence();
     body(sl, true);
   }
-  for (; sl < ns; ++sl) {
-    if (sl < ns - 1) wait_vmcnt<NL>();
-    else wait_vmcnt<0>();
+  for (; sl < ns - 1; ++sl) {
+    if (sl == ns - 3) wait_vmcnt<2 * NL>();
+    else wait_vmcnt<NL>();
     barrier_nofence();
     body(sl, false);
   }
+  // Last slab: the first epilogue pass's factors are loaded during it.
+  wait_vmcnt<0>();
+  barrier_nofence();
+  fac_load(fa, 0);
+  body(sl, false);
 
-  // Epilogue: lane values of block (mi, jb), register v: token
-  // p0 + 64*wave + 32*mi + 8*(v/4) + 4*hf + v%4, unit j0 + 32*jb + r32.  The
-  // four scaled outputs of the tile (o = dA1 K^W, dA1 K^M, dA3 K^W, dA3 K^M)
-  // are staged in LDS as [o][unit][256 tokens + 8] bf16 (the stages are
-  // free: every wave has passed the last slab's barrier and read its
-  // fragments), four tokens per 8-byte write, then copied out in whole
-  // 512-byte rows: ut row (W1 | W3 family) + 64*(j/32) + (0 | 32 for K^M) +
-  // j%32, tokens p0 .. p0+255.  (Direct 8-byte stores from the accumulator
-  // layout touch 32 rows per instruction and measured twice as slow.)
-  constexpr int SW = Bwd256::BM + 8;  // staged row, bf16
-  static_assert(4 * Bwd256::BN * SW * 2 <= static_cast<int>(Bwd256::LDS_BYTES), "staging fits");
+  // Epilogue, in NB/2 passes of 64 units (blocks jb = 2p, 2p+1).  Lane values
+  // of block (mi, jb), register v: token p0 + 64*wave + 32*mi + 8*(v/4) +
+  // 4*hf + v%4, unit j0 + 32*jb + r32; the factors of the same token and unit
+  // are word v of the lane's quarter of the factor block.  A pass stages its
+  // four scaled outputs (o = dA1 K^W, dA1 K^M, dA3 K^W, dA3 K^M) in LDS as
+  // [o][unit][256 tokens + 8] bf16 (the stages are free: every wave has
+  // passed the last slab's barrier and read its fragments), then copies them
+  // out in whole 512-byte rows: ut row (W1 | W3 family) + 64*(j/32) + (0 | 32
+  // for K^M) + j%32, tokens p0 .. p0+255.  The next pass's factors are loaded
+  // before this pass's stores, so that waiting for them does not wait for
+  // the stores.
+  constexpr int SW = B::SW;
   bf16_t* stg = reinterpret_cast<bf16_t*>(smem_raw);
-  __syncthreads();  // every wave's last fragment reads are done
+  float* ksh = reinterpret_cast<float*>(smem_raw + B::KS);
+  ksh[threadIdx.x] = kwt;
+  ksh[B::BM + threadIdx.x] = kmt;
+  auto pass = [&](auto P, const Fac& f) __attribute__((always_inline)) {
+    constexpr int p = decltype(P)::value;
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
+    for (int mi = 0; mi < 2; ++mi) {
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      pin_acc(dz[mi][jb]);
-      pin_acc(a1[mi][jb]);
-      pin_acc(a3[mi][jb]);
-    }
+      for (int j2 = 0; j2 < 2; ++j2) pin_acc(dz[mi][2 * p + j2]);
 #pragma unroll
-    for (int vq = 0; vq < 4; ++vq) {
-      const int tk = 32 * mi + 8 * vq + 4 * hf;
+      for (int vq = 0; vq < 4; ++vq) {
+        const int tk = 64 * wave + 32 * mi + 8 * vq + 4 * hf;
+        const f32x4_t kw4 = *reinterpret_cast<const f32x4_t*>(ksh + tk);
+        const f32x4_t km4 = *reinterpret_cast<const f32x4_t*>(ksh + B::BM + tk);
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
-        float x1w[4], x1m[4], x3w[4], x3m[4];
+        for (int j2 = 0; j2 < 2; ++j2) {
+          const uint4 fv = f[mi][j2][vq];
+          const uint32_t fw[4] = {fv.x, fv.y, fv.z, fv.w};
+          float x1w[4], x1m[4], x3w[4], x3m[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int v = 4 * vq + e;
-          const float A1 = a1[mi][jb][v];
-          const float A3 = s.gated ? a3[mi][jb][v] : 1.0f;
-          const float dzv = dz[mi][jb][v];
-          const float sg = sigmoidf_(A1);
-          const float d3 = s.gated ? dzv * (A1 * sg) : 0.0f;
-          const float d1 = dzv * A3 * (sg * (1.0f + A1 * (1.0f - sg)));
-          x1w[e] = kw4[mi][vq][e] * d1;
-          x1m[e] = km4[mi][vq][e] * d1;
-          x3w[e] = kw4[mi][vq][e] * d3;
-          x3m[e] = km4[mi][vq][e] * d3;
+          for (int e = 0; e < 4; ++e) {
+            const float dzv = dz[mi][2 * p + j2][4 * vq + e];
+            const float d1 = dzv * __uint_as_float(fw[e] << 16);
+            const float d3 = s.gated ? dzv * __uint_as_float(fw[e] & 0xffff0000u) : 0.0f;
+            x1w[e] = kw4[e] * d1;
+            x1m[e] = km4[e] * d1;
+            x3w[e] = kw4[e] * d3;
+            x3m[e] = km4[e] * d3;
+          }
+          const int jj = 32 * j2 + r32;
+          auto put = [&](int o, const float (&x)[4]) {
+            *reinterpret_cast<uint2*>(stg + (o * 64 + jj) * SW + tk) =
+                make_uint2(f2bf(x[0]) | (static_cast<uint32_t>(f2bf(x[1])) << 16),
+                           f2bf(x[2]) | (static_cast<uint32_t>(f2bf(x[3])) << 16));
+          };
+          put(0, x1w);
+          put(1, x1m);
+          put(2, x3w);
+          put(3, x3m);
         }
-        const int jj = 32 * jb + r32, col = 64 * wave + tk;
-        auto put = [&](int o, const float (&x)[4]) {
-          *reinterpret_cast<uint2*>(stg + (o * Bwd256::BN + jj) * SW + col) =
-              make_uint2(f2bf(x[0]) | (static_cast<uint32_t>(f2bf(x[1])) << 16),
-                         f2bf(x[2]) | (static_cast<uint32_t>(f2bf(x[3])) << 16));
-        };
-        put(0, x1w);
-        put(1, x1m);
-        put(2, x3w);
-        put(3, x3m);
       }
     }
-  }
-  __syncthreads();
+  };
   bf16_t* ub = ut + u * 4 * s.h * s.Cp + p0;
-  constexpr int VPR = Bwd256::BM / 8;  // 16-byte pieces per row
-  for (int idx = threadIdx.x; idx < 4 * Bwd256::BN * VPR; idx += 256) {
-    const int row = idx / VPR, c = idx % VPR;
-    const int o = row / Bwd256::BN, jj = row % Bwd256::BN;
-    const int64_t j = j0 + jj;
-    const int64_t dst = (o >= 2 ? 2 * s.h : 0) + 64 * (j / 32) + (o & 1 ? 32 : 0) + j % 32;
-    *reinterpret_cast<uint4*>(ub + dst * s.Cp + 8 * c) =
-        *reinterpret_cast<const uint4*>(stg + row * SW + 8 * c);
-  }
+  auto copy_out = [&](int p) __attribute__((always_inline)) {
+    constexpr int VPR = B::BM / 8;  // 16-byte pieces per row
+#pragma unroll
+    for (int i = 0; i < 4 * 64 * VPR / 256; ++i) {
+      const int idx = threadIdx.x + 256 * i;
+      const int row = idx / VPR, c = idx % VPR;
+      const int o = row / 64, jj = row % 64;
+      const int64_t j = j0 + 64 * p + jj;
+      const int64_t dst = (o >= 2 ? 2 * s.h : 0) + 64 * (j / 32) + (o & 1 ? 32 : 0) + j % 32;
+      *reinterpret_cast<uint4*>(ub + dst * s.Cp + 8 * c) =
+          *reinterpret_cast<const uint4*>(stg + row * SW + 8 * c);
+    }
+  };
+  // LDS writes visible to the workgroup; vector memory left in flight.
+  auto barrier_lds = [] {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    barrier_nofence();
+  };
+  barrier_lds();  // every wave's last fragment reads are done; K^W, K^M visible
+  auto run = [&](auto P, const Fac& cur, Fac& nxt) __attribute__((always_inline)) {
+    constexpr int p = decltype(P)::value;
+    pass(P, cur);
+    barrier_lds();
+    if constexpr (p + 1 < NB / 2) fac_load(nxt, p + 1);
+    copy_out(p);
+    if constexpr (p + 1 < NB / 2) barrier_lds();  // the stores have read the staging area
+  };
+  run(Band<0>{}, fa, fb);
+  if constexpr (NB >= 4) run(Band<1>{}, fb, fa);
+  if constexpr (NB >= 6) run(Band<2>{}, fa, fb);
 }
 
 }  // namespace e2ttt

@@ -299,8 +299,9 @@ void set_lds_attributes() {
       reinterpret_cast<const void*>(&k_phaseA<64, 2>), reinterpret_cast<const void*>(&k_phaseB<1>),
       reinterpret_cast<const void*>(&k_phaseB<2>), reinterpret_cast<const void*>(&k_phaseA2<32>),
       reinterpret_cast<const void*>(&k_phaseA2<64>), reinterpret_cast<const void*>(&k_agg256),
-      reinterpret_cast<const void*>(&k_fwd13_256), reinterpret_cast<const void*>(&k_fwd2_256),
+      reinterpret_cast<const void*>(&k_fwd13_256),
       reinterpret_cast<const void*>(&k_bwd256<4>), reinterpret_cast<const void*>(&k_bwd256<6>),
+      reinterpret_cast<const void*>(&k_fwd2r<4>), reinterpret_cast<const void*>(&k_fwd2r<6>),
       reinterpret_cast<const void*>(&k_lin_bwd_tok<1>), reinterpret_cast<const void*>(&k_lin_bwd_tok<2>),
       reinterpret_cast<const void*>(&k_lin_bwd_tok<3>), reinterpret_cast<const void*>(&k_lin_bwd_tok<4>)};
   for (const void* f : fused_kernels)
@@ -450,9 +451,17 @@ void launch_fwd_bwd256(const Plan& q, const Shape& s, int r, const T* Q, const T
     E2TTT_LAUNCH(I, E2TTT_KERNEL_FWD13, k_fwd13_256,
                  dim3(grid1(q.BH * (2 * q.Cp / 256) * (2 * q.h / 256))), dim3(256),
                  Tile256::LDS_BYTES, st, s, r, Q, K, w13s, zrow, zt, fac);
-    E2TTT_LAUNCH(I, E2TTT_KERNEL_FWD2, k_fwd2_256,
-                 dim3(grid1(q.BH * (2 * q.Cp / 256) * (q.d / 256))), dim3(256), Fwd2Epi::LDS_BYTES,
-                 st, s, r, V, O, zrow, w2s, kw, km, grow, gt);
+    // 192 output features per readout tile where d allows (one workgroup per
+    // CU at d = 768), else 128.
+    if (q.d % 192 == 0) {
+      E2TTT_LAUNCH(I, E2TTT_KERNEL_FWD2, k_fwd2r<6>,
+                   dim3(grid1(q.BH * (2 * q.Cp / 256) * (q.d / 192))), dim3(256),
+                   Fwd2R<6>::LDS_BYTES, st, s, r, V, O, zrow, w2s, kw, km, grow, gt);
+    } else {
+      E2TTT_LAUNCH(I, E2TTT_KERNEL_FWD2, k_fwd2r<4>,
+                   dim3(grid1(q.BH * (2 * q.Cp / 256) * (q.d / 128))), dim3(256),
+                   Fwd2R<4>::LDS_BYTES, st, s, r, V, O, zrow, w2s, kw, km, grow, gt);
+    }
     // 192 hidden units per backward tile where h allows (one workgroup per
     // CU at d = 768, h = 1536), else 128.
     if (q.h % 192 == 0) {

@@ -78,6 +78,12 @@ __device__ __forceinline__ void barrier_nofence() {
   asm volatile("" ::: "memory");
 }
 
+// LDS writes visible to the workgroup; vector memory left in flight.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  barrier_nofence();
+}
+
 // Wait until at most 8n of this wave's slab loads are in flight (n slabs).
 __device__ __forceinline__ void wait_slabs(int n);
 
@@ -476,11 +482,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int h = static_cast<int>(s.h);
   // Row p0 of this tile in each output; offsets below are 32-bit.
   bf16_t* zq = zrow + (u * 2 * s.Cp + (isQ ? s.Cp : 0) + p0) * s.h + nt * 128;
-  // LDS writes visible to the workgroup; vector memory left in flight.
-  auto barrier_lds = [] {
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    barrier_nofence();
-  };
   // Each band in two pieces (one per 32 hidden units), kept apart by
   // scheduling barriers so that only one piece's values are live at a time.
   // Z leaves in whole 256-byte row pieces from the staged rows; for K rows Z^T
@@ -538,220 +539,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   else for_bands([&](auto MI) { band(MI, Flag<true>{}); });
 }
 
-// fwd2: Z rows x W2^T -> Y; the readout for Q rows, g = v - Y for K rows
-// (row-major) and K^W g, K^M g feature-major (rows 64*(i/32) + i%32, +32 for
-// the momentum copy).
-//
-// Epilogue, one accumulator band at a time (band mi = tile rows 32*mi +
-// [0,32) of both wave rows; band row br = 32*wm + [0,32)): the band's rows
-// of v come straight into LDS (512-byte rows, in pairs padded to 1056 bytes
-// so that the two lane halves, 4 rows apart, read distinct banks), the next
-// band's while this one is computed; each lane reads its values of v there
-// and writes g back in place; g and the readout leave in whole rows, and the
-// two scaled copies of g go through the transposing band buffers.  The
-// chunk's kernels for the tile's 256 tokens sit in LDS as well.
-struct Fwd2Epi {
-  static constexpr int PAIR = 1056;                    // two 512-byte rows + pad
-  static constexpr int GBUF = 32 * PAIR;               // one band of v / g: 64 rows
-  static constexpr int TBUF = 256 * 72 * 2;            // one transposed band (band_put)
-  static constexpr int G0 = 0, G1 = GBUF, TW = 2 * GBUF, TM = TW + TBUF, KS = TM + TBUF;
-  static constexpr size_t LDS_BYTES = KS + 2 * 256 * 4;  // + K^W, K^M of the tile: 140 KB
-  static_assert(LDS_BYTES >= Tile256::LDS_BYTES, "the main loop's stages fit");
-  __device__ static int off(int br, int c) { return (br >> 1) * PAIR + (br & 1) * 512 + 2 * c; }
-};
-
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_fwd2_256(
-    Shape s, int r, const bf16_t* __restrict__ v, bf16_t* out, const bf16_t* __restrict__ zrow,
-    const bf16_t* __restrict__ w2s, const float* __restrict__ kw, const float* __restrict__ km,
-    bf16_t* grow, bf16_t* gt) {
-  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  const int64_t ntn = s.d / 256, ntm = 2 * s.Cp / 256, mtK = s.Cp / 256;
-  int64_t bid = xcd_logical_block();
-  const int64_t nt = bid % ntn; bid /= ntn;
-  // K and Q row blocks alternate in the numbering, so that every XCD gets
-  // as many of the K blocks (whose epilogue writes more) as of the Q blocks.
-  const int64_t tq = bid % ntm;
-  const int64_t u = bid / ntm;
-  const bool isQ = tq & 1;
-  const int64_t mt = (tq >> 1) + (isQ ? mtK : 0);  // row block of [K; Q]
-  const int64_t p0 = (tq >> 1) * 256;
-  const int64_t tok0 = static_cast<int64_t>(r) * s.C;
-  const int64_t nv = n_valid(s, r);
-  Loader256 la, lb;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c8 = 8 * loader256_chunk(i);
-    la.rowp[i] = zrow + (u * 2 * s.Cp + mt * 256 + loader256_row(i)) * s.h + c8;
-    lb.rowp[i] = w2s + (u * s.d + nt * 256 + loader256_row(i)) * s.h + c8;
-  }
-  f32x16_t acc[4][4];
-  gemm_tile256(acc, la, lb, 0, s.h, smem_raw);
-
-  const Acc256Pos ps;
-  const int64_t d = s.d;
-  const int nvt = static_cast<int>(nv - p0 < 256 ? nv - p0 : 256);  // valid rows of the tile
-  using E = Fwd2Epi;
-  // Tile row of band row br in band mi.
-  auto trow = [](int mi, int br) { return 128 * (br >> 5) + 32 * mi + (br & 31); };
-  // Band row of this lane's register vv.
-  auto brow = [&](int vv) { return 32 * ps.wm + 8 * (vv >> 2) + 4 * ps.hf + (vv & 3); };
-  // Copy band mi's 64 rows from G out to dst + tile row * d (rows below
-  // `valid` only), 16 bytes per thread and step; 8 steps per thread.
-  auto rows_out = [&](int mi, const char* G, bf16_t* dst, int valid) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = threadIdx.x + 256 * i;
-      const int k = idx >> 6, rr = (idx >> 5) & 1, c16 = idx & 31;
-      const int tr = trow(mi, 2 * k + rr);
-      const uint4 x = *reinterpret_cast<const uint4*>(G + k * E::PAIR + rr * 512 + 16 * c16);
-      if (tr < valid) *reinterpret_cast<uint4*>(dst + tr * d + 8 * c16) = x;
-    }
-  };
-  if (isQ) {
-    bf16_t* o = out + (u * s.L + tok0 + p0) * d + nt * 256;
-    char* G = smem_raw + E::G0;
-    auto band = [&](auto MI) {
-      constexpr int mi = decltype(MI)::value;
-      __syncthreads();  // the main loop's stages, or the previous band's rows, are free
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        pin_acc(acc[mi][ni]);
-#pragma unroll
-        for (int vv = 0; vv < 16; ++vv)
-          *reinterpret_cast<bf16_t*>(G + E::off(brow(vv), ps.col(ni))) = f2bf(acc[mi][ni][vv]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      __syncthreads();
-      rows_out(mi, G, o, nvt);
-    };
-    for_bands(band);
-    return;
-  }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const bf16_t* vs = v + (u * s.L + tok0 + p0) * d + nt * 256;
-  bf16_t* gr = grow + (u * s.Cp + p0) * d + nt * 256;
-  bf16_t* gbase = gt + u * 2 * s.d * s.Cp + p0;
-  bf16_t* tW = reinterpret_cast<bf16_t*>(smem_raw + E::TW);
-  bf16_t* tM = reinterpret_cast<bf16_t*>(smem_raw + E::TM);
-  const float* kws = reinterpret_cast<const float*>(smem_raw + E::KS);
-  const float* kms = kws + 256;
-  // Band mi's v rows into G: wave w loads row pairs w, w+4, ..., w+28 (lane
-  // l: row 2k + l/32, bytes 16*(l%32)); rows past the valid tokens read zeros.
-  auto load_v = [&](int mi, char* G) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int k = 4 * i + wave;
-      const int tr = trow(mi, 2 * k + (lane >> 5));
-      const bf16_t* src = (tr < nvt ? vs + tr * d : kZeroRow256) + 8 * (lane & 31);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
-                                       (__attribute__((address_space(3))) void*)(G + k * E::PAIR),
-                                       16, 0, 0);
-    }
-  };
-  __syncthreads();  // the main loop's stages are free
-  if (wave < 2) {   // K^W (wave 0), K^M (wave 1) of the tile's tokens: 1 KB each
-    const float* src = (wave == 0 ? kw : km) + (u * s.nC + r) * s.Cp + p0 + 4 * lane;
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
-                                     (__attribute__((address_space(3))) void*)(smem_raw + E::KS + 1024 * wave),
-                                     16, 0, 0);
-  }
-  load_v(0, smem_raw + E::G0);
-  auto band = [&](auto MI) {
-    constexpr int mi = decltype(MI)::value;
-    char* G = smem_raw + ((mi & 1) ? E::G1 : E::G0);
-    if constexpr (mi > 0) barrier_nofence();  // band mi-1's rows have been copied out
-    if constexpr (mi < 3) load_v(mi + 1, smem_raw + ((mi & 1) ? E::G0 : E::G1));
-    // Band mi's rows (and the kernels) have landed: after them this wave
-    // issued band mi-1's 24 stores and band mi+1's 8 loads.
-    wait_vmcnt<(mi > 0 ? 24 : 0) + (mi < 3 ? 8 : 0)>();
-    barrier_nofence();
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      pin_acc(acc[mi][ni]);
-      const int c = ps.col(ni);
-      float g[16];
-#pragma unroll
-      for (int vv = 0; vv < 16; ++vv) {
-        bf16_t* e = reinterpret_cast<bf16_t*>(G + E::off(brow(vv), c));
-        g[vv] = bf2f(*e) - acc[mi][ni][vv];
-        *e = f2bf(g[vv]);
-      }
-#pragma unroll
-      for (int vq = 0; vq < 4; ++vq) {
-        const int t0 = 128 * ps.wm + 32 * mi + 8 * vq + 4 * ps.hf;
-        const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(kws + t0);
-        const f32x4_t m4 = *reinterpret_cast<const f32x4_t*>(kms + t0);
-        band_put(tW, c, ps, vq, w4[0] * g[4 * vq], w4[1] * g[4 * vq + 1], w4[2] * g[4 * vq + 2],
-                 w4[3] * g[4 * vq + 3]);
-        band_put(tM, c, ps, vq, m4[0] * g[4 * vq], m4[1] * g[4 * vq + 1], m4[2] * g[4 * vq + 2],
-                 m4[3] * g[4 * vq + 3]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    __syncthreads();
-    rows_out(mi, G, gr, 256);
-    band_copy(tW, 256, [&](int c) {
-      const int64_t i = nt * 256 + c;
-      return gbase + (64 * (i / 32) + i % 32) * s.Cp + 32 * mi;
-    });
-    band_copy(tM, 256, [&](int c) {
-      const int64_t i = nt * 256 + c;
-      return gbase + (64 * (i / 32) + 32 + i % 32) * s.Cp + 32 * mi;
-    });
-  };
-  for_bands(band);
-}
-
 // ---------------------------------------------------------------------------
-// Backward of the 256 path: dZ = g W2 on the tile's tokens and hidden units,
-// then dA1 = dZ f1 and dA3 = dZ f3 with the SiLU factors that k_fwd13_256
-// stored for the same K rows (bf16), scaled by both kernels into the
-// feature-major operands of the aggregation.  Storing the factors costs 4
-// bytes per token and hidden unit written and read; recomputing A1 and A3
-// here instead cost twice the products of dZ (4dh flop per token) on top.
-//
-// Tile: 256 tokens x 32*NB hidden units of one unit.  Each of the 4 waves
-// takes 64 tokens (accumulator blocks mi = 0, 1) and all 32*NB units (jb =
-// 0 .. NB-1): 2*NB blocks, 32*NB accumulator registers.  A stage holds one
-// 32-deep slab of 256 + 32*NB rows of 64 bytes: g rows 0..255, then the W2^T
-// rows of the units, stored with the swizzle of the 256 engine.  Loads go
-// straight to LDS, NST stages deep.
+// Row engine: a 256 x 32*NB output tile, each of the 4 waves taking 64 rows
+// (accumulator blocks mi = 0, 1) and all 32*NB columns (jb = 0 .. NB-1):
+// 2*NB blocks, 32*NB accumulator registers.  A stage holds one 32-deep slab
+// of 256 + 32*NB rows of 64 bytes (the A rows, then the B rows), stored with
+// the swizzle of the 256 engine; loads go straight to LDS, NST stages deep,
+// spread one every few MFMAs over the slab.  Used where a 256 x 256 tile
+// would leave CUs idle: 256 x 192 tiles put one workgroup on every CU at
+// d = 768 (the readout GEMM) and h = 1536 (the backward's dZ).
 template <int NB>
-struct Bwd256 {
-  static_assert(NB % 2 == 0 && NB >= 2 && NB <= 6, "units per tile");
+struct Rows256 {
+  static_assert(NB % 2 == 0 && NB >= 2 && NB <= 6, "columns per tile");
   static constexpr int BM = 256, BN = 32 * NB, BK = 32, NST = 4;
   static constexpr int ROWS = BM + BN;
   static constexpr int STAGE = ROWS * 64;
-  static constexpr int LOADS = ROWS / 64;        // direct loads per wave per slab
-  static constexpr int SW = BM + 8;              // staged output row, bf16
-  static constexpr int STG = 4 * 64 * SW * 2;    // one epilogue pass: 4 outputs x 64 units
-  static constexpr int KS = NST * STAGE > STG ? NST * STAGE : STG;  // K^W, K^M of the tile
-  static constexpr size_t LDS_BYTES = static_cast<size_t>(KS) + 2 * BM * 4;
+  static constexpr int LOADS = ROWS / 64;  // direct loads per wave per slab
+  static constexpr int STAGES_BYTES = NST * STAGE;
 };
 
-template <int NB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_bwd256(
-    Shape s, int r, const bf16_t* __restrict__ grow, const bf16_t* __restrict__ w2ts,
-    const uint32_t* __restrict__ fac, const float* __restrict__ kw,
-    const float* __restrict__ km, bf16_t* ut) {
-  using B = Bwd256<NB>;
-  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  constexpr int NST = B::NST, SB = B::STAGE, NL = B::LOADS;
-  const int64_t ntn = s.h / B::BN, ntm = s.Cp / B::BM;
-  // XCD-aware numbering, then groups of 4 token blocks x all hidden tiles
-  // with the token block fastest, so that the workgroups an XCD runs at a
-  // time share a few token and weight panels in its L2.
-  int64_t bid = xcd_logical_block();
-  const int64_t GT = ntm % 4 == 0 ? 4 : 1;
-  const int64_t u = bid / (ntm * ntn);
-  bid %= ntm * ntn;
-  const int64_t wi = bid % (GT * ntn);
-  const int64_t nt = wi / GT;
-  const int64_t mt = bid / (GT * ntn) * GT + wi % GT;
-  const int64_t p0 = mt * B::BM, j0 = nt * B::BN;
-  const int64_t d = s.d;
+// acc[mi][jb] = sum over k < 32*ns of A(64*wave + 32*mi + i, k) B(32*jb + j, k)
+// with A row R at arow(R) and B row R at brow(R) (k contiguous).  before_last()
+// runs after the last slab's wait and barrier, before its MFMAs (an
+// epilogue's first loads overlap them).  ns >= NST - 1.
+template <int NB, typename ARow, typename BRow, typename Hook>
+__device__ __forceinline__ void gemm_rows256(f32x16_t (&acc)[2][NB], ARow arow, BRow brow, int ns,
+                                             char* smem, Hook&& before_last) {
+  using G = Rows256<NB>;
+  constexpr int NST = G::NST, SB = G::STAGE, NL = G::LOADS;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-
   // Source of this lane's piece for load i: stage row R = 16*(4i + wave) +
   // lane/4, physical piece lane%4 = logical k-chunk (lane%4) ^ swz256(R).
   const bf16_t* src[NL];
@@ -759,45 +575,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int i = 0; i < NL; ++i) {
     const int R = 16 * (4 * i + wave) + (lane >> 2);
     const int c8 = 8 * ((lane & 3) ^ swz256(R));
-    const bf16_t* row = R < B::BM ? grow + (u * s.Cp + p0 + R) * d
-                                  : w2ts + (u * s.h + j0 + R - B::BM) * d;
-    src[i] = row + c8;
+    src[i] = (R < G::BM ? arow(R) : brow(R - G::BM)) + c8;
   }
   auto load = [&](int slab, int i) {
-    char* st = smem_raw + (slab % NST) * SB;
+    char* st = smem + (slab % NST) * SB;
     __builtin_amdgcn_global_load_lds(
-        static_cast<const void*>(src[i] + static_cast<int64_t>(slab) * B::BK),
+        static_cast<const void*>(src[i] + static_cast<int64_t>(slab) * G::BK),
         (__attribute__((address_space(3))) void*)(st + (4 * i + wave) * 1024), 16, 0, 0);
   };
-  // The tile's K^W, K^M (one token per thread), stored in LDS past the
-  // stages for the epilogue.
-  const float kwt = kw[(u * s.nC + r) * s.Cp + p0 + threadIdx.x];
-  const float kmt = km[(u * s.nC + r) * s.Cp + p0 + threadIdx.x];
-
-  f32x16_t dz[2][NB];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) dz[i][j][v] = 0.0f;
-
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
   const int r32 = lane & 31, hf = lane >> 5, sw = swz256(r32);
   const int off0 = r32 * 64 + ((hf ^ sw) << 4), off1 = r32 * 64 + (((2 + hf) ^ sw) << 4);
-  const int ns = static_cast<int>(d / B::BK);
-  // Fragment set of one 16-deep step: g blocks of this wave's tokens, then
-  // the W2^T blocks of the tile's units.
-  struct Frags { bf16x8_t g[2], w2[NB]; };
+  // Fragment set of one 16-deep step: the A blocks of this wave's rows, then
+  // the B blocks of the tile's columns.
+  struct Frags { bf16x8_t a[2], b[NB]; };
   auto rd = [&](const char* st, int off, int rowbase) {
     return *reinterpret_cast<const bf16x8_t*>(st + rowbase * 64 + off);
   };
   auto read_frags = [&](Frags& f, const char* st, int ks) {
     const int off = ks ? off1 : off0;
-    f.g[0] = rd(st, off, 64 * wave);
-    f.w2[0] = rd(st, off, B::BM);
-    f.g[1] = rd(st, off, 64 * wave + 32);
+    f.a[0] = rd(st, off, 64 * wave);
+    f.b[0] = rd(st, off, G::BM);
+    f.a[1] = rd(st, off, 64 * wave + 32);
 #pragma unroll
-    for (int jb = 1; jb < NB; ++jb) f.w2[jb] = rd(st, off, B::BM + 32 * jb);
+    for (int jb = 1; jb < NB; ++jb) f.b[jb] = rd(st, off, G::BM + 32 * jb);
   };
   // The 2*NB MFMAs of one step; the slab's refill loads go one every LSTEP
   // MFMAs from the third of the slab's 4*NB on.
@@ -807,12 +613,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int m = 0; m < 2 * NB; ++m) {
       const int mi = m & 1, jb = m >> 1;
-      dz[mi][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.g[mi], f.w2[jb], dz[mi][jb], 0, 0, 0);
+      acc[mi][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[jb], acc[mi][jb], 0, 0, 0);
       between(m);
     }
   };
   auto body = [&](int sl, bool refill) {
-    const char* st = smem_raw + (sl % NST) * SB;
+    const char* st = smem + (sl % NST) * SB;
     Frags f0, f1;
     read_frags(f0, st, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -827,20 +633,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     });
     step(f1, [&](int m) { slot(2 * NB + m); });
   };
-  using Fac = uint4[2][2][4];
-  auto fac_load = [&](Fac& f, int p) __attribute__((always_inline)) {
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int j2 = 0; j2 < 2; ++j2) {
-        const int64_t tb = (p0 + 64 * wave + 32 * mi) / 32, hb = (j0 + 64 * p + 32 * j2) / 32;
-        const uint32_t* fb = fac + fac_block(s, u, tb, hb) + 4 * lane;
-#pragma unroll
-        for (int vq = 0; vq < 4; ++vq) f[mi][j2][vq] = *reinterpret_cast<const uint4*>(fb + 256 * vq);
-      }
-  };
-  Fac fa, fb;
-  // d is a multiple of 256 on this path, so ns >= 8 > NST - 1.
 #pragma unroll
   for (int p = 0; p < NST - 1; ++p)
 #pragma unroll
@@ -857,11 +649,80 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     barrier_nofence();
     body(sl, false);
   }
-  // Last slab: the first epilogue pass's factors are loaded during it.
   wait_vmcnt<0>();
   barrier_nofence();
-  fac_load(fa, 0);
+  before_last();
   body(sl, false);
+}
+
+// ---------------------------------------------------------------------------
+// Backward of the 256 path: dZ = g W2 on the tile's tokens and hidden units,
+// then dA1 = dZ f1 and dA3 = dZ f3 with the SiLU factors that k_fwd13_256
+// stored for the same K rows (bf16), scaled by both kernels into the
+// feature-major operands of the aggregation.  Storing the factors costs 4
+// bytes per token and hidden unit written and read; recomputing A1 and A3
+// here instead cost twice the products of dZ (4dh flop per token) on top.
+//
+// Tile: 256 tokens x 32*NB hidden units of one unit on the row engine (A = g
+// rows, B = W2^T rows of the units).
+template <int NB>
+struct Bwd256 {
+  using G = Rows256<NB>;
+  static constexpr int BM = G::BM;
+  static constexpr int SW = BM + 8;              // staged output row, bf16
+  static constexpr int STG = 4 * 64 * SW * 2;    // one epilogue pass: 4 outputs x 64 units
+  static constexpr int KS = G::STAGES_BYTES > STG ? G::STAGES_BYTES : STG;  // K^W, K^M
+  static constexpr size_t LDS_BYTES = static_cast<size_t>(KS) + 2 * BM * 4;
+};
+
+template <int NB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_bwd256(
+    Shape s, int r, const bf16_t* __restrict__ grow, const bf16_t* __restrict__ w2ts,
+    const uint32_t* __restrict__ fac, const float* __restrict__ kw,
+    const float* __restrict__ km, bf16_t* ut) {
+  using B = Bwd256<NB>;
+  constexpr int BN = 32 * NB;
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  const int64_t ntn = s.h / BN, ntm = s.Cp / B::BM;
+  // XCD-aware numbering, then groups of 4 token blocks x all hidden tiles
+  // with the token block fastest, so that the workgroups an XCD runs at a
+  // time share a few token and weight panels in its L2.
+  int64_t bid = xcd_logical_block();
+  const int64_t GT = ntm % 4 == 0 ? 4 : 1;
+  const int64_t u = bid / (ntm * ntn);
+  bid %= ntm * ntn;
+  const int64_t wi = bid % (GT * ntn);
+  const int64_t nt = wi / GT;
+  const int64_t mt = bid / (GT * ntn) * GT + wi % GT;
+  const int64_t p0 = mt * B::BM, j0 = nt * BN;
+  const int64_t d = s.d;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r32 = lane & 31, hf = lane >> 5;
+  // The tile's K^W, K^M (one token per thread), stored in LDS past the
+  // stages for the epilogue.
+  const float kwt = kw[(u * s.nC + r) * s.Cp + p0 + threadIdx.x];
+  const float kmt = km[(u * s.nC + r) * s.Cp + p0 + threadIdx.x];
+
+  using Fac = uint4[2][2][4];
+  auto fac_load = [&](Fac& f, int p) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int j2 = 0; j2 < 2; ++j2) {
+        const int64_t tb = (p0 + 64 * wave + 32 * mi) / 32, hb = (j0 + 64 * p + 32 * j2) / 32;
+        const uint32_t* fb = fac + fac_block(s, u, tb, hb) + 4 * lane;
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq) f[mi][j2][vq] = *reinterpret_cast<const uint4*>(fb + 256 * vq);
+      }
+  };
+  Fac fa, fb;
+  f32x16_t dz[2][NB];
+  // d is a multiple of 256 on this path, so ns >= 8 > NST - 1.  The first
+  // epilogue pass's factors are loaded during the last slab.
+  gemm_rows256<NB>(
+      dz, [&](int R) { return grow + (u * s.Cp + p0 + R) * d; },
+      [&](int R) { return w2ts + (u * s.h + j0 + R) * d; }, static_cast<int>(d / 32), smem_raw,
+      [&]() __attribute__((always_inline)) { fac_load(fa, 0); });
 
   // Epilogue, in NB/2 passes of 64 units (blocks jb = 2p, 2p+1).  Lane values
   // of block (mi, jb), register v: token p0 + 64*wave + 32*mi + 8*(v/4) +
@@ -933,11 +794,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           *reinterpret_cast<const uint4*>(stg + row * SW + 8 * c);
     }
   };
-  // LDS writes visible to the workgroup; vector memory left in flight.
-  auto barrier_lds = [] {
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    barrier_nofence();
-  };
   barrier_lds();  // every wave's last fragment reads are done; K^W, K^M visible
   auto run = [&](auto P, const Fac& cur, Fac& nxt) __attribute__((always_inline)) {
     constexpr int p = decltype(P)::value;
@@ -950,6 +806,193 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   run(Band<0>{}, fa, fb);
   if constexpr (NB >= 4) run(Band<1>{}, fb, fa);
   if constexpr (NB >= 6) run(Band<2>{}, fa, fb);
+}
+
+// ---------------------------------------------------------------------------
+// fwd2 on the row engine: Z rows x W2^T -> Y for 256 tokens x 32*NB output
+// features (NB = 6: 256 workgroups at d = 768, one per CU, where 256 x 256
+// tiles gave 192).  The readout for Q rows; g = v - Y for K rows (row-major)
+// and K^W g, K^M g feature-major (rows 64*(i/32) + i%32, +32 for the
+// momentum copy): the operands of the backward and of the aggregation's
+// second family.
+//
+// Epilogue in NB/2 passes of 64 features (blocks jb = 2p, 2p+1).  A pass
+// stages the tile's 256 x 64 values row-major in LDS ([256][64 + 8] bf16:
+// the two lane halves, 4 rows apart, hit distinct banks), for K rows first
+// filled with v (loaded into registers during the previous pass, or during
+// the last slab for pass 0, 16-byte pieces of whole 128-byte row segments),
+// which each lane reads and overwrites with g; K^W g and K^M g go through
+// two transposed buffers ([64 features][256 + 8] bf16); then everything
+// leaves in 16-byte pieces of whole rows.  Rows past the chunk's valid
+// tokens read v from a device zero row; the readout writes only valid rows.
+template <int NB>
+struct Fwd2R {
+  using G = Rows256<NB>;
+  static constexpr int BM = G::BM;
+  static constexpr int VW = 64 + 8;                 // staged row, bf16
+  static constexpr int TWW = BM + 8;                // transposed row, bf16
+  static constexpr int VR = 0;                      // [256][VW]
+  static constexpr int TW = VR + BM * VW * 2;       // [64][TWW]
+  static constexpr int TM = TW + 64 * TWW * 2;
+  static constexpr int END = TM + 64 * TWW * 2;
+  static constexpr int KS = G::STAGES_BYTES > END ? G::STAGES_BYTES : END;  // K^W, K^M
+  static constexpr size_t LDS_BYTES = static_cast<size_t>(KS) + 2 * BM * 4;
+};
+
+template <int NB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_fwd2r(
+    Shape s, int r, const bf16_t* __restrict__ v, bf16_t* out, const bf16_t* __restrict__ zrow,
+    const bf16_t* __restrict__ w2s, const float* __restrict__ kw, const float* __restrict__ km,
+    bf16_t* grow, bf16_t* gt) {
+  using E = Fwd2R<NB>;
+  constexpr int BN = 32 * NB, VW = E::VW, TWW = E::TWW;
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  const int64_t ntn = s.d / BN, ntm = 2 * s.Cp / 256, mtK = s.Cp / 256;
+  int64_t bid = xcd_logical_block();
+  const int64_t nt = bid % ntn; bid /= ntn;
+  // K and Q row blocks alternate in the numbering, so that every XCD gets
+  // as many of the K blocks (whose epilogue writes more) as of the Q blocks.
+  const int64_t tq = bid % ntm;
+  const int64_t u = bid / ntm;
+  const bool isQ = tq & 1;
+  const int64_t mt = (tq >> 1) + (isQ ? mtK : 0);  // row block of [K; Q]
+  const int64_t p0 = (tq >> 1) * 256, n0 = nt * BN;
+  const int64_t tok0 = static_cast<int64_t>(r) * s.C;
+  const int64_t nv = n_valid(s, r);
+  const int nvt = static_cast<int>(nv - p0 < 256 ? nv - p0 : 256);  // valid rows of the tile
+  const int64_t d = s.d;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r32 = lane & 31, hf = lane >> 5;
+  float kwt = 0.0f, kmt = 0.0f;
+  if (!isQ) {
+    kwt = kw[(u * s.nC + r) * s.Cp + p0 + threadIdx.x];
+    kmt = km[(u * s.nC + r) * s.Cp + p0 + threadIdx.x];
+  }
+  // v of pass p: thread piece i (0..7) is row (tid + 256 i) / 8, 16-byte
+  // piece (tid + 256 i) % 8 of the pass's 128-byte row segment.
+  const bf16_t* vs = v + (u * s.L + tok0 + p0) * d + n0;
+  // (One wide vector value: an array of uint4 here was placed in scratch.)
+  typedef uint32_t VReg __attribute__((ext_vector_type(32)));
+  auto v_load = [&](VReg& x, int p) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = threadIdx.x + 256 * i, row = idx >> 3, c = idx & 7;
+      const bf16_t* src = row < nvt ? vs + row * d + 64 * p + 8 * c : kZeroRow256;
+      const uint4 y = *reinterpret_cast<const uint4*>(src);
+      x[4 * i] = y.x;
+      x[4 * i + 1] = y.y;
+      x[4 * i + 2] = y.z;
+      x[4 * i + 3] = y.w;
+    }
+  };
+  VReg va, vb;
+  f32x16_t acc[2][NB];
+  gemm_rows256<NB>(
+      acc, [&](int R) { return zrow + (u * 2 * s.Cp + mt * 256 + R) * s.h; },
+      [&](int R) { return w2s + (u * d + n0 + R) * s.h; }, static_cast<int>(s.h / 32), smem_raw,
+      [&]() __attribute__((always_inline)) {
+        if (!isQ) v_load(va, 0);
+      });
+
+  bf16_t* vr = reinterpret_cast<bf16_t*>(smem_raw + E::VR);
+  bf16_t* tW = reinterpret_cast<bf16_t*>(smem_raw + E::TW);
+  bf16_t* tM = reinterpret_cast<bf16_t*>(smem_raw + E::TM);
+  float* ksh = reinterpret_cast<float*>(smem_raw + E::KS);
+  // Staged row of this lane's register v in block mi.
+  auto srow = [&](int mi, int vv) { return 64 * wave + 32 * mi + 8 * (vv >> 2) + 4 * hf + (vv & 3); };
+  // The staged rows out: row t's 64 features to dst + t*d (rows below
+  // `valid`), 16 bytes per thread and step.
+  auto rows_out = [&](bf16_t* dst, int valid) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = threadIdx.x + 256 * i, row = idx >> 3, c = idx & 7;
+      const uint4 x = *reinterpret_cast<const uint4*>(vr + row * VW + 8 * c);
+      if (row < valid) *reinterpret_cast<uint4*>(dst + row * d + 8 * c) = x;
+    }
+  };
+  if (isQ) {
+    bf16_t* o = out + (u * s.L + tok0 + p0) * d + n0;
+    auto qpass = [&](auto P) __attribute__((always_inline)) {
+      constexpr int p = decltype(P)::value;
+      barrier_lds();  // the stages, or the previous pass's rows, are free
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int j2 = 0; j2 < 2; ++j2) {
+          pin_acc(acc[mi][2 * p + j2]);
+#pragma unroll
+          for (int vv = 0; vv < 16; ++vv)
+            vr[srow(mi, vv) * VW + 32 * j2 + r32] = f2bf(acc[mi][2 * p + j2][vv]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      barrier_lds();
+      rows_out(o + 64 * p, nvt);
+    };
+    qpass(Band<0>{});
+    if constexpr (NB >= 4) qpass(Band<1>{});
+    if constexpr (NB >= 6) qpass(Band<2>{});
+    return;
+  }
+  bf16_t* gr = grow + (u * s.Cp + p0) * d + n0;
+  bf16_t* gbase = gt + u * 2 * d * s.Cp + p0;
+  auto kpass = [&](auto P, const VReg& cur, VReg& nxt) __attribute__((always_inline)) {
+    constexpr int p = decltype(P)::value;
+    barrier_lds();  // the stages, or the previous pass's buffers, are free
+    if constexpr (p == 0) {
+      ksh[threadIdx.x] = kwt;
+      ksh[256 + threadIdx.x] = kmt;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = threadIdx.x + 256 * i, row = idx >> 3, c = idx & 7;
+      *reinterpret_cast<uint4*>(vr + row * VW + 8 * c) =
+          make_uint4(cur[4 * i], cur[4 * i + 1], cur[4 * i + 2], cur[4 * i + 3]);
+    }
+    barrier_lds();
+    if constexpr (p + 1 < NB / 2) v_load(nxt, p + 1);  // before this pass's stores
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int j2 = 0; j2 < 2; ++j2) {
+        pin_acc(acc[mi][2 * p + j2]);
+        const int f = 32 * j2 + r32;
+        float g[16];
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) {
+          bf16_t* e = vr + srow(mi, vv) * VW + f;
+          g[vv] = bf2f(*e) - acc[mi][2 * p + j2][vv];
+          *e = f2bf(g[vv]);
+        }
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq) {
+          const int t0 = 64 * wave + 32 * mi + 8 * vq + 4 * hf;
+          const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(ksh + t0);
+          const f32x4_t m4 = *reinterpret_cast<const f32x4_t*>(ksh + 256 + t0);
+          *reinterpret_cast<uint2*>(tW + f * TWW + t0) =
+              make_uint2(f2bf(w4[0] * g[4 * vq]) | (static_cast<uint32_t>(f2bf(w4[1] * g[4 * vq + 1])) << 16),
+                         f2bf(w4[2] * g[4 * vq + 2]) | (static_cast<uint32_t>(f2bf(w4[3] * g[4 * vq + 3])) << 16));
+          *reinterpret_cast<uint2*>(tM + f * TWW + t0) =
+              make_uint2(f2bf(m4[0] * g[4 * vq]) | (static_cast<uint32_t>(f2bf(m4[1] * g[4 * vq + 1])) << 16),
+                         f2bf(m4[2] * g[4 * vq + 2]) | (static_cast<uint32_t>(f2bf(m4[3] * g[4 * vq + 3])) << 16));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    barrier_lds();
+    rows_out(gr + 64 * p, 256);
+    // Transposed rows: 2 x 64 rows of 256 tokens, 32 pieces each.
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int idx = threadIdx.x + 256 * i, row = idx >> 5, c = idx & 31;
+      const int fr = row & 63;
+      const int64_t fi = n0 + 64 * p + fr;
+      const int64_t dst = 64 * (fi / 32) + (row >= 64 ? 32 : 0) + fi % 32;
+      const bf16_t* srcb = (row >= 64 ? tM : tW) + fr * TWW + 8 * c;
+      *reinterpret_cast<uint4*>(gbase + dst * s.Cp + 8 * c) = *reinterpret_cast<const uint4*>(srcb);
+    }
+  };
+  kpass(Band<0>{}, va, vb);
+  if constexpr (NB >= 4) kpass(Band<1>{}, vb, va);
+  if constexpr (NB >= 6) kpass(Band<2>{}, va, vb);
 }
 
 }  // namespace e2ttt

@@ -17,25 +17,24 @@ __device__ __forceinline__ float bf2f(bf16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16, round to nearest even; NaN stays NaN (quiet bit forced).
-// Written as a select, not an early return, so that it compiles without a
-// branch per conversion.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even, by gfx950's conversion instruction
+// (v_cvt_pk_bf16_f32, one per two values).  It equals rounding the fp32 bit
+// pattern to its upper half with ties to even for every non-NaN input,
+// denormals included (compared on the device over all 2^32 patterns); a NaN
+// stays a NaN.  A software rounding costs about six VALU instructions per
+// value, and the wave64 VALU issues at a quarter of the lane rate, which made
+// it a visible part of the GEMM epilogues.
 __device__ __forceinline__ bf16_t f2bf(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  const uint32_t qnan = (u >> 16) | 0x40u;
-  return static_cast<bf16_t>((u & 0x7fffffffu) > 0x7f800000u ? qnan : rne);
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 
-// The same conversion written with an early return for NaN: the compiler
-// then branches around the rare case.  Which form schedules better depends on
-// the kernel (measured: this one in the 128-tile backward's stores, the
-// select everywhere else).
-__device__ __forceinline__ bf16_t f2bf_br(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+// Two fp32 -> one dword of two bf16 (same rounding), lo = a.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 template <typename T> __device__ __forceinline__ float to_f32(T x);

@@ -41,15 +41,7 @@ namespace e2ttt {
 constexpr int FD = 128;  // head dim of the fused path
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// Two fp32 -> one dword of two bf16 (round to nearest even), lo = a.
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  f32x2_t v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
 
 struct FusedArgs {
   int64_t BH, L, h, C, Cp, nC;

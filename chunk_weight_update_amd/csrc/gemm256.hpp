@@ -395,8 +395,8 @@ struct Acc256Pos {
 __device__ __forceinline__ void band_put(bf16_t* lds, int c, const Acc256Pos& ps, int vq,
                                          float x0, float x1, float x2, float x3) {
   *reinterpret_cast<uint2*>(lds + c * 72 + 32 * ps.wm + 8 * vq + 4 * ps.hf) =
-      make_uint2(f2bf(x0) | (static_cast<uint32_t>(f2bf(x1)) << 16),
-                 f2bf(x2) | (static_cast<uint32_t>(f2bf(x3)) << 16));
+      make_uint2(pack_bf16x2(x0, x1),
+                 pack_bf16x2(x2, x3));
 }
 
 // Copy ncol band columns out: column c's 64 tokens go to dst_row(c)[0 .. 31]
@@ -506,8 +506,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         zv[v] = z;
         zr[(32 * ps.wm + 8 * (v >> 2) + 4 * ps.hf + (v & 3)) * ZRW + j] = f2bf(z);
         if constexpr (krows)
-          fw[v] = f2bf(a3 * (sg * (1.0f + a1 * (1.0f - sg)))) |
-                  (static_cast<uint32_t>(f2bf(sl)) << 16);
+          fw[v] = pack_bf16x2(a3 * (sg * (1.0f + a1 * (1.0f - sg))), sl);
       }
       if constexpr (krows) {
 #pragma unroll
@@ -769,8 +768,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           const int jj = 32 * j2 + r32;
           auto put = [&](int o, const float (&x)[4]) {
             *reinterpret_cast<uint2*>(stg + (o * 64 + jj) * SW + tk) =
-                make_uint2(f2bf(x[0]) | (static_cast<uint32_t>(f2bf(x[1])) << 16),
-                           f2bf(x[2]) | (static_cast<uint32_t>(f2bf(x[3])) << 16));
+                make_uint2(pack_bf16x2(x[0], x[1]),
+                           pack_bf16x2(x[2], x[3]));
           };
           put(0, x1w);
           put(1, x1m);
@@ -969,11 +968,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(ksh + t0);
           const f32x4_t m4 = *reinterpret_cast<const f32x4_t*>(ksh + 256 + t0);
           *reinterpret_cast<uint2*>(tW + f * TWW + t0) =
-              make_uint2(f2bf(w4[0] * g[4 * vq]) | (static_cast<uint32_t>(f2bf(w4[1] * g[4 * vq + 1])) << 16),
-                         f2bf(w4[2] * g[4 * vq + 2]) | (static_cast<uint32_t>(f2bf(w4[3] * g[4 * vq + 3])) << 16));
+              make_uint2(pack_bf16x2(w4[0] * g[4 * vq], w4[1] * g[4 * vq + 1]),
+                         pack_bf16x2(w4[2] * g[4 * vq + 2], w4[3] * g[4 * vq + 3]));
           *reinterpret_cast<uint2*>(tM + f * TWW + t0) =
-              make_uint2(f2bf(m4[0] * g[4 * vq]) | (static_cast<uint32_t>(f2bf(m4[1] * g[4 * vq + 1])) << 16),
-                         f2bf(m4[2] * g[4 * vq + 2]) | (static_cast<uint32_t>(f2bf(m4[3] * g[4 * vq + 3])) << 16));
+              make_uint2(pack_bf16x2(m4[0] * g[4 * vq], m4[1] * g[4 * vq + 1]),
+                         pack_bf16x2(m4[2] * g[4 * vq + 2], m4[3] * g[4 * vq + 3]));
         }
         __builtin_amdgcn_sched_barrier(0);
       }

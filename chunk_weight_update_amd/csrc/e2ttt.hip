@@ -430,7 +430,7 @@ void launch_agg256(const Plan& q, const Shape& s, int r, int last, const T* ut, 
   if constexpr (sizeof(T) == 2) {
     const int64_t tiles = (4 * q.h / 256) * (q.d / 256) + (2 * q.d / 256) * (q.h / 256);
     E2TTT_LAUNCH(I, E2TTT_KERNEL_AGG, k_agg256, dim3(grid1(q.BH * tiles * q.nsplitAgg)),
-                 dim3(256), Tile256::LDS_BYTES, st, s, q.nsplitAgg, ut, kt, gt, zt, r, part);
+                 dim3(512), Tile256w8::LDS_BYTES, st, s, q.nsplitAgg, ut, kt, gt, zt, r, part);
     void (*kred)(Shape, int, int, int, const float*, const float*, const float*, const float*,
                  float*, float*, T*, T*, T*) = k_agg_reduce<T>;
     // (the kernels' state layout [W1 | W3 | W2]: 3dh per unit, also for the MLP)

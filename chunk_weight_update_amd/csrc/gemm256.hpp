@@ -196,11 +196,114 @@ __device__ __forceinline__ void gemm_tile256(f32x16_t (&acc)[4][4], const Loader
   barrier_nofence();  // every wave's last reads are done before LDS is reused
 }
 
+// The same 256 x 256 tile with 8 waves, two per SIMD: wave w takes rows
+// 128*(w/4) + [0,128) (blocks mi = 0..3) and columns 64*(w%4) + [0,64)
+// (blocks ni = 0, 1), 128 accumulator registers.  A stage holds the slab's
+// 256 A rows then 256 B rows (64 bytes each, the engine's swizzle); each wave
+// issues 4 of the slab's 32 direct loads, one every 4 of its 16 MFMAs.  With
+// two waves per SIMD one wave's MFMAs run while the other is held by its
+// load issue or its fragment reads, which with one wave per SIMD took turns.
+struct Tile256w8 {
+  static constexpr int BK = 32, NST = 4;
+  static constexpr int STAGE = 512 * 64;                      // 32 KB
+  static constexpr size_t LDS_BYTES = static_cast<size_t>(NST) * STAGE;  // 128 KB
+};
+
+// acc[mi][ni] += A B^T over k [k0, k0 + 32*ns), ns >= 1; arow(R), brow(R)
+// point at row R of A, B (R < 256, k contiguous, at k = 0).
+template <typename ARow, typename BRow>
+__device__ __forceinline__ void gemm_tile256w8(f32x16_t (&acc)[4][2], ARow arow, BRow brow,
+                                               int64_t k0, int ns, char* lds) {
+  constexpr int NST = Tile256w8::NST, SB = Tile256w8::STAGE, BK = Tile256w8::BK;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const bf16_t* src[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int R = 16 * (8 * i + wave) + (lane >> 2);
+    const int c8 = 8 * ((lane & 3) ^ swz256(R));
+    src[i] = (R < 256 ? arow(R) : brow(R - 256)) + k0 + c8;
+  }
+  auto load = [&](int slab, int i) {
+    char* st = lds + (slab % NST) * SB;
+    __builtin_amdgcn_global_load_lds(
+        static_cast<const void*>(src[i] + static_cast<int64_t>(slab) * BK),
+        (__attribute__((address_space(3))) void*)(st + (8 * i + wave) * 1024), 16, 0, 0);
+  };
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  const int r32 = lane & 31, hf = lane >> 5, sw = swz256(r32);
+  const int off0 = r32 * 64 + ((hf ^ sw) << 4), off1 = r32 * 64 + (((2 + hf) ^ sw) << 4);
+  struct Frags { bf16x8_t a[4], b[2]; };
+  auto read_frags = [&](Frags& f, const char* st, int ks) {
+    const int off = ks ? off1 : off0;
+    const char* As = st + wm * 128 * 64 + off;
+    const char* Bs = st + (256 + wn * 64) * 64 + off;
+    f.b[0] = *reinterpret_cast<const bf16x8_t*>(Bs);
+    f.a[0] = *reinterpret_cast<const bf16x8_t*>(As);
+    f.b[1] = *reinterpret_cast<const bf16x8_t*>(Bs + 32 * 64);
+#pragma unroll
+    for (int mi = 1; mi < 4; ++mi) f.a[mi] = *reinterpret_cast<const bf16x8_t*>(As + mi * 32 * 64);
+  };
+  auto step = [&](const Frags& f, auto&& between) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int mi = m >> 1, ni = m & 1;
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
+      between(m);
+    }
+  };
+  auto body = [&](int sl, bool refill) {
+    const char* st = lds + (sl % NST) * SB;
+    Frags f0, f1;
+    read_frags(f0, st, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    step(f0, [&](int m) {
+      if (m == 1) read_frags(f1, st, 1);
+      if (refill && (m & 3) == 1) load(sl + NST - 1, m >> 2);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    step(f1, [&](int m) {
+      if (refill && (m & 3) == 1) load(sl + NST - 1, 2 + (m >> 2));
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  static_assert(NST == 4, "wait counts below assume four stages");
+#pragma unroll
+  for (int p = 0; p < NST - 1; ++p)
+    if (p < ns)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) load(p, i);
+  // Iteration sl: wait for slab sl (at most NST-2 later slabs in flight),
+  // barrier (every wave has it, and every wave has read slab sl-1, whose
+  // stage takes slab sl+NST-1), then slab sl's MFMAs with that refill.
+  int sl = 0;
+  for (; sl < ns - (NST - 1); ++sl) {
+    wait_vmcnt<4 * (NST - 2)>();
+    barrier_nofence();
+    body(sl, true);
+  }
+  for (; sl < ns; ++sl) {
+    const int later = ns - 1 - sl;  // slabs loaded after this one
+    if (later >= 2) wait_vmcnt<8>();
+    else if (later == 1) wait_vmcnt<4>();
+    else wait_vmcnt<0>();
+    barrier_nofence();
+    body(sl, false);
+  }
+  barrier_nofence();  // every wave's last reads are done before LDS is reused
+}
+
 // Partial aggregates of split sp over token slabs [k0, k1): workgroup
 // (unit, split, tile); tiles 0 .. na-1 are family A (4h/256 x d/256), then
 // family B (2d/256 x h/256).  The partial of state entry e goes to
 // part[((sp * 2 + wm) * BH + u) * P + e], wm = 0 for A^W, 1 for A^M.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_agg256(
+// 8 waves on the 256 x 256 tile (gemm_tile256w8).
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_agg256(
     Shape s, int nsplit, const bf16_t* __restrict__ ut, const bf16_t* __restrict__ kt,
     const bf16_t* __restrict__ gt, const bf16_t* __restrict__ zt, int r, float* part) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
@@ -214,36 +317,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int64_t t = rest % (na + nb);
   const bool famA = t < na;
   int64_t mt, nt;
-  Loader256 la, lb;
+  const bf16_t* abase;
+  const bf16_t* bbase;
   if (famA) {
     mt = t / (d / 256); nt = t % (d / 256);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c8 = 8 * loader256_chunk(i);
-      la.rowp[i] = ut + (u * 4 * h + mt * 256 + loader256_row(i)) * s.Cp + c8;
-      lb.rowp[i] = kt + ((u * s.nC + r) * d + nt * 256 + loader256_row(i)) * s.Cp + c8;
-    }
+    abase = ut + (u * 4 * h + mt * 256) * s.Cp;
+    bbase = kt + ((u * s.nC + r) * d + nt * 256) * s.Cp;
   } else {
     const int64_t tb = t - na;
     mt = tb / (h / 256); nt = tb % (h / 256);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c8 = 8 * loader256_chunk(i);
-      la.rowp[i] = gt + (u * 2 * d + mt * 256 + loader256_row(i)) * s.Cp + c8;
-      lb.rowp[i] = zt + (u * h + nt * 256 + loader256_row(i)) * s.Cp + c8;
-    }
+    abase = gt + (u * 2 * d + mt * 256) * s.Cp;
+    bbase = zt + (u * h + nt * 256) * s.Cp;
   }
-  const int64_t nslab = s.Cp / Tile256::BK;
+  const int64_t nslab = s.Cp / Tile256w8::BK;
   const int64_t per = (nslab + nsplit - 1) / nsplit;
-  const int64_t k0 = sp * per * Tile256::BK;
-  const int64_t k1 = (sp * per + per < nslab ? sp * per + per : nslab) * Tile256::BK;
-  f32x16_t acc[4][4];
-  gemm_tile256(acc, la, lb, k0, k1, smem_raw);
+  const int64_t sl0 = sp * per;
+  const int64_t sl1 = sl0 + per < nslab ? sl0 + per : nslab;
+  f32x16_t acc[4][2];
+  gemm_tile256w8(acc, [&](int R) { return abase + R * s.Cp; }, [&](int R) { return bbase + R * s.Cp; },
+                 sl0 * Tile256w8::BK, static_cast<int>(sl1 - sl0), smem_raw);
 
   // Output row R (tile row): 64-row block R/64 holds 32 W rows then 32 M rows
   // of the same 32 state rows, so accumulator block mi is W (mi even) or M.
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int r32 = lane & 31, hf = lane >> 5;
   const int64_t P = 3 * d * h;
 #pragma unroll
@@ -261,8 +358,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     float* dst = part + ((static_cast<int64_t>(sp) * 2 + (mi & 1)) * s.BH + u) * P + base;
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      const int64_t c = nt * 256 + wn * 128 + ni * 32 + r32;
+    for (int ni = 0; ni < 2; ++ni) {
+      const int64_t c = nt * 256 + wn * 64 + ni * 32 + r32;
 #pragma unroll
       for (int v = 0; v < 16; ++v)
         dst[(8 * (v >> 2) + 4 * hf + (v & 3)) * stride + c] = acc[mi][ni][v];

@@ -639,23 +639,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ---------------------------------------------------------------------------
-// Phase B.  LDS: for the hi/lo variant (KREP = 2) the recompute weights of
-// the workgroup's 64 hidden units ([4 waves][W1, W3, W2^T][16][KREP*FD + 8]);
-// with KREP = 1 they live in registers.  Then NBUF token-tile buffers (three
-// for KREP = 1, one for the hi/lo variant).
+// Phase B.  LDS: three token-tile buffers (the recompute weights of the
+// wave's hidden units live in registers, hi and lo parts alike).
 template <int KREP> struct PhaseBCfg {
   static constexpr int TB = 32;               // tokens per tile
   static constexpr int KS = FD + 8;           // token-major tile row stride
   static constexpr int TS = TB + 8;           // feature-major tile row stride
-  static constexpr int WS = KREP * FD + 8;    // weight row stride
-  static constexpr int NBUF = KREP == 1 ? 3 : 1;
+  static constexpr int NBUF = 3;
   static constexpr int BUF_ELEMS = 2 * TB * KS + 2 * FD * TS;  // K, g | K^T, g^T
-  static constexpr size_t W_BYTES =
-      KREP == 1 ? 0 : static_cast<size_t>(4 * 3 * 16 * WS) * sizeof(bf16_t);
   static constexpr size_t BUF_BYTES = BUF_ELEMS * sizeof(bf16_t) + 2 * TB * sizeof(float);
-  static constexpr size_t LDS_BYTES = W_BYTES + NBUF * BUF_BYTES;
+  static constexpr size_t LDS_BYTES = NBUF * BUF_BYTES;
   static_assert((BUF_ELEMS * sizeof(bf16_t)) % 16 == 0, "buffer alignment");
-  static_assert(W_BYTES % 16 == 0, "weight alignment");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -736,25 +730,25 @@ __device__ __forceinline__ StateSlot phaseB_slot(int h, int ib, int tid, int t, 
 
 // Phase B: 4 waves (one per SIMD), wave w owns hidden units
 // 64*ib + 16*w .. +15 for all FD output columns.  The recompute weights of
-// the wave's hidden units stay in registers (KREP = 1) or are read from LDS
-// per tile (KREP = 2).  Fragments of the next step are read from LDS before
-// the MFMAs of the current step are issued.
+// the wave's hidden units stay in registers for the whole launch (KREP = 2:
+// hi and lo parts, 96 VGPRs; reading them from LDS per tile, as a first
+// version of the hi/lo variant did, cost about 48 KB of LDS reads per wave
+// and tile and measured 343 against about 290 us per launch on the 128-unit
+// workload).  Fragments of the next step are read from LDS before the MFMAs
+// of the current step are issued.
 template <int KREP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_phaseB(
     FusedArgs a) {
   typedef PhaseBCfg<KREP> S;
-  constexpr int TB = S::TB, KS = S::KS, TS = S::TS, WS = S::WS;
+  constexpr int TB = S::TB, KS = S::KS, TS = S::TS;
   constexpr int NT = 256;
   constexpr int KSTEPS = KREP * FD / 32;  // recompute k-steps (16x16x32)
-  constexpr bool WREG = KREP == 1;        // weights in registers
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  bf16_t* Wl = reinterpret_cast<bf16_t*>(smem_raw);
   auto bufp = [&](int b) -> bf16_t* {
-    return reinterpret_cast<bf16_t*>(smem_raw + S::W_BYTES + b * S::BUF_BYTES);
+    return reinterpret_cast<bf16_t*>(smem_raw + b * S::BUF_BYTES);
   };
   auto kscp = [&](int b) -> float* {
-    return reinterpret_cast<float*>(smem_raw + S::W_BYTES + b * S::BUF_BYTES +
-                                    S::BUF_ELEMS * sizeof(bf16_t));
+    return reinterpret_cast<float*>(smem_raw + b * S::BUF_BYTES + S::BUF_ELEMS * sizeof(bf16_t));
   };
 
   const int64_t nib = a.h / 64;
@@ -774,35 +768,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int64_t i_glob = 64 * ib + 16 * wave + l16;  // this lane's hidden unit (B column)
 
   // Recompute B operands: row = hidden unit, k = d (hi | lo when KREP = 2).
-  bf16x8_t wreg[3][WREG ? KSTEPS : 1];
+  bf16x8_t wreg[3][KSTEPS];
   {
     const bf16_t* w13 = a.w13s + u * 2 * a.h * (KREP * FD);
-    const bf16_t* w2t = a.w2ts + u * a.h * (KREP * FD);
-    if (WREG) {
-      const bf16_t* w1r = w13 + (64 * (i_glob / 32) + i_glob % 32) * (KREP * FD);
-      const bf16_t* w2r = a.w2ts + (u * a.h + i_glob) * (KREP * FD);
+    const bf16_t* w1r = w13 + (64 * (i_glob / 32) + i_glob % 32) * (KREP * FD);
+    const bf16_t* w2r = a.w2ts + (u * a.h + i_glob) * (KREP * FD);
 #pragma unroll
-      for (int ks = 0; ks < (WREG ? KSTEPS : 1); ++ks) {
-        wreg[0][ks] = *reinterpret_cast<const bf16x8_t*>(w1r + ks * 32 + g4 * 8);
-        wreg[1][ks] = *reinterpret_cast<const bf16x8_t*>(w1r + 32 * (KREP * FD) + ks * 32 + g4 * 8);
-        wreg[2][ks] = *reinterpret_cast<const bf16x8_t*>(w2r + ks * 32 + g4 * 8);
-      }
-    } else {
-      TileCopy<4 * 3 * 16, KREP * FD, NT> cw;
-      cw.load([&](int rr) -> const bf16_t* {
-        const int grp = rr / 48, q = (rr / 16) % 3, il = rr % 16;
-        const int64_t i = 64 * ib + 16 * grp + il;
-        if (q == 2) return w2t + i * (KREP * FD);
-        return w13 + (64 * (i / 32) + (q == 1 ? 32 : 0) + i % 32) * (KREP * FD);
-      });
-      cw.store(Wl, WS);
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      wreg[0][ks] = *reinterpret_cast<const bf16x8_t*>(w1r + ks * 32 + g4 * 8);
+      wreg[1][ks] = *reinterpret_cast<const bf16x8_t*>(w1r + 32 * (KREP * FD) + ks * 32 + g4 * 8);
+      wreg[2][ks] = *reinterpret_cast<const bf16x8_t*>(w2r + ks * 32 + g4 * 8);
     }
   }
-  const bf16_t* Wq = Wl + wave * 3 * 16 * WS;  // this wave's [3][16][WS] (KREP = 2)
-  auto wfrag = [&](int q, int ks) -> bf16x8_t {
-    if (WREG) return wreg[q][WREG ? ks : 0];
-    return *reinterpret_cast<const bf16x8_t*>(Wq + (q * 16 + l16) * WS + ks * 32 + g4 * 8);
-  };
+  auto wfrag = [&](int q, int ks) -> bf16x8_t { return wreg[q][ks]; };
 
   // Accumulators (16x16 blocks): [0..7] A^W_W1 (rows i of this wave, cols j
   // block jb), [8..15] A^M_W1, [16..23] A^W_W3, [24..31] A^M_W3,
@@ -926,24 +904,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     acc[32 + jb] = mfma16(fg, f.zw, acc[32 + jb]);
     acc[40 + jb] = mfma16(fg, f.zm, acc[40 + jb]);
   };
-  auto aggregate = [&](const Frags& f, const bf16_t* Ks) {
-    const bf16_t* KTs = Ks + 2 * TB * KS;
-    const bf16_t* GTs = KTs + FD * TS;
-    bf16x8_t fk = pfrag(KTs, 0), fg = pfrag(GTs, 0);
-#pragma unroll
-    for (int jb = 0; jb < FD / 16; ++jb) {
-      bf16x8_t fk_n = fk, fg_n = fg;
-      if (jb + 1 < FD / 16) {
-        fk_n = pfrag(KTs, jb + 1);
-        fg_n = pfrag(GTs, jb + 1);
-      }
-      mma_block(f, jb, fk, fg);
-      fk = fk_n;
-      fg = fg_n;
-    }
-  };
-
-  // aggregate() of tile it fused with elementwise() of tile it+1: step jb
+  // The aggregation of tile it fused with elementwise() of tile it+1: step jb
   // issues the six MFMAs of column block jb alternating with the VALU work
   // of fragment slot jb of the next tile (8 slots, 8 blocks), and a
   // scheduling fence after each step keeps the compiler from clustering the
@@ -1017,51 +978,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     return fn;
   };
 
-  if constexpr (S::NBUF == 3) {
-    // Software pipeline over three buffers: iteration it aggregates tile it
-    // (fragments formed in the previous iteration) while it recomputes tile
-    // it+1 and forms its fragments, so the elementwise VALU work of one tile
-    // overlaps the MFMAs of the other; tile it+2 is in flight from global
-    // memory meanwhile and lands in the buffer tile it-1 used.  The recompute
-    // past the last tile reads a stale (in-bounds) buffer and is discarded.
-    {  // the first two tiles' loads in flight together
-      TileRegs tr1;
-      load_tile(tr, tbase);
-      if (ntiles > 1) load_tile(tr1, tbase + TB);
-      store_tile(tr, 0);
-      if (ntiles > 1) store_tile(tr1, 1);
-    }
-    __syncthreads();
-    Frags f = elementwise(recompute(bufp(0)), kscp(0));
-    // No conditional loads or stores in the body: past the end the last
-    // tile is fetched again and stored into the free buffer.
-    int bc = 0;  // buffer of tile it
-    for (int it = 0; it < ntiles; ++it) {
-      const int bn = bc == 2 ? 0 : bc + 1;  // tile it+1
-      const int bnn = bn == 2 ? 0 : bn + 1; // tile it+2 (= tile it-1's)
-      const int tl = it + 2 < ntiles ? it + 2 : ntiles - 1;
-      load_tile(tr, tbase + static_cast<int64_t>(tl) * TB);
-      const Rec rn = recompute(bufp(bn));
-      f = aggregate_next(f, bufp(bc), rn, kscp(bn));
-      store_tile(tr, bnn);
-      __syncthreads();
-      bc = bn;
-    }
-  } else {
+  // Software pipeline over three buffers: iteration it aggregates tile it
+  // (fragments formed in the previous iteration) while it recomputes tile
+  // it+1 and forms its fragments, so the elementwise VALU work of one tile
+  // overlaps the MFMAs of the other; tile it+2 is in flight from global
+  // memory meanwhile and lands in the buffer tile it-1 used.  The recompute
+  // past the last tile reads a stale (in-bounds) buffer and is discarded.
+  {  // the first two tiles' loads in flight together
+    TileRegs tr1;
     load_tile(tr, tbase);
+    if (ntiles > 1) load_tile(tr1, tbase + TB);
     store_tile(tr, 0);
+    if (ntiles > 1) store_tile(tr1, 1);
+  }
+  __syncthreads();
+  Frags f = elementwise(recompute(bufp(0)), kscp(0));
+  // No conditional loads or stores in the body: past the end the last
+  // tile is fetched again and stored into the free buffer.
+  int bc = 0;  // buffer of tile it
+  for (int it = 0; it < ntiles; ++it) {
+    const int bn = bc == 2 ? 0 : bc + 1;  // tile it+1
+    const int bnn = bn == 2 ? 0 : bn + 1; // tile it+2 (= tile it-1's)
+    const int tl = it + 2 < ntiles ? it + 2 : ntiles - 1;
+    load_tile(tr, tbase + static_cast<int64_t>(tl) * TB);
+    const Rec rn = recompute(bufp(bn));
+    f = aggregate_next(f, bufp(bc), rn, kscp(bn));
+    store_tile(tr, bnn);
     __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
-      const int b = S::NBUF == 2 ? (it & 1) : 0;
-      if (it + 1 < ntiles) load_tile(tr, tbase + static_cast<int64_t>(it + 1) * TB);
-      aggregate(elementwise(recompute(bufp(b)), kscp(b)), bufp(b));
-      if (S::NBUF == 1) __syncthreads();  // single buffer: everyone is done reading it
-      if (it + 1 < ntiles) {
-        // With two buffers, b^1 was last read in iteration it-1 (barrier since).
-        store_tile(tr, S::NBUF == 2 ? (b ^ 1) : 0);
-      }
-      __syncthreads();
-    }
+    bc = bn;
   }
 
   if (a.nsplit > 1) {

@@ -300,3 +300,16 @@ def test_swiglu_empty_sequence_copies_state():
     assert out.size == 0
     assert np.array_equal(W, inp["W0"].astype(np.float64))
     assert np.array_equal(M, inp["M0"].astype(np.float64))
+
+
+@pytest.mark.parametrize("d,h", [
+    (512, 768),    # readout tiles of 128 features, backward tiles of 192 units
+    (768, 1024),   # readout tiles of 192 features, backward tiles of 128 units
+    (1024, 256),   # both at 128, the largest d
+])
+def test_swiglu_bf16_256_path_tile_widths(d, h):
+    """The 256-tile path's readout and backward take 192-wide tiles where 192
+    divides d (readout) or h (backward), else 128-wide: every combination,
+    two chunks with a ragged last one (Cp = 256)."""
+    check(SWIGLU, 1, 1, 450, d, h, 256, BF16, seed=12, regime="nearunit",
+          m0_scale=M0["nearunit"])

@@ -1,24 +1,28 @@
-// gemm256.hpp -- 256x256-tile bf16 MFMA GEMM for the generic (d != 128)
-// aggregation of the SwiGLU learner, with a token split and a streaming
-// state epilogue.
+// gemm256.hpp -- the bf16 MFMA GEMMs of the generic SwiGLU path when d, h
+// and the padded chunk are multiples of 256 (the large-state layer): the
+// forward products, the backward's dZ and the aggregation, with their fused
+// epilogues, and the streaming state epilogue.
 //
 // The aggregations of §3.2 / App. A.4 of "Rethinking Expressivity and
 // Efficiency in Test-Time Training" contract over the chunk's tokens:
 //   family A: [K^W dA1 | K^M dA1 | K^W dA3 | K^M dA3]^T K   (4h x d)
 //   family B: [K^W g | K^M g]^T Z                          (2d x h)
-// with operands already scaled and rounded once (k_bwd, k_fwd2) and stored
-// feature-major (rows = output rows, contiguous along tokens).
+// with operands already scaled and rounded once (the backward, the readout)
+// and stored feature-major (rows = output rows, contiguous along tokens).
 //
-// Tile: 256 x 256 per workgroup, 4 waves in a 2 x 2 grid, 128 x 128 per wave
-// (4 x 4 blocks of 32x32x16 MFMA, 256 accumulator registers), k-slabs of 32
-// tokens.  Slabs go from global memory straight into LDS (global_load_lds,
-// no registers), four stages deep, so three slabs are in flight while one is
-// computed: the memory latency is covered by three slabs of MFMA work rather
-// than one.  LDS rows are 64 bytes, unpadded; the four 16-byte pieces of row
-// r are stored in the order kc ^ swz256(r), so the 8 or 16 rows that one
-// fragment read serves together hit distinct bank groups.  Per slab a wave
-// reads 16 KB of fragments for 32 MFMAs.
-
+// Three engines share one slab format: k-slabs of 32 (tokens or features)
+// go from global memory straight into LDS (global_load_lds, no registers),
+// several stages deep, so later slabs are in flight while one is computed.
+// LDS rows are 64 bytes, unpadded; the four 16-byte pieces of row r are
+// stored in the order kc ^ swz256(r), so the 8 or 16 rows that one fragment
+// read serves together hit distinct bank groups.
+//   gemm_tile256:   256 x 256 tile, 4 waves of 128 x 128 (4 x 4 blocks of
+//                   32x32x16 MFMA, 256 accumulator registers) -- k_fwd13_256.
+//   gemm_tile256w8: the same tile with 8 waves of 128 x 64 -- k_agg256.
+//   gemm_rows256:   256 x 32*NB tile, 4 waves of 64 x 32*NB -- the readout
+//                   (k_fwd2r) and the backward (k_bwd256), where 192-wide
+//                   tiles give one workgroup per CU.
+//
 // Token split: the tile count of one unit can be small (108 at d = 768,
 // h = 1536), so the chunk's token slabs are split over S workgroups.  Each
 // writes its fp32 partial aggregates in the packed state layout, and

@@ -77,21 +77,24 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // Rows of a [rows][n] fp32 matrix dotted with lane-strided vectors: lane l
-// holds x[l + 64 m] (m < M; zero for l + 64 m >= n, n % 64 == 0, n <= 64 M).
-// Every load of the wave is issued before any product, unconditionally: the
-// chunks past n read a clamped in-range element, which meets x = 0.  (A load
-// under a runtime condition makes the compiler wait for each one in turn.)
-template <int R, int NX, int M>
-__device__ __forceinline__ void wave_dots(const float* const (&rows)[R], int64_t n,
-                                          const float (&x)[NX][M], float (&out)[R][NX]) {
+// holds x[4 l + 256 m .. +3] (m < M4; zero past n, n % 4 == 0, n <= 256 M4),
+// so a wave reads a 1 KB piece of each row per 16-byte load instruction.
+// Every load of the wave is issued before any product, unconditionally:
+// pieces past n read the row's last (in-range) 16 bytes, which meet x = 0.
+// (A load under a runtime condition makes the compiler wait for each one in
+// turn; the first version's 4-byte loads took four times the instructions,
+// more than the 63 a wave can have in flight at d = 768.)
+template <int R, int NX, int M4>
+__device__ __forceinline__ void wave_dots4(const float* const (&rows)[R], int64_t n,
+                                           const f32x4_t (&x)[NX][M4], float (&out)[R][NX]) {
   const int lane = threadIdx.x & 63;
-  float w[M][R];
+  f32x4_t w[M4][R];
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int64_t e0 = lane + 64 * m;
-    const int64_t e = e0 < n ? e0 : n - 1;
+  for (int m = 0; m < M4; ++m) {
+    const int64_t e0 = 4 * lane + 256 * m;
+    const int64_t e = e0 < n ? e0 : n - 4;
 #pragma unroll
-    for (int r = 0; r < R; ++r) w[m][r] = rows[r][e];
+    for (int r = 0; r < R; ++r) w[m][r] = *reinterpret_cast<const f32x4_t*>(rows[r] + e);
   }
   float acc[R][NX];
 #pragma unroll
@@ -99,40 +102,47 @@ __device__ __forceinline__ void wave_dots(const float* const (&rows)[R], int64_t
 #pragma unroll
     for (int c = 0; c < NX; ++c) acc[r][c] = 0.0f;
 #pragma unroll
-  for (int m = 0; m < M; ++m)
+  for (int m = 0; m < M4; ++m)
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int c = 0; c < NX; ++c) acc[r][c] = fmaf(w[m][r], x[c][m], acc[r][c]);
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < NX; ++c) acc[r][c] = fmaf(w[m][r][j], x[c][m][j], acc[r][c]);
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int c = 0; c < NX; ++c) out[r][c] = wave_sum(acc[r][c]);
 }
 
-// Smallest of 2, 4, 8, ... >= n / 64: the chunk count a wave_dots instance
-// covers.
-__host__ __device__ inline int dot_chunks(int64_t n) {
-  int m = 2;
-  while (64 * static_cast<int64_t>(m) < n) m *= 2;
-  return m;
+// Piece count of wave_dots4 for a vector of n: the smallest of 1, 2, 3, 4, 6,
+// 8, 12, 16 with 256 times it >= n.
+__host__ __device__ inline int dot_pieces(int64_t n) {
+  const int need = static_cast<int>((n + 255) / 256);
+  const int set[] = {1, 2, 3, 4, 6, 8, 12, 16};
+  for (int v : set)
+    if (v >= need) return v;
+  return 16;
 }
 
+
 // W1 and W3 rows of 2 hidden units per wave (8 per workgroup) dotted with q
-// and k (the MLP learner: W1 only, a3 = 1).  Grid BH * (h / 8); d <= 64 M.
-template <typename T, int M>
+// and k (the MLP learner: W1 only, a3 = 1).  Grid BH * (h / 8); d <= 256 M4.
+template <typename T, int M4>
 __global__ __launch_bounds__(256) void k_dec_fwd13(DecodeArgs a, const T* __restrict__ q,
                                                    const T* __restrict__ k) {
   const int64_t nb = a.h / 8, u = blockIdx.x / nb, ib = blockIdx.x % nb;
   const int64_t d = a.d, h = a.h;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float x[2][M];
+  f32x4_t x[2][M4];
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int64_t e = lane + 64 * m;
-    x[0][m] = e < d ? to_f32<T>(q[u * d + e]) : 0.0f;
-    x[1][m] = e < d ? to_f32<T>(k[u * d + e]) : 0.0f;
-  }
+  for (int m = 0; m < M4; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t e = 4 * lane + 256 * m + j;
+      x[0][m][j] = e < d ? to_f32<T>(q[u * d + e]) : 0.0f;
+      x[1][m][j] = e < d ? to_f32<T>(k[u * d + e]) : 0.0f;
+    }
   const float* Wu = a.W0 + u * a.P;
   const int64_t i0 = ib * 8 + wave * 2;
   const float* rows[4];
@@ -142,7 +152,7 @@ __global__ __launch_bounds__(256) void k_dec_fwd13(DecodeArgs a, const T* __rest
     rows[2 + r] = a.gated ? Wu + h * d + (i0 + r) * d : rows[r];  // W3 (MLP: unused)
   }
   float s[4][2];
-  wave_dots<4, 2, M>(rows, d, x, s);
+  wave_dots4<4, 2, M4>(rows, d, x, s);
   if (lane < 2) {
     const float s1q = lane ? s[1][0] : s[0][0], s1k = lane ? s[1][1] : s[0][1];
     const float s3q = a.gated ? (lane ? s[3][0] : s[2][0]) : 1.0f;
@@ -156,26 +166,28 @@ __global__ __launch_bounds__(256) void k_dec_fwd13(DecodeArgs a, const T* __rest
 }
 
 // One W2 row per wave (4 per workgroup): y = W2 z for both z; the readout
-// and the residual g.  Grid BH * (d / 4); h <= 64 M.
-template <typename T, int M>
+// and the residual g.  Grid BH * (d / 4); h <= 256 M4.
+template <typename T, int M4>
 __global__ __launch_bounds__(256) void k_dec_fwd2(DecodeArgs a, const T* __restrict__ v,
                                                   T* __restrict__ out) {
   const int64_t nb = a.d / 4, u = blockIdx.x / nb, jb = blockIdx.x % nb;
   const int64_t d = a.d, h = a.h;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float z[2][M];
+  f32x4_t z[2][M4];
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int64_t e0 = lane + 64 * m;
-    const int64_t e = e0 < h ? e0 : h - 1;
-    const float zq = a.zq[u * h + e], zk = a.zk[u * h + e];
-    z[0][m] = e0 < h ? zq : 0.0f;
-    z[1][m] = e0 < h ? zk : 0.0f;
+  for (int m = 0; m < M4; ++m) {
+    const int64_t e0 = 4 * lane + 256 * m;
+    const int64_t e = e0 < h ? e0 : h - 4;
+    const f32x4_t zq = *reinterpret_cast<const f32x4_t*>(a.zq + u * h + e);
+    const f32x4_t zk = *reinterpret_cast<const f32x4_t*>(a.zk + u * h + e);
+    const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    z[0][m] = e0 < h ? zq : zero;
+    z[1][m] = e0 < h ? zk : zero;
   }
   const int64_t j = jb * 4 + wave;
   const float* rows[1] = {a.W0 + u * a.P + (a.P - h * d) + j * h};  // W2 row j
   float y[1][2];
-  wave_dots<1, 2, M>(rows, h, z, y);
+  wave_dots4<1, 2, M4>(rows, h, z, y);
   if (lane == 0) {
     out[u * d + j] = from_f32<T>(y[0][0]);
     a.g[u * d + j] = to_f32<T>(v[u * d + j]) - y[0][1];

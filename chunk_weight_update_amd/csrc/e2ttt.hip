@@ -1137,15 +1137,16 @@ e2ttt_status e2ttt_decode_step(const e2ttt_problem* prob, const void* q, const v
     if (h == 0) {
       hipLaunchKernelGGL(k_dec_lin_fwd<T>, dim3(grid1(BH)), dim3(256), 0, s, a, Q, K, V, O);
     } else {
-      // (d <= 1024, h <= 4096: the dot products take 2 .. 16 and 2 .. 64
-      // chunks of 64 per lane)
-      const int md = dot_chunks(d), mh = dot_chunks(h);
+      // (d <= 1024, h <= 4096: the dot products take 1 .. 4 and 1 .. 16
+      // pieces of 256 floats, 16 bytes per lane each)
+      const int md = dot_pieces(d), mh = dot_pieces(h);
       void (*f13)(DecodeArgs, const T*, const T*) =
-          md <= 2 ? k_dec_fwd13<T, 2> : md <= 4 ? k_dec_fwd13<T, 4>
-          : md <= 8 ? k_dec_fwd13<T, 8> : k_dec_fwd13<T, 16>;
+          md <= 1 ? k_dec_fwd13<T, 1> : md <= 2 ? k_dec_fwd13<T, 2>
+          : md <= 3 ? k_dec_fwd13<T, 3> : k_dec_fwd13<T, 4>;
       void (*f2)(DecodeArgs, const T*, T*) =
-          mh <= 2 ? k_dec_fwd2<T, 2> : mh <= 4 ? k_dec_fwd2<T, 4> : mh <= 8 ? k_dec_fwd2<T, 8>
-          : mh <= 16 ? k_dec_fwd2<T, 16> : mh <= 32 ? k_dec_fwd2<T, 32> : k_dec_fwd2<T, 64>;
+          mh <= 1 ? k_dec_fwd2<T, 1> : mh <= 2 ? k_dec_fwd2<T, 2> : mh <= 3 ? k_dec_fwd2<T, 3>
+          : mh <= 4 ? k_dec_fwd2<T, 4> : mh <= 6 ? k_dec_fwd2<T, 6> : mh <= 8 ? k_dec_fwd2<T, 8>
+          : mh <= 12 ? k_dec_fwd2<T, 12> : k_dec_fwd2<T, 16>;
       hipLaunchKernelGGL(f13, dim3(grid1(BH * (h / 8))), dim3(256), 0, s, a, Q, K);
       hipLaunchKernelGGL(f2, dim3(grid1(BH * (d / 4))), dim3(256), 0, s, a, V, O);
       hipLaunchKernelGGL(k_dec_bwd, dim3(grid1(BH * (h / 64) * (d / 64))), dim3(256), 0, s, a,

@@ -1249,7 +1249,6 @@ struct BwdPlan {
   size_t hk, hq, tw, tm, du, uw, um, da, daq;  // width 2h
   size_t zk, zq, wv, dzq, r2w, r2m, dwv, dza;  // width h
   size_t e, s2w, s2m, dea;                     // width d
-  size_t gpart;                                // K-split partials of the products
   // bf16 io: fp32 copies of q, k, v, dout and fp32 dq, dk, dv, [BH][L][d]
   bool bf16io;
   size_t xq, xk, xv, xdo, xdq, xdk, xdv;
@@ -1310,8 +1309,6 @@ e2ttt_status make_bwd_plan(const e2ttt_problem* p, BwdPlan* bp) {
                       &bp->dza})
       *b = take(rows * q.h);
     for (size_t* b : {&bp->e, &bp->s2w, &bp->s2m, &bp->dea}) *b = take(rows * q.d);
-    // A split product has at most 2 * kCUs workgroups of 64 x 64 partial outputs.
-    bp->gpart = take(4 * static_cast<size_t>(GF_T * GF_T) * 2 * kCUs);
   }
   if (bp->bf16io)
     for (size_t* b : {&bp->xq, &bp->xk, &bp->xv, &bp->xdo, &bp->xdq, &bp->xdk, &bp->xdv})
@@ -1329,33 +1326,27 @@ e2ttt_status make_bwd_plan(const e2ttt_problem* p, BwdPlan* bp) {
   return E2TTT_OK;
 }
 
-// Batched fp32 GEMM over the BH units (grid z).  Products with few output
-// tiles and a long K are split over K (up to GF_MAX_SPLIT ways, so that the
-// grid has about two workgroups per CU) into the partial buffer, then summed
-// in split order.
-constexpr int GF_MAX_SPLIT = 8;
-
-void gemm_f32(GemmF32 g, int64_t BH, float* part, hipStream_t s) {
+// Batched fp32 GEMM over the BH units (grid z).  Products with few 64 x 64
+// output tiles and a long K (where the grid would leave most CUs idle) run
+// on 32 x 32 tiles with K split four ways inside each workgroup.
+void gemm_f32(GemmF32 g, int64_t BH, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return;
   const int64_t tiles = ((g.N + GF_T - 1) / GF_T) * ((g.M + GF_T - 1) / GF_T) * BH;
-  int ns = 1;
-  while (ns < GF_MAX_SPLIT && tiles * ns * 2 <= 2 * kCUs && g.K >= 2 * ns * 4 * GF_K) ns *= 2;
-  g.nsplit = ns;
-  g.kchunk = ns == 1 ? g.K : ((g.K + ns - 1) / ns + GF_K - 1) / GF_K * GF_K;
-  g.part = part;
+  if (tiles <= kCUs && g.K >= 2 * 4 * GF_K) {
+    const dim3 grid(static_cast<unsigned>((g.N + GQ_T - 1) / GQ_T),
+                    static_cast<unsigned>((g.M + GQ_T - 1) / GQ_T), static_cast<unsigned>(BH));
+    hipLaunchKernelGGL(k_gemm_f32_k4, grid, dim3(256), 0, s, g);
+    return;
+  }
   const dim3 grid(static_cast<unsigned>((g.N + GF_T - 1) / GF_T),
-                  static_cast<unsigned>((g.M + GF_T - 1) / GF_T), static_cast<unsigned>(BH * ns));
+                  static_cast<unsigned>((g.M + GF_T - 1) / GF_T), static_cast<unsigned>(BH));
   hipLaunchKernelGGL(k_gemm_f32, grid, dim3(256), 0, s, g);
-  if (ns > 1)
-    hipLaunchKernelGGL(k_gemm_split_sum, dim3(grid1((BH * g.M * g.N + 255) / 256)), dim3(256), 0,
-                       s, g, BH);
 }
 
 GemmF32 gf(int64_t M, int64_t N, int64_t K, const float* A, int64_t sAb, int64_t sAm,
            int64_t sAk, const float* B, int64_t sBb, int64_t sBk, int64_t sBn, const float* D,
            int64_t sDb, int64_t ldd, float* C, int64_t sCb, int64_t ldc, float alpha = 1.0f) {
-  return GemmF32{M, N, K, A, sAb, sAm, sAk, B, sBb, sBk, sBn, D, sDb, ldd, C, sCb, ldc, alpha,
-                 1, K, nullptr};
+  return GemmF32{M, N, K, A, sAb, sAm, sAk, B, sBb, sBk, sBn, D, sDb, ldd, C, sCb, ldc, alpha};
 }
 
 // The SwiGLU learner's backward (fp32): forward re-run for the chunk-start
@@ -1436,7 +1427,7 @@ void swiglu_backward(const BwdPlan& bp, char* ws, const float* Q, const float* K
         *DAQ = wsf(bp.daq), *ZK = wsf(bp.zk), *ZQ = wsf(bp.zq), *WV = wsf(bp.wv),
         *DZQ = wsf(bp.dzq), *R2W = wsf(bp.r2w), *R2M = wsf(bp.r2m), *DW = wsf(bp.dwv),
         *DZA = wsf(bp.dza), *E = wsf(bp.e), *S2W = wsf(bp.s2w), *S2M = wsf(bp.s2m),
-        *DEA = wsf(bp.dea), *PART = wsf(bp.gpart);
+        *DEA = wsf(bp.dea);
   const int64_t b2 = Cp * 2 * h, b1 = Cp * h, bd = Cp * d;  // unit strides of the buffers
   const int64_t o2 = 2 * h * d;                              // offset of W2 in a state
   const int64_t nrows = BH * (2 * h + d);
@@ -1463,21 +1454,21 @@ void swiglu_backward(const BwdPlan& bp, char* ws, const float* Q, const float* K
       dMp = dMC == wsf(bp.dma) ? wsf(bp.dmb) : wsf(bp.dma);
     }
     // Forward quantities at Ws.
-    gemm_f32(gf(n, 2 * h, d, Kr, Ld, d, 1, Ws, P, 1, d, nullptr, 0, 0, HK, b2, 2 * h), BH, PART, s);
-    gemm_f32(gf(n, 2 * h, d, Qr, Ld, d, 1, Ws, P, 1, d, nullptr, 0, 0, HQ, b2, 2 * h), BH, PART, s);
+    gemm_f32(gf(n, 2 * h, d, Kr, Ld, d, 1, Ws, P, 1, d, nullptr, 0, 0, HK, b2, 2 * h), BH, s);
+    gemm_f32(gf(n, 2 * h, d, Qr, Ld, d, 1, Ws, P, 1, d, nullptr, 0, 0, HQ, b2, 2 * h), BH, s);
     const unsigned gact = grid1((BH * n * h + 255) / 256);
     hipLaunchKernelGGL(k_swb_act, dim3(gact), dim3(256), 0, s, BH, n, h, Cp, sh.gated, HK, ZK);
     hipLaunchKernelGGL(k_swb_act, dim3(gact), dim3(256), 0, s, BH, n, h, Cp, sh.gated, HQ, ZQ);
-    gemm_f32(gf(n, d, h, ZK, b1, h, 1, Ws + o2, P, 1, h, Vr, Ld, d, E, bd, d, -1.0f), BH, PART, s);
-    gemm_f32(gf(n, h, d, E, bd, d, 1, Ws + o2, P, h, 1, nullptr, 0, 0, WV, b1, h), BH, PART, s);
-    gemm_f32(gf(n, h, d, DOr, Ld, d, 1, Ws + o2, P, h, 1, nullptr, 0, 0, DZQ, b1, h), BH, PART, s);
+    gemm_f32(gf(n, d, h, ZK, b1, h, 1, Ws + o2, P, 1, h, Vr, Ld, d, E, bd, d, -1.0f), BH, s);
+    gemm_f32(gf(n, h, d, E, bd, d, 1, Ws + o2, P, h, 1, nullptr, 0, 0, WV, b1, h), BH, s);
+    gemm_f32(gf(n, h, d, DOr, Ld, d, 1, Ws + o2, P, h, 1, nullptr, 0, 0, DZQ, b1, h), BH, s);
     // Products with the chunk-end adjoints.
-    gemm_f32(gf(n, 2 * h, d, Kr, Ld, d, 1, dWC, P, 1, d, nullptr, 0, 0, TW, b2, 2 * h), BH, PART, s);
-    gemm_f32(gf(n, 2 * h, d, Kr, Ld, d, 1, dMC, P, 1, d, nullptr, 0, 0, TM, b2, 2 * h), BH, PART, s);
-    gemm_f32(gf(n, d, h, ZK, b1, h, 1, dWC + o2, P, 1, h, nullptr, 0, 0, S2W, bd, d), BH, PART, s);
-    gemm_f32(gf(n, d, h, ZK, b1, h, 1, dMC + o2, P, 1, h, nullptr, 0, 0, S2M, bd, d), BH, PART, s);
-    gemm_f32(gf(n, h, d, E, bd, d, 1, dWC + o2, P, h, 1, nullptr, 0, 0, R2W, b1, h), BH, PART, s);
-    gemm_f32(gf(n, h, d, E, bd, d, 1, dMC + o2, P, h, 1, nullptr, 0, 0, R2M, b1, h), BH, PART, s);
+    gemm_f32(gf(n, 2 * h, d, Kr, Ld, d, 1, dWC, P, 1, d, nullptr, 0, 0, TW, b2, 2 * h), BH, s);
+    gemm_f32(gf(n, 2 * h, d, Kr, Ld, d, 1, dMC, P, 1, d, nullptr, 0, 0, TM, b2, 2 * h), BH, s);
+    gemm_f32(gf(n, d, h, ZK, b1, h, 1, dWC + o2, P, 1, h, nullptr, 0, 0, S2W, bd, d), BH, s);
+    gemm_f32(gf(n, d, h, ZK, b1, h, 1, dMC + o2, P, 1, h, nullptr, 0, 0, S2M, bd, d), BH, s);
+    gemm_f32(gf(n, h, d, E, bd, d, 1, dWC + o2, P, h, 1, nullptr, 0, 0, R2W, b1, h), BH, s);
+    gemm_f32(gf(n, h, d, E, bd, d, 1, dMC + o2, P, h, 1, nullptr, 0, 0, R2M, b1, h), BH, s);
     if (n > 0) {
       SwbTokArgs ta;
       ta.n = n; ta.d = d; ta.h = h; ta.Cp = Cp; ta.nC = q.nC; ta.r = ri; ta.gated = sh.gated;
@@ -1488,24 +1479,24 @@ void swiglu_backward(const BwdPlan& bp, char* ws, const float* Q, const float* K
       hipLaunchKernelGGL(k_swb_tok, dim3(grid1(BH * n)), dim3(256), 0, s, ta);
     }
     // de (= dv) and dz.
-    gemm_f32(gf(n, d, h, DW, b1, h, 1, Ws + o2, P, 1, h, DEA, bd, d, dvr, Ld, d), BH, PART, s);
-    gemm_f32(gf(n, h, d, dvr, Ld, d, 1, Ws + o2, P, h, 1, DZA, b1, h, DZA, b1, h, -1.0f), BH, PART, s);
+    gemm_f32(gf(n, d, h, DW, b1, h, 1, Ws + o2, P, 1, h, DEA, bd, d, dvr, Ld, d), BH, s);
+    gemm_f32(gf(n, h, d, dvr, Ld, d, 1, Ws + o2, P, h, 1, DZA, b1, h, DZA, b1, h, -1.0f), BH, s);
     hipLaunchKernelGGL(k_swb_da, dim3(gact), dim3(256), 0, s, BH, n, h, Cp, sh.gated, HK, WV,
                        DU, DZA, HQ, DZQ, DA, DAQ);
     // dk, dq.
-    gemm_f32(gf(n, d, 2 * h, DA, b2, 2 * h, 1, Ws, P, d, 1, nullptr, 0, 0, dkr, Ld, d), BH, PART, s);
-    gemm_f32(gf(n, d, 2 * h, UW, b2, 2 * h, 1, dWC, P, d, 1, dkr, Ld, d, dkr, Ld, d), BH, PART, s);
-    gemm_f32(gf(n, d, 2 * h, UM, b2, 2 * h, 1, dMC, P, d, 1, dkr, Ld, d, dkr, Ld, d), BH, PART, s);
-    gemm_f32(gf(n, d, 2 * h, DAQ, b2, 2 * h, 1, Ws, P, d, 1, nullptr, 0, 0, dqr, Ld, d), BH, PART, s);
+    gemm_f32(gf(n, d, 2 * h, DA, b2, 2 * h, 1, Ws, P, d, 1, nullptr, 0, 0, dkr, Ld, d), BH, s);
+    gemm_f32(gf(n, d, 2 * h, UW, b2, 2 * h, 1, dWC, P, d, 1, dkr, Ld, d, dkr, Ld, d), BH, s);
+    gemm_f32(gf(n, d, 2 * h, UM, b2, 2 * h, 1, dMC, P, d, 1, dkr, Ld, d, dkr, Ld, d), BH, s);
+    gemm_f32(gf(n, d, 2 * h, DAQ, b2, 2 * h, 1, Ws, P, d, 1, nullptr, 0, 0, dqr, Ld, d), BH, s);
     // Previous chunk's state adjoints: state terms, then the token sums.
     hipLaunchKernelGGL(k_swb_state, dim3(grid1(BH * bp.nrb)), dim3(256), 0, s, P, bp.nrb, q.nC,
                        ri, coef, Ws, Ms, dWC, dMC, dWp, dMp, wsf(bp.dots));
-    gemm_f32(gf(2 * h, d, n, DA, b2, 1, 2 * h, Kr, Ld, d, 1, dWp, P, d, dWp, P, d), BH, PART, s);
-    gemm_f32(gf(2 * h, d, n, DAQ, b2, 1, 2 * h, Qr, Ld, d, 1, dWp, P, d, dWp, P, d), BH, PART, s);
-    gemm_f32(gf(d, h, n, E, bd, 1, d, DW, b1, h, 1, dWp + o2, P, h, dWp + o2, P, h), BH, PART, s);
+    gemm_f32(gf(2 * h, d, n, DA, b2, 1, 2 * h, Kr, Ld, d, 1, dWp, P, d, dWp, P, d), BH, s);
+    gemm_f32(gf(2 * h, d, n, DAQ, b2, 1, 2 * h, Qr, Ld, d, 1, dWp, P, d, dWp, P, d), BH, s);
+    gemm_f32(gf(d, h, n, E, bd, 1, d, DW, b1, h, 1, dWp + o2, P, h, dWp + o2, P, h), BH, s);
     gemm_f32(gf(d, h, n, dvr, Ld, 1, d, ZK, b1, h, 1, dWp + o2, P, h, dWp + o2, P, h, -1.0f),
-             BH, PART, s);
-    gemm_f32(gf(d, h, n, DOr, Ld, 1, d, ZQ, b1, h, 1, dWp + o2, P, h, dWp + o2, P, h), BH, PART, s);
+             BH, s);
+    gemm_f32(gf(d, h, n, DOr, Ld, 1, d, ZQ, b1, h, 1, dWp + o2, P, h, dWp + o2, P, h), BH, s);
     dWC = dWp;
     dMC = dMp;
   }

@@ -26,8 +26,10 @@
 // three dots exactly as for the linear learner.
 //
 // Every product over tokens or features is a call of one batched, strided
-// fp32 GEMM (64 x 64 tiles through LDS, fp32 MFMA); the per-token steps are
-// small elementwise kernels.  Only the chunk's n valid tokens enter any product.
+// fp32 GEMM (64 x 64 tiles through LDS, fp32 MFMA; products with few tiles
+// and a long K on 32 x 32 tiles with K split inside the workgroup); the
+// per-token steps are small elementwise kernels.  Only the chunk's n valid
+// tokens enter any product.
 #pragma once
 
 #include "kernels.hpp"
@@ -49,13 +51,6 @@ struct GemmF32 {
   float* C;
   int64_t sCb, ldc;
   float alpha;
-  // Split of K over nsplit workgroups (grid z = unit * nsplit + split), each
-  // taking kchunk (a multiple of 16) of K and writing its alpha-scaled partial
-  // to part[(unit * nsplit + split) * M * N + m * N + n]; k_gemm_split_sum then
-  // adds D and the splits in split order into C.  nsplit = 1: direct.
-  int nsplit;
-  int64_t kchunk;
-  float* part;
 };
 
 constexpr int GF_T = 64, GF_K = 16;
@@ -71,10 +66,8 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmF32 g) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, hf = lane >> 5;
-  const int64_t b = blockIdx.z / g.nsplit;
-  const int sp = static_cast<int>(blockIdx.z % g.nsplit);
-  const int64_t kb = sp * g.kchunk;
-  const int64_t ke = g.nsplit == 1 ? g.K : (kb + g.kchunk < g.K ? kb + g.kchunk : g.K);
+  const int64_t b = blockIdx.z;
+  const int64_t kb = 0, ke = g.K;
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * GF_T;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * GF_T;
   const float* A = g.A + b * g.sAb;
@@ -127,15 +120,6 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmF32 g) {
   // the wave's block.
   const int64_t n = n0 + 32 * wn + l32;
   if (n >= g.N) return;
-  if (g.nsplit > 1) {
-    float* Pp = g.part + blockIdx.z * g.M * g.N;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t m = m0 + 32 * wm + 8 * (v / 4) + 4 * hf + (v % 4);
-      if (m < g.M) Pp[m * g.N + n] = g.alpha * acc[v];
-    }
-    return;
-  }
   float* C = g.C + b * g.sCb;
   const float* D = g.D ? g.D + b * g.sDb : nullptr;
 #pragma unroll
@@ -147,16 +131,88 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmF32 g) {
   }
 }
 
-// C = D + the nsplit partials of a K-split product, added in split order.
-__global__ __launch_bounds__(256) void k_gemm_split_sum(GemmF32 g, int64_t BH) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t MN = g.M * g.N;
-  if (i >= BH * MN) return;
-  const int64_t b = i / MN, e = i % MN, m = e / g.N, n = e % g.N;
-  float acc = g.D ? g.D[b * g.sDb + m * g.ldd + n] : 0.0f;
-  for (int sp = 0; sp < g.nsplit; ++sp) acc += g.part[(b * g.nsplit + sp) * MN + e];
-  g.C[b * g.sCb + m * g.ldc + n] = acc;
+// Products with few output tiles and a long K: one 32 x 32 output tile per
+// workgroup, K split four ways inside it.  Wave w takes the w-th quarter of
+// the 16-deep slabs, staged through its own double-buffered LDS (so the
+// waves never wait for each other in the loop) and accumulated on
+// v_mfma_f32_32x32x2f32; the four partial tiles then meet in LDS and are
+// added in wave order, so the result does not depend on scheduling, and
+// C = D + alpha * sum is written directly: no partial buffer and no second
+// launch.  Loads run along whichever of an operand's strides is 1, as above.
+constexpr int GQ_T = 32;
+__global__ __launch_bounds__(256) void k_gemm_f32_k4(GemmF32 g) {
+  __shared__ float St[4][2][2][GF_K][GQ_T + 4];  // [wave][buffer][A, B][k][m or n]
+  __shared__ float Red[4][GQ_T][GQ_T + 1];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  const int64_t b = blockIdx.z;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * GQ_T;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * GQ_T;
+  const float* A = g.A + b * g.sAb;
+  const float* B = g.B + b * g.sBb;
+  const bool aK = g.sAk == 1;
+  const bool bN = g.sBn == 1;
+  // This wave's slabs: [s0, s1) of the ceil(K / 16) slabs.
+  const int64_t ns = (g.K + GF_K - 1) / GF_K;
+  const int64_t s0 = ns * wave / 4, s1 = ns * (wave + 1) / 4;
+  float ra[8], rb[8];
+  auto fetch = [&](int64_t k0) {
+#pragma unroll
+    for (int l = 0; l < 8; ++l) {
+      const int e = lane + 64 * l;  // 512 elements of each 32 x 16 slab
+      const int mm = aK ? e / GF_K : e % GQ_T, kk = aK ? e % GF_K : e / GQ_T;
+      const int64_t m = m0 + mm, k = k0 + kk;
+      ra[l] = (m < g.M && k < g.K) ? A[m * g.sAm + k * g.sAk] : 0.0f;
+      const int nn = bN ? e % GQ_T : e / GF_K, kq = bN ? e / GQ_T : e % GF_K;
+      const int64_t n = n0 + nn, kb = k0 + kq;
+      rb[l] = (n < g.N && kb < g.K) ? B[kb * g.sBk + n * g.sBn] : 0.0f;
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int l = 0; l < 8; ++l) {
+      const int e = lane + 64 * l;
+      St[wave][buf][0][aK ? e % GF_K : e / GQ_T][aK ? e / GF_K : e % GQ_T] = ra[l];
+      St[wave][buf][1][bN ? e / GQ_T : e % GF_K][bN ? e % GQ_T : e / GF_K] = rb[l];
+    }
+  };
+  f32x16_t acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  if (s0 < s1) {
+    fetch(s0 * GF_K);
+    stash(0);
+  }
+  int buf = 0;
+  for (int64_t sl = s0; sl < s1; ++sl) {
+    const bool more = sl + 1 < s1;
+    if (more) fetch((sl + 1) * GF_K);
+#pragma unroll
+    for (int ks = 0; ks < GF_K / 2; ++ks) {
+      const int k = 2 * ks + hf;
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(St[wave][buf][0][k][l32], St[wave][buf][1][k][l32],
+                                                 acc, 0, 0, 0);
+    }
+    if (more) stash(buf ^ 1);
+    buf ^= 1;
+  }
+  // Lane l, register v holds row 8 (v / 4) + 4 hf + v % 4, column l % 32.
+#pragma unroll
+  for (int v = 0; v < 16; ++v) Red[wave][8 * (v / 4) + 4 * hf + (v % 4)][l32] = acc[v];
+  __syncthreads();
+  float* C = g.C + b * g.sCb;
+  const float* D = g.D ? g.D + b * g.sDb : nullptr;
+#pragma unroll
+  for (int l = 0; l < 4; ++l) {
+    const int e = tid + 256 * l, mm = e / GQ_T, nn = e % GQ_T;
+    const int64_t m = m0 + mm, n = n0 + nn;
+    if (m >= g.M || n >= g.N) continue;
+    const float sum = ((Red[0][mm][nn] + Red[1][mm][nn]) + Red[2][mm][nn]) + Red[3][mm][nn];
+    const float base = D ? D[m * g.ldd + n] : 0.0f;
+    C[m * g.ldc + n] = base + g.alpha * sum;
+  }
 }
+
 
 __device__ __forceinline__ float sig_acc(float x) { return 1.0f / (1.0f + expf(-x)); }
 

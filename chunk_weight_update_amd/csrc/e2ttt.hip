@@ -1335,7 +1335,7 @@ void gemm_f32(GemmF32 g, int64_t BH, hipStream_t s) {
   if (tiles <= kCUs && g.K >= 2 * 4 * GF_K) {
     const dim3 grid(static_cast<unsigned>((g.N + GQ_T - 1) / GQ_T),
                     static_cast<unsigned>((g.M + GQ_T - 1) / GQ_T), static_cast<unsigned>(BH));
-    hipLaunchKernelGGL(k_gemm_f32_k4, grid, dim3(256), 0, s, g);
+    hipLaunchKernelGGL(k_gemm_f32_k4<32>, grid, dim3(256), GemmK4<32>::LDS_BYTES, s, g);
     return;
   }
   const dim3 grid(static_cast<unsigned>((g.N + GF_T - 1) / GF_T),

@@ -131,23 +131,40 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmF32 g) {
   }
 }
 
-// Products with few output tiles and a long K: one 32 x 32 output tile per
-// workgroup, K split four ways inside it.  Wave w takes the w-th quarter of
-// the 16-deep slabs, staged through its own double-buffered LDS (so the
-// waves never wait for each other in the loop) and accumulated on
+constexpr int GQ_T = 32;
+
+// K split four ways inside the workgroup: each wave computes the whole
+// TxT output tile (T = 32: one 32 x 32 MFMA block; T = 64: four) over its
+// quarter of the 16-deep slabs, staged through its own double-buffered LDS
+// (so the waves never wait for each other in the loop, and four slabs per
+// workgroup are in flight instead of one) and accumulated on
 // v_mfma_f32_32x32x2f32; the four partial tiles then meet in LDS and are
 // added in wave order, so the result does not depend on scheduling, and
 // C = D + alpha * sum is written directly: no partial buffer and no second
 // launch.  Loads run along whichever of an operand's strides is 1, as above.
-constexpr int GQ_T = 32;
+template <int T>
+struct GemmK4 {
+  static constexpr int LD = T + 4;                            // staged row, floats
+  static constexpr int STAGE = 2 * 2 * GF_K * LD;             // [buffer][A, B][k][m or n]
+  static constexpr int RED = T * (T + 1);                     // one wave's partial tile
+  static constexpr size_t LDS_BYTES =
+      4 * static_cast<size_t>(STAGE > RED ? STAGE : RED) * sizeof(float);
+  static constexpr int PER = T * GF_K / 64;                   // elements per lane per operand slab
+};
+
+template <int T>
 __global__ __launch_bounds__(256) void k_gemm_f32_k4(GemmF32 g) {
-  __shared__ float St[4][2][2][GF_K][GQ_T + 4];  // [wave][buffer][A, B][k][m or n]
-  __shared__ float Red[4][GQ_T][GQ_T + 1];
+  using Q = GemmK4<T>;
+  constexpr int LD = Q::LD, NB = T / 32;
+  extern __shared__ float smem_f[];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  float* St = smem_f + wave * (Q::STAGE > Q::RED ? Q::STAGE : Q::RED);
+  auto sa = [&](int buf, int k, int m) -> float& { return St[((buf * 2 + 0) * GF_K + k) * LD + m]; };
+  auto sb = [&](int buf, int k, int n) -> float& { return St[((buf * 2 + 1) * GF_K + k) * LD + n]; };
   const int64_t b = blockIdx.z;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * GQ_T;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * GQ_T;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * T;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * T;
   const float* A = g.A + b * g.sAb;
   const float* B = g.B + b * g.sBb;
   const bool aK = g.sAk == 1;
@@ -155,30 +172,34 @@ __global__ __launch_bounds__(256) void k_gemm_f32_k4(GemmF32 g) {
   // This wave's slabs: [s0, s1) of the ceil(K / 16) slabs.
   const int64_t ns = (g.K + GF_K - 1) / GF_K;
   const int64_t s0 = ns * wave / 4, s1 = ns * (wave + 1) / 4;
-  float ra[8], rb[8];
+  float ra[Q::PER], rb[Q::PER];
   auto fetch = [&](int64_t k0) {
 #pragma unroll
-    for (int l = 0; l < 8; ++l) {
-      const int e = lane + 64 * l;  // 512 elements of each 32 x 16 slab
-      const int mm = aK ? e / GF_K : e % GQ_T, kk = aK ? e % GF_K : e / GQ_T;
+    for (int l = 0; l < Q::PER; ++l) {
+      const int e = lane + 64 * l;
+      const int mm = aK ? e / GF_K : e % T, kk = aK ? e % GF_K : e / T;
       const int64_t m = m0 + mm, k = k0 + kk;
       ra[l] = (m < g.M && k < g.K) ? A[m * g.sAm + k * g.sAk] : 0.0f;
-      const int nn = bN ? e % GQ_T : e / GF_K, kq = bN ? e / GQ_T : e % GF_K;
+      const int nn = bN ? e % T : e / GF_K, kq = bN ? e / T : e % GF_K;
       const int64_t n = n0 + nn, kb = k0 + kq;
       rb[l] = (n < g.N && kb < g.K) ? B[kb * g.sBk + n * g.sBn] : 0.0f;
     }
   };
   auto stash = [&](int buf) {
 #pragma unroll
-    for (int l = 0; l < 8; ++l) {
+    for (int l = 0; l < Q::PER; ++l) {
       const int e = lane + 64 * l;
-      St[wave][buf][0][aK ? e % GF_K : e / GQ_T][aK ? e / GF_K : e % GQ_T] = ra[l];
-      St[wave][buf][1][bN ? e / GQ_T : e % GF_K][bN ? e % GQ_T : e / GF_K] = rb[l];
+      sa(buf, aK ? e % GF_K : e / T, aK ? e / GF_K : e % T) = ra[l];
+      sb(buf, bN ? e / T : e % GF_K, bN ? e % T : e / GF_K) = rb[l];
     }
   };
-  f32x16_t acc;
+  f32x16_t acc[NB][NB];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
   if (s0 < s1) {
     fetch(s0 * GF_K);
     stash(0);
@@ -190,24 +211,38 @@ __global__ __launch_bounds__(256) void k_gemm_f32_k4(GemmF32 g) {
 #pragma unroll
     for (int ks = 0; ks < GF_K / 2; ++ks) {
       const int k = 2 * ks + hf;
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(St[wave][buf][0][k][l32], St[wave][buf][1][k][l32],
-                                                 acc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(sa(buf, k, 32 * i + l32),
+                                                           sb(buf, k, 32 * j + l32), acc[i][j],
+                                                           0, 0, 0);
     }
     if (more) stash(buf ^ 1);
     buf ^= 1;
   }
-  // Lane l, register v holds row 8 (v / 4) + 4 hf + v % 4, column l % 32.
+  // Partial tile of this wave into its own area (the staging area is this
+  // wave's alone); lane l, register v of block (i, j) holds row
+  // 32 i + 8 (v / 4) + 4 hf + v % 4, column 32 j + l % 32.
 #pragma unroll
-  for (int v = 0; v < 16; ++v) Red[wave][8 * (v / 4) + 4 * hf + (v % 4)][l32] = acc[v];
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        St[(32 * i + 8 * (v / 4) + 4 * hf + (v % 4)) * (T + 1) + 32 * j + l32] = acc[i][j][v];
   __syncthreads();
+  const int WS = Q::STAGE > Q::RED ? Q::STAGE : Q::RED;
   float* C = g.C + b * g.sCb;
   const float* D = g.D ? g.D + b * g.sDb : nullptr;
 #pragma unroll
-  for (int l = 0; l < 4; ++l) {
-    const int e = tid + 256 * l, mm = e / GQ_T, nn = e % GQ_T;
+  for (int l = 0; l < T * T / 256; ++l) {
+    const int e = tid + 256 * l, mm = e / T, nn = e % T;
     const int64_t m = m0 + mm, n = n0 + nn;
     if (m >= g.M || n >= g.N) continue;
-    const float sum = ((Red[0][mm][nn] + Red[1][mm][nn]) + Red[2][mm][nn]) + Red[3][mm][nn];
+    const int o = mm * (T + 1) + nn;
+    const float sum = ((smem_f[o] + smem_f[WS + o]) + smem_f[2 * WS + o]) + smem_f[3 * WS + o];
     const float base = D ? D[m * g.ldd + n] : 0.0f;
     C[m * g.ldc + n] = base + g.alpha * sum;
   }

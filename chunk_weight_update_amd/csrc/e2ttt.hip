@@ -190,15 +190,17 @@ e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
     q.kw = take(f4 * q.BH * q.nC * q.Cp);
     q.km = take(f4 * q.BH * q.nC * q.Cp);
     q.coef = take(f4 * q.BH * q.nC * 4);
-    q.kt = take(T * q.BH * q.nC * q.d * q.Cp);
+    // Plain bf16 operands with d, h and the padded chunk multiples of 256:
+    // the forward GEMMs (fwd13, fwd2) run on 256x256 tiles, the backward
+    // takes the SiLU factors as bf16 pairs instead of an fp32 copy of A1, A3
+    // and writes dA1, dA3 unscaled; the aggregation contracts them against
+    // the keys scaled by K^W and K^M (two feature-major copies per chunk).
+    q.tile256 = q.io == E2TTT_BF16 && q.krep == 1 && q.d % 256 == 0 && q.h % 256 == 0 &&
+                q.Cp % 256 == 0;
+    q.kt = take(T * q.BH * q.nC * (q.tile256 ? 2 : 1) * q.d * q.Cp);
     q.w13s = take(T * q.BH * 2 * q.h * q.krep * q.d);
     q.w2s = take(T * q.BH * q.d * q.krep * q.h);
     q.w2ts = take(T * q.BH * q.h * q.krep * q.d);
-    // Plain bf16 operands with d, h and the padded chunk multiples of 256:
-    // the forward GEMMs (fwd13, fwd2) run on 256x256 tiles, and the backward
-    // takes the SiLU factors as bf16 pairs instead of an fp32 copy of A1, A3.
-    q.tile256 = q.io == E2TTT_BF16 && q.krep == 1 && q.d % 256 == 0 && q.h % 256 == 0 &&
-                q.Cp % 256 == 0;
     q.zrow = take(T * q.BH * 2 * q.Cp * q.h);
     q.a1s = q.a3s = q.fac = 0;
     if (q.tile256) {
@@ -208,7 +210,7 @@ e2ttt_status make_plan(const e2ttt_problem* p, Plan* pl) {
       q.a3s = take(f4 * q.BH * q.Cp * q.h);
     }
     q.grow = take(T * q.BH * q.Cp * q.d);
-    q.ut = take(T * q.BH * 4 * q.h * q.Cp);
+    q.ut = take(T * q.BH * (q.tile256 ? 2 : 4) * q.h * q.Cp);
     q.gt = take(T * q.BH * 2 * q.d * q.Cp);
     q.zt = take(T * q.BH * q.h * q.Cp);
     // bf16 operands with d, h multiples of 256: the aggregation runs on
@@ -467,11 +469,11 @@ void launch_fwd_bwd256(const Plan& q, const Shape& s, int r, const T* Q, const T
     if (q.h % 192 == 0) {
       E2TTT_LAUNCH(I, E2TTT_KERNEL_BWD, k_bwd256<6>,
                    dim3(grid1(q.BH * (q.Cp / 256) * (q.h / 192))), dim3(256),
-                   Bwd256<6>::LDS_BYTES, st, s, r, grow, w2ts, fac, kw, km, ut);
+                   Bwd256<6>::LDS_BYTES, st, s, r, grow, w2ts, fac, ut);
     } else {
       E2TTT_LAUNCH(I, E2TTT_KERNEL_BWD, k_bwd256<4>,
                    dim3(grid1(q.BH * (q.Cp / 256) * (q.h / 128))), dim3(256),
-                   Bwd256<4>::LDS_BYTES, st, s, r, grow, w2ts, fac, kw, km, ut);
+                   Bwd256<4>::LDS_BYTES, st, s, r, grow, w2ts, fac, ut);
     }
   }
 }
@@ -487,6 +489,7 @@ void launch_swiglu(const Plan& q, const void* qv, const void* kv, const void* vv
   T* O = static_cast<T*>(outv);
   Shape s{q.BH, q.L, q.d, q.h, q.C, q.Cp, q.nC, q.krep};
   s.gated = q.kind == E2TTT_MLP ? 0 : 1;
+  s.sk = q.tile256 ? 1 : 0;
   float* kw = reinterpret_cast<float*>(ws + q.kw);
   float* km = reinterpret_cast<float*>(ws + q.km);
   float* coef = reinterpret_cast<float*>(ws + q.coef);
@@ -503,9 +506,16 @@ void launch_swiglu(const Plan& q, const void* qv, const void* kv, const void* vv
   T* zt = reinterpret_cast<T*>(ws + q.zt);
 
   launch_scan(q, eta, alpha, beta, kw, km, q.nC * q.Cp, q.Cp, q.Cp, coef, 4, st, I);
-  void (*kprep)(Shape, const T*, T*) = k_prep_kt<T, false>;
-  E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, kprep,
-               dim3(grid1(q.BH * q.nC * (q.Cp / 64) * (q.d / 64))), dim3(256), 0, st, s, K, kt);
+  if (q.tile256) {
+    if constexpr (sizeof(T) == 2)
+      E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, k_prep_kts,
+                   dim3(grid1(q.BH * q.nC * (q.Cp / 64) * (q.d / 64))), dim3(256), 0, st, s, K,
+                   kw, km, kt);
+  } else {
+    void (*kprep)(Shape, const T*, T*) = k_prep_kt<T, false>;
+    E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, kprep,
+                 dim3(grid1(q.BH * q.nC * (q.Cp / 64) * (q.d / 64))), dim3(256), 0, st, s, K, kt);
+  }
   E2TTT_LAUNCH(I, E2TTT_KERNEL_PREP, k_prep_shadow<T>, dim3(grid1(shadow_blocks(s))),
                dim3(256), 0, st, s, W0, w13s, w2s, w2ts);
   const int64_t na = (4 * q.h / 128) * (q.d / 128), nb = (2 * q.d / 128) * (q.h / 128);

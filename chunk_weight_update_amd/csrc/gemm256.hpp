@@ -303,10 +303,14 @@ __device__ __forceinline__ void gemm_tile256w8(f32x16_t (&acc)[4][2], ARow arow,
 }
 
 // Partial aggregates of split sp over token slabs [k0, k1): workgroup
-// (unit, split, tile); tiles 0 .. na-1 are family A (4h/256 x d/256), then
-// family B (2d/256 x h/256).  The partial of state entry e goes to
-// part[((sp * 2 + wm) * BH + u) * P + e], wm = 0 for A^W, 1 for A^M.
-// 8 waves on the 256 x 256 tile (gemm_tile256w8).
+// (unit, split, tile); tiles 0 .. na-1 are family A, then family B (2d/256 x
+// h/256).  Family A is either (s.sk = 0) the scaled backward operands
+// [K^W dA1 | K^M dA1 | K^W dA3 | K^M dA3]^T against K (4h/256 x d/256 tiles,
+// W and M rows interleaved in 32-row groups) or (s.sk = 1) the unscaled
+// [dA1 | dA3]^T against the scaled keys [K^W K | K^M K] (2h/256 x 2d/256
+// tiles; column block nt < d/256 is A^W, the rest A^M).  The partial of
+// state entry e goes to part[((sp * 2 + wm) * BH + u) * P + e], wm = 0 for
+// A^W, 1 for A^M.  8 waves on the 256 x 256 tile (gemm_tile256w8).
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_agg256(
     Shape s, int nsplit, const bf16_t* __restrict__ ut, const bf16_t* __restrict__ kt,
     const bf16_t* __restrict__ gt, const bf16_t* __restrict__ zt, int r, float* part) {
@@ -323,7 +327,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   int64_t mt, nt;
   const bf16_t* abase;
   const bf16_t* bbase;
-  if (famA) {
+  if (famA && s.sk) {
+    mt = t / (2 * d / 256); nt = t % (2 * d / 256);
+    abase = ut + (u * 2 * h + mt * 256) * s.Cp;
+    bbase = kt + ((u * s.nC + r) * 2 * d + nt * 256) * s.Cp;
+  } else if (famA) {
     mt = t / (d / 256); nt = t % (d / 256);
     abase = ut + (u * 4 * h + mt * 256) * s.Cp;
     bbase = kt + ((u * s.nC + r) * d + nt * 256) * s.Cp;
@@ -347,6 +355,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int wm = wave >> 2, wn = wave & 3;
   const int r32 = lane & 31, hf = lane >> 5;
   const int64_t P = 3 * d * h;
+  if (famA && s.sk) {
+    // Tile rows: state rows of W1 (R < h) or W3 (R >= h, which follow W1 in
+    // the packed state); columns: A^W (c < d) or A^M (c - d).
+    const int mflag = nt * 256 >= d ? 1 : 0;
+    float* dst = part + ((static_cast<int64_t>(sp) * 2 + mflag) * s.BH + u) * P +
+                 (mt * 256 + wm * 128) * d + nt * 256 - mflag * d;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const int64_t c = wn * 64 + ni * 32 + r32;
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          dst[(32 * mi + 8 * (v >> 2) + 4 * hf + (v & 3)) * d + c] = acc[mi][ni][v];
+      }
+    return;
+  }
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
     // State rows of block mi: row base and stride in the packed state.
@@ -758,10 +783,13 @@ __device__ __forceinline__ void gemm_rows256(f32x16_t (&acc)[2][NB], ARow arow, 
 // ---------------------------------------------------------------------------
 // Backward of the 256 path: dZ = g W2 on the tile's tokens and hidden units,
 // then dA1 = dZ f1 and dA3 = dZ f3 with the SiLU factors that k_fwd13_256
-// stored for the same K rows (bf16), scaled by both kernels into the
-// feature-major operands of the aggregation.  Storing the factors costs 4
-// bytes per token and hidden unit written and read; recomputing A1 and A3
-// here instead cost twice the products of dZ (4dh flop per token) on top.
+// stored for the same K rows (bf16), written once each, unscaled and
+// feature-major: the aggregation's first family contracts them against the
+// scaled keys K^W K, K^M K (k_prep_kts), since (K^W dA1)^T K = dA1^T (K^W K).
+// Writing the four scaled products here instead moved twice the bytes.
+// Storing the factors costs 4 bytes per token and hidden unit written and
+// read; recomputing A1 and A3 here instead cost twice the products of dZ
+// (4dh flop per token) on top.
 //
 // Tile: 256 tokens x 32*NB hidden units of one unit on the row engine (A = g
 // rows, B = W2^T rows of the units).
@@ -770,16 +798,14 @@ struct Bwd256 {
   using G = Rows256<NB>;
   static constexpr int BM = G::BM;
   static constexpr int SW = BM + 8;              // staged output row, bf16
-  static constexpr int STG = 4 * 64 * SW * 2;    // one epilogue pass: 4 outputs x 64 units
-  static constexpr int KS = G::STAGES_BYTES > STG ? G::STAGES_BYTES : STG;  // K^W, K^M
-  static constexpr size_t LDS_BYTES = static_cast<size_t>(KS) + 2 * BM * 4;
+  static constexpr int STG = 2 * 64 * SW * 2;    // one epilogue pass: 2 outputs x 64 units
+  static constexpr size_t LDS_BYTES = G::STAGES_BYTES > STG ? G::STAGES_BYTES : STG;
 };
 
 template <int NB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_bwd256(
     Shape s, int r, const bf16_t* __restrict__ grow, const bf16_t* __restrict__ w2ts,
-    const uint32_t* __restrict__ fac, const float* __restrict__ kw,
-    const float* __restrict__ km, bf16_t* ut) {
+    const uint32_t* __restrict__ fac, bf16_t* ut) {
   using B = Bwd256<NB>;
   constexpr int BN = 32 * NB;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
@@ -798,10 +824,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int64_t d = s.d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r32 = lane & 31, hf = lane >> 5;
-  // The tile's K^W, K^M (one token per thread), stored in LDS past the
-  // stages for the epilogue.
-  const float kwt = kw[(u * s.nC + r) * s.Cp + p0 + threadIdx.x];
-  const float kmt = km[(u * s.nC + r) * s.Cp + p0 + threadIdx.x];
+  (void)r;
 
   using Fac = uint4[2][2][4];
   auto fac_load = [&](Fac& f, int p) __attribute__((always_inline)) {
@@ -828,18 +851,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // of block (mi, jb), register v: token p0 + 64*wave + 32*mi + 8*(v/4) +
   // 4*hf + v%4, unit j0 + 32*jb + r32; the factors of the same token and unit
   // are word v of the lane's quarter of the factor block.  A pass stages its
-  // four scaled outputs (o = dA1 K^W, dA1 K^M, dA3 K^W, dA3 K^M) in LDS as
-  // [o][unit][256 tokens + 8] bf16 (the stages are free: every wave has
-  // passed the last slab's barrier and read its fragments), then copies them
-  // out in whole 512-byte rows: ut row (W1 | W3 family) + 64*(j/32) + (0 | 32
-  // for K^M) + j%32, tokens p0 .. p0+255.  The next pass's factors are loaded
+  // two outputs (o = dA1, dA3) in LDS as [o][unit][256 tokens + 8] bf16 (the
+  // stages are free: every wave has passed the last slab's barrier and read
+  // its fragments), then copies them out in whole 512-byte rows: ut row
+  // (0 | h) + j, tokens p0 .. p0+255.  The next pass's factors are loaded
   // before this pass's stores, so that waiting for them does not wait for
   // the stores.
   constexpr int SW = B::SW;
   bf16_t* stg = reinterpret_cast<bf16_t*>(smem_raw);
-  float* ksh = reinterpret_cast<float*>(smem_raw + B::KS);
-  ksh[threadIdx.x] = kwt;
-  ksh[B::BM + threadIdx.x] = kmt;
   auto pass = [&](auto P, const Fac& f) __attribute__((always_inline)) {
     constexpr int p = decltype(P)::value;
 #pragma unroll
@@ -849,22 +868,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int vq = 0; vq < 4; ++vq) {
         const int tk = 64 * wave + 32 * mi + 8 * vq + 4 * hf;
-        const f32x4_t kw4 = *reinterpret_cast<const f32x4_t*>(ksh + tk);
-        const f32x4_t km4 = *reinterpret_cast<const f32x4_t*>(ksh + B::BM + tk);
 #pragma unroll
         for (int j2 = 0; j2 < 2; ++j2) {
           const uint4 fv = f[mi][j2][vq];
           const uint32_t fw[4] = {fv.x, fv.y, fv.z, fv.w};
-          float x1w[4], x1m[4], x3w[4], x3m[4];
+          float x1[4], x3[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float dzv = dz[mi][2 * p + j2][4 * vq + e];
-            const float d1 = dzv * __uint_as_float(fw[e] << 16);
-            const float d3 = s.gated ? dzv * __uint_as_float(fw[e] & 0xffff0000u) : 0.0f;
-            x1w[e] = kw4[e] * d1;
-            x1m[e] = km4[e] * d1;
-            x3w[e] = kw4[e] * d3;
-            x3m[e] = km4[e] * d3;
+            x1[e] = dzv * __uint_as_float(fw[e] << 16);
+            x3[e] = s.gated ? dzv * __uint_as_float(fw[e] & 0xffff0000u) : 0.0f;
           }
           const int jj = 32 * j2 + r32;
           auto put = [&](int o, const float (&x)[4]) {
@@ -872,29 +885,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 make_uint2(pack_bf16x2(x[0], x[1]),
                            pack_bf16x2(x[2], x[3]));
           };
-          put(0, x1w);
-          put(1, x1m);
-          put(2, x3w);
-          put(3, x3m);
+          put(0, x1);
+          put(1, x3);
         }
       }
     }
   };
-  bf16_t* ub = ut + u * 4 * s.h * s.Cp + p0;
+  bf16_t* ub = ut + u * 2 * s.h * s.Cp + p0;
   auto copy_out = [&](int p) __attribute__((always_inline)) {
     constexpr int VPR = B::BM / 8;  // 16-byte pieces per row
 #pragma unroll
-    for (int i = 0; i < 4 * 64 * VPR / 256; ++i) {
+    for (int i = 0; i < 2 * 64 * VPR / 256; ++i) {
       const int idx = threadIdx.x + 256 * i;
       const int row = idx / VPR, c = idx % VPR;
       const int o = row / 64, jj = row % 64;
-      const int64_t j = j0 + 64 * p + jj;
-      const int64_t dst = (o >= 2 ? 2 * s.h : 0) + 64 * (j / 32) + (o & 1 ? 32 : 0) + j % 32;
+      const int64_t dst = (o ? s.h : 0) + j0 + 64 * p + jj;
       *reinterpret_cast<uint4*>(ub + dst * s.Cp + 8 * c) =
           *reinterpret_cast<const uint4*>(stg + row * SW + 8 * c);
     }
   };
-  barrier_lds();  // every wave's last fragment reads are done; K^W, K^M visible
+  barrier_lds();  // every wave's last fragment reads are done
   auto run = [&](auto P, const Fac& cur, Fac& nxt) __attribute__((always_inline)) {
     constexpr int p = decltype(P)::value;
     pass(P, cur);
@@ -906,6 +916,68 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   run(Band<0>{}, fa, fb);
   if constexpr (NB >= 4) run(Band<1>{}, fb, fa);
   if constexpr (NB >= 6) run(Band<2>{}, fa, fb);
+}
+
+// Family A's token operand on the 256 path: the chunk's keys scaled by both
+// kernels, feature-major, [BH][nC][2d][Cp]: rows 0 .. d-1 hold K^W k, rows
+// d .. 2d-1 hold K^M k (padded tokens have k = 0 and K = 0), each value
+// rounded once to bf16 from the fp32 product.  One block per 64 tokens x 64
+// features of one (unit, chunk): the tile goes through LDS transposed, then
+// both scaled copies leave in 16-byte pieces of whole rows.
+__global__ __launch_bounds__(256) void k_prep_kts(Shape s, const bf16_t* __restrict__ k,
+                                                  const float* __restrict__ kw,
+                                                  const float* __restrict__ km,
+                                                  bf16_t* __restrict__ kts) {
+  __shared__ float tile[64][64 + 1];
+  __shared__ float ksc[2][64];
+  int64_t bid = blockIdx.x;
+  const int64_t ptiles = s.Cp / 64, ctiles = s.d / 64;
+  const int64_t ct = bid % ctiles; bid /= ctiles;
+  const int64_t pt = bid % ptiles; bid /= ptiles;
+  const int r = static_cast<int>(bid % s.nC);
+  const int64_t u = bid / s.nC;
+  const int64_t nv = n_valid(s, r);
+  const int tid = threadIdx.x;
+  const bf16_t* ks = k + (u * s.L + static_cast<int64_t>(r) * s.C) * s.d + ct * 64;
+  uint4 reg[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {  // 64 token rows x 8 pieces of 8 values
+    const int idx = tid + 256 * i;
+    const int pr = idx / 8, cv = idx % 8;
+    const int64_t p = pt * 64 + pr;
+    const uint4 val = *reinterpret_cast<const uint4*>(ks + (p < nv ? p : 0) * s.d + cv * 8);
+    reg[i] = p < nv ? val : make_uint4(0u, 0u, 0u, 0u);
+  }
+  if (tid < 128) {
+    const float* kk = tid < 64 ? kw : km;
+    ksc[tid / 64][tid % 64] = kk[(u * s.nC + r) * s.Cp + pt * 64 + tid % 64];
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int idx = tid + 256 * i;
+    const int pr = idx / 8, cv = idx % 8;
+    const uint32_t w[4] = {reg[i].x, reg[i].y, reg[i].z, reg[i].w};
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      tile[cv * 8 + 2 * x][pr] = __uint_as_float(w[x] << 16);
+      tile[cv * 8 + 2 * x + 1][pr] = __uint_as_float(w[x] & 0xffff0000u);
+    }
+  }
+  __syncthreads();
+  bf16_t* dst = kts + ((u * s.nC + r) * 2 * s.d + ct * 64) * s.Cp + pt * 64;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // 2 x 64 feature rows x 8 pieces of 8 tokens
+    const int idx = tid + 256 * i;
+    const int o = idx / 512, cr = (idx / 8) % 64, pv = idx % 8;
+    uint32_t pk[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int t0 = pv * 8 + 2 * x;
+      pk[x] = pack_bf16x2(tile[cr][t0] * ksc[o][t0], tile[cr][t0 + 1] * ksc[o][t0 + 1]);
+    }
+    *reinterpret_cast<uint4*>(dst + (o * s.d + cr) * s.Cp + pv * 8) =
+        make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -45,6 +45,9 @@ struct Shape {
   // A3 is taken as 1 (its weights are zero) and its gradient dA3 as 0, so
   // z = silu(A1), dA1 = dZ silu'(A1) and W3 stays zero.
   int gated = 1;
+  // 1 on the 256-tile path: the aggregation's first family takes the
+  // unscaled dA1, dA3 against the keys scaled by K^W and K^M.
+  int sk = 0;
 };
 
 __device__ __forceinline__ int64_t n_valid(const Shape& s, int r) {

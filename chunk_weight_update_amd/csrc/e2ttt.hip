@@ -451,8 +451,8 @@ void launch_fwd_bwd256(const Plan& q, const Shape& s, int r, const T* Q, const T
   static_assert(sizeof(T) == 2 || sizeof(T) == 4, "operand type");
   if constexpr (sizeof(T) == 2) {
     E2TTT_LAUNCH(I, E2TTT_KERNEL_FWD13, k_fwd13_256,
-                 dim3(grid1(q.BH * (2 * q.Cp / 256) * (2 * q.h / 256))), dim3(256),
-                 Tile256::LDS_BYTES, st, s, r, Q, K, w13s, zrow, zt, fac);
+                 dim3(grid1(q.BH * (2 * q.Cp / 256) * (2 * q.h / 256))), dim3(512),
+                 Tile256w8::LDS_BYTES, st, s, r, Q, K, w13s, zrow, zt, fac);
     // 192 output features per readout tile where d allows (one workgroup per
     // CU at d = 768), else 128.
     if (q.d % 192 == 0) {

@@ -10,15 +10,15 @@
 // with operands already scaled and rounded once (the backward, the readout)
 // and stored feature-major (rows = output rows, contiguous along tokens).
 //
-// Three engines share one slab format: k-slabs of 32 (tokens or features)
+// Two engines share one slab format: k-slabs of 32 (tokens or features)
 // go from global memory straight into LDS (global_load_lds, no registers),
 // several stages deep, so later slabs are in flight while one is computed.
 // LDS rows are 64 bytes, unpadded; the four 16-byte pieces of row r are
 // stored in the order kc ^ swz256(r), so the 8 or 16 rows that one fragment
 // read serves together hit distinct bank groups.
-//   gemm_tile256:   256 x 256 tile, 4 waves of 128 x 128 (4 x 4 blocks of
-//                   32x32x16 MFMA, 256 accumulator registers) -- k_fwd13_256.
-//   gemm_tile256w8: the same tile with 8 waves of 128 x 64 -- k_agg256.
+//   gemm_tile256w8: 256 x 256 tile, 8 waves of 128 x 64 (4 x 2 blocks of
+//                   32x32x16 MFMA, 128 accumulator registers, two waves per
+//                   SIMD) -- k_fwd13_256 and k_agg256.
 //   gemm_rows256:   256 x 32*NB tile, 4 waves of 64 x 32*NB -- the readout
 //                   (k_fwd2r) and the backward (k_bwd256), where 192-wide
 //                   tiles give one workgroup per CU.
@@ -35,39 +35,10 @@
 
 namespace e2ttt {
 
-struct Tile256 {
-  static constexpr int BM = 256, BN = 256, BK = 32;
-  static constexpr int NST = 4;                             // LDS stages
-  static constexpr int SLAB_BYTES = BM * BK * 2;            // one operand slab (bf16)
-  static constexpr size_t LDS_BYTES = NST * 2 * SLAB_BYTES;  // A and B per stage: 128 KB
-};
-
-// Source of one 256-row operand for the direct LDS loads.  Load i (0..3) of
-// wave w fills the 1 KB of LDS that holds slab rows 16*(4w+i) .. +15: lane l
-// brings row 16*(4w+i) + l/4, physical piece l%4, which holds logical k-chunk
-// loader256_chunk(i).  rowp[i] points at that row's chunk (k offset 0).
-struct Loader256 {
-  const bf16_t* rowp[4];
-  // Load i of this wave for the slab starting at token k0 into `slab`.
-  __device__ __forceinline__ void issue1(int i, int64_t k0, char* slab) const {
-    const int wave = threadIdx.x >> 6;
-    __builtin_amdgcn_global_load_lds(
-        static_cast<const void*>(rowp[i] + k0),
-        (__attribute__((address_space(3))) void*)(slab + (4 * wave + i) * 1024), 16, 0, 0);
-  }
-};
-
 // Physical 16-byte piece of logical k-chunk kc in slab row r: kc ^ swz(r),
 // with swz chosen so that 8 or 16 consecutive rows read at one chunk hit
 // distinct 16-byte bank groups.
 __device__ __forceinline__ int swz256(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
-
-__device__ __forceinline__ int loader256_row(int i) {
-  return 16 * (4 * (threadIdx.x >> 6) + i) + ((threadIdx.x & 63) >> 2);
-}
-__device__ __forceinline__ int loader256_chunk(int i) {
-  return (threadIdx.x & 3) ^ swz256(loader256_row(i));
-}
 
 // Workgroup barrier without the memory fence of __syncthreads (whose
 // release would wait for every load in flight, the prefetched slabs
@@ -88,9 +59,6 @@ __device__ __forceinline__ void barrier_lds() {
   barrier_nofence();
 }
 
-// Wait until at most 8n of this wave's slab loads are in flight (n slabs).
-__device__ __forceinline__ void wait_slabs(int n);
-
 // Wait until at most N vector memory operations of this wave are in flight
 // (gfx9 s_waitcnt encoding; expcnt and lgkmcnt left unconstrained).
 template <int N>
@@ -99,114 +67,17 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
-__device__ __forceinline__ void wait_slabs(int n) {
-  if (n >= 3) wait_vmcnt<24>();
-  else if (n == 2) wait_vmcnt<16>();
-  else if (n == 1) wait_vmcnt<8>();
-  else wait_vmcnt<0>();
-}
-
-// acc[mi][ni] (rows wm*128 + 32*mi, cols wn*128 + 32*ni) += A B^T over k
-// [k0, k1) (multiples of 32).  Each slab costs a wave 8 loads (4 per
-// operand); NST-1 slabs are in flight from global memory while one is
-// computed.
-//
-// Order of one slab's instructions (fixed with scheduling fences): the
-// fragments of the first MFMA group, then eight groups of four MFMAs, each
-// followed by one of the slab's eight direct LDS loads and by the fragment
-// reads of a later group.  A wave with all eight loads up front stalls on
-// their issue (the load queue drains at the memory rate) before its first
-// MFMA, so the loads and the matrix core took turns instead of overlapping
-// (measured: about 1.25x more cycles per slab).  The loop over the slabs that
-// issue a refill is kept free of conditions so that each slab body is one
-// scheduling region; the last NST-1 slabs run in a second loop.
-__device__ __forceinline__ void gemm_tile256(f32x16_t (&acc)[4][4], const Loader256& la,
-                                             const Loader256& lb, int64_t k0, int64_t k1,
-                                             char* lds) {
-  constexpr int NST = Tile256::NST, SB = Tile256::SLAB_BYTES, BK = Tile256::BK;
-  static_assert(NST == 4, "wait counts below assume four stages");
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int r32 = lane & 31, hf = lane >> 5, sw = swz256(r32);
-  // Byte offset of this lane's fragment piece in k-step ks, inside a
-  // 32-row block (the block bases are multiples of 32 rows, so the swizzle
-  // only depends on r32).
-  const int off0 = r32 * 64 + ((hf ^ sw) << 4), off1 = r32 * 64 + (((2 + hf) ^ sw) << 4);
-  const int ns = static_cast<int>((k1 - k0) / BK);
-  // Load q (0..7) of a slab: operand q / 4, piece q % 4 of the wave's rows.
-  auto load = [&](int slab, int q) {
-    char* st = lds + (slab % NST) * 2 * SB;
-    (q < 4 ? la : lb).issue1(q & 3, k0 + static_cast<int64_t>(slab) * BK, st + (q < 4 ? 0 : SB));
-  };
-  auto body = [&](int s, bool refill) {
-    const char* As = lds + (s % NST) * 2 * SB + wm * 128 * 64;
-    const char* Bs = lds + (s % NST) * 2 * SB + SB + wn * 128 * 64;
-    bf16x8_t fa[2][4], fb[2][4];
-    auto rda = [&](int ks, int i) {
-      fa[ks][i] = *reinterpret_cast<const bf16x8_t*>(As + i * 32 * 64 + (ks ? off1 : off0));
-    };
-    auto rdb = [&](int ks, int j) {
-      fb[ks][j] = *reinterpret_cast<const bf16x8_t*>(Bs + j * 32 * 64 + (ks ? off1 : off0));
-    };
-    // Fragments read after group g (= 4 ks + i), one group ahead of their use.
-    auto reads_after = [&](int g) {
-      if (g == 0) rda(0, 2);
-      else if (g == 1) rda(0, 3);
-      else if (g == 2) { rdb(1, 0); rdb(1, 1); rdb(1, 2); rdb(1, 3); rda(1, 0); }
-      else if (g == 3) rda(1, 1);
-      else if (g == 4) rda(1, 2);
-      else if (g == 5) rda(1, 3);
-    };
-    rdb(0, 0); rdb(0, 1); rdb(0, 2); rdb(0, 3); rda(0, 0); rda(0, 1);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const int ks = g >> 2, i = g & 3;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
-      if (refill) load(s + NST - 1, g);
-      reads_after(g);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  // Iteration s: wait for slab s (at most NST-2 later slabs in flight),
-  // barrier (every wave has it, and every wave has read slab s-1, whose stage
-  // takes slab s+NST-1), then slab s's MFMAs with that refill spread among
-  // them.
-#pragma unroll
-  for (int p = 0; p < NST - 1; ++p)
-    if (p < ns)
-#pragma unroll
-      for (int q = 0; q < 8; ++q) load(p, q);
-  int s = 0;
-  for (; s < ns - (NST - 1); ++s) {
-    wait_vmcnt<8 * (NST - 2)>();
-    barrier_nofence();
-    body(s, true);
-  }
-  for (; s < ns; ++s) {
-    const int later = ns - 1 - s;
-    wait_slabs(later < NST - 2 ? later : NST - 2);
-    barrier_nofence();
-    body(s, false);
-  }
-  barrier_nofence();  // every wave's last reads are done before LDS is reused
-}
-
-// The same 256 x 256 tile with 8 waves, two per SIMD: wave w takes rows
+// 256 x 256 tile with 8 waves, two per SIMD: wave w takes rows
 // 128*(w/4) + [0,128) (blocks mi = 0..3) and columns 64*(w%4) + [0,64)
 // (blocks ni = 0, 1), 128 accumulator registers.  A stage holds the slab's
 // 256 A rows then 256 B rows (64 bytes each, the engine's swizzle); each wave
 // issues 4 of the slab's 32 direct loads, one every 4 of its 16 MFMAs.  With
 // two waves per SIMD one wave's MFMAs run while the other is held by its
-// load issue or its fragment reads, which with one wave per SIMD took turns.
+// load issue or its fragment reads, which with one wave per SIMD (4 waves of
+// 128 x 128) took turns.  A wave with all of a slab's loads up front stalls
+// on their issue (the load queue drains at the memory rate) before its first
+// MFMA, so the loads are spread among the MFMA groups (measured on the
+// 4-wave form: about 1.25x more cycles per slab otherwise).
 struct Tile256w8 {
   static constexpr int BK = 32, NST = 4;
   static constexpr int STAGE = 512 * 64;                      // 32 KB
@@ -568,11 +439,18 @@ __device__ __forceinline__ int64_t fac_block(const Shape& s, int64_t u, int64_t 
   return ((u * (s.Cp / 32) + tb) * (s.h / 32) + hb) * 1024;
 }
 
-// fwd13: [K; Q] rows x [W1; W3]^T (w13s rows interleaved in blocks of 32, so
-// accumulator blocks 2*pr and 2*pr+1 are A1 and A3 of the same 32 hidden
-// units) -> Z = silu(A1) A3 row-major, and for K rows Z^T and the SiLU
-// factors of the backward.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_fwd13_256(
+// fwd13: [K; Q] rows x [W1; W3]^T -> Z = silu(A1) A3 row-major, and for K
+// rows Z^T and the SiLU factors of the backward, on the 8-wave engine
+// (gemm_tile256w8, two waves per SIMD).  w13s rows are interleaved in blocks
+// of 32, so wave w, which holds tile rows 128*(w/4) + [0,128) and columns
+// 64*(w%4) + [0,64), has A1 (block ni = 0) and A3 (ni = 1) of the 32 hidden
+// units 32*(w%4) + [0,32) of the tile's 128.  The epilogue runs band by band
+// (a band: tile rows 32*mi + [0,32) of both wave rows), each wave taking its
+// A1/A3 pair and 512 threads sharing the copies out; with two waves per SIMD
+// one wave's epilogue arithmetic and LDS traffic run while the other waits
+// (a 4-wave version, 128x128 per wave with 256 accumulators, took 105.8
+// against 97.9 us per launch at d = 768, h = 1536, C = 8192).
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_fwd13_256(
     Shape s, int r, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ w13s, bf16_t* zrow, bf16_t* zt, uint32_t* fac) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
@@ -588,45 +466,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int64_t tok0 = static_cast<int64_t>(r) * s.C;
   const int64_t nv = n_valid(s, r);
   const bf16_t* X = (isQ ? q : k) + (u * s.L + tok0) * s.d;
-  Loader256 la, lb;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c8 = 8 * loader256_chunk(i);
-    const int64_t p = p0 + loader256_row(i);
-    la.rowp[i] = (p < nv ? X + p * s.d : kZeroRow256) + c8;
-    lb.rowp[i] = w13s + (u * 2 * s.h + nt * 256 + loader256_row(i)) * s.d + c8;
-  }
-  f32x16_t acc[4][4];
-  gemm_tile256(acc, la, lb, 0, s.d, smem_raw);
+  const bf16_t* W = w13s + (u * 2 * s.h + nt * 256) * s.d;
+  f32x16_t acc[4][2];
+  gemm_tile256w8(
+      acc, [&](int R) { return p0 + R < nv ? X + (p0 + R) * s.d : kZeroRow256; },
+      [&](int R) { return W + R * s.d; }, 0, static_cast<int>(s.d / 32), smem_raw);
 
-  const Acc256Pos ps;
+  Acc256Pos ps;
+  ps.wm = ps.wave >> 2;
+  ps.wn = ps.wave & 3;
   bf16_t* lds = reinterpret_cast<bf16_t*>(smem_raw);
-  // The band's Z rows, row-major: [64 band rows][128 units + 8] bf16, after
-  // the transposed band buffer (128 x 72 bf16).
   constexpr int ZRW = 136;
   bf16_t* zr = lds + 128 * 72;
   const int h = static_cast<int>(s.h);
-  // Row p0 of this tile in each output; offsets below are 32-bit.
   bf16_t* zq = zrow + (u * 2 * s.Cp + (isQ ? s.Cp : 0) + p0) * s.h + nt * 128;
-  // Each band in two pieces (one per 32 hidden units), kept apart by
-  // scheduling barriers so that only one piece's values are live at a time.
-  // Z leaves in whole 256-byte row pieces from the staged rows; for K rows Z^T
-  // leaves through the transposed buffer, and the SiLU factors go straight
-  // out (1 KB per instruction).
+  const int j = ps.wn * 32 + ps.r32;  // this lane's hidden unit - nt*128
   auto band = [&](auto MI, auto KROWS) {
     constexpr int mi = decltype(MI)::value;
     constexpr bool krows = decltype(KROWS)::value;
     barrier_lds();  // the previous band's staged rows have been copied out
-#pragma unroll
-    for (int pr = 0; pr < 2; ++pr) {
-      const int j = ps.wn * 64 + pr * 32 + ps.r32;  // hidden unit - nt*128
-      pin_acc(acc[mi][2 * pr]);
-      pin_acc(acc[mi][2 * pr + 1]);
+    {
+      pin_acc(acc[mi][0]);
+      pin_acc(acc[mi][1]);
       float zv[16];
       uint32_t fw[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float a1 = acc[mi][2 * pr][v], a3 = s.gated ? acc[mi][2 * pr + 1][v] : 1.0f;
+        const float a1 = acc[mi][0][v], a3 = s.gated ? acc[mi][1][v] : 1.0f;
         const float sg = sigmoidf_(a1), sl = a1 * sg;
         const float z = sl * a3;
         zv[v] = z;
@@ -639,26 +505,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int vq = 0; vq < 4; ++vq)
           band_put(lds, j, ps, vq, zv[4 * vq], zv[4 * vq + 1], zv[4 * vq + 2], zv[4 * vq + 3]);
         const int64_t tb = (p0 + 128 * ps.wm + 32 * mi) / 32;
-        const int64_t hb = nt * 4 + 2 * ps.wn + pr;
+        const int64_t hb = nt * 4 + ps.wn;
         uint32_t* fb = fac + fac_block(s, u, tb, hb) + 4 * ps.lane;
 #pragma unroll
         for (int vq = 0; vq < 4; ++vq)
           *reinterpret_cast<uint4*>(fb + 256 * vq) =
               make_uint4(fw[4 * vq], fw[4 * vq + 1], fw[4 * vq + 2], fw[4 * vq + 3]);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
     barrier_lds();
-    // Band row br is tile row 128*(br/32) + 32*mi + br%32.
+    // Band row br is tile row 128*(br/32) + 32*mi + br%32: 64 rows x 16
+    // pieces of 16 bytes, two per thread.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = threadIdx.x + 256 * i, br = idx >> 4, c = idx & 15;
+    for (int i = 0; i < 2; ++i) {
+      const int idx = threadIdx.x + 512 * i, br = idx >> 4, c = idx & 15;
       const int tr = 128 * (br >> 5) + 32 * mi + (br & 31);
       *reinterpret_cast<uint4*>(zq + tr * h + 8 * c) =
           *reinterpret_cast<const uint4*>(zr + br * ZRW + 8 * c);
     }
-    if constexpr (krows)  // Z^T band: 128 hidden rows x 64 tokens
-      band_copy(lds, 128, [&](int c) { return zt + (u * s.h + nt * 128 + c) * s.Cp + p0 + 32 * mi; });
+    if constexpr (krows) {  // Z^T band: 128 hidden rows x 64 tokens, two pieces per thread
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int idx = threadIdx.x + 512 * i;
+        const int c = idx >> 3, qq = idx & 7, half = qq >> 2, tok = 8 * (qq & 3);
+        *reinterpret_cast<uint4*>(zt + (u * s.h + nt * 128 + c) * s.Cp + p0 + 32 * mi + 128 * half + tok) =
+            *reinterpret_cast<const uint4*>(lds + c * 72 + 32 * half + tok);
+      }
+    }
   };
   if (isQ) for_bands([&](auto MI) { band(MI, Flag<false>{}); });
   else for_bands([&](auto MI) { band(MI, Flag<true>{}); });

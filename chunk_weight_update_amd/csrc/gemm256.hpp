@@ -448,8 +448,8 @@ __device__ __forceinline__ int64_t fac_block(const Shape& s, int64_t u, int64_t 
 // (a band: tile rows 32*mi + [0,32) of both wave rows), each wave taking its
 // A1/A3 pair and 512 threads sharing the copies out; with two waves per SIMD
 // one wave's epilogue arithmetic and LDS traffic run while the other waits
-// (a 4-wave version, 128x128 per wave with 256 accumulators, took 105.8
-// against 97.9 us per launch at d = 768, h = 1536, C = 8192).
+// (a 4-wave version, 128x128 per wave with 256 accumulators, took 103.5
+// against 98.0 us per launch at d = 768, h = 1536, C = 8192, same box).
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_fwd13_256(
     Shape s, int r, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ w13s, bf16_t* zrow, bf16_t* zt, uint32_t* fac) {

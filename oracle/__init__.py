@@ -119,13 +119,16 @@ def set_threads(n: int) -> None:
 
 def chunk_forward(kind, q, k, v, eta, alpha, beta, W0, M0, chunk, hidden=0,
                   decay_mode=GAMMA_1_MINUS_ETA_ALPHA, averaged=False, qk_norm=False,
-                  row_norm=False, lact=False):
+                  row_norm=False, lact=False, qk_round_bf16=False):
     """Run the literal recurrence.  q,k,v: [B,H,L,d]; eta/alpha/beta: [B,H,L];
     W0, M0: [B,H,P].  averaged: the chunk-averaged variant (beta, gamma
     replaced by their means over each chunk).  lact: the LaCT rule instead
     (one step per chunk on the eta-weighted sum of the descent directions,
     with the chunk means of beta and gamma; exclusive with averaged).  qk_norm: the q/k prologue (SiLU,
-    then L2 normalisation per token) before use.  row_norm: every row of every
+    then L2 normalisation per token) before use; with qk_round_bf16 its
+    outputs are rounded to bf16 (the precision a bf16 layer keeps q and k in,
+    so that, as for bf16 inputs, that rounding is not charged to the GPU).
+    row_norm: every row of every
     fast-weight matrix divided by its L2 norm after each chunk (the
     chunk-boundary stabiliser of App. B.1).  Returns (out [B,H,L,d],
     Wend, Mend), all float64."""
@@ -145,7 +148,8 @@ def chunk_forward(kind, q, k, v, eta, alpha, beta, W0, M0, chunk, hidden=0,
                                   _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
                                   _ptr(alpha), _ptr(beta), _ptr(W0), _ptr(M0),
                                   _ptr(out), _ptr(Wend), _ptr(Mend),
-                                  _variant(averaged, lact), int(bool(qk_norm)),
+                                  _variant(averaged, lact),
+                                  (2 if qk_round_bf16 else 1) if qk_norm else 0,
                                   int(bool(row_norm)))
     if rc != 0:
         raise RuntimeError(f"oracle_chunk_forward failed with code {rc}")

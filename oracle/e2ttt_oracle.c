@@ -40,7 +40,11 @@
  *   - Option (qk_norm != 0): the TTT branch's input prologue of §4 ("Overall
  *     Architecture"): SiLU applied to q_t and k_t, then L2 normalisation of
  *     each token's vector, before anything else uses them.  The pages give no
- *     epsilon; this divides by max(||x||, 1e-12).
+ *     epsilon; this divides by max(||x||, 1e-12).  With qk_norm == 2 every
+ *     normalised value is then rounded to bf16 (to nearest, ties to even,
+ *     through fp32), the precision a bf16 layer stores its q and k in: read
+ *     as the unfused form of the prologue, whose outputs the chunk update
+ *     consumes as its bf16 inputs, like the layer's own q and k.
  *   - Variant (averaged != 0): the chunk-averaged ablation of §5.4 (Table 5)
  *     and App. B.3 (Table 8), where the per-token momentum and decay factors
  *     beta_t, gamma_t of a chunk are collapsed to chunk-level scalars.  The
@@ -102,8 +106,23 @@ enum { OR_GAMMA_1_MINUS_ETA_ALPHA = 0, OR_ALPHA_IS_GAMMA = 1 };
 
 static double sigm(double x) { return 1.0 / (1.0 + exp(-x)); }
 
-/* x <- silu(x) / max(||silu(x)||_2, 1e-12) for L rows of d (the q/k prologue). */
-static void silu_l2_rows(double* x, int64_t L, int64_t d) {
+/* x rounded to the nearest bf16 value (ties to even) through fp32; inf and
+ * NaN pass through. */
+static double round_bf16(double x) {
+  float f = (float)x;
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  if ((u & 0x7f800000u) != 0x7f800000u) {
+    u += 0x7fffu + ((u >> 16) & 1u);
+    u &= 0xffff0000u;
+    memcpy(&f, &u, sizeof f);
+  }
+  return (double)f;
+}
+
+/* x <- silu(x) / max(||silu(x)||_2, 1e-12) for L rows of d (the q/k
+ * prologue), each result rounded to bf16 when round16 != 0. */
+static void silu_l2_rows(double* x, int64_t L, int64_t d, int round16) {
   for (int64_t t = 0; t < L; ++t) {
     double* r = x + t * d;
     double ss = 0.0;
@@ -113,7 +132,7 @@ static void silu_l2_rows(double* x, int64_t L, int64_t d) {
     }
     double nrm = sqrt(ss);
     if (nrm < 1e-12) nrm = 1e-12;
-    for (int64_t i = 0; i < d; ++i) r[i] = r[i] / nrm;
+    for (int64_t i = 0; i < d; ++i) r[i] = round16 ? round_bf16(r[i] / nrm) : r[i] / nrm;
   }
 }
 
@@ -369,8 +388,8 @@ int oracle_chunk_forward(int kind, int decay_mode, int64_t B, int64_t H,
       }
       memcpy(qn, qu, sizeof(double) * (size_t)(L * d));
       memcpy(kn, ku, sizeof(double) * (size_t)(L * d));
-      silu_l2_rows(qn, L, d);
-      silu_l2_rows(kn, L, d);
+      silu_l2_rows(qn, L, d, qk_norm == 2);
+      silu_l2_rows(kn, L, d, qk_norm == 2);
       qu = qn;
       ku = kn;
     }
@@ -885,8 +904,8 @@ int oracle_chunk_backward(int kind, int decay_mode, int64_t B, int64_t H,
     if (qkn) {
       memcpy(qkn, qu, sizeof(double) * (size_t)(L * d));
       memcpy(qkn + L * d, ku, sizeof(double) * (size_t)(L * d));
-      silu_l2_rows(qkn, L, d);
-      silu_l2_rows(qkn + L * d, L, d);
+      silu_l2_rows(qkn, L, d, 0);
+      silu_l2_rows(qkn + L * d, L, d, 0);
       qu = qkn;
       ku = qkn + L * d;
     }

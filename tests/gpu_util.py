@@ -57,9 +57,14 @@ def run_gpu(prob, t, stream=None):
 
 
 def run_oracle(kind, inp, C, h, decay_mode=0, averaged=False, qk_norm=False, row_norm=False,
-               lact=False):
+               lact=False, io=F32):
+    """The oracle's chunk forward on a test's inputs.  With the q/k prologue
+    and bf16 io the prologue's outputs are rounded to bf16, as the forward
+    stores them for its bf16 products (input rounding is not charged to the
+    GPU path)."""
     import oracle
     return oracle.chunk_forward(kind, inp["q64"], inp["k64"], inp["v64"], inp["eta"],
                                 inp["alpha"], inp["beta"], inp["W0"], inp["M0"], C, h,
                                 decay_mode=decay_mode, averaged=averaged, qk_norm=qk_norm,
-                                row_norm=row_norm, lact=lact)
+                                row_norm=row_norm, lact=lact,
+                                qk_round_bf16=bool(qk_norm) and io == BF16)

@@ -76,7 +76,7 @@ def test_decode_with_qk_prologue():
     import oracle
     ro, rW, rM = oracle.chunk_forward(kind, inp["q64"], inp["k64"], inp["v64"], inp["eta"],
                                       inp["alpha"], inp["beta"], inp["W0"], inp["M0"], C, h,
-                                      qk_norm=True)
+                                      qk_norm=True, qk_round_bf16=io == BF16)
     e = (rel_fro(out, ro), rel_fro(W, rW), rel_fro(M, rM))
     log(f"  rel_fro out={e[0]:.3e} W={e[1]:.3e} M={e[2]:.3e}")
     assert e[0] <= 1e-2 and e[1] <= 5e-3 and e[2] <= 5e-3, e

@@ -46,7 +46,7 @@ def check(kind, B, H, L, d, h, C, io, seed=0, regime="default", m0_scale=0.0, de
     out, W, M = run_gpu(prob, to_device(inp, io))
     ro, rW, rM = run_oracle(kind, inp, C, h, decay_mode, averaged=bool(flags & 2),
                             qk_norm=bool(flags & 4), row_norm=bool(flags & 8),
-                            lact=bool(flags & 32))
+                            lact=bool(flags & 32), io=io)
     e = (rel_fro(out, ro), rel_fro(W, rW), rel_fro(M, rM))
     log(f"  rel_fro out={e[0]:.3e} W={e[1]:.3e} M={e[2]:.3e}")
     t = tol or TOL[io]

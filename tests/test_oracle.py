@@ -398,6 +398,30 @@ def test_qk_prologue_is_silu_then_l2_normalisation(kind, d, h):
     assert np.all(out[0, 0, 2] == 0.0)
 
 
+@pytest.mark.parametrize("kind,d,h", [(oracle.LINEAR, 5, 0), (oracle.SWIGLU, 4, 6)])
+def test_qk_prologue_rounded_to_bf16(kind, d, h):
+    """With qk_round_bf16 the option equals the plain run on inputs prepared
+    by torch's silu and normalize, then rounded to bf16 by torch's own
+    conversion (fp32, then bf16 to nearest even); the rounding changes the
+    result (it is not a no-op on these inputs)."""
+    rng = np.random.default_rng(22)
+    L, C = 13, 5
+    q, k, v, eta, alpha, beta, W0, M0 = _rand_problem(rng, kind, L, d, h)
+    q = 3.0 * rng.standard_normal(q.shape)
+    k = 3.0 * rng.standard_normal(k.shape)
+    out, Wend, Mend = oracle.chunk_forward(kind, q, k, v, eta, alpha, beta, W0, M0, C, h,
+                                           qk_norm=True, qk_round_bf16=True)
+    F = torch.nn.functional
+    prep = lambda x: (F.normalize(F.silu(torch.from_numpy(x)), dim=-1, eps=1e-12)
+                      .float().to(torch.bfloat16).double().numpy())
+    out2, W2, M2 = oracle.chunk_forward(kind, prep(q), prep(k), v, eta, alpha, beta, W0, M0,
+                                        C, h)
+    assert _rel(out, out2) <= 1e-13 and _rel(Wend, W2) <= 1e-13 and _rel(Mend, M2) <= 1e-13
+    out3, W3, M3 = oracle.chunk_forward(kind, q, k, v, eta, alpha, beta, W0, M0, C, h,
+                                        qk_norm=True)
+    assert _rel(Wend, W3) > 1e-5
+
+
 def _normalise_rows_np(kind, W, d, h):
     """Rows of every fast-weight matrix divided by max(||row||, 1e-12) (numpy)."""
     W = np.array(W, dtype=np.float64)

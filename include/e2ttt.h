@@ -284,18 +284,22 @@ E2TTT_API e2ttt_status e2ttt_scalar_heads(const e2ttt_problem* prob, const void*
 /* Kernel classes of the chunk forward, for e2ttt_chunk_forward_timed. */
 typedef enum {
   E2TTT_KERNEL_SCAN = 0,       /* scalar kernels, all chunks (one launch)    */
-  E2TTT_KERNEL_PREP = 1,       /* K^T staging and W0 operand shadow          */
+  E2TTT_KERNEL_PREP = 1,       /* K^T staging (on the 256-tile path: the keys
+                                  scaled by K^W and K^M) and W0 operand
+                                  shadow                                    */
   E2TTT_KERNEL_FWD13 = 2,      /* [K;Q] x [W1;W3]^T -> Z (per chunk)          */
   E2TTT_KERNEL_FWD2 = 3,       /* Z x W2^T -> readout, g (per chunk)         */
   E2TTT_KERNEL_BWD = 4,        /* g x W2 -> dA1, dA3 (per chunk)             */
-  E2TTT_KERNEL_AGG = 5,        /* scaled aggregations + state (per chunk)    */
+  E2TTT_KERNEL_AGG = 5,        /* scaled aggregations (+ state, unless split)
+                                  (per chunk)                               */
   E2TTT_KERNEL_LINEAR_FWD = 6, /* linear learner: readout and residuals      */
   E2TTT_KERNEL_LINEAR_AGG = 7, /* linear learner: aggregations + state       */
   E2TTT_KERNEL_PHASE_A = 8,    /* d = 128 bf16: fused forward, readout, g     */
   E2TTT_KERNEL_PHASE_B = 9,    /* d = 128 bf16: fused backward, aggregations,
                                   chunk-end state (unless token-split)      */
-  E2TTT_KERNEL_STATE = 10,     /* d = 128 bf16, token-split phase B: sum of
-                                  the splits, chunk-end state, shadows      */
+  E2TTT_KERNEL_STATE = 10,     /* sum of the token splits (d = 128 bf16
+                                  token-split phase B, or the split 256x256
+                                  aggregation), chunk-end state, shadows    */
   E2TTT_KERNEL_PROLOGUE = 11,  /* d = 128 bf16: scalar kernels, K^T staging
                                   and W0 shadow in one launch               */
   E2TTT_KERNEL_NUM_CLASSES = 12

@@ -18,6 +18,9 @@ CASES = [
     (SWIGLU, 2, 4, 4096, 128, 256, 512, BF16, 0),
     (SWIGLU, 1, 2, 1000, 128, 256, 256, BF16, 0),   # smaller, ragged last chunk
     (LINEAR, 1, 3, 300, 64, 0, 64, F32, 0),
+    # the 256-tile path (scaled keys, split aggregation): ~56 MiB, then ~28 MiB
+    (SWIGLU, 1, 2, 700, 256, 512, 256, BF16, 0),
+    (SWIGLU, 1, 1, 512, 256, 512, 256, BF16, 0),
 ]
 
 
@@ -53,6 +56,11 @@ def test_noalloc_matches_workspace_entry_point_two_calls():
 def test_noalloc_linear_and_repeat():
     run_both(CASES[2], seed=2)
     run_both(CASES[1], seed=3)
+
+
+def test_noalloc_256_tile_path_two_calls():
+    run_both(CASES[3], seed=4)
+    run_both(CASES[4], seed=5)   # smaller, after the larger one
 
 
 def test_noalloc_rejects_problems_beyond_the_scratch():
